@@ -1,0 +1,229 @@
+/*
+ * dsa.h -- C ABI of libdsa: DSA sparse-attention decode over an MLA history
+ * offloaded to pinned host memory behind an HBM hot cache, for MI355X (gfx950).
+ *
+ * Method (page "From 1M total to 15+ streams x 1M: the capacity breakthrough of
+ * GLM-5.3 KV cache offload", zhuai.tech; the "offload page" below):
+ *   - The full MLA history lives in host RAM; the GPU keeps a hot cache of
+ *     S slots that is not a sliding window: any position may be cached, and
+ *     an old position selected by the indexer is read on a miss (section
+ *     "Starting point: separate capacity from the working set").
+ *   - A decode step scores every history position with the DSA indexer,
+ *     takes the exact Top-K, and the GPU itself resolves each selected
+ *     position: a hit reads its HBM slot, a miss reads the registered host
+ *     mirror, producing a compact selection consumed by MLA attention; new
+ *     rows enter a GPU recent ring and are written back in batches; the CPU
+ *     performs no per-selection lookup or copy (section "Decision 3: let the
+ *     GPU manage the hot cache directly", data-flow figure).
+ *   - Slots filled in a round count as hits only from the next round; a
+ *     position missed by several query rows in one round is read from host
+ *     memory; slots in use are pinned; replacement walks the slots as a ring
+ *     and skips the pinned ones (section "GPU cache management errs too:
+ *     cross-block visibility and long replacement sweeps").
+ *   - Before the full history is exported, pending rows are flushed and the
+ *     host row count must reach the logical row count (section "Capacity must
+ *     survive the session lifecycle").
+ *
+ * Data formats
+ *   Q8G64 MLA row (656 bytes for latent_dim=512, group=64, rope_dim=64):
+ *     bytes [0, 512)     int8 latent, two's complement
+ *     bytes [512, 528)   8 fp16 scales, little endian; latent d uses scale d/64
+ *     bytes [528, 656)   64 bf16 RoPE values, little endian
+ *   (offload page, section "Starting point": 512 B latent + 16 B scale +
+ *   128 B RoPE = 656 B.)  Dequantised latent: c[d] = int8[d] * scale[d/64].
+ *   Index keys: bf16 [index_dim] per position, kept in HBM for every position.
+ *
+ * Units.  A unit is one (layer, sequence) pair with its own key store, host
+ * mirror, recent ring, hot cache and slot table.  All sequences of one layer
+ * are stepped together by one dsa_decode_step call.
+ *
+ * Step semantics (per unit, round r = number of decode steps done so far):
+ *   1. Query row i of R sits at position L-R+i (the caller appended the R new
+ *      rows first) and sees positions [0, L-R+i].
+ *   2. score[i][t] = sum_h w[i][h] * max(0, q[i][h] . key[t]), fp32, -0 -> +0.
+ *   3. Selection: the K positions with the largest scores, ties broken by the
+ *      lower position (all visible positions if fewer than K), reported in
+ *      ascending position order.
+ *   4. Union U of the R selections, ascending; map[i][j] = index in U.
+ *   5. Each union entry is classified on the round-start state: RING if the
+ *      row is not yet written back (position >= M), else HIT if cached in a
+ *      slot filled in an earlier round, else MISS.
+ *   6. HIT slots are pinned for round r.  MISSes, in ascending position order,
+ *      take the next slots in ring order from the hand that are not pinned in
+ *      round r (each slot visited at most once); a MISS left without a slot is
+ *      read from host memory and not cached.  hand = last assigned slot + 1.
+ *   7. compact[u] = the 656 bytes of U[u] from its source (slot, ring, or host
+ *      mirror; a freshly filled slot is never the source in the same round).
+ *   8. out[i][h][:] = sum_j softmax_j(scale * (q_lat[i][h] . c_j +
+ *      q_rope[i][h] . rope_j)) * c_j  over row i's selection (absorbed MLA:
+ *      the values are the dequantised latent itself).
+ *   9. If 64 (ring_rows) rows are pending in the ring, they are written back
+ *      to the host mirror as one batch.
+ *
+ * Ownership.  The session owns every persistent buffer: key stores, hot
+ * slots, rings, slot tables and scratch in HBM (allocated once, at exact
+ * sizes, at create), and the host mirrors in pinned, device-mapped host memory
+ * (hipHostMalloc, touched once at create).  append and decode never allocate.
+ * All pointer arguments are borrowed from the caller and must stay valid until
+ * the work enqueued on `stream` completes.
+ *
+ * Asynchrony.  Every call except create, destroy, dsa_unit_state,
+ * dsa_mirror_rows and dsa_last_error only enqueues work on the caller's stream;
+ * results are valid after the caller synchronises that stream.  All calls on
+ * one session must use the same stream, or streams the caller orders; calls on
+ * one session from several host threads must be serialised by the caller.
+ *
+ * Errors.  Arguments are validated before anything is enqueued, so a call that
+ * returns an error other than DSA_E_HIP has no effect.  A failing HIP call
+ * returns DSA_E_HIP and makes the session sticky-failed: every later call
+ * except destroy returns DSA_E_STATE.  dsa_last_error gives the text.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1u
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_E_INVALID = 1,      /* bad argument (NULL, out of range, mismatched size) */
+  DSA_E_NOMEM = 2,        /* allocation failed at create */
+  DSA_E_CAPACITY = 3,     /* append past max_positions */
+  DSA_E_UNSUPPORTED = 4,  /* shape outside what the kernels implement */
+  DSA_E_STATE = 5,        /* wrong order of calls, or the session has failed */
+  DSA_E_HIP = 6           /* a HIP runtime call failed */
+} dsa_status;
+
+typedef enum {
+  DSA_KV_OFFLOAD = 0,       /* rows in a pinned host mirror behind an HBM hot cache */
+  DSA_KV_HBM_RESIDENT = 1   /* every row in HBM; same scoring, selection and attention */
+} dsa_kv_mode;
+
+typedef struct {
+  uint32_t abi_version;    /* DSA_ABI_VERSION */
+  int32_t device;          /* HIP device ordinal */
+  int32_t n_layers;        /* >= 1 */
+  int32_t n_seqs;          /* sequences per layer, 1..64 */
+  int64_t max_positions;   /* per unit: history plus every later append */
+  int32_t index_heads;     /* H_I in {4, 8, 16, 32} */
+  int32_t index_dim;       /* 128 */
+  int32_t heads;           /* H, multiple of 16, <= 128 */
+  int32_t latent_dim;      /* 512 */
+  int32_t rope_dim;        /* 64 */
+  int32_t group;           /* 64 */
+  int32_t top_k;           /* K, 1..4096 */
+  int32_t hot_slots;       /* S >= 1 (offload mode) */
+  int32_t ring_rows;       /* writeback batch, 64 */
+  int32_t max_query_rows;  /* R_max; R_max * K <= 16384 */
+  float softmax_scale;     /* 1/sqrt(latent_dim + rope_dim) */
+  int32_t mode;            /* dsa_kv_mode */
+} dsa_config;
+
+typedef struct dsa_session dsa_session;
+
+/* Validate the configuration and allocate every buffer.  On failure *out is
+ * NULL and nothing is left allocated.  Pass 0 for abi_version-mismatched or
+ * unsupported shapes to get DSA_E_INVALID / DSA_E_UNSUPPORTED. */
+dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out);
+
+/* Synchronise the device, then free everything.  NULL is accepted. */
+dsa_status dsa_session_destroy(dsa_session* s);
+
+/* Append n rows at positions L..L+n-1 of unit (layer, seq).
+ *   index_keys: device, bf16 [n][index_dim], row-major.
+ *   rows:       device, uint8 [n][row_bytes] packed Q8G64 rows.
+ * Keys go to the HBM key store.  Offload mode: rows enter the recent ring;
+ * if the ring (ring_rows + max_query_rows rows) would overflow, whole batches
+ * of ring_rows oldest rows are written to the host mirror first.  Resident
+ * mode: rows go to the HBM row store.  DSA_E_CAPACITY if L+n > max_positions
+ * (nothing is appended). */
+dsa_status dsa_append_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t n,
+                           const void* index_keys, const void* rows, hipStream_t stream);
+
+/* Write every pending ring row of the unit to the host mirror (M = L). */
+dsa_status dsa_flush(dsa_session* s, int32_t layer, int32_t seq, hipStream_t stream);
+
+/* Offload mode: refill the unit's hot cache with its most recent min(S, L)
+ * positions (slot v holds position L-min(S,L)+v), clear all round marks and
+ * set the hand past the last filled slot.  Requires a flushed unit (M == L),
+ * else DSA_E_STATE.  Resident mode: no-op. */
+dsa_status dsa_warm_hot(dsa_session* s, int32_t layer, int32_t seq, hipStream_t stream);
+
+/* One decode step of every sequence of `layer`, R = rows_per_seq query rows
+ * each (1 <= R <= max_query_rows; every sequence must hold at least R rows).
+ *   index_q:  device bf16 [n_seqs][R][index_heads][index_dim]
+ *   index_w:  device f32  [n_seqs][R][index_heads]
+ *   q_latent: device bf16 [n_seqs][R][heads][latent_dim]
+ *   q_rope:   device bf16 [n_seqs][R][heads][rope_dim]
+ *   out:      device f32  [n_seqs][R][heads][latent_dim]  (written) */
+dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq,
+                           const void* index_q, const float* index_w, const void* q_latent,
+                           const void* q_rope, float* out, hipStream_t stream);
+
+/* Host-side logical state of a unit, without blocking:
+ * out[0] = L (rows appended), out[1] = M (rows whose writeback has been
+ * enqueued), out[2] = decode rounds done, out[3] = row bytes. */
+dsa_status dsa_unit_state(const dsa_session* s, int32_t layer, int32_t seq, int64_t out[4]);
+
+/* Rows of the unit known to be in the host mirror: the count of the most
+ * recent writeback whose completion has been observed (non-blocking query).
+ * After dsa_flush and a synchronisation of its stream this equals L. */
+dsa_status dsa_mirror_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t* rows);
+
+/* Text of the most recent error on this session ("" if none).  The pointer
+ * stays valid until the next call on the session. */
+const char* dsa_last_error(const dsa_session* s);
+
+/* ---- Inspection, for parity tests and measurement ------------------------
+ * Copy internal state of unit (layer, seq) into the caller's device buffer
+ * `dst` of `bytes` bytes, stream-ordered.  Step items describe the most recent
+ * dsa_decode_step of that layer.  DSA_E_INVALID if `bytes` is smaller than
+ * the item (dsa_debug_size gives the size). */
+typedef enum {
+  DSA_DBG_SCORES = 0,      /* f32 [R][L]          scores (only t <= L-R+i meaningful for row i) */
+  DSA_DBG_SELECTION = 1,   /* i32 [R][K]          selected positions, ascending, -1 padded */
+  DSA_DBG_SEL_COUNT = 2,   /* i32 [R]             selected count per row */
+  DSA_DBG_UNION = 3,       /* i32 [R*K]           union positions (first U valid) */
+  DSA_DBG_UNION_KIND = 4,  /* i32 [R*K]           0 HIT, 1 RING, 2 MISS, 3 MISS_NOSLOT, 4 RESIDENT */
+  DSA_DBG_UNION_SRC = 5,   /* i32 [R*K]           slot / ring index / position */
+  DSA_DBG_MAP = 6,         /* i32 [R][K]          union index per selected position, -1 padded */
+  DSA_DBG_COMPACT = 7,     /* u8  [R*K][row_bytes] compact selection (first U rows valid) */
+  DSA_DBG_COUNTERS = 8,    /* i64 [8]  union, hit, ring, miss, miss_noslot, evict, host_bytes, resident */
+  DSA_DBG_SLOT_POS = 9,    /* i32 [S] */
+  DSA_DBG_FILL_ROUND = 10, /* i32 [S] */
+  DSA_DBG_PIN_ROUND = 11,  /* i32 [S] */
+  DSA_DBG_POS_SLOT = 12,   /* i32 [L] */
+  DSA_DBG_HAND = 13,       /* i32 [1] */
+  DSA_DBG_SLOT_BYTES = 14, /* u8  [S][row_bytes] */
+  DSA_DBG_MIRROR = 15,     /* u8  [M][row_bytes] host mirror (resident: row store [L]) */
+  DSA_DBG_KEYS = 16        /* bf16 [L][index_dim] */
+} dsa_debug_item;
+
+dsa_status dsa_debug_size(const dsa_session* s, int32_t layer, int32_t seq, int32_t item,
+                          size_t* bytes);
+dsa_status dsa_debug_get(dsa_session* s, int32_t layer, int32_t seq, int32_t item, void* dst,
+                         size_t bytes, hipStream_t stream);
+
+/* ---- Per-kernel timing -----------------------------------------------------
+ * When enabled, every kernel launch of dsa_decode_step is bracketed by HIP
+ * events on the launch stream; dsa_kernel_times synchronises those events and
+ * returns, per kernel kind, the launch count and total milliseconds since the
+ * last reset.  Kinds: 0 index score, 1 top-k histogram passes, 2 top-k emit,
+ * 3 gather plan, 4 gather copy, 5 attention, 6 attention merge. */
+#define DSA_KERNEL_KINDS 7
+dsa_status dsa_set_kernel_timing(dsa_session* s, int32_t enable);
+dsa_status dsa_kernel_times(dsa_session* s, int64_t counts[DSA_KERNEL_KINDS],
+                            double total_ms[DSA_KERNEL_KINDS]);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

@@ -1,0 +1,181 @@
+// k_score.hip -- DSA indexer score over every visible history position.
+//
+//   score[i][t] = sum_h w[i][h] * max(0, q[i][h] . key[t])
+//
+// The indexer scans the whole history so that only the top positions reach
+// attention (page "From 1M total to 15+ streams x 1M: the capacity breakthrough
+// of GLM-5.3 KV cache offload", section "Starting point").  Index keys stay in
+// HBM for every position.
+//
+// gfx950 mapping.  The (query row, head) pairs of a sequence form the M
+// dimension (R*H_I rows, padded to 32), positions form N, the 128 key dims K.
+// One v_mfma_f32_32x32x16_bf16 tile covers 32 (row, head) pairs x 32
+// positions x 16 dims.  Q lives in LDS (row stride padded to 272 B), keys are
+// streamed from HBM straight into B fragments: lane (n, half) loads 16 bytes of
+// key t0+n, so every byte of a key is read exactly once per wave.  The K index
+// is permuted (half 0 takes dims 0..63, half 1 dims 64..127, 8 per k-step);
+// both operands use the same permutation, so the dot products are unchanged.
+// The fp32 accumulator is exact for integer-valued bf16 inputs (|q.k| <= 2^13).
+// After the tile, each lane applies ReLU and the head weight to its 16
+// accumulator rows and the head sum is finished with one cross-half shuffle.
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+typedef short bf16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+constexpr int kQStride = 136;           // bf16 per Q row in LDS (128 + 8 pad)
+constexpr int kWaves = 4;
+
+struct ScoreKArgs {
+  StepArgs a;
+  const uint16_t* q;                    // [n_seqs][R][HI][128]
+  const float* w;                       // [n_seqs][R][HI]
+  int64_t p_pad;
+  int subs_per_wave;                    // 32-position sub-tiles per wave
+};
+
+__device__ inline float canon0(float s) { return s == 0.0f ? 0.0f : s; }
+
+template <int HI>
+__global__ __launch_bounds__(256) void score_kernel(ScoreKArgs ka) {
+  extern __shared__ __align__(16) uint16_t sq[];   // [MT*32][kQStride] then weights
+  const StepArgs& a = ka.a;
+  const int seq = blockIdx.y;
+  const UnitDev u = a.units[a.unit_base + seq];
+  const SeqScratch s = a.scr[seq];
+  const int64_t L = u.dyn[0];
+  const int R = a.R;
+  const int M = R * HI;
+  const int MT = (M + 31) / 32;
+  float* sw = reinterpret_cast<float*>(sq + MT * 32 * kQStride);
+
+  // Stage Q (zero padded to MT*32 rows) and the head weights in LDS.
+  const uint16_t* qg = ka.q + (int64_t)seq * M * 128;
+  for (int c = threadIdx.x; c < MT * 32 * 16; c += blockDim.x) {
+    int row = c >> 4, col = (c & 15) * 8;
+    bf16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (row < M) v = *reinterpret_cast<const bf16x8*>(qg + (int64_t)row * 128 + col);
+    *reinterpret_cast<bf16x8*>(sq + row * kQStride + col) = v;
+  }
+  for (int m = threadIdx.x; m < MT * 32; m += blockDim.x)
+    sw[m] = m < M ? ka.w[(int64_t)seq * M + m] : 0.0f;
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31;
+  const int hf = lane >> 5;
+  const int64_t first_sub = ((int64_t)blockIdx.x * kWaves + wave) * ka.subs_per_wave;
+  float* scores = s.scores;
+
+  for (int si = 0; si < ka.subs_per_wave; ++si) {
+    const int64_t t0 = (first_sub + si) * 32;
+    if (t0 >= L) break;
+    const int64_t t = t0 + n;
+    // B fragments: 8 k-steps x 16 bytes of key t.
+    bf16x8 b[8];
+    if (t < L) {
+      const bf16x8* kp = reinterpret_cast<const bf16x8*>(u.keys + t * 128 + 64 * hf);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) b[ks] = kp[ks];
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) b[ks] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x16 acc = {0};
+      const uint16_t* ap = sq + (mt * 32 + n) * kQStride + 64 * hf;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        bf16x8 av = *reinterpret_cast<const bf16x8*>(ap + 8 * ks);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[ks], acc, 0, 0, 0);
+      }
+      // acc[v] holds C[row = (v/4)*8 + hf*4 + v%4][col = n]
+      float part[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float p = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          int m = mt * 32 + i * 8 + hf * 4 + j;
+          p += sw[m] * fmaxf(acc[i * 4 + j], 0.0f);
+        }
+        part[i] = p;
+      }
+      if constexpr (HI == 32) {
+        float sum = (part[0] + part[1]) + (part[2] + part[3]);
+        sum += __shfl_xor(sum, 32);
+        const int r = mt;
+        if (hf == 0 && r < R && t < L - R + r + 1)
+          scores[(int64_t)r * ka.p_pad + t] = canon0(sum);
+      } else if constexpr (HI == 16) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          float sum = part[2 * k2] + part[2 * k2 + 1];
+          sum += __shfl_xor(sum, 32);
+          const int r = mt * 2 + k2;
+          if (hf == 0 && r < R && t < L - R + r + 1)
+            scores[(int64_t)r * ka.p_pad + t] = canon0(sum);
+        }
+      } else if constexpr (HI == 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float sum = part[i] + __shfl_xor(part[i], 32);
+          const int r = mt * 4 + i;
+          if (hf == 0 && r < R && t < L - R + r + 1)
+            scores[(int64_t)r * ka.p_pad + t] = canon0(sum);
+        }
+      } else {  // HI == 4: rows of one query row sit in one lane half
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = mt * 8 + 2 * i + hf;
+          if (r < R && t < L - R + r + 1)
+            scores[(int64_t)r * ka.p_pad + t] = canon0(part[i]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t prepare_score_kernels() {
+  const int max_lds = 256 * kQStride * 2 + 256 * 4;
+  hipError_t e;
+  if ((e = hipFuncSetAttribute((const void*)score_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds))) return e;
+  if ((e = hipFuncSetAttribute((const void*)score_kernel<8>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds))) return e;
+  if ((e = hipFuncSetAttribute((const void*)score_kernel<16>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds))) return e;
+  return hipFuncSetAttribute((const void*)score_kernel<32>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+}
+
+hipError_t launch_score(const Geometry& g, const StepArgs& a, const uint16_t* q, const float* w,
+                        hipStream_t st) {
+  ScoreKArgs ka;
+  ka.a = a;
+  ka.q = q;
+  ka.w = w;
+  ka.p_pad = g.p_pad;
+  const int64_t subs = (a.l_max + 31) / 32;
+  // Enough waves to cover the chip several times; longer per-wave runs amortise the Q staging.
+  int spw = (int)((subs + 4 * 256 * 4 - 1) / (4 * 256 * 4));
+  if (spw < 1) spw = 1;
+  if (spw > 8) spw = 8;
+  ka.subs_per_wave = spw;
+  const int64_t blocks = (subs + (int64_t)kWaves * spw - 1) / ((int64_t)kWaves * spw);
+  const int MT = (a.R * g.index_heads + 31) / 32;
+  const size_t lds = (size_t)MT * 32 * kQStride * sizeof(uint16_t) + (size_t)MT * 32 * sizeof(float);
+  dim3 grid((unsigned)blocks, (unsigned)a.n_seqs), block(256);
+  switch (g.index_heads) {
+    case 4: hipLaunchKernelGGL(score_kernel<4>, grid, block, lds, st, ka); break;
+    case 8: hipLaunchKernelGGL(score_kernel<8>, grid, block, lds, st, ka); break;
+    case 16: hipLaunchKernelGGL(score_kernel<16>, grid, block, lds, st, ka); break;
+    case 32: hipLaunchKernelGGL(score_kernel<32>, grid, block, lds, st, ka); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,628 @@
+// session.hip -- host runtime behind the C ABI of include/dsa.h.
+//
+// The session owns every allocation (exact sizes, made once at create: the
+// page "From 1M total to 15+ streams x 1M: the capacity breakthrough of
+// GLM-5.3 KV cache offload", section "The ten-way experiment", found that
+// long-lived caches carved from a general caching pool held on to far larger
+// blocks; here nothing long-lived comes from a pool).  Host mirrors are pinned,
+// device-mapped allocations owned by the session and touched once at create.
+// After create, append and decode only enqueue kernels on the caller's stream:
+// no allocation, no host synchronisation, no per-selection host work (section
+// "Decision 3").  The host keeps a mirror of each unit's logical counters
+// (L, M, round) -- they depend only on the call sequence, never on data -- for
+// validation and grid sizing; the kernels keep their own copy in device memory.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dsa.h"
+#include "dsa_internal.h"
+
+using namespace dsa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+struct UnitHost {
+  int64_t L = 0, M = 0, round = 0;
+  int64_t m_done = 0;            // mirror rows known complete
+  int64_t m_event = 0;           // mirror rows covered by `ev`
+  hipEvent_t ev = nullptr;
+  bool ev_pending = false;
+};
+
+struct TimedLaunch {
+  int kind;
+  hipEvent_t a, b;
+};
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+}  // namespace
+
+struct dsa_session {
+  dsa_config cfg{};
+  Geometry g{};
+  int device = 0;
+  bool failed = false;
+  std::string err;
+  void* arena = nullptr;
+  size_t arena_bytes = 0;
+  std::vector<void*> mirrors;              // host pointers (offload)
+  std::vector<UnitDev> units;              // host copies of the device descriptors
+  std::vector<SeqScratch> scr;
+  UnitDev* d_units = nullptr;              // inside the arena
+  SeqScratch* d_scr = nullptr;
+  std::vector<UnitHost> uh;
+  int parity = 0;
+  int last_layer = -1;
+  int last_R = 0;
+  bool timing = false;
+  std::vector<TimedLaunch> timed;
+  std::vector<hipEvent_t> free_events;
+  int64_t t_counts[DSA_KERNEL_KINDS] = {};
+  double t_ms[DSA_KERNEL_KINDS] = {};
+};
+
+namespace {
+
+dsa_status fail(dsa_session* s, dsa_status st, const std::string& msg) {
+  if (s) s->err = msg;
+  return st;
+}
+
+dsa_status hip_fail(dsa_session* s, hipError_t e, const char* what) {
+  s->failed = true;
+  s->err = std::string(what) + ": " + hipGetErrorString(e);
+  return DSA_E_HIP;
+}
+
+#define HIPCHK(expr, what)                         \
+  do {                                             \
+    hipError_t e_ = (expr);                        \
+    if (e_ != hipSuccess) return hip_fail(s, e_, what); \
+  } while (0)
+
+// Keeps the caller's current device.
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+dsa_status entry(dsa_session* s) {
+  if (!s) return DSA_E_INVALID;
+  if (s->failed) return DSA_E_STATE;
+  s->err.clear();
+  return DSA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+dsa_status check_unit(dsa_session* s, int32_t layer, int32_t seq) {
+  if (layer < 0 || layer >= s->cfg.n_layers || seq < 0 || seq >= s->cfg.n_seqs)
+    return fail(s, DSA_E_INVALID, "layer or sequence out of range");
+  return DSA_OK;
+}
+
+size_t unit_index(const dsa_session* s, int32_t layer, int32_t seq) {
+  return (size_t)layer * s->cfg.n_seqs + seq;
+}
+
+// Event bookkeeping for dsa_mirror_rows.
+dsa_status note_mirror(dsa_session* s, UnitHost& h, hipStream_t st) {
+  if (h.ev_pending && hipEventQuery(h.ev) == hipSuccess) h.m_done = h.m_event;
+  HIPCHK(hipEventRecord(h.ev, st), "hipEventRecord");
+  h.m_event = h.M;
+  h.ev_pending = true;
+  return DSA_OK;
+}
+
+hipEvent_t take_event(dsa_session* s) {
+  if (!s->free_events.empty()) {
+    hipEvent_t e = s->free_events.back();
+    s->free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+dsa_status timed_launch(dsa_session* s, int kind, hipStream_t st, const char* what, F&& fn) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (s->timing) {
+    a = take_event(s);
+    b = take_event(s);
+    if (!a || !b) return hip_fail(s, hipErrorOutOfMemory, "hipEventCreate");
+    HIPCHK(hipEventRecord(a, st), "hipEventRecord");
+  }
+  HIPCHK(fn(), what);
+  if (s->timing) {
+    HIPCHK(hipEventRecord(b, st), "hipEventRecord");
+    s->timed.push_back({kind, a, b});
+  }
+  return DSA_OK;
+}
+
+dsa_status validate_config(const dsa_config* c, std::string* why) {
+  auto bad = [&](dsa_status st, const char* m) { *why = m; return st; };
+  if (c->abi_version != DSA_ABI_VERSION) return bad(DSA_E_INVALID, "abi_version mismatch");
+  if (c->n_layers < 1 || c->n_seqs < 1 || c->n_seqs > 64) return bad(DSA_E_INVALID, "n_layers >= 1 and 1 <= n_seqs <= 64");
+  if (c->max_positions < 1 || c->max_positions > ((int64_t)1 << 30)) return bad(DSA_E_INVALID, "max_positions out of range");
+  if (c->mode != DSA_KV_OFFLOAD && c->mode != DSA_KV_HBM_RESIDENT) return bad(DSA_E_INVALID, "unknown mode");
+  if (c->top_k < 1 || c->max_query_rows < 1 || c->ring_rows < 1) return bad(DSA_E_INVALID, "top_k, max_query_rows, ring_rows >= 1");
+  if (c->mode == DSA_KV_OFFLOAD && (c->hot_slots < 1 || c->hot_slots > (1 << 28))) return bad(DSA_E_INVALID, "hot_slots out of range");
+  if (!std::isfinite(c->softmax_scale)) return bad(DSA_E_INVALID, "softmax_scale not finite");
+  if (c->index_dim != 128 || c->latent_dim != 512 || c->rope_dim != 64 || c->group != 64)
+    return bad(DSA_E_UNSUPPORTED, "kernels implement index_dim 128, latent 512, rope 64, group 64");
+  if (c->index_heads != 4 && c->index_heads != 8 && c->index_heads != 16 && c->index_heads != 32)
+    return bad(DSA_E_UNSUPPORTED, "index_heads must be 4, 8, 16 or 32");
+  if (c->heads != 16 && c->heads != 32 && c->heads != 64 && c->heads != 128)
+    return bad(DSA_E_UNSUPPORTED, "heads must be 16, 32, 64 or 128");
+  if (c->max_query_rows > 8 || (int64_t)c->max_query_rows * c->index_heads > 256)
+    return bad(DSA_E_UNSUPPORTED, "max_query_rows <= 8 and max_query_rows * index_heads <= 256");
+  if (c->top_k > 4096 || (int64_t)c->max_query_rows * c->top_k > kMaxUnion)
+    return bad(DSA_E_UNSUPPORTED, "top_k <= 4096 and max_query_rows * top_k <= 16384");
+  if (c->ring_rows > 4096) return bad(DSA_E_UNSUPPORTED, "ring_rows <= 4096");
+  return DSA_OK;
+}
+
+void free_all(dsa_session* s) {
+  for (auto& h : s->uh)
+    if (h.ev) (void)hipEventDestroy(h.ev);
+  for (auto& t : s->timed) {
+    (void)hipEventDestroy(t.a);
+    (void)hipEventDestroy(t.b);
+  }
+  for (auto e : s->free_events) (void)hipEventDestroy(e);
+  for (void* m : s->mirrors)
+    if (m) (void)hipHostFree(m);
+  if (s->arena) (void)hipFree(s->arena);
+  s->uh.clear();
+  s->timed.clear();
+  s->free_events.clear();
+  s->mirrors.clear();
+  s->arena = nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
+  if (!out) return DSA_E_INVALID;
+  *out = nullptr;
+  if (!cfg) return DSA_E_INVALID;
+  std::string why;
+  dsa_status st = validate_config(cfg, &why);
+  if (st != DSA_OK) return st;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device < 0 || cfg->device >= ndev) return DSA_E_INVALID;
+
+  dsa_session* s = new dsa_session();
+  s->cfg = *cfg;
+  s->device = cfg->device;
+  DeviceGuard dg(s->device);
+
+  Geometry& g = s->g;
+  g.index_heads = cfg->index_heads;
+  g.index_dim = cfg->index_dim;
+  g.heads = cfg->heads;
+  g.latent = cfg->latent_dim;
+  g.rope = cfg->rope_dim;
+  g.group = cfg->group;
+  g.top_k = cfg->top_k;
+  g.hot_slots = cfg->mode == DSA_KV_OFFLOAD ? cfg->hot_slots : 0;
+  g.ring_rows = cfg->ring_rows;
+  g.ring_cap = cfg->ring_rows + cfg->max_query_rows;
+  g.r_max = cfg->max_query_rows;
+  g.row_bytes = cfg->latent_dim + 2 * (cfg->latent_dim / cfg->group) + 2 * cfg->rope_dim;
+  g.mode = cfg->mode;
+  g.max_positions = cfg->max_positions;
+  g.p_pad = (cfg->max_positions + kTopkChunk - 1) / kTopkChunk * kTopkChunk;
+  g.n_chunks = (int)(g.p_pad / kTopkChunk);
+  g.attn_split_rows = 128;
+  g.nsplit = (cfg->top_k + g.attn_split_rows - 1) / g.attn_split_rows;
+  g.softmax_scale = cfg->softmax_scale;
+
+  const int n_units = cfg->n_layers * cfg->n_seqs;
+  const int64_t P = g.p_pad, S = g.hot_slots, RK = (int64_t)g.r_max * g.top_k, rb = g.row_bytes;
+  const bool off = cfg->mode == DSA_KV_OFFLOAD;
+
+  // ---- arena layout (exact sizes, 256-byte aligned pieces)
+  size_t cur = 0;
+  auto take = [&](size_t bytes) { size_t at = cur; cur += align_up(bytes ? bytes : 1); return at; };
+  const size_t o_units = take(sizeof(UnitDev) * n_units);
+  const size_t o_scr = take(sizeof(SeqScratch) * cfg->n_seqs);
+  struct UnitOff { size_t keys, rows, slots, ring, pos_slot, slot_pos, fill, pin, hand, dyn; };
+  std::vector<UnitOff> uo(n_units);
+  for (int i = 0; i < n_units; ++i) {
+    uo[i].keys = take((size_t)P * g.index_dim * 2);
+    uo[i].rows = off ? 0 : take((size_t)P * rb);
+    uo[i].slots = off ? take((size_t)S * rb) : 0;
+    uo[i].ring = off ? take((size_t)g.ring_cap * rb) : 0;
+    uo[i].pos_slot = off ? take((size_t)P * 4) : 0;
+    uo[i].slot_pos = off ? take((size_t)S * 4) : 0;
+    uo[i].fill = off ? take((size_t)S * 4) : 0;
+    uo[i].pin = off ? take((size_t)S * 4) : 0;
+    uo[i].hand = take(4);
+    uo[i].dyn = take(32);
+  }
+  struct ScrOff { size_t scores, hist, suffix, gt22, sel, sel_n, uni, kind, src, fill, map, compact, po, pml, cnt, info; };
+  std::vector<ScrOff> so(cfg->n_seqs);
+  for (int q = 0; q < cfg->n_seqs; ++q) {
+    so[q].scores = take((size_t)g.r_max * P * 4);
+    so[q].hist = take((size_t)2 * g.r_max * 3 * kRadixBins * 4);
+    so[q].suffix = take((size_t)g.r_max * g.n_chunks * kSuffixLen * 4);
+    so[q].gt22 = take((size_t)g.r_max * g.n_chunks * 4);
+    so[q].sel = take((size_t)RK * 4);
+    so[q].sel_n = take((size_t)g.r_max * 4);
+    so[q].uni = take((size_t)RK * 4);
+    so[q].kind = take((size_t)RK * 4);
+    so[q].src = take((size_t)RK * 4);
+    so[q].fill = take((size_t)RK * 4);
+    so[q].map = take((size_t)RK * 4);
+    so[q].compact = take((size_t)RK * rb);
+    so[q].po = take((size_t)g.r_max * g.nsplit * g.heads * g.latent * 4);
+    so[q].pml = take((size_t)g.r_max * g.nsplit * g.heads * 2 * 4);
+    so[q].cnt = take(8 * 8);
+    so[q].info = take(4 * 8);
+  }
+  s->arena_bytes = cur;
+
+  auto bail = [&](dsa_status code, const char* msg) {
+    free_all(s);
+    delete s;
+    (void)msg;
+    return code;
+  };
+  hipError_t e;
+  if ((e = prepare_score_kernels()) != hipSuccess) return bail(DSA_E_HIP, "prepare");
+  if ((e = prepare_gather_kernels()) != hipSuccess) return bail(DSA_E_HIP, "prepare");
+  if (hipMalloc(&s->arena, s->arena_bytes) != hipSuccess) {
+    s->arena = nullptr;
+    (void)hipGetLastError();
+    return bail(DSA_E_NOMEM, "hipMalloc");
+  }
+  uint8_t* base = static_cast<uint8_t*>(s->arena);
+  if (hipMemset(s->arena, 0, s->arena_bytes) != hipSuccess) return bail(DSA_E_HIP, "hipMemset");
+
+  s->mirrors.assign(n_units, nullptr);
+  s->units.resize(n_units);
+  s->uh.resize(n_units);
+  for (int i = 0; i < n_units; ++i) {
+    UnitDev& u = s->units[i];
+    u.keys = reinterpret_cast<uint16_t*>(base + uo[i].keys);
+    if (off) {
+      void* hp = nullptr;
+      if (hipHostMalloc(&hp, (size_t)P * rb, hipHostMallocMapped) != hipSuccess || !hp) {
+        (void)hipGetLastError();
+        return bail(DSA_E_NOMEM, "hipHostMalloc");
+      }
+      s->mirrors[i] = hp;
+      std::memset(hp, 0, (size_t)P * rb);            // touch every page once, before use
+      void* dp = nullptr;
+      if (hipHostGetDevicePointer(&dp, hp, 0) != hipSuccess) return bail(DSA_E_HIP, "hipHostGetDevicePointer");
+      u.rows = static_cast<uint8_t*>(dp);
+      u.slots = base + uo[i].slots;
+      u.ring = base + uo[i].ring;
+      u.pos_slot = reinterpret_cast<int32_t*>(base + uo[i].pos_slot);
+      u.slot_pos = reinterpret_cast<int32_t*>(base + uo[i].slot_pos);
+      u.fill_round = reinterpret_cast<int32_t*>(base + uo[i].fill);
+      u.pin_round = reinterpret_cast<int32_t*>(base + uo[i].pin);
+      if (hipMemset(u.pos_slot, 0xFF, (size_t)P * 4) != hipSuccess ||
+          hipMemset(u.slot_pos, 0xFF, (size_t)S * 4) != hipSuccess ||
+          hipMemset(u.fill_round, 0xFF, (size_t)S * 4) != hipSuccess ||
+          hipMemset(u.pin_round, 0xFF, (size_t)S * 4) != hipSuccess)
+        return bail(DSA_E_HIP, "hipMemset");
+    } else {
+      u.rows = base + uo[i].rows;
+    }
+    u.hand = reinterpret_cast<int32_t*>(base + uo[i].hand);
+    u.dyn = reinterpret_cast<int64_t*>(base + uo[i].dyn);
+    if (hipEventCreateWithFlags(&s->uh[i].ev, hipEventDisableTiming) != hipSuccess) return bail(DSA_E_HIP, "event");
+  }
+  s->scr.resize(cfg->n_seqs);
+  for (int q = 0; q < cfg->n_seqs; ++q) {
+    SeqScratch& c = s->scr[q];
+    c.scores = reinterpret_cast<float*>(base + so[q].scores);
+    c.hist = reinterpret_cast<uint32_t*>(base + so[q].hist);
+    c.suffix = reinterpret_cast<uint32_t*>(base + so[q].suffix);
+    c.gt22 = reinterpret_cast<uint32_t*>(base + so[q].gt22);
+    c.sel = reinterpret_cast<int32_t*>(base + so[q].sel);
+    c.sel_n = reinterpret_cast<int32_t*>(base + so[q].sel_n);
+    c.uni = reinterpret_cast<int32_t*>(base + so[q].uni);
+    c.kind = reinterpret_cast<int32_t*>(base + so[q].kind);
+    c.src = reinterpret_cast<int32_t*>(base + so[q].src);
+    c.fill = reinterpret_cast<int32_t*>(base + so[q].fill);
+    c.map = reinterpret_cast<int32_t*>(base + so[q].map);
+    c.compact = base + so[q].compact;
+    c.part_o = reinterpret_cast<float*>(base + so[q].po);
+    c.part_ml = reinterpret_cast<float*>(base + so[q].pml);
+    c.counters = reinterpret_cast<int64_t*>(base + so[q].cnt);
+    c.info = reinterpret_cast<int64_t*>(base + so[q].info);
+    if (hipMemset(c.sel, 0xFF, (size_t)RK * 4) != hipSuccess || hipMemset(c.map, 0xFF, (size_t)RK * 4) != hipSuccess)
+      return bail(DSA_E_HIP, "hipMemset");
+  }
+  s->d_units = reinterpret_cast<UnitDev*>(base + o_units);
+  s->d_scr = reinterpret_cast<SeqScratch*>(base + o_scr);
+  if (hipMemcpy(s->d_units, s->units.data(), sizeof(UnitDev) * n_units, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(s->d_scr, s->scr.data(), sizeof(SeqScratch) * cfg->n_seqs, hipMemcpyHostToDevice) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess)
+    return bail(DSA_E_HIP, "hipMemcpy");
+  *out = s;
+  return DSA_OK;
+}
+
+dsa_status dsa_session_destroy(dsa_session* s) {
+  if (!s) return DSA_OK;
+  {
+    DeviceGuard dg(s->device);
+    (void)hipDeviceSynchronize();
+    free_all(s);
+  }
+  delete s;
+  return DSA_OK;
+}
+
+dsa_status dsa_append_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t n, const void* index_keys,
+                           const void* rows, hipStream_t stream) {
+  dsa_status st = entry(s);
+  if (st != DSA_OK) return st;
+  if ((st = check_unit(s, layer, seq)) != DSA_OK) return st;
+  if (n < 0) return fail(s, DSA_E_INVALID, "n < 0");
+  if (n == 0) return DSA_OK;
+  if (!index_keys || !rows || !aligned(index_keys, 16) || !aligned(rows, 16))
+    return fail(s, DSA_E_INVALID, "keys and rows must be non-NULL and 16-byte aligned");
+  const size_t ui = unit_index(s, layer, seq);
+  UnitHost& h = s->uh[ui];
+  if (h.L + n > s->cfg.max_positions) return fail(s, DSA_E_CAPACITY, "append past max_positions");
+  DeviceGuard dg(s->device);
+  int64_t newM = h.M;
+  if (s->g.mode == DSA_KV_OFFLOAD)
+    while (h.L + n - newM > s->g.ring_cap) newM += s->g.ring_rows;
+  HIPCHK(launch_append(s->g, s->units[ui], h.L, h.M, newM, n, static_cast<const uint16_t*>(index_keys),
+                       static_cast<const uint8_t*>(rows), stream), "append kernel");
+  const bool moved = newM != h.M;
+  h.L += n;
+  h.M = s->g.mode == DSA_KV_OFFLOAD ? newM : h.L;
+  if (moved && s->g.mode == DSA_KV_OFFLOAD) return note_mirror(s, h, stream);
+  return DSA_OK;
+}
+
+dsa_status dsa_flush(dsa_session* s, int32_t layer, int32_t seq, hipStream_t stream) {
+  dsa_status st = entry(s);
+  if (st != DSA_OK) return st;
+  if ((st = check_unit(s, layer, seq)) != DSA_OK) return st;
+  UnitHost& h = s->uh[unit_index(s, layer, seq)];
+  if (s->g.mode != DSA_KV_OFFLOAD) return DSA_OK;
+  DeviceGuard dg(s->device);
+  if (h.M < h.L) {
+    HIPCHK(launch_flush(s->g, s->units[unit_index(s, layer, seq)], h.M, h.L, stream), "flush kernel");
+    h.M = h.L;
+  }
+  return note_mirror(s, h, stream);
+}
+
+dsa_status dsa_warm_hot(dsa_session* s, int32_t layer, int32_t seq, hipStream_t stream) {
+  dsa_status st = entry(s);
+  if (st != DSA_OK) return st;
+  if ((st = check_unit(s, layer, seq)) != DSA_OK) return st;
+  if (s->g.mode != DSA_KV_OFFLOAD) return DSA_OK;
+  UnitHost& h = s->uh[unit_index(s, layer, seq)];
+  if (h.M != h.L) return fail(s, DSA_E_STATE, "warm needs a flushed unit (M == L)");
+  DeviceGuard dg(s->device);
+  HIPCHK(launch_warm(s->g, s->units[unit_index(s, layer, seq)], h.L, stream), "warm kernels");
+  return DSA_OK;
+}
+
+dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq, const void* index_q,
+                           const float* index_w, const void* q_latent, const void* q_rope, float* out,
+                           hipStream_t stream) {
+  dsa_status st = entry(s);
+  if (st != DSA_OK) return st;
+  if (layer < 0 || layer >= s->cfg.n_layers) return fail(s, DSA_E_INVALID, "layer out of range");
+  const int R = rows_per_seq;
+  if (R < 1 || R > s->g.r_max) return fail(s, DSA_E_INVALID, "rows_per_seq out of range");
+  if (!index_q || !index_w || !q_latent || !q_rope || !out || !aligned(index_q, 16) || !aligned(q_latent, 16) ||
+      !aligned(q_rope, 16) || !aligned(index_w, 4) || !aligned(out, 4))
+    return fail(s, DSA_E_INVALID, "step buffers must be non-NULL; bf16 inputs 16-byte aligned");
+  const int n_seqs = s->cfg.n_seqs;
+  int64_t l_max = 0;
+  for (int q = 0; q < n_seqs; ++q) {
+    const UnitHost& h = s->uh[unit_index(s, layer, q)];
+    if (h.L < R) return fail(s, DSA_E_STATE, "a sequence holds fewer rows than rows_per_seq");
+    l_max = std::max(l_max, h.L);
+  }
+  DeviceGuard dg(s->device);
+  StepArgs a;
+  a.units = s->d_units;
+  a.scr = s->d_scr;
+  a.unit_base = layer * n_seqs;
+  a.n_seqs = n_seqs;
+  a.R = R;
+  a.parity = s->parity;
+  a.l_max = l_max;
+  const Geometry& g = s->g;
+  const uint16_t* iq = static_cast<const uint16_t*>(index_q);
+  const uint16_t* ql = static_cast<const uint16_t*>(q_latent);
+  const uint16_t* qr = static_cast<const uint16_t*>(q_rope);
+  if ((st = timed_launch(s, KK_SCORE, stream, "score kernel", [&] { return launch_score(g, a, iq, index_w, stream); })) != DSA_OK) return st;
+  for (int pass = 0; pass < 3; ++pass)
+    if ((st = timed_launch(s, KK_TOPK_HIST, stream, "top-k histogram", [&] { return launch_topk_hist(g, a, pass, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_TOPK_EMIT, stream, "top-k emit", [&] { return launch_topk_emit(g, a, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_PLAN, stream, "gather plan", [&] { return launch_plan(g, a, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_COPY, stream, "gather copy", [&] { return launch_copy(g, a, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_ATTN, stream, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream); })) != DSA_OK) return st;
+  if (g.nsplit > 1)
+    if ((st = timed_launch(s, KK_MERGE, stream, "attention merge", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK) return st;
+  s->parity ^= 1;
+  s->last_layer = layer;
+  s->last_R = R;
+  for (int q = 0; q < n_seqs; ++q) {
+    UnitHost& h = s->uh[unit_index(s, layer, q)];
+    h.round += 1;
+    if (g.mode == DSA_KV_OFFLOAD && h.L - h.M >= g.ring_rows) {
+      h.M += g.ring_rows;
+      if ((st = note_mirror(s, h, stream)) != DSA_OK) return st;
+    }
+  }
+  return DSA_OK;
+}
+
+dsa_status dsa_unit_state(const dsa_session* s, int32_t layer, int32_t seq, int64_t out[4]) {
+  if (!s || !out) return DSA_E_INVALID;
+  if (layer < 0 || layer >= s->cfg.n_layers || seq < 0 || seq >= s->cfg.n_seqs) return DSA_E_INVALID;
+  const UnitHost& h = s->uh[unit_index(s, layer, seq)];
+  out[0] = h.L;
+  out[1] = h.M;
+  out[2] = h.round;
+  out[3] = s->g.row_bytes;
+  return DSA_OK;
+}
+
+dsa_status dsa_mirror_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t* rows) {
+  dsa_status st = entry(s);
+  if (st != DSA_OK) return st;
+  if ((st = check_unit(s, layer, seq)) != DSA_OK) return st;
+  if (!rows) return DSA_E_INVALID;
+  UnitHost& h = s->uh[unit_index(s, layer, seq)];
+  if (s->g.mode != DSA_KV_OFFLOAD) {
+    *rows = 0;
+    return DSA_OK;
+  }
+  if (h.ev_pending) {
+    DeviceGuard dg(s->device);
+    hipError_t q = hipEventQuery(h.ev);
+    if (q == hipSuccess) {
+      h.m_done = h.m_event;
+      h.ev_pending = false;
+    } else if (q != hipErrorNotReady) {
+      return hip_fail(s, q, "hipEventQuery");
+    }
+  }
+  *rows = h.m_done;
+  return DSA_OK;
+}
+
+const char* dsa_last_error(const dsa_session* s) { return s ? s->err.c_str() : "NULL session"; }
+
+dsa_status dsa_debug_size(const dsa_session* s, int32_t layer, int32_t seq, int32_t item, size_t* bytes) {
+  if (!s || !bytes) return DSA_E_INVALID;
+  if (layer < 0 || layer >= s->cfg.n_layers || seq < 0 || seq >= s->cfg.n_seqs) return DSA_E_INVALID;
+  const Geometry& g = s->g;
+  const UnitHost& h = s->uh[unit_index(s, layer, seq)];
+  const int64_t R = s->last_R, K = g.top_k, S = g.hot_slots, rb = g.row_bytes;
+  size_t b = 0;
+  switch (item) {
+    case DSA_DBG_SCORES: b = (size_t)R * h.L * 4; break;
+    case DSA_DBG_SELECTION: b = (size_t)R * K * 4; break;
+    case DSA_DBG_SEL_COUNT: b = (size_t)R * 4; break;
+    case DSA_DBG_UNION: case DSA_DBG_UNION_KIND: case DSA_DBG_UNION_SRC: b = (size_t)R * K * 4; break;
+    case DSA_DBG_MAP: b = (size_t)R * K * 4; break;
+    case DSA_DBG_COMPACT: b = (size_t)R * K * rb; break;
+    case DSA_DBG_COUNTERS: b = 64; break;
+    case DSA_DBG_SLOT_POS: case DSA_DBG_FILL_ROUND: case DSA_DBG_PIN_ROUND: b = (size_t)S * 4; break;
+    case DSA_DBG_POS_SLOT: b = g.mode == DSA_KV_OFFLOAD ? (size_t)h.L * 4 : 0; break;
+    case DSA_DBG_HAND: b = 4; break;
+    case DSA_DBG_SLOT_BYTES: b = (size_t)S * rb; break;
+    case DSA_DBG_MIRROR: b = (size_t)(g.mode == DSA_KV_OFFLOAD ? h.M : h.L) * rb; break;
+    case DSA_DBG_KEYS: b = (size_t)h.L * g.index_dim * 2; break;
+    default: return DSA_E_INVALID;
+  }
+  *bytes = b;
+  return DSA_OK;
+}
+
+dsa_status dsa_debug_get(dsa_session* s, int32_t layer, int32_t seq, int32_t item, void* dst, size_t bytes,
+                         hipStream_t stream) {
+  dsa_status st = entry(s);
+  if (st != DSA_OK) return st;
+  if ((st = check_unit(s, layer, seq)) != DSA_OK) return st;
+  const bool step_item = item <= DSA_DBG_COUNTERS;
+  if (step_item && s->last_layer != layer) return fail(s, DSA_E_STATE, "no step of this layer is the most recent");
+  size_t need = 0;
+  if ((st = dsa_debug_size(s, layer, seq, item, &need)) != DSA_OK) return fail(s, st, "unknown item");
+  if (!dst || bytes < need) return fail(s, DSA_E_INVALID, "destination too small");
+  if (need == 0) return DSA_OK;
+  const Geometry& g = s->g;
+  const size_t ui = unit_index(s, layer, seq);
+  const UnitDev& u = s->units[ui];
+  const SeqScratch& c = s->scr[seq];
+  const UnitHost& h = s->uh[ui];
+  const int64_t R = s->last_R, K = g.top_k;
+  DeviceGuard dg(s->device);
+  const void* src = nullptr;
+  switch (item) {
+    case DSA_DBG_SCORES:
+      for (int64_t r = 0; r < R; ++r)
+        HIPCHK(hipMemcpyAsync(static_cast<uint8_t*>(dst) + r * h.L * 4, c.scores + r * g.p_pad, (size_t)h.L * 4,
+                              hipMemcpyDeviceToDevice, stream), "hipMemcpyAsync");
+      return DSA_OK;
+    case DSA_DBG_SELECTION: src = c.sel; break;
+    case DSA_DBG_SEL_COUNT: src = c.sel_n; break;
+    case DSA_DBG_UNION: src = c.uni; break;
+    case DSA_DBG_UNION_KIND: src = c.kind; break;
+    case DSA_DBG_UNION_SRC: src = c.src; break;
+    case DSA_DBG_MAP: src = c.map; break;
+    case DSA_DBG_COMPACT: src = c.compact; break;
+    case DSA_DBG_COUNTERS: src = c.counters; break;
+    case DSA_DBG_SLOT_POS: src = u.slot_pos; break;
+    case DSA_DBG_FILL_ROUND: src = u.fill_round; break;
+    case DSA_DBG_PIN_ROUND: src = u.pin_round; break;
+    case DSA_DBG_POS_SLOT: src = u.pos_slot; break;
+    case DSA_DBG_HAND: src = u.hand; break;
+    case DSA_DBG_SLOT_BYTES: src = u.slots; break;
+    case DSA_DBG_MIRROR: src = g.mode == DSA_KV_OFFLOAD ? s->mirrors[ui] : (const void*)u.rows; break;
+    case DSA_DBG_KEYS: src = u.keys; break;
+    default: return fail(s, DSA_E_INVALID, "unknown item");
+  }
+  (void)K;
+  HIPCHK(hipMemcpyAsync(dst, src, need, hipMemcpyDefault, stream), "hipMemcpyAsync");
+  return DSA_OK;
+}
+
+dsa_status dsa_set_kernel_timing(dsa_session* s, int32_t enable) {
+  dsa_status st = entry(s);
+  if (st != DSA_OK) return st;
+  s->timing = enable != 0;
+  return DSA_OK;
+}
+
+dsa_status dsa_kernel_times(dsa_session* s, int64_t counts[DSA_KERNEL_KINDS], double total_ms[DSA_KERNEL_KINDS]) {
+  dsa_status st = entry(s);
+  if (st != DSA_OK) return st;
+  if (!counts || !total_ms) return DSA_E_INVALID;
+  DeviceGuard dg(s->device);
+  for (auto& t : s->timed) {
+    HIPCHK(hipEventSynchronize(t.b), "hipEventSynchronize");
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, t.a, t.b), "hipEventElapsedTime");
+    s->t_counts[t.kind] += 1;
+    s->t_ms[t.kind] += ms;
+    s->free_events.push_back(t.a);
+    s->free_events.push_back(t.b);
+  }
+  s->timed.clear();
+  for (int k = 0; k < DSA_KERNEL_KINDS; ++k) {
+    counts[k] = s->t_counts[k];
+    total_ms[k] = s->t_ms[k];
+    s->t_counts[k] = 0;
+    s->t_ms[k] = 0.0;
+  }
+  return DSA_OK;
+}
+
+}  // extern "C"
