@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark: DSA sparse-attention decode steps over an offloaded MLA history on one MI355X.
+
+One step = append the step's R new rows (index keys to HBM, Q8G64 rows into the
+recent ring) + one decode step (index score over every history position, exact
+Top-K, hot-cache gather with host-mirror misses, absorbed-MLA attention over the
+selected rows, 64-row batched writeback), for the 50,023-row single-stream
+workload (R = 4 query rows, Top-2048, 32,768 hot slots, H_I = 32, H = 64).
+All inputs are synthetic, seeded, and resident in HBM before timing starts.
+
+Prints ONE JSON line.  Per-kernel durations come from HIP events recorded by the
+library around each launch on the launch stream, in a separate pass after the
+timed region (the timed region itself carries no events).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode steps/s at 50,023 history (query rows/s; % HBM roofline)"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+HOST_LINK_PEAK_GBPS = 64.0      # PCIe Gen5 x16, one direction, nominal
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=1024)
+    p.add_argument("--warmup", type=int, default=16)
+    p.add_argument("--workload", default="single_stream_50k")
+    p.add_argument("--kernel-steps", type=int, default=128, help="steps of the per-kernel event pass")
+    p.add_argument("--no-resident", action="store_true", help="skip the HBM-resident comparison run")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--calib-copy", action="store_true", help="also run a plain 256 MiB device copy (PMC scaling)")
+    return p.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def gen_inputs(w, n_steps):
+    import dsa_synth as S
+    R = w.rows_per_step
+    keys = np.empty((n_steps, R, w.index_dim), np.uint16)
+    rows = np.empty((n_steps, R, w.row_bytes), np.uint8)
+    iq = np.empty((n_steps, 1, R, w.index_heads, w.index_dim), np.uint16)
+    iw = np.empty((n_steps, 1, R, w.index_heads), np.float32)
+    ql = np.empty((n_steps, 1, R, w.heads, w.latent_dim), np.uint16)
+    qr = np.empty((n_steps, 1, R, w.heads, w.rope_dim), np.uint16)
+    for s in range(n_steps):
+        keys[s], rows[s] = S.step_rows(w, 0, 0, s)
+        iq[s, 0], iw[s, 0], ql[s, 0], qr[s, 0] = S.step_queries(w, 0, 0, s)
+    return keys, rows, iq, iw, ql, qr
+
+
+class Runner:
+    """One session with every step's inputs already in HBM; calls the C ABI directly."""
+
+    def __init__(self, w, mode, host_inputs, hist):
+        import torch
+        import kv_cache_offload_amd as K
+        from tests.parity_util import dev_tensor
+        self.K, self.torch, self.w = K, torch, w
+        cfg = K.make_config(max_positions=w.max_positions, index_heads=w.index_heads, heads=w.heads,
+                            top_k=w.top_k, hot_slots=w.hot_slots, max_query_rows=w.rows_per_step,
+                            n_seqs=w.seqs, softmax_scale=w.softmax_scale, mode=mode)
+        self.sess = K.Session(cfg)
+        dev = self.sess.device
+        hk, hr = hist
+        for c in range(0, hk.shape[0], 65536):
+            self.sess.append_rows(0, 0, dev_tensor(hk[c:c + 65536], dev), dev_tensor(hr[c:c + 65536], dev))
+        self.sess.flush(0, 0)
+        if mode == K.KV_OFFLOAD and w.warm:
+            self.sess.warm_hot(0, 0)
+        self.d = [dev_tensor(a, dev) for a in host_inputs]
+        self.out = torch.empty((1, w.rows_per_step, w.heads, w.latent_dim), dtype=torch.float32, device=dev)
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        keys, rows, iq, iw, ql, qr = self.d
+        self.ptr = [tuple(int(t[s].data_ptr()) for t in self.d) for s in range(keys.shape[0])]
+        self.h = self.sess.h
+        self.next = 0
+        torch.cuda.synchronize()
+
+    def steps(self, n):
+        K, R, lib = self.K, self.w.rows_per_step, self.K._lib
+        out = ctypes.c_void_p(self.out.data_ptr())
+        for _ in range(n):
+            pk, pr, piq, piw, pql, pqr = self.ptr[self.next]
+            st = lib.dsa_append_rows(self.h, 0, 0, R, ctypes.c_void_p(pk), ctypes.c_void_p(pr), self.stream)
+            if st != K.OK:
+                raise K.DsaError("dsa_append_rows", st, K.dsa_last_error(self.h))
+            st = lib.dsa_decode_step(self.h, 0, R, ctypes.c_void_p(piq), ctypes.c_void_p(piw), ctypes.c_void_p(pql),
+                                     ctypes.c_void_p(pqr), out, self.stream)
+            if st != K.OK:
+                raise K.DsaError("dsa_decode_step", st, K.dsa_last_error(self.h))
+            self.next += 1
+
+    def totals(self):
+        self.torch.cuda.synchronize()
+        return self.sess.debug("totals").cpu().numpy().view(np.int64).copy()
+
+    def L(self):
+        return self.sess.unit_state(0, 0)["L"]
+
+
+def timed(runner, n):
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    runner.steps(n)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def kernel_pass(runner, n):
+    """Per-kernel average durations (ms) over n more steps, plus the unit's counter deltas."""
+    L0 = runner.L()
+    c0 = runner.totals()
+    runner.sess.set_kernel_timing(True)
+    runner.steps(n)
+    runner.torch.cuda.synchronize()
+    kt = runner.sess.kernel_times()
+    runner.sess.set_kernel_timing(False)
+    c1 = runner.totals()
+    return kt, (c1 - c0), L0
+
+
+def algorithmic_bytes(w, kind, n_steps, L0, cnt):
+    """Bytes each kernel must move per launch, averaged over the kernel pass."""
+    R, K, H = w.rows_per_step, w.top_k, w.heads
+    Lmean = L0 + R * (n_steps + 1) / 2.0
+    rb = w.row_bytes
+    U = cnt[0] / n_steps
+    hit, ring, miss, noslot = (cnt[i] / n_steps for i in (1, 2, 3, 4))
+    res = cnt[7] / n_steps
+    if kind == "index_score":
+        return Lmean * w.index_dim * 2                     # every key once
+    if kind == "topk_collect":
+        return R * Lmean * 4                               # one pass over the scores
+    if kind == "topk_resolve":
+        return R * K * 4 * 2                               # candidates in, selection out
+    if kind == "gather_scan":
+        return Lmean / 32 * 4 * 3                          # the union and hit bitmaps, word prefixes
+    if kind == "gather_assign":
+        return U * 4 * 4 + (miss * 4 * 5)                  # union entries, slot-table updates
+    if kind == "gather_copy":
+        return (hit + ring + res) * rb + U * rb + miss * rb  # HBM: reads of HBM sources, compact + fills written
+    if kind == "attention":
+        return R * K * rb + R * H * (512 + 64) * 2
+    if kind == "attention_merge":
+        return R * ((K + 127) // 128) * H * 512 * 4 + R * H * 512 * 4
+    return 0.0
+
+
+def run_mode(w, mode, inputs, hist, args):
+    import kv_cache_offload_amd as K
+    name = "offload" if mode == K.KV_OFFLOAD else "resident"
+    r = Runner(w, mode, inputs, hist)
+    log(f"{name}: history loaded (L={r.L()}), warmup {args.warmup}")
+    r.steps(args.warmup)
+    c_before = r.totals()
+    L_before = r.L()
+    dt = timed(r, args.steps)
+    c_timed = r.totals() - c_before
+    log(f"{name}: {args.steps} steps in {dt * 1e3:.1f} ms ({args.steps / dt:.1f} steps/s)")
+    kt, kc, kL0 = kernel_pass(r, args.kernel_steps)
+    res = dict(seconds=dt, steps_per_s=args.steps / dt, L_start=L_before, counters=c_timed.tolist(),
+               kernels={k: dict(launches=c, avg_us=(m / c * 1e3) if c else 0.0,
+                                bytes_per_launch=algorithmic_bytes(w, k, args.kernel_steps, kL0, kc))
+                        for k, (c, m) in kt.items()},
+               kernel_steps=args.kernel_steps)
+    for k, v in res["kernels"].items():
+        v["GBps"] = v["bytes_per_launch"] / (v["avg_us"] * 1e-6) / 1e9 if v["avg_us"] > 0 else 0.0
+    r.sess.close()
+    return res
+
+
+def cpu_baseline(w, inputs, hist, budget_s):
+    """The oracle as it stands, on the host cores, on the first decode steps of the same workload."""
+    from oracle import MODE_OFFLOAD, OracleUnit, UnitShape
+    u = OracleUnit(UnitShape(max_positions=w.max_positions, index_heads=w.index_heads, index_dim=w.index_dim,
+                             heads=w.heads, top_k=w.top_k, hot_slots=w.hot_slots, max_query_rows=w.rows_per_step,
+                             mode=MODE_OFFLOAD, softmax_scale=w.softmax_scale))
+    u.append(*hist)
+    u.flush()
+    if w.warm:
+        u.warm()
+    keys, rows, iq, iw, ql, qr = inputs
+    t0 = time.perf_counter()
+    n = 0
+    while n < keys.shape[0] and (n < 2 or time.perf_counter() - t0 < budget_s):
+        u.append(keys[n], rows[n])
+        u.decode_step(iq[n, 0], iw[n, 0], ql[n, 0], qr[n, 0])
+        n += 1
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return dict(value=n / dt, unit="decode steps/s", cores=cores, kind="oracle",
+                sample=f"first {n} decode steps (append + decode) of {w.name} after loading the "
+                       f"{w.history}-row history and warming the cache; {dt:.1f} s of CPU work")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import dsa_synth as S
+    import kv_cache_offload_amd as K
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    base = S.WORKLOADS[args.workload]
+    n_steps = args.warmup + args.steps + args.kernel_steps
+    w = base.scaled(steps=max(base.steps, n_steps))
+    log(f"generating {n_steps} steps of inputs for {w.name}")
+    t0 = time.perf_counter()
+    inputs = gen_inputs(w, n_steps)
+    hist = S.history(w, 0, 0)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    off = run_mode(w, K.KV_OFFLOAD, inputs, hist, args)
+    resd = None if args.no_resident else run_mode(w, K.KV_HBM_RESIDENT, inputs, hist, args)
+
+    # dominant kernel of the offloaded step and its roofline
+    kern = off["kernels"]
+    total_ms = {k: v["avg_us"] * v["launches"] for k, v in kern.items()}
+    dom = max(total_ms, key=total_ms.get)
+    d = kern[dom]
+    roof = dict(kernel=dom, bound="hbm", achieved=d["GBps"], peak=HBM_PEAK_GBPS, unit="GB/s",
+                frac=d["GBps"] / HBM_PEAK_GBPS, traffic=None, avg_us=d["avg_us"],
+                bytes_per_launch=d["bytes_per_launch"])
+
+    R = w.rows_per_step
+    c = off["counters"]
+    host_bytes = c[6]
+    sel_keys = ("index_score", "topk_collect", "topk_resolve", "gather_scan", "gather_assign", "gather_copy")
+    ssg_us = sum(kern[k]["avg_us"] * kern[k]["launches"] / off["kernel_steps"] for k in sel_keys)
+    ssg_bytes = sum(kern[k]["bytes_per_launch"] * kern[k]["launches"] / off["kernel_steps"]
+                    for k in ("index_score", "gather_copy"))
+    line = {
+        "metric": METRIC,
+        "value": off["steps_per_s"],
+        "unit": "decode steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": 1e3 * off["seconds"] / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "history": w.history, "query_rows": R, "top_k": w.top_k,
+                   "hot_slots": w.hot_slots, "index_heads": w.index_heads, "heads": w.heads,
+                   "row_bytes": w.row_bytes, "mode": "offload", "L_at_timed_start": off["L_start"]},
+        "query_rows_per_s": off["steps_per_s"] * R,
+        "roofline": roof,
+        "score_select_gather": {"us_per_step": ssg_us, "hbm_bytes_per_step": ssg_bytes,
+                                "hbm_frac": ssg_bytes / (ssg_us * 1e-6) / 1e9 / HBM_PEAK_GBPS},
+        "host_link": {"miss_bytes_per_step": host_bytes / args.steps,
+                      "miss_rows_per_step": (c[3] + c[4]) / args.steps,
+                      "hit_rate": c[1] / max(1, c[0] - c[2]),
+                      "gather_copy_GBps": (kern["gather_copy"]["launches"] and
+                                           (host_bytes / args.steps) / (kern["gather_copy"]["avg_us"] * 1e-6) / 1e9),
+                      "peak_GBps": HOST_LINK_PEAK_GBPS},
+        "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
+        "kernels_GBps": {k: round(v["GBps"], 1) for k, v in kern.items()},
+        "counters_timed": dict(zip(K.COUNTER_NAMES, c)),
+    }
+    if resd is not None:
+        line["resident"] = {"value": resd["steps_per_s"], "ms_per_step": 1e3 * resd["seconds"] / args.steps,
+                            "kernels_us": {k: round(v["avg_us"], 2) for k, v in resd["kernels"].items()}}
+        line["offload_slowdown"] = resd["steps_per_s"] / off["steps_per_s"] - 1.0
+    if not args.no_cpu:
+        log("timing the oracle on the host")
+        line["cpu_baseline"] = cpu_baseline(w, inputs, hist, args.cpu_seconds)
+    if args.calib_copy:
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["calib_copy_bytes"] = n
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -112,7 +112,7 @@ typedef struct {
   int32_t device;          /* HIP device ordinal */
   int32_t n_layers;        /* >= 1 */
   int32_t n_seqs;          /* sequences per layer, 1..64 */
-  int64_t max_positions;   /* per unit: history plus every later append */
+  int64_t max_positions;   /* per unit: history plus every later append, <= 4,194,304 */
   int32_t index_heads;     /* H_I in {4, 8, 16, 32} */
   int32_t index_dim;       /* 128 */
   int32_t heads;           /* H, multiple of 16, <= 128 */
@@ -120,7 +120,7 @@ typedef struct {
   int32_t rope_dim;        /* 64 */
   int32_t group;           /* 64 */
   int32_t top_k;           /* K, 1..4096 */
-  int32_t hot_slots;       /* S >= 1 (offload mode) */
+  int32_t hot_slots;       /* S in [1, 2^20] (offload mode) */
   int32_t ring_rows;       /* writeback batch, 64 */
   int32_t max_query_rows;  /* R_max; R_max * K <= 16384 */
   float softmax_scale;     /* 1/sqrt(latent_dim + rope_dim) */
@@ -204,7 +204,8 @@ typedef enum {
   DSA_DBG_HAND = 13,       /* i32 [1] */
   DSA_DBG_SLOT_BYTES = 14, /* u8  [S][row_bytes] */
   DSA_DBG_MIRROR = 15,     /* u8  [M][row_bytes] host mirror (resident: row store [L]) */
-  DSA_DBG_KEYS = 16        /* bf16 [L][index_dim] */
+  DSA_DBG_KEYS = 16,       /* bf16 [L][index_dim] */
+  DSA_DBG_TOTALS = 17      /* i64 [8]  the counters above summed over every step of the unit */
 } dsa_debug_item;
 
 dsa_status dsa_debug_size(const dsa_session* s, int32_t layer, int32_t seq, int32_t item,
@@ -216,9 +217,11 @@ dsa_status dsa_debug_get(dsa_session* s, int32_t layer, int32_t seq, int32_t ite
  * When enabled, every kernel launch of dsa_decode_step is bracketed by HIP
  * events on the launch stream; dsa_kernel_times synchronises those events and
  * returns, per kernel kind, the launch count and total milliseconds since the
- * last reset.  Kinds: 0 index score, 1 top-k histogram passes, 2 top-k emit,
- * 3 gather plan, 4 gather copy, 5 attention, 6 attention merge. */
-#define DSA_KERNEL_KINDS 7
+ * last call, then resets.  Kinds: 0 index score (with the first top-k digit
+ * histogram), 1 top-k collect, 2 top-k resolve (selection, union marking and
+ * cache classification), 3 gather scan, 4 gather assign (slot table), 5 gather
+ * copy, 6 attention, 7 attention merge. */
+#define DSA_KERNEL_KINDS 8
 dsa_status dsa_set_kernel_timing(dsa_session* s, int32_t enable);
 dsa_status dsa_kernel_times(dsa_session* s, int64_t counts[DSA_KERNEL_KINDS],
                             double total_ms[DSA_KERNEL_KINDS]);

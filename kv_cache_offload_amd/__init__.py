@@ -22,13 +22,13 @@ OK, E_INVALID, E_NOMEM, E_CAPACITY, E_UNSUPPORTED, E_STATE, E_HIP = range(7)
 STATUS_NAMES = {0: "DSA_OK", 1: "DSA_E_INVALID", 2: "DSA_E_NOMEM", 3: "DSA_E_CAPACITY",
                 4: "DSA_E_UNSUPPORTED", 5: "DSA_E_STATE", 6: "DSA_E_HIP"}
 KV_OFFLOAD, KV_HBM_RESIDENT = 0, 1
-KERNEL_KINDS = ("index_score", "topk_hist", "topk_emit", "gather_plan", "gather_copy",
-                "attention", "attention_merge")
+KERNEL_KINDS = ("index_score", "topk_collect", "topk_resolve", "gather_scan", "gather_assign",
+                "gather_copy", "attention", "attention_merge")
 
 # inspection items (dsa_debug_item)
 DBG = dict(scores=0, selection=1, sel_count=2, union=3, union_kind=4, union_src=5, map=6,
            compact=7, counters=8, slot_pos=9, fill_round=10, pin_round=11, pos_slot=12, hand=13,
-           slot_bytes=14, mirror=15, keys=16)
+           slot_bytes=14, mirror=15, keys=16, totals=17)
 COUNTER_NAMES = ("union", "hit", "ring", "miss", "miss_noslot", "evict", "host_bytes", "res")
 
 # every symbol include/dsa.h declares

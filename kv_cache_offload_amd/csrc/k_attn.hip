@@ -36,6 +36,8 @@ constexpr int kLatStride = 520;        // bf16 per row in the row-major latent (
 constexpr int kDjStride = 40;          // bf16 per dim in the dim-major latent (32 + 8)
 constexpr int kRopeStride = 72;        // bf16 per row of RoPE (64 + 8)
 constexpr int kPStride = 33;           // f32 per head row of P (32 + 1)
+constexpr int kMaxSplitRows = 256;     // selected rows per workgroup at most
+constexpr int kMaxSplits = 4096 / 64;  // K <= 4096, at least 64 rows per split
 
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -54,20 +56,97 @@ struct AttnKArgs {
   const uint16_t* q_lat;     // [n_seqs][R][H][512]
   const uint16_t* q_rope;    // [n_seqs][R][H][64]
   float* out;                // [n_seqs][R][H][512]
-  int K, H, split_rows, nsplit, row_bytes;
+  int K, H, split_rows, nsplit, ns_stride, row_bytes;
+  int64_t max_positions;
   float scale_log2;          // softmax_scale * log2(e)
 };
 
+// Raw Q8G64 bytes of one 32-row block, held in registers so the next block's
+// loads are in flight while the current block is computed.  Latent task t covers
+// 8 rows (group t % 4) x 8 dims (chunk t / 4); side task covers one row's scale
+// of one group plus 16 bytes of its RoPE.
+template <int NW>
+struct RawBlock {
+  static constexpr int kLatTasks = (kSub / 8) * 64 / (NW * 64);   // per thread
+  static constexpr int kSideTasks = kSub * 8 / (NW * 64);
+  uint2 lat[kLatTasks][8];
+  uint16_t scl[kSideTasks];
+  uint4 rope[kSideTasks];
+
+  __device__ inline void load(const uint8_t* compact, const int* idx, int64_t rb, int tid) {
+#pragma unroll
+    for (int q = 0; q < kLatTasks; ++q) {
+      const int task = tid + q * NW * 64;
+      const int jg = task & 3, dc = task >> 2;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int id = idx[jg * 8 + e];
+        lat[q][e] = id >= 0 ? *reinterpret_cast<const uint2*>(compact + id * rb + dc * 8) : make_uint2(0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kSideTasks; ++q) {
+      const int task = tid + q * NW * 64;
+      const int j = task >> 3, g = task & 7;
+      const int id = idx[j];
+      scl[q] = id >= 0 ? *reinterpret_cast<const uint16_t*>(compact + id * rb + 512 + 2 * g) : (uint16_t)0;
+      rope[q] = id >= 0 ? *reinterpret_cast<const uint4*>(compact + id * rb + 528 + 16 * g) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  // int8 -> bf16 (exact) in both layouts; scales to fp32; RoPE copied.
+  __device__ inline void store(uint16_t* lat_jd, uint16_t* lat_dj, uint16_t* rope_jd, float* sclf, int tid) const {
+#pragma unroll
+    for (int q = 0; q < kLatTasks; ++q) {
+      const int task = tid + q * NW * 64;
+      const int jg = task & 3, dc = task >> 2;        // row group fastest: conflict-free dim-major writes
+      uint16_t w[8][8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t word = k < 4 ? lat[q][e].x : lat[q][e].y;
+          const int8_t v = (int8_t)((word >> (8 * (k & 3))) & 0xFFu);
+          w[e][k] = (uint16_t)(__float_as_uint((float)v) >> 16);
+        }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16x8 row;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) row[k] = (short)w[e][k];
+        *reinterpret_cast<bf16x8*>(lat_jd + (jg * 8 + e) * kLatStride + dc * 8) = row;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        bf16x8 col;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) col[e] = (short)w[e][k];
+        *reinterpret_cast<bf16x8*>(lat_dj + (dc * 8 + k) * kDjStride + jg * 8) = col;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kSideTasks; ++q) {
+      const int task = tid + q * NW * 64;
+      const int j = task >> 3, g = task & 7;
+      sclf[j * 8 + g] = f16_bits_to_f32(scl[q]);
+      *reinterpret_cast<uint4*>(rope_jd + j * kRopeStride + 8 * g) = rope[q];
+    }
+  }
+};
+
+// One workgroup: one query row, NW*16 heads, one split of the row's selection.
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   __shared__ __align__(16) uint16_t lat_jd[kSub * kLatStride];   // also the P staging area
   __shared__ __align__(16) uint16_t lat_dj[512 * kDjStride];
   __shared__ __align__(16) uint16_t rope_jd[kSub * kRopeStride];
   __shared__ float scl[kSub * 8];
-  __shared__ int s_idx[kSub];
+  __shared__ int s_idx[kMaxSplitRows];
 
   const StepArgs& a = ka.a;
-  const int split = blockIdx.x, r = blockIdx.y, seq = blockIdx.z;
+  const int split = blockIdx.x, seq = blockIdx.z;
+  const int n_hg = ka.H / (NW * 16);
+  const int r = blockIdx.y / n_hg, hg = blockIdx.y % n_hg;
   const SeqScratch s = a.scr[seq];
   const int n_sel = s.sel_n[r];
   const int j_begin = split * ka.split_rows;
@@ -76,8 +155,30 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int H = ka.H;
-  const int h0 = wave * 16;
+  const int h0 = hg * NW * 16 + wave * 16;
   const int64_t rb = ka.row_bytes;
+
+  // Compact-row index of every selected row of this split (the map: union index of
+  // the selected position, from the per-position index the gather wrote).
+  const int* sel = s.sel + (int64_t)r * ka.K;
+  int* map = s.map + (int64_t)r * ka.K;
+  const int64_t U = s.info[kInfoUnion];
+  for (int j = tid; j < ka.split_rows; j += NW * 64) {
+    int idx = -1;
+    if (j_begin + j < j_end) {
+      const int32_t p = sel[j_begin + j];
+      idx = (p >= 0 && p < ka.max_positions) ? s.upos[p] : -1;
+      if (idx >= U) idx = -1;                        // never index past the compact rows
+      if (hg == 0) map[j_begin + j] = idx;
+    }
+    s_idx[j] = idx;
+  }
+  if (split == 0 && hg == 0)
+    for (int j = n_sel + tid; j < ka.K; j += NW * 64) map[j] = -1;
+  __syncthreads();
+
+  RawBlock<NW> raw;
+  raw.load(s.compact, s_idx, rb, tid);
 
   // Query fragments: lane holds Q[h0 + l16][32*ks + 8*g4 .. +7].
   bf16x8 qa[18];
@@ -98,61 +199,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
 #pragma unroll
   for (int v = 0; v < 4; ++v) { m_run[v] = -INFINITY; l_run[v] = 0.f; }
 
-  const int* map = s.map + (int64_t)r * ka.K;
-
   for (int jb = j_begin; jb < j_end; jb += kSub) {
     const int nrows = min(kSub, j_end - jb);
     __syncthreads();                                   // previous block's PV is done with LDS
-    if (tid < kSub) s_idx[tid] = tid < nrows ? map[jb + tid] : -1;
+    raw.store(lat_jd, lat_dj, rope_jd, scl, tid);
+    if (jb + kSub < j_end) raw.load(s.compact, s_idx + (jb + kSub - j_begin), rb, tid);
     __syncthreads();
-
-    // Latent: task = (group of 8 rows, 8 dims) -> 64 bf16 in both layouts.
-    for (int task = tid; task < (kSub / 8) * 64; task += NW * 64) {
-      const int jg = task >> 6, dc = task & 63;
-      uint2 raw[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int idx = s_idx[jg * 8 + e];
-        raw[e] = idx >= 0 ? *reinterpret_cast<const uint2*>(s.compact + idx * rb + dc * 8) : make_uint2(0u, 0u);
-      }
-      uint16_t w[8][8];                                // [row e][dim k]
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const uint32_t word = k < 4 ? raw[e].x : raw[e].y;
-          const int8_t q = (int8_t)((word >> (8 * (k & 3))) & 0xFFu);
-          w[e][k] = (uint16_t)(__float_as_uint((float)q) >> 16);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16x8 row;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) row[k] = (short)w[e][k];
-        *reinterpret_cast<bf16x8*>(lat_jd + (jg * 8 + e) * kLatStride + dc * 8) = row;
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        bf16x8 col;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) col[e] = (short)w[e][k];
-        *reinterpret_cast<bf16x8*>(lat_dj + (dc * 8 + k) * kDjStride + jg * 8) = col;
-      }
-    }
-    // Scales (fp16 -> fp32) and RoPE (bf16 copy).
-    for (int task = tid; task < kSub * 8; task += NW * 64) {
-      const int j = task >> 3, g = task & 7;
-      const int idx = s_idx[j];
-      float sc = 0.f;
-      if (idx >= 0) sc = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(s.compact + idx * rb + 512 + 2 * g));
-      scl[j * 8 + g] = sc;
-      uint4 rv = make_uint4(0u, 0u, 0u, 0u);
-      if (idx >= 0) rv = *reinterpret_cast<const uint4*>(s.compact + idx * rb + 528 + 16 * g);
-      *reinterpret_cast<uint4*>(rope_jd + j * kRopeStride + 8 * g) = rv;
-    }
-    __syncthreads();
-
     // QK^T: logits for heads h0+4*g4+v, rows nt*16 + l16.
     f32x4 lg[2];
 #pragma unroll
@@ -253,7 +305,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int h = h0 + 4 * g4 + v;
-      const int64_t base = ((int64_t)r * ka.nsplit + split) * H + h;
+      const int64_t base = ((int64_t)r * ka.ns_stride + split) * H + h;
       float* dst = s.part_o + base * 512;
 #pragma unroll
       for (int nt2 = 0; nt2 < 32; ++nt2) dst[nt2 * 16 + l16] = o[nt2][v];
@@ -268,53 +320,75 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
 struct MergeKArgs {
   StepArgs a;
   float* out;
-  int H, nsplit, split_rows;
+  int H, split_rows, ns_stride;
 };
 
-// out[h][d] = sum_s 2^(m_s - M) O_s[h][d] / sum_s 2^(m_s - M) l_s[h]
-__global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
+// One workgroup per (head, query row): out[d] = sum_s w_s O_s[d] with
+// w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s'.
+__global__ __launch_bounds__(128) void attn_merge_kernel(MergeKArgs ka) {
+  __shared__ float wgt[kMaxSplits];
   const StepArgs& a = ka.a;
-  const int r = blockIdx.y, seq = blockIdx.z;
+  const int h = blockIdx.x, r = blockIdx.y, seq = blockIdx.z;
   const SeqScratch s = a.scr[seq];
   const int used = (s.sel_n[r] + ka.split_rows - 1) / ka.split_rows;
   const int H = ka.H;
-  for (int hd = blockIdx.x * blockDim.x + threadIdx.x; hd < H * 512; hd += gridDim.x * blockDim.x) {
-    const int h = hd >> 9, d = hd & 511;
-    float mx = -INFINITY;
-    for (int sp = 0; sp < used; ++sp) mx = fmaxf(mx, s.part_ml[(((int64_t)r * ka.nsplit + sp) * H + h) * 2]);
-    float num = 0.f, den = 0.f;
-    for (int sp = 0; sp < used; ++sp) {
-      const int64_t base = ((int64_t)r * ka.nsplit + sp) * H + h;
-      const float wgt = exp2f(s.part_ml[base * 2] - mx);
-      den += wgt * s.part_ml[base * 2 + 1];
-      num += wgt * s.part_o[base * 512 + d];
+  // splits' (max, sum) in the first wave, one split per lane (used <= 64)
+  if (threadIdx.x < 64) {
+    const int sp = threadIdx.x;
+    float m = -INFINITY, l = 0.f;
+    if (sp < used) {
+      const int64_t base = ((int64_t)r * ka.ns_stride + sp) * H + h;
+      m = s.part_ml[base * 2];
+      l = s.part_ml[base * 2 + 1];
     }
-    ka.out[(((int64_t)seq * a.R + r) * H + h) * 512 + d] = num / den;
+    float mx = m;
+    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float w = sp < used ? exp2f(m - mx) : 0.f;
+    float den = w * l;
+    for (int o = 1; o < 64; o <<= 1) den += __shfl_xor(den, o);
+    if (sp < used) wgt[sp] = w / den;
   }
+  __syncthreads();
+  const int d = threadIdx.x * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int sp = 0; sp < used; ++sp) {
+    const float4 v = *reinterpret_cast<const float4*>(
+        s.part_o + (((int64_t)r * ka.ns_stride + sp) * H + h) * 512 + d);
+    const float w = wgt[sp];
+    acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+  }
+  *reinterpret_cast<float4*>(ka.out + (((int64_t)seq * a.R + r) * H + h) * 512 + d) = acc;
+}
+
+// Rows per workgroup: 128, or 64 when that leaves fewer than 256 workgroups.
+int attn_split_rows(const Geometry& g, const StepArgs& a) {
+  const int nw = g.heads >= 32 ? 2 : 1;
+  const int64_t groups = (int64_t)a.R * a.n_seqs * (g.heads / (16 * nw));
+  const int64_t wg128 = groups * ((g.top_k + 127) / 128);
+  return wg128 >= 256 ? 128 : 64;
 }
 
 }  // namespace
 
 hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_lat, const uint16_t* q_rope,
                        float* out, hipStream_t st) {
-  AttnKArgs ka{a, q_lat, q_rope, out, g.top_k, g.heads, g.attn_split_rows, g.nsplit, g.row_bytes,
-               g.softmax_scale * 1.4426950408889634f};
-  dim3 grid((unsigned)g.nsplit, (unsigned)a.R, (unsigned)a.n_seqs);
-  switch (g.heads / 16) {
-    case 1: hipLaunchKernelGGL(attn_kernel<1>, grid, dim3(64), 0, st, ka); break;
-    case 2: hipLaunchKernelGGL(attn_kernel<2>, grid, dim3(128), 0, st, ka); break;
-    case 4: hipLaunchKernelGGL(attn_kernel<4>, grid, dim3(256), 0, st, ka); break;
-    case 8: hipLaunchKernelGGL(attn_kernel<8>, grid, dim3(512), 0, st, ka); break;
-    default: return hipErrorInvalidValue;
-  }
+  const int split_rows = attn_split_rows(g, a);
+  const int nsplit = (g.top_k + split_rows - 1) / split_rows;
+  const int nw = g.heads >= 32 ? 2 : 1;
+  AttnKArgs ka{a, q_lat, q_rope, out, g.top_k, g.heads, split_rows, nsplit, g.nsplit_max, g.row_bytes,
+               g.max_positions, g.softmax_scale * 1.4426950408889634f};
+  dim3 grid((unsigned)nsplit, (unsigned)(a.R * (g.heads / (16 * nw))), (unsigned)a.n_seqs);
+  if (nw == 1) hipLaunchKernelGGL(attn_kernel<1>, grid, dim3(64), 0, st, ka);
+  else hipLaunchKernelGGL(attn_kernel<2>, grid, dim3(128), 0, st, ka);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_merge(const Geometry& g, const StepArgs& a, float* out, hipStream_t st) {
-  if (g.nsplit == 1) return hipSuccess;
-  MergeKArgs ka{a, out, g.heads, g.nsplit, g.attn_split_rows};
-  const int blocks = (g.heads * 512 + 255) / 256;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)blocks, (unsigned)a.R, (unsigned)a.n_seqs), dim3(256), 0,
+  const int split_rows = attn_split_rows(g, a);
+  if ((g.top_k + split_rows - 1) / split_rows == 1) return hipSuccess;
+  MergeKArgs ka{a, out, g.heads, split_rows, g.nsplit_max};
+  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)g.heads, (unsigned)a.R, (unsigned)a.n_seqs), dim3(128), 0,
                      st, ka);
   return hipGetLastError();
 }

@@ -15,27 +15,31 @@
 //   * section "Capacity must survive the session lifecycle": flush before the
 //     full history is exported.
 //
-// gfx950 design.  The plan is one 1024-thread workgroup per sequence working
-// in LDS: the R sorted selections are merged pairwise with merge-path
-// partitioning, duplicates are dropped with a block scan (a position several
-// rows select is read once, which is how "repeated misses read host memory"
-// holds structurally), each union entry is classified on the round-start
-// state, hits are pinned, and the k-th miss in ascending position order takes
-// the k-th unpinned slot after the hand, found from a bitmap of pinned slots
-// over the window the walk can reach and a prefix count of unpinned slots per
-// 32-slot word.  The copy is a separate wide kernel: one thread per 16-byte
-// piece of a row, loading from the hot slot, the ring, or the host mirror
-// (zero-copy reads of pinned host memory over the host link), storing to the
-// compact buffer and, for a miss that got a slot, to the slot as well.  No
-// workgroup ever reads a slot filled in the same round.
+// gfx950 design.  Selection, classification and pinning happen where the
+// selection is produced: the top-k emit kernel sets, for every selected
+// position, a bit in a per-position selection bitmap (so a position several
+// rows select is one union entry -- "repeated misses read host memory" holds
+// structurally: one host read per distinct position), classifies it against
+// the round-start state (a hit needs a slot filled in an earlier round) and
+// pins the hit's slot.  The gather scan is one workgroup per sequence: it turns
+// the bitmaps into per-32-position-word prefix counts of union entries and of
+// misses, and the pinned-slot bitmap into a per-word prefix of unpinned slots in
+// ring order from the hand, and lists the victim slot of the k-th miss.  The
+// gather assign kernel is wide: one wave per 32-position word, one lane per
+// position; the k-th miss in ascending position order takes victim[k], evicts
+// its old position and fills the slot table.  The copy is a separate
+// wide kernel: one thread per 16-byte piece of a row, loading from the hot
+// slot, the ring, or the host mirror (zero-copy reads of pinned host memory
+// over the host link), storing to the compact buffer and, for a miss that got
+// a slot, to the slot as well.  No thread ever reads a slot filled in the same
+// round.
 #include "dsa_internal.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kPlanThreads = 1024;
-constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int kMaxPer = kMaxUnion / kPlanThreads;   // 16 elements per thread at most
+constexpr int kScanThreads = 1024;
+constexpr int kScanWaves = kScanThreads / 64;
 
 __device__ inline uint32_t wave_incl_scan(uint32_t v, int lane) {
 #pragma unroll
@@ -54,7 +58,7 @@ __device__ inline uint32_t block_scan(uint32_t v, uint32_t* tot, uint32_t* sh /*
   __syncthreads();
   uint32_t base = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kPlanWaves; ++w) {
+  for (int w = 0; w < kScanWaves; ++w) {
     uint32_t x = sh[w];
     base += (w < wave) ? x : 0u;
     all += x;
@@ -64,269 +68,244 @@ __device__ inline uint32_t block_scan(uint32_t v, uint32_t* tot, uint32_t* sh /*
   return base + inc - v;
 }
 
-// Stable merge of sorted A[na] and B[nb] into dst by all threads (merge path).
-__device__ inline void merge_pair(const uint32_t* A, int na, const uint32_t* B, int nb, uint32_t* dst) {
-  const int total = na + nb;
-  const int per = (total + kPlanThreads - 1) / kPlanThreads;
-  const int d0 = threadIdx.x * per;
-  if (d0 >= total) return;
-  const int d1 = min(total, d0 + per);
-  int lo = max(0, d0 - nb), hi = min(d0, na);
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (A[mid] <= B[d0 - 1 - mid]) lo = mid + 1;
-    else hi = mid;
-  }
-  int i = lo, j = d0 - lo;
-  for (int d = d0; d < d1; ++d) {
-    if (j >= nb || (i < na && A[i] <= B[j])) dst[d] = A[i++];
-    else dst[d] = B[j++];
-  }
+// Bits of word w (positions 32w..32w+31) that lie at or above M.
+__device__ inline uint32_t ring_bits(int64_t w, int64_t M) {
+  const int64_t first = w * 32;
+  if (first >= M) return 0xFFFFFFFFu;
+  if (first + 32 <= M) return 0u;
+  return ~((1u << (uint32_t)(M - first)) - 1u);
 }
 
-__device__ inline int nth_set_bit(uint32_t x, int n) {
-  for (int i = 0; i < n; ++i) x &= x - 1;
-  return __ffs(x) - 1;
-}
-
-struct PlanKArgs {
+struct ScanKArgs {
   StepArgs a;
-  int K, S, ring_cap, ring_rows, mode;
+  int S, s_words, ring_rows, mode;
 };
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanKArgs ka) {
-  extern __shared__ __align__(16) uint32_t lds[];   // two buffers of R*K entries
-  __shared__ uint32_t sh_scan[kPlanWaves];
-  __shared__ int s_off[9], s_n[9];
-  __shared__ uint32_t bm[kMaxUnion / 32];            // pinned bitmap, then unpinned words
-  __shared__ uint32_t wpre[kMaxUnion / 32];          // exclusive prefix of unpinned counts
-  __shared__ int s_new_hand;
-
+__global__ __launch_bounds__(kScanThreads) void gather_scan_kernel(ScanKArgs ka) {
+  __shared__ uint32_t sh[kScanWaves];
+  __shared__ int s_hand;
   const StepArgs& a = ka.a;
-  const int seq = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int seq = blockIdx.x, tid = threadIdx.x;
   const UnitDev u = a.units[a.unit_base + seq];
   const SeqScratch s = a.scr[seq];
-  const int R = a.R, K = ka.K, S = ka.S;
   const int64_t L = u.dyn[0], M = u.dyn[1];
   const int32_t round = (int32_t)u.dyn[2];
-  const int hand = ka.mode == 0 ? *u.hand : 0;
-  uint32_t* X = lds;
-  uint32_t* Y = lds + R * K;
+  const bool off = ka.mode == 0;
+  const int hand = off ? *u.hand : 0;
+  const int64_t nw = (L + 31) / 32;
+  const uint32_t* sel = s.selmask;
+  const uint32_t* hit = s.hitmask;
 
-  // 1. the R selections, concatenated
-  if (tid < R) s_n[tid] = s.sel_n[tid];
-  __syncthreads();
-  if (tid == 0) {
-    int o = 0;
-    for (int i = 0; i < R; ++i) { s_off[i] = o; o += s_n[i]; }
-    s_off[R] = o;
+  // Union and miss counts per word, scanned in word (= position) order.
+  const int64_t per = (nw + kScanThreads - 1) / kScanThreads;
+  const int64_t w0 = min(nw, (int64_t)tid * per), w1 = min(nw, w0 + per);
+  uint32_t cu = 0, cm = 0, cr = 0, ch = 0;
+  for (int64_t w = w0; w < w1; ++w) {
+    const uint32_t sw = sel[w];
+    if (!sw) continue;
+    const uint32_t hw = off ? hit[w] : 0u;
+    const uint32_t rw = off ? (sw & ring_bits(w, M)) : 0u;
+    cu += __popc(sw);
+    cr += __popc(rw);
+    ch += __popc(hw);
+    if (off) cm += __popc(sw & ~hw & ~rw);
   }
-  __syncthreads();
-  const int total = s_off[R];
-  for (int i = 0; i < R; ++i)
-    for (int j = tid; j < s_n[i]; j += kPlanThreads) X[s_off[i] + j] = (uint32_t)s.sel[i * K + j];
-  __syncthreads();
-
-  // 2. pairwise merge rounds
-  uint32_t* cur = X;
-  uint32_t* nxt = Y;
-  int nl = R;
-  while (nl > 1) {
-    for (int p = 0; p + 1 < nl; p += 2) {
-      merge_pair(cur + s_off[p], s_n[p], cur + s_off[p + 1], s_n[p + 1], nxt + s_off[p]);
-      __syncthreads();
-    }
-    if (nl & 1)
-      for (int j = tid; j < s_n[nl - 1]; j += kPlanThreads) nxt[s_off[nl - 1] + j] = cur[s_off[nl - 1] + j];
-    __syncthreads();
-    if (tid == 0) {
-      int q = 0;
-      for (int p = 0; p < nl; p += 2) {
-        s_off[q] = s_off[p];
-        s_n[q] = s_n[p] + (p + 1 < nl ? s_n[p + 1] : 0);
-        ++q;
-      }
-    }
-    __syncthreads();
-    uint32_t* t = cur; cur = nxt; nxt = t;
-    nl = (nl + 1) >> 1;
+  uint32_t U, n_miss, n_ring, n_hit;
+  uint32_t bu = block_scan(cu, &U, sh);
+  uint32_t bm = block_scan(cm, &n_miss, sh);
+  block_scan(cr, &n_ring, sh);
+  block_scan(ch, &n_hit, sh);
+  for (int64_t w = w0; w < w1; ++w) {
+    const uint32_t sw = sel[w];
+    s.base_u[w] = bu;
+    s.base_m[w] = bm;
+    if (!sw) continue;
+    const uint32_t hw = off ? hit[w] : 0u;
+    const uint32_t rw = off ? (sw & ring_bits(w, M)) : 0u;
+    bu += __popc(sw);
+    if (off) bm += __popc(sw & ~hw & ~rw);
   }
 
-  // 3. drop duplicates: union U in ascending order, into nxt
-  uint32_t U;
-  {
-    const int per = (total + kPlanThreads - 1) / kPlanThreads;
-    const int x0 = min(total, tid * per), x1 = min(total, x0 + per);
+  // Unpinned slots in ring order from the hand.
+  uint32_t n_unpinned = 0, n_evict = 0;
+  if (off) {
+    const int S = ka.S, nsw = ka.s_words;
+    const int sper = (nsw + kScanThreads - 1) / kScanThreads;
+    const int j0 = min(nsw, tid * sper), j1 = min(nsw, j0 + sper);
     uint32_t cnt = 0;
-    for (int x = x0; x < x1; ++x) cnt += (x == 0 || cur[x] != cur[x - 1]);
-    uint32_t base = block_scan(cnt, &U, sh_scan);
-    for (int x = x0; x < x1; ++x)
-      if (x == 0 || cur[x] != cur[x - 1]) nxt[base++] = cur[x];
+    for (int j = j0; j < j1; ++j) {
+      uint32_t bits = 0;
+      if ((S & 31) == 0) {
+        // 32 offsets from a word-aligned ring: two pinned words, funnel-shifted
+        const int v0 = (hand + 32 * j) % S;
+        const int w0 = v0 >> 5, sh0 = v0 & 31;
+        const uint32_t lo = s.pinmask[w0];
+        const uint32_t hi = sh0 ? s.pinmask[(w0 + 1) % nsw] : 0u;
+        bits = ~(sh0 ? ((lo >> sh0) | (hi << (32 - sh0))) : lo);
+      } else {
+        int last = -1;
+        uint32_t pw_ = 0;
+        for (int i = 0; i < 32; ++i) {
+          const int o = 32 * j + i;
+          if (o >= S) break;
+          const int v = (hand + o) % S;
+          if ((v >> 5) != last) { last = v >> 5; pw_ = s.pinmask[last]; }
+          if (!((pw_ >> (v & 31)) & 1u)) bits |= 1u << i;
+        }
+      }
+      s.upw[j] = bits;
+      cnt += __popc(bits);
+    }
+    uint32_t base = block_scan(cnt, &n_unpinned, sh);
+    const uint32_t n_assigned = min(n_miss, n_unpinned);
+    // victim[k] = the k-th unpinned slot after the hand, for the misses that get one,
+    // with the position it holds now (to be evicted)
+    for (int j = j0; j < j1; ++j) {
+      uint32_t bits = s.upw[j];
+      while (bits && base < n_assigned) {
+        const int b = __ffs(bits) - 1;
+        bits &= bits - 1;
+        s.victim[base++] = (int32_t)((hand + 32 * j + b) % S);
+      }
+    }
+    __syncthreads();                                   // victims written; pinmask no longer read
+    uint32_t my_evict = 0;
+    for (uint32_t k0 = tid; k0 < n_assigned; k0 += 4 * kScanThreads) {
+      int32_t v[4], old[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t k = k0 + e * kScanThreads;
+        v[e] = k < n_assigned ? s.victim[k] : -1;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) old[e] = v[e] >= 0 ? u.slot_pos[v[e]] : -1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t k = k0 + e * kScanThreads;
+        if (k < n_assigned) {
+          s.victim_old[k] = old[e];
+          my_evict += old[e] >= 0;
+        }
+      }
+    }
+    block_scan(my_evict, &n_evict, sh);
+    for (int j = tid; j < nsw; j += kScanThreads) s.pinmask[j] = 0;
+    if (tid == 0) {
+      s_hand = hand;
+      if (n_assigned > 0) s_hand = (s.victim[n_assigned - 1] + 1) % S;
+    }
   }
   __syncthreads();
-  const uint32_t* uni = nxt;
-  for (uint32_t x = tid; x < U; x += kPlanThreads) s.uni[x] = (int32_t)uni[x];
-
-  // 4. map every selected position to its union index
-  for (int i = 0; i < R; ++i) {
-    for (int j = tid; j < K; j += kPlanThreads) {
-      int32_t m = -1;
-      if (j < s.sel_n[i]) {
-        const uint32_t pos = (uint32_t)s.sel[i * K + j];
-        uint32_t lo = 0, hi = U;
-        while (lo < hi) {
-          const uint32_t mid = (lo + hi) >> 1;
-          if (uni[mid] < pos) lo = mid + 1;
-          else hi = mid;
-        }
-        m = (int32_t)lo;
-      }
-      s.map[i * K + j] = m;
-    }
-  }
-
-  // 5. classify on the round-start state; pin hits
-  const int per = ((int)U + kPlanThreads - 1) / kPlanThreads;   // <= kMaxPer
-  const int x0 = min((int)U, tid * per), x1 = min((int)U, x0 + per);
-  int32_t kind[kMaxPer], src[kMaxPer];
-  uint32_t my_hit = 0, my_ring = 0, my_miss = 0;
-  if (ka.mode == 1) {
-#pragma unroll
-    for (int e = 0; e < kMaxPer; ++e) {
-      const int x = x0 + e;
-      kind[e] = SRC_RES;
-      src[e] = x < x1 ? (int32_t)uni[x] : -1;
-    }
-  } else {
-    int32_t v[kMaxPer];
-#pragma unroll
-    for (int e = 0; e < kMaxPer; ++e) {
-      const int x = x0 + e;
-      v[e] = -1;
-      if (x < x1) {
-        const int64_t pos = uni[x];
-        if (pos < M) v[e] = u.pos_slot[pos];
-      }
-    }
-    int32_t fr[kMaxPer];
-#pragma unroll
-    for (int e = 0; e < kMaxPer; ++e) fr[e] = (x0 + e < x1 && v[e] >= 0) ? u.fill_round[v[e]] : 0;
-#pragma unroll
-    for (int e = 0; e < kMaxPer; ++e) {
-      const int x = x0 + e;
-      kind[e] = SRC_RES;
-      src[e] = -1;
-      if (x >= x1) continue;
-      const int64_t pos = uni[x];
-      if (pos >= M) {
-        kind[e] = SRC_RING; src[e] = (int32_t)(pos % ka.ring_cap); ++my_ring;
-      } else if (v[e] >= 0 && fr[e] < round) {
-        kind[e] = SRC_HIT; src[e] = v[e]; ++my_hit;
-        u.pin_round[v[e]] = round;
-      } else {
-        kind[e] = SRC_MISS; src[e] = (int32_t)pos; ++my_miss;
-      }
-    }
-  }
-  uint32_t n_hit, n_ring, n_miss;
-  const uint32_t miss_base = block_scan(my_miss, &n_miss, sh_scan);
-  block_scan(my_hit, &n_hit, sh_scan);
-  block_scan(my_ring, &n_ring, sh_scan);
-
-  // 6. replacement window: the walk from the hand reaches at most n_miss + n_hit slots
-  uint32_t n_assigned = 0, evicted = 0;
-  if (ka.mode == 0) {
-    const uint32_t W = min((uint32_t)S, n_miss + n_hit);
-    const uint32_t nw = (W + 31) / 32;
-    for (uint32_t w = tid; w < nw; w += kPlanThreads) bm[w] = 0;
-    if (tid == 0) s_new_hand = hand;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < kMaxPer; ++e)
-      if (x0 + e < x1 && kind[e] == SRC_HIT) {
-        const uint32_t off = (uint32_t)((src[e] - hand + S) % S);
-        if (off < W) atomicOr(&bm[off >> 5], 1u << (off & 31));
-      }
-    __syncthreads();
-    uint32_t uw = 0;
-    if ((uint32_t)tid < nw) {
-      const uint32_t valid = ((uint32_t)tid + 1) * 32 <= W ? 0xFFFFFFFFu : ((1u << (W & 31)) - 1u);
-      uw = ~bm[tid] & valid;
-    }
-    uint32_t n_unpinned;
-    const uint32_t wbase = block_scan(__popc(uw), &n_unpinned, sh_scan);
-    if ((uint32_t)tid < nw) { bm[tid] = uw; wpre[tid] = wbase; }
-    __syncthreads();
-    n_assigned = min(n_miss, n_unpinned);
-
-    // 7. misses in ascending position order take the unpinned slots in ring order
-    uint32_t k = miss_base;
-#pragma unroll
-    for (int e = 0; e < kMaxPer; ++e) {
-      if (x0 + e >= x1 || kind[e] != SRC_MISS) continue;
-      if (k < n_assigned) {
-        uint32_t lo = 0, hi = nw;            // last word with wpre <= k
-        while (hi - lo > 1) {
-          const uint32_t mid = (lo + hi) >> 1;
-          if (wpre[mid] <= k) lo = mid;
-          else hi = mid;
-        }
-        const uint32_t off = lo * 32 + nth_set_bit(bm[lo], (int)(k - wpre[lo]));
-        const int32_t vslot = (int32_t)((hand + off) % (uint32_t)S);
-        const int32_t pos = src[e];
-        const int32_t old = u.slot_pos[vslot];
-        if (old >= 0) { u.pos_slot[old] = -1; ++evicted; }
-        u.slot_pos[vslot] = pos;
-        u.pos_slot[pos] = vslot;
-        u.fill_round[vslot] = round;
-        u.pin_round[vslot] = round;
-        s.fill[x0 + e] = vslot;
-        if (k + 1 == n_assigned) s_new_hand = (vslot + 1) % S;
-      } else {
-        kind[e] = SRC_MISS_NOSLOT;
-        s.fill[x0 + e] = -1;
-      }
-      ++k;
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < kMaxPer; ++e) {
-    if (x0 + e >= x1) continue;
-    s.kind[x0 + e] = kind[e];
-    s.src[x0 + e] = src[e];
-    if (kind[e] != SRC_MISS) s.fill[x0 + e] = -1;
-  }
-  uint32_t n_evict;
-  block_scan(evicted, &n_evict, sh_scan);
-
-  // 8. counters, writeback decision, state for the next round
   if (tid == 0) {
     const int64_t rb = 656;
-    const int64_t noslot = (int64_t)n_miss - n_assigned;
+    const uint32_t n_assigned = off ? min(n_miss, n_unpinned) : 0u;
+    const int64_t noslot = off ? (int64_t)n_miss - n_assigned : 0;
     s.counters[0] = U;
-    s.counters[1] = ka.mode == 0 ? n_hit : 0;
-    s.counters[2] = ka.mode == 0 ? n_ring : 0;
-    s.counters[3] = ka.mode == 0 ? n_assigned : 0;
-    s.counters[4] = ka.mode == 0 ? noslot : 0;
+    s.counters[1] = off ? n_hit : 0;
+    s.counters[2] = off ? n_ring : 0;
+    s.counters[3] = n_assigned;
+    s.counters[4] = noslot;
     s.counters[5] = n_evict;
-    s.counters[6] = ka.mode == 0 ? ((int64_t)n_assigned + noslot) * rb : 0;
-    s.counters[7] = ka.mode == 1 ? U : 0;
-    s.info[0] = U;
+    s.counters[6] = off ? ((int64_t)n_assigned + noslot) * rb : 0;
+    s.counters[7] = off ? 0 : U;
+    for (int c = 0; c < 8; ++c) u.totals[c] += s.counters[c];
     int64_t wb = -1;
-    if (ka.mode == 0 && L - M >= ka.ring_rows) wb = M;
-    s.info[1] = wb;
-    if (ka.mode == 0) {
-      *u.hand = s_new_hand;
+    if (off && L - M >= ka.ring_rows) wb = M;
+    s.info[kInfoUnion] = U;
+    s.info[kInfoWriteback] = wb;
+    s.info[kInfoAssigned] = n_assigned;
+    s.info[kInfoRound] = round;
+    s.info[kInfoM] = M;
+    s.info[kInfoHand] = hand;
+    if (off) {
+      *u.hand = s_hand;
       if (wb >= 0) u.dyn[1] = M + ka.ring_rows;
     }
     u.dyn[2] = round + 1;
   }
 }
 
+struct AssignKArgs {
+  StepArgs a;
+  int S, s_words, ring_cap, mode;
+  int64_t max_positions;
+};
+
+// One wave per 32-position word, one lane per position.
+__global__ __launch_bounds__(256) void gather_assign_kernel(AssignKArgs ka) {
+  const StepArgs& a = ka.a;
+  const int seq = blockIdx.y;
+  const UnitDev u = a.units[a.unit_base + seq];
+  const SeqScratch s = a.scr[seq];
+  const int64_t L = u.dyn[0];
+  const int64_t M = s.info[kInfoM];
+  const int32_t round = (int32_t)s.info[kInfoRound];
+  const uint32_t n_assigned = (uint32_t)s.info[kInfoAssigned];
+  const bool off = ka.mode == 0;
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (L + 31) / 32;
+  const int64_t wave_id = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t n_waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  uint32_t* sel = s.selmask;
+  uint32_t* hit = s.hitmask;
+  for (int64_t w = wave_id; w < nw; w += n_waves) {
+    const uint32_t sw = sel[w];
+    if (!sw) continue;
+    const uint32_t hw0 = off ? hit[w] : 0u;
+    // every lane has read the word; clear it for the next step
+    if (lane == 32) {
+      sel[w] = 0;
+      if (hw0) hit[w] = 0;
+    }
+    if (lane >= 32) continue;
+    const uint32_t bit = 1u << lane;
+    if (!(sw & bit)) continue;
+    const uint32_t below = bit - 1u;
+    const int64_t p = w * 32 + lane;
+    const uint32_t ux = s.base_u[w] + __popc(sw & below);
+    int32_t kind, src, fill = -1;
+    if (!off) {
+      kind = SRC_RES;
+      src = (int32_t)p;
+    } else {
+      const uint32_t hw = hw0;
+      const uint32_t rw = sw & ring_bits(w, M);
+      if (rw & bit) {
+        kind = SRC_RING;
+        src = (int32_t)(p % ka.ring_cap);
+      } else if (hw & bit) {
+        kind = SRC_HIT;
+        src = u.pos_slot[p];
+      } else {
+        const uint32_t k = s.base_m[w] + __popc(sw & ~hw & ~rw & below);
+        src = (int32_t)p;
+        if (k < n_assigned) {
+          kind = SRC_MISS;
+          const int32_t v = s.victim[k];
+          const int32_t old = s.victim_old[k];
+          if (old >= 0 && old < ka.max_positions) u.pos_slot[old] = -1;
+          u.slot_pos[v] = (int32_t)p;
+          u.pos_slot[p] = v;
+          u.fill_round[v] = round;
+          u.pin_round[v] = round;
+          fill = v;
+        } else {
+          kind = SRC_MISS_NOSLOT;
+        }
+      }
+    }
+    s.uni[ux] = (int32_t)p;
+    s.upos[p] = (int32_t)ux;
+    s.kind[ux] = kind;
+    s.src[ux] = src;
+    s.fill[ux] = fill;
+  }
+}
+
 struct CopyKArgs {
   StepArgs a;
-  int row_bytes, ring_cap, ring_rows;
+  int row_bytes, ring_cap, ring_rows, hot_slots;
+  int64_t max_positions;
 };
 
 __global__ __launch_bounds__(256) void copy_kernel(CopyKArgs ka) {
@@ -345,6 +324,11 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyKArgs ka) {
       const int64_t x = t / kCopyChunks16, c = t % kCopyChunks16;
       const int32_t kind = s.kind[x];
       const int64_t src = s.src[x];
+      // every source index is range-checked: an inconsistent plan copies nothing
+      const bool ok = kind == SRC_HIT ? (src >= 0 && src < ka.hot_slots)
+                    : kind == SRC_RING ? (src >= 0 && src < ka.ring_cap)
+                    : (src >= 0 && src < ka.max_positions);
+      if (!ok) continue;
       const uint8_t* from = kind == SRC_HIT ? u.slots + src * rb
                           : kind == SRC_RING ? u.ring + src * rb
                           : u.rows + src * rb;
@@ -352,7 +336,7 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyKArgs ka) {
       *reinterpret_cast<uint4*>(s.compact + x * rb + c * 16) = v;
       if (kind == SRC_MISS) {
         const int32_t f = s.fill[x];
-        if (f >= 0) *reinterpret_cast<uint4*>(u.slots + (int64_t)f * rb + c * 16) = v;
+        if (f >= 0 && f < ka.hot_slots) *reinterpret_cast<uint4*>(u.slots + (int64_t)f * rb + c * 16) = v;
       }
     } else {
       const int64_t w = t - n_gather;
@@ -448,20 +432,24 @@ unsigned grid_for(int64_t work, int64_t cap = 4096) {
 
 }  // namespace
 
-hipError_t prepare_gather_kernels() {
-  return hipFuncSetAttribute((const void*)plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             2 * kMaxUnion * (int)sizeof(uint32_t));
+hipError_t launch_gather_scan(const Geometry& g, const StepArgs& a, hipStream_t st) {
+  ScanKArgs ka{a, g.hot_slots, g.s_words, g.ring_rows, g.mode};
+  hipLaunchKernelGGL(gather_scan_kernel, dim3((unsigned)a.n_seqs), dim3(kScanThreads), 0, st, ka);
+  return hipGetLastError();
 }
 
-hipError_t launch_plan(const Geometry& g, const StepArgs& a, hipStream_t st) {
-  PlanKArgs ka{a, g.top_k, g.hot_slots, g.ring_cap, g.ring_rows, g.mode};
-  const size_t lds = 2 * (size_t)a.R * g.top_k * sizeof(uint32_t);
-  hipLaunchKernelGGL(plan_kernel, dim3((unsigned)a.n_seqs), dim3(kPlanThreads), lds, st, ka);
+hipError_t launch_gather_assign(const Geometry& g, const StepArgs& a, hipStream_t st) {
+  AssignKArgs ka{a, g.hot_slots, g.s_words, g.ring_cap, g.mode, g.max_positions};
+  const int64_t words = (a.l_max + 31) / 32;
+  int64_t blocks = (words + 3) / 4;                 // 4 waves per block, one word per wave
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(gather_assign_kernel, dim3((unsigned)blocks, (unsigned)a.n_seqs), dim3(256), 0, st, ka);
   return hipGetLastError();
 }
 
 hipError_t launch_copy(const Geometry& g, const StepArgs& a, hipStream_t st) {
-  CopyKArgs ka{a, g.row_bytes, g.ring_cap, g.ring_rows};
+  CopyKArgs ka{a, g.row_bytes, g.ring_cap, g.ring_rows, g.hot_slots, g.max_positions};
   const int64_t work = (int64_t)a.R * g.top_k * kCopyChunks16 + (int64_t)g.ring_rows * kCopyChunks16;
   hipLaunchKernelGGL(copy_kernel, dim3(grid_for(work, 2048), (unsigned)a.n_seqs), dim3(256), 0, st, ka);
   return hipGetLastError();

@@ -18,6 +18,10 @@
 // The fp32 accumulator is exact for integer-valued bf16 inputs (|q.k| <= 2^13).
 // After the tile, each lane applies ReLU and the head weight to its 16
 // accumulator rows and the head sum is finished with one cross-half shuffle.
+// While the scores are in registers, the workgroup also counts the first
+// radix digit (top 11 bits of the order-preserving key) of every visible score
+// per query row, in packed 16-bit LDS counters, and adds them to the row's
+// global histogram -- the first pass of the exact Top-K.
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -35,13 +39,37 @@ struct ScoreKArgs {
   const float* w;                       // [n_seqs][R][HI]
   int64_t p_pad;
   int subs_per_wave;                    // 32-position sub-tiles per wave
+  int r_max;
 };
 
 __device__ inline float canon0(float s) { return s == 0.0f ? 0.0f : s; }
 
+__device__ inline uint32_t first_digit(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return ((u & 0x80000000u) ? ~u : (u | 0x80000000u)) >> 21;
+}
+
+// Count the scores of the active lanes in row r's packed LDS histogram (two 16-bit
+// bins per word).  Scores of neighbouring positions share few first digits, so
+// lanes with equal digits are combined first: one atomic per distinct digit.
+__device__ inline void count_digit(uint32_t* lh, int r, float score) {
+  const uint32_t key = ((uint32_t)r << 11) | first_digit(score);   // (row, digit); lanes may differ in row
+  uint64_t todo = __ballot(1);
+  while (todo) {
+    const int leader = __ffsll((unsigned long long)todo) - 1;
+    const uint32_t kl = __shfl(key, leader);
+    const uint64_t same = __ballot(key == kl) & todo;
+    if ((int)(threadIdx.x & 63) == leader) {
+      const uint32_t rl = kl >> 11, dl = kl & 2047u;
+      atomicAdd(&lh[rl * (kRadixBins / 2) + (dl >> 1)], (uint32_t)__popcll(same) << (16 * (dl & 1)));
+    }
+    todo &= ~same;
+  }
+}
+
 template <int HI>
 __global__ __launch_bounds__(256) void score_kernel(ScoreKArgs ka) {
-  extern __shared__ __align__(16) uint16_t sq[];   // [MT*32][kQStride] then weights
+  extern __shared__ __align__(16) uint16_t sq[];   // [MT*32][kQStride], weights, digit histograms
   const StepArgs& a = ka.a;
   const int seq = blockIdx.y;
   const UnitDev u = a.units[a.unit_base + seq];
@@ -51,8 +79,30 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreKArgs ka) {
   const int M = R * HI;
   const int MT = (M + 31) / 32;
   float* sw = reinterpret_cast<float*>(sq + MT * 32 * kQStride);
+  uint32_t* lh = reinterpret_cast<uint32_t*>(sw + MT * 32);   // [R][1024] packed pairs of bins
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31;
+  const int hf = lane >> 5;
+  const int64_t first_sub = ((int64_t)blockIdx.x * kWaves + wave) * ka.subs_per_wave;
+
+  // Start the first key tile's loads before staging Q.
+  bf16x8 b[8];
+  {
+    const int64_t t = first_sub * 32 + n;
+    if (t < L) {
+      const bf16x8* kp = reinterpret_cast<const bf16x8*>(u.keys + t * 128 + 64 * hf);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) b[ks] = kp[ks];
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) b[ks] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
 
   // Stage Q (zero padded to MT*32 rows) and the head weights in LDS.
+  for (int w = threadIdx.x; w < R * (kRadixBins / 2); w += blockDim.x) lh[w] = 0;
   const uint16_t* qg = ka.q + (int64_t)seq * M * 128;
   for (int c = threadIdx.x; c < MT * 32 * 16; c += blockDim.x) {
     int row = c >> 4, col = (c & 15) * 8;
@@ -64,26 +114,22 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreKArgs ka) {
     sw[m] = m < M ? ka.w[(int64_t)seq * M + m] : 0.0f;
   __syncthreads();
 
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 31;
-  const int hf = lane >> 5;
-  const int64_t first_sub = ((int64_t)blockIdx.x * kWaves + wave) * ka.subs_per_wave;
   float* scores = s.scores;
 
   for (int si = 0; si < ka.subs_per_wave; ++si) {
     const int64_t t0 = (first_sub + si) * 32;
     if (t0 >= L) break;
     const int64_t t = t0 + n;
-    // B fragments: 8 k-steps x 16 bytes of key t.
-    bf16x8 b[8];
-    if (t < L) {
-      const bf16x8* kp = reinterpret_cast<const bf16x8*>(u.keys + t * 128 + 64 * hf);
+    // B fragments: 8 k-steps x 16 bytes of key t (the first tile's are already loaded).
+    if (si > 0) {
+      if (t < L) {
+        const bf16x8* kp = reinterpret_cast<const bf16x8*>(u.keys + t * 128 + 64 * hf);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) b[ks] = kp[ks];
-    } else {
+        for (int ks = 0; ks < 8; ++ks) b[ks] = kp[ks];
+      } else {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) b[ks] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
+        for (int ks = 0; ks < 8; ++ks) b[ks] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
+      }
     }
     for (int mt = 0; mt < MT; ++mt) {
       f32x16 acc = {0};
@@ -109,41 +155,59 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreKArgs ka) {
         float sum = (part[0] + part[1]) + (part[2] + part[3]);
         sum += __shfl_xor(sum, 32);
         const int r = mt;
-        if (hf == 0 && r < R && t < L - R + r + 1)
+        if (hf == 0 && r < R && t < L - R + r + 1) {
           scores[(int64_t)r * ka.p_pad + t] = canon0(sum);
+          count_digit(lh, r, canon0(sum));
+        }
       } else if constexpr (HI == 16) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
           float sum = part[2 * k2] + part[2 * k2 + 1];
           sum += __shfl_xor(sum, 32);
           const int r = mt * 2 + k2;
-          if (hf == 0 && r < R && t < L - R + r + 1)
+          if (hf == 0 && r < R && t < L - R + r + 1) {
             scores[(int64_t)r * ka.p_pad + t] = canon0(sum);
+            count_digit(lh, r, canon0(sum));
+          }
         }
       } else if constexpr (HI == 8) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float sum = part[i] + __shfl_xor(part[i], 32);
           const int r = mt * 4 + i;
-          if (hf == 0 && r < R && t < L - R + r + 1)
+          if (hf == 0 && r < R && t < L - R + r + 1) {
             scores[(int64_t)r * ka.p_pad + t] = canon0(sum);
+            count_digit(lh, r, canon0(sum));
+          }
         }
       } else {  // HI == 4: rows of one query row sit in one lane half
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = mt * 8 + 2 * i + hf;
-          if (r < R && t < L - R + r + 1)
+          if (r < R && t < L - R + r + 1) {
             scores[(int64_t)r * ka.p_pad + t] = canon0(part[i]);
+            count_digit(lh, r, canon0(part[i]));
+          }
         }
       }
     }
+  }
+  __syncthreads();
+  for (int w = threadIdx.x; w < R * (kRadixBins / 2); w += blockDim.x) {
+    const uint32_t v = lh[w];
+    if (!v) continue;
+    const int r = w / (kRadixBins / 2), d = 2 * (w % (kRadixBins / 2));
+    const int rep = blockIdx.x % kHistReps;
+    uint32_t* gh = s.hist0 + ((int64_t)rep * ka.r_max + r) * kRadixBins + d;
+    if (v & 0xFFFFu) atomicAdd(gh, v & 0xFFFFu);
+    if (v >> 16) atomicAdd(gh + 1, v >> 16);
   }
 }
 
 }  // namespace
 
 hipError_t prepare_score_kernels() {
-  const int max_lds = 256 * kQStride * 2 + 256 * 4;
+  const int max_lds = 256 * kQStride * 2 + 256 * 4 + 8 * (kRadixBins / 2) * 4;
   hipError_t e;
   if ((e = hipFuncSetAttribute((const void*)score_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds))) return e;
   if ((e = hipFuncSetAttribute((const void*)score_kernel<8>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds))) return e;
@@ -158,6 +222,7 @@ hipError_t launch_score(const Geometry& g, const StepArgs& a, const uint16_t* q,
   ka.q = q;
   ka.w = w;
   ka.p_pad = g.p_pad;
+  ka.r_max = g.r_max;
   const int64_t subs = (a.l_max + 31) / 32;
   // Enough waves to cover the chip several times; longer per-wave runs amortise the Q staging.
   int spw = (int)((subs + 4 * 256 * 4 - 1) / (4 * 256 * 4));
@@ -166,7 +231,8 @@ hipError_t launch_score(const Geometry& g, const StepArgs& a, const uint16_t* q,
   ka.subs_per_wave = spw;
   const int64_t blocks = (subs + (int64_t)kWaves * spw - 1) / ((int64_t)kWaves * spw);
   const int MT = (a.R * g.index_heads + 31) / 32;
-  const size_t lds = (size_t)MT * 32 * kQStride * sizeof(uint16_t) + (size_t)MT * 32 * sizeof(float);
+  const size_t lds = (size_t)MT * 32 * kQStride * sizeof(uint16_t) + (size_t)MT * 32 * sizeof(float) +
+                     (size_t)a.R * (kRadixBins / 2) * sizeof(uint32_t);
   dim3 grid((unsigned)blocks, (unsigned)a.n_seqs), block(256);
   switch (g.index_heads) {
     case 4: hipLaunchKernelGGL(score_kernel<4>, grid, block, lds, st, ka); break;

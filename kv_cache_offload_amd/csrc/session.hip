@@ -18,7 +18,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/dsa.h"
+#include "dsa.h"
 #include "dsa_internal.h"
 
 using namespace dsa;
@@ -58,7 +58,6 @@ struct dsa_session {
   UnitDev* d_units = nullptr;              // inside the arena
   SeqScratch* d_scr = nullptr;
   std::vector<UnitHost> uh;
-  int parity = 0;
   int last_layer = -1;
   int last_R = 0;
   bool timing = false;
@@ -160,10 +159,11 @@ dsa_status validate_config(const dsa_config* c, std::string* why) {
   auto bad = [&](dsa_status st, const char* m) { *why = m; return st; };
   if (c->abi_version != DSA_ABI_VERSION) return bad(DSA_E_INVALID, "abi_version mismatch");
   if (c->n_layers < 1 || c->n_seqs < 1 || c->n_seqs > 64) return bad(DSA_E_INVALID, "n_layers >= 1 and 1 <= n_seqs <= 64");
-  if (c->max_positions < 1 || c->max_positions > ((int64_t)1 << 30)) return bad(DSA_E_INVALID, "max_positions out of range");
+  if (c->max_positions < 1) return bad(DSA_E_INVALID, "max_positions < 1");
+  if (c->max_positions > (int64_t)kMaxTopkChunks * kTopkChunk) return bad(DSA_E_UNSUPPORTED, "max_positions > 4,194,304");
   if (c->mode != DSA_KV_OFFLOAD && c->mode != DSA_KV_HBM_RESIDENT) return bad(DSA_E_INVALID, "unknown mode");
   if (c->top_k < 1 || c->max_query_rows < 1 || c->ring_rows < 1) return bad(DSA_E_INVALID, "top_k, max_query_rows, ring_rows >= 1");
-  if (c->mode == DSA_KV_OFFLOAD && (c->hot_slots < 1 || c->hot_slots > (1 << 28))) return bad(DSA_E_INVALID, "hot_slots out of range");
+  if (c->mode == DSA_KV_OFFLOAD && (c->hot_slots < 1 || c->hot_slots > (1 << 20))) return bad(DSA_E_INVALID, "hot_slots out of range (1..2^20)");
   if (!std::isfinite(c->softmax_scale)) return bad(DSA_E_INVALID, "softmax_scale not finite");
   if (c->index_dim != 128 || c->latent_dim != 512 || c->rope_dim != 64 || c->group != 64)
     return bad(DSA_E_UNSUPPORTED, "kernels implement index_dim 128, latent 512, rope 64, group 64");
@@ -233,8 +233,8 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   g.max_positions = cfg->max_positions;
   g.p_pad = (cfg->max_positions + kTopkChunk - 1) / kTopkChunk * kTopkChunk;
   g.n_chunks = (int)(g.p_pad / kTopkChunk);
-  g.attn_split_rows = 128;
-  g.nsplit = (cfg->top_k + g.attn_split_rows - 1) / g.attn_split_rows;
+  g.s_words = (g.hot_slots + 31) / 32;
+  g.nsplit_max = (cfg->top_k + 63) / 64;
   g.softmax_scale = cfg->softmax_scale;
 
   const int n_units = cfg->n_layers * cfg->n_seqs;
@@ -246,7 +246,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   auto take = [&](size_t bytes) { size_t at = cur; cur += align_up(bytes ? bytes : 1); return at; };
   const size_t o_units = take(sizeof(UnitDev) * n_units);
   const size_t o_scr = take(sizeof(SeqScratch) * cfg->n_seqs);
-  struct UnitOff { size_t keys, rows, slots, ring, pos_slot, slot_pos, fill, pin, hand, dyn; };
+  struct UnitOff { size_t keys, rows, slots, ring, pos_slot, slot_pos, fill, pin, hand, dyn, totals; };
   std::vector<UnitOff> uo(n_units);
   for (int i = 0; i < n_units; ++i) {
     uo[i].keys = take((size_t)P * g.index_dim * 2);
@@ -259,14 +259,14 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     uo[i].pin = off ? take((size_t)S * 4) : 0;
     uo[i].hand = take(4);
     uo[i].dyn = take(32);
+    uo[i].totals = take(64);
   }
-  struct ScrOff { size_t scores, hist, suffix, gt22, sel, sel_n, uni, kind, src, fill, map, compact, po, pml, cnt, info; };
+  struct ScrOff { size_t scores, sel, sel_n, uni, kind, src, fill, map, compact, po, pml, cnt, info,
+                  selmask, hitmask, base_u, base_m, pinmask, upw, upos, victim, victim_old, hist0, hist1, cand,
+                  cand_n; };
   std::vector<ScrOff> so(cfg->n_seqs);
   for (int q = 0; q < cfg->n_seqs; ++q) {
     so[q].scores = take((size_t)g.r_max * P * 4);
-    so[q].hist = take((size_t)2 * g.r_max * 3 * kRadixBins * 4);
-    so[q].suffix = take((size_t)g.r_max * g.n_chunks * kSuffixLen * 4);
-    so[q].gt22 = take((size_t)g.r_max * g.n_chunks * 4);
     so[q].sel = take((size_t)RK * 4);
     so[q].sel_n = take((size_t)g.r_max * 4);
     so[q].uni = take((size_t)RK * 4);
@@ -275,10 +275,23 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     so[q].fill = take((size_t)RK * 4);
     so[q].map = take((size_t)RK * 4);
     so[q].compact = take((size_t)RK * rb);
-    so[q].po = take((size_t)g.r_max * g.nsplit * g.heads * g.latent * 4);
-    so[q].pml = take((size_t)g.r_max * g.nsplit * g.heads * 2 * 4);
+    so[q].po = take((size_t)g.r_max * g.nsplit_max * g.heads * g.latent * 4);
+    so[q].pml = take((size_t)g.r_max * g.nsplit_max * g.heads * 2 * 4);
     so[q].cnt = take(8 * 8);
-    so[q].info = take(4 * 8);
+    so[q].info = take(8 * 8);
+    so[q].selmask = take((size_t)P / 32 * 4);
+    so[q].hitmask = take((size_t)P / 32 * 4);
+    so[q].base_u = take((size_t)P / 32 * 4);
+    so[q].base_m = take((size_t)P / 32 * 4);
+    so[q].pinmask = take((size_t)g.s_words * 4);
+    so[q].upw = take((size_t)g.s_words * 4);
+    so[q].upos = take((size_t)P * 4);
+    so[q].victim = take((size_t)g.s_words * 32 * 4);
+    so[q].victim_old = take((size_t)g.s_words * 32 * 4);
+    so[q].hist0 = take((size_t)kHistReps * g.r_max * kRadixBins * 4);
+    so[q].hist1 = take((size_t)g.r_max * kRadixBins * 4);
+    so[q].cand = take((size_t)g.r_max * P * 8);
+    so[q].cand_n = take((size_t)g.r_max * g.n_chunks * 4);
   }
   s->arena_bytes = cur;
 
@@ -290,7 +303,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   };
   hipError_t e;
   if ((e = prepare_score_kernels()) != hipSuccess) return bail(DSA_E_HIP, "prepare");
-  if ((e = prepare_gather_kernels()) != hipSuccess) return bail(DSA_E_HIP, "prepare");
+  if ((e = prepare_topk_kernels()) != hipSuccess) return bail(DSA_E_HIP, "prepare");
   if (hipMalloc(&s->arena, s->arena_bytes) != hipSuccess) {
     s->arena = nullptr;
     (void)hipGetLastError();
@@ -332,15 +345,13 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     }
     u.hand = reinterpret_cast<int32_t*>(base + uo[i].hand);
     u.dyn = reinterpret_cast<int64_t*>(base + uo[i].dyn);
+    u.totals = reinterpret_cast<int64_t*>(base + uo[i].totals);
     if (hipEventCreateWithFlags(&s->uh[i].ev, hipEventDisableTiming) != hipSuccess) return bail(DSA_E_HIP, "event");
   }
   s->scr.resize(cfg->n_seqs);
   for (int q = 0; q < cfg->n_seqs; ++q) {
     SeqScratch& c = s->scr[q];
     c.scores = reinterpret_cast<float*>(base + so[q].scores);
-    c.hist = reinterpret_cast<uint32_t*>(base + so[q].hist);
-    c.suffix = reinterpret_cast<uint32_t*>(base + so[q].suffix);
-    c.gt22 = reinterpret_cast<uint32_t*>(base + so[q].gt22);
     c.sel = reinterpret_cast<int32_t*>(base + so[q].sel);
     c.sel_n = reinterpret_cast<int32_t*>(base + so[q].sel_n);
     c.uni = reinterpret_cast<int32_t*>(base + so[q].uni);
@@ -353,6 +364,19 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     c.part_ml = reinterpret_cast<float*>(base + so[q].pml);
     c.counters = reinterpret_cast<int64_t*>(base + so[q].cnt);
     c.info = reinterpret_cast<int64_t*>(base + so[q].info);
+    c.selmask = reinterpret_cast<uint32_t*>(base + so[q].selmask);
+    c.hitmask = reinterpret_cast<uint32_t*>(base + so[q].hitmask);
+    c.base_u = reinterpret_cast<uint32_t*>(base + so[q].base_u);
+    c.base_m = reinterpret_cast<uint32_t*>(base + so[q].base_m);
+    c.pinmask = reinterpret_cast<uint32_t*>(base + so[q].pinmask);
+    c.upw = reinterpret_cast<uint32_t*>(base + so[q].upw);
+    c.upos = reinterpret_cast<int32_t*>(base + so[q].upos);
+    c.victim = reinterpret_cast<int32_t*>(base + so[q].victim);
+    c.victim_old = reinterpret_cast<int32_t*>(base + so[q].victim_old);
+    c.hist0 = reinterpret_cast<uint32_t*>(base + so[q].hist0);
+    c.hist1 = reinterpret_cast<uint32_t*>(base + so[q].hist1);
+    c.cand = reinterpret_cast<int2*>(base + so[q].cand);
+    c.cand_n = reinterpret_cast<uint32_t*>(base + so[q].cand_n);
     if (hipMemset(c.sel, 0xFF, (size_t)RK * 4) != hipSuccess || hipMemset(c.map, 0xFF, (size_t)RK * 4) != hipSuccess)
       return bail(DSA_E_HIP, "hipMemset");
   }
@@ -453,22 +477,20 @@ dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq, 
   a.unit_base = layer * n_seqs;
   a.n_seqs = n_seqs;
   a.R = R;
-  a.parity = s->parity;
   a.l_max = l_max;
   const Geometry& g = s->g;
   const uint16_t* iq = static_cast<const uint16_t*>(index_q);
   const uint16_t* ql = static_cast<const uint16_t*>(q_latent);
   const uint16_t* qr = static_cast<const uint16_t*>(q_rope);
   if ((st = timed_launch(s, KK_SCORE, stream, "score kernel", [&] { return launch_score(g, a, iq, index_w, stream); })) != DSA_OK) return st;
-  for (int pass = 0; pass < 3; ++pass)
-    if ((st = timed_launch(s, KK_TOPK_HIST, stream, "top-k histogram", [&] { return launch_topk_hist(g, a, pass, stream); })) != DSA_OK) return st;
-  if ((st = timed_launch(s, KK_TOPK_EMIT, stream, "top-k emit", [&] { return launch_topk_emit(g, a, stream); })) != DSA_OK) return st;
-  if ((st = timed_launch(s, KK_PLAN, stream, "gather plan", [&] { return launch_plan(g, a, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_TOPK_COLLECT, stream, "top-k refine", [&] { return launch_topk_refine(g, a, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_TOPK_COLLECT, stream, "top-k collect", [&] { return launch_topk_collect(g, a, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_TOPK_RESOLVE, stream, "top-k resolve", [&] { return launch_topk_resolve(g, a, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_SCAN, stream, "gather scan", [&] { return launch_gather_scan(g, a, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_ASSIGN, stream, "gather assign", [&] { return launch_gather_assign(g, a, stream); })) != DSA_OK) return st;
   if ((st = timed_launch(s, KK_COPY, stream, "gather copy", [&] { return launch_copy(g, a, stream); })) != DSA_OK) return st;
   if ((st = timed_launch(s, KK_ATTN, stream, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream); })) != DSA_OK) return st;
-  if (g.nsplit > 1)
-    if ((st = timed_launch(s, KK_MERGE, stream, "attention merge", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK) return st;
-  s->parity ^= 1;
+  if ((st = timed_launch(s, KK_MERGE, stream, "attention merge", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK) return st;
   s->last_layer = layer;
   s->last_R = R;
   for (int q = 0; q < n_seqs; ++q) {
@@ -540,6 +562,7 @@ dsa_status dsa_debug_size(const dsa_session* s, int32_t layer, int32_t seq, int3
     case DSA_DBG_SLOT_BYTES: b = (size_t)S * rb; break;
     case DSA_DBG_MIRROR: b = (size_t)(g.mode == DSA_KV_OFFLOAD ? h.M : h.L) * rb; break;
     case DSA_DBG_KEYS: b = (size_t)h.L * g.index_dim * 2; break;
+    case DSA_DBG_TOTALS: b = 64; break;
     default: return DSA_E_INVALID;
   }
   *bytes = b;
@@ -587,6 +610,7 @@ dsa_status dsa_debug_get(dsa_session* s, int32_t layer, int32_t seq, int32_t ite
     case DSA_DBG_SLOT_BYTES: src = u.slots; break;
     case DSA_DBG_MIRROR: src = g.mode == DSA_KV_OFFLOAD ? s->mirrors[ui] : (const void*)u.rows; break;
     case DSA_DBG_KEYS: src = u.keys; break;
+    case DSA_DBG_TOTALS: src = u.totals; break;
     default: return fail(s, DSA_E_INVALID, "unknown item");
   }
   (void)K;

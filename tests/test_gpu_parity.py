@@ -75,6 +75,20 @@ def test_all_scores_equal_select_lowest_positions():
     assert sel[0].tolist() == list(range(w.top_k))
 
 
+def test_all_equal_scores_long_history():
+    # 50,023 equal scores: the Top-K candidates exceed what the resolve keeps in LDS,
+    # so the selection runs its streaming path; the lowest 2048 positions are selected
+    w = S.WORKLOADS["single_stream_50k"]
+
+    def q_zero_weight(w_, layer, seq, step):
+        iq, iw, ql, qr = S.step_queries(w_, layer, seq, step)
+        return iq, np.zeros_like(iw), ql, qr
+    _note("ties, long history")
+    orcs = _run_and_compare(w, MODE_OFFLOAD, steps=1, query_fn=q_zero_weight)
+    sel, _ = orcs[(0, 0)].selection()
+    assert sel[3].tolist() == list(range(w.top_k))
+
+
 def test_planted_ties_small_key_alphabet():
     # keys and queries from {-1, 0, 1}: scores collide often, the tie rule decides the cutoff
     w = S.WORKLOADS["tiny"].scaled(rows_per_step=3, steps=3, history=6000)
