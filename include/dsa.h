@@ -90,7 +90,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1u
+#define DSA_ABI_VERSION 2u
 
 typedef enum {
   DSA_OK = 0,
@@ -214,14 +214,25 @@ dsa_status dsa_debug_get(dsa_session* s, int32_t layer, int32_t seq, int32_t ite
                          size_t bytes, hipStream_t stream);
 
 /* ---- Per-kernel timing -----------------------------------------------------
- * When enabled, every kernel launch of dsa_decode_step is bracketed by HIP
- * events on the launch stream; dsa_kernel_times synchronises those events and
- * returns, per kernel kind, the launch count and total milliseconds since the
- * last call, then resets.  Kinds: 0 index score (with the first top-k digit
- * histogram), 1 top-k collect, 2 top-k resolve (selection, union marking and
- * cache classification), 3 gather scan, 4 gather assign (slot table), 5 gather
- * copy, 6 attention, 7 attention merge. */
-#define DSA_KERNEL_KINDS 8
+ * When enabled, each group of kernels below carries HIP events on its first
+ * and last dispatch (hipExtLaunchKernel), so the interval is the kernels' own
+ * execution time, as a kernel trace reports it.  dsa_kernel_times
+ * synchronises those events and returns, per kind, the number of timed groups
+ * and their total milliseconds since the last call, then resets.  Kinds:
+ *   0 index score (with the first Top-K digit histogram)
+ *   1 Top-K collect (candidate lists per 4096-position chunk; with a refine
+ *     pass before it for histories longer than 65,536 positions)
+ *   2 Top-K resolve (selection, union marks, cache classification, then the
+ *     gather plan of each sequence)
+ *   3 gather (slot table update, row copies to the compact buffer and the hot
+ *     slots, ring writeback)
+ *   4 attention
+ *   5 attention merge (absent when one split covers the selection)
+ *   6 append (dsa_append_rows)
+ * dsa_set_kernel_timing: enable <= 0 turns timing off; enable > 0 turns it on
+ * and pre-creates the events of `enable` decode steps (at most 2^18), so that
+ * the timed calls themselves create none. */
+#define DSA_KERNEL_KINDS 7
 dsa_status dsa_set_kernel_timing(dsa_session* s, int32_t enable);
 dsa_status dsa_kernel_times(dsa_session* s, int64_t counts[DSA_KERNEL_KINDS],
                             double total_ms[DSA_KERNEL_KINDS]);

@@ -17,13 +17,12 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdsa.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 OK, E_INVALID, E_NOMEM, E_CAPACITY, E_UNSUPPORTED, E_STATE, E_HIP = range(7)
 STATUS_NAMES = {0: "DSA_OK", 1: "DSA_E_INVALID", 2: "DSA_E_NOMEM", 3: "DSA_E_CAPACITY",
                 4: "DSA_E_UNSUPPORTED", 5: "DSA_E_STATE", 6: "DSA_E_HIP"}
 KV_OFFLOAD, KV_HBM_RESIDENT = 0, 1
-KERNEL_KINDS = ("index_score", "topk_collect", "topk_resolve", "gather_scan", "gather_assign",
-                "gather_copy", "attention", "attention_merge")
+KERNEL_KINDS = ("index_score", "topk_collect", "topk_resolve", "gather", "attention", "attention_merge", "append")
 
 # inspection items (dsa_debug_item)
 DBG = dict(scores=0, selection=1, sel_count=2, union=3, union_kind=4, union_src=5, map=6,
@@ -258,8 +257,10 @@ class Session:
                                                    self._stream()))
         return buf[:n]
 
-    def set_kernel_timing(self, enable=True):
-        self._check("dsa_set_kernel_timing", dsa_set_kernel_timing(self.h, enable))
+    def set_kernel_timing(self, enable=True, reserve_steps=64):
+        """Turn per-kernel timing on (events pre-created for reserve_steps steps) or off."""
+        n = max(1, int(reserve_steps)) if enable else 0
+        self._check("dsa_set_kernel_timing", dsa_set_kernel_timing(self.h, n))
 
     def kernel_times(self):
         st, counts, ms = dsa_kernel_times(self.h)

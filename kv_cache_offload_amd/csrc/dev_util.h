@@ -1,0 +1,123 @@
+// dev_util.h -- small device helpers shared by the libdsa kernels: wave and
+// workgroup scans, the order-preserving key of an fp32 score, and the radix
+// bin search of the Top-K.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// Order-preserving 32-bit key of an fp32 value (larger float -> larger key).
+__device__ inline uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ inline uint32_t wave_incl_scan(uint32_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive scan in thread order over a workgroup of NW waves; total in *tot.
+// sh: NW words of LDS.  Contains two barriers; every thread must call it.
+template <int NW>
+__device__ inline uint32_t block_scan(uint32_t v, uint32_t* tot, uint32_t* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t inc = wave_incl_scan(v, lane);
+  if (lane == 63) sh[wave] = inc;
+  __syncthreads();
+  uint32_t base = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t x = sh[w];
+    base += (w < wave) ? x : 0u;
+    all += x;
+  }
+  __syncthreads();
+  *tot = all;
+  return base + inc - v;
+}
+
+// Four independent exclusive scans with one pair of barriers.  sh: 4*NW words.
+template <int NW>
+__device__ inline uint4 block_scan4(uint4 v, uint4* tot, uint32_t* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint4 inc;
+  inc.x = wave_incl_scan(v.x, lane);
+  inc.y = wave_incl_scan(v.y, lane);
+  inc.z = wave_incl_scan(v.z, lane);
+  inc.w = wave_incl_scan(v.w, lane);
+  if (lane == 63) {
+    sh[4 * wave + 0] = inc.x;
+    sh[4 * wave + 1] = inc.y;
+    sh[4 * wave + 2] = inc.z;
+    sh[4 * wave + 3] = inc.w;
+  }
+  __syncthreads();
+  uint4 base = make_uint4(0u, 0u, 0u, 0u), all = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t a = sh[4 * w], b = sh[4 * w + 1], c = sh[4 * w + 2], d = sh[4 * w + 3];
+    if (w < wave) { base.x += a; base.y += b; base.z += c; base.w += d; }
+    all.x += a; all.y += b; all.z += c; all.w += d;
+  }
+  __syncthreads();
+  *tot = all;
+  return make_uint4(base.x + inc.x - v.x, base.y + inc.y - v.y, base.z + inc.z - v.z, base.w + inc.w - v.w);
+}
+
+// The bin holding the k-th largest key among those counted in hist[NBINS] (summed
+// over REPS replicas `stride` apart): the largest b with suffix(b) >= k, and the
+// number of keys still needed from it.  Each thread owns NBINS/(64 NW)
+// contiguous bins, loaded together; thread 0 owns the highest.  hist may be in
+// global memory or LDS.  Every thread of the workgroup must call it.
+template <int NW, int NBINS, int REPS, class HistPtr>
+__device__ inline void find_bin(HistPtr hist, uint32_t k, uint32_t* sh, int* out_bin,
+                                uint32_t* out_need, int64_t stride = 0) {
+  constexpr int PER = NBINS / (NW * 64);
+  static_assert(PER >= 1 && NBINS % (NW * 64) == 0, "bins per thread");
+  __shared__ int s_bin;
+  __shared__ uint32_t s_need;
+  const int lo = NBINS - ((int)threadIdx.x + 1) * PER;
+  uint32_t c[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) c[e] = 0;
+#pragma unroll
+  for (int q = 0; q < REPS; ++q)
+#pragma unroll
+    for (int e = 0; e < PER; ++e) c[e] += hist[q * stride + lo + e];
+  uint32_t local = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) local += c[e];
+  uint32_t tot;
+  const uint32_t before = block_scan<NW>(local, &tot, sh);   // keys in higher bins
+  if (before < k && before + local >= k) {
+    uint32_t acc = before;
+    bool done = false;
+#pragma unroll
+    for (int e = PER - 1; e >= 0; --e) {
+      if (!done && acc + c[e] >= k) {
+        s_bin = lo + e;
+        s_need = k - acc;
+        done = true;
+      }
+      acc += c[e];
+    }
+  }
+  __syncthreads();
+  *out_bin = s_bin;
+  *out_need = s_need;
+  __syncthreads();
+}
+
+// Lanes below this one, as a 64-bit mask.
+__device__ inline uint64_t lanes_below(int lane) {
+  return lane ? (~0ull >> (64 - lane)) : 0ull;
+}
+
+}  // namespace dsa

@@ -3,13 +3,13 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace dsa {
 
 // Kernel kinds for the optional per-kernel timing (order matches dsa.h).
-enum KernelKind { KK_SCORE = 0, KK_TOPK_COLLECT, KK_TOPK_RESOLVE, KK_SCAN, KK_ASSIGN, KK_COPY, KK_ATTN, KK_MERGE, KK__N };
-// (the top-k refine pass is timed with the collect kind)
+enum KernelKind { KK_SCORE = 0, KK_TOPK_PARTIAL, KK_TOPK_SELECT, KK_GATHER, KK_ATTN, KK_MERGE, KK_APPEND, KK__N };
 
 // Source kinds of a compact row (same numbering as the inspection interface).
 enum SrcKind { SRC_HIT = 0, SRC_RING = 1, SRC_MISS = 2, SRC_MISS_NOSLOT = 3, SRC_RES = 4 };
@@ -22,50 +22,72 @@ constexpr int kAttnSubRows = 32;      // selected rows per attention sub-chunk
 constexpr int kMaxUnion = 16384;      // R_max * K limit
 constexpr int kCopyChunks16 = 41;     // 656 / 16
 
+// Pointer flavours of the descriptors below.  The host fills them with plain
+// pointers; device code reads the same bytes as pointers into the global
+// address space, so every access through them compiles to global_*
+// instructions (a flat access also counts against the LDS counter, and LDS
+// work in the same wave would wait for it).
+#define DSA_GLOBAL __attribute__((address_space(1)))
+template <class T> using HostPtr = T*;
+// Plain vector types for 8- and 16-byte moves (they load and store through any
+// address space, unlike the HIP vector classes).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+template <class T> using GlobalPtr = DSA_GLOBAL T*;
+
 // Per-unit persistent state, device-visible.
-struct UnitDev {
-  uint16_t* keys;        // [P_pad][index_dim] bf16, HBM
-  uint8_t* rows;         // offload: device address of the pinned host mirror; resident: HBM row store
-  uint8_t* slots;        // [S][row_bytes] hot slots (offload)
-  uint8_t* ring;         // [ring_cap][row_bytes] recent ring (offload)
-  int32_t* pos_slot;     // [P_pad]  -1 = not cached
-  int32_t* slot_pos;     // [S]      -1 = empty
-  int32_t* fill_round;   // [S]
-  int32_t* pin_round;    // [S]
-  int32_t* hand;         // [1]
-  int64_t* dyn;          // [4] L, M, round, reserved -- updated only by kernels, in stream order
-  int64_t* totals;       // [8] step counters summed over every decode step of the unit
+template <template <class> class P>
+struct UnitT {
+  P<uint16_t> keys;        // [P_pad][index_dim] bf16, HBM
+  P<uint8_t> rows;         // offload: device address of the pinned host mirror; resident: HBM row store
+  P<uint8_t> slots;        // [S][row_bytes] hot slots (offload)
+  P<uint8_t> ring;         // [ring_cap][row_bytes] recent ring (offload)
+  P<int32_t> pos_slot;     // [P_pad]  -1 = not cached
+  P<int32_t> slot_pos;     // [S]      -1 = empty
+  P<int32_t> fill_round;   // [S]
+  P<int32_t> pin_round;    // [S]
+  P<int32_t> hand;         // [1]
+  P<int64_t> dyn;          // [4] L, M, round, reserved -- updated only by kernels, in stream order
+  P<int64_t> totals;       // [8] step counters summed over every decode step of the unit
 };
 
 // Per-sequence step scratch, shared by the layers (layers run in stream order).
-struct SeqScratch {
-  float* scores;          // [R_max][P_pad]
-  int32_t* sel;           // [R_max][K]
-  int32_t* sel_n;         // [R_max]
-  int32_t* uni;           // [R_max*K]
-  int32_t* kind;          // [R_max*K]
-  int32_t* src;           // [R_max*K]
-  int32_t* fill;          // [R_max*K]
-  int32_t* map;           // [R_max][K]
-  uint8_t* compact;       // [R_max*K][row_bytes]
-  float* part_o;          // [R_max][nsplit_max][H][latent]
-  float* part_ml;         // [R_max][nsplit_max][H][2]
-  int64_t* counters;      // [8] union, hit, ring, miss, miss_noslot, evict, host_bytes, resident
-  int64_t* info;          // [8] see kInfo* below
-  uint32_t* selmask;      // [P_pad/32] positions selected by any row this step (cleared by the assign)
-  uint32_t* hitmask;      // [P_pad/32] selected positions that hit a slot (cleared by the assign)
-  int32_t* upos;          // [P_pad] union index of each selected position (valid for this step's selection)
-  uint32_t* base_u;       // [P_pad/32] union entries before each 32-position word
-  uint32_t* base_m;       // [P_pad/32] misses before each word
-  uint32_t* pinmask;      // [S_pad/32] slots pinned this round (cleared by the scan)
-  uint32_t* upw;          // [S_pad/32] unpinned slots, in ring order from the hand
-  int32_t* victim;        // [S_pad] slot given to the k-th miss of the step
-  uint32_t* hist0;        // [kHistReps][R_max][2048] first-digit histogram replicas (zeroed after use)
-  uint32_t* hist1;        // [R_max][2048] second-digit histogram within the first-digit bin
-  int2* cand;             // [R_max][P_pad] top-k candidates (key, position), by chunk, in position order
-  uint32_t* cand_n;       // [R_max][n_chunks] candidates per chunk
-  int32_t* victim_old;    // [S_pad] position held by victim[k] before the step (-1: empty)
+template <template <class> class P>
+struct ScratchT {
+  P<float> scores;          // [R_max][P_pad]
+  P<int32_t> sel;           // [R_max][K]
+  P<int32_t> sel_n;         // [R_max]
+  P<int32_t> uni;           // [R_max*K]
+  P<int32_t> kind;          // [R_max*K]
+  P<int32_t> src;           // [R_max*K]
+  P<int32_t> fill;          // [R_max*K] slot a miss fills (-1: none)
+  P<int32_t> map;           // [R_max][K]
+  P<uint8_t> compact;       // [R_max*K][row_bytes]
+  P<float> part_o;          // [R_max][nsplit_max][H][latent]
+  P<float> part_ml;         // [R_max][nsplit_max][H][2]
+  P<int64_t> counters;      // [8] union, hit, ring, miss, miss_noslot, evict, host_bytes, resident
+  P<int64_t> info;          // [8] see kInfo* below
+  P<uint32_t> selmask;      // [P_pad/32] positions selected by any row this step (cleared by the assign)
+  P<uint32_t> hitmask;      // [P_pad/32] selected positions that hit a slot (cleared by the assign)
+  P<int32_t> upos;          // [P_pad] union index of each selected position (valid for this step's selection)
+  P<uint32_t> base_u;       // [P_pad/32] union entries before each 32-position word
+  P<uint32_t> base_m;       // [P_pad/32] misses before each word
+  P<uint32_t> pinmask;      // [S_pad/32] slots pinned this round (cleared by the scan)
+  P<uint32_t> upw;          // [S_pad/32] unpinned slots, in ring order from the hand
+  P<int32_t> victim;        // [S_pad] slot given to the k-th miss of the step
+  P<uint32_t> hist0;        // [kHistReps][R_max][2048] first-digit histogram replicas (zeroed after use)
+  P<uint32_t> hist1;        // [R_max][2048] second-digit histogram within the first-digit bin
+  P<i32x2> cand;            // [R_max][P_pad] top-k candidates (key, position), by chunk, in position order
+  P<uint32_t> cand_n;       // [R_max][n_chunks] candidates per chunk
+  P<uint32_t> done;         // [1] rows of the step that finished their selection (reset by the last)
 };
+
+using UnitDev = UnitT<HostPtr>;
+using SeqScratch = ScratchT<HostPtr>;
+using UnitG = UnitT<GlobalPtr>;
+using ScratchG = ScratchT<GlobalPtr>;
+static_assert(sizeof(UnitDev) == sizeof(UnitG) && sizeof(SeqScratch) == sizeof(ScratchG), "same layout");
 
 // SeqScratch::info fields, written by the gather scan for the rest of the step.
 enum { kInfoUnion = 0, kInfoWriteback = 1, kInfoAssigned = 2, kInfoRound = 3, kInfoM = 4, kInfoHand = 5 };
@@ -89,16 +111,58 @@ struct StepArgs {
   int64_t l_max;          // max L over the layer's sequences (grid sizing)
 };
 
+// Optional timing of the next launches: `start` goes with the first kernel
+// launched after it is set (then cleared), `stop` with every kernel, so a
+// group of launches is timed from the first kernel's start to the last one's
+// end.  The events take the dispatch's own begin/end timestamps.
+struct LaunchTimer {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+extern thread_local LaunchTimer t_launch_timer;
+
+template <typename... Args, typename F = void (*)(Args...)>
+inline hipError_t launch_k(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t st, Args... args) {
+  LaunchTimer& t = t_launch_timer;
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, t.start, t.stop, 0u, args...);
+  t.start = nullptr;
+  return hipGetLastError();
+}
+
+// Device views of the descriptors of sequence `seq`.
+__device__ inline UnitG unit_of(const StepArgs& a, int seq) {
+  return reinterpret_cast<const UnitG*>(a.units)[a.unit_base + seq];
+}
+__device__ inline ScratchG scratch_of(const StepArgs& a, int seq) {
+  return reinterpret_cast<const ScratchG*>(a.scr)[seq];
+}
+__device__ inline UnitG as_global(const UnitDev& u) {
+  UnitG g;
+  __builtin_memcpy(&g, &u, sizeof(g));
+  return g;
+}
+
+// Relaxed device-scope atomics on global memory.
+__device__ inline void g_or(DSA_GLOBAL uint32_t* p, uint32_t v) {
+  __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void g_add(DSA_GLOBAL uint32_t* p, uint32_t v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void g_add(DSA_GLOBAL int64_t* p, int64_t v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---- launchers (each returns the hipError_t of its launch) ----
 hipError_t launch_score(const Geometry& g, const StepArgs& a, const uint16_t* q, const float* w,
                         hipStream_t st);
-hipError_t launch_topk_refine(const Geometry& g, const StepArgs& a, hipStream_t st);
-hipError_t launch_topk_collect(const Geometry& g, const StepArgs& a, hipStream_t st);
-hipError_t launch_topk_resolve(const Geometry& g, const StepArgs& a, hipStream_t st);
+// Top-K: collect (+ refine for long histories) over chunks, then resolve per
+// row; the resolve ends with the gather plan, run by the last row of each
+// sequence.
+hipError_t launch_topk_partial(const Geometry& g, const StepArgs& a, hipStream_t st);
+hipError_t launch_topk_select(const Geometry& g, const StepArgs& a, hipStream_t st);
 hipError_t prepare_topk_kernels();
-hipError_t launch_gather_scan(const Geometry& g, const StepArgs& a, hipStream_t st);
-hipError_t launch_gather_assign(const Geometry& g, const StepArgs& a, hipStream_t st);
-hipError_t launch_copy(const Geometry& g, const StepArgs& a, hipStream_t st);
+hipError_t launch_gather(const Geometry& g, const StepArgs& a, hipStream_t st);
 hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_lat,
                        const uint16_t* q_rope, float* out, hipStream_t st);
 hipError_t launch_attn_merge(const Geometry& g, const StepArgs& a, float* out, hipStream_t st);

@@ -1,0 +1,181 @@
+// gather_plan.h -- the per-sequence plan of the hot gather, run by one
+// 1024-thread workgroup once every query row of the sequence has marked its
+// selection in the step's bitmaps.
+//
+// Page "From 1M total to 15+ streams x 1M: the capacity breakthrough of
+// GLM-5.3 KV cache offload", section "GPU cache management errs too": misses
+// are served after the hits are pinned, and replacement walks the slots as a
+// ring, skipping the pinned ones.  The plan turns the position bitmaps into
+// per-32-position-word prefix counts of union entries and of misses, lists the
+// unpinned slots in ring order from the hand (the victim of the k-th miss in
+// ascending position order is victim[k]), and publishes the step's counters,
+// the new hand and the round-end state (M after writeback, round + 1).
+#pragma once
+
+#include "dev_util.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+
+struct PlanParams {
+  int S, s_words, ring_rows, mode;
+};
+
+// Bits of word w (positions 32w..32w+31) that lie at or above M.
+__device__ inline uint32_t ring_bits(int64_t w, int64_t M) {
+  const int64_t first = w * 32;
+  if (first >= M) return 0xFFFFFFFFu;
+  if (first + 32 <= M) return 0u;
+  return ~((1u << (uint32_t)(M - first)) - 1u);
+}
+
+__device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, const PlanParams& pp) {
+  __shared__ uint32_t sh[4 * kPlanWaves];
+  __shared__ int s_hand;
+  const int tid = threadIdx.x;
+  const int64_t L = u.dyn[0], M = u.dyn[1];
+  const int32_t round = (int32_t)u.dyn[2];
+  const bool off = pp.mode == 0;
+  const int hand = off ? *u.hand : 0;
+  const int64_t nw = (L + 31) / 32;
+  const auto sel = s.selmask;
+  const auto hit = s.hitmask;
+
+  // Union, miss, ring and hit counts per word, scanned in word (= position) order.
+  const int64_t per = (nw + kPlanThreads - 1) / kPlanThreads;
+  const int64_t w0 = min(nw, (int64_t)tid * per), w1 = min(nw, w0 + per);
+  uint4 c = make_uint4(0u, 0u, 0u, 0u);        // union, miss, ring, hit
+  for (int64_t w = w0; w < w1; ++w) {
+    const uint32_t sw = sel[w];
+    if (!sw) continue;
+    const uint32_t hw = off ? hit[w] : 0u;
+    const uint32_t rw = off ? (sw & ring_bits(w, M)) : 0u;
+    c.x += __popc(sw);
+    if (off) {
+      c.y += __popc(sw & ~hw & ~rw);
+      c.z += __popc(rw);
+      c.w += __popc(hw);
+    }
+  }
+  uint4 tot;
+  const uint4 base = block_scan4<kPlanWaves>(c, &tot, sh);
+  const uint32_t U = tot.x, n_miss = tot.y, n_ring = tot.z, n_hit = tot.w;
+  {
+    uint32_t bu = base.x, bm = base.y;
+    for (int64_t w = w0; w < w1; ++w) {
+      const uint32_t sw = sel[w];
+      s.base_u[w] = bu;
+      s.base_m[w] = bm;
+      if (!sw) continue;
+      const uint32_t hw = off ? hit[w] : 0u;
+      const uint32_t rw = off ? (sw & ring_bits(w, M)) : 0u;
+      bu += __popc(sw);
+      if (off) bm += __popc(sw & ~hw & ~rw);
+    }
+  }
+
+  // Unpinned slots in ring order from the hand; victim[k] for the misses that get one.
+  uint32_t n_assigned = 0;
+  if (tid == 0) s_hand = hand;
+  if (off) {
+    const int S = pp.S, nsw = pp.s_words;
+    const int sper = (nsw + kPlanThreads - 1) / kPlanThreads;
+    const int j0 = min(nsw, tid * sper), j1 = min(nsw, j0 + sper);
+    uint32_t cnt = 0;
+    for (int j = j0; j < j1; ++j) {
+      uint32_t bits = 0;
+      if ((S & 31) == 0) {
+        // 32 offsets from a word-aligned ring: two pinned words, funnel-shifted
+        const int v0 = (hand + 32 * j) % S;
+        const int wa = v0 >> 5, sa = v0 & 31;
+        const uint32_t lo = s.pinmask[wa];
+        const uint32_t hi = sa ? s.pinmask[(wa + 1) % nsw] : 0u;
+        bits = ~(sa ? ((lo >> sa) | (hi << (32 - sa))) : lo);
+      } else {
+        int last = -1;
+        uint32_t pw = 0;
+        for (int i = 0; i < 32; ++i) {
+          const int o = 32 * j + i;
+          if (o >= S) break;
+          const int v = (hand + o) % S;
+          if ((v >> 5) != last) { last = v >> 5; pw = s.pinmask[last]; }
+          if (!((pw >> (v & 31)) & 1u)) bits |= 1u << i;
+        }
+      }
+      s.upw[j] = bits;
+      cnt += __popc(bits);
+    }
+    uint32_t n_unpinned;
+    uint32_t k = block_scan<kPlanWaves>(cnt, &n_unpinned, sh);
+    n_assigned = min(n_miss, n_unpinned);
+    for (int j = j0; j < j1 && k < n_assigned; ++j) {
+      uint32_t bits = s.upw[j];
+      while (bits && k < n_assigned) {
+        const int b = __ffs(bits) - 1;
+        bits &= bits - 1;
+        const int v = (hand + 32 * j + b) % S;
+        s.victim[k] = v;
+        if (k + 1 == n_assigned) s_hand = (v + 1) % S;
+        ++k;
+      }
+    }
+    __syncthreads();                                   // every pinned word has been read
+    for (int j = tid; j < nsw; j += kPlanThreads) s.pinmask[j] = 0;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int64_t rb = 656;
+    const int64_t noslot = off ? (int64_t)n_miss - n_assigned : 0;
+    int64_t cn[8];
+    cn[0] = U;
+    cn[1] = off ? n_hit : 0;
+    cn[2] = off ? n_ring : 0;
+    cn[3] = n_assigned;
+    cn[4] = noslot;
+    cn[5] = 0;                                         // evictions: added by the gather
+    cn[6] = off ? ((int64_t)n_assigned + noslot) * rb : 0;
+    cn[7] = off ? 0 : U;
+    for (int q = 0; q < 8; ++q) {
+      s.counters[q] = cn[q];
+      u.totals[q] += cn[q];
+    }
+    int64_t wb = -1;
+    if (off && L - M >= pp.ring_rows) wb = M;
+    s.info[kInfoUnion] = U;
+    s.info[kInfoWriteback] = wb;
+    s.info[kInfoAssigned] = n_assigned;
+    s.info[kInfoRound] = round;
+    s.info[kInfoM] = M;
+    s.info[kInfoHand] = hand;
+    if (off) {
+      *u.hand = s_hand;
+      if (wb >= 0) u.dyn[1] = M + pp.ring_rows;
+    }
+    u.dyn[2] = round + 1;
+  }
+}
+
+// Called by every workgroup (one per query row) of a sequence at the end of its
+// selection; the last of the n_rows workgroups to arrive runs the plan.  The
+// workgroup barrier orders every thread's marks before thread 0's arrival; the
+// arrival is an acquire-release atomic at device scope, so the marks of every
+// earlier arrival are visible to the last workgroup (one wave per workgroup
+// carries the device-scope cache maintenance).  No workgroup waits for another.
+__device__ inline void plan_if_last(const UnitG& u, const ScratchG& s, const PlanParams& pp, uint32_t n_rows) {
+  __shared__ uint32_t s_last;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(s.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev + 1 == n_rows;
+    s_last = last ? 1u : 0u;
+    if (last) __hip_atomic_store(s.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  gather_plan_block(u, s, pp);
+}
+
+}  // namespace dsa

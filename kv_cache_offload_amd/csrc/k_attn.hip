@@ -69,11 +69,11 @@ template <int NW>
 struct RawBlock {
   static constexpr int kLatTasks = (kSub / 8) * 64 / (NW * 64);   // per thread
   static constexpr int kSideTasks = kSub * 8 / (NW * 64);
-  uint2 lat[kLatTasks][8];
+  u32x2 lat[kLatTasks][8];
   uint16_t scl[kSideTasks];
-  uint4 rope[kSideTasks];
+  u32x4 rope[kSideTasks];
 
-  __device__ inline void load(const uint8_t* compact, const int* idx, int64_t rb, int tid) {
+  __device__ inline void load(const DSA_GLOBAL uint8_t* compact, const int* idx, int64_t rb, int tid) {
 #pragma unroll
     for (int q = 0; q < kLatTasks; ++q) {
       const int task = tid + q * NW * 64;
@@ -81,7 +81,9 @@ struct RawBlock {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int id = idx[jg * 8 + e];
-        lat[q][e] = id >= 0 ? *reinterpret_cast<const uint2*>(compact + id * rb + dc * 8) : make_uint2(0u, 0u);
+        // unconditional loads (row 0 always exists); rows past the split's end are
+        // masked out of the softmax, so their values never reach the output
+        lat[q][e] = *reinterpret_cast<const DSA_GLOBAL u32x2*>(compact + (id >= 0 ? id : 0) * rb + dc * 8);
       }
     }
 #pragma unroll
@@ -89,8 +91,9 @@ struct RawBlock {
       const int task = tid + q * NW * 64;
       const int j = task >> 3, g = task & 7;
       const int id = idx[j];
-      scl[q] = id >= 0 ? *reinterpret_cast<const uint16_t*>(compact + id * rb + 512 + 2 * g) : (uint16_t)0;
-      rope[q] = id >= 0 ? *reinterpret_cast<const uint4*>(compact + id * rb + 528 + 16 * g) : make_uint4(0u, 0u, 0u, 0u);
+      const int64_t row = (id >= 0 ? id : 0) * rb;
+      scl[q] = *reinterpret_cast<const DSA_GLOBAL uint16_t*>(compact + row + 512 + 2 * g);
+      rope[q] = *reinterpret_cast<const DSA_GLOBAL u32x4*>(compact + row + 528 + 16 * g);
     }
   }
 
@@ -129,7 +132,7 @@ struct RawBlock {
       const int task = tid + q * NW * 64;
       const int j = task >> 3, g = task & 7;
       sclf[j * 8 + g] = f16_bits_to_f32(scl[q]);
-      *reinterpret_cast<uint4*>(rope_jd + j * kRopeStride + 8 * g) = rope[q];
+      *reinterpret_cast<u32x4*>(rope_jd + j * kRopeStride + 8 * g) = rope[q];
     }
   }
 };
@@ -147,7 +150,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   const int split = blockIdx.x, seq = blockIdx.z;
   const int n_hg = ka.H / (NW * 16);
   const int r = blockIdx.y / n_hg, hg = blockIdx.y % n_hg;
-  const SeqScratch s = a.scr[seq];
+  const ScratchG s = scratch_of(a, seq);
   const int n_sel = s.sel_n[r];
   const int j_begin = split * ka.split_rows;
   if (j_begin >= n_sel) return;
@@ -160,8 +163,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
 
   // Compact-row index of every selected row of this split (the map: union index of
   // the selected position, from the per-position index the gather wrote).
-  const int* sel = s.sel + (int64_t)r * ka.K;
-  int* map = s.map + (int64_t)r * ka.K;
+  const auto sel = s.sel + (int64_t)r * ka.K;
+  const auto map = s.map + (int64_t)r * ka.K;
   const int64_t U = s.info[kInfoUnion];
   for (int j = tid; j < ka.split_rows; j += NW * 64) {
     int idx = -1;
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
         const bf16x8 b = *reinterpret_cast<const bf16x8*>(rope_jd + jrow * kRopeStride + 32 * kk + 8 * g4);
         ra = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[16 + kk], b, ra, 0, 0, 0);
       }
-      const bool valid = jrow < nrows;
+      const bool valid = jrow < nrows && s_idx[jb - j_begin + jrow] >= 0;
 #pragma unroll
       for (int v = 0; v < 4; ++v) lg[nt][v] = valid ? (acc_all[v] + ra[v]) * ka.scale_log2 : -INFINITY;
     }
@@ -306,7 +309,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     for (int v = 0; v < 4; ++v) {
       const int h = h0 + 4 * g4 + v;
       const int64_t base = ((int64_t)r * ka.ns_stride + split) * H + h;
-      float* dst = s.part_o + base * 512;
+      const auto dst = s.part_o + base * 512;
 #pragma unroll
       for (int nt2 = 0; nt2 < 32; ++nt2) dst[nt2 * 16 + l16] = o[nt2][v];
       if (l16 == 0) {
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(MergeKArgs ka) {
   __shared__ float wgt[kMaxSplits];
   const StepArgs& a = ka.a;
   const int h = blockIdx.x, r = blockIdx.y, seq = blockIdx.z;
-  const SeqScratch s = a.scr[seq];
+  const ScratchG s = scratch_of(a, seq);
   const int used = (s.sel_n[r] + ka.split_rows - 1) / ka.split_rows;
   const int H = ka.H;
   // splits' (max, sum) in the first wave, one split per lane (used <= 64)
@@ -353,10 +356,10 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(MergeKArgs ka) {
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
   for (int sp = 0; sp < used; ++sp) {
-    const float4 v = *reinterpret_cast<const float4*>(
+    const f32x4 v = *reinterpret_cast<const DSA_GLOBAL f32x4*>(
         s.part_o + (((int64_t)r * ka.ns_stride + sp) * H + h) * 512 + d);
     const float w = wgt[sp];
-    acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+    acc.x += w * v[0]; acc.y += w * v[1]; acc.z += w * v[2]; acc.w += w * v[3];
   }
   *reinterpret_cast<float4*>(ka.out + (((int64_t)seq * a.R + r) * H + h) * 512 + d) = acc;
 }
@@ -379,18 +382,16 @@ hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_l
   AttnKArgs ka{a, q_lat, q_rope, out, g.top_k, g.heads, split_rows, nsplit, g.nsplit_max, g.row_bytes,
                g.max_positions, g.softmax_scale * 1.4426950408889634f};
   dim3 grid((unsigned)nsplit, (unsigned)(a.R * (g.heads / (16 * nw))), (unsigned)a.n_seqs);
-  if (nw == 1) hipLaunchKernelGGL(attn_kernel<1>, grid, dim3(64), 0, st, ka);
-  else hipLaunchKernelGGL(attn_kernel<2>, grid, dim3(128), 0, st, ka);
-  return hipGetLastError();
+  if (nw == 1) return launch_k(attn_kernel<1>, grid, dim3(64), 0, st, ka);
+  return launch_k(attn_kernel<2>, grid, dim3(128), 0, st, ka);
 }
 
 hipError_t launch_attn_merge(const Geometry& g, const StepArgs& a, float* out, hipStream_t st) {
   const int split_rows = attn_split_rows(g, a);
   if ((g.top_k + split_rows - 1) / split_rows == 1) return hipSuccess;
   MergeKArgs ka{a, out, g.heads, split_rows, g.nsplit_max};
-  hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)g.heads, (unsigned)a.R, (unsigned)a.n_seqs), dim3(128), 0,
-                     st, ka);
-  return hipGetLastError();
+  return launch_k(attn_merge_kernel, dim3((unsigned)g.heads, (unsigned)a.R, (unsigned)a.n_seqs), dim3(128), 0, st,
+                  ka);
 }
 
 }  // namespace dsa

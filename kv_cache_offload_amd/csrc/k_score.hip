@@ -72,8 +72,8 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreKArgs ka) {
   extern __shared__ __align__(16) uint16_t sq[];   // [MT*32][kQStride], weights, digit histograms
   const StepArgs& a = ka.a;
   const int seq = blockIdx.y;
-  const UnitDev u = a.units[a.unit_base + seq];
-  const SeqScratch s = a.scr[seq];
+  const UnitG u = unit_of(a, seq);
+  const ScratchG s = scratch_of(a, seq);
   const int64_t L = u.dyn[0];
   const int R = a.R;
   const int M = R * HI;
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreKArgs ka) {
   {
     const int64_t t = first_sub * 32 + n;
     if (t < L) {
-      const bf16x8* kp = reinterpret_cast<const bf16x8*>(u.keys + t * 128 + 64 * hf);
+      const DSA_GLOBAL bf16x8* kp = reinterpret_cast<const DSA_GLOBAL bf16x8*>(u.keys + t * 128 + 64 * hf);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) b[ks] = kp[ks];
     } else {
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreKArgs ka) {
     sw[m] = m < M ? ka.w[(int64_t)seq * M + m] : 0.0f;
   __syncthreads();
 
-  float* scores = s.scores;
+  const auto scores = s.scores;
 
   for (int si = 0; si < ka.subs_per_wave; ++si) {
     const int64_t t0 = (first_sub + si) * 32;
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreKArgs ka) {
     // B fragments: 8 k-steps x 16 bytes of key t (the first tile's are already loaded).
     if (si > 0) {
       if (t < L) {
-        const bf16x8* kp = reinterpret_cast<const bf16x8*>(u.keys + t * 128 + 64 * hf);
+        const DSA_GLOBAL bf16x8* kp = reinterpret_cast<const DSA_GLOBAL bf16x8*>(u.keys + t * 128 + 64 * hf);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) b[ks] = kp[ks];
       } else {
@@ -198,9 +198,9 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreKArgs ka) {
     if (!v) continue;
     const int r = w / (kRadixBins / 2), d = 2 * (w % (kRadixBins / 2));
     const int rep = blockIdx.x % kHistReps;
-    uint32_t* gh = s.hist0 + ((int64_t)rep * ka.r_max + r) * kRadixBins + d;
-    if (v & 0xFFFFu) atomicAdd(gh, v & 0xFFFFu);
-    if (v >> 16) atomicAdd(gh + 1, v >> 16);
+    const auto gh = s.hist0 + ((int64_t)rep * ka.r_max + r) * kRadixBins + d;
+    if (v & 0xFFFFu) g_add(gh, v & 0xFFFFu);
+    if (v >> 16) g_add(gh + 1, v >> 16);
   }
 }
 
@@ -235,13 +235,12 @@ hipError_t launch_score(const Geometry& g, const StepArgs& a, const uint16_t* q,
                      (size_t)a.R * (kRadixBins / 2) * sizeof(uint32_t);
   dim3 grid((unsigned)blocks, (unsigned)a.n_seqs), block(256);
   switch (g.index_heads) {
-    case 4: hipLaunchKernelGGL(score_kernel<4>, grid, block, lds, st, ka); break;
-    case 8: hipLaunchKernelGGL(score_kernel<8>, grid, block, lds, st, ka); break;
-    case 16: hipLaunchKernelGGL(score_kernel<16>, grid, block, lds, st, ka); break;
-    case 32: hipLaunchKernelGGL(score_kernel<32>, grid, block, lds, st, ka); break;
+    case 4: return launch_k(score_kernel<4>, grid, block, lds, st, ka);
+    case 8: return launch_k(score_kernel<8>, grid, block, lds, st, ka);
+    case 16: return launch_k(score_kernel<16>, grid, block, lds, st, ka);
+    case 32: return launch_k(score_kernel<32>, grid, block, lds, st, ka);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace dsa

@@ -9,135 +9,50 @@
 // while the scores are still in registers (in kHistReps replicas, so that the
 // few bins integer-valued scores crowd into do not serialise the atomics).
 // Then, per query row:
-//   * refine (one workgroup per 4096-position chunk): finds the first-digit bin
-//     b0 that holds the K-th largest key and histograms the second digit of the
-//     keys in that bin;
-//   * collect (same grid): finds b1 likewise and writes, in position order, the
-//     (key, position) of every key whose first two digits are at or above
-//     (b0, b1) -- every position that can be selected, barely more than K;
-//   * resolve (one 1024-thread workgroup per row): loads the candidates into LDS,
-//     histograms the last digit to get the threshold key tau and the number E of
-//     keys equal to tau that are taken, and writes the selection in ascending
-//     position order with an ordered block scan: every key above tau plus the
-//     lowest-position keys equal to tau.  Each selected position is marked in the
-//     step's union bitmap and classified against the hot cache on the spot.  If
-//     the candidates do not fit in LDS (e.g. nearly all scores equal), the same
-//     passes stream the candidate list from global memory instead.
-#include "dsa_internal.h"
+//   * collect (one 256-thread workgroup per 4096-position chunk): finds the
+//     first-digit bin b0 that holds the K-th largest key and writes, in
+//     position order, the (key, position) of every key whose first digit is at
+//     or above b0 -- every position that can be selected;
+//     for histories longer than 65,536 positions that list would be long, so a
+//     refine pass (same grid) first histograms the second digit of the keys in
+//     bin b0, and collect keeps only keys whose first two digits are at or
+//     above (b0, b1): barely more than K;
+//   * resolve (one 1024-thread workgroup per row): loads the candidates into
+//     LDS, finds the remaining digits with LDS histograms -- the threshold key
+//     tau and the number E of keys equal to tau that are taken -- and writes
+//     the selection in ascending position order with an ordered block scan:
+//     every key above tau plus the E lowest-position keys equal to tau.  Each
+//     selected position is marked in the step's union bitmap and classified
+//     against the hot cache.  If the candidates do not fit in LDS (nearly all
+//     scores equal), the same passes stream the candidate lists from global
+//     memory instead.  The last row of each sequence to finish runs the
+//     gather plan (gather_plan.h).
+//
+// Memory-level parallelism: gathers whose addresses are known are issued
+// together, unconditionally (indices clamped into the buffer), and pinned with
+// keep() before any of them is used, so a batch costs one memory round trip.
+#include "gather_plan.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kCollectThreads = 256;
-constexpr int kPerThread = kTopkChunk / kCollectThreads;   // 16 consecutive positions per thread
+constexpr int kPartThreads = 256;
+constexpr int kPerThread = kTopkChunk / kPartThreads;     // 16 consecutive positions per thread
 constexpr int kResolveThreads = 1024;
 constexpr int kResolveWaves = kResolveThreads / 64;
-constexpr int kCandCap = 16384;                            // candidates held in LDS
-constexpr int kTile = kResolveThreads * 16;                 // emit tile (16 per thread)
+constexpr int kCandCap = 12288;                            // candidates held in LDS
+constexpr int kTile = kResolveThreads * 16;                // emit tile (16 per thread)
 constexpr int kMaxChunks = 1024;                           // chunk offsets kept in LDS
+constexpr int kMaxK = 4096;
+constexpr int kOneDigitMax = 65536;                        // collect on the first digit up to this length
+static_assert(kResolveThreads == kPlanThreads, "the plan runs on a resolve workgroup");
 
-__device__ inline uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ inline uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
-
-// Exclusive block scan (thread order) for NW waves; total in *tot.
-template <int NW>
-__device__ inline uint32_t block_scan(uint32_t v, uint32_t* tot, uint32_t* sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t inc = wave_incl_scan(v, lane);
-  if (lane == 63) sh[wave] = inc;
-  __syncthreads();
-  uint32_t base = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    uint32_t x = sh[w];
-    base += (w < wave) ? x : 0u;
-    all += x;
-  }
-  __syncthreads();
-  *tot = all;
-  return base + inc - v;
-}
-
-// The bin holding the k-th largest key among those counted in hist[NBINS] (summed
-// over REPS replicas `stride` apart): the largest b with suffix(b) >= k, and the
-// number of keys still needed from it.  Each thread owns NBINS/(64 NW)
-// contiguous bins, loaded together; thread 0 owns the highest.
-template <int NW, int NBINS, int REPS>
-__device__ inline void find_bin(const uint32_t* hist, uint32_t k, uint32_t* sh, int* out_bin,
-                                uint32_t* out_need, int64_t stride = 0) {
-  constexpr int PER = NBINS / (NW * 64);
-  static_assert(PER >= 1 && NBINS % (NW * 64) == 0, "bins per thread");
-  __shared__ int s_bin;
-  __shared__ uint32_t s_need;
-  const int lo = NBINS - ((int)threadIdx.x + 1) * PER;
-  uint32_t c[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) c[e] = 0;
-#pragma unroll
-  for (int q = 0; q < REPS; ++q)
-#pragma unroll
-    for (int e = 0; e < PER; ++e) c[e] += hist[q * stride + lo + e];
-  uint32_t local = 0;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) local += c[e];
-  uint32_t tot;
-  const uint32_t before = block_scan<NW>(local, &tot, sh);   // keys in higher bins
-  if (before < k && before + local >= k) {
-    uint32_t acc = before;
-    bool done = false;
-#pragma unroll
-    for (int e = PER - 1; e >= 0; --e) {
-      if (!done && acc + c[e] >= k) {
-        s_bin = lo + e;
-        s_need = k - acc;
-        done = true;
-      }
-      acc += c[e];
-    }
-  }
-  __syncthreads();
-  *out_bin = s_bin;
-  *out_need = s_need;
-  __syncthreads();
-}
-
-// A selected position joins this step's union (one bit per position), and is
-// classified on the round-start state: a hit needs a slot filled in an earlier
-// round; the hit's slot is pinned for this round.  Rows selecting the same
-// position repeat identical writes.  Up to 16 positions of one thread are marked
-// together, their cache lookups issued at once (two dependent rounds of loads).
-__device__ inline void mark_batch(const UnitDev& u, const SeqScratch& s, const int32_t* pos, const bool* taken,
-                                  bool off, int64_t M, int32_t round) {
-  int32_t v[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    v[e] = -1;
-    if (taken[e]) {
-      atomicOr(&s.selmask[pos[e] >> 5], 1u << (pos[e] & 31));
-      if (off && pos[e] < M) v[e] = u.pos_slot[pos[e]];
-    }
-  }
-  int32_t fr[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) fr[e] = v[e] >= 0 ? u.fill_round[v[e]] : round;
-#pragma unroll
-  for (int e = 0; e < 16; ++e)
-    if (v[e] >= 0 && fr[e] < round) {
-      atomicOr(&s.hitmask[pos[e] >> 5], 1u << (pos[e] & 31));
-      u.pin_round[v[e]] = round;
-      atomicOr(&s.pinmask[v[e] >> 5], 1u << (v[e] & 31));
-    }
+// Keeps x live at this point: a load feeding it cannot be moved into a later
+// branch.  Issue a batch of loads first, then keep() each: the loads stay
+// together and the batch costs one memory round trip.
+template <class T>
+__device__ inline void keep(T& x) {
+  asm volatile("" : "+v"(x));
 }
 
 struct TopkKArgs {
@@ -147,90 +62,155 @@ struct TopkKArgs {
   int K;
   int mode;
   int r_max;
+  int digits;          // 11: candidates by the first digit; 22: by the first two
+  PlanParams plan;
 };
 
-__device__ inline void load_chunk(const float* sc, int64_t t0, float* v) {
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// 16 consecutive scores from t0 (in bounds: rows are P_pad long, P_pad a
+// multiple of the chunk).
+__device__ inline void load_chunk(const DSA_GLOBAL float* sc, int64_t t0, float* v) {
+  f32x4v f[kPerThread / 4];
+#pragma unroll
+  for (int q = 0; q < kPerThread / 4; ++q) f[q] = *reinterpret_cast<const DSA_GLOBAL f32x4v*>(sc + t0 + 4 * q);
 #pragma unroll
   for (int q = 0; q < kPerThread / 4; ++q) {
-    const float4 f = *reinterpret_cast<const float4*>(sc + t0 + 4 * q);   // in bounds: rows are P_pad long
-    v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+    v[4 * q] = f[q].x;
+    v[4 * q + 1] = f[q].y;
+    v[4 * q + 2] = f[q].z;
+    v[4 * q + 3] = f[q].w;
   }
 }
 
-// Second-digit histogram of the keys in the first-digit bin b0.
-__global__ __launch_bounds__(kCollectThreads) void topk_refine_kernel(TopkKArgs ka) {
-  __shared__ uint32_t sh[kCollectThreads / 64];
+// In offload mode a selected position is classified on the round-start state
+// -- a hit needs a slot filled in an earlier round -- and the hit's slot is
+// pinned for this round.  N positions per thread (-1: none), their lookups
+// issued together (two dependent round trips).
+template <int N>
+__device__ inline void classify_and_pin(const UnitG& u, const ScratchG& s, const int32_t* pos, int64_t M,
+                                        int32_t round) {
+  int32_t v[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) v[e] = u.pos_slot[(pos[e] >= 0 && pos[e] < M) ? pos[e] : 0];
+#pragma unroll
+  for (int e = 0; e < N; ++e) keep(v[e]);
+#pragma unroll
+  for (int e = 0; e < N; ++e)
+    if (!(pos[e] >= 0 && pos[e] < M)) v[e] = -1;
+  int32_t fr[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) fr[e] = u.fill_round[v[e] >= 0 ? v[e] : 0];
+#pragma unroll
+  for (int e = 0; e < N; ++e) keep(fr[e]);
+#pragma unroll
+  for (int e = 0; e < N; ++e)
+    if (v[e] >= 0 && fr[e] < round) {
+      g_or(&s.hitmask[pos[e] >> 5], 1u << (pos[e] & 31));
+      u.pin_round[v[e]] = round;
+      g_or(&s.pinmask[v[e] >> 5], 1u << (v[e] & 31));
+    }
+}
+
+// Marks the row's first n selected positions (in LDS) in the union bitmap -- a
+// position several rows select is one union entry -- and, in offload mode,
+// classifies and pins them.  Every thread of the workgroup calls it.
+__device__ inline void mark_selection(const UnitG& u, const ScratchG& s, const int32_t* s_sel, int n, bool offl,
+                                      int64_t M, int32_t round) {
+  constexpr int kPer = kMaxK / kResolveThreads;
+  int32_t pos[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int j = threadIdx.x + e * kResolveThreads;
+    pos[e] = j < n ? s_sel[j] : -1;
+  }
+#pragma unroll
+  for (int e = 0; e < kPer; ++e)
+    if (pos[e] >= 0) g_or(&s.selmask[pos[e] >> 5], 1u << (pos[e] & 31));
+  if (offl) classify_and_pin<kPer>(u, s, pos, M, round);
+}
+
+// Second-digit histogram of the keys in the first-digit bin b0 (long histories).
+__global__ __launch_bounds__(kPartThreads) void topk_refine_kernel(TopkKArgs ka) {
+  __shared__ uint32_t sh[kPartThreads / 64];
   __shared__ uint32_t lh[kRadixBins];
   const StepArgs& a = ka.a;
   const int chunk = blockIdx.x, r = blockIdx.y, seq = blockIdx.z;
-  const UnitDev u = a.units[a.unit_base + seq];
-  const SeqScratch s = a.scr[seq];
+  const UnitG u = unit_of(a, seq);
+  const ScratchG s = scratch_of(a, seq);
   const int64_t L = u.dyn[0];
   const int64_t n_vis = L - a.R + r + 1;
   const int64_t start = (int64_t)chunk * kTopkChunk;
   if (n_vis <= ka.K || start >= n_vis) return;
-  int b0;
-  uint32_t need;
-  find_bin<kCollectThreads / 64, kRadixBins, kHistReps>(s.hist0 + (int64_t)r * kRadixBins, (uint32_t)ka.K, sh, &b0,
-                                                        &need, (int64_t)ka.r_max * kRadixBins);
-  for (int b = threadIdx.x; b < kRadixBins; b += kCollectThreads) lh[b] = 0;
-  __syncthreads();
   const int64_t t0 = start + threadIdx.x * kPerThread;
   float v[kPerThread];
   load_chunk(s.scores + (int64_t)r * ka.p_pad, t0, v);
+  int b0;
+  uint32_t need;
+  find_bin<kPartThreads / 64, kRadixBins, kHistReps>(s.hist0 + (int64_t)r * kRadixBins, (uint32_t)ka.K, sh, &b0,
+                                                     &need, (int64_t)ka.r_max * kRadixBins);
+  for (int b = threadIdx.x; b < kRadixBins; b += kPartThreads) lh[b] = 0;
+  __syncthreads();
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     const uint32_t key = order_key(v[e]);
     if (t0 + e < n_vis && (key >> 21) == (uint32_t)b0) atomicAdd(&lh[(key >> 10) & 2047u], 1u);
   }
   __syncthreads();
-  uint32_t* gh = s.hist1 + (int64_t)r * kRadixBins;
-  for (int b = threadIdx.x; b < kRadixBins; b += kCollectThreads)
-    if (lh[b]) atomicAdd(&gh[b], lh[b]);
+  const auto gh = s.hist1 + (int64_t)r * kRadixBins;
+  for (int b = threadIdx.x; b < kRadixBins; b += kPartThreads)
+    if (lh[b]) g_add(&gh[b], lh[b]);
 }
 
-// Every (key, position) whose first two digits are at or above (b0, b1), in order.
-__global__ __launch_bounds__(kCollectThreads) void topk_collect_kernel(TopkKArgs ka) {
-  __shared__ uint32_t sh[kCollectThreads / 64];
+// Every (key, position) of the chunk whose leading `digits` bits are at or above
+// the threshold digits, in position order.
+__global__ __launch_bounds__(kPartThreads) void topk_collect_kernel(TopkKArgs ka) {
+  __shared__ uint32_t sh[kPartThreads / 64];
   const StepArgs& a = ka.a;
   const int chunk = blockIdx.x, r = blockIdx.y, seq = blockIdx.z;
-  const UnitDev u = a.units[a.unit_base + seq];
-  const SeqScratch s = a.scr[seq];
+  const UnitG u = unit_of(a, seq);
+  const ScratchG s = scratch_of(a, seq);
   const int64_t L = u.dyn[0];
   const int64_t n_vis = L - a.R + r + 1;
   const int64_t start = (int64_t)chunk * kTopkChunk;
   if (n_vis <= ka.K || start >= n_vis) return;
-  int b0, b1;
-  uint32_t need;
-  find_bin<kCollectThreads / 64, kRadixBins, kHistReps>(s.hist0 + (int64_t)r * kRadixBins, (uint32_t)ka.K, sh, &b0,
-                                                        &need, (int64_t)ka.r_max * kRadixBins);
-  find_bin<kCollectThreads / 64, kRadixBins, 1>(s.hist1 + (int64_t)r * kRadixBins, need, sh, &b1, &need);
-  const uint32_t p22 = ((uint32_t)b0 << 11) | (uint32_t)b1;
-
   const int64_t t0 = start + threadIdx.x * kPerThread;
   float v[kPerThread];
   load_chunk(s.scores + (int64_t)r * ka.p_pad, t0, v);
+  int b0;
+  uint32_t need;
+  find_bin<kPartThreads / 64, kRadixBins, kHistReps>(s.hist0 + (int64_t)r * kRadixBins, (uint32_t)ka.K, sh, &b0,
+                                                     &need, (int64_t)ka.r_max * kRadixBins);
+  uint32_t thr = (uint32_t)b0;
+  int shift = 21;
+  if (ka.digits == 22) {
+    int b1;
+    find_bin<kPartThreads / 64, kRadixBins, 1>(s.hist1 + (int64_t)r * kRadixBins, need, sh, &b1, &need);
+    thr = ((uint32_t)b0 << 11) | (uint32_t)b1;
+    shift = 10;
+  }
   uint32_t mine = 0;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e)
-    mine += (t0 + e < n_vis && (order_key(v[e]) >> 10) >= p22) ? 1u : 0u;
+    mine += (t0 + e < n_vis && (order_key(v[e]) >> shift) >= thr) ? 1u : 0u;
   uint32_t tot;
-  uint32_t at = block_scan<kCollectThreads / 64>(mine, &tot, sh);
-  int2* out = s.cand + (int64_t)r * ka.p_pad + start;
+  uint32_t at = block_scan<kPartThreads / 64>(mine, &tot, sh);
+  const auto out = s.cand + (int64_t)r * ka.p_pad + start;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     const uint32_t key = order_key(v[e]);
-    if (t0 + e < n_vis && (key >> 10) >= p22) out[at++] = make_int2((int)key, (int)(t0 + e));
+    if (t0 + e < n_vis && (key >> shift) >= thr) out[at++] = (i32x2){(int)key, (int)(t0 + e)};
   }
   if (threadIdx.x == 0) s.cand_n[(int64_t)r * ka.n_chunks + chunk] = tot;
 }
 
-// Candidate source for the resolve passes: LDS when the candidates fit, else global.
+// Candidate source for the resolve passes: LDS when the candidates fit, else the
+// global per-chunk lists.
 struct CandSrc {
-  const uint32_t* lkey;     // LDS keys (or null)
-  const int32_t* lpos;      // LDS positions (or null)
-  const int2* gcand;        // global candidate lists of the row (by chunk)
-  const uint32_t* off;      // LDS: first candidate index of each chunk
+  const uint32_t* lkey;              // LDS keys (or null)
+  const int32_t* lpos;               // LDS positions (or null)
+  const DSA_GLOBAL i32x2* gcand;     // global candidate lists of the row (by chunk)
+  const uint32_t* off;               // LDS: first candidate index of each chunk
   int n_chunks;
   __device__ inline int chunk_of(uint32_t i) const {   // last chunk with off <= i
     int lo = 0, hi = n_chunks;
@@ -248,7 +228,7 @@ struct CandSrc {
       return;
     }
     const int c = chunk_of(i);
-    const int2 kp = gcand[(int64_t)c * kTopkChunk + (i - off[c])];
+    const i32x2 kp = gcand[(int64_t)c * kTopkChunk + (i - off[c])];
     *key = (uint32_t)kp.x;
     *pos = kp.y;
   }
@@ -256,60 +236,57 @@ struct CandSrc {
 
 __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkKArgs ka) {
   extern __shared__ __align__(16) uint32_t lds[];   // keys[kCandCap], pos[kCandCap]
-  __shared__ uint32_t sh[kResolveWaves];
+  __shared__ uint32_t sh[4 * kResolveWaves];
   __shared__ uint32_t hist[kRadixBins];
   __shared__ uint32_t off[kMaxChunks + 1];
+  __shared__ int32_t s_sel[kMaxK];
   __shared__ uint32_t s_run[2];
   const StepArgs& a = ka.a;
   const int r = blockIdx.x, seq = blockIdx.y, tid = threadIdx.x;
-  const UnitDev u = a.units[a.unit_base + seq];
-  const SeqScratch s = a.scr[seq];
+  const UnitG u = unit_of(a, seq);
+  const ScratchG s = scratch_of(a, seq);
   const int64_t L = u.dyn[0];
   const int64_t M = u.dyn[1];
   const int32_t round = (int32_t)u.dyn[2];
   const bool offl = ka.mode == 0;
   const int K = ka.K;
   const int64_t n_vis = L - a.R + r + 1;
-  int32_t* sel = s.sel + (int64_t)r * K;
-  uint32_t* h0 = s.hist0 + (int64_t)r * kRadixBins;
+  const auto h0 = s.hist0 + (int64_t)r * kRadixBins;
+  const auto h1 = s.hist1 + (int64_t)r * kRadixBins;
+  const int64_t rep_stride = (int64_t)ka.r_max * kRadixBins;
+  const auto sel = s.sel + (int64_t)r * K;
 
-  if (n_vis <= K) {                                  // every visible position is selected
-    for (int64_t t0 = (int64_t)tid * 16; t0 < K; t0 += (int64_t)kResolveThreads * 16) {
-      int32_t poss[16];
-      bool taken[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t t = t0 + e;
-        taken[e] = t < n_vis;
-        poss[e] = (int32_t)t;
-        if (t < K) sel[t] = taken[e] ? (int32_t)t : -1;
-      }
-      mark_batch(u, s, poss, taken, offl, M, round);
-    }
+  if (n_vis <= K) {
+    // every visible position is selected
     for (int b = tid; b < kRadixBins; b += kResolveThreads)
-      for (int q = 0; q < kHistReps; ++q) h0[(int64_t)q * ka.r_max * kRadixBins + b] = 0;
+      for (int q = 0; q < kHistReps; ++q) h0[q * rep_stride + b] = 0;
+    for (int t = tid; t < K; t += kResolveThreads) {
+      sel[t] = t < n_vis ? t : -1;
+      s_sel[t] = t < n_vis ? t : -1;
+    }
+    __syncthreads();
+    mark_selection(u, s, s_sel, (int)n_vis, offl, M, round);
     if (tid == 0) s.sel_n[r] = (int32_t)n_vis;
+    plan_if_last(u, s, ka.plan, (uint32_t)a.R);
     return;
   }
 
-  int b0, b1, b2;
-  uint32_t need;
-  const int64_t rep_stride = (int64_t)ka.r_max * kRadixBins;
-  uint32_t* h1 = s.hist1 + (int64_t)r * kRadixBins;
-  find_bin<kResolveWaves, kRadixBins, kHistReps>(h0, (uint32_t)K, sh, &b0, &need, rep_stride);
-  find_bin<kResolveWaves, kRadixBins, 1>(h1, need, sh, &b1, &need);
-  for (int b = tid; b < kRadixBins; b += kResolveThreads) {   // consumed
-    for (int q = 0; q < kHistReps; ++q) h0[q * rep_stride + b] = 0;
-    h1[b] = 0;
-  }
-
-  // chunk offsets of the candidate lists
+  // chunk counts of the candidate lists (loads issued before the histograms are read)
   const int n_chunks = (int)((n_vis + kTopkChunk - 1) / kTopkChunk);
+  const int per = (n_chunks + kResolveThreads - 1) / kResolveThreads;
+  const int c0 = min(n_chunks, tid * per), c1 = min(n_chunks, c0 + per);
+  uint32_t cnt = 0;
+  for (int c = c0; c < c1; ++c) cnt += s.cand_n[(int64_t)r * ka.n_chunks + c];
+
+  int b0, b1 = 0, b2;
+  uint32_t need;
+  find_bin<kResolveWaves, kRadixBins, kHistReps>(h0, (uint32_t)K, sh, &b0, &need, rep_stride);
+  if (ka.digits == 22) find_bin<kResolveWaves, kRadixBins, 1>(h1, need, sh, &b1, &need);
+  for (int b = tid; b < kRadixBins; b += kResolveThreads) {   // consumed: clear for the next step
+    for (int q = 0; q < kHistReps; ++q) h0[q * rep_stride + b] = 0;
+    if (ka.digits == 22) h1[b] = 0;
+  }
   {
-    const int per = (n_chunks + kResolveThreads - 1) / kResolveThreads;
-    const int c0 = min(n_chunks, tid * per), c1 = min(n_chunks, c0 + per);
-    uint32_t cnt = 0;
-    for (int c = c0; c < c1; ++c) cnt += s.cand_n[(int64_t)r * ka.n_chunks + c];
     uint32_t tot;
     uint32_t base = block_scan<kResolveWaves>(cnt, &tot, sh);
     for (int c = c0; c < c1; ++c) {
@@ -322,31 +299,49 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkKArgs
   const uint32_t C = off[n_chunks];
   uint32_t* lkey = lds;
   int32_t* lpos = reinterpret_cast<int32_t*>(lds + kCandCap);
-  const int2* gcand = s.cand + (int64_t)r * ka.p_pad;
+  const DSA_GLOBAL i32x2* gcand = s.cand + (int64_t)r * ka.p_pad;
   CandSrc src{nullptr, nullptr, gcand, off, n_chunks};
   if (C <= (uint32_t)kCandCap) {
-    // 16 consecutive candidates per thread, loads issued together
-    for (uint32_t i0 = tid * 16; i0 < C; i0 += kResolveThreads * 16) {
-      int c = src.chunk_of(i0);
-      int2 kp[16];
+    // candidate i = k * 1024 + tid, four at a time: loads issued together
+    const uint32_t nk = (C + kResolveThreads - 1) / kResolveThreads;
+    for (uint32_t k0 = 0; k0 < nk; k0 += 4) {
+      i32x2 kp[4];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const uint32_t i = i0 + e;
-        while (c + 1 < n_chunks && off[c + 1] <= i) ++c;
-        kp[e] = i < C ? gcand[(int64_t)c * kTopkChunk + (i - off[c])] : make_int2(0, 0);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t i = (k0 + e) * kResolveThreads + tid;
+        const uint32_t ic = i < C ? i : C - 1;
+        const int c = src.chunk_of(ic);
+        kp[e] = gcand[(int64_t)c * kTopkChunk + (ic - off[c])];
       }
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (i0 + e < C) {
-          lkey[i0 + e] = (uint32_t)kp[e].x;
-          lpos[i0 + e] = kp[e].y;
+      for (int e = 0; e < 4; ++e) keep(kp[e]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t i = (k0 + e) * kResolveThreads + tid;
+        if (i < C) {
+          lkey[i] = (uint32_t)kp[e].x;
+          lpos[i] = kp[e].y;
         }
+      }
     }
     src.lkey = lkey;
     src.lpos = lpos;
   }
   __syncthreads();
 
+  if (ka.digits == 11) {
+    // second digit of the candidates in bin b0
+    for (int b = tid; b < kRadixBins; b += kResolveThreads) hist[b] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < C; i += kResolveThreads) {
+      uint32_t key;
+      int32_t pos;
+      src.get(i, &key, &pos);
+      if ((key >> 21) == (uint32_t)b0) atomicAdd(&hist[(key >> 10) & 2047u], 1u);
+    }
+    __syncthreads();
+    find_bin<kResolveWaves, kRadixBins, 1>(hist, need, sh, &b1, &need);
+  }
   const uint32_t p22 = ((uint32_t)b0 << 11) | (uint32_t)b1;
   for (int b = tid; b < 1024; b += kResolveThreads) hist[b] = 0;
   __syncthreads();
@@ -359,7 +354,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkKArgs
   __syncthreads();
   find_bin<kResolveWaves, 1024, 1>(hist, need, sh, &b2, &need);
   const uint32_t tau = (p22 << 10) | (uint32_t)b2;
-  const uint32_t E = need;
+  const uint32_t E = need;                             // keys equal to tau that are taken
 
   // ordered emit, 16 consecutive candidates per thread per tile
   if (tid == 0) { s_run[0] = 0; s_run[1] = 0; }
@@ -380,34 +375,37 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkKArgs
       }
     }
     const uint32_t run_gt = s_run[0], run_eq = s_run[1];
-    uint32_t tg, te;
-    uint32_t gt = run_gt + block_scan<kResolveWaves>(my_gt, &tg, sh);
-    uint32_t eq = run_eq + block_scan<kResolveWaves>(my_eq, &te, sh);
-    bool taken[16];
+    uint4 tot;
+    const uint4 ex = block_scan4<kResolveWaves>(make_uint4(my_gt, my_eq, 0u, 0u), &tot, sh);
+    uint32_t gt = run_gt + ex.x, eq = run_eq + ex.y;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      taken[e] = false;
-      if (i0 + e < C) {
-        const uint32_t k = keys[e];
-        if (k > tau) {
-          sel[gt + (eq < E ? eq : E)] = poss[e];
-          taken[e] = true;
-          ++gt;
-        } else if (k == tau) {
-          if (eq < E) {
-            sel[gt + eq] = poss[e];
-            taken[e] = true;
-          }
-          ++eq;
-        }
+      const uint32_t k = keys[e];
+      uint32_t at = 0xFFFFFFFFu;
+      if (k > tau) {
+        at = gt + (eq < E ? eq : E);
+        ++gt;
+      } else if (k == tau) {
+        if (eq < E) at = gt + eq;
+        ++eq;
+      }
+      if (at < (uint32_t)K) {                          // always, when the histograms match the keys
+        sel[at] = poss[e];
+        s_sel[at] = poss[e];
       }
     }
-    mark_batch(u, s, poss, taken, offl, M, round);
     __syncthreads();
-    if (tid == 0) { s_run[0] = run_gt + tg; s_run[1] = run_eq + te; }
+    if (tid == 0) { s_run[0] = run_gt + tot.x; s_run[1] = run_eq + tot.y; }
     __syncthreads();
   }
+  mark_selection(u, s, s_sel, K, offl, M, round);
   if (tid == 0) s.sel_n[r] = K;
+  plan_if_last(u, s, ka.plan, (uint32_t)a.R);
+}
+
+TopkKArgs topk_args(const Geometry& g, const StepArgs& a) {
+  return TopkKArgs{a, g.p_pad, g.n_chunks, g.top_k, g.mode, g.r_max, a.l_max <= kOneDigitMax ? 11 : 22,
+                   PlanParams{g.hot_slots, g.s_words, g.ring_rows, g.mode}};
 }
 
 }  // namespace
@@ -417,27 +415,22 @@ hipError_t prepare_topk_kernels() {
                              2 * kCandCap * (int)sizeof(uint32_t));
 }
 
-hipError_t launch_topk_refine(const Geometry& g, const StepArgs& a, hipStream_t st) {
-  TopkKArgs ka{a, g.p_pad, g.n_chunks, g.top_k, g.mode, g.r_max};
+hipError_t launch_topk_partial(const Geometry& g, const StepArgs& a, hipStream_t st) {
+  const TopkKArgs ka = topk_args(g, a);
   const int chunks = (int)((a.l_max + kTopkChunk - 1) / kTopkChunk);
-  dim3 grid((unsigned)chunks, (unsigned)a.R, (unsigned)a.n_seqs);
-  hipLaunchKernelGGL(topk_refine_kernel, grid, dim3(kCollectThreads), 0, st, ka);
-  return hipGetLastError();
+  const dim3 grid((unsigned)chunks, (unsigned)a.R, (unsigned)a.n_seqs);
+  if (ka.digits == 22) {
+    const hipError_t e = launch_k(topk_refine_kernel, grid, dim3(kPartThreads), 0, st, ka);
+    if (e != hipSuccess) return e;
+  }
+  return launch_k(topk_collect_kernel, grid, dim3(kPartThreads), 0, st, ka);
 }
 
-hipError_t launch_topk_collect(const Geometry& g, const StepArgs& a, hipStream_t st) {
-  TopkKArgs ka{a, g.p_pad, g.n_chunks, g.top_k, g.mode, g.r_max};
-  const int chunks = (int)((a.l_max + kTopkChunk - 1) / kTopkChunk);
-  dim3 grid((unsigned)chunks, (unsigned)a.R, (unsigned)a.n_seqs);
-  hipLaunchKernelGGL(topk_collect_kernel, grid, dim3(kCollectThreads), 0, st, ka);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_resolve(const Geometry& g, const StepArgs& a, hipStream_t st) {
-  TopkKArgs ka{a, g.p_pad, g.n_chunks, g.top_k, g.mode, g.r_max};
-  dim3 grid((unsigned)a.R, (unsigned)a.n_seqs);
-  hipLaunchKernelGGL(topk_resolve_kernel, grid, dim3(kResolveThreads), 2 * kCandCap * sizeof(uint32_t), st, ka);
-  return hipGetLastError();
+hipError_t launch_topk_select(const Geometry& g, const StepArgs& a, hipStream_t st) {
+  const TopkKArgs ka = topk_args(g, a);
+  const dim3 grid((unsigned)a.R, (unsigned)a.n_seqs);
+  return launch_k(topk_resolve_kernel, grid, dim3(kResolveThreads), 2 * kCandCap * (uint32_t)sizeof(uint32_t), st,
+                  ka);
 }
 
 }  // namespace dsa

@@ -23,6 +23,10 @@
 
 using namespace dsa;
 
+namespace dsa {
+thread_local LaunchTimer t_launch_timer;
+}  // namespace dsa
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -138,19 +142,31 @@ hipEvent_t take_event(dsa_session* s) {
   return e;
 }
 
+// Runs fn (one or more kernel launches).  With timing on, the group's first
+// dispatch carries a start event and its last a stop event: the events take the
+// dispatches' own timestamps, so the interval is the kernels' execution time.
 template <class F>
-dsa_status timed_launch(dsa_session* s, int kind, hipStream_t st, const char* what, F&& fn) {
+dsa_status timed_launch(dsa_session* s, int kind, const char* what, F&& fn) {
   hipEvent_t a = nullptr, b = nullptr;
   if (s->timing) {
     a = take_event(s);
     b = take_event(s);
     if (!a || !b) return hip_fail(s, hipErrorOutOfMemory, "hipEventCreate");
-    HIPCHK(hipEventRecord(a, st), "hipEventRecord");
+    t_launch_timer.start = a;
+    t_launch_timer.stop = b;
   }
-  HIPCHK(fn(), what);
+  const hipError_t e = fn();
+  const bool launched = t_launch_timer.start == nullptr;   // consumed by a dispatch
+  t_launch_timer.start = nullptr;
+  t_launch_timer.stop = nullptr;
+  HIPCHK(e, what);
   if (s->timing) {
-    HIPCHK(hipEventRecord(b, st), "hipEventRecord");
-    s->timed.push_back({kind, a, b});
+    if (launched) {
+      s->timed.push_back({kind, a, b});
+    } else {
+      s->free_events.push_back(a);
+      s->free_events.push_back(b);
+    }
   }
   return DSA_OK;
 }
@@ -262,7 +278,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     uo[i].totals = take(64);
   }
   struct ScrOff { size_t scores, sel, sel_n, uni, kind, src, fill, map, compact, po, pml, cnt, info,
-                  selmask, hitmask, base_u, base_m, pinmask, upw, upos, victim, victim_old, hist0, hist1, cand,
+                  selmask, hitmask, base_u, base_m, pinmask, upw, upos, victim, done, hist0, hist1, cand,
                   cand_n; };
   std::vector<ScrOff> so(cfg->n_seqs);
   for (int q = 0; q < cfg->n_seqs; ++q) {
@@ -287,7 +303,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     so[q].upw = take((size_t)g.s_words * 4);
     so[q].upos = take((size_t)P * 4);
     so[q].victim = take((size_t)g.s_words * 32 * 4);
-    so[q].victim_old = take((size_t)g.s_words * 32 * 4);
+    so[q].done = take(4);
     so[q].hist0 = take((size_t)kHistReps * g.r_max * kRadixBins * 4);
     so[q].hist1 = take((size_t)g.r_max * kRadixBins * 4);
     so[q].cand = take((size_t)g.r_max * P * 8);
@@ -372,10 +388,10 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     c.upw = reinterpret_cast<uint32_t*>(base + so[q].upw);
     c.upos = reinterpret_cast<int32_t*>(base + so[q].upos);
     c.victim = reinterpret_cast<int32_t*>(base + so[q].victim);
-    c.victim_old = reinterpret_cast<int32_t*>(base + so[q].victim_old);
+    c.done = reinterpret_cast<uint32_t*>(base + so[q].done);
     c.hist0 = reinterpret_cast<uint32_t*>(base + so[q].hist0);
     c.hist1 = reinterpret_cast<uint32_t*>(base + so[q].hist1);
-    c.cand = reinterpret_cast<int2*>(base + so[q].cand);
+    c.cand = reinterpret_cast<i32x2*>(base + so[q].cand);
     c.cand_n = reinterpret_cast<uint32_t*>(base + so[q].cand_n);
     if (hipMemset(c.sel, 0xFF, (size_t)RK * 4) != hipSuccess || hipMemset(c.map, 0xFF, (size_t)RK * 4) != hipSuccess)
       return bail(DSA_E_HIP, "hipMemset");
@@ -417,8 +433,11 @@ dsa_status dsa_append_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t n
   int64_t newM = h.M;
   if (s->g.mode == DSA_KV_OFFLOAD)
     while (h.L + n - newM > s->g.ring_cap) newM += s->g.ring_rows;
-  HIPCHK(launch_append(s->g, s->units[ui], h.L, h.M, newM, n, static_cast<const uint16_t*>(index_keys),
-                       static_cast<const uint8_t*>(rows), stream), "append kernel");
+  if ((st = timed_launch(s, KK_APPEND, "append kernel", [&] {
+         return launch_append(s->g, s->units[ui], h.L, h.M, newM, n, static_cast<const uint16_t*>(index_keys),
+                              static_cast<const uint8_t*>(rows), stream);
+       })) != DSA_OK)
+    return st;
   const bool moved = newM != h.M;
   h.L += n;
   h.M = s->g.mode == DSA_KV_OFFLOAD ? newM : h.L;
@@ -482,15 +501,13 @@ dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq, 
   const uint16_t* iq = static_cast<const uint16_t*>(index_q);
   const uint16_t* ql = static_cast<const uint16_t*>(q_latent);
   const uint16_t* qr = static_cast<const uint16_t*>(q_rope);
-  if ((st = timed_launch(s, KK_SCORE, stream, "score kernel", [&] { return launch_score(g, a, iq, index_w, stream); })) != DSA_OK) return st;
-  if ((st = timed_launch(s, KK_TOPK_COLLECT, stream, "top-k refine", [&] { return launch_topk_refine(g, a, stream); })) != DSA_OK) return st;
-  if ((st = timed_launch(s, KK_TOPK_COLLECT, stream, "top-k collect", [&] { return launch_topk_collect(g, a, stream); })) != DSA_OK) return st;
-  if ((st = timed_launch(s, KK_TOPK_RESOLVE, stream, "top-k resolve", [&] { return launch_topk_resolve(g, a, stream); })) != DSA_OK) return st;
-  if ((st = timed_launch(s, KK_SCAN, stream, "gather scan", [&] { return launch_gather_scan(g, a, stream); })) != DSA_OK) return st;
-  if ((st = timed_launch(s, KK_ASSIGN, stream, "gather assign", [&] { return launch_gather_assign(g, a, stream); })) != DSA_OK) return st;
-  if ((st = timed_launch(s, KK_COPY, stream, "gather copy", [&] { return launch_copy(g, a, stream); })) != DSA_OK) return st;
-  if ((st = timed_launch(s, KK_ATTN, stream, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream); })) != DSA_OK) return st;
-  if ((st = timed_launch(s, KK_MERGE, stream, "attention merge", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_SCORE, "score kernel", [&] { return launch_score(g, a, iq, index_w, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_TOPK_PARTIAL, "top-k collect", [&] { return launch_topk_partial(g, a, stream); })) != DSA_OK)
+    return st;
+  if ((st = timed_launch(s, KK_TOPK_SELECT, "top-k resolve", [&] { return launch_topk_select(g, a, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_GATHER, "gather", [&] { return launch_gather(g, a, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_MERGE, "attention merge", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK) return st;
   s->last_layer = layer;
   s->last_R = R;
   for (int q = 0; q < n_seqs; ++q) {
@@ -621,7 +638,18 @@ dsa_status dsa_debug_get(dsa_session* s, int32_t layer, int32_t seq, int32_t ite
 dsa_status dsa_set_kernel_timing(dsa_session* s, int32_t enable) {
   dsa_status st = entry(s);
   if (st != DSA_OK) return st;
-  s->timing = enable != 0;
+  s->timing = enable > 0;
+  if (enable > 0) {
+    // pre-create the events of `enable` decode steps, so timed calls create none
+    if (enable > (1 << 18)) return fail(s, DSA_E_INVALID, "timing reserve above 262,144 steps");
+    DeviceGuard dg(s->device);
+    const size_t want = (size_t)enable * DSA_KERNEL_KINDS * 2;
+    while (s->free_events.size() < want) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return hip_fail(s, hipErrorOutOfMemory, "hipEventCreate");
+      s->free_events.push_back(e);
+    }
+  }
   return DSA_OK;
 }
 
