@@ -42,7 +42,7 @@ constexpr int kGatherThreads = 256;
 
 struct GatherKArgs {
   StepArgs a;
-  int S, ring_cap, ring_rows, mode, row_bytes;
+  int S, ring_cap, ring_rows, mode, row_bytes, K;
   int max_union;                        // R_max * K: compact rows in the scratch
   int64_t max_positions;
 };
@@ -135,7 +135,9 @@ __global__ __launch_bounds__(kGatherThreads) void gather_assign_kernel(GatherKAr
 
 // Row copies, one thread per 16-byte piece: compact <- slot / ring / host
 // mirror / HBM row store; a miss that got a slot fills the slot too.  Then the
-// ring writeback of the 64 oldest pending rows when a batch is due.
+// ring writeback of the 64 oldest pending rows when a batch is due, and the
+// map: the compact row of every (query row, selected index), -1 past the
+// row's selection.
 __global__ __launch_bounds__(kGatherThreads) void copy_kernel(GatherKArgs ka) {
   const StepArgs& a = ka.a;
   const int seq = blockIdx.y;
@@ -145,7 +147,9 @@ __global__ __launch_bounds__(kGatherThreads) void copy_kernel(GatherKArgs ka) {
   const int64_t wb = s.info[kInfoWriteback];
   const int64_t rb = ka.row_bytes;
   const int64_t n_gather = U * kCopyChunks16;
-  const int64_t total = n_gather + (wb >= 0 ? (int64_t)ka.ring_rows * kCopyChunks16 : 0);
+  const int64_t n_wb = wb >= 0 ? (int64_t)ka.ring_rows * kCopyChunks16 : 0;
+  const int64_t n_map = (int64_t)a.R * ka.K;
+  const int64_t total = n_gather + n_wb + n_map;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
        t += (int64_t)gridDim.x * blockDim.x) {
     if (t < n_gather) {
@@ -166,11 +170,18 @@ __global__ __launch_bounds__(kGatherThreads) void copy_kernel(GatherKArgs ka) {
       *reinterpret_cast<DSA_GLOBAL u32x4*>(s.compact + x * rb + c * 16) = v;
       if (kind == SRC_MISS && f >= 0 && f < ka.S)
         *reinterpret_cast<DSA_GLOBAL u32x4*>(u.slots + (int64_t)f * rb + c * 16) = v;
-    } else {
+    } else if (t < n_gather + n_wb) {
       const int64_t i = t - n_gather;
       const int64_t p = wb + i / kCopyChunks16, c = i % kCopyChunks16;
       const u32x4 v = *reinterpret_cast<const DSA_GLOBAL u32x4*>(u.ring + (p % ka.ring_cap) * rb + c * 16);
       *reinterpret_cast<DSA_GLOBAL u32x4*>(u.rows + p * rb + c * 16) = v;
+    } else {
+      const int64_t i = t - n_gather - n_wb;
+      const int r = (int)(i / ka.K), j = (int)(i % ka.K);
+      const int32_t p = s.sel[i];
+      int32_t idx = -1;
+      if (j < s.sel_n[r] && p >= 0 && p < ka.max_positions) idx = s.upos[p];
+      s.map[i] = (idx >= 0 && idx < U) ? idx : -1;
     }
   }
 }
@@ -265,14 +276,15 @@ unsigned grid_for(int64_t work, int64_t cap = 4096) {
 }  // namespace
 
 hipError_t launch_gather(const Geometry& g, const StepArgs& a, hipStream_t st) {
-  GatherKArgs ka{a, g.hot_slots, g.ring_cap, g.ring_rows, g.mode, g.row_bytes, g.r_max * g.top_k, g.max_positions};
+  GatherKArgs ka{a, g.hot_slots, g.ring_cap, g.ring_rows, g.mode, g.row_bytes, g.top_k, g.r_max * g.top_k,
+                 g.max_positions};
   const int64_t words = (a.l_max + 31) / 32;
   const int64_t waves = (words + 1) / 2;
   const int64_t blocks = (waves + 3) / 4;
   hipError_t e = launch_k(gather_assign_kernel, dim3((unsigned)blocks, (unsigned)a.n_seqs), dim3(kGatherThreads), 0,
                           st, ka);
   if (e != hipSuccess) return e;
-  const int64_t work = (int64_t)a.R * g.top_k * kCopyChunks16 + (int64_t)g.ring_rows * kCopyChunks16;
+  const int64_t work = (int64_t)a.R * g.top_k * (kCopyChunks16 + 1) + (int64_t)g.ring_rows * kCopyChunks16;
   return launch_k(copy_kernel, dim3(grid_for(work, 2048), (unsigned)a.n_seqs), dim3(kGatherThreads), 0, st, ka);
 }
 
