@@ -81,6 +81,7 @@ struct ScratchT {
   P<i32x2> cand;            // [R_max][P_pad] top-k candidates (key, position), by chunk, in position order
   P<uint32_t> cand_n;       // [R_max][n_chunks] candidates per chunk
   P<uint32_t> done;         // [1] rows of the step that finished their selection (reset by the last)
+  P<uint32_t> arrive;       // [R_max] chunks of each row that finished their candidate lists (reset by the last)
 };
 
 using UnitDev = UnitT<HostPtr>;
@@ -156,8 +157,9 @@ __device__ inline void g_add(DSA_GLOBAL int64_t* p, int64_t v) {
 // ---- launchers (each returns the hipError_t of its launch) ----
 hipError_t launch_score(const Geometry& g, const StepArgs& a, const uint16_t* q, const float* w,
                         hipStream_t st);
-// Top-K: collect (+ refine for long histories) over chunks, then resolve per
-// row; the resolve ends with the gather plan, run by the last row of each
+// Top-K: a refine pass over chunks for long histories (partial), then the
+// select kernel: candidate lists per chunk, resolved per row by the row's last
+// chunk to finish; it ends with the gather plan, run by the last row of each
 // sequence.
 hipError_t launch_topk_partial(const Geometry& g, const StepArgs& a, hipStream_t st);
 hipError_t launch_topk_select(const Geometry& g, const StepArgs& a, hipStream_t st);

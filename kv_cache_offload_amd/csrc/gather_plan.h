@@ -160,10 +160,11 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
 
 // Called by every workgroup (one per query row) of a sequence at the end of its
 // selection; the last of the n_rows workgroups to arrive runs the plan.  The
-// workgroup barrier orders every thread's marks before thread 0's arrival; the
-// arrival is an acquire-release atomic at device scope, so the marks of every
-// earlier arrival are visible to the last workgroup (one wave per workgroup
-// carries the device-scope cache maintenance).  No workgroup waits for another.
+// workgroup barrier (a workgroup-scope release and acquire) orders every wave's
+// marks before thread 0's arrival, an acquire-release atomic at device scope;
+// by transitivity the marks of every earlier arrival are visible to every wave
+// of the last workgroup after its barrier.  Only one wave per workgroup carries
+// the device-scope cache maintenance.  No workgroup waits for another.
 __device__ inline void plan_if_last(const UnitG& u, const ScratchG& s, const PlanParams& pp, uint32_t n_rows) {
   __shared__ uint32_t s_last;
   __syncthreads();

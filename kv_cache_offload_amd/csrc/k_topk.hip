@@ -8,25 +8,27 @@
 // 11, 11 and 10 bits.  The first digit's histogram is built by the score kernel
 // while the scores are still in registers (in kHistReps replicas, so that the
 // few bins integer-valued scores crowd into do not serialise the atomics).
-// Then, per query row:
-//   * collect (one 256-thread workgroup per 4096-position chunk): finds the
-//     first-digit bin b0 that holds the K-th largest key and writes, in
-//     position order, the (key, position) of every key whose first digit is at
-//     or above b0 -- every position that can be selected;
+// Then one select kernel, one 1024-thread workgroup per (4096-position chunk,
+// query row):
+//   * every workgroup finds the first-digit bin b0 that holds the K-th largest
+//     key and writes, in position order, the (key, position) of every key of
+//     its chunk whose first digit is at or above b0 -- every position that can
+//     be selected -- and adds the second-digit histogram of its keys in b0;
 //     for histories longer than 65,536 positions that list would be long, so a
-//     refine pass (same grid) first histograms the second digit of the keys in
-//     bin b0, and collect keeps only keys whose first two digits are at or
-//     above (b0, b1): barely more than K;
-//   * resolve (one 1024-thread workgroup per row): loads the candidates into
-//     LDS, finds the remaining digits with LDS histograms -- the threshold key
-//     tau and the number E of keys equal to tau that are taken -- and writes
-//     the selection in ascending position order with an ordered block scan:
-//     every key above tau plus the E lowest-position keys equal to tau.  Each
-//     selected position is marked in the step's union bitmap and classified
-//     against the hot cache.  If the candidates do not fit in LDS (nearly all
-//     scores equal), the same passes stream the candidate lists from global
-//     memory instead.  The last row of each sequence to finish runs the
-//     gather plan (gather_plan.h).
+//     refine pass first builds the second-digit histogram and the lists keep
+//     only keys whose first two digits are at or above (b0, b1): barely more
+//     than K;
+//   * the last chunk of a row to finish (an acquire-release arrival counter;
+//     nobody waits) loads the row's candidates into LDS, finds the remaining
+//     digits -- the threshold key tau and the number E of keys equal to tau
+//     that are taken -- and emits the selection in ascending position order:
+//     every key above tau plus the E lowest-position keys equal to tau.  If the
+//     candidates do not fit in LDS (nearly all scores equal), the same passes
+//     read the candidate lists from global memory.
+// Each selected position is marked in the step's union bitmap and classified
+// against the hot cache, and the last row of each sequence to finish runs the
+// gather plan (gather_plan.h).  All heavy per-position work is spread over the
+// chunks; only the candidates, a few thousand per row, reach the final step.
 //
 // Memory-level parallelism: gathers whose addresses are known are issued
 // together, unconditionally (indices clamped into the buffer), and pinned with
@@ -38,14 +40,16 @@ namespace {
 
 constexpr int kPartThreads = 256;
 constexpr int kPerThread = kTopkChunk / kPartThreads;     // 16 consecutive positions per thread
-constexpr int kResolveThreads = 1024;
-constexpr int kResolveWaves = kResolveThreads / 64;
-constexpr int kCandCap = 12288;                            // candidates held in LDS
-constexpr int kTile = kResolveThreads * 16;                // emit tile (16 per thread)
-constexpr int kMaxChunks = 1024;                           // chunk offsets kept in LDS
+constexpr int kSelThreads = 1024;                         // select workgroup (also runs the plan)
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelPer = kTopkChunk / kSelThreads;          // 4 consecutive positions per thread
+constexpr int kCandCap = 6144;                             // candidates of a row held in LDS
+constexpr int kMaxChunks = kMaxTopkChunks;                 // chunk offsets kept in LDS
 constexpr int kMaxK = 4096;
-constexpr int kOneDigitMax = 65536;                        // collect on the first digit up to this length
-static_assert(kResolveThreads == kPlanThreads, "the plan runs on a resolve workgroup");
+constexpr int kShortMax = 65536;                           // candidates by the first digit up to this length
+static_assert(kSelThreads == kPlanThreads, "the plan runs on a select workgroup");
+static_assert(kSelPer == 4, "one 16-byte score load per thread");
+static_assert(kMaxChunks <= kSelThreads, "one chunk count per thread");
 
 // Keeps x live at this point: a load feeding it cannot be moved into a later
 // branch.  Issue a batch of loads first, then keep() each: the loads stay
@@ -62,7 +66,7 @@ struct TopkKArgs {
   int K;
   int mode;
   int r_max;
-  int digits;          // 11: candidates by the first digit; 22: by the first two
+  int long_mode;       // 0: candidates by the first digit; 1: by the first two (refine pass first)
   PlanParams plan;
 };
 
@@ -117,17 +121,35 @@ __device__ inline void classify_and_pin(const UnitG& u, const ScratchG& s, const
 // classifies and pins them.  Every thread of the workgroup calls it.
 __device__ inline void mark_selection(const UnitG& u, const ScratchG& s, const int32_t* s_sel, int n, bool offl,
                                       int64_t M, int32_t round) {
-  constexpr int kPer = kMaxK / kResolveThreads;
+  constexpr int kPer = kMaxK / kSelThreads;
   int32_t pos[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    const int j = threadIdx.x + e * kResolveThreads;
+    const int j = threadIdx.x + e * kSelThreads;
     pos[e] = j < n ? s_sel[j] : -1;
   }
 #pragma unroll
   for (int e = 0; e < kPer; ++e)
     if (pos[e] >= 0) g_or(&s.selmask[pos[e] >> 5], 1u << (pos[e] & 31));
   if (offl) classify_and_pin<kPer>(u, s, pos, M, round);
+}
+
+// Fewer visible positions than K: every visible position is selected.  The
+// row's first-digit histogram is cleared for the next step.
+__device__ inline void select_all_visible(const UnitG& u, const ScratchG& s, int r, int K, int64_t n_vis,
+                                          DSA_GLOBAL uint32_t* h0, int64_t rep_stride, bool offl, int64_t M,
+                                          int32_t round, int32_t* s_sel) {
+  const int tid = threadIdx.x;
+  const auto sel = s.sel + (int64_t)r * K;
+  for (int b = tid; b < kRadixBins; b += kSelThreads)
+    for (int q = 0; q < kHistReps; ++q) h0[q * rep_stride + b] = 0;
+  for (int t = tid; t < K; t += kSelThreads) {
+    sel[t] = t < n_vis ? t : -1;
+    s_sel[t] = t < n_vis ? t : -1;
+  }
+  __syncthreads();
+  mark_selection(u, s, s_sel, (int)n_vis, offl, M, round);
+  if (tid == 0) s.sel_n[r] = (int32_t)n_vis;
 }
 
 // Second-digit histogram of the keys in the first-digit bin b0 (long histories).
@@ -162,57 +184,15 @@ __global__ __launch_bounds__(kPartThreads) void topk_refine_kernel(TopkKArgs ka)
     if (lh[b]) g_add(&gh[b], lh[b]);
 }
 
-// Every (key, position) of the chunk whose leading `digits` bits are at or above
-// the threshold digits, in position order.
-__global__ __launch_bounds__(kPartThreads) void topk_collect_kernel(TopkKArgs ka) {
-  __shared__ uint32_t sh[kPartThreads / 64];
-  const StepArgs& a = ka.a;
-  const int chunk = blockIdx.x, r = blockIdx.y, seq = blockIdx.z;
-  const UnitG u = unit_of(a, seq);
-  const ScratchG s = scratch_of(a, seq);
-  const int64_t L = u.dyn[0];
-  const int64_t n_vis = L - a.R + r + 1;
-  const int64_t start = (int64_t)chunk * kTopkChunk;
-  if (n_vis <= ka.K || start >= n_vis) return;
-  const int64_t t0 = start + threadIdx.x * kPerThread;
-  float v[kPerThread];
-  load_chunk(s.scores + (int64_t)r * ka.p_pad, t0, v);
-  int b0;
-  uint32_t need;
-  find_bin<kPartThreads / 64, kRadixBins, kHistReps>(s.hist0 + (int64_t)r * kRadixBins, (uint32_t)ka.K, sh, &b0,
-                                                     &need, (int64_t)ka.r_max * kRadixBins);
-  uint32_t thr = (uint32_t)b0;
-  int shift = 21;
-  if (ka.digits == 22) {
-    int b1;
-    find_bin<kPartThreads / 64, kRadixBins, 1>(s.hist1 + (int64_t)r * kRadixBins, need, sh, &b1, &need);
-    thr = ((uint32_t)b0 << 11) | (uint32_t)b1;
-    shift = 10;
-  }
-  uint32_t mine = 0;
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e)
-    mine += (t0 + e < n_vis && (order_key(v[e]) >> shift) >= thr) ? 1u : 0u;
-  uint32_t tot;
-  uint32_t at = block_scan<kPartThreads / 64>(mine, &tot, sh);
-  const auto out = s.cand + (int64_t)r * ka.p_pad + start;
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    const uint32_t key = order_key(v[e]);
-    if (t0 + e < n_vis && (key >> shift) >= thr) out[at++] = (i32x2){(int)key, (int)(t0 + e)};
-  }
-  if (threadIdx.x == 0) s.cand_n[(int64_t)r * ka.n_chunks + chunk] = tot;
-}
-
-// Candidate source for the resolve passes: LDS when the candidates fit, else the
-// global per-chunk lists.
+// The candidates of one row, in position order: LDS copies when they fit, else
+// the global per-chunk lists (chunk c's list starts at c * kTopkChunk).
 struct CandSrc {
   const uint32_t* lkey;              // LDS keys (or null)
   const int32_t* lpos;               // LDS positions (or null)
-  const DSA_GLOBAL i32x2* gcand;     // global candidate lists of the row (by chunk)
-  const uint32_t* off;               // LDS: first candidate index of each chunk
+  const DSA_GLOBAL i32x2* gcand;     // global candidate lists of the row
+  const uint32_t* off;               // LDS: first candidate index of each chunk, [n_chunks + 1]
   int n_chunks;
-  __device__ inline int chunk_of(uint32_t i) const {   // last chunk with off <= i
+  __device__ inline int chunk_of(uint32_t i) const {   // the chunk with off[c] <= i < off[c + 1]
     int lo = 0, hi = n_chunks;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -221,216 +201,263 @@ struct CandSrc {
     }
     return lo;
   }
+  __device__ inline i32x2 global(uint32_t i) const {
+    const int c = chunk_of(i);
+    return gcand[(int64_t)c * kTopkChunk + (i - off[c])];
+  }
   __device__ inline void get(uint32_t i, uint32_t* key, int32_t* pos) const {
     if (lkey) {
       *key = lkey[i];
       *pos = lpos[i];
       return;
     }
-    const int c = chunk_of(i);
-    const i32x2 kp = gcand[(int64_t)c * kTopkChunk + (i - off[c])];
+    const i32x2 kp = global(i);
     *key = (uint32_t)kp.x;
     *pos = kp.y;
   }
 };
 
-__global__ __launch_bounds__(kResolveThreads) void topk_resolve_kernel(TopkKArgs ka) {
-  extern __shared__ __align__(16) uint32_t lds[];   // keys[kCandCap], pos[kCandCap]
-  __shared__ uint32_t sh[4 * kResolveWaves];
-  __shared__ uint32_t hist[kRadixBins];
-  __shared__ uint32_t off[kMaxChunks + 1];
-  __shared__ int32_t s_sel[kMaxK];
-  __shared__ uint32_t s_run[2];
-  const StepArgs& a = ka.a;
-  const int r = blockIdx.x, seq = blockIdx.y, tid = threadIdx.x;
-  const UnitG u = unit_of(a, seq);
-  const ScratchG s = scratch_of(a, seq);
-  const int64_t L = u.dyn[0];
+// LDS of the select workgroup.
+struct SelectLds {
+  uint32_t sh[4 * kSelWaves];
+  uint32_t hist[kRadixBins];
+  uint32_t off[kMaxChunks + 1];
+  uint32_t wcnt[2 * kSelWaves];
+  int32_t sel[kMaxK];
+  uint32_t last;
+};
+
+// The row's final step, run by the workgroup of its last chunk to finish: the
+// remaining digits over the candidates -- the threshold key tau and the number
+// E of keys equal to tau that are taken -- then the selection in position
+// order (every key above tau, and the E lowest-position keys equal to tau),
+// its marks in the step's bitmaps, and the classification against the cache.
+__device__ void resolve_row(const TopkKArgs& ka, const UnitG& u, const ScratchG& s, int r, int64_t n_vis, int b0,
+                            int b1, uint32_t need, SelectLds& sm, uint32_t* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = ka.K;
   const int64_t M = u.dyn[1];
   const int32_t round = (int32_t)u.dyn[2];
   const bool offl = ka.mode == 0;
-  const int K = ka.K;
-  const int64_t n_vis = L - a.R + r + 1;
   const auto h0 = s.hist0 + (int64_t)r * kRadixBins;
   const auto h1 = s.hist1 + (int64_t)r * kRadixBins;
   const int64_t rep_stride = (int64_t)ka.r_max * kRadixBins;
-  const auto sel = s.sel + (int64_t)r * K;
-
-  if (n_vis <= K) {
-    // every visible position is selected
-    for (int b = tid; b < kRadixBins; b += kResolveThreads)
-      for (int q = 0; q < kHistReps; ++q) h0[q * rep_stride + b] = 0;
-    for (int t = tid; t < K; t += kResolveThreads) {
-      sel[t] = t < n_vis ? t : -1;
-      s_sel[t] = t < n_vis ? t : -1;
-    }
-    __syncthreads();
-    mark_selection(u, s, s_sel, (int)n_vis, offl, M, round);
-    if (tid == 0) s.sel_n[r] = (int32_t)n_vis;
-    plan_if_last(u, s, ka.plan, (uint32_t)a.R);
-    return;
-  }
-
-  // chunk counts of the candidate lists (loads issued before the histograms are read)
   const int n_chunks = (int)((n_vis + kTopkChunk - 1) / kTopkChunk);
-  const int per = (n_chunks + kResolveThreads - 1) / kResolveThreads;
-  const int c0 = min(n_chunks, tid * per), c1 = min(n_chunks, c0 + per);
-  uint32_t cnt = 0;
-  for (int c = c0; c < c1; ++c) cnt += s.cand_n[(int64_t)r * ka.n_chunks + c];
 
-  int b0, b1 = 0, b2;
-  uint32_t need;
-  find_bin<kResolveWaves, kRadixBins, kHistReps>(h0, (uint32_t)K, sh, &b0, &need, rep_stride);
-  if (ka.digits == 22) find_bin<kResolveWaves, kRadixBins, 1>(h1, need, sh, &b1, &need);
-  for (int b = tid; b < kRadixBins; b += kResolveThreads) {   // consumed: clear for the next step
+  // chunk list sizes (one chunk per thread at most), loaded before the histogram is read
+  const uint32_t cnt = tid < n_chunks ? s.cand_n[(int64_t)r * ka.n_chunks + tid] : 0u;
+  if (!ka.long_mode) find_bin<kSelWaves, kRadixBins, 1>(h1, need, sm.sh, &b1, &need);
+  for (int b = tid; b < kRadixBins; b += kSelThreads) {   // consumed: clear for the next step
+#pragma unroll
     for (int q = 0; q < kHistReps; ++q) h0[q * rep_stride + b] = 0;
-    if (ka.digits == 22) h1[b] = 0;
+    h1[b] = 0;
   }
   {
     uint32_t tot;
-    uint32_t base = block_scan<kResolveWaves>(cnt, &tot, sh);
-    for (int c = c0; c < c1; ++c) {
-      off[c] = base;
-      base += s.cand_n[(int64_t)r * ka.n_chunks + c];
-    }
-    if (tid == 0) off[n_chunks] = tot;
+    const uint32_t base = block_scan<kSelWaves>(cnt, &tot, sm.sh);
+    if (tid < n_chunks) sm.off[tid] = base;
+    if (tid == 0) sm.off[n_chunks] = tot;
   }
   __syncthreads();
-  const uint32_t C = off[n_chunks];
+  const uint32_t C = sm.off[n_chunks];                 // >= K: every key of tau's first digits or above
   uint32_t* lkey = lds;
   int32_t* lpos = reinterpret_cast<int32_t*>(lds + kCandCap);
-  const DSA_GLOBAL i32x2* gcand = s.cand + (int64_t)r * ka.p_pad;
-  CandSrc src{nullptr, nullptr, gcand, off, n_chunks};
+  CandSrc src{nullptr, nullptr, s.cand + (int64_t)r * ka.p_pad, sm.off, n_chunks};
   if (C <= (uint32_t)kCandCap) {
-    // candidate i = k * 1024 + tid, four at a time: loads issued together
-    const uint32_t nk = (C + kResolveThreads - 1) / kResolveThreads;
-    for (uint32_t k0 = 0; k0 < nk; k0 += 4) {
-      i32x2 kp[4];
+    constexpr int kLoads = kCandCap / kSelThreads;
+    i32x2 kp[kLoads];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t i = (k0 + e) * kResolveThreads + tid;
-        const uint32_t ic = i < C ? i : C - 1;
-        const int c = src.chunk_of(ic);
-        kp[e] = gcand[(int64_t)c * kTopkChunk + (ic - off[c])];
-      }
+    for (int e = 0; e < kLoads; ++e) {
+      const uint32_t i = e * kSelThreads + tid;
+      kp[e] = src.global(i < C ? i : C - 1);
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) keep(kp[e]);
+    for (int e = 0; e < kLoads; ++e) keep(kp[e]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t i = (k0 + e) * kResolveThreads + tid;
-        if (i < C) {
-          lkey[i] = (uint32_t)kp[e].x;
-          lpos[i] = kp[e].y;
-        }
+    for (int e = 0; e < kLoads; ++e) {
+      const uint32_t i = e * kSelThreads + tid;
+      if (i < C) {
+        lkey[i] = (uint32_t)kp[e].x;
+        lpos[i] = kp[e].y;
       }
     }
     src.lkey = lkey;
     src.lpos = lpos;
   }
-  __syncthreads();
-
-  if (ka.digits == 11) {
-    // second digit of the candidates in bin b0
-    for (int b = tid; b < kRadixBins; b += kResolveThreads) hist[b] = 0;
-    __syncthreads();
-    for (uint32_t i = tid; i < C; i += kResolveThreads) {
-      uint32_t key;
-      int32_t pos;
-      src.get(i, &key, &pos);
-      if ((key >> 21) == (uint32_t)b0) atomicAdd(&hist[(key >> 10) & 2047u], 1u);
-    }
-    __syncthreads();
-    find_bin<kResolveWaves, kRadixBins, 1>(hist, need, sh, &b1, &need);
-  }
+  // last digit of the keys whose first two digits are (b0, b1)
   const uint32_t p22 = ((uint32_t)b0 << 11) | (uint32_t)b1;
-  for (int b = tid; b < 1024; b += kResolveThreads) hist[b] = 0;
+  for (int b = tid; b < 1024; b += kSelThreads) sm.hist[b] = 0;
+  for (int j = tid; j < K; j += kSelThreads) sm.sel[j] = -1;   // every entry is written below
   __syncthreads();
-  for (uint32_t i = tid; i < C; i += kResolveThreads) {
+  for (uint32_t i = tid; i < C; i += kSelThreads) {
     uint32_t key;
     int32_t pos;
     src.get(i, &key, &pos);
-    if ((key >> 10) == p22) atomicAdd(&hist[key & 1023u], 1u);
+    if ((key >> 10) == p22) atomicAdd(&sm.hist[key & 1023u], 1u);
   }
   __syncthreads();
-  find_bin<kResolveWaves, 1024, 1>(hist, need, sh, &b2, &need);
+  int b2;
+  find_bin<kSelWaves, 1024, 1>(sm.hist, need, sm.sh, &b2, &need);
   const uint32_t tau = (p22 << 10) | (uint32_t)b2;
   const uint32_t E = need;                             // keys equal to tau that are taken
 
-  // ordered emit, 16 consecutive candidates per thread per tile
-  if (tid == 0) { s_run[0] = 0; s_run[1] = 0; }
-  __syncthreads();
-  for (uint32_t t0 = 0; t0 < C; t0 += kTile) {
-    const uint32_t i0 = t0 + tid * 16;
-    uint32_t keys[16];
-    int32_t poss[16];
-    uint32_t my_gt = 0, my_eq = 0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      keys[e] = 0;
-      poss[e] = -1;
-      if (i0 + e < C) {
-        src.get(i0 + e, &keys[e], &poss[e]);
-        my_gt += keys[e] > tau;
-        my_eq += keys[e] == tau;
-      }
-    }
-    const uint32_t run_gt = s_run[0], run_eq = s_run[1];
-    uint4 tot;
-    const uint4 ex = block_scan4<kResolveWaves>(make_uint4(my_gt, my_eq, 0u, 0u), &tot, sh);
-    uint32_t gt = run_gt + ex.x, eq = run_eq + ex.y;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t k = keys[e];
-      uint32_t at = 0xFFFFFFFFu;
-      if (k > tau) {
-        at = gt + (eq < E ? eq : E);
-        ++gt;
-      } else if (k == tau) {
-        if (eq < E) at = gt + eq;
-        ++eq;
-      }
-      if (at < (uint32_t)K) {                          // always, when the histograms match the keys
-        sel[at] = poss[e];
-        s_sel[at] = poss[e];
-      }
-    }
-    __syncthreads();
-    if (tid == 0) { s_run[0] = run_gt + tot.x; s_run[1] = run_eq + tot.y; }
-    __syncthreads();
+  // Ordered emit.  Wave w owns candidates [w seg, (w+1) seg), 64 consecutive at
+  // a time; a first pass counts its keys above and equal to tau, a scan over the
+  // waves gives each wave its starting ranks, a second pass writes.
+  const uint32_t seg = ((C + kSelWaves * 64 - 1) / (kSelWaves * 64)) * 64;
+  const uint32_t w0 = min(C, wave * seg), w1 = min(C, w0 + seg);
+  const uint64_t below = lanes_below(lane);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (uint32_t i0 = w0; i0 < w1; i0 += 64) {
+    const uint32_t i = i0 + lane;
+    uint32_t key = 0;
+    int32_t pos;
+    if (i < w1) src.get(i, &key, &pos);
+    n_gt += (uint32_t)__popcll(__ballot(i < w1 && key > tau));
+    n_eq += (uint32_t)__popcll(__ballot(i < w1 && key == tau));
   }
-  mark_selection(u, s, s_sel, K, offl, M, round);
+  if (lane == 0) {
+    sm.wcnt[wave] = n_gt;
+    sm.wcnt[kSelWaves + wave] = n_eq;
+  }
+  __syncthreads();
+  uint32_t gt_run = 0, eq_run = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    gt_run += w < wave ? sm.wcnt[w] : 0u;
+    eq_run += w < wave ? sm.wcnt[kSelWaves + w] : 0u;
+  }
+  const auto sel = s.sel + (int64_t)r * K;
+  for (uint32_t i0 = w0; i0 < w1; i0 += 64) {
+    const uint32_t i = i0 + lane;
+    uint32_t key = 0;
+    int32_t pos = -1;
+    if (i < w1) src.get(i, &key, &pos);
+    const bool gt = i < w1 && key > tau, eq = i < w1 && key == tau;
+    const uint64_t bg = __ballot(gt), be = __ballot(eq);
+    const uint32_t gr = gt_run + (uint32_t)__popcll(bg & below);
+    const uint32_t er = eq_run + (uint32_t)__popcll(be & below);
+    uint32_t at = 0xFFFFFFFFu;
+    if (gt) at = gr + min(er, E);
+    else if (eq && er < E) at = gr + er;
+    if (at < (uint32_t)K) {                            // always, when the histograms match the keys
+      sel[at] = pos;
+      sm.sel[at] = pos;
+    }
+    gt_run += (uint32_t)__popcll(bg);
+    eq_run += (uint32_t)__popcll(be);
+  }
+  __syncthreads();
+  mark_selection(u, s, sm.sel, K, offl, M, round);
   if (tid == 0) s.sel_n[r] = K;
+}
+
+// Top-K of every query row.  One workgroup per (4096-position chunk, row,
+// sequence) keeps the chunk's candidates -- every key whose first digit is at
+// or above the bin b0 of the K-th key (whose first two digits are at or above
+// (b0, b1) for long histories, b1 from the refine pass) -- in position order,
+// and, for short histories, adds the second-digit histogram of its keys in bin
+// b0.  The last chunk of a row to finish resolves the row; the last row of a
+// sequence to finish then runs the gather plan.  No workgroup waits for another.
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkKArgs ka) {
+  extern __shared__ __align__(16) uint32_t lds[];   // keys[kCandCap], positions[kCandCap]
+  __shared__ SelectLds sm;
+  const StepArgs& a = ka.a;
+  const int chunk = blockIdx.x, r = blockIdx.y, seq = blockIdx.z, tid = threadIdx.x;
+  const UnitG u = unit_of(a, seq);
+  const ScratchG s = scratch_of(a, seq);
+  const int64_t L = u.dyn[0];
+  const int64_t n_vis = L - a.R + r + 1;
+  const int K = ka.K;
+  const auto h0 = s.hist0 + (int64_t)r * kRadixBins;
+  const int64_t rep_stride = (int64_t)ka.r_max * kRadixBins;
+  const int64_t start = (int64_t)chunk * kTopkChunk;
+
+  if (n_vis <= K) {
+    if (chunk != 0) return;
+    select_all_visible(u, s, r, K, n_vis, h0, rep_stride, ka.mode == 0, u.dyn[1], (int32_t)u.dyn[2], sm.sel);
+    plan_if_last(u, s, ka.plan, (uint32_t)a.R);
+    return;
+  }
+  if (start >= n_vis) return;
+  const int n_chunks = (int)((n_vis + kTopkChunk - 1) / kTopkChunk);
+
+  const int64_t t0 = start + tid * kSelPer;
+  const f32x4v f = *reinterpret_cast<const DSA_GLOBAL f32x4v*>(s.scores + (int64_t)r * ka.p_pad + t0);
+  int b0, b1 = 0;
+  uint32_t need;
+  find_bin<kSelWaves, kRadixBins, kHistReps>(h0, (uint32_t)K, sm.sh, &b0, &need, rep_stride);
+  if (ka.long_mode)
+    find_bin<kSelWaves, kRadixBins, 1>(s.hist1 + (int64_t)r * kRadixBins, need, sm.sh, &b1, &need);
+  uint32_t key[kSelPer];
+#pragma unroll
+  for (int e = 0; e < kSelPer; ++e) key[e] = t0 + e < n_vis ? order_key(f[e]) : 0u;   // 0: not visible
+  const int shift = ka.long_mode ? 10 : 21;
+  const uint32_t thr = ka.long_mode ? (((uint32_t)b0 << 11) | (uint32_t)b1) : (uint32_t)b0;
+
+  if (!ka.long_mode) {
+    for (int b = tid; b < kRadixBins; b += kSelThreads) sm.hist[b] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kSelPer; ++e)
+      if (t0 + e < n_vis && (key[e] >> 21) == (uint32_t)b0) atomicAdd(&sm.hist[(key[e] >> 10) & 2047u], 1u);
+    __syncthreads();
+    const auto gh = s.hist1 + (int64_t)r * kRadixBins;
+    for (int b = tid; b < kRadixBins; b += kSelThreads)
+      if (sm.hist[b]) g_add(&gh[b], sm.hist[b]);
+  }
+  uint32_t mine = 0;
+#pragma unroll
+  for (int e = 0; e < kSelPer; ++e) mine += (t0 + e < n_vis && (key[e] >> shift) >= thr) ? 1u : 0u;
+  uint32_t tot;
+  uint32_t at = block_scan<kSelWaves>(mine, &tot, sm.sh);
+  const auto out = s.cand + (int64_t)r * ka.p_pad + start;
+#pragma unroll
+  for (int e = 0; e < kSelPer; ++e)
+    if (t0 + e < n_vis && (key[e] >> shift) >= thr) out[at++] = (i32x2){(int)key[e], (int)(t0 + e)};
+  if (tid == 0) s.cand_n[(int64_t)r * ka.n_chunks + chunk] = tot;
+
+  // Arrival: the barrier orders every wave's writes before thread 0's
+  // acquire-release arrival at device scope, so the last chunk to arrive sees
+  // every chunk's lists and histogram counts (as in plan_if_last).
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&s.arrive[r], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev + 1 == (uint32_t)n_chunks;
+    if (last) __hip_atomic_store(&s.arrive[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.last = last ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!sm.last) return;
+  resolve_row(ka, u, s, r, n_vis, b0, b1, need, sm, lds);
   plan_if_last(u, s, ka.plan, (uint32_t)a.R);
 }
 
 TopkKArgs topk_args(const Geometry& g, const StepArgs& a) {
-  return TopkKArgs{a, g.p_pad, g.n_chunks, g.top_k, g.mode, g.r_max, a.l_max <= kOneDigitMax ? 11 : 22,
+  return TopkKArgs{a, g.p_pad, g.n_chunks, g.top_k, g.mode, g.r_max, a.l_max > kShortMax ? 1 : 0,
                    PlanParams{g.hot_slots, g.s_words, g.ring_rows, g.mode}};
 }
 
 }  // namespace
 
 hipError_t prepare_topk_kernels() {
-  return hipFuncSetAttribute((const void*)topk_resolve_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+  return hipFuncSetAttribute((const void*)topk_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                              2 * kCandCap * (int)sizeof(uint32_t));
 }
 
 hipError_t launch_topk_partial(const Geometry& g, const StepArgs& a, hipStream_t st) {
   const TopkKArgs ka = topk_args(g, a);
+  if (!ka.long_mode) return hipSuccess;
   const int chunks = (int)((a.l_max + kTopkChunk - 1) / kTopkChunk);
   const dim3 grid((unsigned)chunks, (unsigned)a.R, (unsigned)a.n_seqs);
-  if (ka.digits == 22) {
-    const hipError_t e = launch_k(topk_refine_kernel, grid, dim3(kPartThreads), 0, st, ka);
-    if (e != hipSuccess) return e;
-  }
-  return launch_k(topk_collect_kernel, grid, dim3(kPartThreads), 0, st, ka);
+  return launch_k(topk_refine_kernel, grid, dim3(kPartThreads), 0, st, ka);
 }
 
 hipError_t launch_topk_select(const Geometry& g, const StepArgs& a, hipStream_t st) {
   const TopkKArgs ka = topk_args(g, a);
-  const dim3 grid((unsigned)a.R, (unsigned)a.n_seqs);
-  return launch_k(topk_resolve_kernel, grid, dim3(kResolveThreads), 2 * kCandCap * (uint32_t)sizeof(uint32_t), st,
-                  ka);
+  const int chunks = (int)((a.l_max + kTopkChunk - 1) / kTopkChunk);
+  const dim3 grid((unsigned)chunks, (unsigned)a.R, (unsigned)a.n_seqs);
+  return launch_k(topk_select_kernel, grid, dim3(kSelThreads), 2 * kCandCap * (uint32_t)sizeof(uint32_t), st, ka);
 }
 
 }  // namespace dsa

@@ -279,7 +279,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   }
   struct ScrOff { size_t scores, sel, sel_n, uni, kind, src, fill, map, compact, po, pml, cnt, info,
                   selmask, hitmask, base_u, base_m, pinmask, upw, upos, victim, done, hist0, hist1, cand,
-                  cand_n; };
+                  cand_n, arrive; };
   std::vector<ScrOff> so(cfg->n_seqs);
   for (int q = 0; q < cfg->n_seqs; ++q) {
     so[q].scores = take((size_t)g.r_max * P * 4);
@@ -304,6 +304,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     so[q].upos = take((size_t)P * 4);
     so[q].victim = take((size_t)g.s_words * 32 * 4);
     so[q].done = take(4);
+    so[q].arrive = take((size_t)g.r_max * 4);
     so[q].hist0 = take((size_t)kHistReps * g.r_max * kRadixBins * 4);
     so[q].hist1 = take((size_t)g.r_max * kRadixBins * 4);
     so[q].cand = take((size_t)g.r_max * P * 8);
@@ -389,6 +390,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     c.upos = reinterpret_cast<int32_t*>(base + so[q].upos);
     c.victim = reinterpret_cast<int32_t*>(base + so[q].victim);
     c.done = reinterpret_cast<uint32_t*>(base + so[q].done);
+    c.arrive = reinterpret_cast<uint32_t*>(base + so[q].arrive);
     c.hist0 = reinterpret_cast<uint32_t*>(base + so[q].hist0);
     c.hist1 = reinterpret_cast<uint32_t*>(base + so[q].hist1);
     c.cand = reinterpret_cast<i32x2*>(base + so[q].cand);
