@@ -71,26 +71,18 @@ __device__ inline uint4 block_scan4(uint4 v, uint4* tot, uint32_t* sh) {
   return make_uint4(base.x + inc.x - v.x, base.y + inc.y - v.y, base.z + inc.z - v.z, base.w + inc.w - v.w);
 }
 
-// The bin holding the k-th largest key among those counted in hist[NBINS] (summed
-// over REPS replicas `stride` apart): the largest b with suffix(b) >= k, and the
-// number of keys still needed from it.  Each thread owns NBINS/(64 NW)
-// contiguous bins, loaded together; thread 0 owns the highest.  hist may be in
-// global memory or LDS.  Every thread of the workgroup must call it.
-template <int NW, int NBINS, int REPS, class HistPtr>
-__device__ inline void find_bin(HistPtr hist, uint32_t k, uint32_t* sh, int* out_bin,
-                                uint32_t* out_need, int64_t stride = 0) {
-  constexpr int PER = NBINS / (NW * 64);
-  static_assert(PER >= 1 && NBINS % (NW * 64) == 0, "bins per thread");
+// The bin holding the k-th largest key, from counts already in registers: each
+// thread holds the PER contiguous bins lo(tid) .. lo(tid) + PER - 1 with
+// lo(tid) = NBINS - (tid + 1) PER (thread 0 owns the highest).  Returns the
+// largest b with suffix(b) >= k and the number of keys still needed from it.
+// Every thread of the workgroup must call it.
+template <int NW, int NBINS, int PER>
+__device__ inline void find_bin_regs(const uint32_t* c, uint32_t k, uint32_t* sh, int* out_bin,
+                                     uint32_t* out_need) {
+  static_assert(PER >= 1 && NBINS == NW * 64 * PER, "bins per thread");
   __shared__ int s_bin;
   __shared__ uint32_t s_need;
   const int lo = NBINS - ((int)threadIdx.x + 1) * PER;
-  uint32_t c[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) c[e] = 0;
-#pragma unroll
-  for (int q = 0; q < REPS; ++q)
-#pragma unroll
-    for (int e = 0; e < PER; ++e) c[e] += hist[q * stride + lo + e];
   uint32_t local = 0;
 #pragma unroll
   for (int e = 0; e < PER; ++e) local += c[e];
@@ -113,6 +105,33 @@ __device__ inline void find_bin(HistPtr hist, uint32_t k, uint32_t* sh, int* out
   *out_bin = s_bin;
   *out_need = s_need;
   __syncthreads();
+}
+
+// This thread's bins of hist[NBINS] (summed over REPS replicas `stride` apart),
+// in the layout find_bin_regs expects.  hist may be in global memory or LDS.
+template <int NW, int NBINS, int REPS, class HistPtr>
+__device__ inline void load_bins(HistPtr hist, uint32_t* c, int64_t stride = 0) {
+  constexpr int PER = NBINS / (NW * 64);
+  const int lo = NBINS - ((int)threadIdx.x + 1) * PER;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) c[e] = 0;
+#pragma unroll
+  for (int q = 0; q < REPS; ++q)
+#pragma unroll
+    for (int e = 0; e < PER; ++e) c[e] += hist[q * stride + lo + e];
+}
+
+// The bin holding the k-th largest key among those counted in hist[NBINS] (summed
+// over REPS replicas `stride` apart): the largest b with suffix(b) >= k, and the
+// number of keys still needed from it.  Every thread of the workgroup must call it.
+template <int NW, int NBINS, int REPS, class HistPtr>
+__device__ inline void find_bin(HistPtr hist, uint32_t k, uint32_t* sh, int* out_bin,
+                                uint32_t* out_need, int64_t stride = 0) {
+  constexpr int PER = NBINS / (NW * 64);
+  static_assert(PER >= 1 && NBINS % (NW * 64) == 0, "bins per thread");
+  uint32_t c[PER];
+  load_bins<NW, NBINS, REPS>(hist, c, stride);
+  find_bin_regs<NW, NBINS, PER>(c, k, sh, out_bin, out_need);
 }
 
 // Lanes below this one, as a 64-bit mask.

@@ -34,6 +34,7 @@ template <class T> using HostPtr = T*;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 template <class T> using GlobalPtr = DSA_GLOBAL T*;
 
 // Per-unit persistent state, device-visible.
@@ -74,14 +75,13 @@ struct ScratchT {
   P<uint32_t> base_u;       // [P_pad/32] union entries before each 32-position word
   P<uint32_t> base_m;       // [P_pad/32] misses before each word
   P<uint32_t> pinmask;      // [S_pad/32] slots pinned this round (cleared by the scan)
-  P<uint32_t> upw;          // [S_pad/32] unpinned slots, in ring order from the hand
   P<int32_t> victim;        // [S_pad] slot given to the k-th miss of the step
   P<uint32_t> hist0;        // [kHistReps][R_max][2048] first-digit histogram replicas (zeroed after use)
   P<uint32_t> hist1;        // [R_max][2048] second-digit histogram within the first-digit bin
   P<i32x2> cand;            // [R_max][P_pad] top-k candidates (key, position), by chunk, in position order
   P<uint32_t> cand_n;       // [R_max][n_chunks] candidates per chunk
+  P<int32_t> rowdig;        // [R_max][4] b0, b1, keys still needed: the row's threshold digits so far
   P<uint32_t> done;         // [1] rows of the step that finished their selection (reset by the last)
-  P<uint32_t> arrive;       // [R_max] chunks of each row that finished their candidate lists (reset by the last)
 };
 
 using UnitDev = UnitT<HostPtr>;
@@ -157,10 +157,9 @@ __device__ inline void g_add(DSA_GLOBAL int64_t* p, int64_t v) {
 // ---- launchers (each returns the hipError_t of its launch) ----
 hipError_t launch_score(const Geometry& g, const StepArgs& a, const uint16_t* q, const float* w,
                         hipStream_t st);
-// Top-K: a refine pass over chunks for long histories (partial), then the
-// select kernel: candidate lists per chunk, resolved per row by the row's last
-// chunk to finish; it ends with the gather plan, run by the last row of each
-// sequence.
+// Top-K: a refine pass over chunks for long histories (partial), then candidate
+// lists per chunk and a per-row resolve (select); the resolve ends with the
+// gather plan, run by the last row of each sequence.
 hipError_t launch_topk_partial(const Geometry& g, const StepArgs& a, hipStream_t st);
 hipError_t launch_topk_select(const Geometry& g, const StepArgs& a, hipStream_t st);
 hipError_t prepare_topk_kernels();

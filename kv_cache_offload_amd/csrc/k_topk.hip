@@ -8,26 +8,25 @@
 // 11, 11 and 10 bits.  The first digit's histogram is built by the score kernel
 // while the scores are still in registers (in kHistReps replicas, so that the
 // few bins integer-valued scores crowd into do not serialise the atomics).
-// Then one select kernel, one 1024-thread workgroup per (4096-position chunk,
-// query row):
-//   * every workgroup finds the first-digit bin b0 that holds the K-th largest
-//     key and writes, in position order, the (key, position) of every key of
-//     its chunk whose first digit is at or above b0 -- every position that can
-//     be selected -- and adds the second-digit histogram of its keys in b0;
-//     for histories longer than 65,536 positions that list would be long, so a
-//     refine pass first builds the second-digit histogram and the lists keep
-//     only keys whose first two digits are at or above (b0, b1): barely more
-//     than K;
-//   * the last chunk of a row to finish (an acquire-release arrival counter;
-//     nobody waits) loads the row's candidates into LDS, finds the remaining
-//     digits -- the threshold key tau and the number E of keys equal to tau
-//     that are taken -- and emits the selection in ascending position order:
-//     every key above tau plus the E lowest-position keys equal to tau.  If the
-//     candidates do not fit in LDS (nearly all scores equal), the same passes
-//     read the candidate lists from global memory.
+// Then, per query row:
+//   * chunk (one 1024-thread workgroup per 4096-position chunk): finds the
+//     first-digit bin b0 that holds the K-th largest key and writes, in
+//     position order, the (key, position) of every key of the chunk whose first
+//     digit is at or above b0 -- every position that can be selected -- and
+//     adds the second-digit histogram of its keys in b0; for histories longer
+//     than 65,536 positions that list would be long, so a refine pass first
+//     builds the second-digit histogram and the lists keep only keys whose
+//     first two digits are at or above (b0, b1): barely more than K;
+//   * final (one 1024-thread workgroup per row): loads the row's candidates
+//     into LDS, finds the remaining digits -- the threshold key tau and the
+//     number E of keys equal to tau that are taken -- and emits the selection
+//     in ascending position order: every key above tau plus the E
+//     lowest-position keys equal to tau.  If the candidates do not fit in LDS
+//     (nearly all scores equal), the same passes read the candidate lists from
+//     global memory.
 // Each selected position is marked in the step's union bitmap and classified
 // against the hot cache, and the last row of each sequence to finish runs the
-// gather plan (gather_plan.h).  All heavy per-position work is spread over the
+// gather plan (gather_plan.h).  All per-position work is spread over the
 // chunks; only the candidates, a few thousand per row, reach the final step.
 //
 // Memory-level parallelism: gathers whose addresses are known are issued
@@ -43,13 +42,14 @@ constexpr int kPerThread = kTopkChunk / kPartThreads;     // 16 consecutive posi
 constexpr int kSelThreads = 1024;                         // select workgroup (also runs the plan)
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelPer = kTopkChunk / kSelThreads;          // 4 consecutive positions per thread
-constexpr int kCandCap = 6144;                             // candidates of a row held in LDS
+constexpr int kCandCap = 16384;                            // candidates of a row held in LDS
 constexpr int kMaxChunks = kMaxTopkChunks;                 // chunk offsets kept in LDS
 constexpr int kMaxK = 4096;
 constexpr int kShortMax = 65536;                           // candidates by the first digit up to this length
 static_assert(kSelThreads == kPlanThreads, "the plan runs on a select workgroup");
 static_assert(kSelPer == 4, "one 16-byte score load per thread");
 static_assert(kMaxChunks <= kSelThreads, "one chunk count per thread");
+static_assert(2 * kCandCap >= 2 * kPlanThreads, "the plan reuses the candidate LDS");
 
 // Keeps x live at this point: a load feeding it cannot be moved into a later
 // branch.  Issue a batch of loads first, then keep() each: the loads stay
@@ -232,21 +232,18 @@ struct SelectLds {
 // E of keys equal to tau that are taken -- then the selection in position
 // order (every key above tau, and the E lowest-position keys equal to tau),
 // its marks in the step's bitmaps, and the classification against the cache.
-__device__ void resolve_row(const TopkKArgs& ka, const UnitG& u, const ScratchG& s, int r, int64_t n_vis, int b0,
-                            int b1, uint32_t need, SelectLds& sm, uint32_t* lds) {
+__device__ void resolve_row(const TopkKArgs& ka, const UnitG& u, const ScratchG& s, int r, int64_t n_vis,
+                            int64_t M, int32_t round, int b0, int b1, uint32_t need, uint32_t cnt,
+                            const uint32_t* h1c, SelectLds& sm, uint32_t* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = ka.K;
-  const int64_t M = u.dyn[1];
-  const int32_t round = (int32_t)u.dyn[2];
   const bool offl = ka.mode == 0;
   const auto h0 = s.hist0 + (int64_t)r * kRadixBins;
   const auto h1 = s.hist1 + (int64_t)r * kRadixBins;
   const int64_t rep_stride = (int64_t)ka.r_max * kRadixBins;
   const int n_chunks = (int)((n_vis + kTopkChunk - 1) / kTopkChunk);
 
-  // chunk list sizes (one chunk per thread at most), loaded before the histogram is read
-  const uint32_t cnt = tid < n_chunks ? s.cand_n[(int64_t)r * ka.n_chunks + tid] : 0u;
-  if (!ka.long_mode) find_bin<kSelWaves, kRadixBins, 1>(h1, need, sm.sh, &b1, &need);
+  if (!ka.long_mode) find_bin_regs<kSelWaves, kRadixBins, kRadixBins / kSelThreads>(h1c, need, sm.sh, &b1, &need);
   for (int b = tid; b < kRadixBins; b += kSelThreads) {   // consumed: clear for the next step
 #pragma unroll
     for (int q = 0; q < kHistReps; ++q) h0[q * rep_stride + b] = 0;
@@ -269,10 +266,11 @@ __device__ void resolve_row(const TopkKArgs& ka, const UnitG& u, const ScratchG&
 #pragma unroll
     for (int e = 0; e < kLoads; ++e) {
       const uint32_t i = e * kSelThreads + tid;
-      kp[e] = src.global(i < C ? i : C - 1);
+      if (e * kSelThreads < (int)C) kp[e] = src.global(i < C ? i : C - 1);   // uniform branch
     }
 #pragma unroll
-    for (int e = 0; e < kLoads; ++e) keep(kp[e]);
+    for (int e = 0; e < kLoads; ++e)
+      if (e * kSelThreads < (int)C) keep(kp[e]);
 #pragma unroll
     for (int e = 0; e < kLoads; ++e) {
       const uint32_t i = e * kSelThreads + tid;
@@ -352,85 +350,91 @@ __device__ void resolve_row(const TopkKArgs& ka, const UnitG& u, const ScratchG&
   if (tid == 0) s.sel_n[r] = K;
 }
 
-// Top-K of every query row.  One workgroup per (4096-position chunk, row,
-// sequence) keeps the chunk's candidates -- every key whose first digit is at
-// or above the bin b0 of the K-th key (whose first two digits are at or above
-// (b0, b1) for long histories, b1 from the refine pass) -- in position order,
-// and, for short histories, adds the second-digit histogram of its keys in bin
-// b0.  The last chunk of a row to finish resolves the row; the last row of a
-// sequence to finish then runs the gather plan.  No workgroup waits for another.
-__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkKArgs ka) {
-  extern __shared__ __align__(16) uint32_t lds[];   // keys[kCandCap], positions[kCandCap]
-  __shared__ SelectLds sm;
+// Candidate lists.  One workgroup per (4096-position chunk, row, sequence)
+// keeps the chunk's candidates -- every key whose first digit is at or above
+// the bin b0 of the K-th key (whose first two digits are at or above (b0, b1)
+// for long histories, b1 from the refine pass) -- in position order, and, for
+// short histories, adds the second-digit histogram of its keys in bin b0.
+__global__ __launch_bounds__(kSelThreads) void topk_chunk_kernel(TopkKArgs ka) {
+  __shared__ uint32_t sh[kSelWaves];
+  __shared__ uint32_t hist[kRadixBins];
   const StepArgs& a = ka.a;
   const int chunk = blockIdx.x, r = blockIdx.y, seq = blockIdx.z, tid = threadIdx.x;
   const UnitG u = unit_of(a, seq);
   const ScratchG s = scratch_of(a, seq);
   const int64_t L = u.dyn[0];
   const int64_t n_vis = L - a.R + r + 1;
-  const int K = ka.K;
-  const auto h0 = s.hist0 + (int64_t)r * kRadixBins;
-  const int64_t rep_stride = (int64_t)ka.r_max * kRadixBins;
   const int64_t start = (int64_t)chunk * kTopkChunk;
-
-  if (n_vis <= K) {
-    if (chunk != 0) return;
-    select_all_visible(u, s, r, K, n_vis, h0, rep_stride, ka.mode == 0, u.dyn[1], (int32_t)u.dyn[2], sm.sel);
-    plan_if_last(u, s, ka.plan, (uint32_t)a.R);
-    return;
-  }
-  if (start >= n_vis) return;
-  const int n_chunks = (int)((n_vis + kTopkChunk - 1) / kTopkChunk);
+  if (n_vis <= ka.K || start >= n_vis) return;
 
   const int64_t t0 = start + tid * kSelPer;
   const f32x4v f = *reinterpret_cast<const DSA_GLOBAL f32x4v*>(s.scores + (int64_t)r * ka.p_pad + t0);
   int b0, b1 = 0;
   uint32_t need;
-  find_bin<kSelWaves, kRadixBins, kHistReps>(h0, (uint32_t)K, sm.sh, &b0, &need, rep_stride);
+  find_bin<kSelWaves, kRadixBins, kHistReps>(s.hist0 + (int64_t)r * kRadixBins, (uint32_t)ka.K, sh, &b0, &need,
+                                             (int64_t)ka.r_max * kRadixBins);
   if (ka.long_mode)
-    find_bin<kSelWaves, kRadixBins, 1>(s.hist1 + (int64_t)r * kRadixBins, need, sm.sh, &b1, &need);
+    find_bin<kSelWaves, kRadixBins, 1>(s.hist1 + (int64_t)r * kRadixBins, need, sh, &b1, &need);
   uint32_t key[kSelPer];
 #pragma unroll
   for (int e = 0; e < kSelPer; ++e) key[e] = t0 + e < n_vis ? order_key(f[e]) : 0u;   // 0: not visible
   const int shift = ka.long_mode ? 10 : 21;
   const uint32_t thr = ka.long_mode ? (((uint32_t)b0 << 11) | (uint32_t)b1) : (uint32_t)b0;
+  if (chunk == 0 && tid == 0)                          // the row's digits so far, for the final pass
+    *reinterpret_cast<DSA_GLOBAL i32x4*>(s.rowdig + 4 * r) = (i32x4){b0, b1, (int32_t)need, 0};
 
   if (!ka.long_mode) {
-    for (int b = tid; b < kRadixBins; b += kSelThreads) sm.hist[b] = 0;
+    for (int b = tid; b < kRadixBins; b += kSelThreads) hist[b] = 0;
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < kSelPer; ++e)
-      if (t0 + e < n_vis && (key[e] >> 21) == (uint32_t)b0) atomicAdd(&sm.hist[(key[e] >> 10) & 2047u], 1u);
+      if (t0 + e < n_vis && (key[e] >> 21) == (uint32_t)b0) atomicAdd(&hist[(key[e] >> 10) & 2047u], 1u);
     __syncthreads();
     const auto gh = s.hist1 + (int64_t)r * kRadixBins;
     for (int b = tid; b < kRadixBins; b += kSelThreads)
-      if (sm.hist[b]) g_add(&gh[b], sm.hist[b]);
+      if (hist[b]) g_add(&gh[b], hist[b]);
   }
   uint32_t mine = 0;
 #pragma unroll
   for (int e = 0; e < kSelPer; ++e) mine += (t0 + e < n_vis && (key[e] >> shift) >= thr) ? 1u : 0u;
   uint32_t tot;
-  uint32_t at = block_scan<kSelWaves>(mine, &tot, sm.sh);
+  uint32_t at = block_scan<kSelWaves>(mine, &tot, sh);
   const auto out = s.cand + (int64_t)r * ka.p_pad + start;
 #pragma unroll
   for (int e = 0; e < kSelPer; ++e)
     if (t0 + e < n_vis && (key[e] >> shift) >= thr) out[at++] = (i32x2){(int)key[e], (int)(t0 + e)};
   if (tid == 0) s.cand_n[(int64_t)r * ka.n_chunks + chunk] = tot;
+}
 
-  // Arrival: the barrier orders every wave's writes before thread 0's
-  // acquire-release arrival at device scope, so the last chunk to arrive sees
-  // every chunk's lists and histogram counts (as in plan_if_last).
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&s.arrive[r], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = prev + 1 == (uint32_t)n_chunks;
-    if (last) __hip_atomic_store(&s.arrive[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = last ? 1u : 0u;
+// One workgroup per (row, sequence): resolves the row from its candidate lists;
+// the last row of a sequence to finish then runs the gather plan.
+__global__ __launch_bounds__(kSelThreads) void topk_final_kernel(TopkKArgs ka) {
+  extern __shared__ __align__(16) uint32_t lds[];   // keys[kCandCap], positions[kCandCap]
+  __shared__ SelectLds sm;
+  const StepArgs& a = ka.a;
+  const int r = blockIdx.x, seq = blockIdx.y, tid = threadIdx.x;
+  const UnitG u = unit_of(a, seq);
+  const ScratchG s = scratch_of(a, seq);
+  // the round-start state, read once (the plan needs it too)
+  const PlanState ps{u.dyn[0], u.dyn[1], (int32_t)u.dyn[2], ka.mode == 0 ? *u.hand : 0};
+  const int64_t n_vis = ps.L - a.R + r + 1;
+  const int K = ka.K;
+  const auto h0 = s.hist0 + (int64_t)r * kRadixBins;
+  const int64_t rep_stride = (int64_t)ka.r_max * kRadixBins;
+  if (n_vis <= K) {
+    select_all_visible(u, s, r, K, n_vis, h0, rep_stride, ka.mode == 0, ps.M, ps.round, sm.sel);
+  } else {
+    // everything this pass reads first, issued together: the row's digits from
+    // the chunk pass, the chunk list sizes (one chunk per thread at most) and
+    // this thread's bins of the second-digit histogram
+    const int n_chunks = (int)((n_vis + kTopkChunk - 1) / kTopkChunk);
+    const i32x4 dig = *reinterpret_cast<const DSA_GLOBAL i32x4*>(s.rowdig + 4 * r);
+    const uint32_t cnt = tid < n_chunks ? s.cand_n[(int64_t)r * ka.n_chunks + tid] : 0u;
+    uint32_t h1c[kRadixBins / kSelThreads];
+    load_bins<kSelWaves, kRadixBins, 1>(s.hist1 + (int64_t)r * kRadixBins, h1c);
+    resolve_row(ka, u, s, r, n_vis, ps.M, ps.round, dig.x, dig.y, (uint32_t)dig.z, cnt, h1c, sm, lds);
   }
-  __syncthreads();
-  if (!sm.last) return;
-  resolve_row(ka, u, s, r, n_vis, b0, b1, need, sm, lds);
-  plan_if_last(u, s, ka.plan, (uint32_t)a.R);
+  plan_if_last(u, s, ka.plan, (uint32_t)a.R, ps, lds);
 }
 
 TopkKArgs topk_args(const Geometry& g, const StepArgs& a) {
@@ -441,7 +445,7 @@ TopkKArgs topk_args(const Geometry& g, const StepArgs& a) {
 }  // namespace
 
 hipError_t prepare_topk_kernels() {
-  return hipFuncSetAttribute((const void*)topk_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+  return hipFuncSetAttribute((const void*)topk_final_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                              2 * kCandCap * (int)sizeof(uint32_t));
 }
 
@@ -456,8 +460,11 @@ hipError_t launch_topk_partial(const Geometry& g, const StepArgs& a, hipStream_t
 hipError_t launch_topk_select(const Geometry& g, const StepArgs& a, hipStream_t st) {
   const TopkKArgs ka = topk_args(g, a);
   const int chunks = (int)((a.l_max + kTopkChunk - 1) / kTopkChunk);
-  const dim3 grid((unsigned)chunks, (unsigned)a.R, (unsigned)a.n_seqs);
-  return launch_k(topk_select_kernel, grid, dim3(kSelThreads), 2 * kCandCap * (uint32_t)sizeof(uint32_t), st, ka);
+  const hipError_t e = launch_k(topk_chunk_kernel, dim3((unsigned)chunks, (unsigned)a.R, (unsigned)a.n_seqs),
+                                dim3(kSelThreads), 0, st, ka);
+  if (e != hipSuccess) return e;
+  return launch_k(topk_final_kernel, dim3((unsigned)a.R, (unsigned)a.n_seqs), dim3(kSelThreads),
+                  2 * kCandCap * (uint32_t)sizeof(uint32_t), st, ka);
 }
 
 }  // namespace dsa

@@ -278,8 +278,8 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     uo[i].totals = take(64);
   }
   struct ScrOff { size_t scores, sel, sel_n, uni, kind, src, fill, map, compact, po, pml, cnt, info,
-                  selmask, hitmask, base_u, base_m, pinmask, upw, upos, victim, done, hist0, hist1, cand,
-                  cand_n, arrive; };
+                  selmask, hitmask, base_u, base_m, pinmask, upos, victim, done, hist0, hist1, cand,
+                  cand_n, rowdig; };
   std::vector<ScrOff> so(cfg->n_seqs);
   for (int q = 0; q < cfg->n_seqs; ++q) {
     so[q].scores = take((size_t)g.r_max * P * 4);
@@ -300,15 +300,14 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     so[q].base_u = take((size_t)P / 32 * 4);
     so[q].base_m = take((size_t)P / 32 * 4);
     so[q].pinmask = take((size_t)g.s_words * 4);
-    so[q].upw = take((size_t)g.s_words * 4);
     so[q].upos = take((size_t)P * 4);
     so[q].victim = take((size_t)g.s_words * 32 * 4);
     so[q].done = take(4);
-    so[q].arrive = take((size_t)g.r_max * 4);
     so[q].hist0 = take((size_t)kHistReps * g.r_max * kRadixBins * 4);
     so[q].hist1 = take((size_t)g.r_max * kRadixBins * 4);
     so[q].cand = take((size_t)g.r_max * P * 8);
     so[q].cand_n = take((size_t)g.r_max * g.n_chunks * 4);
+    so[q].rowdig = take((size_t)g.r_max * 16);
   }
   s->arena_bytes = cur;
 
@@ -386,15 +385,14 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     c.base_u = reinterpret_cast<uint32_t*>(base + so[q].base_u);
     c.base_m = reinterpret_cast<uint32_t*>(base + so[q].base_m);
     c.pinmask = reinterpret_cast<uint32_t*>(base + so[q].pinmask);
-    c.upw = reinterpret_cast<uint32_t*>(base + so[q].upw);
     c.upos = reinterpret_cast<int32_t*>(base + so[q].upos);
     c.victim = reinterpret_cast<int32_t*>(base + so[q].victim);
     c.done = reinterpret_cast<uint32_t*>(base + so[q].done);
-    c.arrive = reinterpret_cast<uint32_t*>(base + so[q].arrive);
     c.hist0 = reinterpret_cast<uint32_t*>(base + so[q].hist0);
     c.hist1 = reinterpret_cast<uint32_t*>(base + so[q].hist1);
     c.cand = reinterpret_cast<i32x2*>(base + so[q].cand);
     c.cand_n = reinterpret_cast<uint32_t*>(base + so[q].cand_n);
+    c.rowdig = reinterpret_cast<int32_t*>(base + so[q].rowdig);
     if (hipMemset(c.sel, 0xFF, (size_t)RK * 4) != hipSuccess || hipMemset(c.map, 0xFF, (size_t)RK * 4) != hipSuccess)
       return bail(DSA_E_HIP, "hipMemset");
   }
