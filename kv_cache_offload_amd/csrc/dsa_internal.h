@@ -75,7 +75,7 @@ struct ScratchT {
   P<uint32_t> base_u;       // [P_pad/32] union entries before each 32-position word
   P<uint32_t> base_m;       // [P_pad/32] misses before each word
   P<uint32_t> pinmask;      // [S_pad/32] slots pinned this round (cleared by the scan)
-  P<int32_t> victim;        // [S_pad] slot given to the k-th miss of the step
+  P<i32x2> victim;          // [S_pad] (slot, position it held or -1) given to the k-th miss of the step
   P<uint32_t> hist0;        // [kHistReps][R_max][2048] first-digit histogram replicas (zeroed after use)
   P<uint32_t> hist1;        // [R_max][2048] second-digit histogram within the first-digit bin
   P<i32x2> cand;            // [R_max][P_pad] top-k candidates (key, position), by chunk, in position order

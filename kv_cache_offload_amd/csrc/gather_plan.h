@@ -71,6 +71,7 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
                                          const PlanState& ps, uint32_t* lds) {
   __shared__ uint32_t sh[4 * kPlanWaves];
   __shared__ int s_hand;
+  __shared__ uint32_t s_evict;
   const int tid = threadIdx.x;
   const int64_t L = ps.L, M = ps.M;
   const int32_t round = ps.round;
@@ -146,7 +147,10 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
 
   // Unpinned slots in ring order from the hand; victim[k] for the misses that get one.
   uint32_t n_assigned = 0;
-  if (tid == 0) s_hand = hand;
+  if (tid == 0) {
+    s_hand = hand;
+    s_evict = 0;
+  }
   if (off) {
     uint32_t cnt = 0;
     if (slots_in_regs) {
@@ -171,14 +175,20 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
         const uint32_t kj = s_k[j];
         if (kj >= n_assigned) break;                   // k_j never decreases with j
         const uint32_t bits = s_bits[j];
+        bool evicts = false;
         if ((bits >> bit) & 1u) {
           const uint32_t kk = kj + __popc(bits & ((1u << bit) - 1u));
           if (kk < n_assigned) {
             const int v = (hand + 32 * j + bit) % S;
-            s.victim[kk] = v;
+            const int32_t old = u.slot_pos[v];         // the position the slot gives up
+            s.victim[kk] = (i32x2){v, old};
+            evicts = old >= 0;
             if (kk + 1 == n_assigned) s_hand = (v + 1) % S;
           }
         }
+        // the two half-waves may leave the loop at different j: each counts its own half
+        const uint32_t eb = (uint32_t)(__ballot(evicts) >> (tid & 32));
+        if (bit == 0 && eb) atomicAdd(&s_evict, (uint32_t)__popc(eb));
       }
     } else {
       for (int j = j0, e = 0; j < j1 && k < n_assigned; ++j, ++e) {
@@ -188,7 +198,9 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
           const int b = __ffs(bits) - 1;
           bits &= bits - 1;
           const int v = (hand + 32 * j + b) % S;
-          s.victim[k] = v;
+          const int32_t old = u.slot_pos[v];
+          s.victim[k] = (i32x2){v, old};
+          if (old >= 0) atomicAdd(&s_evict, 1u);
           if (k + 1 == n_assigned) s_hand = (v + 1) % S;
           ++k;
         }
@@ -208,7 +220,7 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
       case 2: cn = off ? n_ring : 0; break;
       case 3: cn = n_assigned; break;
       case 4: cn = noslot; break;
-      case 5: cn = 0; break;                           // evictions: added by the gather
+      case 5: cn = off ? s_evict : 0; break;
       case 6: cn = off ? ((int64_t)n_assigned + noslot) * rb : 0; break;
       default: cn = off ? 0 : U; break;
     }

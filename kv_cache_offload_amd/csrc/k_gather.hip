@@ -79,7 +79,6 @@ __global__ __launch_bounds__(kGatherThreads) void gather_assign_kernel(GatherKAr
     s.selmask[w] = 0;
     if (hw) s.hitmask[w] = 0;
   }
-  bool evicted = false;
   if (mine) {
     const uint32_t below = bit - 1u;
     const uint32_t ux = bu + __popc(sw & below);
@@ -100,13 +99,10 @@ __global__ __launch_bounds__(kGatherThreads) void gather_assign_kernel(GatherKAr
         src = (int32_t)p;
         if (k < n_assigned) {
           kind = SRC_MISS;
-          const int32_t v = s.victim[k];
+          const i32x2 vo = s.victim[k];                // (slot, position it held), from the plan
+          const int32_t v = vo.x, old = vo.y;
           if (v >= 0 && v < ka.S) {
-            const int32_t old = u.slot_pos[v];
-            if (old >= 0 && old < ka.max_positions) {
-              u.pos_slot[old] = -1;
-              evicted = true;
-            }
+            if (old >= 0 && old < ka.max_positions) u.pos_slot[old] = -1;
             u.slot_pos[v] = (int32_t)p;
             u.pos_slot[p] = v;
             u.fill_round[v] = round;
@@ -125,11 +121,6 @@ __global__ __launch_bounds__(kGatherThreads) void gather_assign_kernel(GatherKAr
       s.src[ux] = src;
       s.fill[ux] = fill;
     }
-  }
-  const uint64_t evb = __ballot(evicted);
-  if (lane == 0 && evb) {
-    g_add(&s.counters[5], (int64_t)__popcll(evb));
-    g_add(&u.totals[5], (int64_t)__popcll(evb));
   }
 }
 

@@ -301,7 +301,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     so[q].base_m = take((size_t)P / 32 * 4);
     so[q].pinmask = take((size_t)g.s_words * 4);
     so[q].upos = take((size_t)P * 4);
-    so[q].victim = take((size_t)g.s_words * 32 * 4);
+    so[q].victim = take((size_t)g.s_words * 32 * 8);
     so[q].done = take(4);
     so[q].hist0 = take((size_t)kHistReps * g.r_max * kRadixBins * 4);
     so[q].hist1 = take((size_t)g.r_max * kRadixBins * 4);
@@ -386,7 +386,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     c.base_m = reinterpret_cast<uint32_t*>(base + so[q].base_m);
     c.pinmask = reinterpret_cast<uint32_t*>(base + so[q].pinmask);
     c.upos = reinterpret_cast<int32_t*>(base + so[q].upos);
-    c.victim = reinterpret_cast<int32_t*>(base + so[q].victim);
+    c.victim = reinterpret_cast<i32x2*>(base + so[q].victim);
     c.done = reinterpret_cast<uint32_t*>(base + so[q].done);
     c.hist0 = reinterpret_cast<uint32_t*>(base + so[q].hist0);
     c.hist1 = reinterpret_cast<uint32_t*>(base + so[q].hist1);
