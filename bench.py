@@ -147,9 +147,12 @@ def algorithmic_bytes(w, kind, n_steps, L0, cnt, long_hist):
     if kind == "topk_resolve":
         return R * K * 4                                   # the selection out
     if kind == "gather":
-        return (hit + ring + res + miss + noslot) * rb + U * rb + miss * rb + wb
+        # union bookkeeping: descriptor + union arrays per entry, victim and slot-table entries per miss
+        return U * (16 + 12) + miss * (8 + 16) + wb
     if kind == "attention":
-        return R * K * rb + R * H * (512 + 64) * 2
+        # every selected row read from its source (slot, ring, host mirror, HBM row store), the compact
+        # copy and the misses' slot fills written, the queries read
+        return R * K * rb + U * rb + miss * rb + R * H * (512 + 64) * 2
     if kind == "attention_merge":
         return R * H * 512 * 4
     if kind == "append":

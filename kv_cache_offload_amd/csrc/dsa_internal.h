@@ -62,7 +62,6 @@ struct ScratchT {
   P<int32_t> uni;           // [R_max*K]
   P<int32_t> kind;          // [R_max*K]
   P<int32_t> src;           // [R_max*K]
-  P<int32_t> fill;          // [R_max*K] slot a miss fills (-1: none)
   P<int32_t> map;           // [R_max][K]
   P<uint8_t> compact;       // [R_max*K][row_bytes]
   P<float> part_o;          // [R_max][nsplit_max][H][latent]
@@ -71,7 +70,7 @@ struct ScratchT {
   P<int64_t> info;          // [8] see kInfo* below
   P<uint32_t> selmask;      // [P_pad/32] positions selected by any row this step (cleared by the assign)
   P<uint32_t> hitmask;      // [P_pad/32] selected positions that hit a slot (cleared by the assign)
-  P<int32_t> upos;          // [P_pad] union index of each selected position (valid for this step's selection)
+  P<i32x4> pdesc;           // [P_pad] per selected position: union index, kind, source, slot to fill (this step)
   P<uint32_t> base_u;       // [P_pad/32] union entries before each 32-position word
   P<uint32_t> base_m;       // [P_pad/32] misses before each word
   P<uint32_t> pinmask;      // [S_pad/32] slots pinned this round (cleared by the scan)

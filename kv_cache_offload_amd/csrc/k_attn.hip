@@ -44,12 +44,14 @@ typedef __bf16 bfx2 __attribute__((ext_vector_type(2)));
 #define DSA_LDS __attribute__((address_space(3)))
 
 constexpr int kSplit = 64;             // selected rows per workgroup
-constexpr int kMT = kSplit / 16;       // 16-row tiles of the logits
+constexpr int kBlk = 32;               // rows per staged block (online softmax over the blocks)
+constexpr int kNBlk = kSplit / kBlk;
+constexpr int kRowPieces = kCopyChunks16;            // 16-byte pieces of a 656-byte row
+constexpr int kBlkPieces = kBlk * kRowPieces;
 constexpr int kLatStride = 536;        // bf16 per row of the latent in LDS (512 + 24: no bank conflicts
                                        // for the row reads of the logits nor the transpose reads)
 constexpr int kRopeStride = 72;        // bf16 per row of RoPE (64 + 8)
 constexpr int kMaxSplits = 4096 / kSplit;
-constexpr int kSidePieces = kSplit * 9;  // 16-byte pieces of scales + RoPE
 
 struct AttnKArgs {
   StepArgs a;
@@ -57,6 +59,7 @@ struct AttnKArgs {
   const uint16_t* q_rope;    // [n_seqs][R][H][64]
   float* out;                // [n_seqs][R][H][512]
   int K, H, nsplit, ns_stride, row_bytes;
+  int S, ring_cap, max_union;
   int64_t max_positions;
   float scale_log2;          // softmax_scale * log2(e)
 };
@@ -104,21 +107,55 @@ __device__ inline bf16x4 read_tr(const uint16_t* lat_s, int r0, int col0, int la
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   constexpr int NT = NW * 64;
-  constexpr int LP = kSplit * 32 / NT;                    // latent pieces per thread
-  constexpr int SP = (kSidePieces + NT - 1) / NT;         // side pieces per thread
-  __shared__ __align__(16) uint16_t lat_s[kSplit * kLatStride];
-  __shared__ __align__(16) uint16_t rope_s[kSplit * kRopeStride];
-  __shared__ __align__(16) float scl_s[8 * kSplit];
-  __shared__ int s_idx[kSplit];
+  constexpr int PPT = (kBlkPieces + NT - 1) / NT;        // row pieces per thread per block
+  __shared__ __align__(16) uint16_t lat_s[kNBlk][kBlk * kLatStride];
+  __shared__ __align__(16) uint16_t rope_s[kNBlk][kBlk * kRopeStride];
+  __shared__ __align__(16) float scl_s[kNBlk][8 * kBlk];
+  __shared__ const DSA_GLOBAL uint8_t* s_from[kSplit];   // where each row is read from (null: masked)
+  __shared__ int s_ux[kSplit];                            // its compact row, -1 if masked
+  __shared__ int s_fill[kSplit];                          // the slot a miss fills, -1 if none
 
   const StepArgs& a = ka.a;
   const int split = blockIdx.x, r = blockIdx.y, seq = blockIdx.z;
+  const UnitG u = unit_of(a, seq);
   const ScratchG s = scratch_of(a, seq);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, q4 = lane >> 4;
   const int H = ka.H;
   const int h0 = wave * 16;
   const int64_t rb = ka.row_bytes;
+  const int j_begin = split * kSplit;
+
+  // The split's rows: position (selection), then the gather's descriptor of the
+  // position -- compact row, source kind, source index, slot to fill -- from
+  // which the row's address follows: a hit from its HBM slot, a ring row from
+  // the recent ring, a miss from the host mirror (repeated misses of the same
+  // round each read host memory), a resident row from the HBM row store.  The
+  // map entry of every selected index of the split is written here.
+  const int n_sel = s.sel_n[r];
+  if (tid < kSplit) {
+    const int j = j_begin + tid;
+    const int32_t pos = j < ka.K ? s.sel[(int64_t)r * ka.K + j] : -1;
+    const bool ok = j < n_sel && pos >= 0 && pos < ka.max_positions;
+    const i32x4 d = s.pdesc[ok ? pos : 0];
+    const int32_t ux = d.x, kind = d.y, src = d.z, fill = d.w;
+    const DSA_GLOBAL uint8_t* from = nullptr;
+    if (ok && ux >= 0 && ux < ka.max_union) {
+      if (kind == SRC_HIT) {
+        if (src >= 0 && src < ka.S) from = u.slots + (int64_t)src * rb;
+      } else if (kind == SRC_RING) {
+        if (src >= 0 && src < ka.ring_cap) from = u.ring + (int64_t)src * rb;
+      } else if (kind == SRC_MISS || kind == SRC_MISS_NOSLOT || kind == SRC_RES) {
+        if (src >= 0 && src < ka.max_positions) from = u.rows + (int64_t)src * rb;
+      }
+    }
+    s_from[tid] = from;
+    s_ux[tid] = from ? ux : -1;
+    s_fill[tid] = (from && kind == SRC_MISS && fill >= 0 && fill < ka.S) ? fill : -1;
+    if (j < ka.K) s.map[(int64_t)r * ka.K + j] = from ? ux : -1;
+  }
+  if (j_begin >= n_sel) return;                          // (uniform) map entries written above
+  const int nrows = min(n_sel - j_begin, kSplit);
 
   // Query fragments (B operand of the logits): lane holds Q[h0 + l16][32 ks + 8 q4 .. +7].
   bf16x8 qa[18];
@@ -131,183 +168,192 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) qa[16 + ks] = *reinterpret_cast<const bf16x8*>(qr + 32 * ks);
   }
-
-  const int n_sel = s.sel_n[r];
-  const int j_begin = split * kSplit;
-  if (j_begin >= n_sel) return;
-  const int nrows = min(n_sel - j_begin, kSplit);
-
-  // Compact-row index of every selected row of the split (the gather's map,
-  // range-checked there: -1 or a row below the union size).
-  const auto map = s.map + (int64_t)r * ka.K;
-  for (int j = tid; j < kSplit; j += NT) s_idx[j] = j < nrows ? map[j_begin + j] : -1;
   __syncthreads();
 
-  // Stage the 64 rows: latent piece p (16 bytes): row p / 32, bytes 16 (p % 32)..;
-  // side piece q: row q / 9, part q % 9 (0: the 8 scales, 1..8: 16 bytes of RoPE).
-  // Rows past the split's end, or with no valid union index, read compact row 0
-  // (it exists whenever a split has work); their logits are masked, so their
-  // values never reach the output.
-  {
-    u32x4 lat[LP], side[SP];
+  // Every 16-byte piece of a block is requested at once.  Block b + 1 is
+  // requested as soon as block b has arrived, before block b is computed: the
+  // host link then serves every workgroup's first block before any second
+  // block, and the first blocks are computed while the second ones arrive.
+  // Piece q of a block: row q / 41, bytes 16 (q % 41) .. ; masked rows read the
+  // unit's key store (always mapped) and are zeroed below.
+  u32x4 raw[kNBlk][PPT];
+  auto request = [&](int b) {
 #pragma unroll
-    for (int p = 0; p < LP; ++p) {
-      const int piece = tid + p * NT;
-      const int id = s_idx[piece >> 5];
-      lat[p] = *reinterpret_cast<const DSA_GLOBAL u32x4*>(s.compact + (id >= 0 ? id : 0) * rb + 16 * (piece & 31));
+    for (int e = 0; e < PPT; ++e) {
+      const int q = min(tid + e * NT, kBlkPieces - 1);
+      const int row = b * kBlk + q / kRowPieces, part = q % kRowPieces;
+      const DSA_GLOBAL uint8_t* from = s_from[row];
+      const DSA_GLOBAL uint8_t* at = from ? from + 16 * part : reinterpret_cast<const DSA_GLOBAL uint8_t*>(u.keys);
+      raw[b][e] = *reinterpret_cast<const DSA_GLOBAL u32x4*>(at);
     }
-#pragma unroll
-    for (int q = 0; q < SP; ++q) {
-      const int piece = min(tid + q * NT, kSidePieces - 1);
-      const int row = piece / 9, part = piece % 9;
-      const int id = s_idx[row];
-      side[q] = *reinterpret_cast<const DSA_GLOBAL u32x4*>(s.compact + (id >= 0 ? id : 0) * rb + 512 +
-                                                           (part ? 16 * part : 0));
-    }
-#pragma unroll
-    for (int p = 0; p < LP; ++p) {
-      const int piece = tid + p * NT;
-      const int row = piece >> 5, c16 = piece & 31;
-      uint32_t w[8];
-      widen16(lat[p], w);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(lat_s + row * kLatStride + 16 * c16);
-      *reinterpret_cast<u32x4*>(dst) = (u32x4){w[0], w[1], w[2], w[3]};
-      *reinterpret_cast<u32x4*>(dst + 4) = (u32x4){w[4], w[5], w[6], w[7]};
-    }
-#pragma unroll
-    for (int q = 0; q < SP; ++q) {
-      const int piece = tid + q * NT;
-      if (piece >= kSidePieces) continue;
-      const int row = piece / 9, part = piece % 9;
-      if (part == 0) {
-#pragma unroll
-        for (int g = 0; g < 8; ++g) {
-          const uint32_t word = side[q][g >> 1];
-          scl_s[g * kSplit + row] = f16_bits_to_f32((g & 1) ? (word >> 16) : (word & 0xFFFFu));
-        }
-      } else {
-        *reinterpret_cast<u32x4*>(rope_s + row * kRopeStride + 8 * (part - 1)) = side[q];
-      }
-    }
-  }
-  __syncthreads();
+  };
+  request(0);
 
-  // Logits S^T[j][h]: lane holds rows 16 mt + 4 q4 + v of head h0 + l16.  The four
-  // row tiles are independent chains; each 64-dim group is scaled per row.
-  float lg[kMT][4];
-  {
-    f32x4 sacc[kMT];
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) sacc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      f32x4 acc[kMT];
-#pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int ks = 2 * g + kk;
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(lat_s + (16 * mt + l16) * kLatStride + 32 * ks + 8 * q4);
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qa[ks], acc[mt], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) {
-        const f32x4 sc = *reinterpret_cast<const f32x4*>(scl_s + g * kSplit + 16 * mt + 4 * q4);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) sacc[mt][v] += sc[v] * acc[mt][v];
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(rope_s + (16 * mt + l16) * kRopeStride + 32 * kk + 8 * q4);
-        sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qa[16 + kk], sacc[mt], 0, 0, 0);
-      }
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int j = 16 * mt + 4 * q4 + v;
-        lg[mt][v] = (j < nrows && s_idx[j] >= 0) ? sacc[mt][v] * ka.scale_log2 : -INFINITY;
-      }
-  }
-
-  // Softmax of head h0 + l16 over the 64 rows (they sit in the 4 lane groups).
-  float mx = -INFINITY;
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) mx = fmaxf(mx, lg[mt][v]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const bool none = mx == -INFINITY;
-  float p[kMT][4];
-  float ps = 0.f;
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      p[mt][v] = none ? 0.f : exp2f(lg[mt][v] - mx);
-      ps += p[mt][v];
-    }
-  ps += __shfl_xor(ps, 16);
-  ps += __shfl_xor(ps, 32);
-
-  // O[h][d] = sum_j (p[h][j] * scale_j[g]) * int8_j[d].  For the 32-row half kc
-  // the A fragment of head h0 + l16 holds rows 32 kc + {4 q4 .. 4 q4 + 3,
-  // 16 + 4 q4 .. 16 + 4 q4 + 3}, in that order; the B fragments match it.
   f32x4 o[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;                  // of head h0 + l16
+
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    bf16x8 pa_hi[2], pa_lo[2];
+  for (int b = 0; b < kNBlk; ++b) {
+    uint16_t* lat = lat_s[b];
+    uint16_t* rope = rope_s[b];
+    float* scl = scl_s[b];
+    // This block's rows: the compact copy and a miss's slot fill (the gather's
+    // writes), and the LDS staging -- the int8 latent widened to bf16, the
+    // scales as fp32, the RoPE as is.
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const f32x4 sa = *reinterpret_cast<const f32x4*>(scl_s + g * kSplit + 32 * kc + 4 * q4);
-      const f32x4 sb = *reinterpret_cast<const f32x4*>(scl_s + g * kSplit + 32 * kc + 16 + 4 * q4);
-      float pv[8];
+    for (int e = 0; e < PPT; ++e) {
+      const int q = tid + e * NT;
+      if (q >= kBlkPieces) continue;
+      const int rl = q / kRowPieces, part = q % kRowPieces, row = b * kBlk + rl;
+      const int ux = s_ux[row];
+      const u32x4 v = ux >= 0 ? raw[b][e] : (u32x4){0u, 0u, 0u, 0u};
+      if (ux >= 0) {
+        *reinterpret_cast<DSA_GLOBAL u32x4*>(s.compact + (int64_t)ux * rb + 16 * part) = v;
+        const int f = s_fill[row];
+        if (f >= 0) *reinterpret_cast<DSA_GLOBAL u32x4*>(u.slots + (int64_t)f * rb + 16 * part) = v;
+      }
+      if (part < 32) {
+        uint32_t w[8];
+        widen16(v, w);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(lat + rl * kLatStride + 16 * part);
+        *reinterpret_cast<u32x4*>(dst) = (u32x4){w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4*>(dst + 4) = (u32x4){w[4], w[5], w[6], w[7]};
+      } else if (part == 32) {
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          const uint32_t word = v[g >> 1];
+          scl[g * kBlk + rl] = f16_bits_to_f32((g & 1) ? (word >> 16) : (word & 0xFFFFu));
+        }
+      } else {
+        *reinterpret_cast<u32x4*>(rope + rl * kRopeStride + 8 * (part - 33)) = v;
+      }
+    }
+    if (b + 1 < kNBlk) request(b + 1);
+    __syncthreads();
+
+    // Logits S^T[j][h]: lane holds rows 16 mt + 4 q4 + v of head h0 + l16; each
+    // 64-dim group is accumulated separately and scaled by its fp32 scale per row.
+    float lg[2][4];
+    {
+      f32x4 sacc[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) sacc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        f32x4 acc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int ks = 2 * g + kk;
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            const bf16x8 av = *reinterpret_cast<const bf16x8*>(lat + (16 * mt + l16) * kLatStride + 32 * ks + 8 * q4);
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qa[ks], acc[mt], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const f32x4 sc = *reinterpret_cast<const f32x4*>(scl + g * kBlk + 16 * mt + 4 * q4);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sacc[mt][v] += sc[v] * acc[mt][v];
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(rope + (16 * mt + l16) * kRopeStride + 32 * kk + 8 * q4);
+          sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qa[16 + kk], sacc[mt], 0, 0, 0);
+        }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int j = b * kBlk + 16 * mt + 4 * q4 + v;
+          lg[mt][v] = (j < nrows && s_ux[j] >= 0) ? sacc[mt][v] * ka.scale_log2 : -INFINITY;
+        }
+    }
+
+    // Online softmax of head h0 + l16 (the block's 32 rows sit in the 4 lane groups).
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, lg[mt][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const bool none = m_new == -INFINITY;
+    const float alpha = none ? 1.f : exp2f(m_run - m_new);
+    float p[2][4];
+    float ps = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        pv[v] = p[2 * kc][v] * sa[v];
-        pv[4 + v] = p[2 * kc + 1][v] * sb[v];
+        p[mt][v] = none ? 0.f : exp2f(lg[mt][v] - m_new);
+        ps += p[mt][v];
       }
-      uint32_t hi[4], lo[4];
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    if (b > 0) {
+      // O rows are heads h0 + 4 q4 + v: their alphas come from lanes 4 q4 + v
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hi[e] = pack_bf16(pv[2 * e], pv[2 * e + 1]);
-        lo[e] = pack_bf16(pv[2 * e] - bf16_lo_to_f32(hi[e]), pv[2 * e + 1] - bf16_hi_to_f32(hi[e]));
+      for (int v = 0; v < 4; ++v) {
+        const float av = __shfl(alpha, 4 * q4 + v);
+#pragma unroll
+        for (int nt = 0; nt < 32; ++nt) o[nt][v] *= av;
       }
-      __builtin_memcpy(&pa_hi[kc], hi, 16);
-      __builtin_memcpy(&pa_lo[kc], lo, 16);
     }
+
+    // O[h][d] += sum_j (p[h][j] * scale_j[g]) * int8_j[d].  The A fragment of
+    // head h0 + l16 holds rows {4 q4 .. 4 q4 + 3, 16 + 4 q4 .. 16 + 4 q4 + 3}, in
+    // that order; the B fragments (LDS transpose reads) match it.
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const int nt = 4 * g + t4;
-      bf16x8 bv[2];
+    for (int g = 0; g < 8; ++g) {
+      bf16x8 pa_hi, pa_lo;
+      {
+        const f32x4 sa = *reinterpret_cast<const f32x4*>(scl + g * kBlk + 4 * q4);
+        const f32x4 sb = *reinterpret_cast<const f32x4*>(scl + g * kBlk + 16 + 4 * q4);
+        float pv[8];
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const bf16x4 b0 = read_tr(lat_s, 32 * kc + 4 * q4, 16 * nt, lane);
-        const bf16x4 b1 = read_tr(lat_s, 32 * kc + 16 + 4 * q4, 16 * nt, lane);
-        bv[kc] = (bf16x8){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        for (int v = 0; v < 4; ++v) {
+          pv[v] = p[0][v] * sa[v];
+          pv[4 + v] = p[1][v] * sb[v];
+        }
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hi[e] = pack_bf16(pv[2 * e], pv[2 * e + 1]);
+          lo[e] = pack_bf16(pv[2 * e] - bf16_lo_to_f32(hi[e]), pv[2 * e + 1] - bf16_hi_to_f32(hi[e]));
+        }
+        __builtin_memcpy(&pa_hi, hi, 16);
+        __builtin_memcpy(&pa_lo, lo, 16);
       }
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi[kc], bv[kc], o[nt], 0, 0, 0);
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo[kc], bv[kc], o[nt], 0, 0, 0);
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const int nt = 4 * g + t4;
+        const bf16x4 b0 = read_tr(lat, 4 * q4, 16 * nt, lane);
+        const bf16x4 b1 = read_tr(lat, 16 + 4 * q4, 16 * nt, lane);
+        const bf16x8 bv = (bf16x8){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, bv, o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, bv, o[nt], 0, 0, 0);
       }
     }
   }
+  const float mx = m_run, ps = l_run;
 
   // o[nt][v] = O[h0 + 4 q4 + v][16 nt + l16]; (max, sum) of head h0 + l16 in every lane group
   if (ka.nsplit == 1) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const float inv = 1.f / __shfl(ps, 4 * q4 + v);
+      const float den = __shfl(ps, 4 * q4 + v);
+      const float inv = den > 0.f ? 1.f / den : 0.f;
       float* dst = ka.out + (((int64_t)seq * a.R + r) * H + h0 + 4 * q4 + v) * 512;
 #pragma unroll
       for (int nt = 0; nt < 32; ++nt) dst[nt * 16 + l16] = o[nt][v] * inv;
@@ -332,29 +378,32 @@ struct MergeKArgs {
   int H, ns_stride;
 };
 
-// One workgroup per (16-dim tile nt, 16-head group hg, query row):
+// One workgroup per (16-dim tile nt, 16-head group hg, query row), for at most
+// MAXS splits:
 // out[h][d] = sum_s w_s[h] O_s[h][d] with w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s'.
 // Thread (l16, hl) reads element (l16, 16 hg + hl) of each split's [16][H] tile;
 // the sums leave through LDS as [h][16] (16 contiguous floats per head).
+template <int MAXS>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
-  __shared__ float wgt[kMaxSplits * 16];      // [split][hl]: the max, then the weight
-  __shared__ float sl[kMaxSplits * 16];       // [split][hl]: the sum
+  __shared__ float wgt[MAXS * 16];            // [split][hl]: the max, then the weight
+  __shared__ float sl[MAXS * 16];             // [split][hl]: the sum
   __shared__ float tile[16 * 17];
   const StepArgs& a = ka.a;
   const int n_hg = ka.H / 16;
   const int nt = blockIdx.x / n_hg, hg = blockIdx.x % n_hg, r = blockIdx.y, seq = blockIdx.z;
   const ScratchG s = scratch_of(a, seq);
   const int H = ka.H;
-  const int used = (s.sel_n[r] + kSplit - 1) / kSplit;
+  const int used = min(MAXS, (s.sel_n[r] + kSplit - 1) / kSplit);
+  if (used < 1) return;                                  // (uniform) no selection: nothing to merge
   const int tid = threadIdx.x;
   const int l16 = tid / 16, hl = tid % 16;
   // this thread's element of every split, loaded before the weights are known
   // (splits past `used` re-read the last one and get weight 0)
   const auto src = s.part_o + (((int64_t)r * ka.ns_stride * 32 + nt) * 16 + l16) * H + 16 * hg + hl;
   const int64_t split_stride = (int64_t)32 * 16 * H;
-  float x[kMaxSplits];
+  float x[MAXS];
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp) x[sp] = src[(sp < used ? sp : used - 1) * split_stride];
+  for (int sp = 0; sp < MAXS; ++sp) x[sp] = src[(sp < used ? sp : used - 1) * split_stride];
   for (int t = tid; t < used * 16; t += 256) {            // every split's (max, sum) at once
     const int sp = t / 16, h = t % 16;
     const int64_t base = ((int64_t)r * ka.ns_stride + sp) * H + 16 * hg + h;
@@ -377,7 +426,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
   __syncthreads();
   float acc = 0.f;
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp) acc += (sp < used ? wgt[sp * 16 + hl] : 0.f) * x[sp];
+  for (int sp = 0; sp < MAXS; ++sp) acc += (sp < used ? wgt[sp * 16 + hl] : 0.f) * x[sp];
   tile[hl * 17 + l16] = acc;
   __syncthreads();
   {
@@ -391,8 +440,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
 hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_lat, const uint16_t* q_rope,
                        float* out, hipStream_t st) {
   const int nsplit = (g.top_k + kSplit - 1) / kSplit;
-  AttnKArgs ka{a, q_lat, q_rope, out, g.top_k, g.heads, nsplit, g.nsplit_max, g.row_bytes, g.max_positions,
-               g.softmax_scale * 1.4426950408889634f};
+  AttnKArgs ka{a, q_lat, q_rope, out, g.top_k, g.heads, nsplit, g.nsplit_max, g.row_bytes,
+               g.hot_slots, g.ring_cap, g.r_max * g.top_k, g.max_positions, g.softmax_scale * 1.4426950408889634f};
   dim3 grid((unsigned)nsplit, (unsigned)a.R, (unsigned)a.n_seqs);
   switch (g.heads) {
     case 16: return launch_k(attn_kernel<1>, grid, dim3(64), 0, st, ka);
@@ -406,8 +455,10 @@ hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_l
 hipError_t launch_attn_merge(const Geometry& g, const StepArgs& a, float* out, hipStream_t st) {
   if ((g.top_k + kSplit - 1) / kSplit == 1) return hipSuccess;
   MergeKArgs ka{a, out, g.heads, g.nsplit_max};
-  return launch_k(attn_merge_kernel, dim3(32u * (unsigned)(g.heads / 16), (unsigned)a.R, (unsigned)a.n_seqs), dim3(256),
-                  0, st, ka);
+  const dim3 grid(32u * (unsigned)(g.heads / 16), (unsigned)a.R, (unsigned)a.n_seqs);
+  const int nsplit = (g.top_k + kSplit - 1) / kSplit;
+  if (nsplit <= 32) return launch_k(attn_merge_kernel<32>, grid, dim3(256), 0, st, ka);
+  return launch_k(attn_merge_kernel<kMaxSplits>, grid, dim3(256), 0, st, ka);
 }
 
 }  // namespace dsa

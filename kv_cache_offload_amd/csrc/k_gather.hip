@@ -17,22 +17,24 @@
 //
 // gfx950 design.  Selection, classification and pinning happen where the
 // selection is produced: the Top-K kernel sets, for every selected position, a
-// bit in a per-position selection bitmap (so a position several rows select is
-// one union entry -- "repeated misses read host memory" holds structurally: one
-// host read per distinct position), classifies it against the round-start
-// state (a hit needs a slot filled in an earlier round) and pins the hit's
-// slot.  The last Top-K workgroup of the sequence then runs the gather plan
-// (gather_plan.h): prefix counts per 32-position word and the victim list.
-// The assign kernel is wide: one wave per 64 positions, one lane per position.
-// Each selected lane computes its union index, kind and source; the k-th miss
-// in ascending position order takes victim[k], evicts the position the slot
-// held and updates the slot table.  The copy kernel is wide too: one thread
-// per 16-byte piece of a row (so every load of the step is in flight at once),
-// from the hot slot, the ring, or the host mirror (zero-copy reads of pinned
-// host memory over the host link), to the compact buffer and, for a miss that
-// got a slot, to the slot as well; it also writes the pending 64 ring rows
-// back to the mirror when a batch is due.  No thread reads a slot filled in
-// the same round: victims are unpinned, hits are pinned.
+// bit in a per-position selection bitmap (a position several rows select is
+// one union entry), classifies it against the round-start state (a hit needs a
+// slot filled in an earlier round) and pins the hit's slot.  The last Top-K
+// workgroup of the sequence then runs the gather plan (gather_plan.h): prefix
+// counts per 32-position word and the victim list.  The assign kernel is wide:
+// one wave per 64 positions, one lane per position.  Each selected lane
+// computes its union index, kind and source; the k-th miss in ascending
+// position order takes victim[k], evicts the position the slot held and
+// updates the slot table; the lane leaves a descriptor of the position (union
+// index, kind, source, slot to fill).  The row copies themselves are done by
+// the attention kernel while it stages the rows (k_attn.hip): one 16-byte
+// piece per thread, from the hot slot, the ring, or the host mirror (zero-copy
+// reads of pinned host memory over the host link; a miss that several query
+// rows select is read from host memory by each of them, as the page's rule for
+// repeated misses has it), to LDS, the compact buffer and, for a miss that got
+// a slot, to the slot.  No reader consults a slot filled in the same round:
+// victims are unpinned, hits are pinned.  When a batch is due, the assign
+// kernel's last blocks write the 64 oldest ring rows back to the mirror.
 #include "gather_plan.h"
 
 namespace dsa {
@@ -44,15 +46,31 @@ struct GatherKArgs {
   StepArgs a;
   int S, ring_cap, ring_rows, mode, row_bytes, K;
   int max_union;                        // R_max * K: compact rows in the scratch
+  int word_blocks;                      // blocks of the union/slot-table part; the rest write back the ring
   int64_t max_positions;
 };
 
 // Union entries and slot table: one wave per 64 positions, one lane per position.
+// The last blocks write the 64 oldest pending ring rows back to the host mirror
+// when a batch is due (positions the step reads from the ring, never from the
+// mirror).
 __global__ __launch_bounds__(kGatherThreads) void gather_assign_kernel(GatherKArgs ka) {
   const StepArgs& a = ka.a;
   const int seq = blockIdx.y;
   const UnitG u = unit_of(a, seq);
   const ScratchG s = scratch_of(a, seq);
+  if ((int)blockIdx.x >= ka.word_blocks) {
+    const int64_t wb = s.info[kInfoWriteback];
+    if (wb < 0) return;
+    const int64_t t = (int64_t)(blockIdx.x - ka.word_blocks) * kGatherThreads + threadIdx.x;
+    if (t >= (int64_t)ka.ring_rows * kCopyChunks16) return;
+    const int64_t rb = ka.row_bytes;
+    const int64_t p = wb + t / kCopyChunks16, c = t % kCopyChunks16;
+    if (p >= ka.max_positions) return;
+    const u32x4 v = *reinterpret_cast<const DSA_GLOBAL u32x4*>(u.ring + (p % ka.ring_cap) * rb + c * 16);
+    *reinterpret_cast<DSA_GLOBAL u32x4*>(u.rows + p * rb + c * 16) = v;
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int64_t wave_id = ((int64_t)blockIdx.x * kGatherThreads + threadIdx.x) >> 6;
   const int64_t L = u.dyn[0];
@@ -116,63 +134,9 @@ __global__ __launch_bounds__(kGatherThreads) void gather_assign_kernel(GatherKAr
     }
     if (ux < (uint32_t)ka.max_union) {                 // always true for a consistent plan
       s.uni[ux] = (int32_t)p;
-      s.upos[p] = (int32_t)ux;
       s.kind[ux] = kind;
       s.src[ux] = src;
-      s.fill[ux] = fill;
-    }
-  }
-}
-
-// Row copies, one thread per 16-byte piece: compact <- slot / ring / host
-// mirror / HBM row store; a miss that got a slot fills the slot too.  Then the
-// ring writeback of the 64 oldest pending rows when a batch is due, and the
-// map: the compact row of every (query row, selected index), -1 past the
-// row's selection.
-__global__ __launch_bounds__(kGatherThreads) void copy_kernel(GatherKArgs ka) {
-  const StepArgs& a = ka.a;
-  const int seq = blockIdx.y;
-  const UnitG u = unit_of(a, seq);
-  const ScratchG s = scratch_of(a, seq);
-  const int64_t U = s.info[kInfoUnion];
-  const int64_t wb = s.info[kInfoWriteback];
-  const int64_t rb = ka.row_bytes;
-  const int64_t n_gather = U * kCopyChunks16;
-  const int64_t n_wb = wb >= 0 ? (int64_t)ka.ring_rows * kCopyChunks16 : 0;
-  const int64_t n_map = (int64_t)a.R * ka.K;
-  const int64_t total = n_gather + n_wb + n_map;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * blockDim.x) {
-    if (t < n_gather) {
-      const int64_t x = t / kCopyChunks16, c = t % kCopyChunks16;
-      const int32_t kind = s.kind[x];
-      const int64_t src = s.src[x];
-      const int32_t f = s.fill[x];
-      // every source index is range-checked: an inconsistent plan copies nothing
-      const bool ok = x < ka.max_union &&
-                      (kind == SRC_HIT ? (src >= 0 && src < ka.S)
-                       : kind == SRC_RING ? (src >= 0 && src < ka.ring_cap)
-                       : (kind >= 0 && src >= 0 && src < ka.max_positions));
-      if (!ok) continue;
-      const DSA_GLOBAL uint8_t* from = kind == SRC_HIT ? u.slots + src * rb
-                                     : kind == SRC_RING ? u.ring + src * rb
-                                     : u.rows + src * rb;
-      const u32x4 v = *reinterpret_cast<const DSA_GLOBAL u32x4*>(from + c * 16);
-      *reinterpret_cast<DSA_GLOBAL u32x4*>(s.compact + x * rb + c * 16) = v;
-      if (kind == SRC_MISS && f >= 0 && f < ka.S)
-        *reinterpret_cast<DSA_GLOBAL u32x4*>(u.slots + (int64_t)f * rb + c * 16) = v;
-    } else if (t < n_gather + n_wb) {
-      const int64_t i = t - n_gather;
-      const int64_t p = wb + i / kCopyChunks16, c = i % kCopyChunks16;
-      const u32x4 v = *reinterpret_cast<const DSA_GLOBAL u32x4*>(u.ring + (p % ka.ring_cap) * rb + c * 16);
-      *reinterpret_cast<DSA_GLOBAL u32x4*>(u.rows + p * rb + c * 16) = v;
-    } else {
-      const int64_t i = t - n_gather - n_wb;
-      const int r = (int)(i / ka.K), j = (int)(i % ka.K);
-      const int32_t p = s.sel[i];
-      int32_t idx = -1;
-      if (j < s.sel_n[r] && p >= 0 && p < ka.max_positions) idx = s.upos[p];
-      s.map[i] = (idx >= 0 && idx < U) ? idx : -1;
+      s.pdesc[p] = (i32x4){(int32_t)ux, kind, src, fill};
     }
   }
 }
@@ -267,16 +231,14 @@ unsigned grid_for(int64_t work, int64_t cap = 4096) {
 }  // namespace
 
 hipError_t launch_gather(const Geometry& g, const StepArgs& a, hipStream_t st) {
-  GatherKArgs ka{a, g.hot_slots, g.ring_cap, g.ring_rows, g.mode, g.row_bytes, g.top_k, g.r_max * g.top_k,
-                 g.max_positions};
   const int64_t words = (a.l_max + 31) / 32;
   const int64_t waves = (words + 1) / 2;
   const int64_t blocks = (waves + 3) / 4;
-  hipError_t e = launch_k(gather_assign_kernel, dim3((unsigned)blocks, (unsigned)a.n_seqs), dim3(kGatherThreads), 0,
-                          st, ka);
-  if (e != hipSuccess) return e;
-  const int64_t work = (int64_t)a.R * g.top_k * (kCopyChunks16 + 1) + (int64_t)g.ring_rows * kCopyChunks16;
-  return launch_k(copy_kernel, dim3(grid_for(work, 2048), (unsigned)a.n_seqs), dim3(kGatherThreads), 0, st, ka);
+  const int64_t wb_blocks = ((int64_t)g.ring_rows * kCopyChunks16 + kGatherThreads - 1) / kGatherThreads;
+  GatherKArgs ka{a, g.hot_slots, g.ring_cap, g.ring_rows, g.mode, g.row_bytes, g.top_k, g.r_max * g.top_k,
+                 (int)blocks, g.max_positions};
+  return launch_k(gather_assign_kernel, dim3((unsigned)(blocks + (g.mode == 0 ? wb_blocks : 0)), (unsigned)a.n_seqs),
+                  dim3(kGatherThreads), 0, st, ka);
 }
 
 hipError_t launch_append(const Geometry& g, const UnitDev& unit, int64_t L, int64_t M, int64_t newM,

@@ -277,8 +277,8 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     uo[i].dyn = take(32);
     uo[i].totals = take(64);
   }
-  struct ScrOff { size_t scores, sel, sel_n, uni, kind, src, fill, map, compact, po, pml, cnt, info,
-                  selmask, hitmask, base_u, base_m, pinmask, upos, victim, done, hist0, hist1, cand,
+  struct ScrOff { size_t scores, sel, sel_n, uni, kind, src, map, compact, po, pml, cnt, info,
+                  selmask, hitmask, base_u, base_m, pinmask, pdesc, victim, done, hist0, hist1, cand,
                   cand_n, rowdig; };
   std::vector<ScrOff> so(cfg->n_seqs);
   for (int q = 0; q < cfg->n_seqs; ++q) {
@@ -288,7 +288,6 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     so[q].uni = take((size_t)RK * 4);
     so[q].kind = take((size_t)RK * 4);
     so[q].src = take((size_t)RK * 4);
-    so[q].fill = take((size_t)RK * 4);
     so[q].map = take((size_t)RK * 4);
     so[q].compact = take((size_t)RK * rb);
     so[q].po = take((size_t)g.r_max * g.nsplit_max * g.heads * g.latent * 4);
@@ -300,7 +299,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     so[q].base_u = take((size_t)P / 32 * 4);
     so[q].base_m = take((size_t)P / 32 * 4);
     so[q].pinmask = take((size_t)g.s_words * 4);
-    so[q].upos = take((size_t)P * 4);
+    so[q].pdesc = take((size_t)P * 16);
     so[q].victim = take((size_t)g.s_words * 32 * 8);
     so[q].done = take(4);
     so[q].hist0 = take((size_t)kHistReps * g.r_max * kRadixBins * 4);
@@ -373,7 +372,6 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     c.uni = reinterpret_cast<int32_t*>(base + so[q].uni);
     c.kind = reinterpret_cast<int32_t*>(base + so[q].kind);
     c.src = reinterpret_cast<int32_t*>(base + so[q].src);
-    c.fill = reinterpret_cast<int32_t*>(base + so[q].fill);
     c.map = reinterpret_cast<int32_t*>(base + so[q].map);
     c.compact = base + so[q].compact;
     c.part_o = reinterpret_cast<float*>(base + so[q].po);
@@ -385,7 +383,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     c.base_u = reinterpret_cast<uint32_t*>(base + so[q].base_u);
     c.base_m = reinterpret_cast<uint32_t*>(base + so[q].base_m);
     c.pinmask = reinterpret_cast<uint32_t*>(base + so[q].pinmask);
-    c.upos = reinterpret_cast<int32_t*>(base + so[q].upos);
+    c.pdesc = reinterpret_cast<i32x4*>(base + so[q].pdesc);
     c.victim = reinterpret_cast<i32x2*>(base + so[q].victim);
     c.done = reinterpret_cast<uint32_t*>(base + so[q].done);
     c.hist0 = reinterpret_cast<uint32_t*>(base + so[q].hist0);
