@@ -44,7 +44,7 @@ struct UnitT {
   P<uint8_t> rows;         // offload: device address of the pinned host mirror; resident: HBM row store
   P<uint8_t> slots;        // [S][row_bytes] hot slots (offload)
   P<uint8_t> ring;         // [ring_cap][row_bytes] recent ring (offload)
-  P<int32_t> pos_slot;     // [P_pad]  -1 = not cached
+  P<i32x2> pos_slot;       // [P_pad] (slot, round the slot was filled) of a cached position; slot -1 = not cached
   P<int32_t> slot_pos;     // [S]      -1 = empty
   P<int32_t> fill_round;   // [S]
   P<int32_t> pin_round;    // [S]

@@ -46,7 +46,9 @@ struct GatherKArgs {
   StepArgs a;
   int S, ring_cap, ring_rows, mode, row_bytes, K;
   int max_union;                        // R_max * K: compact rows in the scratch
-  int word_blocks;                      // blocks of the union/slot-table part; the rest write back the ring
+  int word_blocks;                      // blocks of the union/slot-table part
+  int clear_blocks;                     // then blocks clearing the Top-K histograms; the rest write back the ring
+  int r_max;
   int64_t max_positions;
 };
 
@@ -59,10 +61,22 @@ __global__ __launch_bounds__(kGatherThreads) void gather_assign_kernel(GatherKAr
   const int seq = blockIdx.y;
   const UnitG u = unit_of(a, seq);
   const ScratchG s = scratch_of(a, seq);
+  if ((int)blockIdx.x >= ka.word_blocks && (int)blockIdx.x < ka.word_blocks + ka.clear_blocks) {
+    // the Top-K histograms of this step's rows, consumed: zero for the next step
+    const int64_t t = (int64_t)(blockIdx.x - ka.word_blocks) * kGatherThreads + threadIdx.x;
+    const int64_t n0 = (int64_t)kHistReps * a.R * (kRadixBins / 4), n1 = (int64_t)a.R * (kRadixBins / 4);
+    if (t < n0) {
+      const int64_t q = t / (a.R * (kRadixBins / 4)), rest = t % (a.R * (kRadixBins / 4));
+      reinterpret_cast<DSA_GLOBAL u32x4*>(s.hist0 + q * ka.r_max * kRadixBins)[rest] = (u32x4){0u, 0u, 0u, 0u};
+    } else if (t < n0 + n1) {
+      reinterpret_cast<DSA_GLOBAL u32x4*>(s.hist1)[t - n0] = (u32x4){0u, 0u, 0u, 0u};
+    }
+    return;
+  }
   if ((int)blockIdx.x >= ka.word_blocks) {
     const int64_t wb = s.info[kInfoWriteback];
     if (wb < 0) return;
-    const int64_t t = (int64_t)(blockIdx.x - ka.word_blocks) * kGatherThreads + threadIdx.x;
+    const int64_t t = (int64_t)(blockIdx.x - ka.word_blocks - ka.clear_blocks) * kGatherThreads + threadIdx.x;
     if (t >= (int64_t)ka.ring_rows * kCopyChunks16) return;
     const int64_t rb = ka.row_bytes;
     const int64_t p = wb + t / kCopyChunks16, c = t % kCopyChunks16;
@@ -111,7 +125,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_assign_kernel(GatherKAr
         src = (int32_t)(p % ka.ring_cap);
       } else if (hw & bit) {
         kind = SRC_HIT;
-        src = u.pos_slot[p];
+        src = u.pos_slot[p].x;
       } else {
         const uint32_t k = bm + __popc(sw & ~hw & ~rw & below);
         src = (int32_t)p;
@@ -120,9 +134,9 @@ __global__ __launch_bounds__(kGatherThreads) void gather_assign_kernel(GatherKAr
           const i32x2 vo = s.victim[k];                // (slot, position it held), from the plan
           const int32_t v = vo.x, old = vo.y;
           if (v >= 0 && v < ka.S) {
-            if (old >= 0 && old < ka.max_positions) u.pos_slot[old] = -1;
+            if (old >= 0 && old < ka.max_positions) u.pos_slot[old] = (i32x2){-1, -1};
             u.slot_pos[v] = (int32_t)p;
-            u.pos_slot[p] = v;
+            u.pos_slot[p] = (i32x2){v, round};
             u.fill_round[v] = round;
             u.pin_round[v] = round;
             fill = v;
@@ -197,7 +211,7 @@ __global__ __launch_bounds__(256) void warm_clear_kernel(UnitDev ud, int S) {
   const UnitG u = as_global(ud);
   for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < S; v += gridDim.x * blockDim.x) {
     const int32_t old = u.slot_pos[v];
-    if (old >= 0) u.pos_slot[old] = -1;
+    if (old >= 0) u.pos_slot[old] = (i32x2){-1, -1};
   }
 }
 
@@ -210,7 +224,7 @@ __global__ __launch_bounds__(256) void warm_fill_kernel(UnitDev ud, int S, int64
     u.slot_pos[v] = pos;
     u.fill_round[v] = -1;
     u.pin_round[v] = -1;
-    if (pos >= 0) u.pos_slot[pos] = (int32_t)v;
+    if (pos >= 0) u.pos_slot[pos] = (i32x2){(int32_t)v, -1};
   }
   const int64_t total = n * kCopyChunks16;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
@@ -235,9 +249,11 @@ hipError_t launch_gather(const Geometry& g, const StepArgs& a, hipStream_t st) {
   const int64_t waves = (words + 1) / 2;
   const int64_t blocks = (waves + 3) / 4;
   const int64_t wb_blocks = ((int64_t)g.ring_rows * kCopyChunks16 + kGatherThreads - 1) / kGatherThreads;
+  const int64_t clear_blocks = ((int64_t)(kHistReps + 1) * a.R * (kRadixBins / 4) + kGatherThreads - 1) / kGatherThreads;
   GatherKArgs ka{a, g.hot_slots, g.ring_cap, g.ring_rows, g.mode, g.row_bytes, g.top_k, g.r_max * g.top_k,
-                 (int)blocks, g.max_positions};
-  return launch_k(gather_assign_kernel, dim3((unsigned)(blocks + (g.mode == 0 ? wb_blocks : 0)), (unsigned)a.n_seqs),
+                 (int)blocks, (int)clear_blocks, g.r_max, g.max_positions};
+  return launch_k(gather_assign_kernel,
+                  dim3((unsigned)(blocks + clear_blocks + (g.mode == 0 ? wb_blocks : 0)), (unsigned)a.n_seqs),
                   dim3(kGatherThreads), 0, st, ka);
 }
 

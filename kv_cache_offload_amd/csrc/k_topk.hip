@@ -89,24 +89,23 @@ __device__ inline void load_chunk(const DSA_GLOBAL float* sc, int64_t t0, float*
 
 // In offload mode a selected position is classified on the round-start state
 // -- a hit needs a slot filled in an earlier round -- and the hit's slot is
-// pinned for this round.  N positions per thread (-1: none), their lookups
-// issued together (two dependent round trips).
+// pinned for this round.  N positions per thread (-1: none); each lookup is one
+// (slot, fill round) pair, all issued together (one memory round trip).
 template <int N>
 __device__ inline void classify_and_pin(const UnitG& u, const ScratchG& s, const int32_t* pos, int64_t M,
                                         int32_t round) {
-  int32_t v[N];
+  i32x2 ps[N];
 #pragma unroll
-  for (int e = 0; e < N; ++e) v[e] = u.pos_slot[(pos[e] >= 0 && pos[e] < M) ? pos[e] : 0];
+  for (int e = 0; e < N; ++e) ps[e] = u.pos_slot[(pos[e] >= 0 && pos[e] < M) ? pos[e] : 0];
 #pragma unroll
-  for (int e = 0; e < N; ++e) keep(v[e]);
+  for (int e = 0; e < N; ++e) keep(ps[e]);
+  int32_t v[N], fr[N];
 #pragma unroll
-  for (int e = 0; e < N; ++e)
-    if (!(pos[e] >= 0 && pos[e] < M)) v[e] = -1;
-  int32_t fr[N];
-#pragma unroll
-  for (int e = 0; e < N; ++e) fr[e] = u.fill_round[v[e] >= 0 ? v[e] : 0];
-#pragma unroll
-  for (int e = 0; e < N; ++e) keep(fr[e]);
+  for (int e = 0; e < N; ++e) {
+    const bool in = pos[e] >= 0 && pos[e] < M;
+    v[e] = in ? ps[e].x : -1;
+    fr[e] = ps[e].y;
+  }
 #pragma unroll
   for (int e = 0; e < N; ++e)
     if (v[e] >= 0 && fr[e] < round) {
@@ -134,15 +133,11 @@ __device__ inline void mark_selection(const UnitG& u, const ScratchG& s, const i
   if (offl) classify_and_pin<kPer>(u, s, pos, M, round);
 }
 
-// Fewer visible positions than K: every visible position is selected.  The
-// row's first-digit histogram is cleared for the next step.
-__device__ inline void select_all_visible(const UnitG& u, const ScratchG& s, int r, int K, int64_t n_vis,
-                                          DSA_GLOBAL uint32_t* h0, int64_t rep_stride, bool offl, int64_t M,
-                                          int32_t round, int32_t* s_sel) {
+// Fewer visible positions than K: every visible position is selected.
+__device__ inline void select_all_visible(const UnitG& u, const ScratchG& s, int r, int K, int64_t n_vis, bool offl,
+                                          int64_t M, int32_t round, int32_t* s_sel) {
   const int tid = threadIdx.x;
   const auto sel = s.sel + (int64_t)r * K;
-  for (int b = tid; b < kRadixBins; b += kSelThreads)
-    for (int q = 0; q < kHistReps; ++q) h0[q * rep_stride + b] = 0;
   for (int t = tid; t < K; t += kSelThreads) {
     sel[t] = t < n_vis ? t : -1;
     s_sel[t] = t < n_vis ? t : -1;
@@ -238,17 +233,10 @@ __device__ void resolve_row(const TopkKArgs& ka, const UnitG& u, const ScratchG&
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = ka.K;
   const bool offl = ka.mode == 0;
-  const auto h0 = s.hist0 + (int64_t)r * kRadixBins;
-  const auto h1 = s.hist1 + (int64_t)r * kRadixBins;
-  const int64_t rep_stride = (int64_t)ka.r_max * kRadixBins;
   const int n_chunks = (int)((n_vis + kTopkChunk - 1) / kTopkChunk);
 
+  // (the histograms are cleared for the next step by the gather's assign kernel)
   if (!ka.long_mode) find_bin_regs<kSelWaves, kRadixBins, kRadixBins / kSelThreads>(h1c, need, sm.sh, &b1, &need);
-  for (int b = tid; b < kRadixBins; b += kSelThreads) {   // consumed: clear for the next step
-#pragma unroll
-    for (int q = 0; q < kHistReps; ++q) h0[q * rep_stride + b] = 0;
-    h1[b] = 0;
-  }
   {
     uint32_t tot;
     const uint32_t base = block_scan<kSelWaves>(cnt, &tot, sm.sh);
@@ -415,23 +403,22 @@ __global__ __launch_bounds__(kSelThreads) void topk_final_kernel(TopkKArgs ka) {
   const int r = blockIdx.x, seq = blockIdx.y, tid = threadIdx.x;
   const UnitG u = unit_of(a, seq);
   const ScratchG s = scratch_of(a, seq);
-  // the round-start state, read once (the plan needs it too)
+  // Everything this pass reads first, issued together: the round-start state
+  // (the plan needs it too), the row's digits from the chunk pass, the chunk
+  // list sizes (one chunk per thread at most) and this thread's bins of the
+  // second-digit histogram.
   const PlanState ps{u.dyn[0], u.dyn[1], (int32_t)u.dyn[2], ka.mode == 0 ? *u.hand : 0};
+  const i32x4 dig = *reinterpret_cast<const DSA_GLOBAL i32x4*>(s.rowdig + 4 * r);
+  const uint32_t cnt_all = tid < ka.n_chunks ? s.cand_n[(int64_t)r * ka.n_chunks + tid] : 0u;
+  uint32_t h1c[kRadixBins / kSelThreads];
+  load_bins<kSelWaves, kRadixBins, 1>(s.hist1 + (int64_t)r * kRadixBins, h1c);
   const int64_t n_vis = ps.L - a.R + r + 1;
   const int K = ka.K;
-  const auto h0 = s.hist0 + (int64_t)r * kRadixBins;
-  const int64_t rep_stride = (int64_t)ka.r_max * kRadixBins;
   if (n_vis <= K) {
-    select_all_visible(u, s, r, K, n_vis, h0, rep_stride, ka.mode == 0, ps.M, ps.round, sm.sel);
+    select_all_visible(u, s, r, K, n_vis, ka.mode == 0, ps.M, ps.round, sm.sel);
   } else {
-    // everything this pass reads first, issued together: the row's digits from
-    // the chunk pass, the chunk list sizes (one chunk per thread at most) and
-    // this thread's bins of the second-digit histogram
     const int n_chunks = (int)((n_vis + kTopkChunk - 1) / kTopkChunk);
-    const i32x4 dig = *reinterpret_cast<const DSA_GLOBAL i32x4*>(s.rowdig + 4 * r);
-    const uint32_t cnt = tid < n_chunks ? s.cand_n[(int64_t)r * ka.n_chunks + tid] : 0u;
-    uint32_t h1c[kRadixBins / kSelThreads];
-    load_bins<kSelWaves, kRadixBins, 1>(s.hist1 + (int64_t)r * kRadixBins, h1c);
+    const uint32_t cnt = tid < n_chunks ? cnt_all : 0u;  // lists of this step's chunks only
     resolve_row(ka, u, s, r, n_vis, ps.M, ps.round, dig.x, dig.y, (uint32_t)dig.z, cnt, h1c, sm, lds);
   }
   plan_if_last(u, s, ka.plan, (uint32_t)a.R, ps, lds);

@@ -269,7 +269,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     uo[i].rows = off ? 0 : take((size_t)P * rb);
     uo[i].slots = off ? take((size_t)S * rb) : 0;
     uo[i].ring = off ? take((size_t)g.ring_cap * rb) : 0;
-    uo[i].pos_slot = off ? take((size_t)P * 4) : 0;
+    uo[i].pos_slot = off ? take((size_t)P * 8) : 0;
     uo[i].slot_pos = off ? take((size_t)S * 4) : 0;
     uo[i].fill = off ? take((size_t)S * 4) : 0;
     uo[i].pin = off ? take((size_t)S * 4) : 0;
@@ -346,11 +346,11 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
       u.rows = static_cast<uint8_t*>(dp);
       u.slots = base + uo[i].slots;
       u.ring = base + uo[i].ring;
-      u.pos_slot = reinterpret_cast<int32_t*>(base + uo[i].pos_slot);
+      u.pos_slot = reinterpret_cast<i32x2*>(base + uo[i].pos_slot);
       u.slot_pos = reinterpret_cast<int32_t*>(base + uo[i].slot_pos);
       u.fill_round = reinterpret_cast<int32_t*>(base + uo[i].fill);
       u.pin_round = reinterpret_cast<int32_t*>(base + uo[i].pin);
-      if (hipMemset(u.pos_slot, 0xFF, (size_t)P * 4) != hipSuccess ||
+      if (hipMemset(u.pos_slot, 0xFF, (size_t)P * 8) != hipSuccess ||
           hipMemset(u.slot_pos, 0xFF, (size_t)S * 4) != hipSuccess ||
           hipMemset(u.fill_round, 0xFF, (size_t)S * 4) != hipSuccess ||
           hipMemset(u.pin_round, 0xFF, (size_t)S * 4) != hipSuccess)
@@ -620,7 +620,9 @@ dsa_status dsa_debug_get(dsa_session* s, int32_t layer, int32_t seq, int32_t ite
     case DSA_DBG_SLOT_POS: src = u.slot_pos; break;
     case DSA_DBG_FILL_ROUND: src = u.fill_round; break;
     case DSA_DBG_PIN_ROUND: src = u.pin_round; break;
-    case DSA_DBG_POS_SLOT: src = u.pos_slot; break;
+    case DSA_DBG_POS_SLOT:                             // the slot half of each (slot, fill round) pair
+      HIPCHK(hipMemcpy2DAsync(dst, 4, u.pos_slot, 8, 4, need / 4, hipMemcpyDeviceToDevice, stream), "hipMemcpy2DAsync");
+      return DSA_OK;
     case DSA_DBG_HAND: src = u.hand; break;
     case DSA_DBG_SLOT_BYTES: src = u.slots; break;
     case DSA_DBG_MIRROR: src = g.mode == DSA_KV_OFFLOAD ? s->mirrors[ui] : (const void*)u.rows; break;
