@@ -32,6 +32,7 @@ typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 
 constexpr int kQStride = 136;           // bf16 per Q row in LDS (128 + 8 pad)
 constexpr int kWaves = 4;
+constexpr int kMaxQPieces = 256 * 16 / 256;   // 16-byte Q pieces per thread at R * H_I = 256
 
 struct ScoreKArgs {
   StepArgs a;
@@ -49,22 +50,12 @@ __device__ inline uint32_t first_digit(float f) {
   return ((u & 0x80000000u) ? ~u : (u | 0x80000000u)) >> 21;
 }
 
-// Count the scores of the active lanes in row r's packed LDS histogram (two 16-bit
-// bins per word).  Scores of neighbouring positions share few first digits, so
-// lanes with equal digits are combined first: one atomic per distinct digit.
+// Count the score in row r's packed LDS histogram (two 16-bit bins per word):
+// one LDS atomic per lane; lanes that hit the same word are serialised by the
+// LDS unit, which is cheaper than combining them in a loop first.
 __device__ inline void count_digit(uint32_t* lh, int r, float score) {
-  const uint32_t key = ((uint32_t)r << 11) | first_digit(score);   // (row, digit); lanes may differ in row
-  uint64_t todo = __ballot(1);
-  while (todo) {
-    const int leader = __ffsll((unsigned long long)todo) - 1;
-    const uint32_t kl = __shfl(key, leader);
-    const uint64_t same = __ballot(key == kl) & todo;
-    if ((int)(threadIdx.x & 63) == leader) {
-      const uint32_t rl = kl >> 11, dl = kl & 2047u;
-      atomicAdd(&lh[rl * (kRadixBins / 2) + (dl >> 1)], (uint32_t)__popcll(same) << (16 * (dl & 1)));
-    }
-    todo &= ~same;
-  }
+  const uint32_t d = first_digit(score);
+  atomicAdd(&lh[r * (kRadixBins / 2) + (d >> 1)], 1u << (16 * (d & 1)));
 }
 
 template <int HI>
@@ -87,31 +78,38 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreKArgs ka) {
   const int hf = lane >> 5;
   const int64_t first_sub = ((int64_t)blockIdx.x * kWaves + wave) * ka.subs_per_wave;
 
-  // Start the first key tile's loads before staging Q.
+  // Q (zero padded to MT*32 rows) and the head weights, staged in LDS below;
+  // every load issued before the first is used (M <= 256: at most 16 per thread).
+  const uint16_t* qg = ka.q + (int64_t)seq * M * 128;
+  const int nq = MT * 32 * 16;                           // 16-byte pieces of the padded Q
+  bf16x8 qv[kMaxQPieces];
+#pragma unroll
+  for (int e = 0; e < kMaxQPieces; ++e) {
+    const int c = threadIdx.x + e * 256;
+    const int row = c >> 4, col = (c & 15) * 8;
+    qv[e] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    if (c < nq && row < M) qv[e] = *reinterpret_cast<const bf16x8*>(qg + (int64_t)row * 128 + col);
+  }
+  const float wv = threadIdx.x < M ? ka.w[(int64_t)seq * M + threadIdx.x] : 0.0f;
+  // The first key tile's loads, behind the Q loads: loads complete in issue
+  // order, so staging Q does not wait for the keys (HBM).
+  // Positions past L read (unused) rows of the key store, so the loads need not
+  // wait for L.
   bf16x8 b[8];
   {
-    const int64_t t = first_sub * 32 + n;
-    if (t < L) {
-      const DSA_GLOBAL bf16x8* kp = reinterpret_cast<const DSA_GLOBAL bf16x8*>(u.keys + t * 128 + 64 * hf);
+    const int64_t t = min(first_sub * 32 + n, ka.p_pad - 1);
+    const DSA_GLOBAL bf16x8* kp = reinterpret_cast<const DSA_GLOBAL bf16x8*>(u.keys + t * 128 + 64 * hf);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) b[ks] = kp[ks];
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) b[ks] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
-    }
+    for (int ks = 0; ks < 8; ++ks) b[ks] = kp[ks];
   }
 
-  // Stage Q (zero padded to MT*32 rows) and the head weights in LDS.
   for (int w = threadIdx.x; w < R * (kRadixBins / 2); w += blockDim.x) lh[w] = 0;
-  const uint16_t* qg = ka.q + (int64_t)seq * M * 128;
-  for (int c = threadIdx.x; c < MT * 32 * 16; c += blockDim.x) {
-    int row = c >> 4, col = (c & 15) * 8;
-    bf16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (row < M) v = *reinterpret_cast<const bf16x8*>(qg + (int64_t)row * 128 + col);
-    *reinterpret_cast<bf16x8*>(sq + row * kQStride + col) = v;
+#pragma unroll
+  for (int e = 0; e < kMaxQPieces; ++e) {
+    const int c = threadIdx.x + e * 256;
+    if (c < nq) *reinterpret_cast<bf16x8*>(sq + (c >> 4) * kQStride + (c & 15) * 8) = qv[e];
   }
-  for (int m = threadIdx.x; m < MT * 32; m += blockDim.x)
-    sw[m] = m < M ? ka.w[(int64_t)seq * M + m] : 0.0f;
+  if (threadIdx.x < MT * 32) sw[threadIdx.x] = wv;
   __syncthreads();
 
   const auto scores = s.scores;
@@ -131,62 +129,73 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreKArgs ka) {
         for (int ks = 0; ks < 8; ++ks) b[ks] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
       }
     }
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x16 acc = {0};
-      const uint16_t* ap = sq + (mt * 32 + n) * kQStride + 64 * hf;
+    // Up to four row tiles at a time: independent accumulation chains, so the
+    // MFMA pipeline is never waiting on one accumulator.
+    for (int mt0 = 0; mt0 < MT; mt0 += 4) {
+      f32x16 acc4[4];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        bf16x8 av = *reinterpret_cast<const bf16x8*>(ap + 8 * ks);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[ks], acc, 0, 0, 0);
-      }
-      // acc[v] holds C[row = (v/4)*8 + hf*4 + v%4][col = n]
-      float part[4];
+      for (int i4 = 0; i4 < 4; ++i4) acc4[i4] = (f32x16){0};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float p = 0.0f;
+      for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          int m = mt * 32 + i * 8 + hf * 4 + j;
-          p += sw[m] * fmaxf(acc[i * 4 + j], 0.0f);
+        for (int i4 = 0; i4 < 4; ++i4) {
+          if (mt0 + i4 >= MT) continue;
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(sq + ((mt0 + i4) * 32 + n) * kQStride + 64 * hf + 8 * ks);
+          acc4[i4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[ks], acc4[i4], 0, 0, 0);
         }
-        part[i] = p;
-      }
-      if constexpr (HI == 32) {
-        float sum = (part[0] + part[1]) + (part[2] + part[3]);
-        sum += __shfl_xor(sum, 32);
-        const int r = mt;
-        if (hf == 0 && r < R && t < L - R + r + 1) {
-          scores[(int64_t)r * ka.p_pad + t] = canon0(sum);
-          count_digit(lh, r, canon0(sum));
-        }
-      } else if constexpr (HI == 16) {
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          float sum = part[2 * k2] + part[2 * k2 + 1];
+      for (int i4 = 0; i4 < 4; ++i4) {
+        if (mt0 + i4 >= MT) continue;
+        const int mt = mt0 + i4;
+        // acc[v] holds C[row = (v/4)*8 + hf*4 + v%4][col = n]
+        float part[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float p = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            int m = mt * 32 + i * 8 + hf * 4 + j;
+            p += sw[m] * fmaxf(acc4[i4][i * 4 + j], 0.0f);
+          }
+          part[i] = p;
+        }
+        if constexpr (HI == 32) {
+          float sum = (part[0] + part[1]) + (part[2] + part[3]);
           sum += __shfl_xor(sum, 32);
-          const int r = mt * 2 + k2;
+          const int r = mt;
           if (hf == 0 && r < R && t < L - R + r + 1) {
             scores[(int64_t)r * ka.p_pad + t] = canon0(sum);
             count_digit(lh, r, canon0(sum));
           }
-        }
-      } else if constexpr (HI == 8) {
+        } else if constexpr (HI == 16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float sum = part[i] + __shfl_xor(part[i], 32);
-          const int r = mt * 4 + i;
-          if (hf == 0 && r < R && t < L - R + r + 1) {
-            scores[(int64_t)r * ka.p_pad + t] = canon0(sum);
-            count_digit(lh, r, canon0(sum));
+          for (int k2 = 0; k2 < 2; ++k2) {
+            float sum = part[2 * k2] + part[2 * k2 + 1];
+            sum += __shfl_xor(sum, 32);
+            const int r = mt * 2 + k2;
+            if (hf == 0 && r < R && t < L - R + r + 1) {
+              scores[(int64_t)r * ka.p_pad + t] = canon0(sum);
+              count_digit(lh, r, canon0(sum));
+            }
           }
-        }
-      } else {  // HI == 4: rows of one query row sit in one lane half
+        } else if constexpr (HI == 8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = mt * 8 + 2 * i + hf;
-          if (r < R && t < L - R + r + 1) {
-            scores[(int64_t)r * ka.p_pad + t] = canon0(part[i]);
-            count_digit(lh, r, canon0(part[i]));
+          for (int i = 0; i < 4; ++i) {
+            float sum = part[i] + __shfl_xor(part[i], 32);
+            const int r = mt * 4 + i;
+            if (hf == 0 && r < R && t < L - R + r + 1) {
+              scores[(int64_t)r * ka.p_pad + t] = canon0(sum);
+              count_digit(lh, r, canon0(sum));
+            }
+          }
+        } else {  // HI == 4: rows of one query row sit in one lane half
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = mt * 8 + 2 * i + hf;
+            if (r < R && t < L - R + r + 1) {
+              scores[(int64_t)r * ka.p_pad + t] = canon0(part[i]);
+              count_digit(lh, r, canon0(part[i]));
+            }
           }
         }
       }
