@@ -45,6 +45,7 @@ struct UnitT {
   P<uint8_t> slots;        // [S][row_bytes] hot slots (offload)
   P<uint8_t> ring;         // [ring_cap][row_bytes] recent ring (offload)
   P<i32x2> pos_slot;       // [P_pad] (slot, round the slot was filled) of a cached position; slot -1 = not cached
+  P<uint32_t> hot;         // [P_pad/32] bit set iff the position is cached (as of the current round's start)
   P<int32_t> slot_pos;     // [S]      -1 = empty
   P<int32_t> fill_round;   // [S]
   P<int32_t> pin_round;    // [S]
@@ -69,11 +70,10 @@ struct ScratchT {
   P<int64_t> counters;      // [8] union, hit, ring, miss, miss_noslot, evict, host_bytes, resident
   P<int64_t> info;          // [8] see kInfo* below
   P<uint32_t> selmask;      // [P_pad/32] positions selected by any row this step (cleared by the assign)
-  P<uint32_t> hitmask;      // [P_pad/32] selected positions that hit a slot (cleared by the assign)
+  P<uint32_t> hitmask;      // [P_pad/32] selected positions that hit a slot (written by the plan each step)
   P<i32x4> pdesc;           // [P_pad] per selected position: union index, kind, source, slot to fill (this step)
   P<uint32_t> base_u;       // [P_pad/32] union entries before each 32-position word
   P<uint32_t> base_m;       // [P_pad/32] misses before each word
-  P<uint32_t> pinmask;      // [S_pad/32] slots pinned this round (cleared by the scan)
   P<i32x2> victim;          // [S_pad] (slot, position it held or -1) given to the k-th miss of the step
   P<uint32_t> hist0;        // [kHistReps][R_max][2048] first-digit histogram replicas (zeroed after use)
   P<uint32_t> hist1;        // [R_max][2048] second-digit histogram within the first-digit bin

@@ -3,13 +3,16 @@
 // selection in the step's bitmaps.
 //
 // Page "From 1M total to 15+ streams x 1M: the capacity breakthrough of
-// GLM-5.3 KV cache offload", section "GPU cache management errs too": misses
-// are served after the hits are pinned, and replacement walks the slots as a
-// ring, skipping the pinned ones.  The plan turns the position bitmaps into
-// per-32-position-word prefix counts of union entries and of misses, lists the
-// unpinned slots in ring order from the hand (the victim of the k-th miss in
-// ascending position order is victim[k]), and publishes the step's counters,
-// the new hand and the round-end state (M after writeback, round + 1).
+// GLM-5.3 KV cache offload", section "GPU cache management errs too": slots in
+// use this round are pinned, a slot filled this round is a hit source only from
+// the next round, and replacement walks the slots as a ring, skipping the
+// pinned ones.  The plan classifies the round's union against the positions
+// cached at round start (a per-position bitmap: every cached slot was filled
+// in an earlier round), turns the bitmaps into per-32-position-word prefix
+// counts of union entries and of misses, lists the unpinned slots in ring
+// order from the hand (the victim of the k-th miss in ascending position order
+// is victim[k]), and publishes the step's counters, the new hand and the
+// round-end state (M after writeback, round + 1).
 #pragma once
 
 #include "dev_util.h"
@@ -39,69 +42,40 @@ struct PlanState {
   int32_t hand;
 };
 
-constexpr int kPlanRegWords = 4;   // union/hit words a thread keeps in registers (histories <= 131,072)
-constexpr int kPlanRegSlots = 2;   // pinned-slot words a thread keeps in registers (slots <= 65,536)
+constexpr int kPlanRegWords = 4;   // union words a thread keeps in registers (histories <= 131,072)
+constexpr int kWalkPer = 4;        // ring offsets a thread examines per pass of the victim walk
+constexpr int kWalkWords = kPlanThreads * kWalkPer / 32;   // 32-offset words per pass
 
-// Unpinned slots among the 32 ring offsets 32 j .. 32 j + 31 from the hand.
-__device__ inline uint32_t unpinned_word(const ScratchG& s, int S, int nsw, int hand, int j) {
-  uint32_t bits = 0;
-  if ((S & 31) == 0) {
-    // 32 offsets from a word-aligned ring: two pinned words, funnel-shifted
-    const int v0 = (hand + 32 * j) % S;
-    const int wa = v0 >> 5, sa = v0 & 31;
-    const uint32_t lo = s.pinmask[wa];
-    const uint32_t hi = sa ? s.pinmask[(wa + 1) % nsw] : 0u;
-    bits = ~(sa ? ((lo >> sa) | (hi << (32 - sa))) : lo);
-  } else {
-    int last = -1;
-    uint32_t pw = 0;
-    for (int i = 0; i < 32; ++i) {
-      const int o = 32 * j + i;
-      if (o >= S) break;
-      const int v = (hand + o) % S;
-      if ((v >> 5) != last) { last = v >> 5; pw = s.pinmask[last]; }
-      if (!((pw >> (v & 31)) & 1u)) bits |= 1u << i;
-    }
-  }
-  return bits;
-}
-
-// lds: 2 * kPlanThreads words of LDS the caller no longer uses.
+// lds: at least kWalkWords + 32 words of LDS the caller no longer uses.
 __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, const PlanParams& pp,
                                          const PlanState& ps, uint32_t* lds) {
   __shared__ uint32_t sh[4 * kPlanWaves];
-  __shared__ int s_hand;
+  __shared__ int s_last_v, s_assigned_last_v;
   __shared__ uint32_t s_evict;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int64_t L = ps.L, M = ps.M;
   const int32_t round = ps.round;
   const bool off = pp.mode == 0;
   const int hand = off ? ps.hand : 0;
+  const int S = pp.S;
   const int64_t nw = (L + 31) / 32;
   const auto sel = s.selmask;
-  const auto hit = s.hitmask;
   const int64_t per = (nw + kPlanThreads - 1) / kPlanThreads;
   const int64_t w0 = min(nw, (int64_t)tid * per), w1 = min(nw, w0 + per);
-  const int S = pp.S, nsw = off ? pp.s_words : 0;
-  const int sper = (nsw + kPlanThreads - 1) / kPlanThreads;
-  const int j0 = min(nsw, tid * sper), j1 = min(nsw, j0 + sper);
   const bool words_in_regs = per <= kPlanRegWords;
-  const bool slots_in_regs = sper <= kPlanRegSlots;
 
-  // Every independent load at once: this thread's union and hit words, its
-  // unpinned-slot words and the running totals.
-  uint32_t swr[kPlanRegWords], hwr[kPlanRegWords], upr[kPlanRegSlots];
+  // Every independent load at once: this thread's union words and cached-position
+  // words, and the running totals.  A selected position is a hit iff it was
+  // cached when the round started (every cached slot was filled in an earlier
+  // round); the hit words are published for the assign kernel.
+  uint32_t swr[kPlanRegWords], hwr[kPlanRegWords];
   if (words_in_regs) {
 #pragma unroll
     for (int e = 0; e < kPlanRegWords; ++e) {
       const int64_t w = w0 + e;
       swr[e] = w < w1 ? sel[w] : 0u;
-      hwr[e] = (off && w < w1) ? hit[w] : 0u;
+      hwr[e] = (off && w < w1) ? u.hot[w] : 0u;
     }
-  }
-  if (slots_in_regs) {
-#pragma unroll
-    for (int e = 0; e < kPlanRegSlots; ++e) upr[e] = j0 + e < j1 ? unpinned_word(s, S, nsw, hand, j0 + e) : 0u;
   }
   const int64_t total_prev = tid < 8 ? u.totals[tid] : 0;
 
@@ -109,6 +83,7 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
   // (Register arrays are indexed only by unrolled constants.)
   uint4 c = make_uint4(0u, 0u, 0u, 0u);        // union, miss, ring, hit
   auto count = [&](int64_t w, uint32_t sw, uint32_t hw) {
+    if (off) s.hitmask[w] = hw;
     if (!sw) return;
     const uint32_t rw = off ? (sw & ring_bits(w, M)) : 0u;
     c.x += __popc(sw);
@@ -120,10 +95,15 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
   };
   if (words_in_regs) {
 #pragma unroll
-    for (int e = 0; e < kPlanRegWords; ++e)
+    for (int e = 0; e < kPlanRegWords; ++e) {
+      hwr[e] &= swr[e];
       if (w0 + e < w1) count(w0 + e, swr[e], hwr[e]);
+    }
   } else {
-    for (int64_t w = w0; w < w1; ++w) count(w, sel[w], off ? hit[w] : 0u);
+    for (int64_t w = w0; w < w1; ++w) {
+      const uint32_t sw = sel[w];
+      count(w, sw, off ? (sw & u.hot[w]) : 0u);
+    }
   }
   uint4 tot;
   const uint4 base = block_scan4<kPlanWaves>(c, &tot, sh);
@@ -142,74 +122,79 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
     for (int e = 0; e < kPlanRegWords; ++e)
       if (w0 + e < w1) bases(w0 + e, swr[e], hwr[e]);
   } else {
-    for (int64_t w = w0; w < w1; ++w) bases(w, sel[w], off ? hit[w] : 0u);
+    for (int64_t w = w0; w < w1; ++w) {
+      const uint32_t sw = sel[w];
+      bases(w, sw, off ? (sw & u.hot[w]) : 0u);
+    }
   }
 
-  // Unpinned slots in ring order from the hand; victim[k] for the misses that get one.
+  // Victims: slots in ring order from the hand, skipping the pinned ones -- a
+  // slot is pinned this round iff the position it holds is selected (it is then
+  // a hit).  Passes of kWalkWords * 32 ring offsets until every miss has a slot
+  // or every slot has been seen; the k-th miss in ascending position order takes
+  // the k-th unpinned slot.  victim[k] = (slot, the position it gives up).
   uint32_t n_assigned = 0;
   if (tid == 0) {
-    s_hand = hand;
+    s_last_v = -1;
+    s_assigned_last_v = -1;
     s_evict = 0;
   }
-  if (off) {
-    uint32_t cnt = 0;
-    if (slots_in_regs) {
+  if (off && n_miss > 0) {
+    uint32_t* cnt_w = lds;                             // [kWalkWords] unpinned offsets per word, then their scan
+    uint32_t cum = 0;                                  // unpinned slots found in earlier passes
+    const int half = tid >> 5, bit = tid & 31;
+    for (int64_t o0 = 0; o0 < S && cum < n_miss; o0 += (int64_t)kWalkWords * 32) {
+      int32_t held[kWalkPer], slot[kWalkPer];
 #pragma unroll
-      for (int e = 0; e < kPlanRegSlots; ++e) cnt += __popc(upr[e]);
-    } else {
-      for (int j = j0; j < j1; ++j) cnt += __popc(unpinned_word(s, S, nsw, hand, j));
-    }
-    uint32_t n_unpinned;
-    uint32_t k = block_scan<kPlanWaves>(cnt, &n_unpinned, sh);
-    n_assigned = min(n_miss, n_unpinned);
-    if (sper == 1) {
-      // one slot word per thread: expand the words in parallel, 32 lanes (one per
-      // bit) per word; word j's unpinned slots take victim indices k_j, k_j + 1, ...
-      uint32_t* s_bits = lds;
-      uint32_t* s_k = lds + kPlanThreads;
-      s_bits[tid] = j0 < j1 ? upr[0] : 0u;
-      s_k[tid] = k;
+      for (int e = 0; e < kWalkPer; ++e) {             // offset o0 + 32 (half + 32 e) + bit
+        const int64_t o = o0 + 32 * (half + 32 * e) + bit;
+        slot[e] = o < S ? (int32_t)((hand + o) % S) : -1;
+        held[e] = u.slot_pos[slot[e] >= 0 ? slot[e] : 0];
+      }
+      uint32_t pin_word[kWalkPer];
+#pragma unroll
+      for (int e = 0; e < kWalkPer; ++e) {
+        const int32_t p = held[e];
+        pin_word[e] = (slot[e] >= 0 && p >= 0 && p < L) ? sel[p >> 5] : 0u;
+      }
+      uint32_t ub[kWalkPer];
+#pragma unroll
+      for (int e = 0; e < kWalkPer; ++e) {
+        const int32_t p = held[e];
+        const bool pinned = slot[e] >= 0 && p >= 0 && p < L && ((pin_word[e] >> (p & 31)) & 1u);
+        const bool unpinned = slot[e] >= 0 && !pinned;
+        ub[e] = (uint32_t)(__ballot(unpinned) >> (tid & 32));   // this half-wave's word
+        if (bit == 0) cnt_w[half + 32 * e] = __popc(ub[e]);
+      }
       __syncthreads();
-      const int bit = tid & 31;
-      for (int j = tid >> 5; j < nsw; j += kPlanThreads / 32) {
-        const uint32_t kj = s_k[j];
-        if (kj >= n_assigned) break;                   // k_j never decreases with j
-        const uint32_t bits = s_bits[j];
-        bool evicts = false;
-        if ((bits >> bit) & 1u) {
-          const uint32_t kk = kj + __popc(bits & ((1u << bit) - 1u));
-          if (kk < n_assigned) {
-            const int v = (hand + 32 * j + bit) % S;
-            const int32_t old = u.slot_pos[v];         // the position the slot gives up
-            s.victim[kk] = (i32x2){v, old};
-            evicts = old >= 0;
-            if (kk + 1 == n_assigned) s_hand = (v + 1) % S;
-          }
-        }
-        // the two half-waves may leave the loop at different j: each counts its own half
-        const uint32_t eb = (uint32_t)(__ballot(evicts) >> (tid & 32));
-        if (bit == 0 && eb) atomicAdd(&s_evict, (uint32_t)__popc(eb));
+      if (tid < 64) {                                  // exclusive scan of the pass's word counts, in offset order
+        const uint32_t a0 = cnt_w[2 * tid], a1 = cnt_w[2 * tid + 1];
+        const uint32_t inc = wave_incl_scan(a0 + a1, lane);
+        cnt_w[2 * tid] = inc - a0 - a1;
+        cnt_w[2 * tid + 1] = inc - a1;
+        if (tid == 63) cnt_w[kWalkWords] = inc;
       }
-    } else {
-      for (int j = j0, e = 0; j < j1 && k < n_assigned; ++j, ++e) {
-        uint32_t bits = (slots_in_regs && e == 0) ? upr[0] : (slots_in_regs && e == 1) ? upr[1]
-                                                                                        : unpinned_word(s, S, nsw, hand, j);
-        while (bits && k < n_assigned) {
-          const int b = __ffs(bits) - 1;
-          bits &= bits - 1;
-          const int v = (hand + 32 * j + b) % S;
-          const int32_t old = u.slot_pos[v];
-          s.victim[k] = (i32x2){v, old};
-          if (old >= 0) atomicAdd(&s_evict, 1u);
-          if (k + 1 == n_assigned) s_hand = (v + 1) % S;
-          ++k;
+      __syncthreads();
+      const uint32_t pass_total = cnt_w[kWalkWords];
+#pragma unroll
+      for (int e = 0; e < kWalkPer; ++e) {
+        if (!((ub[e] >> bit) & 1u)) continue;
+        const uint32_t k = cum + cnt_w[half + 32 * e] + __popc(ub[e] & ((1u << bit) - 1u));
+        if (k + 1 == cum + pass_total) s_last_v = slot[e];
+        if (k < n_miss) {
+          s.victim[k] = (i32x2){slot[e], held[e]};
+          if (held[e] >= 0) atomicAdd(&s_evict, 1u);
+          if (k + 1 == n_miss) s_assigned_last_v = slot[e];
         }
       }
+      cum += pass_total;
+      __syncthreads();                                 // cnt_w reused by the next pass
     }
-    __syncthreads();                                   // every pinned word has been read
-    for (int j = tid; j < nsw; j += kPlanThreads) s.pinmask[j] = 0;
+    n_assigned = min(n_miss, cum);
   }
   __syncthreads();
+  const int last_v = n_assigned == n_miss ? s_assigned_last_v : s_last_v;
+  const int new_hand = (off && n_assigned > 0 && last_v >= 0) ? (last_v + 1) % S : hand;
   const int64_t rb = 656;
   const int64_t noslot = off ? (int64_t)n_miss - n_assigned : 0;
   if (tid < 8) {
@@ -237,7 +222,7 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
     s.info[kInfoM] = M;
     s.info[kInfoHand] = hand;
     if (off) {
-      *u.hand = s_hand;
+      *u.hand = new_hand;
       if (wb >= 0) u.dyn[1] = M + pp.ring_rows;
     }
     u.dyn[2] = round + 1;

@@ -107,10 +107,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_assign_kernel(GatherKAr
   const bool mine = (sw & bit) != 0;
   const uint64_t selb = __ballot(mine);
   if (!selb) return;
-  if (bitpos == 0 && sw) {                             // read by every lane above: clear for the next step
-    s.selmask[w] = 0;
-    if (hw) s.hitmask[w] = 0;
-  }
+  if (bitpos == 0 && sw) s.selmask[w] = 0;             // read by every lane above: clear for the next step
   if (mine) {
     const uint32_t below = bit - 1u;
     const uint32_t ux = bu + __popc(sw & below);
@@ -124,8 +121,9 @@ __global__ __launch_bounds__(kGatherThreads) void gather_assign_kernel(GatherKAr
         kind = SRC_RING;
         src = (int32_t)(p % ka.ring_cap);
       } else if (hw & bit) {
-        kind = SRC_HIT;
+        kind = SRC_HIT;                                // the hit's slot is pinned for this round
         src = u.pos_slot[p].x;
+        if (src >= 0 && src < ka.S) u.pin_round[src] = round;
       } else {
         const uint32_t k = bm + __popc(sw & ~hw & ~rw & below);
         src = (int32_t)p;
@@ -134,9 +132,13 @@ __global__ __launch_bounds__(kGatherThreads) void gather_assign_kernel(GatherKAr
           const i32x2 vo = s.victim[k];                // (slot, position it held), from the plan
           const int32_t v = vo.x, old = vo.y;
           if (v >= 0 && v < ka.S) {
-            if (old >= 0 && old < ka.max_positions) u.pos_slot[old] = (i32x2){-1, -1};
+            if (old >= 0 && old < ka.max_positions) {
+              u.pos_slot[old] = (i32x2){-1, -1};
+              __hip_atomic_fetch_and(&u.hot[old >> 5], ~(1u << (old & 31)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
             u.slot_pos[v] = (int32_t)p;
             u.pos_slot[p] = (i32x2){v, round};
+            g_or(&u.hot[p >> 5], bit);
             u.fill_round[v] = round;
             u.pin_round[v] = round;
             fill = v;
@@ -211,7 +213,10 @@ __global__ __launch_bounds__(256) void warm_clear_kernel(UnitDev ud, int S) {
   const UnitG u = as_global(ud);
   for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < S; v += gridDim.x * blockDim.x) {
     const int32_t old = u.slot_pos[v];
-    if (old >= 0) u.pos_slot[old] = (i32x2){-1, -1};
+    if (old >= 0) {
+      u.pos_slot[old] = (i32x2){-1, -1};
+      __hip_atomic_fetch_and(&u.hot[old >> 5], ~(1u << (old & 31)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -224,7 +229,10 @@ __global__ __launch_bounds__(256) void warm_fill_kernel(UnitDev ud, int S, int64
     u.slot_pos[v] = pos;
     u.fill_round[v] = -1;
     u.pin_round[v] = -1;
-    if (pos >= 0) u.pos_slot[pos] = (i32x2){(int32_t)v, -1};
+    if (pos >= 0) {
+      u.pos_slot[pos] = (i32x2){(int32_t)v, -1};
+      g_or(&u.hot[pos >> 5], 1u << (pos & 31));
+    }
   }
   const int64_t total = n * kCopyChunks16;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {

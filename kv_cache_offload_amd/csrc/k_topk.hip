@@ -46,6 +46,7 @@ constexpr int kCandCap = 16384;                            // candidates of a ro
 constexpr int kMaxChunks = kMaxTopkChunks;                 // chunk offsets kept in LDS
 constexpr int kMaxK = 4096;
 constexpr int kShortMax = 65536;                           // candidates by the first digit up to this length
+constexpr int kEmitIters = kCandCap / kSelThreads;         // emit iterations of a lane, candidates in LDS
 static_assert(kSelThreads == kPlanThreads, "the plan runs on a select workgroup");
 static_assert(kSelPer == 4, "one 16-byte score load per thread");
 static_assert(kMaxChunks <= kSelThreads, "one chunk count per thread");
@@ -87,55 +88,21 @@ __device__ inline void load_chunk(const DSA_GLOBAL float* sc, int64_t t0, float*
   }
 }
 
-// In offload mode a selected position is classified on the round-start state
-// -- a hit needs a slot filled in an earlier round -- and the hit's slot is
-// pinned for this round.  N positions per thread (-1: none); each lookup is one
-// (slot, fill round) pair, all issued together (one memory round trip).
-template <int N>
-__device__ inline void classify_and_pin(const UnitG& u, const ScratchG& s, const int32_t* pos, int64_t M,
-                                        int32_t round) {
-  i32x2 ps[N];
-#pragma unroll
-  for (int e = 0; e < N; ++e) ps[e] = u.pos_slot[(pos[e] >= 0 && pos[e] < M) ? pos[e] : 0];
-#pragma unroll
-  for (int e = 0; e < N; ++e) keep(ps[e]);
-  int32_t v[N], fr[N];
-#pragma unroll
-  for (int e = 0; e < N; ++e) {
-    const bool in = pos[e] >= 0 && pos[e] < M;
-    v[e] = in ? ps[e].x : -1;
-    fr[e] = ps[e].y;
-  }
-#pragma unroll
-  for (int e = 0; e < N; ++e)
-    if (v[e] >= 0 && fr[e] < round) {
-      g_or(&s.hitmask[pos[e] >> 5], 1u << (pos[e] & 31));
-      u.pin_round[v[e]] = round;
-      g_or(&s.pinmask[v[e] >> 5], 1u << (v[e] & 31));
-    }
-}
-
-// Marks the row's first n selected positions (in LDS) in the union bitmap -- a
-// position several rows select is one union entry -- and, in offload mode,
-// classifies and pins them.  Every thread of the workgroup calls it.
-__device__ inline void mark_selection(const UnitG& u, const ScratchG& s, const int32_t* s_sel, int n, bool offl,
-                                      int64_t M, int32_t round) {
+// Marks the row's first n selected positions (in LDS) in the step's union
+// bitmap -- a position several rows select is one union entry.  Every thread
+// of the workgroup calls it.
+__device__ inline void mark_selection(const ScratchG& s, const int32_t* s_sel, int n) {
   constexpr int kPer = kMaxK / kSelThreads;
-  int32_t pos[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     const int j = threadIdx.x + e * kSelThreads;
-    pos[e] = j < n ? s_sel[j] : -1;
+    const int32_t pos = j < n ? s_sel[j] : -1;
+    if (pos >= 0) g_or(&s.selmask[pos >> 5], 1u << (pos & 31));
   }
-#pragma unroll
-  for (int e = 0; e < kPer; ++e)
-    if (pos[e] >= 0) g_or(&s.selmask[pos[e] >> 5], 1u << (pos[e] & 31));
-  if (offl) classify_and_pin<kPer>(u, s, pos, M, round);
 }
 
 // Fewer visible positions than K: every visible position is selected.
-__device__ inline void select_all_visible(const UnitG& u, const ScratchG& s, int r, int K, int64_t n_vis, bool offl,
-                                          int64_t M, int32_t round, int32_t* s_sel) {
+__device__ inline void select_all_visible(const ScratchG& s, int r, int K, int64_t n_vis, int32_t* s_sel) {
   const int tid = threadIdx.x;
   const auto sel = s.sel + (int64_t)r * K;
   for (int t = tid; t < K; t += kSelThreads) {
@@ -143,7 +110,7 @@ __device__ inline void select_all_visible(const UnitG& u, const ScratchG& s, int
     s_sel[t] = t < n_vis ? t : -1;
   }
   __syncthreads();
-  mark_selection(u, s, s_sel, (int)n_vis, offl, M, round);
+  mark_selection(s, s_sel, (int)n_vis);
   if (tid == 0) s.sel_n[r] = (int32_t)n_vis;
 }
 
@@ -222,17 +189,14 @@ struct SelectLds {
   uint32_t last;
 };
 
-// The row's final step, run by the workgroup of its last chunk to finish: the
-// remaining digits over the candidates -- the threshold key tau and the number
-// E of keys equal to tau that are taken -- then the selection in position
-// order (every key above tau, and the E lowest-position keys equal to tau),
-// its marks in the step's bitmaps, and the classification against the cache.
-__device__ void resolve_row(const TopkKArgs& ka, const UnitG& u, const ScratchG& s, int r, int64_t n_vis,
-                            int64_t M, int32_t round, int b0, int b1, uint32_t need, uint32_t cnt,
-                            const uint32_t* h1c, SelectLds& sm, uint32_t* lds) {
+// The row's final step: the remaining digits over the candidates -- the
+// threshold key tau and the number E of keys equal to tau that are taken --
+// then the selection in position order (every key above tau, and the E
+// lowest-position keys equal to tau) and its marks in the step's union bitmap.
+__device__ void resolve_row(const TopkKArgs& ka, const ScratchG& s, int r, int64_t n_vis, int b0, int b1,
+                            uint32_t need, uint32_t cnt, const uint32_t* h1c, SelectLds& sm, uint32_t* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = ka.K;
-  const bool offl = ka.mode == 0;
   const int n_chunks = (int)((n_vis + kTopkChunk - 1) / kTopkChunk);
 
   // (the histograms are cleared for the next step by the gather's assign kernel)
@@ -275,6 +239,13 @@ __device__ void resolve_row(const TopkKArgs& ka, const UnitG& u, const ScratchG&
   for (int b = tid; b < 1024; b += kSelThreads) sm.hist[b] = 0;
   for (int j = tid; j < K; j += kSelThreads) sm.sel[j] = -1;   // every entry is written below
   __syncthreads();
+
+  // Ordered emit layout: wave w owns candidates [w seg, (w+1) seg), 64
+  // consecutive at a time (with the candidates in LDS, at most kEmitIters per lane).
+  const uint32_t seg = ((C + kSelWaves * 64 - 1) / (kSelWaves * 64)) * 64;
+  const uint32_t w0 = min(C, wave * seg), w1 = min(C, w0 + seg);
+  const bool fused = src.lkey != nullptr;              // seg <= 64 kEmitIters
+
   for (uint32_t i = tid; i < C; i += kSelThreads) {
     uint32_t key;
     int32_t pos;
@@ -287,11 +258,8 @@ __device__ void resolve_row(const TopkKArgs& ka, const UnitG& u, const ScratchG&
   const uint32_t tau = (p22 << 10) | (uint32_t)b2;
   const uint32_t E = need;                             // keys equal to tau that are taken
 
-  // Ordered emit.  Wave w owns candidates [w seg, (w+1) seg), 64 consecutive at
-  // a time; a first pass counts its keys above and equal to tau, a scan over the
+  // A first pass counts each wave's keys above and equal to tau, a scan over the
   // waves gives each wave its starting ranks, a second pass writes.
-  const uint32_t seg = ((C + kSelWaves * 64 - 1) / (kSelWaves * 64)) * 64;
-  const uint32_t w0 = min(C, wave * seg), w1 = min(C, w0 + seg);
   const uint64_t below = lanes_below(lane);
   uint32_t n_gt = 0, n_eq = 0;
   for (uint32_t i0 = w0; i0 < w1; i0 += 64) {
@@ -314,27 +282,50 @@ __device__ void resolve_row(const TopkKArgs& ka, const UnitG& u, const ScratchG&
     eq_run += w < wave ? sm.wcnt[kSelWaves + w] : 0u;
   }
   const auto sel = s.sel + (int64_t)r * K;
-  for (uint32_t i0 = w0; i0 < w1; i0 += 64) {
-    const uint32_t i = i0 + lane;
-    uint32_t key = 0;
-    int32_t pos = -1;
-    if (i < w1) src.get(i, &key, &pos);
+  // the write position of candidate i, or 0xFFFFFFFF if it is not taken
+  auto place = [&](uint32_t i, uint32_t key, uint32_t* at) {
     const bool gt = i < w1 && key > tau, eq = i < w1 && key == tau;
     const uint64_t bg = __ballot(gt), be = __ballot(eq);
     const uint32_t gr = gt_run + (uint32_t)__popcll(bg & below);
     const uint32_t er = eq_run + (uint32_t)__popcll(be & below);
-    uint32_t at = 0xFFFFFFFFu;
-    if (gt) at = gr + min(er, E);
-    else if (eq && er < E) at = gr + er;
-    if (at < (uint32_t)K) {                            // always, when the histograms match the keys
-      sel[at] = pos;
-      sm.sel[at] = pos;
-    }
+    *at = 0xFFFFFFFFu;
+    if (gt) *at = gr + min(er, E);
+    else if (eq && er < E) *at = gr + er;
     gt_run += (uint32_t)__popcll(bg);
     eq_run += (uint32_t)__popcll(be);
+  };
+  if (fused) {
+    // each taken position is written and marked in the union bitmap at once
+#pragma unroll
+    for (int it = 0; it < kEmitIters; ++it) {
+      const uint32_t i0 = w0 + 64 * it;
+      if (i0 >= w1) break;                              // (uniform in the wave)
+      const uint32_t i = i0 + lane;
+      const uint32_t key = i < w1 ? lkey[i] : 0u;
+      const int32_t pos = i < w1 ? lpos[i] : -1;
+      uint32_t at;
+      place(i, key, &at);
+      if (at < (uint32_t)K && pos >= 0) {              // always, when the histograms match the keys
+        sel[at] = pos;
+        g_or(&s.selmask[pos >> 5], 1u << (pos & 31));
+      }
+    }
+  } else {
+    for (uint32_t i0 = w0; i0 < w1; i0 += 64) {
+      const uint32_t i = i0 + lane;
+      uint32_t key = 0;
+      int32_t pos = -1;
+      if (i < w1) src.get(i, &key, &pos);
+      uint32_t at;
+      place(i, key, &at);
+      if (at < (uint32_t)K) {                          // always, when the histograms match the keys
+        sel[at] = pos;
+        sm.sel[at] = pos;
+      }
+    }
+    __syncthreads();
+    mark_selection(s, sm.sel, K);
   }
-  __syncthreads();
-  mark_selection(u, s, sm.sel, K, offl, M, round);
   if (tid == 0) s.sel_n[r] = K;
 }
 
@@ -415,11 +406,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_final_kernel(TopkKArgs ka) {
   const int64_t n_vis = ps.L - a.R + r + 1;
   const int K = ka.K;
   if (n_vis <= K) {
-    select_all_visible(u, s, r, K, n_vis, ka.mode == 0, ps.M, ps.round, sm.sel);
+    select_all_visible(s, r, K, n_vis, sm.sel);
   } else {
     const int n_chunks = (int)((n_vis + kTopkChunk - 1) / kTopkChunk);
     const uint32_t cnt = tid < n_chunks ? cnt_all : 0u;  // lists of this step's chunks only
-    resolve_row(ka, u, s, r, n_vis, ps.M, ps.round, dig.x, dig.y, (uint32_t)dig.z, cnt, h1c, sm, lds);
+    resolve_row(ka, s, r, n_vis, dig.x, dig.y, (uint32_t)dig.z, cnt, h1c, sm, lds);
   }
   plan_if_last(u, s, ka.plan, (uint32_t)a.R, ps, lds);
 }

@@ -262,7 +262,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   auto take = [&](size_t bytes) { size_t at = cur; cur += align_up(bytes ? bytes : 1); return at; };
   const size_t o_units = take(sizeof(UnitDev) * n_units);
   const size_t o_scr = take(sizeof(SeqScratch) * cfg->n_seqs);
-  struct UnitOff { size_t keys, rows, slots, ring, pos_slot, slot_pos, fill, pin, hand, dyn, totals; };
+  struct UnitOff { size_t keys, rows, slots, ring, pos_slot, hot, slot_pos, fill, pin, hand, dyn, totals; };
   std::vector<UnitOff> uo(n_units);
   for (int i = 0; i < n_units; ++i) {
     uo[i].keys = take((size_t)P * g.index_dim * 2);
@@ -270,6 +270,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     uo[i].slots = off ? take((size_t)S * rb) : 0;
     uo[i].ring = off ? take((size_t)g.ring_cap * rb) : 0;
     uo[i].pos_slot = off ? take((size_t)P * 8) : 0;
+    uo[i].hot = off ? take((size_t)P / 32 * 4) : 0;
     uo[i].slot_pos = off ? take((size_t)S * 4) : 0;
     uo[i].fill = off ? take((size_t)S * 4) : 0;
     uo[i].pin = off ? take((size_t)S * 4) : 0;
@@ -278,7 +279,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     uo[i].totals = take(64);
   }
   struct ScrOff { size_t scores, sel, sel_n, uni, kind, src, map, compact, po, pml, cnt, info,
-                  selmask, hitmask, base_u, base_m, pinmask, pdesc, victim, done, hist0, hist1, cand,
+                  selmask, hitmask, base_u, base_m, pdesc, victim, done, hist0, hist1, cand,
                   cand_n, rowdig; };
   std::vector<ScrOff> so(cfg->n_seqs);
   for (int q = 0; q < cfg->n_seqs; ++q) {
@@ -298,7 +299,6 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     so[q].hitmask = take((size_t)P / 32 * 4);
     so[q].base_u = take((size_t)P / 32 * 4);
     so[q].base_m = take((size_t)P / 32 * 4);
-    so[q].pinmask = take((size_t)g.s_words * 4);
     so[q].pdesc = take((size_t)P * 16);
     so[q].victim = take((size_t)g.s_words * 32 * 8);
     so[q].done = take(4);
@@ -347,6 +347,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
       u.slots = base + uo[i].slots;
       u.ring = base + uo[i].ring;
       u.pos_slot = reinterpret_cast<i32x2*>(base + uo[i].pos_slot);
+      u.hot = reinterpret_cast<uint32_t*>(base + uo[i].hot);
       u.slot_pos = reinterpret_cast<int32_t*>(base + uo[i].slot_pos);
       u.fill_round = reinterpret_cast<int32_t*>(base + uo[i].fill);
       u.pin_round = reinterpret_cast<int32_t*>(base + uo[i].pin);
@@ -382,7 +383,6 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     c.hitmask = reinterpret_cast<uint32_t*>(base + so[q].hitmask);
     c.base_u = reinterpret_cast<uint32_t*>(base + so[q].base_u);
     c.base_m = reinterpret_cast<uint32_t*>(base + so[q].base_m);
-    c.pinmask = reinterpret_cast<uint32_t*>(base + so[q].pinmask);
     c.pdesc = reinterpret_cast<i32x4*>(base + so[q].pdesc);
     c.victim = reinterpret_cast<i32x2*>(base + so[q].victim);
     c.done = reinterpret_cast<uint32_t*>(base + so[q].done);
