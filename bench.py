@@ -53,65 +53,84 @@ def log(*a):
 
 
 def gen_inputs(w, n_steps):
+    """Every step's appended rows and queries, per layer, stacked over sequences."""
     import dsa_synth as S
-    R = w.rows_per_step
-    keys = np.empty((n_steps, R, w.index_dim), np.uint16)
-    rows = np.empty((n_steps, R, w.row_bytes), np.uint8)
-    iq = np.empty((n_steps, 1, R, w.index_heads, w.index_dim), np.uint16)
-    iw = np.empty((n_steps, 1, R, w.index_heads), np.float32)
-    ql = np.empty((n_steps, 1, R, w.heads, w.latent_dim), np.uint16)
-    qr = np.empty((n_steps, 1, R, w.heads, w.rope_dim), np.uint16)
+    R, Q, NL = w.rows_per_step, w.seqs, w.layers
+    keys = np.empty((n_steps, NL, Q, R, w.index_dim), np.uint16)
+    rows = np.empty((n_steps, NL, Q, R, w.row_bytes), np.uint8)
+    iq = np.empty((n_steps, NL, Q, R, w.index_heads, w.index_dim), np.uint16)
+    iw = np.empty((n_steps, NL, Q, R, w.index_heads), np.float32)
+    ql = np.empty((n_steps, NL, Q, R, w.heads, w.latent_dim), np.uint16)
+    qr = np.empty((n_steps, NL, Q, R, w.heads, w.rope_dim), np.uint16)
     for s in range(n_steps):
-        keys[s], rows[s] = S.step_rows(w, 0, 0, s)
-        iq[s, 0], iw[s, 0], ql[s, 0], qr[s, 0] = S.step_queries(w, 0, 0, s)
+        for l in range(NL):
+            for q in range(Q):
+                keys[s, l, q], rows[s, l, q] = S.step_rows(w, l, q, s)
+                iq[s, l, q], iw[s, l, q], ql[s, l, q], qr[s, l, q] = S.step_queries(w, l, q, s)
     return keys, rows, iq, iw, ql, qr
 
 
 class Runner:
-    """One session with every step's inputs already in HBM; calls the C ABI directly."""
+    """One session (every layer and sequence of the workload) with every step's
+    inputs already in HBM; calls the C ABI directly.  One step = for each layer
+    in order: append R rows to each sequence, then one decode step of the layer
+    (all sequences together)."""
 
-    def __init__(self, w, mode, host_inputs, hist):
+    def __init__(self, w, mode, host_inputs):
         import torch
+        import dsa_synth as S
         import kv_cache_offload_amd as K
         from tests.parity_util import dev_tensor
         self.K, self.torch, self.w = K, torch, w
         cfg = K.make_config(max_positions=w.max_positions, index_heads=w.index_heads, heads=w.heads,
                             top_k=w.top_k, hot_slots=w.hot_slots, max_query_rows=w.rows_per_step,
-                            n_seqs=w.seqs, softmax_scale=w.softmax_scale, mode=mode)
+                            n_layers=w.layers, n_seqs=w.seqs, softmax_scale=w.softmax_scale, mode=mode)
         self.sess = K.Session(cfg)
         dev = self.sess.device
-        hk, hr = hist
-        for c in range(0, hk.shape[0], 65536):
-            self.sess.append_rows(0, 0, dev_tensor(hk[c:c + 65536], dev), dev_tensor(hr[c:c + 65536], dev))
-        self.sess.flush(0, 0)
-        if mode == K.KV_OFFLOAD and w.warm:
-            self.sess.warm_hot(0, 0)
+        for l in range(w.layers):
+            for q in range(w.seqs):
+                hk, hr = S.history(w, l, q)
+                for c in range(0, hk.shape[0], 65536):
+                    self.sess.append_rows(l, q, dev_tensor(hk[c:c + 65536], dev), dev_tensor(hr[c:c + 65536], dev))
+                self.sess.flush(l, q)
+                if mode == K.KV_OFFLOAD and w.warm:
+                    self.sess.warm_hot(l, q)
+                torch.cuda.synchronize()
         self.d = [dev_tensor(a, dev) for a in host_inputs]
-        self.out = torch.empty((1, w.rows_per_step, w.heads, w.latent_dim), dtype=torch.float32, device=dev)
+        self.out = torch.empty((w.seqs, w.rows_per_step, w.heads, w.latent_dim), dtype=torch.float32, device=dev)
         self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         keys, rows, iq, iw, ql, qr = self.d
-        self.ptr = [tuple(int(t[s].data_ptr()) for t in self.d) for s in range(keys.shape[0])]
+        self.ptr = [[tuple(int(t[s, l].data_ptr()) for t in self.d) for l in range(w.layers)]
+                    for s in range(keys.shape[0])]
         self.h = self.sess.h
         self.next = 0
         torch.cuda.synchronize()
 
     def steps(self, n):
-        K, R, lib = self.K, self.w.rows_per_step, self.K._lib
+        K, R, lib, w = self.K, self.w.rows_per_step, self.K._lib, self.w
         out = ctypes.c_void_p(self.out.data_ptr())
+        kb, rb = w.index_dim * 2 * R, w.row_bytes * R          # bytes of one sequence's appended keys / rows
         for _ in range(n):
-            pk, pr, piq, piw, pql, pqr = self.ptr[self.next]
-            st = lib.dsa_append_rows(self.h, 0, 0, R, ctypes.c_void_p(pk), ctypes.c_void_p(pr), self.stream)
-            if st != K.OK:
-                raise K.DsaError("dsa_append_rows", st, K.dsa_last_error(self.h))
-            st = lib.dsa_decode_step(self.h, 0, R, ctypes.c_void_p(piq), ctypes.c_void_p(piw), ctypes.c_void_p(pql),
-                                     ctypes.c_void_p(pqr), out, self.stream)
-            if st != K.OK:
-                raise K.DsaError("dsa_decode_step", st, K.dsa_last_error(self.h))
+            for l, (pk, pr, piq, piw, pql, pqr) in enumerate(self.ptr[self.next]):
+                for q in range(w.seqs):
+                    st = lib.dsa_append_rows(self.h, l, q, R, ctypes.c_void_p(pk + q * kb), ctypes.c_void_p(pr + q * rb),
+                                             self.stream)
+                    if st != K.OK:
+                        raise K.DsaError("dsa_append_rows", st, K.dsa_last_error(self.h))
+                st = lib.dsa_decode_step(self.h, l, R, ctypes.c_void_p(piq), ctypes.c_void_p(piw),
+                                         ctypes.c_void_p(pql), ctypes.c_void_p(pqr), out, self.stream)
+                if st != K.OK:
+                    raise K.DsaError("dsa_decode_step", st, K.dsa_last_error(self.h))
             self.next += 1
 
     def totals(self):
+        """Step counters summed over every unit."""
         self.torch.cuda.synchronize()
-        return self.sess.debug("totals").cpu().numpy().view(np.int64).copy()
+        t = np.zeros(8, np.int64)
+        for l in range(self.w.layers):
+            for q in range(self.w.seqs):
+                t += self.sess.debug("totals", l, q).cpu().numpy().view(np.int64)
+        return t
 
     def L(self):
         return self.sess.unit_state(0, 0)["L"]
@@ -127,43 +146,44 @@ def timed(runner, n):
 
 
 def algorithmic_bytes(w, kind, n_steps, L0, cnt, long_hist):
-    """Bytes each kernel group must move per launch, averaged over the timed steps.
+    """Bytes each kernel group must move per launch (one layer, every sequence),
+    averaged over the timed steps.
 
     Scratch that only the implementation needs (scores, histograms, split-K
     partials) is not counted, except where the kernel's whole job is to move it
-    (the partial top-k passes and the attention merge).
+    (the partial top-k pass and the attention merge).
     """
-    R, K, H = w.rows_per_step, w.top_k, w.heads
+    R, K, H, Q = w.rows_per_step, w.top_k, w.heads, w.seqs
+    launches = n_steps * w.layers
     Lmean = L0 + R * (n_steps + 1) / 2.0
     rb = w.row_bytes
-    U = cnt[0] / n_steps
-    hit, ring, miss, noslot = (cnt[i] / n_steps for i in (1, 2, 3, 4))
-    res = cnt[7] / n_steps
-    wb = w.ring_rows * rb * 2 * R / w.ring_rows          # 64-row writeback every 64/R steps, read + write
+    U = cnt[0] / launches
+    hit, ring, miss, noslot = (cnt[i] / launches for i in (1, 2, 3, 4))
+    wb = Q * w.ring_rows * rb * 2 * R / w.ring_rows      # 64-row writeback every 64/R steps, read + write
     if kind == "index_score":
-        return Lmean * w.index_dim * 2                     # every key once
+        return Q * Lmean * w.index_dim * 2                 # every key once
     if kind == "topk_collect":
-        return R * Lmean * 4 * (2 if long_hist else 1)     # the scores once (twice with the refine pass)
+        return Q * R * Lmean * 4 * (2 if long_hist else 1)
     if kind == "topk_resolve":
-        return R * K * 4                                   # the selection out
+        return Q * R * Lmean * 4 + Q * R * K * 4          # the scores once, the selection out
     if kind == "gather":
         # union bookkeeping: descriptor + union arrays per entry, victim and slot-table entries per miss
         return U * (16 + 12) + miss * (8 + 16) + wb
     if kind == "attention":
         # every selected row read from its source (slot, ring, host mirror, HBM row store), the compact
         # copy and the misses' slot fills written, the queries read
-        return R * K * rb + U * rb + miss * rb + R * H * (512 + 64) * 2
+        return Q * R * K * rb + U * rb + miss * rb + Q * R * H * (512 + 64) * 2
     if kind == "attention_merge":
-        return R * H * 512 * 4
+        return Q * R * H * 512 * 4
     if kind == "append":
-        return R * (w.index_dim * 2 + rb) * 2
+        return Q * R * (w.index_dim * 2 + rb) * 2
     return 0.0
 
 
-def run_mode(w, mode, inputs, hist, args):
+def run_mode(w, mode, inputs, args):
     import kv_cache_offload_amd as K
     name = "offload" if mode == K.KV_OFFLOAD else "resident"
-    r = Runner(w, mode, inputs, hist)
+    r = Runner(w, mode, inputs)
     log(f"{name}: history loaded (L={r.L()}), warmup {args.warmup}")
     r.steps(args.warmup)
     c_before = r.totals()
@@ -175,7 +195,7 @@ def run_mode(w, mode, inputs, hist, args):
     # dispatch events on (their host-side cost would distort the timed region)
     kc_before = r.totals()
     kL0 = r.L()
-    r.sess.set_kernel_timing(True, reserve_steps=args.kernel_steps)
+    r.sess.set_kernel_timing(True, reserve_steps=args.kernel_steps * w.layers)
     dt_ev = timed(r, args.kernel_steps)
     kt = r.sess.kernel_times()
     r.sess.set_kernel_timing(False)
@@ -192,9 +212,12 @@ def run_mode(w, mode, inputs, hist, args):
     return res
 
 
-def cpu_baseline(w, inputs, hist, budget_s):
-    """The oracle as it stands, on the host cores, on the first decode steps of the same workload."""
+def cpu_baseline(w, inputs, budget_s):
+    """The oracle as it stands, on the host cores, on the first decode steps of the same workload
+    (its first unit: layer 0, sequence 0)."""
+    import dsa_synth as S
     from oracle import MODE_OFFLOAD, OracleUnit, UnitShape
+    hist = S.history(w, 0, 0)
     u = OracleUnit(UnitShape(max_positions=w.max_positions, index_heads=w.index_heads, index_dim=w.index_dim,
                              heads=w.heads, top_k=w.top_k, hot_slots=w.hot_slots, max_query_rows=w.rows_per_step,
                              mode=MODE_OFFLOAD, softmax_scale=w.softmax_scale))
@@ -206,8 +229,8 @@ def cpu_baseline(w, inputs, hist, budget_s):
     t0 = time.perf_counter()
     n = 0
     while n < keys.shape[0] and (n < 2 or time.perf_counter() - t0 < budget_s):
-        u.append(keys[n], rows[n])
-        u.decode_step(iq[n, 0], iw[n, 0], ql[n, 0], qr[n, 0])
+        u.append(keys[n, 0, 0], rows[n, 0, 0])
+        u.decode_step(iq[n, 0, 0], iw[n, 0, 0], ql[n, 0, 0], qr[n, 0, 0])
         n += 1
     dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
@@ -233,11 +256,10 @@ def main():
     log(f"generating {n_steps} steps of inputs for {w.name}")
     t0 = time.perf_counter()
     inputs = gen_inputs(w, n_steps)
-    hist = S.history(w, 0, 0)
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
 
-    off = run_mode(w, K.KV_OFFLOAD, inputs, hist, args)
-    resd = None if args.no_resident else run_mode(w, K.KV_HBM_RESIDENT, inputs, hist, args)
+    off = run_mode(w, K.KV_OFFLOAD, inputs, args)
+    resd = None if args.no_resident else run_mode(w, K.KV_HBM_RESIDENT, inputs, args)
 
     # dominant kernel of the offloaded step and its roofline
     kern = off["kernels"]
@@ -248,18 +270,20 @@ def main():
                 frac=d["GBps"] / HBM_PEAK_GBPS, traffic=None, avg_us=d["avg_us"],
                 bytes_per_launch=d["bytes_per_launch"])
 
-    R = w.rows_per_step
+    R, Q, NL = w.rows_per_step, w.seqs, w.layers
     c = off["counters"]
-    host_bytes = c[6]
     n = args.steps
-    sel_keys = ("index_score", "topk_collect", "topk_resolve", "gather")
-    ssg_us = sum(kern[k]["avg_us"] * kern[k]["launches"] / off["kernel_steps"] for k in sel_keys if k in kern)
-    # HBM bytes of score + select + gather: keys once; rows read from HBM (hits, ring) once;
-    # compact rows and slot fills written once
-    L_mean = off["L_start"] + R * (n + 1) / 2.0
+    per_step = lambda k: kern[k]["avg_us"] * kern[k]["launches"] / off["kernel_steps"] if k in kern else 0.0
     rb = w.row_bytes
-    ssg_bytes = L_mean * w.index_dim * 2 + ((c[1] + c[2] + c[7]) + c[0] + c[3]) * rb / n
-    gather_us = kern["gather"]["avg_us"] if "gather" in kern else 0.0
+    L_mean = off["L_start"] + R * (n + 1) / 2.0
+    # scoring + selection: every index key once per step (HBM)
+    ss_us = per_step("index_score") + per_step("topk_collect") + per_step("topk_resolve")
+    ss_bytes = NL * Q * L_mean * w.index_dim * 2
+    # gather + attention: selected rows from their sources (hits and ring rows from HBM, misses over the
+    # host link), compact rows and slot fills written to HBM
+    host_bytes = c[6] / n
+    ga_us = per_step("gather") + per_step("attention")
+    ga_hbm_bytes = ((c[1] + c[2] + c[7]) + c[0] + c[3]) * rb / n
     line = {
         "metric": METRIC,
         "value": off["steps_per_s"],
@@ -274,17 +298,22 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "history": w.history, "query_rows": R, "top_k": w.top_k,
-                   "hot_slots": w.hot_slots, "index_heads": w.index_heads, "heads": w.heads,
-                   "row_bytes": w.row_bytes, "mode": "offload", "L_at_timed_start": off["L_start"]},
-        "query_rows_per_s": off["steps_per_s"] * R,
+        "config": {"workload": w.name, "layers": NL, "sequences": Q, "history": w.history, "query_rows": R,
+                   "top_k": w.top_k, "hot_slots": w.hot_slots, "index_heads": w.index_heads, "heads": w.heads,
+                   "row_bytes": rb, "mode": "offload", "L_at_timed_start": off["L_start"]},
+        "query_rows_per_s": off["steps_per_s"] * R * Q,
         "roofline": roof,
-        "score_select_gather": {"us_per_step": ssg_us, "hbm_bytes_per_step": ssg_bytes,
-                                "hbm_frac": ssg_bytes / (ssg_us * 1e-6) / 1e9 / HBM_PEAK_GBPS},
-        "host_link": {"miss_bytes_per_step": host_bytes / args.steps,
-                      "miss_rows_per_step": (c[3] + c[4]) / args.steps,
+        "score_select": {"us_per_step": ss_us, "hbm_bytes_per_step": ss_bytes,
+                         "hbm_frac": ss_bytes / (ss_us * 1e-6) / 1e9 / HBM_PEAK_GBPS if ss_us else 0.0},
+        "gather_attention": {"us_per_step": ga_us, "hbm_bytes_per_step": ga_hbm_bytes,
+                             "host_bytes_per_step": host_bytes,
+                             "hbm_frac": ga_hbm_bytes / (ga_us * 1e-6) / 1e9 / HBM_PEAK_GBPS if ga_us else 0.0,
+                             "host_link_GBps": host_bytes / (ga_us * 1e-6) / 1e9 if ga_us else 0.0,
+                             "host_link_frac": host_bytes / (ga_us * 1e-6) / 1e9 / HOST_LINK_PEAK_GBPS
+                             if ga_us else 0.0},
+        "host_link": {"miss_bytes_per_step": host_bytes,
+                      "miss_rows_per_step": (c[3] + c[4]) / n,
                       "hit_rate": c[1] / max(1, c[0] - c[2]),
-                      "gather_GBps": (host_bytes / n) / (gather_us * 1e-6) / 1e9 if gather_us else 0.0,
                       "peak_GBps": HOST_LINK_PEAK_GBPS},
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
         "kernels_GBps": {k: round(v["GBps"], 1) for k, v in kern.items()},
@@ -294,9 +323,9 @@ def main():
         line["resident"] = {"value": resd["steps_per_s"], "ms_per_step": 1e3 * resd["seconds"] / args.steps,
                             "kernels_us": {k: round(v["avg_us"], 2) for k, v in resd["kernels"].items()}}
         line["offload_slowdown"] = resd["steps_per_s"] / off["steps_per_s"] - 1.0
-    if not args.no_cpu:
+    if not args.no_cpu and NL == 1 and Q == 1:
         log("timing the oracle on the host")
-        line["cpu_baseline"] = cpu_baseline(w, inputs, hist, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_seconds)
     if args.calib_copy:
         n = 256 << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
