@@ -43,6 +43,7 @@ struct PlanState {
 };
 
 constexpr int kPlanRegWords = 4;   // union words a thread keeps in registers (histories <= 131,072)
+constexpr int kPlanChunk = 8;      // 64-word rows of a wave per batch of loads (longer histories)
 constexpr int kWalkPer = 4;        // ring offsets a thread examines per pass of the victim walk
 constexpr int kWalkWords = kPlanThreads * kWalkPer / 32;   // 32-offset words per pass
 
@@ -93,6 +94,27 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
       c.w += __popc(hw);
     }
   };
+  // Longer histories: wave v owns the words [v seg, (v+1) seg), 64 consecutive
+  // words per load instruction (coalesced), kPlanChunk rows of loads in flight.
+  const int wave = tid >> 6;
+  const int64_t seg = ((nw + kPlanWaves * 64 - 1) / (kPlanWaves * 64)) * 64;
+  const int64_t sw0 = min(nw, (int64_t)wave * seg), sw1 = min(nw, sw0 + seg);
+  auto wave_rows = [&](auto&& fn) {                    // fn(w, sel word, hit word, valid) per row, all lanes
+    for (int64_t r0 = sw0; r0 < sw1; r0 += 64 * kPlanChunk) {
+      uint32_t cs[kPlanChunk], ch[kPlanChunk];
+#pragma unroll
+      for (int e = 0; e < kPlanChunk; ++e) {
+        const int64_t w = r0 + 64 * e + lane;
+        cs[e] = w < sw1 ? sel[w] : 0u;
+        ch[e] = (off && w < sw1) ? u.hot[w] : 0u;
+      }
+#pragma unroll
+      for (int e = 0; e < kPlanChunk; ++e) {
+        const int64_t w = r0 + 64 * e + lane;
+        if (r0 + 64 * e < sw1) fn(w, cs[e], cs[e] & ch[e], w < sw1);   // (uniform in the wave)
+      }
+    }
+  };
   if (words_in_regs) {
 #pragma unroll
     for (int e = 0; e < kPlanRegWords; ++e) {
@@ -100,13 +122,40 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
       if (w0 + e < w1) count(w0 + e, swr[e], hwr[e]);
     }
   } else {
-    for (int64_t w = w0; w < w1; ++w) {
-      const uint32_t sw = sel[w];
-      count(w, sw, off ? (sw & u.hot[w]) : 0u);
-    }
+    wave_rows([&](int64_t w, uint32_t sw, uint32_t hw, bool valid) {
+      if (valid) count(w, sw, hw);
+    });
   }
   uint4 tot;
-  const uint4 base = block_scan4<kPlanWaves>(c, &tot, sh);
+  uint4 base;
+  if (words_in_regs) {
+    base = block_scan4<kPlanWaves>(c, &tot, sh);
+  } else {
+    // each wave's counts, then the waves' scan (a wave's words are contiguous)
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      c.x += __shfl_xor(c.x, o);
+      c.y += __shfl_xor(c.y, o);
+      c.z += __shfl_xor(c.z, o);
+      c.w += __shfl_xor(c.w, o);
+    }
+    if (lane == 0) {
+      sh[4 * wave] = c.x;
+      sh[4 * wave + 1] = c.y;
+      sh[4 * wave + 2] = c.z;
+      sh[4 * wave + 3] = c.w;
+    }
+    __syncthreads();
+    base = make_uint4(0u, 0u, 0u, 0u);
+    tot = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int v = 0; v < kPlanWaves; ++v) {
+      const uint4 x = make_uint4(sh[4 * v], sh[4 * v + 1], sh[4 * v + 2], sh[4 * v + 3]);
+      if (v < wave) { base.x += x.x; base.y += x.y; }
+      tot.x += x.x; tot.y += x.y; tot.z += x.z; tot.w += x.w;
+    }
+    __syncthreads();                                   // sh is reused below
+  }
   const uint32_t U = tot.x, n_miss = tot.y, n_ring = tot.z, n_hit = tot.w;
   uint32_t bu = base.x, bm = base.y;
   auto bases = [&](int64_t w, uint32_t sw, uint32_t hw) {
@@ -122,10 +171,22 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
     for (int e = 0; e < kPlanRegWords; ++e)
       if (w0 + e < w1) bases(w0 + e, swr[e], hwr[e]);
   } else {
-    for (int64_t w = w0; w < w1; ++w) {
-      const uint32_t sw = sel[w];
-      bases(w, sw, off ? (sw & u.hot[w]) : 0u);
-    }
+    // per row of 64 words: the lanes' exclusive scan of (union, miss) counts
+    wave_rows([&](int64_t w, uint32_t sw, uint32_t hw, bool valid) {
+      uint32_t nu = 0, nm = 0;
+      if (valid && sw) {
+        const uint32_t rw = off ? (sw & ring_bits(w, M)) : 0u;
+        nu = __popc(sw);
+        nm = off ? __popc(sw & ~hw & ~rw) : 0u;
+      }
+      const uint32_t iu = wave_incl_scan(nu, lane), im = wave_incl_scan(nm, lane);
+      if (valid) {
+        s.base_u[w] = bu + iu - nu;
+        s.base_m[w] = bm + im - nm;
+      }
+      bu += __shfl(iu, 63);
+      bm += __shfl(im, 63);
+    });
   }
 
   // Victims: slots in ring order from the hand, skipping the pinned ones -- a

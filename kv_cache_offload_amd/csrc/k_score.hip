@@ -118,16 +118,14 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreKArgs ka) {
     const int64_t t0 = (first_sub + si) * 32;
     if (t0 >= L) break;
     const int64_t t = t0 + n;
-    // B fragments: 8 k-steps x 16 bytes of key t (the first tile's are already loaded).
-    if (si > 0) {
-      if (t < L) {
-        const DSA_GLOBAL bf16x8* kp = reinterpret_cast<const DSA_GLOBAL bf16x8*>(u.keys + t * 128 + 64 * hf);
+    // The next tile's keys are requested before this tile is computed (loads
+    // complete in issue order, so this tile's wait does not include them).
+    bf16x8 bn[8];
+    if (si + 1 < ka.subs_per_wave) {
+      const int64_t tn = min(t + 32, ka.p_pad - 1);
+      const DSA_GLOBAL bf16x8* kp = reinterpret_cast<const DSA_GLOBAL bf16x8*>(u.keys + tn * 128 + 64 * hf);
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) b[ks] = kp[ks];
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) b[ks] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
-      }
+      for (int ks = 0; ks < 8; ++ks) bn[ks] = kp[ks];
     }
     // Up to four row tiles at a time: independent accumulation chains, so the
     // MFMA pipeline is never waiting on one accumulator.
@@ -200,6 +198,10 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreKArgs ka) {
         }
       }
     }
+    if (si + 1 < ka.subs_per_wave) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) b[ks] = bn[ks];
+    }
   }
   __syncthreads();
   for (int w = threadIdx.x; w < R * (kRadixBins / 2); w += blockDim.x) {
@@ -233,8 +235,9 @@ hipError_t launch_score(const Geometry& g, const StepArgs& a, const uint16_t* q,
   ka.p_pad = g.p_pad;
   ka.r_max = g.r_max;
   const int64_t subs = (a.l_max + 31) / 32;
-  // Enough waves to cover the chip several times; longer per-wave runs amortise the Q staging.
-  int spw = (int)((subs + 4 * 256 * 4 - 1) / (4 * 256 * 4));
+  // Enough waves (over all sequences) to cover the chip several times; longer
+  // per-wave runs amortise the Q staging and keep the next tile's keys in flight.
+  int spw = (int)((subs * a.n_seqs + 4 * 256 * 4 - 1) / (4 * 256 * 4));
   if (spw < 1) spw = 1;
   if (spw > 8) spw = 8;
   ka.subs_per_wave = spw;

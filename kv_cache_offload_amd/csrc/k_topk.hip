@@ -114,9 +114,34 @@ __device__ inline void select_all_visible(const ScratchG& s, int r, int K, int64
   if (tid == 0) s.sel_n[r] = (int32_t)n_vis;
 }
 
+// Long histories: the row's threshold digits, once per row (instead of in every
+// chunk's workgroup).  Stage 0: the first-digit bin b0 of the K-th largest key
+// and the keys still needed from it; stage 1 (after the refine pass): the
+// second digit b1 within b0.
+__global__ __launch_bounds__(kSelThreads) void topk_digits_kernel(TopkKArgs ka, int stage) {
+  __shared__ uint32_t sh[kSelWaves];
+  const StepArgs& a = ka.a;
+  const int r = blockIdx.x, seq = blockIdx.y;
+  const UnitG u = unit_of(a, seq);
+  const ScratchG s = scratch_of(a, seq);
+  const int64_t n_vis = u.dyn[0] - a.R + r + 1;
+  if (n_vis <= ka.K) return;
+  const auto dig = reinterpret_cast<DSA_GLOBAL i32x4*>(s.rowdig + 4 * r);
+  int b;
+  uint32_t need;
+  if (stage == 0) {
+    find_bin<kSelWaves, kRadixBins, kHistReps>(s.hist0 + (int64_t)r * kRadixBins, (uint32_t)ka.K, sh, &b, &need,
+                                               (int64_t)ka.r_max * kRadixBins);
+    if (threadIdx.x == 0) *dig = (i32x4){b, 0, (int32_t)need, 0};
+  } else {
+    const i32x4 d = *dig;
+    find_bin<kSelWaves, kRadixBins, 1>(s.hist1 + (int64_t)r * kRadixBins, (uint32_t)d.z, sh, &b, &need);
+    if (threadIdx.x == 0) *dig = (i32x4){d.x, b, (int32_t)need, 0};
+  }
+}
+
 // Second-digit histogram of the keys in the first-digit bin b0 (long histories).
 __global__ __launch_bounds__(kPartThreads) void topk_refine_kernel(TopkKArgs ka) {
-  __shared__ uint32_t sh[kPartThreads / 64];
   __shared__ uint32_t lh[kRadixBins];
   const StepArgs& a = ka.a;
   const int chunk = blockIdx.x, r = blockIdx.y, seq = blockIdx.z;
@@ -129,10 +154,7 @@ __global__ __launch_bounds__(kPartThreads) void topk_refine_kernel(TopkKArgs ka)
   const int64_t t0 = start + threadIdx.x * kPerThread;
   float v[kPerThread];
   load_chunk(s.scores + (int64_t)r * ka.p_pad, t0, v);
-  int b0;
-  uint32_t need;
-  find_bin<kPartThreads / 64, kRadixBins, kHistReps>(s.hist0 + (int64_t)r * kRadixBins, (uint32_t)ka.K, sh, &b0,
-                                                     &need, (int64_t)ka.r_max * kRadixBins);
+  const int b0 = s.rowdig[4 * r];                      // from the digits pass
   for (int b = threadIdx.x; b < kRadixBins; b += kPartThreads) lh[b] = 0;
   __syncthreads();
 #pragma unroll
@@ -350,16 +372,21 @@ __global__ __launch_bounds__(kSelThreads) void topk_chunk_kernel(TopkKArgs ka) {
   const f32x4v f = *reinterpret_cast<const DSA_GLOBAL f32x4v*>(s.scores + (int64_t)r * ka.p_pad + t0);
   int b0, b1 = 0;
   uint32_t need;
-  find_bin<kSelWaves, kRadixBins, kHistReps>(s.hist0 + (int64_t)r * kRadixBins, (uint32_t)ka.K, sh, &b0, &need,
-                                             (int64_t)ka.r_max * kRadixBins);
-  if (ka.long_mode)
-    find_bin<kSelWaves, kRadixBins, 1>(s.hist1 + (int64_t)r * kRadixBins, need, sh, &b1, &need);
+  if (ka.long_mode) {                                  // both digits from the digits passes
+    const i32x4 d = *reinterpret_cast<const DSA_GLOBAL i32x4*>(s.rowdig + 4 * r);
+    b0 = d.x;
+    b1 = d.y;
+    need = (uint32_t)d.z;
+  } else {
+    find_bin<kSelWaves, kRadixBins, kHistReps>(s.hist0 + (int64_t)r * kRadixBins, (uint32_t)ka.K, sh, &b0, &need,
+                                               (int64_t)ka.r_max * kRadixBins);
+  }
   uint32_t key[kSelPer];
 #pragma unroll
   for (int e = 0; e < kSelPer; ++e) key[e] = t0 + e < n_vis ? order_key(f[e]) : 0u;   // 0: not visible
   const int shift = ka.long_mode ? 10 : 21;
   const uint32_t thr = ka.long_mode ? (((uint32_t)b0 << 11) | (uint32_t)b1) : (uint32_t)b0;
-  if (chunk == 0 && tid == 0)                          // the row's digits so far, for the final pass
+  if (!ka.long_mode && chunk == 0 && tid == 0)         // the row's digits so far, for the final pass
     *reinterpret_cast<DSA_GLOBAL i32x4*>(s.rowdig + 4 * r) = (i32x4){b0, b1, (int32_t)need, 0};
 
   if (!ka.long_mode) {
@@ -431,8 +458,13 @@ hipError_t launch_topk_partial(const Geometry& g, const StepArgs& a, hipStream_t
   const TopkKArgs ka = topk_args(g, a);
   if (!ka.long_mode) return hipSuccess;
   const int chunks = (int)((a.l_max + kTopkChunk - 1) / kTopkChunk);
-  const dim3 grid((unsigned)chunks, (unsigned)a.R, (unsigned)a.n_seqs);
-  return launch_k(topk_refine_kernel, grid, dim3(kPartThreads), 0, st, ka);
+  const dim3 rows((unsigned)a.R, (unsigned)a.n_seqs);
+  hipError_t e = launch_k(topk_digits_kernel, rows, dim3(kSelThreads), 0, st, ka, 0);
+  if (e != hipSuccess) return e;
+  e = launch_k(topk_refine_kernel, dim3((unsigned)chunks, (unsigned)a.R, (unsigned)a.n_seqs), dim3(kPartThreads), 0,
+               st, ka);
+  if (e != hipSuccess) return e;
+  return launch_k(topk_digits_kernel, rows, dim3(kSelThreads), 0, st, ka, 1);
 }
 
 hipError_t launch_topk_select(const Geometry& g, const StepArgs& a, hipStream_t st) {
