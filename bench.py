@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--no-resident", action="store_true", help="skip the HBM-resident comparison run")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline")
     p.add_argument("--no-cpu", action="store_true")
-    p.add_argument("--calib-copy", action="store_true", help="also run a plain 256 MiB device copy (PMC scaling)")
+    p.add_argument("--calib-copy", action="store_true", help="also run a plain 2 GiB device copy (PMC scaling)")
     return p.parse_args()
 
 
@@ -327,7 +327,7 @@ def main():
         log("timing the oracle on the host")
         line["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_seconds)
     if args.calib_copy:
-        n = 256 << 20
+        n = 2 << 30                                      # well above the last-level cache
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
