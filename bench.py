@@ -48,6 +48,68 @@ def parse():
     return p.parse_args()
 
 
+# Source file of each kernel group (the PMC traffic of a group is reported only
+# while its source is the one the counters were taken on).
+KERNEL_SOURCES = {"index_score": "k_score.hip", "topk_collect": "k_topk.hip", "topk_resolve": "k_topk.hip",
+                  "gather": "k_gather.hip", "attention": "k_attn.hip", "attention_merge": "k_attn.hip",
+                  "append": "k_gather.hip"}
+# rocprofv3 kernel names of each group
+KERNEL_NAMES = {"index_score": ("score_kernel",), "topk_collect": ("topk_refine_kernel", "topk_digits_kernel"),
+                "topk_resolve": ("topk_chunk_kernel", "topk_final_kernel"), "gather": ("gather_assign_kernel",),
+                "attention": ("attn_kernel",), "attention_merge": ("attn_merge_kernel",), "append": ("append_kernel",)}
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+
+
+def source_hash(kind):
+    import hashlib
+    path = os.path.join(ROOT, "kv_cache_offload_amd", "csrc", KERNEL_SOURCES[kind])
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def pmc_traffic(workload, kind):
+    """HBM bytes per launch of a kernel group from the committed counter summary, or None."""
+    try:
+        d = json.load(open(PMC_FILE))[workload][kind]
+    except (OSError, KeyError, ValueError):
+        return None
+    return d["bytes_per_launch"] if d.get("source_sha256_16") == source_hash(kind) else None
+
+
+def pmc_summary(workload, fetch_csv, write_csv):
+    """Write profiles/pmc_traffic.json from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE), each scaled by
+    what the counter reads for the 2 GiB device copy of the same run (--calib-copy)."""
+    import csv
+    import re
+
+    def per_kernel(path, counter):
+        vals, calib = {}, []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name, v = r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0
+            if "copyBuffer" in name and int(r["Grid_Size"]) >= 131072:
+                calib.append(v)
+                continue
+            for kind, names in KERNEL_NAMES.items():
+                if any(re.search(r"\b" + n + r"\b", name) for n in names):
+                    vals.setdefault(kind, []).append(v)
+        assert calib, f"no calibration copy in {path}"
+        factor = (2 << 30) / (sum(calib) / len(calib))
+        return {k: factor * sum(v) / len(v) for k, v in vals.items()}, factor
+
+    f, ff = per_kernel(fetch_csv, "FETCH_SIZE")
+    w, wf = per_kernel(write_csv, "WRITE_SIZE")
+    try:
+        out = json.load(open(PMC_FILE))
+    except (OSError, ValueError):
+        out = {}
+    out[workload] = {k: {"fetch_bytes": f.get(k, 0.0), "write_bytes": w.get(k, 0.0),
+                         "bytes_per_launch": f.get(k, 0.0) + w.get(k, 0.0), "fetch_scale": ff, "write_scale": wf,
+                         "source_sha256_16": source_hash(k)} for k in sorted(set(f) | set(w))}
+    json.dump(out, open(PMC_FILE, "w"), indent=1, sort_keys=True)
+    print(json.dumps(out[workload], indent=1))
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -240,6 +302,9 @@ def cpu_baseline(w, inputs, budget_s):
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--pmc-summary":
+        pmc_summary(*sys.argv[2:5])
+        return
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -267,7 +332,7 @@ def main():
     dom = max(total_ms, key=total_ms.get)
     d = kern[dom]
     roof = dict(kernel=dom, bound="hbm", achieved=d["GBps"], peak=HBM_PEAK_GBPS, unit="GB/s",
-                frac=d["GBps"] / HBM_PEAK_GBPS, traffic=None, avg_us=d["avg_us"],
+                frac=d["GBps"] / HBM_PEAK_GBPS, traffic=pmc_traffic(w.name, dom), avg_us=d["avg_us"],
                 bytes_per_launch=d["bytes_per_launch"])
 
     R, Q, NL = w.rows_per_step, w.seqs, w.layers
