@@ -79,6 +79,7 @@ def _load():
         lib.orc_append.argtypes = [P, i64, P, P]
         lib.orc_flush.argtypes = [P]
         lib.orc_warm.argtypes = [P]
+        lib.orc_rollback.argtypes = [P, i64]
         lib.orc_decode_step.argtypes = [P, i32, P, P, P, P, P]
         for name in ("orc_get_state", "orc_get_scores", "orc_get_map", "orc_get_compact",
                      "orc_get_counters", "orc_get_pos_slot", "orc_get_slot_bytes"):
@@ -172,6 +173,9 @@ class OracleUnit:
     def warm(self):
         self._check("orc_warm", self._lib.orc_warm(self._h))
 
+    def rollback(self, n: int):
+        self._check("orc_rollback", self._lib.orc_rollback(self._h, n))
+
     def decode_step(self, index_q, index_w, q_lat, q_rope) -> np.ndarray:
         s = self.shape
         index_q = np.ascontiguousarray(index_q, dtype=np.uint16)
@@ -189,10 +193,10 @@ class OracleUnit:
 
     # ---------------------------------------------------------------- getters
     def state(self) -> dict:
-        st = np.zeros(6, dtype=np.int64)
+        st = np.zeros(7, dtype=np.int64)
         self._lib.orc_get_state(self._h, _ptr(st))
         return dict(L=int(st[0]), M=int(st[1]), round=int(st[2]), hand=int(st[3]),
-                    R=int(st[4]), U=int(st[5]))
+                    R=int(st[4]), U=int(st[5]), floor=int(st[6]))
 
     def scores(self) -> np.ndarray:
         st = self.state()

@@ -25,6 +25,7 @@ struct orc_unit {
   int64_t M;              /* rows in the mirror; [M, L) live in the ring */
   int64_t round;          /* decode steps done */
   int64_t hand;           /* replacement ring hand */
+  int64_t rb_floor;       /* lowest row count a rollback may return to */
   /* storage */
   float* keys;            /* [max_positions][index_dim], exact bf16 values */
   uint8_t* mirror;        /* offload: host mirror; resident: the row store */
@@ -184,6 +185,27 @@ int orc_flush(orc_unit* u) {
   return ORC_OK;
 }
 
+/* Rollback after a rejected verify (offload page, "Capacity must survive the
+ * session lifecycle": rejected drafts are rolled back, and the KV rows and the
+ * DSA selection state have to return to the accepted prefix).  The last n rows
+ * stop being part of the history: L becomes L-n and the mirror count M is cut
+ * to at most L-n; rows still in the ring simply become free ring entries.
+ * Offload mode allows this only down to `floor`, the mirror count when the
+ * latest decode round started (or L at the latest warm): rows at or above it
+ * were classified RING in every round that saw them, so no hot slot holds
+ * one and the slot table needs no change.  The round count, the hand and the
+ * slots are left as they are; fills made by the rejected round hold rows below
+ * the floor and stay valid. */
+int orc_rollback(orc_unit* u, int64_t n) {
+  if (n < 0) return ORC_E_INVALID;
+  if (n > u->L) return ORC_E_STATE;
+  const int64_t L2 = u->L - n;
+  if (u->c.mode == ORC_MODE_OFFLOAD && L2 < u->rb_floor) return ORC_E_STATE;
+  u->L = L2;
+  if (u->M > L2) u->M = L2;
+  return ORC_OK;
+}
+
 /* Warm start: the hot cache holds the most recent min(S, L) positions, slot v
  * holding the v-th of them in ascending order; no slot counts as filled or
  * pinned in any round >= 0; the hand points past the last filled slot. */
@@ -206,6 +228,7 @@ int orc_warm(orc_unit* u) {
     memcpy(u->slots + v * u->row_bytes, u->mirror + pos * u->row_bytes, (size_t)u->row_bytes);
   }
   u->hand = n % S;
+  u->rb_floor = u->L;
   return ORC_OK;
 }
 
@@ -331,6 +354,7 @@ int orc_decode_step(orc_unit* u, int32_t R, const uint16_t* index_q, const float
     return ORC_E_INVALID;
   if (u->L < R) return ORC_E_STATE;
   const int32_t r = (int32_t)u->round;
+  if (c->mode == ORC_MODE_OFFLOAD) u->rb_floor = u->M;
   u->last_R = R;
   memset(u->cnt, 0, sizeof(u->cnt));
 
@@ -439,9 +463,9 @@ int orc_decode_step(orc_unit* u, int32_t R, const uint16_t* index_q, const float
 
 /* ---------------------------------------------------------------- getters */
 
-void orc_get_state(const orc_unit* u, int64_t state[6]) {
+void orc_get_state(const orc_unit* u, int64_t state[7]) {
   state[0] = u->L; state[1] = u->M; state[2] = u->round; state[3] = u->hand;
-  state[4] = u->last_R; state[5] = u->n_union;
+  state[4] = u->last_R; state[5] = u->n_union; state[6] = u->rb_floor;
 }
 
 void orc_get_scores(const orc_unit* u, float* dst) {

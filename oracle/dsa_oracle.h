@@ -76,6 +76,10 @@ int orc_append(orc_unit* u, int64_t n, const uint16_t* keys, const uint8_t* rows
 int orc_flush(orc_unit* u);
 /* Offload mode: fill the hot cache with the most recent min(S, L) positions. */
 int orc_warm(orc_unit* u);
+/* Drop the last n rows (L -= n, M = min(M, L)).  Offload mode: ORC_E_STATE if
+ * L-n is below the mirror count at the start of the latest decode round (or L
+ * at the latest warm); ORC_E_STATE if n > L; ORC_E_INVALID if n < 0. */
+int orc_rollback(orc_unit* u, int64_t n);
 
 /* One decode step over the last R appended positions.
  * index_q: bf16 [R][index_heads][index_dim]; index_w: f32 [R][index_heads];
@@ -85,8 +89,8 @@ int orc_decode_step(orc_unit* u, int32_t R, const uint16_t* index_q, const float
                     const uint16_t* q_lat, const uint16_t* q_rope, float* out);
 
 /* ---- state and last-step getters (host buffers owned by the caller) ---- */
-/* state: L, M, round (steps done), hand, last R, union size */
-void orc_get_state(const orc_unit* u, int64_t state[6]);
+/* state: L, M, round (steps done), hand, last R, union size, rollback floor */
+void orc_get_state(const orc_unit* u, int64_t state[7]);
 /* scores of the last step, [R][L] f32 (positions a row cannot see hold 0) */
 void orc_get_scores(const orc_unit* u, float* dst);
 /* selections [R][K] i32 ascending (-1 padded); counts [R] */
