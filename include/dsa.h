@@ -157,6 +157,21 @@ dsa_status dsa_flush(dsa_session* s, int32_t layer, int32_t seq, hipStream_t str
  * else DSA_E_STATE.  Resident mode: no-op. */
 dsa_status dsa_warm_hot(dsa_session* s, int32_t layer, int32_t seq, hipStream_t stream);
 
+/* Drop the last n rows of unit (layer, seq): L becomes L-n and the mirror
+ * count M becomes min(M, L-n).  For a verify step whose drafts were rejected
+ * (offload page, section "Capacity must survive the session lifecycle": a
+ * rejected draft rolls back the KV rows and the DSA selection state).  Keys
+ * and rows past the new L are left in place and are overwritten by the next
+ * appends; the round count, the hand and the hot slots are unchanged.
+ * Offload mode: allowed only while L-n is at least the mirror count at the
+ * start of the unit's latest decode round (L at the latest dsa_warm_hot, 0
+ * before either), so that no hot slot can hold a dropped position; rows
+ * appended since the latest round started can always be dropped.
+ * Stream-ordered: one tiny kernel publishes the new L and M on `stream`.
+ * Errors (nothing changes): DSA_E_INVALID if n < 0; DSA_E_STATE if n > L or,
+ * offloaded, if L-n is below that bound.  n == 0 is a no-op. */
+dsa_status dsa_rollback_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t n, hipStream_t stream);
+
 /* One decode step of every sequence of `layer`, R = rows_per_seq query rows
  * each (1 <= R <= max_query_rows; every sequence must hold at least R rows).
  *   index_q:  device bf16 [n_seqs][R][index_heads][index_dim]

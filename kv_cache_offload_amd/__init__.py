@@ -32,7 +32,7 @@ COUNTER_NAMES = ("union", "hit", "ring", "miss", "miss_noslot", "evict", "host_b
 
 # every symbol include/dsa.h declares
 EXPORTS = ("dsa_session_create", "dsa_session_destroy", "dsa_append_rows", "dsa_flush",
-           "dsa_warm_hot", "dsa_decode_step", "dsa_unit_state", "dsa_mirror_rows",
+           "dsa_warm_hot", "dsa_rollback_rows", "dsa_decode_step", "dsa_unit_state", "dsa_mirror_rows",
            "dsa_last_error", "dsa_debug_size", "dsa_debug_get", "dsa_set_kernel_timing",
            "dsa_kernel_times")
 
@@ -64,7 +64,7 @@ def _load_library() -> ctypes.CDLL:
     # is loaded first and libdsa's dependency on that soname binds to it.
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built (run: python -m kv_cache_offload_amd.build); "
+        raise ImportError(f"{LIB_PATH} is not built (run: python kv_cache_offload_amd/build.py); "
                           "there is no fallback implementation")
     lib = ctypes.CDLL(LIB_PATH)
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -74,6 +74,7 @@ def _load_library() -> ctypes.CDLL:
         "dsa_append_rows": ([P, i32, i32, i64, P, P, P], ctypes.c_int),
         "dsa_flush": ([P, i32, i32, P], ctypes.c_int),
         "dsa_warm_hot": ([P, i32, i32, P], ctypes.c_int),
+        "dsa_rollback_rows": ([P, i32, i32, i64, P], ctypes.c_int),
         "dsa_decode_step": ([P, i32, i32, P, P, P, P, P, P], ctypes.c_int),
         "dsa_unit_state": ([P, i32, i32, ctypes.POINTER(i64)], ctypes.c_int),
         "dsa_mirror_rows": ([P, i32, i32, ctypes.POINTER(i64)], ctypes.c_int),
@@ -127,6 +128,10 @@ def dsa_flush(h, layer, seq, stream) -> int:
 
 def dsa_warm_hot(h, layer, seq, stream) -> int:
     return _lib.dsa_warm_hot(_handle(h), layer, seq, stream)
+
+
+def dsa_rollback_rows(h, layer, seq, n, stream) -> int:
+    return _lib.dsa_rollback_rows(_handle(h), layer, seq, n, stream)
 
 
 def dsa_decode_step(h, layer, rows_per_seq, index_q, index_w, q_latent, q_rope, out, stream) -> int:
@@ -230,6 +235,9 @@ class Session:
 
     def warm_hot(self, layer, seq):
         self._check("dsa_warm_hot", dsa_warm_hot(self.h, layer, seq, self._stream()))
+
+    def rollback_rows(self, layer, seq, n):
+        self._check("dsa_rollback_rows", dsa_rollback_rows(self.h, layer, seq, n, self._stream()))
 
     def decode_step(self, layer, index_q, index_w, q_latent, q_rope, out):
         R = index_q.shape[1]

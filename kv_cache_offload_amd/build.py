@@ -1,6 +1,6 @@
 """Build libdsa.so (HIP for gfx950) in-tree with hipcc.
 
-Usage: python -m kv_cache_offload_amd.build  (or call build()).
+Usage: python kv_cache_offload_amd/build.py  (or call build()).
 """
 from __future__ import annotations
 

@@ -172,6 +172,7 @@ hipError_t launch_append(const Geometry& g, const UnitDev& unit, int64_t L, int6
                          int64_t n, const uint16_t* keys, const uint8_t* rows, hipStream_t st);
 hipError_t launch_flush(const Geometry& g, const UnitDev& unit, int64_t M, int64_t L, hipStream_t st);
 hipError_t launch_warm(const Geometry& g, const UnitDev& unit, int64_t L, hipStream_t st);
+hipError_t launch_rollback(const UnitDev& unit, int64_t L, int64_t M, hipStream_t st);
 
 // One-time kernel attributes (dynamic LDS above 64 KiB).
 hipError_t prepare_score_kernels();

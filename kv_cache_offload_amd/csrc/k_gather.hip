@@ -243,6 +243,15 @@ __global__ __launch_bounds__(256) void warm_fill_kernel(UnitDev ud, int S, int64
   if (blockIdx.x == 0 && threadIdx.x == 0) *u.hand = (int32_t)(n % S);
 }
 
+// Rollback: publish the shortened row count and mirror count in stream order.
+__global__ __launch_bounds__(64) void rollback_kernel(UnitDev ud, int64_t L, int64_t M) {
+  const UnitG u = as_global(ud);
+  if (threadIdx.x == 0) {
+    u.dyn[0] = L;
+    u.dyn[1] = M;
+  }
+}
+
 unsigned grid_for(int64_t work, int64_t cap = 4096) {
   int64_t b = (work + 255) / 256;
   if (b < 1) b = 1;
@@ -289,6 +298,10 @@ hipError_t launch_warm(const Geometry& g, const UnitDev& unit, int64_t L, hipStr
   if (e != hipSuccess) return e;
   return launch_k(warm_fill_kernel, dim3(grid_for(n * kCopyChunks16 > g.hot_slots ? n * kCopyChunks16 : g.hot_slots)),
                   dim3(256), 0, st, unit, g.hot_slots, L, n, g.row_bytes);
+}
+
+hipError_t launch_rollback(const UnitDev& unit, int64_t L, int64_t M, hipStream_t st) {
+  return launch_k(rollback_kernel, dim3(1), dim3(64), 0, st, unit, L, M);
 }
 
 }  // namespace dsa

@@ -33,6 +33,7 @@ constexpr size_t kAlign = 256;
 
 struct UnitHost {
   int64_t L = 0, M = 0, round = 0;
+  int64_t floor = 0;             // lowest L a rollback may return to (offload)
   int64_t m_done = 0;            // mirror rows known complete
   int64_t m_event = 0;           // mirror rows covered by `ev`
   hipEvent_t ev = nullptr;
@@ -466,6 +467,29 @@ dsa_status dsa_warm_hot(dsa_session* s, int32_t layer, int32_t seq, hipStream_t 
   if (h.M != h.L) return fail(s, DSA_E_STATE, "warm needs a flushed unit (M == L)");
   DeviceGuard dg(s->device);
   HIPCHK(launch_warm(s->g, s->units[unit_index(s, layer, seq)], h.L, stream), "warm kernels");
+  h.floor = h.L;
+  return DSA_OK;
+}
+
+dsa_status dsa_rollback_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t n, hipStream_t stream) {
+  dsa_status st = entry(s);
+  if (st != DSA_OK) return st;
+  if ((st = check_unit(s, layer, seq)) != DSA_OK) return st;
+  if (n < 0) return fail(s, DSA_E_INVALID, "n < 0");
+  if (n == 0) return DSA_OK;
+  const size_t ui = unit_index(s, layer, seq);
+  UnitHost& h = s->uh[ui];
+  if (n > h.L) return fail(s, DSA_E_STATE, "rollback past the first row");
+  const int64_t L2 = h.L - n;
+  if (s->g.mode == DSA_KV_OFFLOAD && L2 < h.floor)
+    return fail(s, DSA_E_STATE, "rollback below the rows the latest round could cache");
+  const int64_t M2 = std::min(h.M, L2);
+  DeviceGuard dg(s->device);
+  HIPCHK(launch_rollback(s->units[ui], L2, M2, stream), "rollback kernel");
+  h.L = L2;
+  h.M = M2;
+  h.m_done = std::min(h.m_done, L2);
+  h.m_event = std::min(h.m_event, L2);
   return DSA_OK;
 }
 
@@ -511,6 +535,7 @@ dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq, 
   for (int q = 0; q < n_seqs; ++q) {
     UnitHost& h = s->uh[unit_index(s, layer, q)];
     h.round += 1;
+    h.floor = h.M;
     if (g.mode == DSA_KV_OFFLOAD && h.L - h.M >= g.ring_rows) {
       h.M += g.ring_rows;
       if ((st = note_mirror(s, h, stream)) != DSA_OK) return st;

@@ -12,8 +12,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _ensure_built():
     lib = os.path.join(ROOT, "kv_cache_offload_amd", "libdsa.so")
     if not os.path.exists(lib):
-        from kv_cache_offload_amd.build import build
-        build()
+        from __graft_entry__ import _build_module
+        _build_module().build()
     return lib
 
 
@@ -85,3 +85,4 @@ def test_abi_version_mismatch_and_nulls():
     assert K.dsa_last_error(None) == "NULL session"
     assert K._lib.dsa_append_rows(None, 0, 0, 1, None, None, None) == K.E_INVALID
     assert K._lib.dsa_decode_step(None, 0, 1, None, None, None, None, None, None) == K.E_INVALID
+    assert K._lib.dsa_rollback_rows(None, 0, 0, 1, None) == K.E_INVALID
