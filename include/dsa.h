@@ -148,6 +148,31 @@ dsa_status dsa_session_destroy(dsa_session* s);
 dsa_status dsa_append_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t n,
                            const void* index_keys, const void* rows, hipStream_t stream);
 
+/* Quantise n MLA rows to packed Q8G64 rows (offload page, section "Decision 2",
+ * first problem: the owner quantises a row once and moves the packed 656 B;
+ * section "Starting point" for the layout).  The pages give no scale rule;
+ * per group of 64 latent values x:
+ *   scale = max|x| / 127 in fp32, rounded to fp16 (nearest even; the largest
+ *           finite fp16 if it overflows);
+ *   code  = 0 if scale == 0, else clamp(rint(x / scale), -127, 127), with an
+ *           IEEE fp32 division and rint rounding half to even.
+ * RoPE values are stored unchanged.  Inputs must be finite.
+ *   latent: device, bf16 [n][latent_dim]  (latent_dim = 512)
+ *   rope:   device, bf16 [n][rope_dim]    (rope_dim = 64)
+ *   rows:   device (or pinned host), uint8 [n][row_bytes]  (written)
+ * All 16-byte aligned.  Stream-ordered; touches no unit.  DSA_E_INVALID on
+ * n < 0 or a NULL / misaligned pointer; n == 0 is a no-op. */
+dsa_status dsa_quantize_rows(dsa_session* s, int64_t n, const void* latent, const void* rope, void* rows,
+                             hipStream_t stream);
+
+/* dsa_append_rows with the rows given unquantised: the rows are quantised as
+ * dsa_quantize_rows does, straight into their place (ring, host mirror or
+ * row store), in one pass.  Same state changes and errors as dsa_append_rows.
+ *   index_keys: device bf16 [n][index_dim]; latent: device bf16 [n][512];
+ *   rope: device bf16 [n][64]; all 16-byte aligned. */
+dsa_status dsa_append_latent(dsa_session* s, int32_t layer, int32_t seq, int64_t n, const void* index_keys,
+                             const void* latent, const void* rope, hipStream_t stream);
+
 /* Write every pending ring row of the unit to the host mirror (M = L). */
 dsa_status dsa_flush(dsa_session* s, int32_t layer, int32_t seq, hipStream_t stream);
 

@@ -32,7 +32,8 @@ COUNTER_NAMES = ("union", "hit", "ring", "miss", "miss_noslot", "evict", "host_b
 
 # every symbol include/dsa.h declares
 EXPORTS = ("dsa_session_create", "dsa_session_destroy", "dsa_append_rows", "dsa_flush",
-           "dsa_warm_hot", "dsa_rollback_rows", "dsa_decode_step", "dsa_unit_state", "dsa_mirror_rows",
+           "dsa_warm_hot", "dsa_rollback_rows", "dsa_quantize_rows", "dsa_append_latent",
+           "dsa_decode_step", "dsa_unit_state", "dsa_mirror_rows",
            "dsa_last_error", "dsa_debug_size", "dsa_debug_get", "dsa_set_kernel_timing",
            "dsa_kernel_times")
 
@@ -75,6 +76,8 @@ def _load_library() -> ctypes.CDLL:
         "dsa_flush": ([P, i32, i32, P], ctypes.c_int),
         "dsa_warm_hot": ([P, i32, i32, P], ctypes.c_int),
         "dsa_rollback_rows": ([P, i32, i32, i64, P], ctypes.c_int),
+        "dsa_quantize_rows": ([P, i64, P, P, P, P], ctypes.c_int),
+        "dsa_append_latent": ([P, i32, i32, i64, P, P, P, P], ctypes.c_int),
         "dsa_decode_step": ([P, i32, i32, P, P, P, P, P, P], ctypes.c_int),
         "dsa_unit_state": ([P, i32, i32, ctypes.POINTER(i64)], ctypes.c_int),
         "dsa_mirror_rows": ([P, i32, i32, ctypes.POINTER(i64)], ctypes.c_int),
@@ -128,6 +131,14 @@ def dsa_flush(h, layer, seq, stream) -> int:
 
 def dsa_warm_hot(h, layer, seq, stream) -> int:
     return _lib.dsa_warm_hot(_handle(h), layer, seq, stream)
+
+
+def dsa_quantize_rows(h, n, latent_ptr, rope_ptr, rows_ptr, stream) -> int:
+    return _lib.dsa_quantize_rows(_handle(h), n, latent_ptr, rope_ptr, rows_ptr, stream)
+
+
+def dsa_append_latent(h, layer, seq, n, index_keys_ptr, latent_ptr, rope_ptr, stream) -> int:
+    return _lib.dsa_append_latent(_handle(h), layer, seq, n, index_keys_ptr, latent_ptr, rope_ptr, stream)
 
 
 def dsa_rollback_rows(h, layer, seq, n, stream) -> int:
@@ -235,6 +246,16 @@ class Session:
 
     def warm_hot(self, layer, seq):
         self._check("dsa_warm_hot", dsa_warm_hot(self.h, layer, seq, self._stream()))
+
+    def quantize_rows(self, latent, rope, rows):
+        n = latent.shape[0]
+        self._check("dsa_quantize_rows", dsa_quantize_rows(self.h, n, self._ptr(latent), self._ptr(rope),
+                                                           self._ptr(rows), self._stream()))
+
+    def append_latent(self, layer, seq, index_keys, latent, rope):
+        n = index_keys.shape[0]
+        self._check("dsa_append_latent", dsa_append_latent(self.h, layer, seq, n, self._ptr(index_keys),
+                                                           self._ptr(latent), self._ptr(rope), self._stream()))
 
     def rollback_rows(self, layer, seq, n):
         self._check("dsa_rollback_rows", dsa_rollback_rows(self.h, layer, seq, n, self._stream()))

@@ -173,6 +173,11 @@ hipError_t launch_append(const Geometry& g, const UnitDev& unit, int64_t L, int6
 hipError_t launch_flush(const Geometry& g, const UnitDev& unit, int64_t M, int64_t L, hipStream_t st);
 hipError_t launch_warm(const Geometry& g, const UnitDev& unit, int64_t L, hipStream_t st);
 hipError_t launch_rollback(const UnitDev& unit, int64_t L, int64_t M, hipStream_t st);
+// Quantise-on-append (k_quant.hip).
+hipError_t launch_quantize(const Geometry& g, int64_t n, const uint16_t* latent, const uint16_t* rope, uint8_t* out,
+                           hipStream_t st);
+hipError_t launch_append_latent(const Geometry& g, const UnitDev& unit, int64_t L, int64_t M, int64_t newM, int64_t n,
+                                const uint16_t* keys, const uint16_t* latent, const uint16_t* rope, hipStream_t st);
 
 // One-time kernel attributes (dynamic LDS above 64 KiB).
 hipError_t prepare_score_kernels();

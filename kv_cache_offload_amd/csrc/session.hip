@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 #include <vector>
 
@@ -416,15 +417,22 @@ dsa_status dsa_session_destroy(dsa_session* s) {
   return DSA_OK;
 }
 
-dsa_status dsa_append_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t n, const void* index_keys,
-                           const void* rows, hipStream_t stream) {
+extern "C++" {
+namespace {
+
+// Shared by both append calls: validation, the ring spill bound, the launch
+// (fn(newM) enqueues the kernels) and the host-side row counts.
+template <class F>
+dsa_status append_common(dsa_session* s, int32_t layer, int32_t seq, int64_t n, const void* index_keys,
+                         std::initializer_list<const void*> bufs, hipStream_t stream, F&& fn) {
   dsa_status st = entry(s);
   if (st != DSA_OK) return st;
   if ((st = check_unit(s, layer, seq)) != DSA_OK) return st;
   if (n < 0) return fail(s, DSA_E_INVALID, "n < 0");
   if (n == 0) return DSA_OK;
-  if (!index_keys || !rows || !aligned(index_keys, 16) || !aligned(rows, 16))
-    return fail(s, DSA_E_INVALID, "keys and rows must be non-NULL and 16-byte aligned");
+  if (!index_keys || !aligned(index_keys, 16)) return fail(s, DSA_E_INVALID, "keys must be non-NULL and 16-byte aligned");
+  for (const void* b : bufs)
+    if (!b || !aligned(b, 16)) return fail(s, DSA_E_INVALID, "row inputs must be non-NULL and 16-byte aligned");
   const size_t ui = unit_index(s, layer, seq);
   UnitHost& h = s->uh[ui];
   if (h.L + n > s->cfg.max_positions) return fail(s, DSA_E_CAPACITY, "append past max_positions");
@@ -432,15 +440,48 @@ dsa_status dsa_append_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t n
   int64_t newM = h.M;
   if (s->g.mode == DSA_KV_OFFLOAD)
     while (h.L + n - newM > s->g.ring_cap) newM += s->g.ring_rows;
-  if ((st = timed_launch(s, KK_APPEND, "append kernel", [&] {
-         return launch_append(s->g, s->units[ui], h.L, h.M, newM, n, static_cast<const uint16_t*>(index_keys),
-                              static_cast<const uint8_t*>(rows), stream);
-       })) != DSA_OK)
+  if ((st = timed_launch(s, KK_APPEND, "append kernel", [&] { return fn(s->units[ui], h, newM); })) != DSA_OK)
     return st;
   const bool moved = newM != h.M;
   h.L += n;
   h.M = s->g.mode == DSA_KV_OFFLOAD ? newM : h.L;
   if (moved && s->g.mode == DSA_KV_OFFLOAD) return note_mirror(s, h, stream);
+  return DSA_OK;
+}
+
+}  // namespace
+}  // extern "C++"
+
+dsa_status dsa_append_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t n, const void* index_keys,
+                           const void* rows, hipStream_t stream) {
+  return append_common(s, layer, seq, n, index_keys, {rows}, stream, [&](const UnitDev& u, const UnitHost& h, int64_t newM) {
+    return launch_append(s->g, u, h.L, h.M, newM, n, static_cast<const uint16_t*>(index_keys),
+                         static_cast<const uint8_t*>(rows), stream);
+  });
+}
+
+dsa_status dsa_append_latent(dsa_session* s, int32_t layer, int32_t seq, int64_t n, const void* index_keys,
+                             const void* latent, const void* rope, hipStream_t stream) {
+  return append_common(s, layer, seq, n, index_keys, {latent, rope}, stream,
+                       [&](const UnitDev& u, const UnitHost& h, int64_t newM) {
+                         return launch_append_latent(s->g, u, h.L, h.M, newM, n, static_cast<const uint16_t*>(index_keys),
+                                                     static_cast<const uint16_t*>(latent),
+                                                     static_cast<const uint16_t*>(rope), stream);
+                       });
+}
+
+dsa_status dsa_quantize_rows(dsa_session* s, int64_t n, const void* latent, const void* rope, void* rows,
+                             hipStream_t stream) {
+  dsa_status st = entry(s);
+  if (st != DSA_OK) return st;
+  if (n < 0) return fail(s, DSA_E_INVALID, "n < 0");
+  if (n == 0) return DSA_OK;
+  if (!latent || !rope || !rows || !aligned(latent, 16) || !aligned(rope, 16) || !aligned(rows, 16))
+    return fail(s, DSA_E_INVALID, "latent, rope and rows must be non-NULL and 16-byte aligned");
+  DeviceGuard dg(s->device);
+  HIPCHK(launch_quantize(s->g, n, static_cast<const uint16_t*>(latent), static_cast<const uint16_t*>(rope),
+                         static_cast<uint8_t*>(rows), stream),
+         "quantize kernel");
   return DSA_OK;
 }
 
