@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--calib-copy", action="store_true", help="also run a plain 2 GiB device copy (PMC scaling)")
+    p.add_argument("--quantize-rows", type=int, default=1 << 20,
+                   help="rows of the quantise-on-append measurement (0 skips it)")
     return p.parse_args()
 
 
@@ -114,6 +116,23 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def dev_tensor(a, device):
+    """numpy array -> device tensor with the same bytes (bf16 bit patterns travel as int16)."""
+    import torch
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def make_session(w, mode, n_layers=None):
+    import kv_cache_offload_amd as K
+    cfg = K.make_config(max_positions=w.max_positions, index_heads=w.index_heads, heads=w.heads,
+                        top_k=w.top_k, hot_slots=w.hot_slots, max_query_rows=w.rows_per_step,
+                        n_layers=w.layers if n_layers is None else n_layers, n_seqs=w.seqs,
+                        softmax_scale=w.softmax_scale, mode=mode)
+    return K.Session(cfg)
+
+
 def gen_inputs(w, n_steps):
     """Every step's appended rows and queries, per layer, stacked over sequences."""
     import dsa_synth as S
@@ -142,12 +161,8 @@ class Runner:
         import torch
         import dsa_synth as S
         import kv_cache_offload_amd as K
-        from tests.parity_util import dev_tensor
         self.K, self.torch, self.w = K, torch, w
-        cfg = K.make_config(max_positions=w.max_positions, index_heads=w.index_heads, heads=w.heads,
-                            top_k=w.top_k, hot_slots=w.hot_slots, max_query_rows=w.rows_per_step,
-                            n_layers=w.layers, n_seqs=w.seqs, softmax_scale=w.softmax_scale, mode=mode)
-        self.sess = K.Session(cfg)
+        self.sess = make_session(w, mode)
         dev = self.sess.device
         for l in range(w.layers):
             for q in range(w.seqs):
@@ -274,6 +289,34 @@ def run_mode(w, mode, inputs, args):
     return res
 
 
+def quantize_bench(n_rows, launches=50):
+    """dsa_quantize_rows over n_rows bf16 rows already in HBM: average launch time
+    from events around back-to-back launches on the launch stream."""
+    import torch
+    import dsa_synth as S
+    import kv_cache_offload_amd as K
+    sess = make_session(S.WORKLOADS["tiny"], K.KV_OFFLOAD)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    lat = torch.randn(n_rows, 512, device="cuda", dtype=torch.float32, generator=g).to(torch.bfloat16)
+    rope = torch.randn(n_rows, 64, device="cuda", dtype=torch.float32, generator=g).to(torch.bfloat16)
+    rows = torch.empty(n_rows, 656, dtype=torch.uint8, device="cuda")
+    for _ in range(10):
+        sess.quantize_rows(lat, rope, rows)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(launches):
+        sess.quantize_rows(lat, rope, rows)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / launches
+    sess.close()
+    nbytes = n_rows * (512 * 2 + 64 * 2 + 656)        # latent and RoPE read, packed row written
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"rows": n_rows, "us_per_launch": us, "bytes_per_launch": nbytes, "GBps": gbps,
+            "hbm_frac": gbps / HBM_PEAK_GBPS, "rows_per_s": n_rows / (us * 1e-6)}
+
+
 def cpu_baseline(w, inputs, budget_s):
     """The oracle as it stands, on the host cores, on the first decode steps of the same workload
     (its first unit: layer 0, sequence 0)."""
@@ -388,6 +431,9 @@ def main():
         line["resident"] = {"value": resd["steps_per_s"], "ms_per_step": 1e3 * resd["seconds"] / args.steps,
                             "kernels_us": {k: round(v["avg_us"], 2) for k, v in resd["kernels"].items()}}
         line["offload_slowdown"] = resd["steps_per_s"] / off["steps_per_s"] - 1.0
+    if args.quantize_rows > 0:
+        log(f"quantise-on-append over {args.quantize_rows} rows")
+        line["quantize"] = quantize_bench(args.quantize_rows)
     if not args.no_cpu and NL == 1 and Q == 1:
         log("timing the oracle on the host")
         line["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_seconds)
