@@ -28,6 +28,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 OK, E_INVALID, E_NOMEM, E_CAPACITY, E_STATE = 0, 1, 2, 3, 4
 MODE_OFFLOAD, MODE_RESIDENT = 0, 1
+REPL_RING, REPL_CLOCK = 0, 1
 SRC_HIT, SRC_RING, SRC_MISS, SRC_MISS_NOSLOT, SRC_RES = 0, 1, 2, 3, 4
 CNT_NAMES = ("union", "hit", "ring", "miss", "miss_noslot", "evict", "host_bytes", "res")
 
@@ -59,6 +60,7 @@ class _Config(ctypes.Structure):
         ("max_query_rows", ctypes.c_int32),
         ("mode", ctypes.c_int32),
         ("softmax_scale", ctypes.c_double),
+        ("replacement", ctypes.c_int32),
     ]
 
 
@@ -82,7 +84,7 @@ def _load():
         lib.orc_rollback.argtypes = [P, i64]
         lib.orc_decode_step.argtypes = [P, i32, P, P, P, P, P]
         for name in ("orc_get_state", "orc_get_scores", "orc_get_map", "orc_get_compact",
-                     "orc_get_counters", "orc_get_pos_slot", "orc_get_slot_bytes"):
+                     "orc_get_counters", "orc_get_pos_slot", "orc_get_slot_bytes", "orc_get_ref"):
             getattr(lib, name).argtypes = [P, P]
         lib.orc_get_selection.argtypes = [P, P, P]
         lib.orc_get_union.argtypes = [P, P, P, P]
@@ -120,6 +122,7 @@ class UnitShape:
     ring_rows: int = 64
     mode: int = MODE_OFFLOAD
     softmax_scale: float | None = None
+    replacement: int = REPL_RING
 
     @property
     def row_bytes(self) -> int:
@@ -137,7 +140,7 @@ class OracleUnit:
         cfg = _Config(shape.max_positions, shape.index_heads, shape.index_dim, shape.heads,
                       shape.latent_dim, shape.rope_dim, shape.group, shape.top_k,
                       shape.hot_slots, shape.ring_rows, shape.max_query_rows, shape.mode,
-                      float(scale))
+                      float(scale), shape.replacement)
         st = ctypes.c_int(0)
         h = lib.orc_create(ctypes.byref(cfg), ctypes.byref(st))
         if not h:
@@ -247,6 +250,11 @@ class OracleUnit:
     def pos_slot(self) -> np.ndarray:
         out = np.empty(self.state()["L"], dtype=np.int32)
         self._lib.orc_get_pos_slot(self._h, _ptr(out))
+        return out
+
+    def ref(self) -> np.ndarray:
+        out = np.zeros(self.shape.hot_slots if self.shape.mode == MODE_OFFLOAD else 0, dtype=np.uint8)
+        self._lib.orc_get_ref(self._h, _ptr(out))
         return out
 
     def slot_bytes(self) -> np.ndarray:

@@ -34,6 +34,7 @@ struct orc_unit {
   int32_t* slot_pos;      /* [S], -1 = empty */
   int32_t* fill_round;    /* [S] */
   int32_t* pin_round;     /* [S] */
+  uint8_t* ref;           /* [S] reference bits (CLOCK) */
   int32_t* pos_slot;      /* [max_positions], -1 = not cached */
   /* last step */
   int32_t last_R;
@@ -90,7 +91,8 @@ orc_unit* orc_create(const orc_config* cfg, int* status) {
       c->latent_dim <= 0 || c->rope_dim < 0 || c->group <= 0 || c->latent_dim % c->group ||
       c->top_k <= 0 || c->ring_rows <= 0 || c->max_query_rows <= 0 ||
       (c->mode != ORC_MODE_OFFLOAD && c->mode != ORC_MODE_RESIDENT) ||
-      (c->mode == ORC_MODE_OFFLOAD && c->hot_slots <= 0))
+      (c->mode == ORC_MODE_OFFLOAD && c->hot_slots <= 0) ||
+      (c->replacement != ORC_REPL_RING && c->replacement != ORC_REPL_CLOCK))
     return NULL;
   orc_unit* u = (orc_unit*)calloc(1, sizeof(orc_unit));
   if (!u) { *status = ORC_E_NOMEM; return NULL; }
@@ -108,6 +110,7 @@ orc_unit* orc_create(const orc_config* cfg, int* status) {
   u->slot_pos = (int32_t*)malloc((size_t)(S ? S : 1) * sizeof(int32_t));
   u->fill_round = (int32_t*)malloc((size_t)(S ? S : 1) * sizeof(int32_t));
   u->pin_round = (int32_t*)malloc((size_t)(S ? S : 1) * sizeof(int32_t));
+  u->ref = (uint8_t*)calloc((size_t)(S ? S : 1), 1);
   u->pos_slot = (int32_t*)malloc((size_t)P * sizeof(int32_t));
   u->scores = (float*)calloc((size_t)(c->max_query_rows * P), sizeof(float));
   u->sel = (int32_t*)malloc((size_t)RK * sizeof(int32_t));
@@ -118,7 +121,7 @@ orc_unit* orc_create(const orc_config* cfg, int* status) {
   u->map = (int32_t*)malloc((size_t)RK * sizeof(int32_t));
   u->compact = (uint8_t*)malloc((size_t)(RK * u->row_bytes));
   if (!u->keys || !u->mirror || !u->ring || !u->slots || !u->slot_pos || !u->fill_round ||
-      !u->pin_round || !u->pos_slot || !u->scores || !u->sel || !u->sel_n || !u->uni ||
+      !u->pin_round || !u->ref || !u->pos_slot || !u->scores || !u->sel || !u->sel_n || !u->uni ||
       !u->kind || !u->src || !u->map || !u->compact) {
     orc_destroy(u);
     *status = ORC_E_NOMEM;
@@ -134,7 +137,7 @@ orc_unit* orc_create(const orc_config* cfg, int* status) {
 void orc_destroy(orc_unit* u) {
   if (!u) return;
   free(u->keys); free(u->mirror); free(u->ring); free(u->slots); free(u->slot_pos);
-  free(u->fill_round); free(u->pin_round); free(u->pos_slot); free(u->scores); free(u->sel);
+  free(u->fill_round); free(u->pin_round); free(u->ref); free(u->pos_slot); free(u->scores); free(u->sel);
   free(u->sel_n); free(u->uni); free(u->kind); free(u->src); free(u->map); free(u->compact);
   free(u);
 }
@@ -208,7 +211,10 @@ int orc_rollback(orc_unit* u, int64_t n) {
 
 /* Warm start: the hot cache holds the most recent min(S, L) positions, slot v
  * holding the v-th of them in ascending order; no slot counts as filled or
- * pinned in any round >= 0; the hand points past the last filled slot. */
+ * pinned in any round >= 0; the hand points past the last filled slot.  Under
+ * CLOCK every filled slot starts with its reference bit set (a freshly loaded
+ * entry counts as referenced), which is the full-cache, all-bits-set state of
+ * the page's replacement probe. */
 int orc_warm(orc_unit* u) {
   const orc_config* c = &u->c;
   if (c->mode == ORC_MODE_RESIDENT) return ORC_OK;
@@ -219,11 +225,13 @@ int orc_warm(orc_unit* u) {
     u->slot_pos[v] = -1;
     u->fill_round[v] = -1;
     u->pin_round[v] = -1;
+    u->ref[v] = 0;
   }
   int64_t n = u->L < S ? u->L : S;
   for (int64_t v = 0; v < n; v++) {
     int64_t pos = u->L - n + v;
     u->slot_pos[v] = (int32_t)pos;
+    u->ref[v] = c->replacement == ORC_REPL_CLOCK;
     u->pos_slot[pos] = (int32_t)v;
     memcpy(u->slots + v * u->row_bytes, u->mirror + pos * u->row_bytes, (size_t)u->row_bytes);
   }
@@ -410,25 +418,45 @@ int orc_decode_step(orc_unit* u, int32_t R, const uint16_t* index_q, const float
       else if (v >= 0 && u->fill_round[v] < r) { u->kind[x] = ORC_SRC_HIT; u->src[x] = v; }
       else { u->kind[x] = ORC_SRC_MISS; u->src[x] = pos; }
     }
-    /* 6. Pin every slot this round reads. */
+    /* 6. Pin every slot this round reads (CLOCK: and mark it referenced). */
+    const int clock = c->replacement == ORC_REPL_CLOCK;
     for (int32_t x = 0; x < U; x++)
-      if (u->kind[x] == ORC_SRC_HIT) u->pin_round[u->src[x]] = r;
-    /* 7. Replacement: misses, in ascending position order, take the next slots
-     *    in ring order from the hand that are not pinned this round; the walk
-     *    visits each slot at most once.  A miss that finds no slot is read from
-     *    host memory without being cached.  Every miss's bytes come from the
-     *    host mirror in this round, never from the slot just filled. */
+      if (u->kind[x] == ORC_SRC_HIT) {
+        u->pin_round[u->src[x]] = r;
+        if (clock) u->ref[u->src[x]] = 1;
+      }
+    /* 7. Replacement: misses, in ascending position order, take slots found by
+     *    a hand that walks the slots in ring order and never takes a slot
+     *    pinned this round.  A miss that finds no slot is read from host memory
+     *    without being cached.  Every miss's bytes come from the host mirror in
+     *    this round, never from the slot just filled.
+     *    Ring policy: the next unpinned slot; the walk visits each slot at most
+     *    once per round.
+     *    CLOCK policy (second chance): an unpinned slot whose reference bit is
+     *    set loses the bit and is passed over; one whose bit is clear is taken
+     *    (and, being filled, is marked referenced); the walk visits each slot at
+     *    most twice per round.  With every bit set and few misses, the hand
+     *    clears a whole lap before it takes anything: the long sweep the page
+     *    measured. */
+    const int64_t max_visits = clock ? 2 * S : S;
     int64_t walk = u->hand, visited = 0, last = -1;
     for (int32_t x = 0; x < U; x++) {
       if (u->kind[x] != ORC_SRC_MISS) continue;
-      while (visited < S && u->pin_round[walk] == r) { walk = (walk + 1) % S; visited++; }
-      if (visited >= S) { u->kind[x] = ORC_SRC_MISS_NOSLOT; continue; }
+      int found = 0;
+      while (visited < max_visits) {
+        if (u->pin_round[walk] == r) { walk = (walk + 1) % S; visited++; continue; }
+        if (clock && u->ref[walk]) { u->ref[walk] = 0; walk = (walk + 1) % S; visited++; continue; }
+        found = 1;
+        break;
+      }
+      if (!found) { u->kind[x] = ORC_SRC_MISS_NOSLOT; continue; }
       int32_t v = (int32_t)walk, pos = u->uni[x];
       if (u->slot_pos[v] >= 0) { u->pos_slot[u->slot_pos[v]] = -1; u->cnt[ORC_CNT_EVICT]++; }
       u->slot_pos[v] = pos;
       u->pos_slot[pos] = v;
       u->fill_round[v] = r;
       u->pin_round[v] = r;
+      if (clock) u->ref[v] = 1;
       memcpy(u->slots + (int64_t)v * rb, u->mirror + (int64_t)pos * rb, (size_t)rb);
       last = v;
       walk = (walk + 1) % S;
@@ -499,6 +527,10 @@ void orc_get_slots(const orc_unit* u, int32_t* slot_pos, int32_t* fill_round, in
   memcpy(slot_pos, u->slot_pos, (size_t)S * sizeof(int32_t));
   memcpy(fill_round, u->fill_round, (size_t)S * sizeof(int32_t));
   memcpy(pin_round, u->pin_round, (size_t)S * sizeof(int32_t));
+}
+
+void orc_get_ref(const orc_unit* u, uint8_t* ref) {
+  if (u->c.mode == ORC_MODE_OFFLOAD) memcpy(ref, u->ref, (size_t)u->c.hot_slots);
 }
 
 void orc_get_pos_slot(const orc_unit* u, int32_t* pos_slot) {

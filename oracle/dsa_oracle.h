@@ -39,6 +39,10 @@ extern "C" {
 
 enum { ORC_OK = 0, ORC_E_INVALID = 1, ORC_E_NOMEM = 2, ORC_E_CAPACITY = 3, ORC_E_STATE = 4 };
 enum { ORC_MODE_OFFLOAD = 0, ORC_MODE_RESIDENT = 1 };
+/* Replacement policy of the hot cache: the ring walk that skips pinned slots,
+ * or CLOCK with reference bits (offload page, "GPU cache management errs too",
+ * replacement paragraph: the earlier policy, kept as a variant). */
+enum { ORC_REPL_RING = 0, ORC_REPL_CLOCK = 1 };
 /* Where a selected row's bytes come from in one round. */
 enum { ORC_SRC_HIT = 0, ORC_SRC_RING = 1, ORC_SRC_MISS = 2, ORC_SRC_MISS_NOSLOT = 3, ORC_SRC_RES = 4 };
 /* Per-step counters, in this order. */
@@ -61,6 +65,7 @@ typedef struct {
   int32_t max_query_rows;  /* R_max */
   int32_t mode;            /* ORC_MODE_* */
   double softmax_scale;    /* 1/sqrt(latent_dim + rope_dim) */
+  int32_t replacement;     /* ORC_REPL_* (offload mode) */
 } orc_config;
 
 typedef struct orc_unit orc_unit;
@@ -105,6 +110,8 @@ void orc_get_counters(const orc_unit* u, int64_t cnt[ORC_CNT__N]);
 /* slot table: slot_pos, fill_round, pin_round [S]; pos_slot [L] */
 void orc_get_slots(const orc_unit* u, int32_t* slot_pos, int32_t* fill_round, int32_t* pin_round);
 void orc_get_pos_slot(const orc_unit* u, int32_t* pos_slot);
+/* reference bits [S] (0 or 1; CLOCK only, all 0 for the ring policy) */
+void orc_get_ref(const orc_unit* u, uint8_t* ref);
 /* hot slot bytes [S][row_bytes] */
 void orc_get_slot_bytes(const orc_unit* u, uint8_t* dst);
 /* mirror rows [first, first+n) (offload) or row store (resident) */

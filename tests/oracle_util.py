@@ -6,11 +6,12 @@ from oracle import MODE_OFFLOAD, OracleUnit, UnitShape
 
 
 def unit(max_positions, index_heads=1, index_dim=16, heads=1, top_k=2, hot_slots=4,
-         max_query_rows=2, ring_rows=64, mode=MODE_OFFLOAD, softmax_scale=None):
+         max_query_rows=2, ring_rows=64, mode=MODE_OFFLOAD, softmax_scale=None, replacement=0):
     return OracleUnit(UnitShape(max_positions=max_positions, index_heads=index_heads,
                                 index_dim=index_dim, heads=heads, top_k=top_k,
                                 hot_slots=hot_slots, max_query_rows=max_query_rows,
-                                ring_rows=ring_rows, mode=mode, softmax_scale=softmax_scale))
+                                ring_rows=ring_rows, mode=mode, softmax_scale=softmax_scale,
+                                replacement=replacement))
 
 
 def random_rows(n, seed, row_bytes=656):
