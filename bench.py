@@ -45,6 +45,11 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--calib-copy", action="store_true", help="also run a plain 2 GiB device copy (PMC scaling)")
+    p.add_argument("--replacement", choices=("ring", "clock"), default="ring",
+                   help="hot-cache replacement policy of the offloaded run")
+    p.add_argument("--replacement-probe", action="store_true",
+                   help="instead of the throughput run: time the first decode step after a warm start (full "
+                        "cache, every reference bit set) and the steps after it, under both policies")
     p.add_argument("--quantize-rows", type=int, default=1 << 20,
                    help="rows of the quantise-on-append measurement (0 skips it)")
     return p.parse_args()
@@ -124,12 +129,12 @@ def dev_tensor(a, device):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def make_session(w, mode, n_layers=None):
+def make_session(w, mode, n_layers=None, replacement=0):
     import kv_cache_offload_amd as K
     cfg = K.make_config(max_positions=w.max_positions, index_heads=w.index_heads, heads=w.heads,
                         top_k=w.top_k, hot_slots=w.hot_slots, max_query_rows=w.rows_per_step,
                         n_layers=w.layers if n_layers is None else n_layers, n_seqs=w.seqs,
-                        softmax_scale=w.softmax_scale, mode=mode)
+                        softmax_scale=w.softmax_scale, mode=mode, replacement=replacement)
     return K.Session(cfg)
 
 
@@ -157,12 +162,12 @@ class Runner:
     in order: append R rows to each sequence, then one decode step of the layer
     (all sequences together)."""
 
-    def __init__(self, w, mode, host_inputs):
+    def __init__(self, w, mode, host_inputs, replacement=0):
         import torch
         import dsa_synth as S
         import kv_cache_offload_amd as K
         self.K, self.torch, self.w = K, torch, w
-        self.sess = make_session(w, mode)
+        self.sess = make_session(w, mode, replacement=replacement)
         dev = self.sess.device
         for l in range(w.layers):
             for q in range(w.seqs):
@@ -260,7 +265,7 @@ def algorithmic_bytes(w, kind, n_steps, L0, cnt, long_hist):
 def run_mode(w, mode, inputs, args):
     import kv_cache_offload_amd as K
     name = "offload" if mode == K.KV_OFFLOAD else "resident"
-    r = Runner(w, mode, inputs)
+    r = Runner(w, mode, inputs, replacement=K.REPL_CLOCK if args.replacement == "clock" else K.REPL_RING)
     log(f"{name}: history loaded (L={r.L()}), warmup {args.warmup}")
     r.steps(args.warmup)
     c_before = r.totals()
@@ -287,6 +292,35 @@ def run_mode(w, mode, inputs, args):
         v["GBps"] = v["bytes_per_launch"] / (v["avg_us"] * 1e-6) / 1e9 if v["avg_us"] > 0 else 0.0
     r.sess.close()
     return res
+
+
+def replacement_probe(w, inputs, args):
+    """The replacement A/B of the offload page ("GPU cache management errs too"):
+    with a full cache and every reference bit set (a warm start), the first
+    decode step of each layer makes CLOCK's hand clear a whole lap before it
+    takes a slot; the ring walk takes the next unpinned slot.  Per policy: the
+    kernels of that first step (every layer once) and of the steady steps after
+    it, from the library's dispatch events."""
+    import kv_cache_offload_amd as K
+    out = {}
+    for name, pol in (("ring", K.REPL_RING), ("clock", K.REPL_CLOCK)):
+        r = Runner(w, K.KV_OFFLOAD, inputs, replacement=pol)
+        log(f"replacement probe, {name}: history loaded and warmed")
+        res = {}
+        for phase, n in (("first_step_after_warm", 1), ("steady", args.steps)):
+            r.sess.set_kernel_timing(True, reserve_steps=n * w.layers)
+            c0 = r.totals()
+            dt = timed(r, n)
+            kt = r.sess.kernel_times()
+            r.sess.set_kernel_timing(False)
+            c = (r.totals() - c0).tolist()
+            res[phase] = {"steps": n, "layer_steps": n * w.layers, "ms_per_step_with_events": dt * 1e3 / n,
+                          "kernels_us": {k: round(m / cnt * 1e3, 2) for k, (cnt, m) in kt.items() if cnt},
+                          "misses_per_layer_step": (c[3] + c[4]) / (n * w.layers),
+                          "evictions_per_layer_step": c[5] / (n * w.layers)}
+        r.sess.close()
+        out[name] = res
+    return out
 
 
 def quantize_bench(n_rows, launches=50):
@@ -366,6 +400,10 @@ def main():
     inputs = gen_inputs(w, n_steps)
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
 
+    if args.replacement_probe:
+        probe = replacement_probe(w, inputs, args)
+        print(json.dumps({"workload": w.name, "replacement_probe": probe}), flush=True)
+        return
     off = run_mode(w, K.KV_OFFLOAD, inputs, args)
     resd = None if args.no_resident else run_mode(w, K.KV_HBM_RESIDENT, inputs, args)
 
@@ -408,7 +446,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "layers": NL, "sequences": Q, "history": w.history, "query_rows": R,
                    "top_k": w.top_k, "hot_slots": w.hot_slots, "index_heads": w.index_heads, "heads": w.heads,
-                   "row_bytes": rb, "mode": "offload", "L_at_timed_start": off["L_start"]},
+                   "row_bytes": rb, "mode": "offload", "replacement": args.replacement,
+                   "L_at_timed_start": off["L_start"]},
         "query_rows_per_s": off["steps_per_s"] * R * Q,
         "roofline": roof,
         "score_select": {"us_per_step": ss_us, "hbm_bytes_per_step": ss_bytes,

@@ -90,7 +90,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 2u
+#define DSA_ABI_VERSION 3u
 
 typedef enum {
   DSA_OK = 0,
@@ -106,6 +106,24 @@ typedef enum {
   DSA_KV_OFFLOAD = 0,       /* rows in a pinned host mirror behind an HBM hot cache */
   DSA_KV_HBM_RESIDENT = 1   /* every row in HBM; same scoring, selection and attention */
 } dsa_kv_mode;
+
+/* Replacement policy of the hot cache (offload mode).  Both never take a slot
+ * pinned this round; they differ in which unpinned slot a miss takes.
+ *   DSA_REPL_RING:  the next unpinned slot in ring order from the hand; the
+ *                   hand visits each slot at most once per round (offload
+ *                   page, section "GPU cache management errs too", the policy
+ *                   the page settled on).
+ *   DSA_REPL_CLOCK: second chance with one reference bit per slot (the
+ *                   policy it replaced): in ring order from the hand, an
+ *                   unpinned slot with its bit set loses the bit and is passed
+ *                   over, one with the bit clear is taken; hits, fills and warm
+ *                   fills set the bit; at most two laps per round.  With a full
+ *                   cache, every bit set and few misses the hand clears a whole
+ *                   lap before it takes a slot (the page's replacement probe). */
+typedef enum {
+  DSA_REPL_RING = 0,
+  DSA_REPL_CLOCK = 1
+} dsa_replacement;
 
 typedef struct {
   uint32_t abi_version;    /* DSA_ABI_VERSION */
@@ -125,6 +143,7 @@ typedef struct {
   int32_t max_query_rows;  /* R_max; R_max * K <= 16384 */
   float softmax_scale;     /* 1/sqrt(latent_dim + rope_dim) */
   int32_t mode;            /* dsa_kv_mode */
+  int32_t replacement;     /* dsa_replacement (offload mode; ignored when resident) */
 } dsa_config;
 
 typedef struct dsa_session dsa_session;
@@ -245,7 +264,8 @@ typedef enum {
   DSA_DBG_SLOT_BYTES = 14, /* u8  [S][row_bytes] */
   DSA_DBG_MIRROR = 15,     /* u8  [M][row_bytes] host mirror (resident: row store [L]) */
   DSA_DBG_KEYS = 16,       /* bf16 [L][index_dim] */
-  DSA_DBG_TOTALS = 17      /* i64 [8]  the counters above summed over every step of the unit */
+  DSA_DBG_TOTALS = 17,     /* i64 [8]  the counters above summed over every step of the unit */
+  DSA_DBG_REF_BITS = 18    /* u32 [ceil(S/32)] reference bits, slot v = bit v%32 of word v/32 (CLOCK; 0 otherwise) */
 } dsa_debug_item;
 
 dsa_status dsa_debug_size(const dsa_session* s, int32_t layer, int32_t seq, int32_t item,

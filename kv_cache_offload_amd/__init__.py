@@ -17,17 +17,18 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdsa.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 OK, E_INVALID, E_NOMEM, E_CAPACITY, E_UNSUPPORTED, E_STATE, E_HIP = range(7)
 STATUS_NAMES = {0: "DSA_OK", 1: "DSA_E_INVALID", 2: "DSA_E_NOMEM", 3: "DSA_E_CAPACITY",
                 4: "DSA_E_UNSUPPORTED", 5: "DSA_E_STATE", 6: "DSA_E_HIP"}
 KV_OFFLOAD, KV_HBM_RESIDENT = 0, 1
+REPL_RING, REPL_CLOCK = 0, 1
 KERNEL_KINDS = ("index_score", "topk_collect", "topk_resolve", "gather", "attention", "attention_merge", "append")
 
 # inspection items (dsa_debug_item)
 DBG = dict(scores=0, selection=1, sel_count=2, union=3, union_kind=4, union_src=5, map=6,
            compact=7, counters=8, slot_pos=9, fill_round=10, pin_round=11, pos_slot=12, hand=13,
-           slot_bytes=14, mirror=15, keys=16, totals=17)
+           slot_bytes=14, mirror=15, keys=16, totals=17, ref_bits=18)
 COUNTER_NAMES = ("union", "hit", "ring", "miss", "miss_noslot", "evict", "host_bytes", "res")
 
 # every symbol include/dsa.h declares
@@ -57,6 +58,7 @@ class dsa_config(ctypes.Structure):
         ("max_query_rows", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
         ("mode", ctypes.c_int32),
+        ("replacement", ctypes.c_int32),
     ]
 
 
@@ -192,12 +194,13 @@ def dsa_kernel_times(h):
 
 def make_config(*, max_positions, index_heads, heads, top_k, hot_slots, max_query_rows,
                 n_layers=1, n_seqs=1, index_dim=128, latent_dim=512, rope_dim=64, group=64,
-                ring_rows=64, softmax_scale=None, mode=KV_OFFLOAD, device=0) -> dsa_config:
+                ring_rows=64, softmax_scale=None, mode=KV_OFFLOAD, device=0,
+                replacement=REPL_RING) -> dsa_config:
     if softmax_scale is None:
         softmax_scale = 1.0 / float((latent_dim + rope_dim) ** 0.5)
     return dsa_config(ABI_VERSION, device, n_layers, n_seqs, max_positions, index_heads, index_dim,
                       heads, latent_dim, rope_dim, group, top_k, hot_slots, ring_rows,
-                      max_query_rows, softmax_scale, mode)
+                      max_query_rows, softmax_scale, mode, replacement)
 
 
 class Session:

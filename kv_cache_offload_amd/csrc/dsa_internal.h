@@ -49,6 +49,7 @@ struct UnitT {
   P<int32_t> slot_pos;     // [S]      -1 = empty
   P<int32_t> fill_round;   // [S]
   P<int32_t> pin_round;    // [S]
+  P<uint32_t> ref;         // [ceil(S/32)] reference bits (CLOCK replacement)
   P<int32_t> hand;         // [1]
   P<int64_t> dyn;          // [4] L, M, round, reserved -- updated only by kernels, in stream order
   P<int64_t> totals;       // [8] step counters summed over every decode step of the unit
@@ -95,6 +96,7 @@ enum { kInfoUnion = 0, kInfoWriteback = 1, kInfoAssigned = 2, kInfoRound = 3, kI
 struct Geometry {
   int index_heads, index_dim, heads, latent, rope, group, top_k, hot_slots;
   int ring_rows, ring_cap, r_max, row_bytes, mode;
+  bool clock;             // CLOCK replacement (offload mode)
   int64_t max_positions, p_pad;
   int s_words;            // ceil(hot_slots / 32)
   int n_chunks;           // top-k chunks per row at max_positions

@@ -25,6 +25,7 @@ constexpr int kPlanWaves = kPlanThreads / 64;
 
 struct PlanParams {
   int S, s_words, ring_rows, mode;
+  int clock;          // CLOCK replacement (second chance with reference bits)
 };
 
 // Bits of word w (positions 32w..32w+31) that lie at or above M.
@@ -52,6 +53,7 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
                                          const PlanState& ps, uint32_t* lds) {
   __shared__ uint32_t sh[4 * kPlanWaves];
   __shared__ int s_last_v, s_assigned_last_v;
+  __shared__ int64_t s_end_o;                          // offset (lap * S + o) of the last victim
   __shared__ uint32_t s_evict;
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t L = ps.L, M = ps.M;
@@ -189,71 +191,101 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
     });
   }
 
-  // Victims: slots in ring order from the hand, skipping the pinned ones -- a
-  // slot is pinned this round iff the position it holds is selected (it is then
-  // a hit).  Passes of kWalkWords * 32 ring offsets until every miss has a slot
-  // or every slot has been seen; the k-th miss in ascending position order takes
-  // the k-th unpinned slot.  victim[k] = (slot, the position it gives up).
+  // Victims: slots in ring order from the hand, never a pinned one -- a slot is
+  // pinned this round iff the position it holds is selected (it is then a hit).
+  // Ring policy: every unpinned slot is a candidate; one lap.  CLOCK (second
+  // chance): on the first lap the unpinned slots whose reference bit was clear
+  // at round start, on the second lap the unpinned slots whose bit was set (the
+  // first lap cleared them and took every other unpinned slot).  Passes of
+  // kWalkWords * 32 ring offsets until every miss has a slot or the laps are
+  // done; the k-th miss in ascending position order takes the k-th candidate.
+  // victim[k] = (slot, the position it gives up).
   uint32_t n_assigned = 0;
   if (tid == 0) {
     s_last_v = -1;
     s_assigned_last_v = -1;
+    s_end_o = 2 * (int64_t)S;
     s_evict = 0;
   }
   if (off && n_miss > 0) {
-    uint32_t* cnt_w = lds;                             // [kWalkWords] unpinned offsets per word, then their scan
-    uint32_t cum = 0;                                  // unpinned slots found in earlier passes
+    uint32_t* cnt_w = lds;                             // [kWalkWords] candidates per word, then their scan
+    uint32_t cum = 0;                                  // candidates found in earlier passes
     const int half = tid >> 5, bit = tid & 31;
-    for (int64_t o0 = 0; o0 < S && cum < n_miss; o0 += (int64_t)kWalkWords * 32) {
-      int32_t held[kWalkPer], slot[kWalkPer];
+    const int laps = pp.clock ? 2 : 1;
+    for (int lap = 0; lap < laps && cum < n_miss; ++lap) {
+      for (int64_t o0 = 0; o0 < S && cum < n_miss; o0 += (int64_t)kWalkWords * 32) {
+        int32_t held[kWalkPer], slot[kWalkPer];
+        uint32_t refw[kWalkPer];
 #pragma unroll
-      for (int e = 0; e < kWalkPer; ++e) {             // offset o0 + 32 (half + 32 e) + bit
-        const int64_t o = o0 + 32 * (half + 32 * e) + bit;
-        slot[e] = o < S ? (int32_t)((hand + o) % S) : -1;
-        held[e] = u.slot_pos[slot[e] >= 0 ? slot[e] : 0];
-      }
-      uint32_t pin_word[kWalkPer];
-#pragma unroll
-      for (int e = 0; e < kWalkPer; ++e) {
-        const int32_t p = held[e];
-        pin_word[e] = (slot[e] >= 0 && p >= 0 && p < L) ? sel[p >> 5] : 0u;
-      }
-      uint32_t ub[kWalkPer];
-#pragma unroll
-      for (int e = 0; e < kWalkPer; ++e) {
-        const int32_t p = held[e];
-        const bool pinned = slot[e] >= 0 && p >= 0 && p < L && ((pin_word[e] >> (p & 31)) & 1u);
-        const bool unpinned = slot[e] >= 0 && !pinned;
-        ub[e] = (uint32_t)(__ballot(unpinned) >> (tid & 32));   // this half-wave's word
-        if (bit == 0) cnt_w[half + 32 * e] = __popc(ub[e]);
-      }
-      __syncthreads();
-      if (tid < 64) {                                  // exclusive scan of the pass's word counts, in offset order
-        const uint32_t a0 = cnt_w[2 * tid], a1 = cnt_w[2 * tid + 1];
-        const uint32_t inc = wave_incl_scan(a0 + a1, lane);
-        cnt_w[2 * tid] = inc - a0 - a1;
-        cnt_w[2 * tid + 1] = inc - a1;
-        if (tid == 63) cnt_w[kWalkWords] = inc;
-      }
-      __syncthreads();
-      const uint32_t pass_total = cnt_w[kWalkWords];
-#pragma unroll
-      for (int e = 0; e < kWalkPer; ++e) {
-        if (!((ub[e] >> bit) & 1u)) continue;
-        const uint32_t k = cum + cnt_w[half + 32 * e] + __popc(ub[e] & ((1u << bit) - 1u));
-        if (k + 1 == cum + pass_total) s_last_v = slot[e];
-        if (k < n_miss) {
-          s.victim[k] = (i32x2){slot[e], held[e]};
-          if (held[e] >= 0) atomicAdd(&s_evict, 1u);
-          if (k + 1 == n_miss) s_assigned_last_v = slot[e];
+        for (int e = 0; e < kWalkPer; ++e) {           // offset o0 + 32 (half + 32 e) + bit within the lap
+          const int64_t o = o0 + 32 * (half + 32 * e) + bit;
+          slot[e] = o < S ? (int32_t)((hand + o) % S) : -1;
+          held[e] = u.slot_pos[slot[e] >= 0 ? slot[e] : 0];
+          refw[e] = pp.clock && slot[e] >= 0 ? u.ref[slot[e] >> 5] : 0u;
         }
+        uint32_t pin_word[kWalkPer];
+#pragma unroll
+        for (int e = 0; e < kWalkPer; ++e) {
+          const int32_t p = held[e];
+          pin_word[e] = (slot[e] >= 0 && p >= 0 && p < L) ? sel[p >> 5] : 0u;
+        }
+        uint32_t ub[kWalkPer];
+#pragma unroll
+        for (int e = 0; e < kWalkPer; ++e) {
+          const int32_t p = held[e];
+          const bool pinned = slot[e] >= 0 && p >= 0 && p < L && ((pin_word[e] >> (p & 31)) & 1u);
+          const bool referenced = slot[e] >= 0 && ((refw[e] >> (slot[e] & 31)) & 1u);
+          const bool cand = slot[e] >= 0 && !pinned && (!pp.clock || referenced == (lap == 1));
+          ub[e] = (uint32_t)(__ballot(cand) >> (tid & 32));   // this half-wave's word
+          if (bit == 0) cnt_w[half + 32 * e] = __popc(ub[e]);
+        }
+        __syncthreads();
+        if (tid < 64) {                                // exclusive scan of the pass's word counts, in offset order
+          const uint32_t a0 = cnt_w[2 * tid], a1 = cnt_w[2 * tid + 1];
+          const uint32_t inc = wave_incl_scan(a0 + a1, lane);
+          cnt_w[2 * tid] = inc - a0 - a1;
+          cnt_w[2 * tid + 1] = inc - a1;
+          if (tid == 63) cnt_w[kWalkWords] = inc;
+        }
+        __syncthreads();
+        const uint32_t pass_total = cnt_w[kWalkWords];
+#pragma unroll
+        for (int e = 0; e < kWalkPer; ++e) {
+          if (!((ub[e] >> bit) & 1u)) continue;
+          const uint32_t k = cum + cnt_w[half + 32 * e] + __popc(ub[e] & ((1u << bit) - 1u));
+          if (k + 1 == cum + pass_total) s_last_v = slot[e];
+          if (k < n_miss) {
+            s.victim[k] = (i32x2){slot[e], held[e]};
+            if (held[e] >= 0) atomicAdd(&s_evict, 1u);
+            if (k + 1 == n_miss) {
+              s_assigned_last_v = slot[e];
+              s_end_o = (int64_t)lap * S + o0 + 32 * (half + 32 * e) + bit;
+            }
+          }
+        }
+        cum += pass_total;
+        __syncthreads();                               // cnt_w reused by the next pass
       }
-      cum += pass_total;
-      __syncthreads();                                 // cnt_w reused by the next pass
     }
     n_assigned = min(n_miss, cum);
   }
   __syncthreads();
+  // CLOCK: the hand cleared the reference bit of every unpinned slot it passed
+  // on the first lap before its last victim (all of them if it went further).
+  // Clear every bit of that offset range here: the assign kernel then sets the
+  // bits of the hits (the only pinned slots) and of the filled victims.
+  if (off && pp.clock && n_miss > 0) {
+    const int64_t lim = min(s_end_o, (int64_t)S);
+    for (int w = tid; w < pp.s_words; w += kPlanThreads) {
+      uint32_t m = 0;
+      for (int b = 0; b < 32; ++b) {
+        const int64_t v = 32 * (int64_t)w + b;
+        const int64_t o = v >= hand ? v - hand : v - hand + S;   // ring offset of slot v from the hand
+        if (v < S && o < lim) m |= 1u << b;
+      }
+      if (m) u.ref[w] &= ~m;
+    }
+  }
   const int last_v = n_assigned == n_miss ? s_assigned_last_v : s_last_v;
   const int new_hand = (off && n_assigned > 0 && last_v >= 0) ? (last_v + 1) % S : hand;
   const int64_t rb = 656;

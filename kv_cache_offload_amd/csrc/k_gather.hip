@@ -49,6 +49,7 @@ struct GatherKArgs {
   int word_blocks;                      // blocks of the union/slot-table part
   int clear_blocks;                     // then blocks clearing the Top-K histograms; the rest write back the ring
   int r_max;
+  int clock;                            // CLOCK replacement: hits and fills set their slot's reference bit
   int64_t max_positions;
 };
 
@@ -123,7 +124,10 @@ __global__ __launch_bounds__(kGatherThreads) void gather_assign_kernel(GatherKAr
       } else if (hw & bit) {
         kind = SRC_HIT;                                // the hit's slot is pinned for this round
         src = u.pos_slot[p].x;
-        if (src >= 0 && src < ka.S) u.pin_round[src] = round;
+        if (src >= 0 && src < ka.S) {
+          u.pin_round[src] = round;
+          if (ka.clock) g_or(&u.ref[src >> 5], 1u << (src & 31));
+        }
       } else {
         const uint32_t k = bm + __popc(sw & ~hw & ~rw & below);
         src = (int32_t)p;
@@ -141,6 +145,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_assign_kernel(GatherKAr
             g_or(&u.hot[p >> 5], bit);
             u.fill_round[v] = round;
             u.pin_round[v] = round;
+            if (ka.clock) g_or(&u.ref[v >> 5], 1u << (v & 31));
             fill = v;
           }
         } else {
@@ -220,10 +225,17 @@ __global__ __launch_bounds__(256) void warm_clear_kernel(UnitDev ud, int S) {
   }
 }
 
-// Warm, phase 2: slot v <- position L-n+v for v < n; other slots empty; no round marks.
-__global__ __launch_bounds__(256) void warm_fill_kernel(UnitDev ud, int S, int64_t L, int64_t n, int row_bytes) {
+// Warm, phase 2: slot v <- position L-n+v for v < n; other slots empty; no round
+// marks; under CLOCK every filled slot starts referenced.
+__global__ __launch_bounds__(256) void warm_fill_kernel(UnitDev ud, int S, int64_t L, int64_t n, int row_bytes,
+                                                        int clock) {
   const UnitG u = as_global(ud);
   const int64_t rb = row_bytes;
+  for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < (S + 31) / 32; w += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t lo = 32 * w;                         // slots [lo, lo + 32) filled iff below n
+    const uint32_t m = n <= lo ? 0u : (n >= lo + 32 ? 0xFFFFFFFFu : (1u << (uint32_t)(n - lo)) - 1u);
+    u.ref[w] = clock ? m : 0u;
+  }
   for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < S; v += (int64_t)gridDim.x * blockDim.x) {
     const int32_t pos = v < n ? (int32_t)(L - n + v) : -1;
     u.slot_pos[v] = pos;
@@ -268,7 +280,7 @@ hipError_t launch_gather(const Geometry& g, const StepArgs& a, hipStream_t st) {
   const int64_t wb_blocks = ((int64_t)g.ring_rows * kCopyChunks16 + kGatherThreads - 1) / kGatherThreads;
   const int64_t clear_blocks = ((int64_t)(kHistReps + 1) * a.R * (kRadixBins / 4) + kGatherThreads - 1) / kGatherThreads;
   GatherKArgs ka{a, g.hot_slots, g.ring_cap, g.ring_rows, g.mode, g.row_bytes, g.top_k, g.r_max * g.top_k,
-                 (int)blocks, (int)clear_blocks, g.r_max, g.max_positions};
+                 (int)blocks, (int)clear_blocks, g.r_max, g.clock ? 1 : 0, g.max_positions};
   return launch_k(gather_assign_kernel,
                   dim3((unsigned)(blocks + clear_blocks + (g.mode == 0 ? wb_blocks : 0)), (unsigned)a.n_seqs),
                   dim3(kGatherThreads), 0, st, ka);
@@ -297,7 +309,7 @@ hipError_t launch_warm(const Geometry& g, const UnitDev& unit, int64_t L, hipStr
   hipError_t e = launch_k(warm_clear_kernel, dim3(grid_for(g.hot_slots)), dim3(256), 0, st, unit, g.hot_slots);
   if (e != hipSuccess) return e;
   return launch_k(warm_fill_kernel, dim3(grid_for(n * kCopyChunks16 > g.hot_slots ? n * kCopyChunks16 : g.hot_slots)),
-                  dim3(256), 0, st, unit, g.hot_slots, L, n, g.row_bytes);
+                  dim3(256), 0, st, unit, g.hot_slots, L, n, g.row_bytes, g.clock ? 1 : 0);
 }
 
 hipError_t launch_rollback(const UnitDev& unit, int64_t L, int64_t M, hipStream_t st) {

@@ -444,7 +444,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_final_kernel(TopkKArgs ka) {
 
 TopkKArgs topk_args(const Geometry& g, const StepArgs& a) {
   return TopkKArgs{a, g.p_pad, g.n_chunks, g.top_k, g.mode, g.r_max, a.l_max > kShortMax ? 1 : 0,
-                   PlanParams{g.hot_slots, g.s_words, g.ring_rows, g.mode}};
+                   PlanParams{g.hot_slots, g.s_words, g.ring_rows, g.mode, g.clock ? 1 : 0}};
 }
 
 }  // namespace

@@ -194,6 +194,7 @@ dsa_status validate_config(const dsa_config* c, std::string* why) {
   if (c->top_k > 4096 || (int64_t)c->max_query_rows * c->top_k > kMaxUnion)
     return bad(DSA_E_UNSUPPORTED, "top_k <= 4096 and max_query_rows * top_k <= 16384");
   if (c->ring_rows > 4096) return bad(DSA_E_UNSUPPORTED, "ring_rows <= 4096");
+  if (c->replacement != DSA_REPL_RING && c->replacement != DSA_REPL_CLOCK) return bad(DSA_E_INVALID, "unknown replacement");
   return DSA_OK;
 }
 
@@ -248,6 +249,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   g.r_max = cfg->max_query_rows;
   g.row_bytes = cfg->latent_dim + 2 * (cfg->latent_dim / cfg->group) + 2 * cfg->rope_dim;
   g.mode = cfg->mode;
+  g.clock = cfg->mode == DSA_KV_OFFLOAD && cfg->replacement == DSA_REPL_CLOCK;
   g.max_positions = cfg->max_positions;
   g.p_pad = (cfg->max_positions + kTopkChunk - 1) / kTopkChunk * kTopkChunk;
   g.n_chunks = (int)(g.p_pad / kTopkChunk);
@@ -264,7 +266,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   auto take = [&](size_t bytes) { size_t at = cur; cur += align_up(bytes ? bytes : 1); return at; };
   const size_t o_units = take(sizeof(UnitDev) * n_units);
   const size_t o_scr = take(sizeof(SeqScratch) * cfg->n_seqs);
-  struct UnitOff { size_t keys, rows, slots, ring, pos_slot, hot, slot_pos, fill, pin, hand, dyn, totals; };
+  struct UnitOff { size_t keys, rows, slots, ring, pos_slot, hot, slot_pos, fill, pin, ref, hand, dyn, totals; };
   std::vector<UnitOff> uo(n_units);
   for (int i = 0; i < n_units; ++i) {
     uo[i].keys = take((size_t)P * g.index_dim * 2);
@@ -276,6 +278,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     uo[i].slot_pos = off ? take((size_t)S * 4) : 0;
     uo[i].fill = off ? take((size_t)S * 4) : 0;
     uo[i].pin = off ? take((size_t)S * 4) : 0;
+    uo[i].ref = off ? take((size_t)g.s_words * 4) : 0;
     uo[i].hand = take(4);
     uo[i].dyn = take(32);
     uo[i].totals = take(64);
@@ -353,6 +356,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
       u.slot_pos = reinterpret_cast<int32_t*>(base + uo[i].slot_pos);
       u.fill_round = reinterpret_cast<int32_t*>(base + uo[i].fill);
       u.pin_round = reinterpret_cast<int32_t*>(base + uo[i].pin);
+      u.ref = reinterpret_cast<uint32_t*>(base + uo[i].ref);        // zero (arena cleared above)
       if (hipMemset(u.pos_slot, 0xFF, (size_t)P * 8) != hipSuccess ||
           hipMemset(u.slot_pos, 0xFF, (size_t)S * 4) != hipSuccess ||
           hipMemset(u.fill_round, 0xFF, (size_t)S * 4) != hipSuccess ||
@@ -644,6 +648,7 @@ dsa_status dsa_debug_size(const dsa_session* s, int32_t layer, int32_t seq, int3
     case DSA_DBG_MIRROR: b = (size_t)(g.mode == DSA_KV_OFFLOAD ? h.M : h.L) * rb; break;
     case DSA_DBG_KEYS: b = (size_t)h.L * g.index_dim * 2; break;
     case DSA_DBG_TOTALS: b = 64; break;
+    case DSA_DBG_REF_BITS: b = (size_t)g.s_words * 4; break;
     default: return DSA_E_INVALID;
   }
   *bytes = b;
@@ -694,6 +699,7 @@ dsa_status dsa_debug_get(dsa_session* s, int32_t layer, int32_t seq, int32_t ite
     case DSA_DBG_MIRROR: src = g.mode == DSA_KV_OFFLOAD ? s->mirrors[ui] : (const void*)u.rows; break;
     case DSA_DBG_KEYS: src = u.keys; break;
     case DSA_DBG_TOTALS: src = u.totals; break;
+    case DSA_DBG_REF_BITS: src = u.ref; break;
     default: return fail(s, DSA_E_INVALID, "unknown item");
   }
   (void)K;

@@ -24,23 +24,24 @@ def dev_tensor(a: np.ndarray, device):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def oracle_units(w: S.Workload, mode: int, layers=None, seqs=None):
+def oracle_units(w: S.Workload, mode: int, layers=None, seqs=None, replacement=0):
     layers = range(w.layers) if layers is None else layers
     seqs = range(w.seqs) if seqs is None else seqs
     shape = UnitShape(max_positions=w.max_positions, index_heads=w.index_heads, index_dim=w.index_dim,
                       heads=w.heads, top_k=w.top_k, hot_slots=w.hot_slots, max_query_rows=w.rows_per_step,
                       latent_dim=w.latent_dim, rope_dim=w.rope_dim, group=w.group, ring_rows=w.ring_rows,
-                      mode=mode, softmax_scale=w.softmax_scale)
+                      mode=mode, softmax_scale=w.softmax_scale, replacement=replacement)
     return {(l, q): OracleUnit(shape) for l in layers for q in seqs}
 
 
-def gpu_session(w: S.Workload, mode: int, n_layers=None):
+def gpu_session(w: S.Workload, mode: int, n_layers=None, replacement=0):
     import kv_cache_offload_amd as K
     cfg = K.make_config(max_positions=w.max_positions, index_heads=w.index_heads, heads=w.heads,
                         top_k=w.top_k, hot_slots=w.hot_slots, max_query_rows=w.rows_per_step,
                         n_layers=w.layers if n_layers is None else n_layers, n_seqs=w.seqs,
                         index_dim=w.index_dim, ring_rows=w.ring_rows, softmax_scale=w.softmax_scale,
-                        mode=K.KV_OFFLOAD if mode == MODE_OFFLOAD else K.KV_HBM_RESIDENT)
+                        mode=K.KV_OFFLOAD if mode == MODE_OFFLOAD else K.KV_HBM_RESIDENT,
+                        replacement=replacement)
     return K.Session(cfg)
 
 
@@ -126,6 +127,8 @@ def gpu_items(sess, layer, seq, R, K, S_, L, row_bytes=656):
         d["pin_round"] = get("pin_round").view(np.int32)
         d["pos_slot"] = get("pos_slot").view(np.int32)
         d["hand"] = int(get("hand").view(np.int32)[0])
+        words = get("ref_bits").view(np.uint32)
+        d["ref"] = ((words[:, None] >> np.arange(32, dtype=np.uint32)) & 1).astype(np.uint8).reshape(-1)[:S_]
     return d
 
 
@@ -169,6 +172,9 @@ def compare_unit(sess, o: OracleUnit, gl: int, seq: int, gout, oout, check_score
         assert np.array_equal(g["pin_round"], pr), f"{what} pin_round differs"
         assert np.array_equal(g["pos_slot"], o.pos_slot()), f"{what} pos_slot differs"
         assert g["hand"] == st["hand"], f"{what} hand differs"
+        if not np.array_equal(g["ref"], o.ref()):
+            bad = np.nonzero(g["ref"] != o.ref())[0]
+            raise AssertionError(f"{what} reference bits differ at {len(bad)} slots, first {bad[0]}")
     if gout is not None:
         ref = oout.astype(np.float64)
         got = gout.astype(np.float64)
