@@ -83,6 +83,8 @@ def _load():
         lib.orc_warm.argtypes = [P]
         lib.orc_rollback.argtypes = [P, i64]
         lib.orc_decode_step.argtypes = [P, i32, P, P, P, P, P]
+        lib.orc_decode_step_sel.argtypes = [P, i32, P, P, P, P, P]
+        lib.orc_prefetch_sel.argtypes = [P, i32, P, P]
         for name in ("orc_get_state", "orc_get_scores", "orc_get_map", "orc_get_compact",
                      "orc_get_counters", "orc_get_pos_slot", "orc_get_slot_bytes", "orc_get_ref"):
             getattr(lib, name).argtypes = [P, P]
@@ -193,6 +195,29 @@ class OracleUnit:
         self._check("orc_decode_step", self._lib.orc_decode_step(
             self._h, R, _ptr(index_q), _ptr(index_w), _ptr(q_lat), _ptr(q_rope), _ptr(out)))
         return out
+
+    def _sel_args(self, sel, counts):
+        sel = np.ascontiguousarray(sel, dtype=np.int32)
+        counts = np.ascontiguousarray(counts, dtype=np.int32)
+        assert sel.ndim == 2 and sel.shape[1] == self.shape.top_k and counts.shape == (sel.shape[0],)
+        return sel, counts
+
+    def decode_step_sel(self, sel, counts, q_lat, q_rope) -> np.ndarray:
+        """A round on a given selection (selection reuse): sel [R][K] ascending, -1 padded."""
+        s = self.shape
+        sel, counts = self._sel_args(sel, counts)
+        R = sel.shape[0]
+        q_lat = np.ascontiguousarray(q_lat, dtype=np.uint16)
+        q_rope = np.ascontiguousarray(q_rope, dtype=np.uint16)
+        assert q_lat.shape == (R, s.heads, s.latent_dim) and q_rope.shape == (R, s.heads, s.rope_dim)
+        out = np.empty((R, s.heads, s.latent_dim), dtype=np.float32)
+        self._check("orc_decode_step_sel", self._lib.orc_decode_step_sel(
+            self._h, R, _ptr(sel), _ptr(counts), _ptr(q_lat), _ptr(q_rope), _ptr(out)))
+        return out
+
+    def prefetch_sel(self, sel, counts):
+        sel, counts = self._sel_args(sel, counts)
+        self._check("orc_prefetch_sel", self._lib.orc_prefetch_sel(self._h, sel.shape[0], _ptr(sel), _ptr(counts)))
 
     # ---------------------------------------------------------------- getters
     def state(self) -> dict:

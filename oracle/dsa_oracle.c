@@ -352,33 +352,17 @@ static void attend(const orc_unit* u, const uint16_t* q_lat, const uint16_t* q_r
   free(rho);
 }
 
-int orc_decode_step(orc_unit* u, int32_t R, const uint16_t* index_q, const float* index_w,
-                    const uint16_t* q_lat, const uint16_t* q_rope, float* out) {
+/* Steps 4-10 of a round, on the selections in u->sel / u->sel_n: union,
+ * classification, pins, replacement, compact rows, attention (skipped when
+ * out is NULL) and the batched writeback; the round counter advances. */
+static int run_round(orc_unit* u, int32_t R, const uint16_t* q_lat, const uint16_t* q_rope, float* out) {
   const orc_config* c = &u->c;
   const int32_t K = c->top_k;
   const int64_t rb = u->row_bytes;
-  if (R <= 0 || R > c->max_query_rows || !index_q || !index_w || !q_lat || !out ||
-      (c->rope_dim > 0 && !q_rope))
-    return ORC_E_INVALID;
-  if (u->L < R) return ORC_E_STATE;
   const int32_t r = (int32_t)u->round;
   if (c->mode == ORC_MODE_OFFLOAD) u->rb_floor = u->M;
   u->last_R = R;
   memset(u->cnt, 0, sizeof(u->cnt));
-
-  /* 1. Visibility: the i-th query row sits at position L-R+i and sees every
-   *    position up to and including its own. */
-  for (int32_t i = 0; i < R; i++) {
-    int64_t n_vis = u->L - R + i + 1;
-    float* s = u->scores + (int64_t)i * c->max_positions;
-    memset(s, 0, (size_t)u->L * sizeof(float));
-    /* 2. Score every visible position. */
-    index_scores(u, index_q + (int64_t)i * c->index_heads * c->index_dim,
-                 index_w + (int64_t)i * c->index_heads, n_vis, s);
-    /* 3. Exact Top-K. */
-    for (int32_t j = 0; j < K; j++) u->sel[(int64_t)i * K + j] = -1;
-    u->sel_n[i] = select_top_k(s, n_vis, K, u->sel + (int64_t)i * K);
-  }
 
   /* 4. Union of the rows' selections, ascending; one entry per distinct
    *    position, so a position several rows select is read once. */
@@ -478,7 +462,7 @@ int orc_decode_step(orc_unit* u, int32_t R, const uint16_t* index_q, const float
   }
 
   /* 9. Attention of each query row over its own selection. */
-  for (int32_t i = 0; i < R; i++)
+  for (int32_t i = 0; out && i < R; i++)
     attend(u, q_lat + (int64_t)i * c->heads * c->latent_dim,
            q_rope ? q_rope + (int64_t)i * c->heads * c->rope_dim : NULL,
            u->map + (int64_t)i * K, u->sel_n[i], out + (int64_t)i * c->heads * c->latent_dim);
@@ -487,6 +471,77 @@ int orc_decode_step(orc_unit* u, int32_t R, const uint16_t* index_q, const float
   writeback_batch(u);
   u->round++;
   return ORC_OK;
+}
+
+int orc_decode_step(orc_unit* u, int32_t R, const uint16_t* index_q, const float* index_w,
+                    const uint16_t* q_lat, const uint16_t* q_rope, float* out) {
+  const orc_config* c = &u->c;
+  const int32_t K = c->top_k;
+  if (R <= 0 || R > c->max_query_rows || !index_q || !index_w || !q_lat || !out ||
+      (c->rope_dim > 0 && !q_rope))
+    return ORC_E_INVALID;
+  if (u->L < R) return ORC_E_STATE;
+
+  /* 1. Visibility: the i-th query row sits at position L-R+i and sees every
+   *    position up to and including its own. */
+  for (int32_t i = 0; i < R; i++) {
+    int64_t n_vis = u->L - R + i + 1;
+    float* s = u->scores + (int64_t)i * c->max_positions;
+    memset(s, 0, (size_t)u->L * sizeof(float));
+    /* 2. Score every visible position. */
+    index_scores(u, index_q + (int64_t)i * c->index_heads * c->index_dim,
+                 index_w + (int64_t)i * c->index_heads, n_vis, s);
+    /* 3. Exact Top-K. */
+    for (int32_t j = 0; j < K; j++) u->sel[(int64_t)i * K + j] = -1;
+    u->sel_n[i] = select_top_k(s, n_vis, K, u->sel + (int64_t)i * K);
+  }
+
+  return run_round(u, R, q_lat, q_rope, out);
+}
+
+/* Selection reuse (offload page, "Starting point": some later layers reuse the
+ * selection, while each layer keeps its own KV rows).  The given selection of
+ * R query rows replaces scoring and Top-K: row i lists sel_n[i] <= K positions,
+ * strictly ascending, each visible to it (at most L-R+i).  Nothing changes on
+ * an error. */
+static int set_selection(orc_unit* u, int32_t R, const int32_t* sel, const int32_t* sel_n) {
+  const orc_config* c = &u->c;
+  const int32_t K = c->top_k;
+  if (R <= 0 || R > c->max_query_rows || !sel || !sel_n) return ORC_E_INVALID;
+  if (u->L < R) return ORC_E_STATE;
+  for (int32_t i = 0; i < R; i++) {
+    if (sel_n[i] < 0 || sel_n[i] > K) return ORC_E_INVALID;
+    for (int32_t j = 0; j < sel_n[i]; j++) {
+      int32_t p = sel[(int64_t)i * K + j];
+      if (p < 0 || p > u->L - R + i || (j > 0 && p <= sel[(int64_t)i * K + j - 1])) return ORC_E_INVALID;
+    }
+  }
+  for (int32_t i = 0; i < R; i++) {
+    u->sel_n[i] = sel_n[i];
+    for (int32_t j = 0; j < K; j++) u->sel[(int64_t)i * K + j] = j < sel_n[i] ? sel[(int64_t)i * K + j] : -1;
+  }
+  return ORC_OK;
+}
+
+int orc_decode_step_sel(orc_unit* u, int32_t R, const int32_t* sel, const int32_t* sel_n,
+                        const uint16_t* q_lat, const uint16_t* q_rope, float* out) {
+  if (!q_lat || !out || (u->c.rope_dim > 0 && !q_rope)) return ORC_E_INVALID;
+  int st = set_selection(u, R, sel, sel_n);
+  if (st != ORC_OK) return st;
+  return run_round(u, R, q_lat, q_rope, out);
+}
+
+/* Prefetch with a known selection (offload page, first decision: once the
+ * selection is known, the rows of layers that reuse it could be moved early,
+ * overlapping other work, though not for free).  Read here as one round of the
+ * unit's cache without attention: the selection is classified and its misses
+ * take slots and are filled from the host mirror exactly as in a decode round,
+ * so the unit's next round finds them as hits.  Resident mode: nothing to do. */
+int orc_prefetch_sel(orc_unit* u, int32_t R, const int32_t* sel, const int32_t* sel_n) {
+  if (u->c.mode == ORC_MODE_RESIDENT) return ORC_OK;
+  int st = set_selection(u, R, sel, sel_n);
+  if (st != ORC_OK) return st;
+  return run_round(u, R, NULL, NULL, NULL);
 }
 
 /* ---------------------------------------------------------------- getters */

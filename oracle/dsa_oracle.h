@@ -93,6 +93,16 @@ int orc_rollback(orc_unit* u, int64_t n);
 int orc_decode_step(orc_unit* u, int32_t R, const uint16_t* index_q, const float* index_w,
                     const uint16_t* q_lat, const uint16_t* q_rope, float* out);
 
+/* A decode round on a given selection (a layer that reuses another layer's
+ * selection): sel i32 [R][top_k] ascending, -1 padded; sel_n i32 [R].  No
+ * scoring (the scores getter keeps the previous step's values). */
+int orc_decode_step_sel(orc_unit* u, int32_t R, const int32_t* sel, const int32_t* sel_n,
+                        const uint16_t* q_lat, const uint16_t* q_rope, float* out);
+/* A round without attention on a given selection: classification, pins,
+ * replacement and slot fills, writeback; the next round finds the filled rows
+ * as hits.  Resident mode: no-op. */
+int orc_prefetch_sel(orc_unit* u, int32_t R, const int32_t* sel, const int32_t* sel_n);
+
 /* ---- state and last-step getters (host buffers owned by the caller) ---- */
 /* state: L, M, round (steps done), hand, last R, union size, rollback floor */
 void orc_get_state(const orc_unit* u, int64_t state[7]);
