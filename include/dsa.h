@@ -227,6 +227,42 @@ dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq,
                            const void* index_q, const float* index_w, const void* q_latent,
                            const void* q_rope, float* out, hipStream_t stream);
 
+/* Selection reuse (offload page, section "Starting point": some later layers
+ * reuse the indexer's selection while each layer keeps its own KV rows).  A
+ * decode step of `layer` on the selection made by the most recent
+ * dsa_decode_step, which must have been src_layer's (layer != src_layer), with
+ * the same rows_per_seq, and every sequence of `layer` must hold exactly as
+ * many rows as the same sequence of src_layer held at that step (append the
+ * layer's own new rows first).  Steps 4-9 of the step semantics then run on
+ * the unit of `layer` -- union, classification against its own cache, pins,
+ * replacement, compact rows from its own sources, attention over its own rows,
+ * batched writeback -- without scoring or Top-K.  Buffers as for
+ * dsa_decode_step.  The selection stays valid until the next dsa_decode_step,
+ * so several layers can reuse it.  Errors (nothing enqueued): DSA_E_INVALID for
+ * bad layers, rows or buffers; DSA_E_STATE if the conditions above fail.
+ * The step items of dsa_debug_get then describe this step (the selection and
+ * scores items are the source step's). */
+dsa_status dsa_decode_step_reuse(dsa_session* s, int32_t layer, int32_t src_layer, int32_t rows_per_seq,
+                                 const void* q_latent, const void* q_rope, float* out, hipStream_t stream);
+
+/* Prefetch for a reusing layer (offload page, first decision: once the
+ * selection is known, the rows of layers that reuse it can be moved early,
+ * overlapping other work, though not for free).  A round of `layer`'s cache on
+ * the same selection and under the same conditions as dsa_decode_step_reuse,
+ * without attention: hits are pinned, misses take slots as in any round and
+ * their rows are copied from the host mirror into those slots, the batched
+ * writeback runs, and the round count advances; the layer's next round (its
+ * dsa_decode_step_reuse) then finds those rows as hits.  It uses a scratch set
+ * of its own, so it may run on a second stream while src_layer's step is
+ * still running on the first, provided the caller orders it after that step's
+ * enqueue point (an event recorded after dsa_decode_step returns), orders the
+ * layer's dsa_decode_step_reuse after it, and enqueues no other work of
+ * `layer` and no other prefetch in between.  The next dsa_decode_step must also
+ * wait for it, because that step overwrites the selection the prefetch reads.
+ * Resident mode: nothing to do (DSA_OK). */
+dsa_status dsa_prefetch_reuse(dsa_session* s, int32_t layer, int32_t src_layer, int32_t rows_per_seq,
+                              hipStream_t stream);
+
 /* Host-side logical state of a unit, without blocking:
  * out[0] = L (rows appended), out[1] = M (rows whose writeback has been
  * enqueued), out[2] = decode rounds done, out[3] = row bytes. */

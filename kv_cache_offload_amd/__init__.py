@@ -34,7 +34,8 @@ COUNTER_NAMES = ("union", "hit", "ring", "miss", "miss_noslot", "evict", "host_b
 # every symbol include/dsa.h declares
 EXPORTS = ("dsa_session_create", "dsa_session_destroy", "dsa_append_rows", "dsa_flush",
            "dsa_warm_hot", "dsa_rollback_rows", "dsa_quantize_rows", "dsa_append_latent",
-           "dsa_decode_step", "dsa_unit_state", "dsa_mirror_rows",
+           "dsa_decode_step", "dsa_decode_step_reuse", "dsa_prefetch_reuse", "dsa_unit_state",
+           "dsa_mirror_rows",
            "dsa_last_error", "dsa_debug_size", "dsa_debug_get", "dsa_set_kernel_timing",
            "dsa_kernel_times")
 
@@ -81,6 +82,8 @@ def _load_library() -> ctypes.CDLL:
         "dsa_quantize_rows": ([P, i64, P, P, P, P], ctypes.c_int),
         "dsa_append_latent": ([P, i32, i32, i64, P, P, P, P], ctypes.c_int),
         "dsa_decode_step": ([P, i32, i32, P, P, P, P, P, P], ctypes.c_int),
+        "dsa_decode_step_reuse": ([P, i32, i32, i32, P, P, P, P], ctypes.c_int),
+        "dsa_prefetch_reuse": ([P, i32, i32, i32, P], ctypes.c_int),
         "dsa_unit_state": ([P, i32, i32, ctypes.POINTER(i64)], ctypes.c_int),
         "dsa_mirror_rows": ([P, i32, i32, ctypes.POINTER(i64)], ctypes.c_int),
         "dsa_last_error": ([P], ctypes.c_char_p),
@@ -150,6 +153,14 @@ def dsa_rollback_rows(h, layer, seq, n, stream) -> int:
 def dsa_decode_step(h, layer, rows_per_seq, index_q, index_w, q_latent, q_rope, out, stream) -> int:
     return _lib.dsa_decode_step(_handle(h), layer, rows_per_seq, index_q, index_w, q_latent, q_rope,
                                 out, stream)
+
+
+def dsa_decode_step_reuse(h, layer, src_layer, rows_per_seq, q_latent, q_rope, out, stream) -> int:
+    return _lib.dsa_decode_step_reuse(_handle(h), layer, src_layer, rows_per_seq, q_latent, q_rope, out, stream)
+
+
+def dsa_prefetch_reuse(h, layer, src_layer, rows_per_seq, stream) -> int:
+    return _lib.dsa_prefetch_reuse(_handle(h), layer, src_layer, rows_per_seq, stream)
 
 
 def dsa_unit_state(h, layer, seq):
@@ -268,6 +279,15 @@ class Session:
         self._check("dsa_decode_step", dsa_decode_step(
             self.h, layer, R, self._ptr(index_q), self._ptr(index_w), self._ptr(q_latent),
             self._ptr(q_rope), self._ptr(out), self._stream()))
+
+    def decode_step_reuse(self, layer, src_layer, q_latent, q_rope, out):
+        R = q_latent.shape[1]
+        self._check("dsa_decode_step_reuse", dsa_decode_step_reuse(
+            self.h, layer, src_layer, R, self._ptr(q_latent), self._ptr(q_rope), self._ptr(out), self._stream()))
+
+    def prefetch_reuse(self, layer, src_layer, rows_per_seq):
+        self._check("dsa_prefetch_reuse", dsa_prefetch_reuse(self.h, layer, src_layer, rows_per_seq,
+                                                             self._stream()))
 
     def unit_state(self, layer, seq):
         st, v = dsa_unit_state(self.h, layer, seq)

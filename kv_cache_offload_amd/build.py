@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdsa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["session.hip", "k_score.hip", "k_topk.hip", "k_gather.hip", "k_attn.hip", "k_quant.hip"]
+SOURCES = ["session.hip", "k_score.hip", "k_topk.hip", "k_gather.hip", "k_attn.hip", "k_quant.hip", "k_reuse.hip"]
 ARCH = "gfx950"
 
 CFLAGS = [

@@ -164,7 +164,9 @@ hipError_t launch_score(const Geometry& g, const StepArgs& a, const uint16_t* q,
 hipError_t launch_topk_partial(const Geometry& g, const StepArgs& a, hipStream_t st);
 hipError_t launch_topk_select(const Geometry& g, const StepArgs& a, hipStream_t st);
 hipError_t prepare_topk_kernels();
-hipError_t launch_gather(const Geometry& g, const StepArgs& a, hipStream_t st);
+// clear_hist: also zero the Top-K histograms for the next step (not in a
+// prefetch round, whose scratch set has none).
+hipError_t launch_gather(const Geometry& g, const StepArgs& a, hipStream_t st, bool clear_hist = true);
 hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_lat,
                        const uint16_t* q_rope, float* out, hipStream_t st);
 hipError_t launch_attn_merge(const Geometry& g, const StepArgs& a, float* out, hipStream_t st);
@@ -175,6 +177,9 @@ hipError_t launch_append(const Geometry& g, const UnitDev& unit, int64_t L, int6
 hipError_t launch_flush(const Geometry& g, const UnitDev& unit, int64_t M, int64_t L, hipStream_t st);
 hipError_t launch_warm(const Geometry& g, const UnitDev& unit, int64_t L, hipStream_t st);
 hipError_t launch_rollback(const UnitDev& unit, int64_t L, int64_t M, hipStream_t st);
+// Selection reuse and prefetch (k_reuse.hip).
+hipError_t launch_reuse_mark(const Geometry& g, const StepArgs& a, const SeqScratch* sel_scr, hipStream_t st);
+hipError_t launch_prefetch_fill(const Geometry& g, const StepArgs& a, hipStream_t st);
 // Quantise-on-append (k_quant.hip).
 hipError_t launch_quantize(const Geometry& g, int64_t n, const uint16_t* latent, const uint16_t* rope, uint8_t* out,
                            hipStream_t st);

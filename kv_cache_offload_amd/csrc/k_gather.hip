@@ -273,12 +273,13 @@ unsigned grid_for(int64_t work, int64_t cap = 4096) {
 
 }  // namespace
 
-hipError_t launch_gather(const Geometry& g, const StepArgs& a, hipStream_t st) {
+hipError_t launch_gather(const Geometry& g, const StepArgs& a, hipStream_t st, bool clear_hist) {
   const int64_t words = (a.l_max + 31) / 32;
   const int64_t waves = (words + 1) / 2;
   const int64_t blocks = (waves + 3) / 4;
   const int64_t wb_blocks = ((int64_t)g.ring_rows * kCopyChunks16 + kGatherThreads - 1) / kGatherThreads;
-  const int64_t clear_blocks = ((int64_t)(kHistReps + 1) * a.R * (kRadixBins / 4) + kGatherThreads - 1) / kGatherThreads;
+  const int64_t clear_blocks =
+      clear_hist ? ((int64_t)(kHistReps + 1) * a.R * (kRadixBins / 4) + kGatherThreads - 1) / kGatherThreads : 0;
   GatherKArgs ka{a, g.hot_slots, g.ring_cap, g.ring_rows, g.mode, g.row_bytes, g.top_k, g.r_max * g.top_k,
                  (int)blocks, (int)clear_blocks, g.r_max, g.clock ? 1 : 0, g.max_positions};
   return launch_k(gather_assign_kernel,

@@ -63,9 +63,13 @@ struct dsa_session {
   std::vector<SeqScratch> scr;
   UnitDev* d_units = nullptr;              // inside the arena
   SeqScratch* d_scr = nullptr;
+  SeqScratch* d_scr_pf = nullptr;          // the prefetch rounds' scratch set
   std::vector<UnitHost> uh;
   int last_layer = -1;
   int last_R = 0;
+  int topk_layer = -1;                     // layer of the most recent full decode step
+  int topk_R = 0;
+  std::vector<int64_t> topk_L;             // per sequence: L at that step
   bool timing = false;
   std::vector<TimedLaunch> timed;
   std::vector<hipEvent_t> free_events;
@@ -216,6 +220,53 @@ void free_all(dsa_session* s) {
   s->arena = nullptr;
 }
 
+// Host side of the end of a round of every sequence of `layer`: the round
+// count, the rollback bound (the mirror count the round started with), and the
+// batch the round wrote back.
+dsa_status finish_round(dsa_session* s, int32_t layer, hipStream_t stream) {
+  for (int q = 0; q < s->cfg.n_seqs; ++q) {
+    UnitHost& h = s->uh[unit_index(s, layer, q)];
+    h.round += 1;
+    h.floor = h.M;
+    if (s->g.mode == DSA_KV_OFFLOAD && h.L - h.M >= s->g.ring_rows) {
+      h.M += s->g.ring_rows;
+      dsa_status st = note_mirror(s, h, stream);
+      if (st != DSA_OK) return st;
+    }
+  }
+  return DSA_OK;
+}
+
+StepArgs step_args(const dsa_session* s, int32_t layer, int R, const SeqScratch* scr) {
+  StepArgs a;
+  a.units = s->d_units;
+  a.scr = scr;
+  a.unit_base = layer * s->cfg.n_seqs;
+  a.n_seqs = s->cfg.n_seqs;
+  a.R = R;
+  a.l_max = 0;
+  for (int q = 0; q < s->cfg.n_seqs; ++q) a.l_max = std::max(a.l_max, s->uh[unit_index(s, layer, q)].L);
+  return a;
+}
+
+// A round of `layer` on the selection of the most recent full decode step,
+// which must be src_layer's, with the same rows per sequence and, for every
+// sequence, the same row count as src_layer had then.
+dsa_status check_reuse(dsa_session* s, int32_t layer, int32_t src_layer, int32_t R) {
+  dsa_status st = entry(s);
+  if (st != DSA_OK) return st;
+  if (layer < 0 || layer >= s->cfg.n_layers || src_layer < 0 || src_layer >= s->cfg.n_layers)
+    return fail(s, DSA_E_INVALID, "layer out of range");
+  if (layer == src_layer) return fail(s, DSA_E_INVALID, "a layer cannot reuse its own selection");
+  if (R < 1 || R > s->g.r_max) return fail(s, DSA_E_INVALID, "rows_per_seq out of range");
+  if (s->topk_layer != src_layer) return fail(s, DSA_E_STATE, "src_layer's step is not the most recent full decode step");
+  if (s->topk_R != R) return fail(s, DSA_E_STATE, "rows_per_seq differs from the source step's");
+  for (int q = 0; q < s->cfg.n_seqs; ++q)
+    if (s->uh[unit_index(s, layer, q)].L != s->topk_L[q])
+      return fail(s, DSA_E_STATE, "a sequence's row count differs from the source layer's at its step");
+  return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -313,6 +364,24 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     so[q].cand_n = take((size_t)g.r_max * g.n_chunks * 4);
     so[q].rowdig = take((size_t)g.r_max * 16);
   }
+  // the prefetch rounds' scratch: only what the plan, the assign and the fill use
+  struct PfOff { size_t cnt, info, uni, kind, src, selmask, hitmask, base_u, base_m, pdesc, victim, done; };
+  const size_t o_scr_pf = take(sizeof(SeqScratch) * cfg->n_seqs);
+  std::vector<PfOff> pf(off ? cfg->n_seqs : 0);
+  for (auto& x : pf) {
+    x.cnt = take(8 * 8);
+    x.info = take(8 * 8);
+    x.uni = take((size_t)RK * 4);
+    x.kind = take((size_t)RK * 4);
+    x.src = take((size_t)RK * 4);
+    x.selmask = take((size_t)P / 32 * 4);
+    x.hitmask = take((size_t)P / 32 * 4);
+    x.base_u = take((size_t)P / 32 * 4);
+    x.base_m = take((size_t)P / 32 * 4);
+    x.pdesc = take((size_t)P * 16);
+    x.victim = take((size_t)g.s_words * 32 * 8);
+    x.done = take(4);
+  }
   s->arena_bytes = cur;
 
   auto bail = [&](dsa_status code, const char* msg) {
@@ -400,10 +469,30 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     if (hipMemset(c.sel, 0xFF, (size_t)RK * 4) != hipSuccess || hipMemset(c.map, 0xFF, (size_t)RK * 4) != hipSuccess)
       return bail(DSA_E_HIP, "hipMemset");
   }
+  std::vector<SeqScratch> scr_pf(pf.size());
+  for (size_t q = 0; q < pf.size(); ++q) {
+    SeqScratch& c = scr_pf[q];                        // fields not listed stay NULL
+    c.counters = reinterpret_cast<int64_t*>(base + pf[q].cnt);
+    c.info = reinterpret_cast<int64_t*>(base + pf[q].info);
+    c.uni = reinterpret_cast<int32_t*>(base + pf[q].uni);
+    c.kind = reinterpret_cast<int32_t*>(base + pf[q].kind);
+    c.src = reinterpret_cast<int32_t*>(base + pf[q].src);
+    c.selmask = reinterpret_cast<uint32_t*>(base + pf[q].selmask);
+    c.hitmask = reinterpret_cast<uint32_t*>(base + pf[q].hitmask);
+    c.base_u = reinterpret_cast<uint32_t*>(base + pf[q].base_u);
+    c.base_m = reinterpret_cast<uint32_t*>(base + pf[q].base_m);
+    c.pdesc = reinterpret_cast<i32x4*>(base + pf[q].pdesc);
+    c.victim = reinterpret_cast<i32x2*>(base + pf[q].victim);
+    c.done = reinterpret_cast<uint32_t*>(base + pf[q].done);
+  }
   s->d_units = reinterpret_cast<UnitDev*>(base + o_units);
   s->d_scr = reinterpret_cast<SeqScratch*>(base + o_scr);
+  s->d_scr_pf = reinterpret_cast<SeqScratch*>(base + o_scr_pf);
+  s->topk_L.assign(cfg->n_seqs, -1);
   if (hipMemcpy(s->d_units, s->units.data(), sizeof(UnitDev) * n_units, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(s->d_scr, s->scr.data(), sizeof(SeqScratch) * cfg->n_seqs, hipMemcpyHostToDevice) != hipSuccess ||
+      (!scr_pf.empty() &&
+       hipMemcpy(s->d_scr_pf, scr_pf.data(), sizeof(SeqScratch) * scr_pf.size(), hipMemcpyHostToDevice) != hipSuccess) ||
       hipDeviceSynchronize() != hipSuccess)
     return bail(DSA_E_HIP, "hipMemcpy");
   *out = s;
@@ -577,16 +666,45 @@ dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq, 
   if ((st = timed_launch(s, KK_MERGE, "attention merge", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK) return st;
   s->last_layer = layer;
   s->last_R = R;
-  for (int q = 0; q < n_seqs; ++q) {
-    UnitHost& h = s->uh[unit_index(s, layer, q)];
-    h.round += 1;
-    h.floor = h.M;
-    if (g.mode == DSA_KV_OFFLOAD && h.L - h.M >= g.ring_rows) {
-      h.M += g.ring_rows;
-      if ((st = note_mirror(s, h, stream)) != DSA_OK) return st;
-    }
-  }
-  return DSA_OK;
+  s->topk_layer = layer;
+  s->topk_R = R;
+  for (int q = 0; q < n_seqs; ++q) s->topk_L[q] = s->uh[unit_index(s, layer, q)].L;
+  return finish_round(s, layer, stream);
+}
+
+dsa_status dsa_decode_step_reuse(dsa_session* s, int32_t layer, int32_t src_layer, int32_t rows_per_seq,
+                                 const void* q_latent, const void* q_rope, float* out, hipStream_t stream) {
+  dsa_status st = check_reuse(s, layer, src_layer, rows_per_seq);
+  if (st != DSA_OK) return st;
+  if (!q_latent || !q_rope || !out || !aligned(q_latent, 16) || !aligned(q_rope, 16) || !aligned(out, 4))
+    return fail(s, DSA_E_INVALID, "step buffers must be non-NULL; bf16 inputs 16-byte aligned");
+  DeviceGuard dg(s->device);
+  const StepArgs a = step_args(s, layer, rows_per_seq, s->d_scr);
+  const Geometry& g = s->g;
+  const uint16_t* ql = static_cast<const uint16_t*>(q_latent);
+  const uint16_t* qr = static_cast<const uint16_t*>(q_rope);
+  if ((st = timed_launch(s, KK_TOPK_SELECT, "reuse mark", [&] { return launch_reuse_mark(g, a, s->d_scr, stream); })) != DSA_OK)
+    return st;
+  if ((st = timed_launch(s, KK_GATHER, "gather", [&] { return launch_gather(g, a, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_MERGE, "attention merge", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK) return st;
+  s->last_layer = layer;
+  s->last_R = rows_per_seq;
+  return finish_round(s, layer, stream);
+}
+
+dsa_status dsa_prefetch_reuse(dsa_session* s, int32_t layer, int32_t src_layer, int32_t rows_per_seq,
+                              hipStream_t stream) {
+  dsa_status st = check_reuse(s, layer, src_layer, rows_per_seq);
+  if (st != DSA_OK) return st;
+  if (s->g.mode != DSA_KV_OFFLOAD) return DSA_OK;
+  DeviceGuard dg(s->device);
+  const StepArgs a = step_args(s, layer, rows_per_seq, s->d_scr_pf);
+  const Geometry& g = s->g;
+  HIPCHK(launch_reuse_mark(g, a, s->d_scr, stream), "prefetch mark");
+  HIPCHK(launch_gather(g, a, stream, false), "prefetch assign");
+  HIPCHK(launch_prefetch_fill(g, a, stream), "prefetch fill");
+  return finish_round(s, layer, stream);
 }
 
 dsa_status dsa_unit_state(const dsa_session* s, int32_t layer, int32_t seq, int64_t out[4]) {
