@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--replacement-probe", action="store_true",
                    help="instead of the throughput run: time the first decode step after a warm start (full "
                         "cache, every reference bit set) and the steps after it, under both policies")
+    p.add_argument("--reuse-probe", action="store_true",
+                   help="instead of the throughput run: layer 0 selects, the other layers reuse its "
+                        "selection; steps/s without and with prefetch on a second stream, and resident")
     p.add_argument("--quantize-rows", type=int, default=1 << 20,
                    help="rows of the quantise-on-append measurement (0 skips it)")
     return p.parse_args()
@@ -323,6 +326,70 @@ def replacement_probe(w, inputs, args):
     return out
 
 
+def reuse_probe(w, inputs, args):
+    """Selection reuse (offload page, "Starting point") and prefetch (first
+    decision).  One step: append every layer's rows, a full decode step of layer
+    0, then a reuse step of every other layer on layer 0's selection.  With
+    prefetch, each reusing layer's prefetch round is enqueued on a second stream
+    right after layer 0's step (the library makes it wait for layer 0's Top-K,
+    and each reuse step wait for its layer's prefetch); the host-link reads of
+    the reusing layers' misses then overlap layer 0's gather and attention and
+    the earlier reuse steps."""
+    import torch
+    import kv_cache_offload_amd as K
+    R = w.rows_per_step
+    res = {}
+    for name, mode, pf in (("offload", K.KV_OFFLOAD, False), ("offload_prefetch", K.KV_OFFLOAD, True),
+                           ("resident", K.KV_HBM_RESIDENT, False)):
+        r = Runner(w, mode, inputs)
+        lib, h, main = K._lib, r.h, r.stream
+        side = torch.cuda.Stream(device=r.sess.device)
+        side_h = ctypes.c_void_p(side.cuda_stream)
+        out = ctypes.c_void_p(r.out.data_ptr())
+        kb, rb = w.index_dim * 2 * R, w.row_bytes * R
+
+        def check(st, what):
+            if st != K.OK:
+                raise K.DsaError(what, st, K.dsa_last_error(h))
+
+        def step():
+            ptr = r.ptr[r.next]
+            for l, (pk, pr, _, _, _, _) in enumerate(ptr):
+                check(lib.dsa_append_rows(h, l, 0, R, ctypes.c_void_p(pk), ctypes.c_void_p(pr), main), "append")
+            _, _, piq, piw, pql, pqr = ptr[0]
+            check(lib.dsa_decode_step(h, 0, R, ctypes.c_void_p(piq), ctypes.c_void_p(piw), ctypes.c_void_p(pql),
+                                      ctypes.c_void_p(pqr), out, main), "decode")
+            if pf:                                   # the library orders them with its own events
+                for l in range(1, w.layers):
+                    check(lib.dsa_prefetch_reuse(h, l, 0, R, side_h), "prefetch")
+            for l in range(1, w.layers):
+                _, _, _, _, pql, pqr = ptr[l]
+                check(lib.dsa_decode_step_reuse(h, l, 0, R, ctypes.c_void_p(pql), ctypes.c_void_p(pqr), out, main),
+                      "reuse")
+            r.next += 1
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        c0 = r.totals()
+        host = 0.0
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            th = time.perf_counter()
+            step()
+            host += time.perf_counter() - th
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        c = (r.totals() - c0).tolist()
+        res[name] = {"steps_per_s": args.steps / dt, "ms_per_step": dt * 1e3 / args.steps,
+                     "host_enqueue_us_per_step": host * 1e6 / args.steps,
+                     "hits_per_step": c[1] / args.steps, "misses_per_step": (c[3] + c[4]) / args.steps,
+                     "host_bytes_per_step": c[6] / args.steps}
+        log(f"reuse probe, {name}: {res[name]['steps_per_s']:.1f} steps/s")
+        r.sess.close()
+    return res
+
+
 def quantize_bench(n_rows, launches=50):
     """dsa_quantize_rows over n_rows bf16 rows already in HBM: average launch time
     from events around back-to-back launches on the launch stream."""
@@ -400,6 +467,9 @@ def main():
     inputs = gen_inputs(w, n_steps)
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
 
+    if args.reuse_probe:
+        print(json.dumps({"workload": w.name, "reuse_probe": reuse_probe(w, inputs, args)}), flush=True)
+        return
     if args.replacement_probe:
         probe = replacement_probe(w, inputs, args)
         print(json.dumps({"workload": w.name, "replacement_probe": probe}), flush=True)

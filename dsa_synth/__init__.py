@@ -92,6 +92,11 @@ WORKLOADS = {
     "million": Workload("million", 3, layers=1, seqs=1, history=1048576, rows_per_step=4,
                         steps=256, index_heads=32, heads=64, top_k=2048, hot_slots=32768,
                         warm=True),
+    # Selection reuse: layer 0 makes the selection, layers 1-3 reuse it with their
+    # own rows and caches (single stream at the 50,023-row shape).
+    "reuse_4_layers": Workload("reuse_4_layers", 5, layers=4, seqs=1, history=50023,
+                               rows_per_step=4, steps=256, index_heads=32, heads=64,
+                               top_k=2048, hot_slots=32768, warm=True),
     # 78 layers, full caches, 8 query rows with 99% planted overlap with the cache.
     "stress_78_layers": Workload("stress_78_layers", 4, layers=78, seqs=1, history=50023,
                                  rows_per_step=8, steps=128, index_heads=32, heads=64,

@@ -253,13 +253,16 @@ dsa_status dsa_decode_step_reuse(dsa_session* s, int32_t layer, int32_t src_laye
  * their rows are copied from the host mirror into those slots, the batched
  * writeback runs, and the round count advances; the layer's next round (its
  * dsa_decode_step_reuse) then finds those rows as hits.  It uses a scratch set
- * of its own, so it may run on a second stream while src_layer's step is
- * still running on the first, provided the caller orders it after that step's
- * enqueue point (an event recorded after dsa_decode_step returns), orders the
- * layer's dsa_decode_step_reuse after it, and enqueues no other work of
- * `layer` and no other prefetch in between.  The next dsa_decode_step must also
- * wait for it, because that step overwrites the selection the prefetch reads.
- * Resident mode: nothing to do (DSA_OK). */
+ * of its own, so it may run on a second stream beside the source step.  The
+ * library orders it with events of its own: `stream` first waits for an event
+ * recorded right after the source step's Top-K (once per selection and
+ * stream), so the prefetch may be enqueued as soon as dsa_decode_step has
+ * returned and overlaps that step's gather, attention and merge; the layer's
+ * dsa_decode_step_reuse waits for the prefetch's completion event when it runs
+ * on another stream; the next dsa_decode_step waits for every prefetch still
+ * pending on another stream, since it replaces the selection they read.
+ * Between the prefetch and the layer's reuse step the caller enqueues no other
+ * work of `layer`.  Resident mode: nothing to do (DSA_OK). */
 dsa_status dsa_prefetch_reuse(dsa_session* s, int32_t layer, int32_t src_layer, int32_t rows_per_seq,
                               hipStream_t stream);
 

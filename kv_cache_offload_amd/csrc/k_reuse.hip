@@ -85,8 +85,10 @@ hipError_t launch_reuse_mark(const Geometry& g, const StepArgs& a, const SeqScra
 hipError_t launch_prefetch_fill(const Geometry& g, const StepArgs& a, hipStream_t st) {
   const int max_union = g.r_max * g.top_k;
   FillKArgs ka{a, max_union, g.row_bytes, g.hot_slots};
+  // host-link bound: 64 blocks keep 256 KiB of reads in flight, more than the
+  // link's bandwidth-delay product, and leave the CUs to the kernels it overlaps
   int64_t blocks = ((int64_t)max_union * kCopyChunks16 + 255) / 256;
-  if (blocks > 2048) blocks = 2048;
+  if (blocks > 64) blocks = 64;
   return launch_k(prefetch_fill_kernel, dim3((unsigned)blocks, (unsigned)a.n_seqs), dim3(256), 0, st, ka);
 }
 

@@ -70,6 +70,13 @@ struct dsa_session {
   int topk_layer = -1;                     // layer of the most recent full decode step
   int topk_R = 0;
   std::vector<int64_t> topk_L;             // per sequence: L at that step
+  hipEvent_t sel_ready = nullptr;          // recorded after that step's Top-K (its selection is final)
+  int64_t sel_epoch = 0;                   // full decode steps so far
+  hipStream_t sel_waited = nullptr;        // the stream that already waits for this epoch's selection
+  int64_t sel_waited_epoch = -1;
+  std::vector<hipEvent_t> pf_done;         // per layer: recorded after its prefetch round
+  std::vector<uint8_t> pf_pending;         // per layer: a prefetch whose event no reuse step has waited for
+  std::vector<hipStream_t> pf_stream;
   bool timing = false;
   std::vector<TimedLaunch> timed;
   std::vector<hipEvent_t> free_events;
@@ -210,6 +217,11 @@ void free_all(dsa_session* s) {
     (void)hipEventDestroy(t.b);
   }
   for (auto e : s->free_events) (void)hipEventDestroy(e);
+  if (s->sel_ready) (void)hipEventDestroy(s->sel_ready);
+  s->sel_ready = nullptr;
+  for (auto e : s->pf_done)
+    if (e) (void)hipEventDestroy(e);
+  s->pf_done.clear();
   for (void* m : s->mirrors)
     if (m) (void)hipHostFree(m);
   if (s->arena) (void)hipFree(s->arena);
@@ -489,6 +501,14 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   s->d_scr = reinterpret_cast<SeqScratch*>(base + o_scr);
   s->d_scr_pf = reinterpret_cast<SeqScratch*>(base + o_scr_pf);
   s->topk_L.assign(cfg->n_seqs, -1);
+  // stream-to-stream ordering on this device only: a device-scope release suffices
+  const unsigned order_flags = hipEventDisableTiming | hipEventReleaseToDevice;
+  if (hipEventCreateWithFlags(&s->sel_ready, order_flags) != hipSuccess) return bail(DSA_E_HIP, "event");
+  s->pf_done.assign(cfg->n_layers, nullptr);
+  s->pf_pending.assign(cfg->n_layers, 0);
+  s->pf_stream.assign(cfg->n_layers, nullptr);
+  for (auto& e : s->pf_done)
+    if (hipEventCreateWithFlags(&e, order_flags) != hipSuccess) return bail(DSA_E_HIP, "event");
   if (hipMemcpy(s->d_units, s->units.data(), sizeof(UnitDev) * n_units, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(s->d_scr, s->scr.data(), sizeof(SeqScratch) * cfg->n_seqs, hipMemcpyHostToDevice) != hipSuccess ||
       (!scr_pf.empty() &&
@@ -657,10 +677,16 @@ dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq, 
   const uint16_t* iq = static_cast<const uint16_t*>(index_q);
   const uint16_t* ql = static_cast<const uint16_t*>(q_latent);
   const uint16_t* qr = static_cast<const uint16_t*>(q_rope);
+  // a prefetch on another stream may still read the selection this step replaces
+  for (int l = 0; l < s->cfg.n_layers; ++l)
+    if (s->pf_pending[l] && s->pf_stream[l] != stream)
+      HIPCHK(hipStreamWaitEvent(stream, s->pf_done[l], 0), "hipStreamWaitEvent");
   if ((st = timed_launch(s, KK_SCORE, "score kernel", [&] { return launch_score(g, a, iq, index_w, stream); })) != DSA_OK) return st;
   if ((st = timed_launch(s, KK_TOPK_PARTIAL, "top-k collect", [&] { return launch_topk_partial(g, a, stream); })) != DSA_OK)
     return st;
   if ((st = timed_launch(s, KK_TOPK_SELECT, "top-k resolve", [&] { return launch_topk_select(g, a, stream); })) != DSA_OK) return st;
+  HIPCHK(hipEventRecord(s->sel_ready, stream), "hipEventRecord");
+  s->sel_epoch += 1;
   if ((st = timed_launch(s, KK_GATHER, "gather", [&] { return launch_gather(g, a, stream); })) != DSA_OK) return st;
   if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream); })) != DSA_OK) return st;
   if ((st = timed_launch(s, KK_MERGE, "attention merge", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK) return st;
@@ -683,6 +709,10 @@ dsa_status dsa_decode_step_reuse(dsa_session* s, int32_t layer, int32_t src_laye
   const Geometry& g = s->g;
   const uint16_t* ql = static_cast<const uint16_t*>(q_latent);
   const uint16_t* qr = static_cast<const uint16_t*>(q_rope);
+  if (s->pf_pending[layer]) {                          // the layer's prefetch round comes first
+    if (s->pf_stream[layer] != stream) HIPCHK(hipStreamWaitEvent(stream, s->pf_done[layer], 0), "hipStreamWaitEvent");
+    s->pf_pending[layer] = 0;
+  }
   if ((st = timed_launch(s, KK_TOPK_SELECT, "reuse mark", [&] { return launch_reuse_mark(g, a, s->d_scr, stream); })) != DSA_OK)
     return st;
   if ((st = timed_launch(s, KK_GATHER, "gather", [&] { return launch_gather(g, a, stream); })) != DSA_OK) return st;
@@ -701,9 +731,17 @@ dsa_status dsa_prefetch_reuse(dsa_session* s, int32_t layer, int32_t src_layer, 
   DeviceGuard dg(s->device);
   const StepArgs a = step_args(s, layer, rows_per_seq, s->d_scr_pf);
   const Geometry& g = s->g;
+  if (s->sel_waited != stream || s->sel_waited_epoch != s->sel_epoch) {   // the selection is final
+    HIPCHK(hipStreamWaitEvent(stream, s->sel_ready, 0), "hipStreamWaitEvent");
+    s->sel_waited = stream;
+    s->sel_waited_epoch = s->sel_epoch;
+  }
   HIPCHK(launch_reuse_mark(g, a, s->d_scr, stream), "prefetch mark");
   HIPCHK(launch_gather(g, a, stream, false), "prefetch assign");
   HIPCHK(launch_prefetch_fill(g, a, stream), "prefetch fill");
+  HIPCHK(hipEventRecord(s->pf_done[layer], stream), "hipEventRecord");
+  s->pf_pending[layer] = 1;
+  s->pf_stream[layer] = stream;
   return finish_round(s, layer, stream);
 }
 

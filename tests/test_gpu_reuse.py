@@ -62,8 +62,6 @@ def _reuse_run(w, mode, steps, layers=3, prefetch=(1,), replacement=REPL_RING, s
         out = torch.full((len(seqs), R, w.heads, w.latent_dim), float("nan"), dtype=torch.float32, device=dev)
         sess.decode_step(0, dev_tensor(st(0), dev), dev_tensor(st(1), dev), dev_tensor(st(2), dev),
                          dev_tensor(st(3), dev), out)
-        after_src = torch.cuda.Event()
-        after_src.record()
         oout = {q: orcs[(0, q)].decode_step(*qs[i]) for i, q in enumerate(seqs)}
         sel = {q: orcs[(0, q)].selection() for q in seqs}
         overlap = step % 2 == 1
@@ -75,13 +73,9 @@ def _reuse_run(w, mode, steps, layers=3, prefetch=(1,), replacement=REPL_RING, s
                 compare_unit(sess, orcs[(0, q)], 0, q, g0[i], oout[q], what=f"{w.name} source seq={q} step={step}")
         for l in range(1, layers):
             if l in prefetch:
-                done = torch.cuda.Event()
                 if side_stream:
-                    with torch.cuda.stream(side):
-                        side.wait_event(after_src)
+                    with torch.cuda.stream(side):             # ordered by the library's own events
                         sess.prefetch_reuse(l, 0, R)
-                        done.record(side)
-                    torch.cuda.current_stream().wait_event(done)
                 else:
                     sess.prefetch_reuse(l, 0, R)
                 for q in seqs:
