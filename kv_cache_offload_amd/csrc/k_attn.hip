@@ -411,17 +411,38 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
     sl[t] = s.part_ml[base * 2 + 1];
   }
   __syncthreads();
-  if (tid < 16) {
+  {
+    // the weights of head wh: its 16 threads (one wave quarter) take the splits
+    // c, c + 16, ..., then reduce the max and the denominator by shuffles
+    constexpr int kPer = (MAXS + 15) / 16;
+    const int wh = tid >> 4, c = tid & 15;
+    float mloc[kPer];
     float M = -INFINITY;
-    for (int sp = 0; sp < used; ++sp) M = fmaxf(M, wgt[sp * 16 + tid]);
-    float den = 0.f;
-    for (int sp = 0; sp < used; ++sp) {
-      const float w = M == -INFINITY ? 0.f : exp2f(wgt[sp * 16 + tid] - M);
-      wgt[sp * 16 + tid] = w;
-      den += w * sl[sp * 16 + tid];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int sp = c + 16 * e;
+      mloc[e] = sp < used ? wgt[sp * 16 + wh] : -INFINITY;
+      M = fmaxf(M, mloc[e]);
     }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float wloc[kPer];
+    float den = 0.f;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int sp = c + 16 * e;
+      wloc[e] = (sp < used && M != -INFINITY) ? exp2f(mloc[e] - M) : 0.f;
+      if (sp < used) den += wloc[e] * sl[sp * 16 + wh];
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) den += __shfl_xor(den, o);
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    for (int sp = 0; sp < used; ++sp) wgt[sp * 16 + tid] *= inv;
+    __syncthreads();                                   // every max read before any weight is written
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int sp = c + 16 * e;
+      if (sp < used) wgt[sp * 16 + wh] = wloc[e] * inv;
+    }
   }
   __syncthreads();
   float acc = 0.f;
