@@ -302,7 +302,7 @@ typedef enum {
   DSA_DBG_HAND = 13,       /* i32 [1] */
   DSA_DBG_SLOT_BYTES = 14, /* u8  [S][row_bytes] */
   DSA_DBG_MIRROR = 15,     /* u8  [M][row_bytes] host mirror (resident: row store [L]) */
-  DSA_DBG_KEYS = 16,       /* bf16 [L][index_dim] */
+  DSA_DBG_KEYS = 16,       /* bf16 [L][index_dim] (dst 16-byte aligned; stored in another order, rebuilt by a kernel) */
   DSA_DBG_TOTALS = 17,     /* i64 [8]  the counters above summed over every step of the unit */
   DSA_DBG_REF_BITS = 18    /* u32 [ceil(S/32)] reference bits, slot v = bit v%32 of word v/32 (CLOCK; 0 otherwise) */
 } dsa_debug_item;

@@ -37,10 +37,20 @@ typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 template <class T> using GlobalPtr = DSA_GLOBAL T*;
 
+// Index keys are stored in the score kernel's MFMA operand order.  Positions
+// form tiles of 32; within a tile, 16-byte piece c (dims 8c .. 8c+7) of the key
+// at position t sits at piece index 64 (c % 8) + 32 (c / 8) + t % 32, so that
+// load k (c % 8 == k) of a wave reads 1 KiB contiguous and lane (n, half)
+// receives exactly its B fragment (key n, dims 64 half + 8 k .. +7).
+// Returns the index, in 16-byte pieces from the store's start (index_dim 128).
+__host__ __device__ inline int64_t key_piece(int64_t t, int c) {
+  return (t >> 5) * 512 + (c & 7) * 64 + (c >> 3) * 32 + (t & 31);
+}
+
 // Per-unit persistent state, device-visible.
 template <template <class> class P>
 struct UnitT {
-  P<uint16_t> keys;        // [P_pad][index_dim] bf16, HBM
+  P<uint16_t> keys;        // [P_pad / 32][8][64][8] bf16, HBM, in key_piece order
   P<uint8_t> rows;         // offload: device address of the pinned host mirror; resident: HBM row store
   P<uint8_t> slots;        // [S][row_bytes] hot slots (offload)
   P<uint8_t> ring;         // [ring_cap][row_bytes] recent ring (offload)
@@ -177,6 +187,8 @@ hipError_t launch_append(const Geometry& g, const UnitDev& unit, int64_t L, int6
 hipError_t launch_flush(const Geometry& g, const UnitDev& unit, int64_t M, int64_t L, hipStream_t st);
 hipError_t launch_warm(const Geometry& g, const UnitDev& unit, int64_t L, hipStream_t st);
 hipError_t launch_rollback(const UnitDev& unit, int64_t L, int64_t M, hipStream_t st);
+// Keys of positions [0, L) in plain row order [L][index_dim], for inspection.
+hipError_t launch_keys_linear(const UnitDev& unit, int64_t L, uint16_t* dst, hipStream_t st);
 // Selection reuse and prefetch (k_reuse.hip).
 hipError_t launch_reuse_mark(const Geometry& g, const StepArgs& a, const SeqScratch* sel_scr, hipStream_t st);
 hipError_t launch_prefetch_fill(const Geometry& g, const StepArgs& a, hipStream_t st);

@@ -181,8 +181,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendKArgs ka) {
   const int64_t rb = ka.row_bytes;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < key_chunks + row_chunks;
        t += (int64_t)gridDim.x * blockDim.x) {
-    if (t < key_chunks) {
-      reinterpret_cast<DSA_GLOBAL u32x4*>(u.keys + ka.L * ka.index_dim)[t] = reinterpret_cast<const u32x4*>(ka.keys)[t];
+    if (t < key_chunks) {                                // piece c of new key i, to its operand-order place
+      const int64_t i = t / (ka.index_dim / 8), c = t % (ka.index_dim / 8);
+      reinterpret_cast<DSA_GLOBAL u32x4*>(u.keys)[key_piece(ka.L + i, (int)c)] = reinterpret_cast<const u32x4*>(ka.keys)[t];
     } else {
       const int64_t w = t - key_chunks;
       const int64_t i = w / kCopyChunks16, c = w % kCopyChunks16;
@@ -255,6 +256,13 @@ __global__ __launch_bounds__(256) void warm_fill_kernel(UnitDev ud, int S, int64
   if (blockIdx.x == 0 && threadIdx.x == 0) *u.hand = (int32_t)(n % S);
 }
 
+// Keys of positions [0, L) back in row order, one 16-byte piece per thread.
+__global__ __launch_bounds__(256) void keys_linear_kernel(UnitDev ud, int64_t L, uint16_t* dst) {
+  const UnitG u = as_global(ud);
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < L * 16; t += (int64_t)gridDim.x * blockDim.x)
+    reinterpret_cast<u32x4*>(dst)[t] = reinterpret_cast<const DSA_GLOBAL u32x4*>(u.keys)[key_piece(t / 16, (int)(t % 16))];
+}
+
 // Rollback: publish the shortened row count and mirror count in stream order.
 __global__ __launch_bounds__(64) void rollback_kernel(UnitDev ud, int64_t L, int64_t M) {
   const UnitG u = as_global(ud);
@@ -311,6 +319,10 @@ hipError_t launch_warm(const Geometry& g, const UnitDev& unit, int64_t L, hipStr
   if (e != hipSuccess) return e;
   return launch_k(warm_fill_kernel, dim3(grid_for(n * kCopyChunks16 > g.hot_slots ? n * kCopyChunks16 : g.hot_slots)),
                   dim3(256), 0, st, unit, g.hot_slots, L, n, g.row_bytes, g.clock ? 1 : 0);
+}
+
+hipError_t launch_keys_linear(const UnitDev& unit, int64_t L, uint16_t* dst, hipStream_t st) {
+  return launch_k(keys_linear_kernel, dim3(grid_for(L * 16)), dim3(256), 0, st, unit, L, dst);
 }
 
 hipError_t launch_rollback(const UnitDev& unit, int64_t L, int64_t M, hipStream_t st) {

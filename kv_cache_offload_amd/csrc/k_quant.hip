@@ -90,7 +90,7 @@ __device__ inline void quantize_one(const QuantKArgs& ka, const UnitG& u, int la
     *reinterpret_cast<DSA_GLOBAL u32x4*>(dst + kScaleOff) =
         (u32x4){sc[0] | sc[1] << 16, sc[2] | sc[3] << 16, sc[4] | sc[5] << 16, sc[6] | sc[7] << 16};
   if (lane < kRopePieces) reinterpret_cast<DSA_GLOBAL u32x4*>(dst + kRopeOff)[lane] = rope_raw;
-  if (!ka.out && lane < kKeyPieces) reinterpret_cast<DSA_GLOBAL u32x4*>(u.keys + p * kIndexDim)[lane] = key_raw;
+  if (!ka.out && lane < kKeyPieces) reinterpret_cast<DSA_GLOBAL u32x4*>(u.keys)[key_piece(p, lane)] = key_raw;
 }
 
 // Each wave takes kRowsPerWave consecutive rows per pass and issues all their

@@ -11,10 +11,12 @@
 // dimension (R*H_I rows, padded to 32), positions form N, the 128 key dims K.
 // One v_mfma_f32_32x32x16_bf16 tile covers 32 (row, head) pairs x 32
 // positions x 16 dims.  Q lives in LDS (row stride padded to 272 B), keys are
-// streamed from HBM straight into B fragments: lane (n, half) loads 16 bytes of
-// key t0+n, so every byte of a key is read exactly once per wave.  The K index
-// is permuted (half 0 takes dims 0..63, half 1 dims 64..127, 8 per k-step);
-// both operands use the same permutation, so the dot products are unchanged.
+// streamed from HBM straight into B fragments: the key store keeps each
+// 32-position tile in operand order, so each of a tile's 8 loads reads 1 KiB
+// contiguous (fully coalesced) and lane (n, half) receives 16 bytes of key
+// t0+n; every byte of a key is read exactly once per wave.  The K index is
+// permuted (half 0 takes dims 0..63, half 1 dims 64..127, 8 per k-step); both
+// operands use the same permutation, so the dot products are unchanged.
 // The fp32 accumulator is exact for integer-valued bf16 inputs (|q.k| <= 2^13).
 // After the tile, each lane applies ReLU and the head weight to its 16
 // accumulator rows and the head sum is finished with one cross-half shuffle.
@@ -95,12 +97,15 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreKArgs ka) {
   // order, so staging Q does not wait for the keys (HBM).
   // Positions past L read (unused) rows of the key store, so the loads need not
   // wait for L.
+  // The key store is in operand order (key_piece): load k of a 32-position tile
+  // is 1 KiB contiguous and gives lane (n, hf) its B fragment.
+  const int64_t last_tile = ka.p_pad / 32 - 1;
+  const DSA_GLOBAL bf16x8* keys16 = reinterpret_cast<const DSA_GLOBAL bf16x8*>(u.keys);
   bf16x8 b[8];
   {
-    const int64_t t = min(first_sub * 32 + n, ka.p_pad - 1);
-    const DSA_GLOBAL bf16x8* kp = reinterpret_cast<const DSA_GLOBAL bf16x8*>(u.keys + t * 128 + 64 * hf);
+    const DSA_GLOBAL bf16x8* kp = keys16 + min(first_sub, last_tile) * 512 + lane;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) b[ks] = kp[ks];
+    for (int ks = 0; ks < 8; ++ks) b[ks] = kp[ks * 64];
   }
 
   for (int w = threadIdx.x; w < R * (kRadixBins / 2); w += blockDim.x) lh[w] = 0;
@@ -122,10 +127,9 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreKArgs ka) {
     // complete in issue order, so this tile's wait does not include them).
     bf16x8 bn[8];
     if (si + 1 < ka.subs_per_wave) {
-      const int64_t tn = min(t + 32, ka.p_pad - 1);
-      const DSA_GLOBAL bf16x8* kp = reinterpret_cast<const DSA_GLOBAL bf16x8*>(u.keys + tn * 128 + 64 * hf);
+      const DSA_GLOBAL bf16x8* kp = keys16 + min(first_sub + si + 1, last_tile) * 512 + lane;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) bn[ks] = kp[ks];
+      for (int ks = 0; ks < 8; ++ks) bn[ks] = kp[ks * 64];
     }
     // Up to four row tiles at a time: independent accumulation chains, so the
     // MFMA pipeline is never waiting on one accumulator.

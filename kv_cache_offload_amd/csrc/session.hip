@@ -853,7 +853,10 @@ dsa_status dsa_debug_get(dsa_session* s, int32_t layer, int32_t seq, int32_t ite
     case DSA_DBG_HAND: src = u.hand; break;
     case DSA_DBG_SLOT_BYTES: src = u.slots; break;
     case DSA_DBG_MIRROR: src = g.mode == DSA_KV_OFFLOAD ? s->mirrors[ui] : (const void*)u.rows; break;
-    case DSA_DBG_KEYS: src = u.keys; break;
+    case DSA_DBG_KEYS:                                 // stored in operand order: back to rows
+      if (!aligned(dst, 16)) return fail(s, DSA_E_INVALID, "keys destination must be 16-byte aligned");
+      HIPCHK(launch_keys_linear(u, h.L, static_cast<uint16_t*>(dst), stream), "keys kernel");
+      return DSA_OK;
     case DSA_DBG_TOTALS: src = u.totals; break;
     case DSA_DBG_REF_BITS: src = u.ref; break;
     default: return fail(s, DSA_E_INVALID, "unknown item");

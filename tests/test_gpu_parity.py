@@ -227,3 +227,24 @@ def test_mirror_after_flush_equals_appended_rows():
     m = sess.debug("mirror", 0, 0).cpu().numpy().reshape(-1, 656)
     assert np.array_equal(m, np.concatenate(appended))
     sess.close()
+
+
+def test_key_store_round_trip():
+    # index keys are kept in the score kernel's operand order; the inspection copy
+    # rebuilds row order: both append paths, a ragged tail of a 32-position tile
+    w = S.WORKLOADS["tiny"].scaled(history=1000, rows_per_step=3, steps=3)
+    sess = gpu_session(w, MODE_OFFLOAD)
+    keys, rows = S.history(w, 0, 0)
+    sess.append_rows(0, 0, dev_tensor(keys[:700], sess.device), dev_tensor(rows[:700], sess.device))
+    g = np.random.default_rng(2)
+    lat = S.bf16_bits(g.standard_normal((300, 512)))
+    rope = S.bf16_bits(g.standard_normal((300, 64)))
+    sess.append_latent(0, 0, dev_tensor(keys[700:], sess.device), dev_tensor(lat, sess.device),
+                       dev_tensor(rope, sess.device))
+    nk, nr = S.step_rows(w, 0, 0, 0)
+    sess.append_rows(0, 0, dev_tensor(nk, sess.device), dev_tensor(nr, sess.device))
+    import torch
+    torch.cuda.synchronize()
+    got = sess.debug("keys", 0, 0).cpu().numpy().view(np.uint16).reshape(-1, 128)
+    assert np.array_equal(got, np.concatenate([keys, nk]))
+    sess.close()
