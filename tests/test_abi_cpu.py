@@ -86,3 +86,16 @@ def test_abi_version_mismatch_and_nulls():
     assert K._lib.dsa_append_rows(None, 0, 0, 1, None, None, None) == K.E_INVALID
     assert K._lib.dsa_decode_step(None, 0, 1, None, None, None, None, None, None) == K.E_INVALID
     assert K._lib.dsa_rollback_rows(None, 0, 0, 1, None) == K.E_INVALID
+    assert K._lib.dsa_quantize_rows(None, 1, None, None, None, None) == K.E_INVALID
+    assert K._lib.dsa_append_latent(None, 0, 0, 1, None, None, None, None) == K.E_INVALID
+    assert K._lib.dsa_decode_step_reuse(None, 1, 0, 1, None, None, None, None) == K.E_INVALID
+    assert K._lib.dsa_prefetch_reuse(None, 1, 0, 1, None) == K.E_INVALID
+
+
+def test_config_rejects_unknown_replacement_policy():
+    _ensure_built()
+    import kv_cache_offload_amd as K
+    cfg = _cfg(replacement=2)
+    out = ctypes.c_void_p()
+    assert K._lib.dsa_session_create(ctypes.byref(cfg), ctypes.byref(out)) == K.E_INVALID
+    assert not out.value
