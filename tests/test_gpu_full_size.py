@@ -97,3 +97,38 @@ def test_stress_all_78_layers_sampled():
                              what=f"stress layer={l} step={step}")
         _note(f"stress step {step}: 78 layers, sampled layers match ({time.time() - t0:.1f} s)")
     sess.close()
+
+
+def test_maximum_cache_and_union_long_history():
+    # the largest hot cache (2^20 slots, empty at first: the first step's ~15,000
+    # misses walk several 4,096-offset passes), the largest union (8 rows x
+    # Top-2048 = 16,384 entries) and a history above 65,536 positions (the Top-K's
+    # long-history path with its digit and refine passes)
+    from tests.parity_util import load_history
+    w = S.WORKLOADS["stress_78_layers"].scaled(name="max_cache_union", wid=6, layers=1, history=100_003,
+                                               hot_slots=1 << 20, planted_overlap=False, steps=3, warm=False)
+    t0 = time.time()
+    sess = gpu_session(w, MODE_OFFLOAD)
+    orcs = oracle_units(w, MODE_OFFLOAD)
+    load_history(w, sess, orcs)
+    for step in range(w.steps):
+        gout, oout = run_step(w, 0, step, sess, orcs)
+        compare_unit(sess, orcs[(0, 0)], 0, 0, gout.cpu().numpy()[0], oout[0], what=f"max sizes step={step}")
+        _note(f"max sizes step {step} matches ({time.time() - t0:.1f} s)")
+    sess.close()
+
+
+def test_append_past_capacity_is_refused_without_change():
+    import kv_cache_offload_amd as K
+    w = S.WORKLOADS["tiny"].scaled(history=100, rows_per_step=1, steps=2)
+    sess = gpu_session(w, MODE_OFFLOAD)
+    keys, rows = S.history(w, 0, 0)
+    sess.append_rows(0, 0, dev_tensor(keys, sess.device), dev_tensor(rows, sess.device))
+    k3, r3 = S.history(w.scaled(history=103), 0, 0)
+    with pytest.raises(K.DsaError) as e:
+        sess.append_rows(0, 0, dev_tensor(k3[:3], sess.device), dev_tensor(r3[:3], sess.device))
+    assert e.value.status == K.E_CAPACITY
+    assert sess.unit_state(0, 0)["L"] == 100
+    sess.append_rows(0, 0, dev_tensor(k3[:2], sess.device), dev_tensor(r3[:2], sess.device))   # exactly full
+    assert sess.unit_state(0, 0)["L"] == 102
+    sess.close()
