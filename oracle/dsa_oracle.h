@@ -19,7 +19,13 @@
  *     (sections "Decision 3: let the GPU manage the hot cache directly" and
  *     "GPU cache management errs too: cross-block visibility and long
  *     replacement sweeps");
- *   - absorbed-MLA attention over the selected rows only.
+ *   - absorbed-MLA attention over the selected rows only;
+ *   - around the step: rollback of rejected verify rows (section "Capacity must
+ *     survive the session lifecycle"), the CLOCK replacement variant with
+ *     reference bits (the policy the ring walk replaced, in "GPU cache management
+ *     errs too"), and rounds on a selection made by another layer, with or
+ *     without attention -- selection reuse and prefetch (sections "Starting
+ *     point" and the first decision).  Quantise-on-append lives in quantize.py.
  *
  * Arithmetic is float64 throughout; scores are reported as float32 with -0
  * canonicalised to +0, and the Top-K decision is taken on those float32 values.
