@@ -60,8 +60,13 @@ __device__ inline void count_digit(uint32_t* lh, int r, float score) {
   atomicAdd(&lh[r * (kRadixBins / 2) + (d >> 1)], 1u << (16 * (d & 1)));
 }
 
+// Three workgroups per CU (the LDS allows three): the register budget this
+// implies (at most 168 VGPRs) lets 12 waves per CU keep their next key tile in
+// flight; with the compiler's unbounded choice (about 228) only 8 could, and the
+// kernel waited on HBM latency (2.7 TB/s on a million-row history, 3.5 TB/s with
+// the bound).  H_I = 4 keeps the default: it would spill under the bound.
 template <int HI>
-__global__ __launch_bounds__(256) void score_kernel(ScoreKArgs ka) {
+__global__ __launch_bounds__(256, HI >= 8 ? 3 : 1) void score_kernel(ScoreKArgs ka) {
   extern __shared__ __align__(16) uint16_t sq[];   // [MT*32][kQStride], weights, digit histograms
   const StepArgs& a = ka.a;
   const int seq = blockIdx.y;
