@@ -461,6 +461,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     base = S.WORKLOADS[args.workload]
     n_steps = args.warmup + args.steps + args.kernel_steps
+    if base.planted_overlap:
+        from dsa_synth import planted
+        if n_steps > planted.max_steps(base):
+            print(f"{base.name} has planted queries for {planted.max_steps(base)} steps; "
+                  f"--warmup + --steps + --kernel-steps asks for {n_steps}", file=sys.stderr)
+            sys.exit(2)
     w = base.scaled(steps=max(base.steps, n_steps))
     log(f"generating {n_steps} steps of inputs for {w.name}")
     t0 = time.perf_counter()

@@ -106,6 +106,11 @@ def step_rows(w: Workload, layer: int, seq: int, step: int):
     return bf16_bits(k), rows
 
 
+def max_steps(w: Workload) -> int:
+    """Steps whose queries get fresh codes (codes are never reused)."""
+    return len(_CODE_LIST) // ((w.rows_per_step + 1) // 2 * CODES_PER_ROW)
+
+
 def index_queries(w: Workload, layer: int, seq: int, step: int):
     R, HI = w.rows_per_step, w.index_heads
     q = np.zeros((R, HI, w.index_dim), dtype=np.float64)
@@ -116,6 +121,8 @@ def index_queries(w: Workload, layer: int, seq: int, step: int):
         wt[i, 0] = 4.0
         for h in range(1, 1 + CODES_PER_ROW):
             code = step * pairs * CODES_PER_ROW + (i // 2) * CODES_PER_ROW + (h - 1)
+            if code >= len(_CODE_LIST):
+                raise ValueError(f"the planted workload has fresh codes for {max_steps(w)} steps; step {step} asked")
             a, b = _CODE_LIST[code]
             q[i, h, a] = 8.0
             q[i, h, b] = 8.0

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace dsa {
@@ -114,10 +115,17 @@ struct Geometry {
   float softmax_scale;
 };
 
+// Every unit's arena buffers, and every sequence's scratch, repeat one layout
+// at a constant stride (the session checks this at create).  A kernel gets the
+// descriptors of sequence 0 by value in its arguments and forms those of
+// sequence q by moving each pointer q strides on: no descriptor table in device
+// memory, so no dependent load stands between a kernel's start and its buffers.
 struct StepArgs {
-  const UnitDev* units;   // device array, indexed by unit_base + seq
-  const SeqScratch* scr;  // device array, indexed by seq
-  int unit_base;
+  UnitDev u0;             // unit (layer, sequence 0)
+  SeqScratch s0;          // scratch of sequence 0 (the main set or the prefetch set)
+  int64_t u_stride;       // bytes between consecutive units' arena buffers
+  int64_t rows_stride;    // bytes between consecutive units' row stores (offload: host mirrors)
+  int64_t s_stride;       // bytes between consecutive sequences' scratch
   int n_seqs;
   int R;
   int64_t l_max;          // max L over the layer's sequences (grid sizing)
@@ -141,17 +149,31 @@ inline hipError_t launch_k(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipS
   return hipGetLastError();
 }
 
-// Device views of the descriptors of sequence `seq`.
-__device__ inline UnitG unit_of(const StepArgs& a, int seq) {
-  return reinterpret_cast<const UnitG*>(a.units)[a.unit_base + seq];
-}
-__device__ inline ScratchG scratch_of(const StepArgs& a, int seq) {
-  return reinterpret_cast<const ScratchG*>(a.scr)[seq];
-}
 __device__ inline UnitG as_global(const UnitDev& u) {
   UnitG g;
   __builtin_memcpy(&g, &u, sizeof(g));
   return g;
+}
+// A descriptor (a struct of pointers) moved `delta` bytes on, word `alt` by
+// `alt_delta` instead; NULL fields stay NULL.
+template <class G, class D>
+__device__ inline G moved_desc(const D& d, int64_t delta, int alt, int64_t alt_delta) {
+  constexpr int kWords = sizeof(D) / 8;
+  static_assert(sizeof(D) == kWords * 8 && sizeof(G) == sizeof(D), "descriptors are arrays of pointers");
+  uint64_t v[kWords];
+  __builtin_memcpy(v, &d, sizeof(D));
+#pragma unroll
+  for (int i = 0; i < kWords; ++i) v[i] = v[i] ? v[i] + (uint64_t)(i == alt ? alt_delta : delta) : 0u;
+  G g;
+  __builtin_memcpy(&g, v, sizeof(g));
+  return g;
+}
+// Device views of the descriptors of sequence `seq`.
+__device__ inline UnitG unit_of(const StepArgs& a, int seq) {
+  return moved_desc<UnitG>(a.u0, seq * a.u_stride, (int)(offsetof(UnitDev, rows) / 8), seq * a.rows_stride);
+}
+__device__ inline ScratchG scratch_of(const StepArgs& a, int seq) {
+  return moved_desc<ScratchG>(a.s0, seq * a.s_stride, -1, 0);
 }
 
 // Relaxed device-scope atomics on global memory.
@@ -190,7 +212,9 @@ hipError_t launch_rollback(const UnitDev& unit, int64_t L, int64_t M, hipStream_
 // Keys of positions [0, L) in plain row order [L][index_dim], for inspection.
 hipError_t launch_keys_linear(const UnitDev& unit, int64_t L, uint16_t* dst, hipStream_t st);
 // Selection reuse and prefetch (k_reuse.hip).
-hipError_t launch_reuse_mark(const Geometry& g, const StepArgs& a, const SeqScratch* sel_scr, hipStream_t st);
+// sel0, sel_stride: the main scratch set, where the selection lives.
+hipError_t launch_reuse_mark(const Geometry& g, const StepArgs& a, const SeqScratch& sel0, int64_t sel_stride,
+                             hipStream_t st);
 hipError_t launch_prefetch_fill(const Geometry& g, const StepArgs& a, hipStream_t st);
 // Quantise-on-append (k_quant.hip).
 hipError_t launch_quantize(const Geometry& g, int64_t n, const uint16_t* latent, const uint16_t* rope, uint8_t* out,

@@ -24,8 +24,9 @@ namespace dsa {
 namespace {
 
 struct MarkKArgs {
-  StepArgs a;                 // a.scr: the round's scratch (main, or the prefetch set)
-  const SeqScratch* sel_scr;  // where the selection lives: the main scratch
+  StepArgs a;                 // a.s0: the round's scratch (main, or the prefetch set)
+  SeqScratch sel0;            // where the selection lives: the main scratch (sequence 0)
+  int64_t sel_stride;         // and its stride between sequences
   int K, mode;
   PlanParams plan;
 };
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(kPlanThreads) void reuse_mark_kernel(MarkKArgs ka) 
   const int r = blockIdx.x, seq = blockIdx.y;
   const UnitG u = unit_of(a, seq);
   const ScratchG s = scratch_of(a, seq);
-  const ScratchG src = reinterpret_cast<const ScratchG*>(ka.sel_scr)[seq];
+  const ScratchG src = moved_desc<ScratchG>(ka.sel0, seq * ka.sel_stride, -1, 0);
   const PlanState ps{u.dyn[0], u.dyn[1], (int32_t)u.dyn[2], ka.mode == 0 ? *u.hand : 0};
   const int n = src.sel_n[r];
   const auto sel = src.sel + (int64_t)r * ka.K;
@@ -77,8 +78,9 @@ __global__ __launch_bounds__(256) void prefetch_fill_kernel(FillKArgs ka) {
 
 }  // namespace
 
-hipError_t launch_reuse_mark(const Geometry& g, const StepArgs& a, const SeqScratch* sel_scr, hipStream_t st) {
-  MarkKArgs ka{a, sel_scr, g.top_k, g.mode, PlanParams{g.hot_slots, g.s_words, g.ring_rows, g.mode, g.clock ? 1 : 0}};
+hipError_t launch_reuse_mark(const Geometry& g, const StepArgs& a, const SeqScratch& sel0, int64_t sel_stride,
+                             hipStream_t st) {
+  MarkKArgs ka{a, sel0, sel_stride, g.top_k, g.mode, PlanParams{g.hot_slots, g.s_words, g.ring_rows, g.mode, g.clock ? 1 : 0}};
   return launch_k(reuse_mark_kernel, dim3((unsigned)a.R, (unsigned)a.n_seqs), dim3(kPlanThreads), 0, st, ka);
 }
 

@@ -58,12 +58,14 @@ struct dsa_session {
   std::string err;
   void* arena = nullptr;
   size_t arena_bytes = 0;
-  std::vector<void*> mirrors;              // host pointers (offload)
+  std::vector<void*> mirrors;              // host pointers into mirror_block (offload)
   std::vector<UnitDev> units;              // host copies of the device descriptors
   std::vector<SeqScratch> scr;
-  UnitDev* d_units = nullptr;              // inside the arena
-  SeqScratch* d_scr = nullptr;
-  SeqScratch* d_scr_pf = nullptr;          // the prefetch rounds' scratch set
+  std::vector<SeqScratch> scr_pf;          // host copy of the prefetch scratch set
+  int64_t u_stride = 0;                    // bytes between consecutive units' arena buffers
+  int64_t rows_stride = 0;                 // bytes between consecutive units' row stores
+  int64_t s_stride = 0, pf_stride = 0;     // bytes between consecutive sequences' scratch (main, prefetch)
+  void* mirror_block = nullptr;            // one pinned allocation holding every unit's mirror (offload)
   std::vector<UnitHost> uh;
   int last_layer = -1;
   int last_R = 0;
@@ -222,8 +224,8 @@ void free_all(dsa_session* s) {
   for (auto e : s->pf_done)
     if (e) (void)hipEventDestroy(e);
   s->pf_done.clear();
-  for (void* m : s->mirrors)
-    if (m) (void)hipHostFree(m);
+  if (s->mirror_block) (void)hipHostFree(s->mirror_block);
+  s->mirror_block = nullptr;
   if (s->arena) (void)hipFree(s->arena);
   s->uh.clear();
   s->timed.clear();
@@ -249,11 +251,19 @@ dsa_status finish_round(dsa_session* s, int32_t layer, hipStream_t stream) {
   return DSA_OK;
 }
 
-StepArgs step_args(const dsa_session* s, int32_t layer, int R, const SeqScratch* scr) {
-  StepArgs a;
-  a.units = s->d_units;
-  a.scr = scr;
-  a.unit_base = layer * s->cfg.n_seqs;
+// prefetch_set: the round runs on the prefetch scratch set (offload only).
+StepArgs step_args(const dsa_session* s, int32_t layer, int R, bool prefetch_set) {
+  StepArgs a{};
+  a.u0 = s->units[unit_index(s, layer, 0)];
+  if (prefetch_set) {
+    if (!s->scr_pf.empty()) a.s0 = s->scr_pf[0];
+    a.s_stride = s->pf_stride;
+  } else {
+    a.s0 = s->scr[0];
+    a.s_stride = s->s_stride;
+  }
+  a.u_stride = s->u_stride;
+  a.rows_stride = s->rows_stride;
   a.n_seqs = s->cfg.n_seqs;
   a.R = R;
   a.l_max = 0;
@@ -327,8 +337,6 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   // ---- arena layout (exact sizes, 256-byte aligned pieces)
   size_t cur = 0;
   auto take = [&](size_t bytes) { size_t at = cur; cur += align_up(bytes ? bytes : 1); return at; };
-  const size_t o_units = take(sizeof(UnitDev) * n_units);
-  const size_t o_scr = take(sizeof(SeqScratch) * cfg->n_seqs);
   struct UnitOff { size_t keys, rows, slots, ring, pos_slot, hot, slot_pos, fill, pin, ref, hand, dyn, totals; };
   std::vector<UnitOff> uo(n_units);
   for (int i = 0; i < n_units; ++i) {
@@ -378,7 +386,6 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   }
   // the prefetch rounds' scratch: only what the plan, the assign and the fill use
   struct PfOff { size_t cnt, info, uni, kind, src, selmask, hitmask, base_u, base_m, pdesc, victim, done; };
-  const size_t o_scr_pf = take(sizeof(SeqScratch) * cfg->n_seqs);
   std::vector<PfOff> pf(off ? cfg->n_seqs : 0);
   for (auto& x : pf) {
     x.cnt = take(8 * 8);
@@ -414,22 +421,28 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   if (hipMemset(s->arena, 0, s->arena_bytes) != hipSuccess) return bail(DSA_E_HIP, "hipMemset");
 
   s->mirrors.assign(n_units, nullptr);
+  uint8_t* mirror_dev = nullptr;
+  if (off) {
+    // every unit's mirror in one pinned, device-mapped block, at a stride of P rows
+    const size_t bytes = (size_t)n_units * P * rb;
+    if (hipHostMalloc(&s->mirror_block, bytes, hipHostMallocMapped) != hipSuccess || !s->mirror_block) {
+      s->mirror_block = nullptr;
+      (void)hipGetLastError();
+      return bail(DSA_E_NOMEM, "hipHostMalloc");
+    }
+    std::memset(s->mirror_block, 0, bytes);                  // touch every page once, before use
+    void* dp = nullptr;
+    if (hipHostGetDevicePointer(&dp, s->mirror_block, 0) != hipSuccess) return bail(DSA_E_HIP, "hipHostGetDevicePointer");
+    mirror_dev = static_cast<uint8_t*>(dp);
+  }
   s->units.resize(n_units);
   s->uh.resize(n_units);
   for (int i = 0; i < n_units; ++i) {
     UnitDev& u = s->units[i];
     u.keys = reinterpret_cast<uint16_t*>(base + uo[i].keys);
     if (off) {
-      void* hp = nullptr;
-      if (hipHostMalloc(&hp, (size_t)P * rb, hipHostMallocMapped) != hipSuccess || !hp) {
-        (void)hipGetLastError();
-        return bail(DSA_E_NOMEM, "hipHostMalloc");
-      }
-      s->mirrors[i] = hp;
-      std::memset(hp, 0, (size_t)P * rb);            // touch every page once, before use
-      void* dp = nullptr;
-      if (hipHostGetDevicePointer(&dp, hp, 0) != hipSuccess) return bail(DSA_E_HIP, "hipHostGetDevicePointer");
-      u.rows = static_cast<uint8_t*>(dp);
+      s->mirrors[i] = static_cast<uint8_t*>(s->mirror_block) + (size_t)i * P * rb;
+      u.rows = mirror_dev + (size_t)i * P * rb;
       u.slots = base + uo[i].slots;
       u.ring = base + uo[i].ring;
       u.pos_slot = reinterpret_cast<i32x2*>(base + uo[i].pos_slot);
@@ -481,7 +494,8 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     if (hipMemset(c.sel, 0xFF, (size_t)RK * 4) != hipSuccess || hipMemset(c.map, 0xFF, (size_t)RK * 4) != hipSuccess)
       return bail(DSA_E_HIP, "hipMemset");
   }
-  std::vector<SeqScratch> scr_pf(pf.size());
+  std::vector<SeqScratch>& scr_pf = s->scr_pf;
+  scr_pf.assign(pf.size(), SeqScratch{});
   for (size_t q = 0; q < pf.size(); ++q) {
     SeqScratch& c = scr_pf[q];                        // fields not listed stay NULL
     c.counters = reinterpret_cast<int64_t*>(base + pf[q].cnt);
@@ -497,9 +511,6 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     c.victim = reinterpret_cast<i32x2*>(base + pf[q].victim);
     c.done = reinterpret_cast<uint32_t*>(base + pf[q].done);
   }
-  s->d_units = reinterpret_cast<UnitDev*>(base + o_units);
-  s->d_scr = reinterpret_cast<SeqScratch*>(base + o_scr);
-  s->d_scr_pf = reinterpret_cast<SeqScratch*>(base + o_scr_pf);
   s->topk_L.assign(cfg->n_seqs, -1);
   // stream-to-stream ordering on this device only: a device-scope release suffices
   const unsigned order_flags = hipEventDisableTiming | hipEventReleaseToDevice;
@@ -509,12 +520,37 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   s->pf_stream.assign(cfg->n_layers, nullptr);
   for (auto& e : s->pf_done)
     if (hipEventCreateWithFlags(&e, order_flags) != hipSuccess) return bail(DSA_E_HIP, "event");
-  if (hipMemcpy(s->d_units, s->units.data(), sizeof(UnitDev) * n_units, hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(s->d_scr, s->scr.data(), sizeof(SeqScratch) * cfg->n_seqs, hipMemcpyHostToDevice) != hipSuccess ||
-      (!scr_pf.empty() &&
-       hipMemcpy(s->d_scr_pf, scr_pf.data(), sizeof(SeqScratch) * scr_pf.size(), hipMemcpyHostToDevice) != hipSuccess) ||
-      hipDeviceSynchronize() != hipSuccess)
-    return bail(DSA_E_HIP, "hipMemcpy");
+  // Kernels form sequence q's descriptors from sequence 0's and the strides:
+  // check that every descriptor is sequence 0's moved by q strides.
+  s->u_stride = n_units > 1 ? (int64_t)(uo[1].keys - uo[0].keys) : 0;
+  s->rows_stride = off ? (int64_t)P * rb : s->u_stride;
+  s->s_stride = cfg->n_seqs > 1 ? (int64_t)(so[1].scores - so[0].scores) : 0;
+  s->pf_stride = pf.size() > 1 ? (int64_t)(pf[1].cnt - pf[0].cnt) : 0;
+  auto strided = [](const void* d0, const void* dq, int64_t q, int64_t stride, size_t bytes) {
+    uint64_t a[64], b[64];
+    std::memcpy(a, d0, bytes);
+    std::memcpy(b, dq, bytes);
+    for (size_t i = 0; i < bytes / 8; ++i)
+      if ((a[i] == 0) != (b[i] == 0) || (a[i] && b[i] != a[i] + (uint64_t)(q * stride))) return false;
+    return true;
+  };
+  static_assert(sizeof(UnitDev) <= 64 * 8 && sizeof(SeqScratch) <= 64 * 8, "descriptor check buffers");
+  const size_t rows_word = offsetof(UnitDev, rows) / 8;
+  for (int i = 0; i < n_units; ++i) {
+    UnitDev moved = s->units[i];
+    const int q = i % cfg->n_seqs, l0 = i - q;                       // unit (layer, 0) is index l0
+    uint64_t w[sizeof(UnitDev) / 8];
+    std::memcpy(w, &moved, sizeof(w));
+    w[rows_word] = w[rows_word] ? w[rows_word] - (uint64_t)(q * s->rows_stride) + (uint64_t)(q * s->u_stride) : 0;
+    std::memcpy(&moved, w, sizeof(w));
+    if (!strided(&s->units[l0], &moved, q, s->u_stride, sizeof(UnitDev)))
+      return bail(DSA_E_UNSUPPORTED, "unit descriptors are not strided");
+  }
+  for (int q = 0; q < cfg->n_seqs; ++q)
+    if (!strided(&s->scr[0], &s->scr[q], q, s->s_stride, sizeof(SeqScratch)) ||
+        (!scr_pf.empty() && !strided(&scr_pf[0], &scr_pf[q], q, s->pf_stride, sizeof(SeqScratch))))
+      return bail(DSA_E_UNSUPPORTED, "scratch descriptors are not strided");
+  if (hipDeviceSynchronize() != hipSuccess) return bail(DSA_E_HIP, "hipDeviceSynchronize");
   *out = s;
   return DSA_OK;
 }
@@ -666,13 +702,7 @@ dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq, 
     l_max = std::max(l_max, h.L);
   }
   DeviceGuard dg(s->device);
-  StepArgs a;
-  a.units = s->d_units;
-  a.scr = s->d_scr;
-  a.unit_base = layer * n_seqs;
-  a.n_seqs = n_seqs;
-  a.R = R;
-  a.l_max = l_max;
+  const StepArgs a = step_args(s, layer, R, false);
   const Geometry& g = s->g;
   const uint16_t* iq = static_cast<const uint16_t*>(index_q);
   const uint16_t* ql = static_cast<const uint16_t*>(q_latent);
@@ -705,7 +735,7 @@ dsa_status dsa_decode_step_reuse(dsa_session* s, int32_t layer, int32_t src_laye
   if (!q_latent || !q_rope || !out || !aligned(q_latent, 16) || !aligned(q_rope, 16) || !aligned(out, 4))
     return fail(s, DSA_E_INVALID, "step buffers must be non-NULL; bf16 inputs 16-byte aligned");
   DeviceGuard dg(s->device);
-  const StepArgs a = step_args(s, layer, rows_per_seq, s->d_scr);
+  const StepArgs a = step_args(s, layer, rows_per_seq, false);
   const Geometry& g = s->g;
   const uint16_t* ql = static_cast<const uint16_t*>(q_latent);
   const uint16_t* qr = static_cast<const uint16_t*>(q_rope);
@@ -713,7 +743,7 @@ dsa_status dsa_decode_step_reuse(dsa_session* s, int32_t layer, int32_t src_laye
     if (s->pf_stream[layer] != stream) HIPCHK(hipStreamWaitEvent(stream, s->pf_done[layer], 0), "hipStreamWaitEvent");
     s->pf_pending[layer] = 0;
   }
-  if ((st = timed_launch(s, KK_TOPK_SELECT, "reuse mark", [&] { return launch_reuse_mark(g, a, s->d_scr, stream); })) != DSA_OK)
+  if ((st = timed_launch(s, KK_TOPK_SELECT, "reuse mark", [&] { return launch_reuse_mark(g, a, s->scr[0], s->s_stride, stream); })) != DSA_OK)
     return st;
   if ((st = timed_launch(s, KK_GATHER, "gather", [&] { return launch_gather(g, a, stream); })) != DSA_OK) return st;
   if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream); })) != DSA_OK) return st;
@@ -729,14 +759,14 @@ dsa_status dsa_prefetch_reuse(dsa_session* s, int32_t layer, int32_t src_layer, 
   if (st != DSA_OK) return st;
   if (s->g.mode != DSA_KV_OFFLOAD) return DSA_OK;
   DeviceGuard dg(s->device);
-  const StepArgs a = step_args(s, layer, rows_per_seq, s->d_scr_pf);
+  const StepArgs a = step_args(s, layer, rows_per_seq, true);
   const Geometry& g = s->g;
   if (s->sel_waited != stream || s->sel_waited_epoch != s->sel_epoch) {   // the selection is final
     HIPCHK(hipStreamWaitEvent(stream, s->sel_ready, 0), "hipStreamWaitEvent");
     s->sel_waited = stream;
     s->sel_waited_epoch = s->sel_epoch;
   }
-  HIPCHK(launch_reuse_mark(g, a, s->d_scr, stream), "prefetch mark");
+  HIPCHK(launch_reuse_mark(g, a, s->scr[0], s->s_stride, stream), "prefetch mark");
   HIPCHK(launch_gather(g, a, stream, false), "prefetch assign");
   HIPCHK(launch_prefetch_fill(g, a, stream), "prefetch fill");
   HIPCHK(hipEventRecord(s->pf_done[layer], stream), "hipEventRecord");
