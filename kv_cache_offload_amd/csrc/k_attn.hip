@@ -378,81 +378,99 @@ struct MergeKArgs {
   int H, ns_stride;
 };
 
-// One workgroup per (16-dim tile nt, 16-head group hg, query row), for at most
+// One workgroup per (16-dim tile nt, group of HW heads, query row), for at most
 // MAXS splits:
 // out[h][d] = sum_s w_s[h] O_s[h][d] with w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s'.
-// Thread (l16, hl) reads element (l16, 16 hg + hl) of each split's [16][H] tile;
-// the sums leave through LDS as [h][16] (16 contiguous floats per head).
-template <int MAXS>
+// A split's [16][H] tile of dims nt has rows of H floats; the workgroup reads
+// the HW-head part of each row (whole 128-byte lines for HW = 32), EPT
+// consecutive floats per thread.  The sums leave through LDS as [h][16] (16
+// contiguous floats per head).
+template <int MAXS, int HW>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
-  __shared__ float wgt[MAXS * 16];            // [split][hl]: the max, then the weight
-  __shared__ float sl[MAXS * 16];             // [split][hl]: the sum
-  __shared__ float tile[16 * 17];
+  constexpr int EPT = 16 * HW / 256;          // tile elements per thread
+  constexpr int TPH = 256 / HW;               // threads per head in the weight pass
+  constexpr int kPer = (MAXS + TPH - 1) / TPH;
+  static_assert(EPT >= 1 && 16 * HW == 256 * EPT, "tile of 16 x HW floats over 256 threads");
+  __shared__ float wgt[MAXS * HW];            // [split][head]: the max, then the weight
+  __shared__ float sl[MAXS * HW];             // [split][head]: the sum
+  __shared__ float tile[HW * 17];
   const StepArgs& a = ka.a;
-  const int n_hg = ka.H / 16;
+  const int n_hg = ka.H / HW;
   const int nt = blockIdx.x / n_hg, hg = blockIdx.x % n_hg, r = blockIdx.y, seq = blockIdx.z;
   const ScratchG s = scratch_of(a, seq);
   const int H = ka.H;
   const int used = min(MAXS, (s.sel_n[r] + kSplit - 1) / kSplit);
   if (used < 1) return;                                  // (uniform) no selection: nothing to merge
   const int tid = threadIdx.x;
-  const int l16 = tid / 16, hl = tid % 16;
-  // this thread's element of every split, loaded before the weights are known
+  const int e0 = tid * EPT, l16 = e0 / HW, hl0 = e0 % HW;
+  // this thread's elements of every split, loaded before the weights are known
   // (splits past `used` re-read the last one and get weight 0)
-  const auto src = s.part_o + (((int64_t)r * ka.ns_stride * 32 + nt) * 16 + l16) * H + 16 * hg + hl;
+  const auto src = s.part_o + (((int64_t)r * ka.ns_stride * 32 + nt) * 16 + l16) * H + HW * hg + hl0;
   const int64_t split_stride = (int64_t)32 * 16 * H;
-  float x[MAXS];
+  float x[MAXS][EPT];
 #pragma unroll
-  for (int sp = 0; sp < MAXS; ++sp) x[sp] = src[(sp < used ? sp : used - 1) * split_stride];
-  for (int t = tid; t < used * 16; t += 256) {            // every split's (max, sum) at once
-    const int sp = t / 16, h = t % 16;
-    const int64_t base = ((int64_t)r * ka.ns_stride + sp) * H + 16 * hg + h;
+  for (int sp = 0; sp < MAXS; ++sp) {
+    const auto at = src + (sp < used ? sp : used - 1) * split_stride;
+    if constexpr (EPT == 2) {
+      const u32x2 v = *reinterpret_cast<const DSA_GLOBAL u32x2*>(at);
+      x[sp][0] = __uint_as_float(v.x);
+      x[sp][1] = __uint_as_float(v.y);
+    } else {
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) x[sp][k] = at[k];
+    }
+  }
+  for (int t = tid; t < used * HW; t += 256) {           // every split's (max, sum) at once
+    const int sp = t / HW, h = t % HW;
+    const int64_t base = ((int64_t)r * ka.ns_stride + sp) * H + HW * hg + h;
     wgt[t] = s.part_ml[base * 2];
     sl[t] = s.part_ml[base * 2 + 1];
   }
   __syncthreads();
   {
-    // the weights of head wh: its 16 threads (one wave quarter) take the splits
-    // c, c + 16, ..., then reduce the max and the denominator by shuffles
-    constexpr int kPer = (MAXS + 15) / 16;
-    const int wh = tid >> 4, c = tid & 15;
+    // the weights of head wh: its TPH threads take the splits c, c + TPH, ...,
+    // then reduce the max and the denominator by shuffles
+    const int wh = tid / TPH, c = tid % TPH;
     float mloc[kPer];
     float M = -INFINITY;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-      const int sp = c + 16 * e;
-      mloc[e] = sp < used ? wgt[sp * 16 + wh] : -INFINITY;
+      const int sp = c + TPH * e;
+      mloc[e] = sp < used ? wgt[sp * HW + wh] : -INFINITY;
       M = fmaxf(M, mloc[e]);
     }
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    for (int o = 1; o < TPH; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
     float wloc[kPer];
     float den = 0.f;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-      const int sp = c + 16 * e;
+      const int sp = c + TPH * e;
       wloc[e] = (sp < used && M != -INFINITY) ? exp2f(mloc[e] - M) : 0.f;
-      if (sp < used) den += wloc[e] * sl[sp * 16 + wh];
+      if (sp < used) den += wloc[e] * sl[sp * HW + wh];
     }
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) den += __shfl_xor(den, o);
+    for (int o = 1; o < TPH; o <<= 1) den += __shfl_xor(den, o);
     const float inv = den > 0.f ? 1.f / den : 0.f;
     __syncthreads();                                   // every max read before any weight is written
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
-      const int sp = c + 16 * e;
-      if (sp < used) wgt[sp * 16 + wh] = wloc[e] * inv;
+      const int sp = c + TPH * e;
+      if (sp < used) wgt[sp * HW + wh] = wloc[e] * inv;
     }
   }
   __syncthreads();
-  float acc = 0.f;
 #pragma unroll
-  for (int sp = 0; sp < MAXS; ++sp) acc += (sp < used ? wgt[sp * 16 + hl] : 0.f) * x[sp];
-  tile[hl * 17 + l16] = acc;
+  for (int k = 0; k < EPT; ++k) {
+    float acc = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < MAXS; ++sp) acc += (sp < used ? wgt[sp * HW + hl0 + k] : 0.f) * x[sp][k];
+    tile[(hl0 + k) * 17 + l16] = acc;
+  }
   __syncthreads();
-  {
-    const int h2 = tid / 16, d2 = tid % 16;
-    ka.out[(((int64_t)seq * a.R + r) * H + 16 * hg + h2) * 512 + nt * 16 + d2] = tile[h2 * 17 + d2];
+  for (int t = tid; t < HW * 16; t += 256) {
+    const int h2 = t / 16, d2 = t % 16;
+    ka.out[(((int64_t)seq * a.R + r) * H + HW * hg + h2) * 512 + nt * 16 + d2] = tile[h2 * 17 + d2];
   }
 }
 
@@ -476,10 +494,15 @@ hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_l
 hipError_t launch_attn_merge(const Geometry& g, const StepArgs& a, float* out, hipStream_t st) {
   if ((g.top_k + kSplit - 1) / kSplit == 1) return hipSuccess;
   MergeKArgs ka{a, out, g.heads, g.nsplit_max};
-  const dim3 grid(32u * (unsigned)(g.heads / 16), (unsigned)a.R, (unsigned)a.n_seqs);
   const int nsplit = (g.top_k + kSplit - 1) / kSplit;
-  if (nsplit <= 32) return launch_k(attn_merge_kernel<32>, grid, dim3(256), 0, st, ka);
-  return launch_k(attn_merge_kernel<kMaxSplits>, grid, dim3(256), 0, st, ka);
+  if (g.heads == 16) {                                   // one 16-head group
+    const dim3 grid(32u, (unsigned)a.R, (unsigned)a.n_seqs);
+    if (nsplit <= 32) return launch_k(attn_merge_kernel<32, 16>, grid, dim3(256), 0, st, ka);
+    return launch_k(attn_merge_kernel<kMaxSplits, 16>, grid, dim3(256), 0, st, ka);
+  }
+  const dim3 grid(32u * (unsigned)(g.heads / 32), (unsigned)a.R, (unsigned)a.n_seqs);
+  if (nsplit <= 32) return launch_k(attn_merge_kernel<32, 32>, grid, dim3(256), 0, st, ka);
+  return launch_k(attn_merge_kernel<kMaxSplits, 32>, grid, dim3(256), 0, st, ka);
 }
 
 }  // namespace dsa
