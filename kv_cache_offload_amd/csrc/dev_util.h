@@ -14,12 +14,26 @@ __device__ inline uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// v plus the same register of another lane chosen by a DPP control: lanes
+// whose source is outside the row (row_shr) or whose row is masked off
+// (row_bcast) add 0.
+template <int CTRL, int ROW_MASK>
+__device__ inline uint32_t dpp_add(uint32_t v) {
+  return v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Inclusive scan over the 64 lanes of a wave, on DPP (no LDS traffic): shifts
+// by 1, 2, 4, 8 within each 16-lane row, then lane 15 of each row into the next
+// (rows 1 and 3) and lane 31 into rows 2 and 3.  Every lane of the wave must be
+// active.  (lane: unused, kept for the callers.)
 __device__ inline uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
+  (void)lane;
+  v = dpp_add<0x111, 0xf>(v);   // row_shr:1
+  v = dpp_add<0x112, 0xf>(v);   // row_shr:2
+  v = dpp_add<0x114, 0xf>(v);   // row_shr:4
+  v = dpp_add<0x118, 0xf>(v);   // row_shr:8
+  v = dpp_add<0x142, 0xa>(v);   // row_bcast:15
+  v = dpp_add<0x143, 0xc>(v);   // row_bcast:31
   return v;
 }
 
