@@ -71,9 +71,14 @@ PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
 def source_hash(kind):
+    """Hash of a kernel group's source file and of every header the kernels include."""
+    import glob
     import hashlib
-    path = os.path.join(ROOT, "kv_cache_offload_amd", "csrc", KERNEL_SOURCES[kind])
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    csrc = os.path.join(ROOT, "kv_cache_offload_amd", "csrc")
+    h = hashlib.sha256()
+    for path in [os.path.join(csrc, KERNEL_SOURCES[kind])] + sorted(glob.glob(os.path.join(csrc, "*.h"))):
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def pmc_traffic(workload, kind):
