@@ -323,10 +323,13 @@ dsa_status dsa_debug_get(dsa_session* s, int32_t layer, int32_t seq, int32_t ite
  *     pass before it for histories longer than 65,536 positions)
  *   2 Top-K resolve (selection, union marks, cache classification, then the
  *     gather plan of each sequence)
- *   3 gather (slot table update, row copies to the compact buffer and the hot
- *     slots, ring writeback)
- *   4 attention
- *   5 attention merge (absent when one split covers the selection)
+ *   3 gather (unused in decode steps, count 0: the slot work runs in the
+ *     launch of kind 5, the row copies in kind 4)
+ *   4 attention (row copies from their sources into the compact buffer and
+ *     the filled slots, then attention)
+ *   5 attention merge and the gather's assign pass in one launch (slot table
+ *     update, union entries, histogram clears, ring writeback); the merge
+ *     part is absent when one split covers the selection
  *   6 append (dsa_append_rows)
  * dsa_set_kernel_timing: enable <= 0 turns timing off; enable > 0 turns it on
  * and pre-creates the events of `enable` decode steps (at most 2^18), so that

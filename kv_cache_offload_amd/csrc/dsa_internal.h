@@ -201,6 +201,8 @@ hipError_t prepare_topk_kernels();
 hipError_t launch_gather(const Geometry& g, const StepArgs& a, hipStream_t st, bool clear_hist = true);
 hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_lat,
                        const uint16_t* q_rope, float* out, hipStream_t st);
+// The split merge (skipped when one split covers the selection) and, in the
+// same launch, the gather's assign pass.
 hipError_t launch_attn_merge(const Geometry& g, const StepArgs& a, float* out, hipStream_t st);
 
 // Unit maintenance (one unit per launch).

@@ -1,0 +1,155 @@
+// gather_assign.h -- the assign pass of the hot gather, after the plan.
+//
+// Page "From 1M total to 15+ streams x 1M: the capacity breakthrough of
+// GLM-5.3 KV cache offload", section "GPU cache management errs too": a hit's
+// slot is pinned for the round; the k-th miss in ascending position order takes
+// the plan's k-th victim, evicting the position that slot held; section
+// "Decision 2": the recent ring goes back to the mirror in 64-row batches.
+// One wave per 64 positions, one lane per position: each selected lane writes
+// its union entry (position, kind, source) and descriptor and does its slot
+// work.  Further blocks clear the step's Top-K histograms and write a due ring
+// batch back.  It runs as its own kernel (prefetch rounds) or as extra
+// workgroups of the attention merge (decode steps), after attention: the
+// attention kernel derives its rows' sources from the plan's outputs, and no
+// reader of this round consults what this pass writes.
+#pragma once
+
+#include "gather_plan.h"
+
+namespace dsa {
+
+constexpr int kGatherThreads = 256;
+
+struct GatherKArgs {
+  StepArgs a;
+  int S, ring_cap, ring_rows, mode, row_bytes, K;
+  int max_union;                        // R_max * K: compact rows in the scratch
+  int word_blocks;                      // blocks of the union/slot-table part
+  int clear_blocks;                     // then blocks clearing the Top-K histograms; the rest write back the ring
+  int r_max;
+  int clock;                            // CLOCK replacement: hits and fills set their slot's reference bit
+  int64_t max_positions;
+};
+
+// Union entries and slot table: one wave per 64 positions, one lane per position.
+// The last blocks write the 64 oldest pending ring rows back to the host mirror
+// when a batch is due (positions the step reads from the ring, never from the
+// mirror).
+__device__ inline void assign_block(const GatherKArgs& ka, int block, int seq) {
+  const StepArgs& a = ka.a;
+  const UnitG u = unit_of(a, seq);
+  const ScratchG s = scratch_of(a, seq);
+  if ((int)block >= ka.word_blocks && (int)block < ka.word_blocks + ka.clear_blocks) {
+    // the Top-K histograms of this step's rows, consumed: zero for the next step
+    const int64_t t = (int64_t)(block - ka.word_blocks) * kGatherThreads + threadIdx.x;
+    const int64_t n0 = (int64_t)kHistReps * a.R * (kRadixBins / 4), n1 = (int64_t)a.R * (kRadixBins / 4);
+    if (t < n0) {
+      const int64_t q = t / (a.R * (kRadixBins / 4)), rest = t % (a.R * (kRadixBins / 4));
+      reinterpret_cast<DSA_GLOBAL u32x4*>(s.hist0 + q * ka.r_max * kRadixBins)[rest] = (u32x4){0u, 0u, 0u, 0u};
+    } else if (t < n0 + n1) {
+      reinterpret_cast<DSA_GLOBAL u32x4*>(s.hist1)[t - n0] = (u32x4){0u, 0u, 0u, 0u};
+    }
+    return;
+  }
+  if ((int)block >= ka.word_blocks) {
+    const int64_t wb = s.info[kInfoWriteback];
+    if (wb < 0) return;
+    const int64_t t = (int64_t)(block - ka.word_blocks - ka.clear_blocks) * kGatherThreads + threadIdx.x;
+    if (t >= (int64_t)ka.ring_rows * kCopyChunks16) return;
+    const int64_t rb = ka.row_bytes;
+    const int64_t p = wb + t / kCopyChunks16, c = t % kCopyChunks16;
+    if (p >= ka.max_positions) return;
+    const u32x4 v = *reinterpret_cast<const DSA_GLOBAL u32x4*>(u.ring + (p % ka.ring_cap) * rb + c * 16);
+    *reinterpret_cast<DSA_GLOBAL u32x4*>(u.rows + p * rb + c * 16) = v;
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int64_t wave_id = ((int64_t)block * kGatherThreads + threadIdx.x) >> 6;
+  const int64_t L = u.dyn[0];
+  const int64_t nw = (L + 31) / 32;
+  if (2 * wave_id >= nw) return;
+  const int64_t w = 2 * wave_id + (lane >> 5);        // this lane's 32-position word
+  const int64_t M = s.info[kInfoM];
+  const int32_t round = (int32_t)s.info[kInfoRound];
+  const uint32_t n_assigned = (uint32_t)s.info[kInfoAssigned];
+  const bool off = ka.mode == 0;
+  const int bitpos = lane & 31;
+  const uint32_t bit = 1u << bitpos;
+  const int64_t p = w * 32 + bitpos;
+
+  const int64_t wc = w < nw ? w : nw - 1;
+  uint32_t sw = s.selmask[wc], hw = s.hitmask[wc];    // both loads in flight together
+  const uint32_t bu = s.base_u[wc], bm = s.base_m[wc];
+  if (w >= nw) sw = 0;
+  if (!off) hw = 0;
+  const bool mine = (sw & bit) != 0;
+  const uint64_t selb = __ballot(mine);
+  if (!selb) return;
+  if (bitpos == 0 && sw) s.selmask[w] = 0;             // read by every lane above: clear for the next step
+  if (mine) {
+    const uint32_t below = bit - 1u;
+    const uint32_t ux = bu + __popc(sw & below);
+    int32_t kind, src, fill = -1;
+    if (!off) {
+      kind = SRC_RES;
+      src = (int32_t)p;
+    } else {
+      const uint32_t rw = sw & ring_bits(w, M);
+      if (rw & bit) {
+        kind = SRC_RING;
+        src = (int32_t)(p % ka.ring_cap);
+      } else if (hw & bit) {
+        kind = SRC_HIT;                                // the hit's slot is pinned for this round
+        src = u.pos_slot[p].x;
+        if (src >= 0 && src < ka.S) {
+          u.pin_round[src] = round;
+          if (ka.clock) g_or(&u.ref[src >> 5], 1u << (src & 31));
+        }
+      } else {
+        const uint32_t k = bm + __popc(sw & ~hw & ~rw & below);
+        src = (int32_t)p;
+        if (k < n_assigned) {
+          kind = SRC_MISS;
+          const i32x2 vo = s.victim[k];                // (slot, position it held), from the plan
+          const int32_t v = vo.x, old = vo.y;
+          if (v >= 0 && v < ka.S) {
+            if (old >= 0 && old < ka.max_positions) {
+              u.pos_slot[old] = (i32x2){-1, -1};
+              __hip_atomic_fetch_and(&u.hot[old >> 5], ~(1u << (old & 31)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            u.slot_pos[v] = (int32_t)p;
+            u.pos_slot[p] = (i32x2){v, round};
+            g_or(&u.hot[p >> 5], bit);
+            u.fill_round[v] = round;
+            u.pin_round[v] = round;
+            if (ka.clock) g_or(&u.ref[v >> 5], 1u << (v & 31));
+            fill = v;
+          }
+        } else {
+          kind = SRC_MISS_NOSLOT;
+        }
+      }
+    }
+    if (ux < (uint32_t)ka.max_union) {                 // always true for a consistent plan
+      s.uni[ux] = (int32_t)p;
+      s.kind[ux] = kind;
+      s.src[ux] = src;
+      s.pdesc[p] = (i32x4){(int32_t)ux, kind, src, fill};
+    }
+  }
+}
+
+// Arguments and the number of blocks per sequence of the assign pass.
+inline GatherKArgs gather_args(const Geometry& g, const StepArgs& a, bool clear_hist, int64_t* blocks_per_seq) {
+  const int64_t words = (a.l_max + 31) / 32;
+  const int64_t waves = (words + 1) / 2;
+  const int64_t blocks = (waves + 3) / 4;
+  const int64_t wb_blocks = ((int64_t)g.ring_rows * kCopyChunks16 + kGatherThreads - 1) / kGatherThreads;
+  const int64_t clear_blocks =
+      clear_hist ? ((int64_t)(kHistReps + 1) * a.R * (kRadixBins / 4) + kGatherThreads - 1) / kGatherThreads : 0;
+  *blocks_per_seq = blocks + clear_blocks + (g.mode == 0 ? wb_blocks : 0);
+  return GatherKArgs{a, g.hot_slots, g.ring_cap, g.ring_rows, g.mode, g.row_bytes, g.top_k, g.r_max * g.top_k,
+                     (int)blocks, (int)clear_blocks, g.r_max, g.clock ? 1 : 0, g.max_positions};
+}
+
+}  // namespace dsa

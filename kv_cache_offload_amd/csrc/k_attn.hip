@@ -31,7 +31,7 @@
 //     column per lane).
 // Each workgroup writes (max, sum, unnormalised O) and a merge kernel combines
 // the splits with the log-sum-exp rule.
-#include "dsa_internal.h"
+#include "gather_assign.h"
 
 namespace dsa {
 namespace {
@@ -60,6 +60,7 @@ struct AttnKArgs {
   float* out;                // [n_seqs][R][H][512]
   int K, H, nsplit, ns_stride, row_bytes;
   int S, ring_cap, max_union;
+  int off;                   // offload mode (hot slots, ring, host mirror)
   int64_t max_positions;
   float scale_log2;          // softmax_scale * log2(e)
 };
@@ -126,33 +127,53 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   const int64_t rb = ka.row_bytes;
   const int j_begin = split * kSplit;
 
-  // The split's rows: position (selection), then the gather's descriptor of the
-  // position -- compact row, source kind, source index, slot to fill -- from
-  // which the row's address follows: a hit from its HBM slot, a ring row from
-  // the recent ring, a miss from the host mirror (repeated misses of the same
-  // round each read host memory), a resident row from the HBM row store.  The
-  // map entry of every selected index of the split is written here.
+  // The split's rows: position (selection), then the row's place in the
+  // round, derived from the gather plan's outputs exactly as the assign pass
+  // derives it -- union index from the word's union count and the selected bits
+  // below, kind from the ring boundary M and the hit bits, and the source: a
+  // hit from its HBM slot (the position's slot), a ring row from the recent
+  // ring, a miss from the host mirror (repeated misses of the same round each
+  // read host memory; the k-th miss fills the plan's k-th victim slot), a
+  // resident row from the HBM row store.  The map entry of every selected index
+  // of the split is written here.
   const int n_sel = s.sel_n[r];
   if (tid < kSplit) {
+    const int64_t M = s.info[kInfoM];
+    const uint32_t n_assigned = (uint32_t)s.info[kInfoAssigned];
     const int j = j_begin + tid;
     const int32_t pos = j < ka.K ? s.sel[(int64_t)r * ka.K + j] : -1;
     const bool ok = j < n_sel && pos >= 0 && pos < ka.max_positions;
-    const i32x4 d = s.pdesc[ok ? pos : 0];
-    const int32_t ux = d.x, kind = d.y, src = d.z, fill = d.w;
+    const int64_t w = ok ? pos >> 5 : 0;
+    const uint32_t sw = s.selmask[w], hw = ka.off ? s.hitmask[w] : 0u;
+    const uint32_t bu = s.base_u[w], bm = s.base_m[w];
+    const uint32_t bit = 1u << (pos & 31), below = bit - 1u;
+    const uint32_t ux = bu + __popc(sw & below);
     const DSA_GLOBAL uint8_t* from = nullptr;
-    if (ok && ux >= 0 && ux < ka.max_union) {
-      if (kind == SRC_HIT) {
-        if (src >= 0 && src < ka.S) from = u.slots + (int64_t)src * rb;
-      } else if (kind == SRC_RING) {
-        if (src >= 0 && src < ka.ring_cap) from = u.ring + (int64_t)src * rb;
-      } else if (kind == SRC_MISS || kind == SRC_MISS_NOSLOT || kind == SRC_RES) {
-        if (src >= 0 && src < ka.max_positions) from = u.rows + (int64_t)src * rb;
+    int32_t fill = -1;
+    if (ok && (sw & bit) && ux < (uint32_t)ka.max_union) {
+      if (!ka.off) {
+        from = u.rows + (int64_t)pos * rb;
+      } else {
+        const uint32_t rw = sw & ring_bits(w, M);
+        if (rw & bit) {
+          from = u.ring + (int64_t)(pos % ka.ring_cap) * rb;
+        } else if (hw & bit) {
+          const int32_t slot = u.pos_slot[pos].x;
+          if (slot >= 0 && slot < ka.S) from = u.slots + (int64_t)slot * rb;
+        } else {
+          const uint32_t k = bm + __popc(sw & ~hw & ~rw & below);
+          if (k < n_assigned) {
+            const int32_t v = s.victim[k].x;
+            if (v >= 0 && v < ka.S) fill = v;
+          }
+          from = u.rows + (int64_t)pos * rb;
+        }
       }
     }
     s_from[tid] = from;
-    s_ux[tid] = from ? ux : -1;
-    s_fill[tid] = (from && kind == SRC_MISS && fill >= 0 && fill < ka.S) ? fill : -1;
-    if (j < ka.K) s.map[(int64_t)r * ka.K + j] = from ? ux : -1;
+    s_ux[tid] = from ? (int)ux : -1;
+    s_fill[tid] = from ? fill : -1;
+    if (j < ka.K) s.map[(int64_t)r * ka.K + j] = from ? (int)ux : -1;
   }
   if (j_begin >= n_sel) return;                          // (uniform) map entries written above
   const int nrows = min(n_sel - j_begin, kSplit);
@@ -373,13 +394,16 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
 }
 
 struct MergeKArgs {
-  StepArgs a;
+  GatherKArgs ga;            // the assign pass (ga.a: the step's arguments)
   float* out;
   int H, ns_stride;
+  int merge_blocks;          // merge workgroups per sequence; the rest of a row of the grid assign
 };
 
-// One workgroup per (16-dim tile nt, group of HW heads, query row), for at most
-// MAXS splits:
+// Workgroups [0, merge_blocks) of each sequence merge; the others run the
+// gather's assign pass (gather_assign.h), which nothing in the round waits for.
+// One merge workgroup per (16-dim tile nt, group of HW heads, query row), for
+// at most MAXS splits:
 // out[h][d] = sum_s w_s[h] O_s[h][d] with w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s'.
 // A split's [16][H] tile of dims nt has rows of H floats; the workgroup reads
 // the HW-head part of each row (whole 128-byte lines for HW = 32), EPT
@@ -394,9 +418,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
   __shared__ float wgt[MAXS * HW];            // [split][head]: the max, then the weight
   __shared__ float sl[MAXS * HW];             // [split][head]: the sum
   __shared__ float tile[HW * 17];
-  const StepArgs& a = ka.a;
+  const StepArgs& a = ka.ga.a;
+  const int seq = blockIdx.y;
+  if ((int)blockIdx.x >= ka.merge_blocks) {             // (uniform) an assign workgroup
+    assign_block(ka.ga, (int)blockIdx.x - ka.merge_blocks, seq);
+    return;
+  }
   const int n_hg = ka.H / HW;
-  const int nt = blockIdx.x / n_hg, hg = blockIdx.x % n_hg, r = blockIdx.y, seq = blockIdx.z;
+  const int r = blockIdx.x / (32 * n_hg), rem = blockIdx.x % (32 * n_hg);
+  const int nt = rem / n_hg, hg = rem % n_hg;
   const ScratchG s = scratch_of(a, seq);
   const int H = ka.H;
   const int used = min(MAXS, (s.sel_n[r] + kSplit - 1) / kSplit);
@@ -480,7 +510,8 @@ hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_l
                        float* out, hipStream_t st) {
   const int nsplit = (g.top_k + kSplit - 1) / kSplit;
   AttnKArgs ka{a, q_lat, q_rope, out, g.top_k, g.heads, nsplit, g.nsplit_max, g.row_bytes,
-               g.hot_slots, g.ring_cap, g.r_max * g.top_k, g.max_positions, g.softmax_scale * 1.4426950408889634f};
+               g.hot_slots, g.ring_cap, g.r_max * g.top_k, g.mode == 0 ? 1 : 0, g.max_positions,
+               g.softmax_scale * 1.4426950408889634f};
   dim3 grid((unsigned)nsplit, (unsigned)a.R, (unsigned)a.n_seqs);
   switch (g.heads) {
     case 16: return launch_k(attn_kernel<1>, grid, dim3(64), 0, st, ka);
@@ -492,15 +523,18 @@ hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_l
 }
 
 hipError_t launch_attn_merge(const Geometry& g, const StepArgs& a, float* out, hipStream_t st) {
-  if ((g.top_k + kSplit - 1) / kSplit == 1) return hipSuccess;
-  MergeKArgs ka{a, out, g.heads, g.nsplit_max};
+  int64_t assign_blocks = 0;
+  const GatherKArgs ga = gather_args(g, a, true, &assign_blocks);
   const int nsplit = (g.top_k + kSplit - 1) / kSplit;
-  if (g.heads == 16) {                                   // one 16-head group
-    const dim3 grid(32u, (unsigned)a.R, (unsigned)a.n_seqs);
+  const int HW = g.heads == 16 ? 16 : 32;
+  const int merge_blocks = nsplit == 1 ? 0 : 32 * (g.heads / HW) * a.R;   // one split: attention wrote out
+  MergeKArgs ka{ga, out, g.heads, g.nsplit_max, merge_blocks};
+  const dim3 grid((unsigned)(merge_blocks + assign_blocks), (unsigned)a.n_seqs);
+  static_assert(kGatherThreads == 256, "assign and merge workgroups share the launch");
+  if (HW == 16) {
     if (nsplit <= 32) return launch_k(attn_merge_kernel<32, 16>, grid, dim3(256), 0, st, ka);
     return launch_k(attn_merge_kernel<kMaxSplits, 16>, grid, dim3(256), 0, st, ka);
   }
-  const dim3 grid(32u * (unsigned)(g.heads / 32), (unsigned)a.R, (unsigned)a.n_seqs);
   if (nsplit <= 32) return launch_k(attn_merge_kernel<32, 32>, grid, dim3(256), 0, st, ka);
   return launch_k(attn_merge_kernel<kMaxSplits, 32>, grid, dim3(256), 0, st, ka);
 }

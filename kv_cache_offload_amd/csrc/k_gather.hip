@@ -15,151 +15,33 @@
 //   * section "Capacity must survive the session lifecycle": flush before the
 //     full history is exported.
 //
-// gfx950 design.  Selection, classification and pinning happen where the
-// selection is produced: the Top-K kernel sets, for every selected position, a
-// bit in a per-position selection bitmap (a position several rows select is
-// one union entry), classifies it against the round-start state (a hit needs a
-// slot filled in an earlier round) and pins the hit's slot.  The last Top-K
-// workgroup of the sequence then runs the gather plan (gather_plan.h): prefix
-// counts per 32-position word and the victim list.  The assign kernel is wide:
-// one wave per 64 positions, one lane per position.  Each selected lane
-// computes its union index, kind and source; the k-th miss in ascending
-// position order takes victim[k], evicts the position the slot held and
-// updates the slot table; the lane leaves a descriptor of the position (union
-// index, kind, source, slot to fill).  The row copies themselves are done by
-// the attention kernel while it stages the rows (k_attn.hip): one 16-byte
-// piece per thread, from the hot slot, the ring, or the host mirror (zero-copy
-// reads of pinned host memory over the host link; a miss that several query
-// rows select is read from host memory by each of them, as the page's rule for
-// repeated misses has it), to LDS, the compact buffer and, for a miss that got
-// a slot, to the slot.  No reader consults a slot filled in the same round:
-// victims are unpinned, hits are pinned.  When a batch is due, the assign
-// kernel's last blocks write the 64 oldest ring rows back to the mirror.
-#include "gather_plan.h"
+// gfx950 design.  Selection and classification happen where the selection is
+// produced: the Top-K kernel sets, for every selected position, a bit in a
+// per-position selection bitmap (a position several rows select is one union
+// entry), and the last Top-K workgroup of the sequence runs the gather plan
+// (gather_plan.h): hits against the cached-position bitmap, prefix counts per
+// 32-position word and the victim list.  The attention kernel derives each of
+// its rows' union index, kind and source from those outputs and does the row
+// copies while it stages the rows (k_attn.hip): one 16-byte piece per thread,
+// from the hot slot, the ring, or the host mirror (zero-copy reads of pinned
+// host memory over the host link; a miss that several query rows select is
+// read from host memory by each of them, as the page's rule for repeated
+// misses has it), to LDS, the compact buffer and, for a miss that got a slot,
+// to the slot.  The assign pass (gather_assign.h) then pins the hits' slots,
+// gives the k-th miss in ascending position order victim[k] (evicting the
+// position the slot held and updating the slot table), writes the union
+// entries and descriptors, and, when a batch is due, writes the 64 oldest
+// ring rows back to the mirror; in a decode step it runs as extra workgroups
+// of the merge launch.  No reader consults a slot filled in the same round:
+// victims are unpinned, hits are pinned.  This file holds the assign kernel of
+// prefetch rounds and the unit maintenance kernels.
+#include "gather_assign.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kGatherThreads = 256;
-
-struct GatherKArgs {
-  StepArgs a;
-  int S, ring_cap, ring_rows, mode, row_bytes, K;
-  int max_union;                        // R_max * K: compact rows in the scratch
-  int word_blocks;                      // blocks of the union/slot-table part
-  int clear_blocks;                     // then blocks clearing the Top-K histograms; the rest write back the ring
-  int r_max;
-  int clock;                            // CLOCK replacement: hits and fills set their slot's reference bit
-  int64_t max_positions;
-};
-
-// Union entries and slot table: one wave per 64 positions, one lane per position.
-// The last blocks write the 64 oldest pending ring rows back to the host mirror
-// when a batch is due (positions the step reads from the ring, never from the
-// mirror).
 __global__ __launch_bounds__(kGatherThreads) void gather_assign_kernel(GatherKArgs ka) {
-  const StepArgs& a = ka.a;
-  const int seq = blockIdx.y;
-  const UnitG u = unit_of(a, seq);
-  const ScratchG s = scratch_of(a, seq);
-  if ((int)blockIdx.x >= ka.word_blocks && (int)blockIdx.x < ka.word_blocks + ka.clear_blocks) {
-    // the Top-K histograms of this step's rows, consumed: zero for the next step
-    const int64_t t = (int64_t)(blockIdx.x - ka.word_blocks) * kGatherThreads + threadIdx.x;
-    const int64_t n0 = (int64_t)kHistReps * a.R * (kRadixBins / 4), n1 = (int64_t)a.R * (kRadixBins / 4);
-    if (t < n0) {
-      const int64_t q = t / (a.R * (kRadixBins / 4)), rest = t % (a.R * (kRadixBins / 4));
-      reinterpret_cast<DSA_GLOBAL u32x4*>(s.hist0 + q * ka.r_max * kRadixBins)[rest] = (u32x4){0u, 0u, 0u, 0u};
-    } else if (t < n0 + n1) {
-      reinterpret_cast<DSA_GLOBAL u32x4*>(s.hist1)[t - n0] = (u32x4){0u, 0u, 0u, 0u};
-    }
-    return;
-  }
-  if ((int)blockIdx.x >= ka.word_blocks) {
-    const int64_t wb = s.info[kInfoWriteback];
-    if (wb < 0) return;
-    const int64_t t = (int64_t)(blockIdx.x - ka.word_blocks - ka.clear_blocks) * kGatherThreads + threadIdx.x;
-    if (t >= (int64_t)ka.ring_rows * kCopyChunks16) return;
-    const int64_t rb = ka.row_bytes;
-    const int64_t p = wb + t / kCopyChunks16, c = t % kCopyChunks16;
-    if (p >= ka.max_positions) return;
-    const u32x4 v = *reinterpret_cast<const DSA_GLOBAL u32x4*>(u.ring + (p % ka.ring_cap) * rb + c * 16);
-    *reinterpret_cast<DSA_GLOBAL u32x4*>(u.rows + p * rb + c * 16) = v;
-    return;
-  }
-  const int lane = threadIdx.x & 63;
-  const int64_t wave_id = ((int64_t)blockIdx.x * kGatherThreads + threadIdx.x) >> 6;
-  const int64_t L = u.dyn[0];
-  const int64_t nw = (L + 31) / 32;
-  if (2 * wave_id >= nw) return;
-  const int64_t w = 2 * wave_id + (lane >> 5);        // this lane's 32-position word
-  const int64_t M = s.info[kInfoM];
-  const int32_t round = (int32_t)s.info[kInfoRound];
-  const uint32_t n_assigned = (uint32_t)s.info[kInfoAssigned];
-  const bool off = ka.mode == 0;
-  const int bitpos = lane & 31;
-  const uint32_t bit = 1u << bitpos;
-  const int64_t p = w * 32 + bitpos;
-
-  const int64_t wc = w < nw ? w : nw - 1;
-  uint32_t sw = s.selmask[wc], hw = s.hitmask[wc];    // both loads in flight together
-  const uint32_t bu = s.base_u[wc], bm = s.base_m[wc];
-  if (w >= nw) sw = 0;
-  if (!off) hw = 0;
-  const bool mine = (sw & bit) != 0;
-  const uint64_t selb = __ballot(mine);
-  if (!selb) return;
-  if (bitpos == 0 && sw) s.selmask[w] = 0;             // read by every lane above: clear for the next step
-  if (mine) {
-    const uint32_t below = bit - 1u;
-    const uint32_t ux = bu + __popc(sw & below);
-    int32_t kind, src, fill = -1;
-    if (!off) {
-      kind = SRC_RES;
-      src = (int32_t)p;
-    } else {
-      const uint32_t rw = sw & ring_bits(w, M);
-      if (rw & bit) {
-        kind = SRC_RING;
-        src = (int32_t)(p % ka.ring_cap);
-      } else if (hw & bit) {
-        kind = SRC_HIT;                                // the hit's slot is pinned for this round
-        src = u.pos_slot[p].x;
-        if (src >= 0 && src < ka.S) {
-          u.pin_round[src] = round;
-          if (ka.clock) g_or(&u.ref[src >> 5], 1u << (src & 31));
-        }
-      } else {
-        const uint32_t k = bm + __popc(sw & ~hw & ~rw & below);
-        src = (int32_t)p;
-        if (k < n_assigned) {
-          kind = SRC_MISS;
-          const i32x2 vo = s.victim[k];                // (slot, position it held), from the plan
-          const int32_t v = vo.x, old = vo.y;
-          if (v >= 0 && v < ka.S) {
-            if (old >= 0 && old < ka.max_positions) {
-              u.pos_slot[old] = (i32x2){-1, -1};
-              __hip_atomic_fetch_and(&u.hot[old >> 5], ~(1u << (old & 31)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            u.slot_pos[v] = (int32_t)p;
-            u.pos_slot[p] = (i32x2){v, round};
-            g_or(&u.hot[p >> 5], bit);
-            u.fill_round[v] = round;
-            u.pin_round[v] = round;
-            if (ka.clock) g_or(&u.ref[v >> 5], 1u << (v & 31));
-            fill = v;
-          }
-        } else {
-          kind = SRC_MISS_NOSLOT;
-        }
-      }
-    }
-    if (ux < (uint32_t)ka.max_union) {                 // always true for a consistent plan
-      s.uni[ux] = (int32_t)p;
-      s.kind[ux] = kind;
-      s.src[ux] = src;
-      s.pdesc[p] = (i32x4){(int32_t)ux, kind, src, fill};
-    }
-  }
+  assign_block(ka, (int)blockIdx.x, (int)blockIdx.y);
 }
 
 // ---- unit maintenance ----
@@ -282,17 +164,9 @@ unsigned grid_for(int64_t work, int64_t cap = 4096) {
 }  // namespace
 
 hipError_t launch_gather(const Geometry& g, const StepArgs& a, hipStream_t st, bool clear_hist) {
-  const int64_t words = (a.l_max + 31) / 32;
-  const int64_t waves = (words + 1) / 2;
-  const int64_t blocks = (waves + 3) / 4;
-  const int64_t wb_blocks = ((int64_t)g.ring_rows * kCopyChunks16 + kGatherThreads - 1) / kGatherThreads;
-  const int64_t clear_blocks =
-      clear_hist ? ((int64_t)(kHistReps + 1) * a.R * (kRadixBins / 4) + kGatherThreads - 1) / kGatherThreads : 0;
-  GatherKArgs ka{a, g.hot_slots, g.ring_cap, g.ring_rows, g.mode, g.row_bytes, g.top_k, g.r_max * g.top_k,
-                 (int)blocks, (int)clear_blocks, g.r_max, g.clock ? 1 : 0, g.max_positions};
-  return launch_k(gather_assign_kernel,
-                  dim3((unsigned)(blocks + clear_blocks + (g.mode == 0 ? wb_blocks : 0)), (unsigned)a.n_seqs),
-                  dim3(kGatherThreads), 0, st, ka);
+  int64_t blocks = 0;
+  const GatherKArgs ka = gather_args(g, a, clear_hist, &blocks);
+  return launch_k(gather_assign_kernel, dim3((unsigned)blocks, (unsigned)a.n_seqs), dim3(kGatherThreads), 0, st, ka);
 }
 
 hipError_t launch_append(const Geometry& g, const UnitDev& unit, int64_t L, int64_t M, int64_t newM,

@@ -717,9 +717,9 @@ dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq, 
   if ((st = timed_launch(s, KK_TOPK_SELECT, "top-k resolve", [&] { return launch_topk_select(g, a, stream); })) != DSA_OK) return st;
   HIPCHK(hipEventRecord(s->sel_ready, stream), "hipEventRecord");
   s->sel_epoch += 1;
-  if ((st = timed_launch(s, KK_GATHER, "gather", [&] { return launch_gather(g, a, stream); })) != DSA_OK) return st;
   if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream); })) != DSA_OK) return st;
-  if ((st = timed_launch(s, KK_MERGE, "attention merge", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_MERGE, "attention merge and assign", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK)
+    return st;
   s->last_layer = layer;
   s->last_R = R;
   s->topk_layer = layer;
@@ -745,9 +745,9 @@ dsa_status dsa_decode_step_reuse(dsa_session* s, int32_t layer, int32_t src_laye
   }
   if ((st = timed_launch(s, KK_TOPK_SELECT, "reuse mark", [&] { return launch_reuse_mark(g, a, s->scr[0], s->s_stride, stream); })) != DSA_OK)
     return st;
-  if ((st = timed_launch(s, KK_GATHER, "gather", [&] { return launch_gather(g, a, stream); })) != DSA_OK) return st;
   if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream); })) != DSA_OK) return st;
-  if ((st = timed_launch(s, KK_MERGE, "attention merge", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_MERGE, "attention merge and assign", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK)
+    return st;
   s->last_layer = layer;
   s->last_R = rows_per_seq;
   return finish_round(s, layer, stream);
