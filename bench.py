@@ -67,6 +67,7 @@ KERNEL_SOURCES = {"index_score": "k_score.hip", "topk_collect": "k_topk.hip", "t
 KERNEL_NAMES = {"index_score": ("score_kernel",), "topk_collect": ("topk_refine_kernel", "topk_digits_kernel"),
                 "topk_resolve": ("topk_chunk_kernel", "topk_final_kernel"), "gather": ("gather_assign_kernel",),
                 "attention": ("attn_kernel",), "attention_merge": ("attn_merge_kernel",), "append": ("append_kernel",)}
+# (decode steps run the assign pass inside the merge launch; gather_assign_kernel is the prefetch rounds')
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
@@ -256,15 +257,17 @@ def algorithmic_bytes(w, kind, n_steps, L0, cnt, long_hist):
         return Q * R * Lmean * 4 * (2 if long_hist else 1)
     if kind == "topk_resolve":
         return Q * R * Lmean * 4 + Q * R * K * 4          # the scores once, the selection out
+    assign = U * (16 + 12) + miss * (8 + 16) + wb
     if kind == "gather":
         # union bookkeeping: descriptor + union arrays per entry, victim and slot-table entries per miss
-        return U * (16 + 12) + miss * (8 + 16) + wb
+        return assign
     if kind == "attention":
         # every selected row read from its source (slot, ring, host mirror, HBM row store), the compact
         # copy and the misses' slot fills written, the queries read
         return Q * R * K * rb + U * rb + miss * rb + Q * R * H * (512 + 64) * 2
     if kind == "attention_merge":
-        return Q * R * H * 512 * 4
+        # the merged output, and the assign pass that runs in the same launch
+        return Q * R * H * 512 * 4 + assign
     if kind == "append":
         return Q * R * (w.index_dim * 2 + rb) * 2
     return 0.0
