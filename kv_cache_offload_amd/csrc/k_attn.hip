@@ -43,9 +43,8 @@ typedef float fx2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bfx2 __attribute__((ext_vector_type(2)));
 #define DSA_LDS __attribute__((address_space(3)))
 
-constexpr int kSplit = 64;             // selected rows per workgroup
+constexpr int kSplit = 64;             // selected rows per workgroup (resident; offload takes 2 kSplit)
 constexpr int kBlk = 32;               // rows per staged block (online softmax over the blocks)
-constexpr int kNBlk = kSplit / kBlk;
 constexpr int kRowPieces = kCopyChunks16;            // 16-byte pieces of a 656-byte row
 constexpr int kBlkPieces = kBlk * kRowPieces;
 constexpr int kLatStride = 536;        // bf16 per row of the latent in LDS (512 + 24: no bank conflicts
@@ -104,14 +103,17 @@ __device__ inline bf16x4 read_tr(const uint16_t* lat_s, int r0, int col0, int la
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS bf16x4*)(DSA_LDS void*)p);
 }
 
-// One workgroup: one query row, all H = NW*16 heads, 64 selected rows.
-template <int NW>
+// One workgroup: one query row, all H = NW*16 heads, NBLK * 32 selected rows
+// (a split), staged in 32-row blocks through two LDS buffers.
+template <int NW, int NBLK>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   constexpr int NT = NW * 64;
+  constexpr int kSplit = NBLK * kBlk;                    // this kernel's split
+  static_assert(kSplit <= NT, "one thread per row of the split reads its source");
   constexpr int PPT = (kBlkPieces + NT - 1) / NT;        // row pieces per thread per block
-  __shared__ __align__(16) uint16_t lat_s[kNBlk][kBlk * kLatStride];
-  __shared__ __align__(16) uint16_t rope_s[kNBlk][kBlk * kRopeStride];
-  __shared__ __align__(16) float scl_s[kNBlk][8 * kBlk];
+  __shared__ __align__(16) uint16_t lat_s[2][kBlk * kLatStride];
+  __shared__ __align__(16) uint16_t rope_s[2][kBlk * kRopeStride];
+  __shared__ __align__(16) float scl_s[2][8 * kBlk];
   __shared__ const DSA_GLOBAL uint8_t* s_from[kSplit];   // where each row is read from (null: masked)
   __shared__ int s_ux[kSplit];                            // its compact row, -1 if masked
   __shared__ int s_fill[kSplit];                          // the slot a miss fills, -1 if none
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   // block, and the first blocks are computed while the second ones arrive.
   // Piece q of a block: row q / 41, bytes 16 (q % 41) .. ; masked rows read the
   // unit's key store (always mapped) and are zeroed below.
-  u32x4 raw[kNBlk][PPT];
+  u32x4 raw[2][PPT];
   auto request = [&](int b) {
 #pragma unroll
     for (int e = 0; e < PPT; ++e) {
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
       const int row = b * kBlk + q / kRowPieces, part = q % kRowPieces;
       const DSA_GLOBAL uint8_t* from = s_from[row];
       const DSA_GLOBAL uint8_t* at = from ? from + 16 * part : reinterpret_cast<const DSA_GLOBAL uint8_t*>(u.keys);
-      raw[b][e] = *reinterpret_cast<const DSA_GLOBAL u32x4*>(at);
+      raw[b & 1][e] = *reinterpret_cast<const DSA_GLOBAL u32x4*>(at);
     }
   };
   request(0);
@@ -216,10 +218,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   float m_run = -INFINITY, l_run = 0.f;                  // of head h0 + l16
 
 #pragma unroll
-  for (int b = 0; b < kNBlk; ++b) {
-    uint16_t* lat = lat_s[b];
-    uint16_t* rope = rope_s[b];
-    float* scl = scl_s[b];
+  for (int b = 0; b < NBLK; ++b) {
+    // buffer b & 1 was last read by block b - 2, which every wave finished
+    // before the barrier of block b - 1
+    uint16_t* lat = lat_s[b & 1];
+    uint16_t* rope = rope_s[b & 1];
+    float* scl = scl_s[b & 1];
     // This block's rows: the compact copy and a miss's slot fill (the gather's
     // writes), and the LDS staging -- the int8 latent widened to bf16, the
     // scales as fp32, the RoPE as is.
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
       if (q >= kBlkPieces) continue;
       const int rl = q / kRowPieces, part = q % kRowPieces, row = b * kBlk + rl;
       const int ux = s_ux[row];
-      const u32x4 v = ux >= 0 ? raw[b][e] : (u32x4){0u, 0u, 0u, 0u};
+      const u32x4 v = ux >= 0 ? raw[b & 1][e] : (u32x4){0u, 0u, 0u, 0u};
       if (ux >= 0) {
         *reinterpret_cast<DSA_GLOBAL u32x4*>(s.compact + (int64_t)ux * rb + 16 * part) = v;
         const int f = s_fill[row];
@@ -251,7 +255,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
         *reinterpret_cast<u32x4*>(rope + rl * kRopeStride + 8 * (part - 33)) = v;
       }
     }
-    if (b + 1 < kNBlk) request(b + 1);
+    if (b + 1 < NBLK) request(b + 1);
     __syncthreads();
 
     // Logits S^T[j][h]: lane holds rows 16 mt + 4 q4 + v of head h0 + l16; each
@@ -397,6 +401,7 @@ struct MergeKArgs {
   GatherKArgs ga;            // the assign pass (ga.a: the step's arguments)
   float* out;
   int H, ns_stride;
+  int split_rows;            // selected rows per attention split
   int merge_blocks;          // merge workgroups per sequence; the rest of a row of the grid assign
 };
 
@@ -429,7 +434,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
   const int nt = rem / n_hg, hg = rem % n_hg;
   const ScratchG s = scratch_of(a, seq);
   const int H = ka.H;
-  const int used = min(MAXS, (s.sel_n[r] + kSplit - 1) / kSplit);
+  const int used = min(MAXS, (s.sel_n[r] + ka.split_rows - 1) / ka.split_rows);
   if (used < 1) return;                                  // (uniform) no selection: nothing to merge
   const int tid = threadIdx.x;
   const int e0 = tid * EPT, l16 = e0 / HW, hl0 = e0 % HW;
@@ -506,18 +511,28 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
 
 }  // namespace
 
+// Rows per attention split.  Offloaded, the kernel waits on the host link, so
+// splits of 128 rows (four blocks) keep it as busy as 64-row splits while
+// halving the partials the merge reads; resident, 64-row splits give twice the
+// workgroups.  Up to 32 heads a workgroup has too few threads for 128 rows; at
+// 128 heads (512 threads, 256 registers a lane) the four-block kernel spills.
+inline int split_rows(const Geometry& g) { return (g.mode == 0 && g.heads == 64) ? 2 * kSplit : kSplit; }
+
 hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_lat, const uint16_t* q_rope,
                        float* out, hipStream_t st) {
-  const int nsplit = (g.top_k + kSplit - 1) / kSplit;
+  const int rows = split_rows(g);
+  const int nsplit = (g.top_k + rows - 1) / rows;
   AttnKArgs ka{a, q_lat, q_rope, out, g.top_k, g.heads, nsplit, g.nsplit_max, g.row_bytes,
                g.hot_slots, g.ring_cap, g.r_max * g.top_k, g.mode == 0 ? 1 : 0, g.max_positions,
                g.softmax_scale * 1.4426950408889634f};
   dim3 grid((unsigned)nsplit, (unsigned)a.R, (unsigned)a.n_seqs);
+  const bool wide = rows == 2 * kSplit;
   switch (g.heads) {
-    case 16: return launch_k(attn_kernel<1>, grid, dim3(64), 0, st, ka);
-    case 32: return launch_k(attn_kernel<2>, grid, dim3(128), 0, st, ka);
-    case 64: return launch_k(attn_kernel<4>, grid, dim3(256), 0, st, ka);
-    case 128: return launch_k(attn_kernel<8>, grid, dim3(512), 0, st, ka);
+    case 16: return launch_k(attn_kernel<1, 2>, grid, dim3(64), 0, st, ka);
+    case 32: return launch_k(attn_kernel<2, 2>, grid, dim3(128), 0, st, ka);
+    case 64: return wide ? launch_k(attn_kernel<4, 4>, grid, dim3(256), 0, st, ka)
+                         : launch_k(attn_kernel<4, 2>, grid, dim3(256), 0, st, ka);
+    case 128: return launch_k(attn_kernel<8, 2>, grid, dim3(512), 0, st, ka);
     default: return hipErrorInvalidValue;
   }
 }
@@ -525,16 +540,18 @@ hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_l
 hipError_t launch_attn_merge(const Geometry& g, const StepArgs& a, float* out, hipStream_t st) {
   int64_t assign_blocks = 0;
   const GatherKArgs ga = gather_args(g, a, true, &assign_blocks);
-  const int nsplit = (g.top_k + kSplit - 1) / kSplit;
+  const int rows = split_rows(g);
+  const int nsplit = (g.top_k + rows - 1) / rows;
   const int HW = g.heads == 16 ? 16 : 32;
   const int merge_blocks = nsplit == 1 ? 0 : 32 * (g.heads / HW) * a.R;   // one split: attention wrote out
-  MergeKArgs ka{ga, out, g.heads, g.nsplit_max, merge_blocks};
+  MergeKArgs ka{ga, out, g.heads, g.nsplit_max, rows, merge_blocks};
   const dim3 grid((unsigned)(merge_blocks + assign_blocks), (unsigned)a.n_seqs);
   static_assert(kGatherThreads == 256, "assign and merge workgroups share the launch");
   if (HW == 16) {
     if (nsplit <= 32) return launch_k(attn_merge_kernel<32, 16>, grid, dim3(256), 0, st, ka);
     return launch_k(attn_merge_kernel<kMaxSplits, 16>, grid, dim3(256), 0, st, ka);
   }
+  if (nsplit <= 16) return launch_k(attn_merge_kernel<16, 32>, grid, dim3(256), 0, st, ka);
   if (nsplit <= 32) return launch_k(attn_merge_kernel<32, 32>, grid, dim3(256), 0, st, ka);
   return launch_k(attn_merge_kernel<kMaxSplits, 32>, grid, dim3(256), 0, st, ka);
 }
