@@ -11,17 +11,19 @@
 // the page's 656-byte Q8G64 layout: int8 latent, fp16 scale per group of 64,
 // bf16 RoPE.
 //
-// gfx950 mapping.  A workgroup owns one query row and a split of 64 of its
-// selected rows, all heads: wave w holds heads 16w..16w+15.  The 64 rows are
-// staged in LDS once for all waves: the int8 latent widened to bf16 (exact,
+// gfx950 mapping.  A workgroup owns one query row and a split of its selected
+// rows (64, or 128 when the rows come over the host link), all heads: wave w
+// holds heads 16w..16w+15.  The rows are staged in 32-row blocks through two
+// LDS buffers, once for all waves: the int8 latent widened to bf16 (exact,
 // |int8| < 2^8) in one row-major layout, the fp16 scales as fp32, the RoPE as
 // is.  Both products run on v_mfma_f32_16x16x32_bf16:
 //   * logits, transposed: S^T[j][h] = sum_d C[j][d] Q[h][d], the A operand
 //     read straight from the row-major latent, the query (B operand) held in
 //     registers; each 64-dim group is accumulated separately and scaled by its
 //     fp32 scale per row, so the int8 operand stays exact;
-//   * softmax over the split's 64 rows at once (its max is known before any
-//     weight is formed, so nothing is rescaled);
+//   * softmax online over the 32-row blocks: a block's max is known before
+//     any of its weights is formed, and the running output and sum are
+//     rescaled when a later block raises the max;
 //   * output: O[h][d] += sum_j P'_g[h][j] C[j][d] with P'_g = p * scale_g,
 //     carried as a bf16 high part plus a bf16 low part (~16 mantissa bits).
 //     In the transposed logits a lane already holds p for one head and 8 rows
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   // Every 16-byte piece of a block is requested at once.  Block b + 1 is
   // requested as soon as block b has arrived, before block b is computed: the
   // host link then serves every workgroup's first block before any second
-  // block, and the first blocks are computed while the second ones arrive.
+  // block, and each block is computed while the next one arrives.
   // Piece q of a block: row q / 41, bytes 16 (q % 41) .. ; masked rows read the
   // unit's key store (always mapped) and are zeroed below.
   u32x4 raw[2][PPT];
