@@ -11,9 +11,8 @@
 // the page's 656-byte Q8G64 layout: int8 latent, fp16 scale per group of 64,
 // bf16 RoPE.
 //
-// gfx950 mapping.  A workgroup owns one query row and a split of its selected
-// rows (64, or 128 when the rows come over the host link), all heads: wave w
-// holds heads 16w..16w+15.  The rows are staged in 32-row blocks through two
+// gfx950 mapping.  A workgroup owns one query row and a split of 64 of its
+// selected rows, all heads: wave w holds heads 16w..16w+15.  The rows are staged in 32-row blocks through two
 // LDS buffers, once for all waves: the int8 latent widened to bf16 (exact,
 // |int8| < 2^8) in one row-major layout, the fp16 scales as fp32, the RoPE as
 // is.  Both products run on v_mfma_f32_16x16x32_bf16:
@@ -45,7 +44,7 @@ typedef float fx2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bfx2 __attribute__((ext_vector_type(2)));
 #define DSA_LDS __attribute__((address_space(3)))
 
-constexpr int kSplit = 64;             // selected rows per workgroup (resident; offload takes 2 kSplit)
+constexpr int kSplit = 64;             // selected rows per workgroup
 constexpr int kBlk = 32;               // rows per staged block (online softmax over the blocks)
 constexpr int kRowPieces = kCopyChunks16;            // 16-byte pieces of a 656-byte row
 constexpr int kBlkPieces = kBlk * kRowPieces;
@@ -513,12 +512,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
 
 }  // namespace
 
-// Rows per attention split.  Offloaded, the kernel waits on the host link, so
-// splits of 128 rows (four blocks) keep it as busy as 64-row splits while
-// halving the partials the merge reads; resident, 64-row splits give twice the
-// workgroups.  Up to 32 heads a workgroup has too few threads for 128 rows; at
-// 128 heads (512 threads, 256 registers a lane) the four-block kernel spills.
-inline int split_rows(const Geometry& g) { return (g.mode == 0 && g.heads == 64) ? 2 * kSplit : kSplit; }
+// Rows per attention split: 64 (two blocks).  Longer splits halve the partials
+// the merge reads, but when most selected rows are hits they halve the
+// workgroups of a kernel that is then latency-bound, not link-bound.
+inline int split_rows(const Geometry&) { return kSplit; }
 
 hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_lat, const uint16_t* q_rope,
                        float* out, hipStream_t st) {
@@ -528,12 +525,10 @@ hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_l
                g.hot_slots, g.ring_cap, g.r_max * g.top_k, g.mode == 0 ? 1 : 0, g.max_positions,
                g.softmax_scale * 1.4426950408889634f};
   dim3 grid((unsigned)nsplit, (unsigned)a.R, (unsigned)a.n_seqs);
-  const bool wide = rows == 2 * kSplit;
   switch (g.heads) {
     case 16: return launch_k(attn_kernel<1, 2>, grid, dim3(64), 0, st, ka);
     case 32: return launch_k(attn_kernel<2, 2>, grid, dim3(128), 0, st, ka);
-    case 64: return wide ? launch_k(attn_kernel<4, 4>, grid, dim3(256), 0, st, ka)
-                         : launch_k(attn_kernel<4, 2>, grid, dim3(256), 0, st, ka);
+    case 64: return launch_k(attn_kernel<4, 2>, grid, dim3(256), 0, st, ka);
     case 128: return launch_k(attn_kernel<8, 2>, grid, dim3(512), 0, st, ka);
     default: return hipErrorInvalidValue;
   }
