@@ -139,7 +139,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   // read host memory; the k-th miss fills the plan's k-th victim slot), a
   // resident row from the HBM row store.  The map entry of every selected index
   // of the split is written here.
+  // Only the row's address is on the path to its data: a hit's slot is read
+  // with the words (for every selected position: a non-hit ignores it), and a
+  // miss's victim slot -- needed only when the row is written to it -- is
+  // requested here but used after the rows have been requested.
   const int n_sel = s.sel_n[r];
+  i32x2 victim = (i32x2){-1, -1};
   if (tid < kSplit) {
     const int64_t M = s.info[kInfoM];
     const uint32_t n_assigned = (uint32_t)s.info[kInfoAssigned];
@@ -149,10 +154,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     const int64_t w = ok ? pos >> 5 : 0;
     const uint32_t sw = s.selmask[w], hw = ka.off ? s.hitmask[w] : 0u;
     const uint32_t bu = s.base_u[w], bm = s.base_m[w];
+    const i32x2 ps = ka.off ? u.pos_slot[ok ? pos : 0] : (i32x2){-1, -1};
     const uint32_t bit = 1u << (pos & 31), below = bit - 1u;
     const uint32_t ux = bu + __popc(sw & below);
     const DSA_GLOBAL uint8_t* from = nullptr;
-    int32_t fill = -1;
     if (ok && (sw & bit) && ux < (uint32_t)ka.max_union) {
       if (!ka.off) {
         from = u.rows + (int64_t)pos * rb;
@@ -161,21 +166,17 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
         if (rw & bit) {
           from = u.ring + (int64_t)(pos % ka.ring_cap) * rb;
         } else if (hw & bit) {
-          const int32_t slot = u.pos_slot[pos].x;
+          const int32_t slot = ps.x;
           if (slot >= 0 && slot < ka.S) from = u.slots + (int64_t)slot * rb;
         } else {
           const uint32_t k = bm + __popc(sw & ~hw & ~rw & below);
-          if (k < n_assigned) {
-            const int32_t v = s.victim[k].x;
-            if (v >= 0 && v < ka.S) fill = v;
-          }
+          if (k < n_assigned) victim = s.victim[k];    // (slot, position it held)
           from = u.rows + (int64_t)pos * rb;
         }
       }
     }
     s_from[tid] = from;
     s_ux[tid] = from ? (int)ux : -1;
-    s_fill[tid] = from ? fill : -1;
     if (j < ka.K) s.map[(int64_t)r * ka.K + j] = from ? (int)ux : -1;
   }
   if (j_begin >= n_sel) return;                          // (uniform) map entries written above
@@ -212,6 +213,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     }
   };
   request(0);
+  if (tid < kSplit) s_fill[tid] = (s_from[tid] && victim.x >= 0 && victim.x < ka.S) ? victim.x : -1;
+  __syncthreads();                                       // s_fill before block 0 is staged
 
   f32x4 o[32];
 #pragma unroll
