@@ -62,3 +62,13 @@ def test_planted_overlap_selects_2028_hot_and_20_cold():
         assert set(top.tolist()) == set(hot.tolist()) | set(cold.tolist())
         assert np.all(hot >= w.history - w.hot_slots) and np.all(cold < w.history - w.hot_slots)
         assert len(cold) == 20 and len(hot) == 2028
+
+
+def test_planted_queries_stop_at_their_fresh_codes():
+    # every step's queries use fresh codes; past the last one the generator refuses
+    w = S.WORKLOADS["stress_78_layers"]
+    last = planted.max_steps(w) - 1
+    iq, iw = planted.index_queries(w, 0, 0, last)
+    assert iq.shape[0] == w.rows_per_step and np.all(iw[:, 0] == 4.0)
+    with pytest.raises(ValueError):
+        planted.index_queries(w, 0, 0, last + 1)
