@@ -10,6 +10,8 @@
 namespace dsa {
 
 // Kernel kinds for the optional per-kernel timing (order matches dsa.h).
+// (KK_GATHER is unused by decode steps -- their assign pass runs in the KK_MERGE
+// launch -- and keeps its number for the timing ABI.)
 enum KernelKind { KK_SCORE = 0, KK_TOPK_PARTIAL, KK_TOPK_SELECT, KK_GATHER, KK_ATTN, KK_MERGE, KK_APPEND, KK__N };
 
 // Source kinds of a compact row (same numbering as the inspection interface).
