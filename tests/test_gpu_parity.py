@@ -248,3 +248,15 @@ def test_key_store_round_trip():
     got = sess.debug("keys", 0, 0).cpu().numpy().view(np.uint16).reshape(-1, 128)
     assert np.array_equal(got, np.concatenate([keys, nk]))
     sess.close()
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("heads,index_heads", [(32, 8), (128, 16)], ids=["H32-HI8", "H128-HI16"])
+def test_other_head_counts(mode, heads, index_heads):
+    # the score kernel's H_I = 8 and 16 variants, the attention kernel's 2- and
+    # 8-wave variants and the merge of 32-head groups (one and four per row),
+    # over several splits with a ragged last one (K = 320: five 64-row splits)
+    w = S.WORKLOADS["tiny"].scaled(heads=heads, index_heads=index_heads, top_k=320, rows_per_step=2,
+                                   history=2000, hot_slots=600, steps=4, warm=True)
+    _note("heads", heads, "index heads", index_heads, mode)
+    _run_and_compare(w, mode, steps=w.steps)
