@@ -229,8 +229,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     uint16_t* rope = rope_s[b & 1];
     float* scl = scl_s[b & 1];
     // This block's rows: the compact copy and a miss's slot fill (the gather's
-    // writes), and the LDS staging -- the int8 latent widened to bf16, the
-    // scales as fp32, the RoPE as is.
+    // writes; nothing reads them again in this step, so they are streamed past
+    // the caches with non-temporal stores), and the LDS staging -- the int8
+    // latent widened to bf16, the scales as fp32, the RoPE as is.
 #pragma unroll
     for (int e = 0; e < PPT; ++e) {
       const int q = tid + e * NT;
@@ -239,9 +240,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
       const int ux = s_ux[row];
       const u32x4 v = ux >= 0 ? raw[b & 1][e] : (u32x4){0u, 0u, 0u, 0u};
       if (ux >= 0) {
-        *reinterpret_cast<DSA_GLOBAL u32x4*>(s.compact + (int64_t)ux * rb + 16 * part) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<DSA_GLOBAL u32x4*>(s.compact + (int64_t)ux * rb + 16 * part));
         const int f = s_fill[row];
-        if (f >= 0) *reinterpret_cast<DSA_GLOBAL u32x4*>(u.slots + (int64_t)f * rb + 16 * part) = v;
+        if (f >= 0) __builtin_nontemporal_store(v, reinterpret_cast<DSA_GLOBAL u32x4*>(u.slots + (int64_t)f * rb + 16 * part));
       }
       if (part < 32) {
         uint32_t w[8];
