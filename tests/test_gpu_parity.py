@@ -260,3 +260,14 @@ def test_other_head_counts(mode, heads, index_heads):
                                    history=2000, hot_slots=600, steps=4, warm=True)
     _note("heads", heads, "index heads", index_heads, mode)
     _run_and_compare(w, mode, steps=w.steps)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_several_layers_and_sequences(mode):
+    # kernels form sequence q's buffers from sequence 0's descriptors of the
+    # layer and the strides: layers past the first, sequences past the first
+    # few, the ring writeback and the hot cache of every (layer, sequence)
+    w = S.WORKLOADS["batched_16x131k"].scaled(history=3000, seqs=6, rows_per_step=2, top_k=256,
+                                              hot_slots=512, steps=40, warm=True)
+    _note("layers x sequences", mode)
+    _run_and_compare(w, mode, steps=40, layers=(0, 1, 2))
