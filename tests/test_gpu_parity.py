@@ -25,10 +25,10 @@ def _note(*a):
 
 
 def _run_and_compare(w, mode, steps, layers=(0,), seqs=None, rows_fn=None, query_fn=None, history_fn=None,
-                     warm=None, check_scores=True):
+                     warm=None, check_scores=True, replacement=0):
     seqs = list(range(w.seqs) if seqs is None else seqs)
-    sess = gpu_session(w, mode, n_layers=len(layers))
-    orcs = oracle_units(w, mode, layers=layers, seqs=seqs)
+    sess = gpu_session(w, mode, n_layers=len(layers), replacement=replacement)
+    orcs = oracle_units(w, mode, layers=layers, seqs=seqs, replacement=replacement)
     load_history(w, sess, orcs, layers=layers, seqs=seqs, warm=warm, history_fn=history_fn)
     for step in range(steps):
         for gl, l in enumerate(layers):
@@ -271,3 +271,12 @@ def test_several_layers_and_sequences(mode):
                                               hot_slots=512, steps=40, warm=True)
     _note("layers x sequences", mode)
     _run_and_compare(w, mode, steps=40, layers=(0, 1, 2))
+
+
+def test_several_layers_and_sequences_clock():
+    # CLOCK's reference bits of every (layer, sequence) unit, through the strided descriptors
+    from oracle import REPL_CLOCK
+    w = S.WORKLOADS["batched_16x131k"].scaled(history=3000, seqs=5, rows_per_step=2, top_k=256,
+                                              hot_slots=400, steps=30, warm=True)
+    _note("layers x sequences, CLOCK")
+    _run_and_compare(w, MODE_OFFLOAD, steps=30, layers=(0, 1), replacement=REPL_CLOCK)
