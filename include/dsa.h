@@ -77,6 +77,13 @@
  * returns an error other than DSA_E_HIP has no effect.  A failing HIP call
  * returns DSA_E_HIP and makes the session sticky-failed: every later call
  * except destroy returns DSA_E_STATE.  dsa_last_error gives the text.
+ * The kernels also check every position, slot and union index they follow
+ * against what the round's plan allows.  An entry that fails a check is skipped
+ * (its row is masked out of attention, its slot-table update is not made) and
+ * sets a flag in a small pinned host block that the session reads, without
+ * blocking, at the start of every call: the first call made after such a step
+ * has run returns DSA_E_STATE, and so does every later one, with the kinds of
+ * failed check in dsa_last_error.  A consistent plan never sets a flag.
  */
 #ifndef DSA_H
 #define DSA_H
@@ -148,22 +155,39 @@ typedef struct {
 
 typedef struct dsa_session dsa_session;
 
-/* Validate the configuration and allocate every buffer.  On failure *out is
- * NULL and nothing is left allocated.  Pass 0 for abi_version-mismatched or
- * unsupported shapes to get DSA_E_INVALID / DSA_E_UNSUPPORTED. */
+/* Validate the configuration and allocate every buffer the session will use:
+ * the HBM key stores, hot caches, rings and slot tables, the step scratch, and
+ * the pinned host mirrors (offload page, section "Starting point: separate
+ * capacity from the working set": the capacity lives in host RAM and the GPU
+ * keeps only a hot cache; section "The ten-way experiment": long-lived buffers
+ * are allocated once, at their exact sizes).  On failure *out is NULL and
+ * nothing is left allocated.  DSA_E_INVALID for a NULL pointer, an
+ * abi_version mismatch, a bad device or an out-of-range field;
+ * DSA_E_UNSUPPORTED for shapes the kernels do not implement; DSA_E_NOMEM if
+ * the device or pinned host allocation fails (nothing is kept, and a later
+ * create with a smaller shape may succeed); DSA_E_HIP for another HIP failure. */
 dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out);
 
-/* Synchronise the device, then free everything.  NULL is accepted. */
+/* Synchronise the device, then free everything the session owns.  NULL is
+ * accepted.  Always DSA_OK (zhuai.tech feed article "用 Rust 统一管理内存与显存
+ * 所有权：从 Arc 到 GPU Completion", its closing list of limits: waiting for
+ * the GPU is an explicit call, and a destructor is only a last safety net that
+ * reports no error); synchronise and check the last call's status first. */
 dsa_status dsa_session_destroy(dsa_session* s);
 
-/* Append n rows at positions L..L+n-1 of unit (layer, seq).
- *   index_keys: device, bf16 [n][index_dim], row-major.
- *   rows:       device, uint8 [n][row_bytes] packed Q8G64 rows.
+/* Append n rows at positions L..L+n-1 of unit (layer, seq) (offload page,
+ * section "Decision 3": new rows go to a GPU recent ring and are written back
+ * to host memory in batches; section "Decision 2": the owner quantises a row
+ * once and moves the packed 656 bytes).
+ *   index_keys: device, bf16 [n][index_dim], row-major, 16-byte aligned.
+ *   rows:       device, uint8 [n][row_bytes] packed Q8G64 rows, 16-byte aligned.
  * Keys go to the HBM key store.  Offload mode: rows enter the recent ring;
  * if the ring (ring_rows + max_query_rows rows) would overflow, whole batches
  * of ring_rows oldest rows are written to the host mirror first.  Resident
- * mode: rows go to the HBM row store.  DSA_E_CAPACITY if L+n > max_positions
- * (nothing is appended). */
+ * mode: rows go to the HBM row store.  Both buffers are read in stream order
+ * and may be reused once the stream has passed this call.  Errors (nothing is
+ * appended): DSA_E_INVALID for n < 0, a bad unit or a NULL / misaligned
+ * pointer; DSA_E_CAPACITY if L+n > max_positions.  n == 0 is a no-op. */
 dsa_status dsa_append_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t n,
                            const void* index_keys, const void* rows, hipStream_t stream);
 
@@ -192,13 +216,20 @@ dsa_status dsa_quantize_rows(dsa_session* s, int64_t n, const void* latent, cons
 dsa_status dsa_append_latent(dsa_session* s, int32_t layer, int32_t seq, int64_t n, const void* index_keys,
                              const void* latent, const void* rope, hipStream_t stream);
 
-/* Write every pending ring row of the unit to the host mirror (M = L). */
+/* Write every pending ring row of the unit to the host mirror (M = L), in
+ * stream order (offload page, section "Capacity must survive the session
+ * lifecycle": before the full history is exported, pending rows are flushed
+ * and the host row count must reach the logical row count; dsa_mirror_rows
+ * reports that count).  Resident mode: no-op.  DSA_E_INVALID for a bad unit. */
 dsa_status dsa_flush(dsa_session* s, int32_t layer, int32_t seq, hipStream_t stream);
 
 /* Offload mode: refill the unit's hot cache with its most recent min(S, L)
  * positions (slot v holds position L-min(S,L)+v), clear all round marks and
- * set the hand past the last filled slot.  Requires a flushed unit (M == L),
- * else DSA_E_STATE.  Resident mode: no-op. */
+ * set the hand past the last filled slot (offload page, section "Starting
+ * point": the hot cache is not a sliding window, but a session starts from
+ * its most recent rows; the page's end-to-end runs keep a 32,768-row hot
+ * cache).  Requires a flushed unit (M == L), else DSA_E_STATE.  Resident
+ * mode: no-op. */
 dsa_status dsa_warm_hot(dsa_session* s, int32_t layer, int32_t seq, hipStream_t stream);
 
 /* Drop the last n rows of unit (layer, seq): L becomes L-n and the mirror
@@ -217,12 +248,20 @@ dsa_status dsa_warm_hot(dsa_session* s, int32_t layer, int32_t seq, hipStream_t 
 dsa_status dsa_rollback_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t n, hipStream_t stream);
 
 /* One decode step of every sequence of `layer`, R = rows_per_seq query rows
- * each (1 <= R <= max_query_rows; every sequence must hold at least R rows).
- *   index_q:  device bf16 [n_seqs][R][index_heads][index_dim]
+ * each: steps 1-9 of the step semantics above (offload page, section
+ * "Starting point": the DSA indexer scores the whole history and attention
+ * reads only the Top-2048 rows; section "Decision 3": selection, slot lookup
+ * and gather stay on the GPU, with no per-selection CPU work; section "GPU
+ * cache management errs too": round-scoped visibility, pins, and the ring walk
+ * that skips pinned slots).  1 <= R <= max_query_rows; every sequence must
+ * already hold at least R rows (its last R rows are the query positions).
+ *   index_q:  device bf16 [n_seqs][R][index_heads][index_dim], 16-byte aligned
  *   index_w:  device f32  [n_seqs][R][index_heads]
- *   q_latent: device bf16 [n_seqs][R][heads][latent_dim]
- *   q_rope:   device bf16 [n_seqs][R][heads][rope_dim]
- *   out:      device f32  [n_seqs][R][heads][latent_dim]  (written) */
+ *   q_latent: device bf16 [n_seqs][R][heads][latent_dim], 16-byte aligned
+ *   q_rope:   device bf16 [n_seqs][R][heads][rope_dim], 16-byte aligned
+ *   out:      device f32  [n_seqs][R][heads][latent_dim]  (written)
+ * Errors (nothing enqueued): DSA_E_INVALID for a bad layer, R or buffer;
+ * DSA_E_STATE if a sequence holds fewer than R rows. */
 dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq,
                            const void* index_q, const float* index_w, const void* q_latent,
                            const void* q_rope, float* out, hipStream_t stream);
@@ -272,8 +311,12 @@ dsa_status dsa_prefetch_reuse(dsa_session* s, int32_t layer, int32_t src_layer, 
 dsa_status dsa_unit_state(const dsa_session* s, int32_t layer, int32_t seq, int64_t out[4]);
 
 /* Rows of the unit known to be in the host mirror: the count of the most
- * recent writeback whose completion has been observed (non-blocking query).
- * After dsa_flush and a synchronisation of its stream this equals L. */
+ * recent writeback whose completion has been observed (non-blocking query;
+ * offload page, section "Capacity must survive the session lifecycle": the
+ * host row count must reach the logical row count before the history is
+ * exported).  Until the unit is flushed and that flush has completed it may be
+ * below L; after dsa_flush and a synchronisation of its stream it equals L.
+ * Resident mode: 0 (there is no mirror). */
 dsa_status dsa_mirror_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t* rows);
 
 /* Text of the most recent error on this session ("" if none).  The pointer
@@ -338,6 +381,25 @@ dsa_status dsa_debug_get(dsa_session* s, int32_t layer, int32_t seq, int32_t ite
 dsa_status dsa_set_kernel_timing(dsa_session* s, int32_t enable);
 dsa_status dsa_kernel_times(dsa_session* s, int64_t counts[DSA_KERNEL_KINDS],
                             double total_ms[DSA_KERNEL_KINDS]);
+
+/* ---- Fault injection, for tests of the error model -------------------------
+ * Forces an error condition from the host, so that every kernel still runs to
+ * its normal end (offload page, section "Capacity must survive the session
+ * lifecycle": integrity is checked, not assumed).
+ *   DSA_INJECT_HIP_FAILURE: the next HIP call the session checks is not made
+ *     and reports a failure: that call returns DSA_E_HIP, later calls
+ *     DSA_E_STATE (layer and seq are checked but otherwise unused).
+ *   DSA_INJECT_BAD_SLOT: offload mode; enqueues on `stream` a kernel that gives
+ *     every cached position of unit (layer, seq) an out-of-range slot index,
+ *     so the next decode step's hits fail the device-side checks: they are
+ *     skipped, and the first call after that step has run returns DSA_E_STATE.
+ * DSA_E_INVALID for an unknown `what` or a bad unit; DSA_E_UNSUPPORTED for
+ * DSA_INJECT_BAD_SLOT on a resident session. */
+typedef enum {
+  DSA_INJECT_HIP_FAILURE = 0,
+  DSA_INJECT_BAD_SLOT = 1
+} dsa_injection;
+dsa_status dsa_debug_inject(dsa_session* s, int32_t layer, int32_t seq, int32_t what, hipStream_t stream);
 
 #ifdef __cplusplus
 }

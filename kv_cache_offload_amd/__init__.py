@@ -37,7 +37,8 @@ EXPORTS = ("dsa_session_create", "dsa_session_destroy", "dsa_append_rows", "dsa_
            "dsa_decode_step", "dsa_decode_step_reuse", "dsa_prefetch_reuse", "dsa_unit_state",
            "dsa_mirror_rows",
            "dsa_last_error", "dsa_debug_size", "dsa_debug_get", "dsa_set_kernel_timing",
-           "dsa_kernel_times")
+           "dsa_kernel_times", "dsa_debug_inject")
+INJECT_HIP_FAILURE, INJECT_BAD_SLOT = 0, 1
 
 
 class dsa_config(ctypes.Structure):
@@ -91,6 +92,7 @@ def _load_library() -> ctypes.CDLL:
         "dsa_debug_get": ([P, i32, i32, i32, P, sz, P], ctypes.c_int),
         "dsa_set_kernel_timing": ([P, i32], ctypes.c_int),
         "dsa_kernel_times": ([P, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
+        "dsa_debug_inject": ([P, i32, i32, i32, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -199,6 +201,10 @@ def dsa_kernel_times(h):
     ms = (ctypes.c_double * len(KERNEL_KINDS))()
     st = _lib.dsa_kernel_times(_handle(h), counts, ms)
     return st, list(counts), list(ms)
+
+
+def dsa_debug_inject(h, layer, seq, what, stream) -> int:
+    return _lib.dsa_debug_inject(_handle(h), layer, seq, what, stream)
 
 
 # ---------------------------------------------------------------- torch convenience
@@ -313,6 +319,11 @@ class Session:
         """Turn per-kernel timing on (events pre-created for reserve_steps steps) or off."""
         n = max(1, int(reserve_steps)) if enable else 0
         self._check("dsa_set_kernel_timing", dsa_set_kernel_timing(self.h, n))
+
+    def inject(self, what, layer=0, seq=0):
+        """Force an error condition from the host (tests of the error model)."""
+        code = {"hip_failure": INJECT_HIP_FAILURE, "bad_slot": INJECT_BAD_SLOT}.get(what, what)
+        self._check("dsa_debug_inject", dsa_debug_inject(self.h, layer, seq, code, self._stream()))
 
     def kernel_times(self):
         st, counts, ms = dsa_kernel_times(self.h)

@@ -131,7 +131,26 @@ struct StepArgs {
   int n_seqs;
   int R;
   int64_t l_max;          // max L over the layer's sequences (grid sizing)
+  uint32_t* err;          // device address of the session's error flags (kDevErrWords words)
 };
+
+// Device-side consistency checks.  A kernel that finds a position, slot or
+// union index outside what the step's plan allows skips that access (so it
+// stays in bounds) and raises one of these flags in the session's error block:
+// pinned host memory mapped into the device, one word per kind, written with a
+// plain system-scope store (no read-modify-write over the host link).  The
+// session reads the block at the entry of every call and fails the session
+// (DSA_E_STATE, with the kinds in the error text) once any flag is set.
+enum DevErr {
+  kErrSelection = 0,      // a selected position out of range, unmarked in the round's bitmap, or past the union
+  kErrHitSlot = 1,        // a hit's slot index outside [0, S)
+  kErrVictim = 2,         // a victim slot outside [0, S), or the position it evicts out of range
+  kErrWriteback = 3,      // a ring writeback position out of range
+  kDevErrWords = 8
+};
+__device__ inline void raise_err(uint32_t* err, int kind) {
+  __hip_atomic_store(err + kind, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 
 // Optional timing of the next launches: `start` goes with the first kernel
 // launched after it is set (then cleared), `stop` with every kernel, so a
@@ -213,6 +232,8 @@ hipError_t launch_append(const Geometry& g, const UnitDev& unit, int64_t L, int6
 hipError_t launch_flush(const Geometry& g, const UnitDev& unit, int64_t M, int64_t L, hipStream_t st);
 hipError_t launch_warm(const Geometry& g, const UnitDev& unit, int64_t L, hipStream_t st);
 hipError_t launch_rollback(const UnitDev& unit, int64_t L, int64_t M, hipStream_t st);
+// Test hook: every cached position of [0, L) gets an out-of-range slot index (offload).
+hipError_t launch_inject_bad_slot(const Geometry& g, const UnitDev& unit, int64_t L, hipStream_t st);
 // Keys of positions [0, L) in plain row order [L][index_dim], for inspection.
 hipError_t launch_keys_linear(const UnitDev& unit, int64_t L, uint16_t* dst, hipStream_t st);
 // Selection reuse and prefetch (k_reuse.hip).

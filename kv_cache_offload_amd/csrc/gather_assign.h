@@ -58,7 +58,10 @@ __device__ inline void assign_block(const GatherKArgs& ka, int block, int seq) {
     if (t >= (int64_t)ka.ring_rows * kCopyChunks16) return;
     const int64_t rb = ka.row_bytes;
     const int64_t p = wb + t / kCopyChunks16, c = t % kCopyChunks16;
-    if (p >= ka.max_positions) return;
+    if (p >= ka.max_positions) {                       // never, for a consistent round state
+      raise_err(a.err, kErrWriteback);
+      return;
+    }
     const u32x4 v = *reinterpret_cast<const DSA_GLOBAL u32x4*>(u.ring + (p % ka.ring_cap) * rb + c * 16);
     *reinterpret_cast<DSA_GLOBAL u32x4*>(u.rows + p * rb + c * 16) = v;
     return;
@@ -104,6 +107,8 @@ __device__ inline void assign_block(const GatherKArgs& ka, int block, int seq) {
         if (src >= 0 && src < ka.S) {
           u.pin_round[src] = round;
           if (ka.clock) g_or(&u.ref[src >> 5], 1u << (src & 31));
+        } else {
+          raise_err(a.err, kErrHitSlot);
         }
       } else {
         const uint32_t k = bm + __popc(sw & ~hw & ~rw & below);
@@ -112,6 +117,7 @@ __device__ inline void assign_block(const GatherKArgs& ka, int block, int seq) {
           kind = SRC_MISS;
           const i32x2 vo = s.victim[k];                // (slot, position it held), from the plan
           const int32_t v = vo.x, old = vo.y;
+          if (v < 0 || v >= ka.S || old >= ka.max_positions) raise_err(a.err, kErrVictim);
           if (v >= 0 && v < ka.S) {
             if (old >= 0 && old < ka.max_positions) {
               u.pos_slot[old] = (i32x2){-1, -1};
@@ -135,6 +141,8 @@ __device__ inline void assign_block(const GatherKArgs& ka, int block, int seq) {
       s.kind[ux] = kind;
       s.src[ux] = src;
       s.pdesc[p] = (i32x4){(int32_t)ux, kind, src, fill};
+    } else {
+      raise_err(a.err, kErrSelection);
     }
   }
 }

@@ -323,15 +323,18 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
 }
 
 // Called by every workgroup (one per query row) of a sequence at the end of its
-// selection; the last of the n_rows workgroups to arrive runs the plan.  The
-// workgroup barrier (a workgroup-scope release and acquire) orders every wave's
-// marks before thread 0's arrival, an acquire-release atomic at device scope;
-// by transitivity the marks of every earlier arrival are visible to every wave
-// of the last workgroup after its barrier.  Only one wave per workgroup carries
-// the device-scope cache maintenance.  No workgroup waits for another.
+// selection; the last of the n_rows workgroups to arrive runs the plan.  Every
+// wave first releases its own marks (relaxed atomic ORs) at device scope: a
+// workgroup barrier alone does not wait for another wave's outstanding memory
+// operations, so without it a mark could still be in flight when thread 0
+// announces the arrival.  Thread 0's arrival is an acquire-release atomic at
+// device scope; the last workgroup's barrier after it hands the acquire to every
+// wave (they share the CU's caches), so all marks of all arrivals are visible to
+// the plan.  No workgroup waits for another.
 __device__ inline void plan_if_last(const UnitG& u, const ScratchG& s, const PlanParams& pp, uint32_t n_rows,
                                     const PlanState& ps, uint32_t* lds) {
   __shared__ uint32_t s_last;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(s.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);

@@ -145,6 +145,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   // requested here but used after the rows have been requested.
   const int n_sel = s.sel_n[r];
   i32x2 victim = (i32x2){-1, -1};
+  bool assigned = false;                                 // this row's miss took the plan's victim
   if (tid < kSplit) {
     const int64_t M = s.info[kInfoM];
     const uint32_t n_assigned = (uint32_t)s.info[kInfoAssigned];
@@ -158,6 +159,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     const uint32_t bit = 1u << (pos & 31), below = bit - 1u;
     const uint32_t ux = bu + __popc(sw & below);
     const DSA_GLOBAL uint8_t* from = nullptr;
+    // A selected index whose position, bitmap bit, union index, hit slot or
+    // victim slot is not what the plan allows is skipped (its row masked) and
+    // raises the session's error flag: such a plan is inconsistent.
     if (ok && (sw & bit) && ux < (uint32_t)ka.max_union) {
       if (!ka.off) {
         from = u.rows + (int64_t)pos * rb;
@@ -168,12 +172,18 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
         } else if (hw & bit) {
           const int32_t slot = ps.x;
           if (slot >= 0 && slot < ka.S) from = u.slots + (int64_t)slot * rb;
+          else raise_err(a.err, kErrHitSlot);
         } else {
           const uint32_t k = bm + __popc(sw & ~hw & ~rw & below);
-          if (k < n_assigned) victim = s.victim[k];    // (slot, position it held)
+          if (k < n_assigned) {
+            victim = s.victim[k];                        // (slot, position it held)
+            assigned = true;
+          }
           from = u.rows + (int64_t)pos * rb;
         }
       }
+    } else if (j < n_sel) {
+      raise_err(a.err, kErrSelection);
     }
     s_from[tid] = from;
     s_ux[tid] = from ? (int)ux : -1;
@@ -213,7 +223,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     }
   };
   request(0);
-  if (tid < kSplit) s_fill[tid] = (s_from[tid] && victim.x >= 0 && victim.x < ka.S) ? victim.x : -1;
+  if (tid < kSplit) {
+    const bool fill_ok = victim.x >= 0 && victim.x < ka.S;
+    if (assigned && !fill_ok) raise_err(a.err, kErrVictim);
+    s_fill[tid] = (s_from[tid] && assigned && fill_ok) ? victim.x : -1;
+  }
   __syncthreads();                                       // s_fill before block 0 is staged
 
   f32x4 o[32];

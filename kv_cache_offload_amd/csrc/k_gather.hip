@@ -154,6 +154,17 @@ __global__ __launch_bounds__(64) void rollback_kernel(UnitDev ud, int64_t L, int
   }
 }
 
+// Test hook (dsa_debug_inject): every cached position of [0, L) is given the
+// slot index S + 1, outside the cache, so that the next round's hits fail the
+// device-side checks of attention and the assign pass (which then skip them).
+__global__ __launch_bounds__(256) void bad_slot_kernel(UnitDev ud, int64_t L, int S) {
+  const UnitG u = as_global(ud);
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < L; p += (int64_t)gridDim.x * blockDim.x) {
+    const i32x2 ps = u.pos_slot[p];
+    if (ps.x >= 0) u.pos_slot[p] = (i32x2){S + 1, ps.y};
+  }
+}
+
 unsigned grid_for(int64_t work, int64_t cap = 4096) {
   int64_t b = (work + 255) / 256;
   if (b < 1) b = 1;
@@ -201,6 +212,10 @@ hipError_t launch_keys_linear(const UnitDev& unit, int64_t L, uint16_t* dst, hip
 
 hipError_t launch_rollback(const UnitDev& unit, int64_t L, int64_t M, hipStream_t st) {
   return launch_k(rollback_kernel, dim3(1), dim3(64), 0, st, unit, L, M);
+}
+
+hipError_t launch_inject_bad_slot(const Geometry& g, const UnitDev& unit, int64_t L, hipStream_t st) {
+  return launch_k(bad_slot_kernel, dim3(grid_for(L)), dim3(256), 0, st, unit, L, g.hot_slots);
 }
 
 }  // namespace dsa

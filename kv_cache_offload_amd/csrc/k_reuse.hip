@@ -46,6 +46,7 @@ __global__ __launch_bounds__(kPlanThreads) void reuse_mark_kernel(MarkKArgs ka) 
   for (int j = threadIdx.x; j < n; j += kPlanThreads) {
     const int32_t pos = sel[j];
     if (pos >= 0 && pos < ps.L) g_or(&s.selmask[pos >> 5], 1u << (pos & 31));
+    else raise_err(a.err, kErrSelection);
   }
   plan_if_last(u, s, ka.plan, (uint32_t)a.R, ps, lds);
 }
@@ -53,6 +54,7 @@ __global__ __launch_bounds__(kPlanThreads) void reuse_mark_kernel(MarkKArgs ka) 
 struct FillKArgs {
   StepArgs a;
   int max_union, row_bytes, S;
+  int64_t max_positions;
 };
 
 // Prefetch: copy every union entry that took a slot from the host mirror into
@@ -67,9 +69,17 @@ __global__ __launch_bounds__(256) void prefetch_fill_kernel(FillKArgs ka) {
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < U * kCopyChunks16;
        t += (int64_t)gridDim.x * blockDim.x) {
     const int64_t ux = t / kCopyChunks16, c = t % kCopyChunks16;
-    if (ux >= ka.max_union) break;
+    if (ux >= ka.max_union) {
+      raise_err(a.err, kErrSelection);
+      break;
+    }
     const int32_t p = s.uni[ux];
+    if (p < 0 || p >= ka.max_positions) {
+      raise_err(a.err, kErrSelection);
+      continue;
+    }
     const int32_t fill = s.pdesc[p].w;
+    if (fill >= ka.S) raise_err(a.err, kErrVictim);
     if (fill < 0 || fill >= ka.S) continue;
     const u32x4 v = *reinterpret_cast<const DSA_GLOBAL u32x4*>(u.rows + (int64_t)p * rb + c * 16);
     *reinterpret_cast<DSA_GLOBAL u32x4*>(u.slots + (int64_t)fill * rb + c * 16) = v;
@@ -86,7 +96,7 @@ hipError_t launch_reuse_mark(const Geometry& g, const StepArgs& a, const SeqScra
 
 hipError_t launch_prefetch_fill(const Geometry& g, const StepArgs& a, hipStream_t st) {
   const int max_union = g.r_max * g.top_k;
-  FillKArgs ka{a, max_union, g.row_bytes, g.hot_slots};
+  FillKArgs ka{a, max_union, g.row_bytes, g.hot_slots, g.max_positions};
   // host-link bound: 64 blocks keep 256 KiB of reads in flight, more than the
   // link's bandwidth-delay product, and leave the CUs to the kernels it overlaps
   int64_t blocks = ((int64_t)max_union * kCopyChunks16 + 255) / 256;

@@ -84,6 +84,9 @@ struct dsa_session {
   std::vector<hipEvent_t> free_events;
   int64_t t_counts[DSA_KERNEL_KINDS] = {};
   double t_ms[DSA_KERNEL_KINDS] = {};
+  uint32_t* err_host = nullptr;            // device-side check flags: pinned, mapped host memory
+  uint32_t* err_dev = nullptr;             // the same block's device address (kernels write it)
+  bool inject_hip = false;                 // test hook: the next checked HIP call reports a failure
 };
 
 namespace {
@@ -99,10 +102,25 @@ dsa_status hip_fail(dsa_session* s, hipError_t e, const char* what) {
   return DSA_E_HIP;
 }
 
-#define HIPCHK(expr, what)                         \
-  do {                                             \
-    hipError_t e_ = (expr);                        \
-    if (e_ != hipSuccess) return hip_fail(s, e_, what); \
+// Test hook of dsa_debug_inject: true once, for the next checked HIP call,
+// which is then not made.
+bool take_injected(dsa_session* s) {
+  if (!s->inject_hip) return false;
+  s->inject_hip = false;
+  return true;
+}
+
+dsa_status injected_fail(dsa_session* s, const char* what) {
+  s->failed = true;
+  s->err = std::string("injected failure of ") + what;
+  return DSA_E_HIP;
+}
+
+#define HIPCHK(expr, what)                                 \
+  do {                                                     \
+    if (take_injected(s)) return injected_fail(s, what);   \
+    hipError_t e_ = (expr);                                \
+    if (e_ != hipSuccess) return hip_fail(s, e_, what);    \
   } while (0)
 
 // Keeps the caller's current device.
@@ -118,9 +136,26 @@ struct DeviceGuard {
   }
 };
 
+// The device-side check flags (kernels set them when a plan is inconsistent;
+// see DevErr): read without blocking, so a step's flags are seen by the first
+// call made after the step has run.  Any flag fails the session.
+bool device_checks_failed(dsa_session* s) {
+  if (!s->err_host) return false;
+  static const char* const names[kDevErrWords] = {"selection or union index", "hit slot", "victim slot",
+                                                  "writeback position", "", "", "", ""};
+  std::string kinds;
+  for (int k = 0; k < kDevErrWords; ++k)
+    if (reinterpret_cast<volatile uint32_t*>(s->err_host)[k]) kinds += (kinds.empty() ? "" : ", ") + std::string(names[k]);
+  if (kinds.empty()) return false;
+  s->failed = true;
+  s->err = "device-side consistency check failed (" + kinds + " out of range); the session's state is no longer trusted";
+  return true;
+}
+
 dsa_status entry(dsa_session* s) {
   if (!s) return DSA_E_INVALID;
   if (s->failed) return DSA_E_STATE;
+  if (device_checks_failed(s)) return DSA_E_STATE;
   s->err.clear();
   return DSA_OK;
 }
@@ -163,6 +198,7 @@ hipEvent_t take_event(dsa_session* s) {
 template <class F>
 dsa_status timed_launch(dsa_session* s, int kind, const char* what, F&& fn) {
   hipEvent_t a = nullptr, b = nullptr;
+  if (take_injected(s)) return injected_fail(s, what);
   if (s->timing) {
     a = take_event(s);
     b = take_event(s);
@@ -184,6 +220,76 @@ dsa_status timed_launch(dsa_session* s, int kind, const char* what, F&& fn) {
     }
   }
   return DSA_OK;
+}
+
+// One sequence's step scratch: 256-byte aligned pieces at these offsets of a
+// block of `bytes` bytes.  The session's arena holds one block per sequence.
+struct ScrOff {
+  size_t scores, sel, sel_n, uni, kind, src, map, compact, po, pml, cnt, info, selmask, hitmask, base_u, base_m,
+      pdesc, victim, done, hist0, hist1, cand, cand_n, rowdig;
+  size_t bytes;
+};
+
+ScrOff scratch_layout(const Geometry& g) {
+  const int64_t P = g.p_pad, RK = (int64_t)g.r_max * g.top_k, rb = g.row_bytes;
+  ScrOff o{};
+  size_t cur = 0;
+  auto take = [&](size_t bytes) { size_t at = cur; cur += align_up(bytes ? bytes : 1); return at; };
+  o.scores = take((size_t)g.r_max * P * 4);
+  o.sel = take((size_t)RK * 4);
+  o.sel_n = take((size_t)g.r_max * 4);
+  o.uni = take((size_t)RK * 4);
+  o.kind = take((size_t)RK * 4);
+  o.src = take((size_t)RK * 4);
+  o.map = take((size_t)RK * 4);
+  o.compact = take((size_t)RK * rb);
+  o.po = take((size_t)g.r_max * g.nsplit_max * g.heads * g.latent * 4);
+  o.pml = take((size_t)g.r_max * g.nsplit_max * g.heads * 2 * 4);
+  o.cnt = take(8 * 8);
+  o.info = take(8 * 8);
+  o.selmask = take((size_t)P / 32 * 4);
+  o.hitmask = take((size_t)P / 32 * 4);
+  o.base_u = take((size_t)P / 32 * 4);
+  o.base_m = take((size_t)P / 32 * 4);
+  o.pdesc = take((size_t)P * 16);
+  o.victim = take((size_t)g.s_words * 32 * 8);
+  o.done = take(4);
+  o.hist0 = take((size_t)kHistReps * g.r_max * kRadixBins * 4);
+  o.hist1 = take((size_t)g.r_max * kRadixBins * 4);
+  o.cand = take((size_t)g.r_max * P * 8);
+  o.cand_n = take((size_t)g.r_max * g.n_chunks * 4);
+  o.rowdig = take((size_t)g.r_max * 16);
+  o.bytes = cur;
+  return o;
+}
+
+SeqScratch scratch_at(uint8_t* base, const ScrOff& o) {
+  SeqScratch c{};
+  c.scores = reinterpret_cast<float*>(base + o.scores);
+  c.sel = reinterpret_cast<int32_t*>(base + o.sel);
+  c.sel_n = reinterpret_cast<int32_t*>(base + o.sel_n);
+  c.uni = reinterpret_cast<int32_t*>(base + o.uni);
+  c.kind = reinterpret_cast<int32_t*>(base + o.kind);
+  c.src = reinterpret_cast<int32_t*>(base + o.src);
+  c.map = reinterpret_cast<int32_t*>(base + o.map);
+  c.compact = base + o.compact;
+  c.part_o = reinterpret_cast<float*>(base + o.po);
+  c.part_ml = reinterpret_cast<float*>(base + o.pml);
+  c.counters = reinterpret_cast<int64_t*>(base + o.cnt);
+  c.info = reinterpret_cast<int64_t*>(base + o.info);
+  c.selmask = reinterpret_cast<uint32_t*>(base + o.selmask);
+  c.hitmask = reinterpret_cast<uint32_t*>(base + o.hitmask);
+  c.base_u = reinterpret_cast<uint32_t*>(base + o.base_u);
+  c.base_m = reinterpret_cast<uint32_t*>(base + o.base_m);
+  c.pdesc = reinterpret_cast<i32x4*>(base + o.pdesc);
+  c.victim = reinterpret_cast<i32x2*>(base + o.victim);
+  c.done = reinterpret_cast<uint32_t*>(base + o.done);
+  c.hist0 = reinterpret_cast<uint32_t*>(base + o.hist0);
+  c.hist1 = reinterpret_cast<uint32_t*>(base + o.hist1);
+  c.cand = reinterpret_cast<i32x2*>(base + o.cand);
+  c.cand_n = reinterpret_cast<uint32_t*>(base + o.cand_n);
+  c.rowdig = reinterpret_cast<int32_t*>(base + o.rowdig);
+  return c;
 }
 
 dsa_status validate_config(const dsa_config* c, std::string* why) {
@@ -226,6 +332,9 @@ void free_all(dsa_session* s) {
   s->pf_done.clear();
   if (s->mirror_block) (void)hipHostFree(s->mirror_block);
   s->mirror_block = nullptr;
+  if (s->err_host) (void)hipHostFree(s->err_host);
+  s->err_host = nullptr;
+  s->err_dev = nullptr;
   if (s->arena) (void)hipFree(s->arena);
   s->uh.clear();
   s->timed.clear();
@@ -266,6 +375,7 @@ StepArgs step_args(const dsa_session* s, int32_t layer, int R, bool prefetch_set
   a.rows_stride = s->rows_stride;
   a.n_seqs = s->cfg.n_seqs;
   a.R = R;
+  a.err = s->err_dev;
   a.l_max = 0;
   for (int q = 0; q < s->cfg.n_seqs; ++q) a.l_max = std::max(a.l_max, s->uh[unit_index(s, layer, q)].L);
   return a;
@@ -274,6 +384,16 @@ StepArgs step_args(const dsa_session* s, int32_t layer, int R, bool prefetch_set
 // A round of `layer` on the selection of the most recent full decode step,
 // which must be src_layer's, with the same rows per sequence and, for every
 // sequence, the same row count as src_layer had then.
+// A prefetch round of `layer` enqueued on another stream may still write the
+// layer's ring batch back to the mirror and update its slot tables: work of the
+// same layer enqueued on `stream` (appends, which reuse ring entries; flush,
+// warm and rollback, which move M, L and the slots) waits for it first.
+dsa_status wait_prefetch(dsa_session* s, int32_t layer, hipStream_t stream) {
+  if (s->pf_pending[layer] && s->pf_stream[layer] != stream)
+    HIPCHK(hipStreamWaitEvent(stream, s->pf_done[layer], 0), "hipStreamWaitEvent");
+  return DSA_OK;
+}
+
 dsa_status check_reuse(dsa_session* s, int32_t layer, int32_t src_layer, int32_t R) {
   dsa_status st = entry(s);
   if (st != DSA_OK) return st;
@@ -354,36 +474,9 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     uo[i].dyn = take(32);
     uo[i].totals = take(64);
   }
-  struct ScrOff { size_t scores, sel, sel_n, uni, kind, src, map, compact, po, pml, cnt, info,
-                  selmask, hitmask, base_u, base_m, pdesc, victim, done, hist0, hist1, cand,
-                  cand_n, rowdig; };
-  std::vector<ScrOff> so(cfg->n_seqs);
-  for (int q = 0; q < cfg->n_seqs; ++q) {
-    so[q].scores = take((size_t)g.r_max * P * 4);
-    so[q].sel = take((size_t)RK * 4);
-    so[q].sel_n = take((size_t)g.r_max * 4);
-    so[q].uni = take((size_t)RK * 4);
-    so[q].kind = take((size_t)RK * 4);
-    so[q].src = take((size_t)RK * 4);
-    so[q].map = take((size_t)RK * 4);
-    so[q].compact = take((size_t)RK * rb);
-    so[q].po = take((size_t)g.r_max * g.nsplit_max * g.heads * g.latent * 4);
-    so[q].pml = take((size_t)g.r_max * g.nsplit_max * g.heads * 2 * 4);
-    so[q].cnt = take(8 * 8);
-    so[q].info = take(8 * 8);
-    so[q].selmask = take((size_t)P / 32 * 4);
-    so[q].hitmask = take((size_t)P / 32 * 4);
-    so[q].base_u = take((size_t)P / 32 * 4);
-    so[q].base_m = take((size_t)P / 32 * 4);
-    so[q].pdesc = take((size_t)P * 16);
-    so[q].victim = take((size_t)g.s_words * 32 * 8);
-    so[q].done = take(4);
-    so[q].hist0 = take((size_t)kHistReps * g.r_max * kRadixBins * 4);
-    so[q].hist1 = take((size_t)g.r_max * kRadixBins * 4);
-    so[q].cand = take((size_t)g.r_max * P * 8);
-    so[q].cand_n = take((size_t)g.r_max * g.n_chunks * 4);
-    so[q].rowdig = take((size_t)g.r_max * 16);
-  }
+  const ScrOff lay = scratch_layout(g);
+  std::vector<size_t> so(cfg->n_seqs);
+  for (int q = 0; q < cfg->n_seqs; ++q) so[q] = take(lay.bytes);
   // the prefetch rounds' scratch: only what the plan, the assign and the fill use
   struct PfOff { size_t cnt, info, uni, kind, src, selmask, hitmask, base_u, base_m, pdesc, victim, done; };
   std::vector<PfOff> pf(off ? cfg->n_seqs : 0);
@@ -419,6 +512,18 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   }
   uint8_t* base = static_cast<uint8_t*>(s->arena);
   if (hipMemset(s->arena, 0, s->arena_bytes) != hipSuccess) return bail(DSA_E_HIP, "hipMemset");
+  {
+    void* eh = nullptr;
+    if (hipHostMalloc(&eh, kDevErrWords * sizeof(uint32_t), hipHostMallocMapped) != hipSuccess || !eh) {
+      (void)hipGetLastError();
+      return bail(DSA_E_NOMEM, "hipHostMalloc");
+    }
+    s->err_host = static_cast<uint32_t*>(eh);
+    std::memset(s->err_host, 0, kDevErrWords * sizeof(uint32_t));
+    void* ed = nullptr;
+    if (hipHostGetDevicePointer(&ed, eh, 0) != hipSuccess) return bail(DSA_E_HIP, "hipHostGetDevicePointer");
+    s->err_dev = static_cast<uint32_t*>(ed);
+  }
 
   s->mirrors.assign(n_units, nullptr);
   uint8_t* mirror_dev = nullptr;
@@ -467,30 +572,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   s->scr.resize(cfg->n_seqs);
   for (int q = 0; q < cfg->n_seqs; ++q) {
     SeqScratch& c = s->scr[q];
-    c.scores = reinterpret_cast<float*>(base + so[q].scores);
-    c.sel = reinterpret_cast<int32_t*>(base + so[q].sel);
-    c.sel_n = reinterpret_cast<int32_t*>(base + so[q].sel_n);
-    c.uni = reinterpret_cast<int32_t*>(base + so[q].uni);
-    c.kind = reinterpret_cast<int32_t*>(base + so[q].kind);
-    c.src = reinterpret_cast<int32_t*>(base + so[q].src);
-    c.map = reinterpret_cast<int32_t*>(base + so[q].map);
-    c.compact = base + so[q].compact;
-    c.part_o = reinterpret_cast<float*>(base + so[q].po);
-    c.part_ml = reinterpret_cast<float*>(base + so[q].pml);
-    c.counters = reinterpret_cast<int64_t*>(base + so[q].cnt);
-    c.info = reinterpret_cast<int64_t*>(base + so[q].info);
-    c.selmask = reinterpret_cast<uint32_t*>(base + so[q].selmask);
-    c.hitmask = reinterpret_cast<uint32_t*>(base + so[q].hitmask);
-    c.base_u = reinterpret_cast<uint32_t*>(base + so[q].base_u);
-    c.base_m = reinterpret_cast<uint32_t*>(base + so[q].base_m);
-    c.pdesc = reinterpret_cast<i32x4*>(base + so[q].pdesc);
-    c.victim = reinterpret_cast<i32x2*>(base + so[q].victim);
-    c.done = reinterpret_cast<uint32_t*>(base + so[q].done);
-    c.hist0 = reinterpret_cast<uint32_t*>(base + so[q].hist0);
-    c.hist1 = reinterpret_cast<uint32_t*>(base + so[q].hist1);
-    c.cand = reinterpret_cast<i32x2*>(base + so[q].cand);
-    c.cand_n = reinterpret_cast<uint32_t*>(base + so[q].cand_n);
-    c.rowdig = reinterpret_cast<int32_t*>(base + so[q].rowdig);
+    c = scratch_at(base + so[q], lay);
     if (hipMemset(c.sel, 0xFF, (size_t)RK * 4) != hipSuccess || hipMemset(c.map, 0xFF, (size_t)RK * 4) != hipSuccess)
       return bail(DSA_E_HIP, "hipMemset");
   }
@@ -524,7 +606,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   // check that every descriptor is sequence 0's moved by q strides.
   s->u_stride = n_units > 1 ? (int64_t)(uo[1].keys - uo[0].keys) : 0;
   s->rows_stride = off ? (int64_t)P * rb : s->u_stride;
-  s->s_stride = cfg->n_seqs > 1 ? (int64_t)(so[1].scores - so[0].scores) : 0;
+  s->s_stride = cfg->n_seqs > 1 ? (int64_t)(so[1] - so[0]) : 0;
   s->pf_stride = pf.size() > 1 ? (int64_t)(pf[1].cnt - pf[0].cnt) : 0;
   auto strided = [](const void* d0, const void* dq, int64_t q, int64_t stride, size_t bytes) {
     uint64_t a[64], b[64];
@@ -586,6 +668,7 @@ dsa_status append_common(dsa_session* s, int32_t layer, int32_t seq, int64_t n, 
   UnitHost& h = s->uh[ui];
   if (h.L + n > s->cfg.max_positions) return fail(s, DSA_E_CAPACITY, "append past max_positions");
   DeviceGuard dg(s->device);
+  if ((st = wait_prefetch(s, layer, stream)) != DSA_OK) return st;
   int64_t newM = h.M;
   if (s->g.mode == DSA_KV_OFFLOAD)
     while (h.L + n - newM > s->g.ring_cap) newM += s->g.ring_rows;
@@ -641,6 +724,7 @@ dsa_status dsa_flush(dsa_session* s, int32_t layer, int32_t seq, hipStream_t str
   UnitHost& h = s->uh[unit_index(s, layer, seq)];
   if (s->g.mode != DSA_KV_OFFLOAD) return DSA_OK;
   DeviceGuard dg(s->device);
+  if ((st = wait_prefetch(s, layer, stream)) != DSA_OK) return st;
   if (h.M < h.L) {
     HIPCHK(launch_flush(s->g, s->units[unit_index(s, layer, seq)], h.M, h.L, stream), "flush kernel");
     h.M = h.L;
@@ -656,6 +740,7 @@ dsa_status dsa_warm_hot(dsa_session* s, int32_t layer, int32_t seq, hipStream_t 
   UnitHost& h = s->uh[unit_index(s, layer, seq)];
   if (h.M != h.L) return fail(s, DSA_E_STATE, "warm needs a flushed unit (M == L)");
   DeviceGuard dg(s->device);
+  if ((st = wait_prefetch(s, layer, stream)) != DSA_OK) return st;
   HIPCHK(launch_warm(s->g, s->units[unit_index(s, layer, seq)], h.L, stream), "warm kernels");
   h.floor = h.L;
   return DSA_OK;
@@ -675,6 +760,7 @@ dsa_status dsa_rollback_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t
     return fail(s, DSA_E_STATE, "rollback below the rows the latest round could cache");
   const int64_t M2 = std::min(h.M, L2);
   DeviceGuard dg(s->device);
+  if ((st = wait_prefetch(s, layer, stream)) != DSA_OK) return st;
   HIPCHK(launch_rollback(s->units[ui], L2, M2, stream), "rollback kernel");
   h.L = L2;
   h.M = M2;
@@ -683,27 +769,25 @@ dsa_status dsa_rollback_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t
   return DSA_OK;
 }
 
-dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq, const void* index_q,
-                           const float* index_w, const void* q_latent, const void* q_rope, float* out,
-                           hipStream_t stream) {
+extern "C++" {
+namespace {
+
+// Validation, the step's launches, then the host-side round bookkeeping.
+dsa_status decode_common(dsa_session* s, int32_t layer, int32_t R, const void* index_q, const float* index_w,
+                         const void* q_latent, const void* q_rope, float* out, hipStream_t stream) {
   dsa_status st = entry(s);
   if (st != DSA_OK) return st;
   if (layer < 0 || layer >= s->cfg.n_layers) return fail(s, DSA_E_INVALID, "layer out of range");
-  const int R = rows_per_seq;
   if (R < 1 || R > s->g.r_max) return fail(s, DSA_E_INVALID, "rows_per_seq out of range");
   if (!index_q || !index_w || !q_latent || !q_rope || !out || !aligned(index_q, 16) || !aligned(q_latent, 16) ||
       !aligned(q_rope, 16) || !aligned(index_w, 4) || !aligned(out, 4))
     return fail(s, DSA_E_INVALID, "step buffers must be non-NULL; bf16 inputs 16-byte aligned");
   const int n_seqs = s->cfg.n_seqs;
-  int64_t l_max = 0;
-  for (int q = 0; q < n_seqs; ++q) {
-    const UnitHost& h = s->uh[unit_index(s, layer, q)];
-    if (h.L < R) return fail(s, DSA_E_STATE, "a sequence holds fewer rows than rows_per_seq");
-    l_max = std::max(l_max, h.L);
-  }
-  DeviceGuard dg(s->device);
-  const StepArgs a = step_args(s, layer, R, false);
+  for (int q = 0; q < n_seqs; ++q)
+    if (s->uh[unit_index(s, layer, q)].L < R) return fail(s, DSA_E_STATE, "a sequence holds fewer rows than rows_per_seq");
   const Geometry& g = s->g;
+  const StepArgs a = step_args(s, layer, R, false);
+  DeviceGuard dg(s->device);
   const uint16_t* iq = static_cast<const uint16_t*>(index_q);
   const uint16_t* ql = static_cast<const uint16_t*>(q_latent);
   const uint16_t* qr = static_cast<const uint16_t*>(q_rope);
@@ -726,6 +810,15 @@ dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq, 
   s->topk_R = R;
   for (int q = 0; q < n_seqs; ++q) s->topk_L[q] = s->uh[unit_index(s, layer, q)].L;
   return finish_round(s, layer, stream);
+}
+
+}  // namespace
+}  // extern "C++"
+
+dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq, const void* index_q,
+                           const float* index_w, const void* q_latent, const void* q_rope, float* out,
+                           hipStream_t stream) {
+  return decode_common(s, layer, rows_per_seq, index_q, index_w, q_latent, q_rope, out, stream);
 }
 
 dsa_status dsa_decode_step_reuse(dsa_session* s, int32_t layer, int32_t src_layer, int32_t rows_per_seq,
@@ -894,6 +987,26 @@ dsa_status dsa_debug_get(dsa_session* s, int32_t layer, int32_t seq, int32_t ite
   (void)K;
   HIPCHK(hipMemcpyAsync(dst, src, need, hipMemcpyDefault, stream), "hipMemcpyAsync");
   return DSA_OK;
+}
+
+dsa_status dsa_debug_inject(dsa_session* s, int32_t layer, int32_t seq, int32_t what, hipStream_t stream) {
+  dsa_status st = entry(s);
+  if (st != DSA_OK) return st;
+  if ((st = check_unit(s, layer, seq)) != DSA_OK) return st;
+  switch (what) {
+    case DSA_INJECT_HIP_FAILURE:
+      s->inject_hip = true;
+      return DSA_OK;
+    case DSA_INJECT_BAD_SLOT: {
+      if (s->g.mode != DSA_KV_OFFLOAD) return fail(s, DSA_E_UNSUPPORTED, "bad-slot injection needs offload mode");
+      DeviceGuard dg(s->device);
+      const size_t ui = unit_index(s, layer, seq);
+      HIPCHK(launch_inject_bad_slot(s->g, s->units[ui], s->uh[ui].L, stream), "injection kernel");
+      return DSA_OK;
+    }
+    default:
+      return fail(s, DSA_E_INVALID, "unknown injection");
+  }
 }
 
 dsa_status dsa_set_kernel_timing(dsa_session* s, int32_t enable) {
