@@ -109,8 +109,12 @@ WORKLOADS = {
 def bf16_bits(x) -> np.ndarray:
     """float64 -> float32 (RNE) -> bf16 bits (RNE), as uint16."""
     f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
-    u = f.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = f.view(np.uint32)
+    # finite values are at most 0xFF7FFFFF, so the sum stays below 2^32 in uint32
+    rounded = (u >> 16) & 1
+    rounded += u
+    rounded += 0x7FFF
+    rounded >>= 16
     nan = np.isnan(f)
     out = rounded.astype(np.uint16)
     if nan.any():
@@ -139,7 +143,7 @@ def _int_bf16(g: np.random.Generator, shape, lo: int, hi: int) -> np.ndarray:
 
 def make_rows(g: np.random.Generator, n: int, w: Workload) -> np.ndarray:
     """n packed Q8G64 rows: int8 latent | fp16 scales (LE) | bf16 RoPE (LE)."""
-    lat = g.integers(-127, 128, size=(n, w.latent_dim), dtype=np.int64).astype(np.int8)
+    lat = g.integers(-127, 128, size=(n, w.latent_dim), dtype=np.int8)
     scales = f16_bits(g.uniform(0.002, 0.02, size=(n, w.latent_dim // w.group)))
     rope = bf16_bits(g.standard_normal(size=(n, w.rope_dim)))
     out = np.empty((n, w.row_bytes), dtype=np.uint8)

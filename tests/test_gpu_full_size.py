@@ -3,11 +3,11 @@
 The first decode steps of each workload at its real shape: the same sessions,
 kernels and launch configurations `bench.py` times.  Every item the oracle keeps
 is compared (scores, selections, union, map, compact bytes, counters, slot
-table, outputs).  The 78-layer stress workload runs every layer on the GPU and
-compares a sample of layers against the oracle; the planted miss counts are
-checked on every layer.
+table, outputs).  The 78-layer stress workload compares every layer against the oracle
+on its first step, in both modes, with the planted hit and miss counts checked
+on every layer; offloaded and resident sessions are checked to agree bit for bit
+at the 50,023-row shape across a ring writeback.
 """
-import functools
 import time
 
 import numpy as np
@@ -15,7 +15,7 @@ import pytest
 
 import dsa_synth as S
 from oracle import MODE_OFFLOAD, MODE_RESIDENT
-from tests.parity_util import (HIST_CHUNK, compare_unit, dev_tensor, gpu_items, gpu_session, oracle_units,
+from tests.parity_util import (HIST_CHUNK, compare_unit, dev_tensor, gpu_session, load_history, oracle_units,
                                run_step)
 
 pytestmark = pytest.mark.gpu
@@ -25,15 +25,11 @@ def _note(*a):
     print("[gpu-full]", *a, flush=True)
 
 
-@functools.lru_cache(maxsize=None)
-def _history(name, layer, seq):
-    return S.history(S.WORKLOADS[name], layer, seq)
-
-
-def _load(w, sess, orcs, layers, seqs):
-    for gl, l in enumerate(layers):
+def _load(w, sess, orcs, layers, seqs, gpu_layers=None):
+    gpu_layers = range(len(layers)) if gpu_layers is None else gpu_layers
+    for gl, l in zip(gpu_layers, layers):
         for q in seqs:
-            keys, rows = _history(w.name, l, q)
+            keys, rows = S.history(w, l, q)
             if orcs is not None and (l, q) in orcs:
                 o = orcs[(l, q)]
                 o.append(keys, rows)
@@ -77,26 +73,94 @@ def test_batched_16x131k_offload():
     _full_size("batched_16x131k", MODE_OFFLOAD, steps=2)
 
 
-def test_stress_all_78_layers_sampled():
+def _stress_every_layer(mode):
+    # Every layer is loaded and stepped once with the oracle beside it (the oracle unit is
+    # dropped after its comparison, except for three layers kept for a second step);
+    # then every layer steps again, with the planted hit/miss counts checked on all of
+    # them (offload) and the kept layers compared in full.
     w = S.WORKLOADS["stress_78_layers"]
     t0 = time.time()
-    sampled = (0, 41, 77)
-    sess = gpu_session(w, MODE_OFFLOAD)
-    orcs = oracle_units(w, MODE_OFFLOAD, layers=sampled, seqs=[0])
-    layers = list(range(w.layers))
-    _load(w, sess, orcs, layers, [0])
-    _note(f"stress: 78 layers loaded in {time.time() - t0:.1f} s")
-    for step in range(2):
-        for l in layers:
-            gout, oout = run_step(w, l, step, sess, orcs if l in sampled else None)
-            g = gpu_items(sess, l, 0, w.rows_per_step, w.top_k, 0, w.history + w.rows_per_step * (step + 1))
-            cnt = [int(x) for x in g["counters"][:6]]
-            assert (cnt[1], cnt[3]) == (2028, 80), f"layer {l} step {step}: counters {cnt}"
-            if l in sampled:
-                compare_unit(sess, orcs[(l, 0)], l, 0, gout.cpu().numpy()[0], oout[0],
-                             what=f"stress layer={l} step={step}")
-        _note(f"stress step {step}: 78 layers, sampled layers match ({time.time() - t0:.1f} s)")
+    kept = (0, 41, 77)
+    sess = gpu_session(w, mode)
+    orcs = {}
+    for l in range(w.layers):
+        one = oracle_units(w, mode, layers=(l,), seqs=[0])
+        _load(w, sess, one, (l,), [0], gpu_layers=(l,))
+        gout, oout = run_step(w, l, 0, sess, one)
+        compare_unit(sess, one[(l, 0)], l, 0, gout.cpu().numpy()[0], oout[0], what=f"stress mode={mode} layer={l} step=0")
+        if mode == MODE_OFFLOAD:
+            cnt = sess.debug("counters", l, 0).cpu().numpy().view(np.int64)
+            assert (int(cnt[1]), int(cnt[3])) == (2028, 80), f"layer {l} step 0: counters {cnt}"
+        if l in kept:
+            orcs.update(one)
+        else:
+            one[(l, 0)].close()
+        if l % 13 == 12:
+            _note(f"stress mode={mode}: layers 0..{l} match at step 0 ({time.time() - t0:.1f} s)")
+    for l in range(w.layers):
+        gout, oout = run_step(w, l, 1, sess, orcs if l in kept else None)
+        if mode == MODE_OFFLOAD:
+            cnt = sess.debug("counters", l, 0).cpu().numpy().view(np.int64)
+            assert (int(cnt[1]), int(cnt[3])) == (2028, 80), f"layer {l} step 1: counters {cnt}"
+        if l in kept:
+            compare_unit(sess, orcs[(l, 0)], l, 0, gout.cpu().numpy()[0], oout[0],
+                         what=f"stress mode={mode} layer={l} step=1")
+    _note(f"stress mode={mode}: step 1 on 78 layers, kept layers match ({time.time() - t0:.1f} s)")
     sess.close()
+    for o in orcs.values():
+        o.close()
+
+
+def test_stress_all_78_layers_offload():
+    _stress_every_layer(MODE_OFFLOAD)
+
+
+def test_stress_all_78_layers_resident():
+    _stress_every_layer(MODE_RESIDENT)
+
+
+def test_batched_16x131k_resident():
+    _full_size("batched_16x131k", MODE_RESIDENT, steps=2)
+
+
+def test_offload_and_resident_are_identical_single_stream_50k():
+    # The offload page's acceptance check (section "GPU cache management errs too"): with
+    # the cache fixed, the offloaded run's output matched the resident run's exactly.  Both
+    # sessions take the same inputs for 24 steps: the ring's first 64-row batch goes back
+    # to the mirror after step 15, so the later steps read those rows as misses, not ring
+    # rows.  Outputs, selections and the compact rows must agree bit for bit.
+    import torch
+    w = S.WORKLOADS["single_stream_50k"]
+    t0 = time.time()
+    off = gpu_session(w, MODE_OFFLOAD)
+    res = gpu_session(w, MODE_RESIDENT)
+    load_history(w, off)
+    load_history(w, res)
+    kinds_seen = set()
+    for step in range(24):
+        go, _ = run_step(w, 0, step, off)
+        gr, _ = run_step(w, 0, step, res)
+        torch.cuda.synchronize()
+        assert torch.equal(go.view(torch.int32), gr.view(torch.int32)), f"step {step}: outputs differ"
+        co = off.debug("counters").cpu().numpy().view(np.int64)
+        cr = res.debug("counters").cpu().numpy().view(np.int64)
+        U = int(co[0])
+        assert U == int(cr[0]), f"step {step}: union sizes differ"
+        for item in ("selection", "sel_count", "union", "map"):
+            a, b = off.debug(item).cpu().numpy(), res.debug(item).cpu().numpy()
+            if item == "union":
+                a, b = a.view(np.int32)[:U], b.view(np.int32)[:U]
+            assert np.array_equal(a, b), f"step {step}: {item} differs"
+        ca = off.debug("compact").cpu().numpy().reshape(-1, 656)[:U]
+        cb = res.debug("compact").cpu().numpy().reshape(-1, 656)[:U]
+        assert np.array_equal(ca, cb), f"step {step}: compact rows differ"
+        kinds_seen |= set(off.debug("union_kind").cpu().numpy().view(np.int32)[:U].tolist())
+    st = off.unit_state(0, 0)
+    assert st["M"] == w.history + 64, f"one ring batch written back: {st}"
+    assert {0, 1, 2} <= kinds_seen, f"hits, ring rows and misses all seen: {kinds_seen}"
+    _note(f"offload == resident for 24 steps ({time.time() - t0:.1f} s)")
+    off.close()
+    res.close()
 
 
 def test_maximum_cache_and_union_long_history():
