@@ -266,6 +266,29 @@ dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq,
                            const void* index_q, const float* index_w, const void* q_latent,
                            const void* q_rope, float* out, hipStream_t stream);
 
+/* dsa_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, checks, state changes and results as dsa_decode_step; the
+ * step's scratch (scores, Top-K histograms and candidates, union and plan
+ * words, compact rows, split partials) lives in a static device array of the
+ * library, 64 MiB per GPU (each GPU that loads the library holds its copy until
+ * the process ends), instead of the session's scratch.  The call allocates
+ * nothing; its first kernel zeroes the parts of the array a step expects
+ * zeroed, because the array keeps the previous call's contents.
+ *   - Every such call on one GPU shares that GPU's array: calls that may
+ *     overlap on one GPU (other streams, other sessions, other threads) race
+ *     and must be ordered by the caller (one stream, or events).
+ *   - DSA_E_UNSUPPORTED (nothing enqueued) if the layer's step scratch, which
+ *     grows with n_seqs, max_query_rows, top_k, heads and max_positions, is
+ *     larger than the array (the 50,023-row single stream with 4 query rows
+ *     needs about 27 MB).
+ *   - The step items of dsa_debug_get are not kept for such a step (they
+ *     return DSA_E_STATE until the next dsa_decode_step), and its selection
+ *     cannot be reused by dsa_decode_step_reuse or dsa_prefetch_reuse. */
+dsa_status dsa_decode_step_static(dsa_session* s, int32_t layer, int32_t rows_per_seq,
+                                  const void* index_q, const float* index_w, const void* q_latent,
+                                  const void* q_rope, float* out, hipStream_t stream);
+
 /* Selection reuse (offload page, section "Starting point": some later layers
  * reuse the indexer's selection while each layer keeps its own KV rows).  A
  * decode step of `layer` on the selection made by the most recent

@@ -232,6 +232,10 @@ hipError_t launch_append(const Geometry& g, const UnitDev& unit, int64_t L, int6
 hipError_t launch_flush(const Geometry& g, const UnitDev& unit, int64_t M, int64_t L, hipStream_t st);
 hipError_t launch_warm(const Geometry& g, const UnitDev& unit, int64_t L, hipStream_t st);
 hipError_t launch_rollback(const UnitDev& unit, int64_t L, int64_t M, hipStream_t st);
+// Zero what a step expects zeroed in its scratch set (Top-K histograms, the
+// selection bitmap, the arrival counter): the static scratch keeps the
+// previous call's contents, possibly of another layout.
+hipError_t launch_clear_step_scratch(const Geometry& g, const StepArgs& a, hipStream_t st);
 // Test hook: every cached position of [0, L) gets an out-of-range slot index (offload).
 hipError_t launch_inject_bad_slot(const Geometry& g, const UnitDev& unit, int64_t L, hipStream_t st);
 // Keys of positions [0, L) in plain row order [L][index_dim], for inspection.

@@ -16,6 +16,7 @@
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -28,9 +29,20 @@ namespace dsa {
 thread_local LaunchTimer t_launch_timer;
 }  // namespace dsa
 
+// ---- the step scratch of dsa_decode_step_static ---------------------------
+// A file-scope device array, so that the no-allocation step needs no hipMalloc.
+// Host code never uses its name as an address: the device address of each
+// GPU's copy is looked up once per device (hipGetSymbolAddress, at the first
+// session create on that device) and kept in g_static_scratch.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int kMaxDevices = 256;
+std::mutex g_static_mu;
+void* g_static_scratch[kMaxDevices] = {};
 
 struct UnitHost {
   int64_t L = 0, M = 0, round = 0;
@@ -87,6 +99,8 @@ struct dsa_session {
   uint32_t* err_host = nullptr;            // device-side check flags: pinned, mapped host memory
   uint32_t* err_dev = nullptr;             // the same block's device address (kernels write it)
   bool inject_hip = false;                 // test hook: the next checked HIP call reports a failure
+  void* static_scratch = nullptr;          // this device's copy of the static scratch array
+  bool last_static = false;                // the most recent step ran on the static scratch
 };
 
 namespace {
@@ -223,7 +237,8 @@ dsa_status timed_launch(dsa_session* s, int kind, const char* what, F&& fn) {
 }
 
 // One sequence's step scratch: 256-byte aligned pieces at these offsets of a
-// block of `bytes` bytes.  The session's arena holds one block per sequence.
+// block of `bytes` bytes.  The session's arena holds one block per sequence;
+// dsa_decode_step_static lays the same blocks over the static scratch array.
 struct ScrOff {
   size_t scores, sel, sel_n, uni, kind, src, map, compact, po, pml, cnt, info, selmask, hitmask, base_u, base_m,
       pdesc, victim, done, hist0, hist1, cand, cand_n, rowdig;
@@ -315,6 +330,20 @@ dsa_status validate_config(const dsa_config* c, std::string* why) {
   if (c->ring_rows > 4096) return bad(DSA_E_UNSUPPORTED, "ring_rows <= 4096");
   if (c->replacement != DSA_REPL_RING && c->replacement != DSA_REPL_CLOCK) return bad(DSA_E_INVALID, "unknown replacement");
   return DSA_OK;
+}
+
+// Device address of the static scratch array on the current device, looked up
+// once per device.
+hipError_t static_scratch_address(int device, void** out) {
+  std::lock_guard<std::mutex> lk(g_static_mu);
+  if (!g_static_scratch[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_static_scratch[device] = p;
+  }
+  *out = g_static_scratch[device];
+  return hipSuccess;
 }
 
 void free_all(dsa_session* s) {
@@ -421,7 +450,8 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   dsa_status st = validate_config(cfg, &why);
   if (st != DSA_OK) return st;
   int ndev = 0;
-  if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device < 0 || cfg->device >= ndev) return DSA_E_INVALID;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device < 0 || cfg->device >= ndev || cfg->device >= kMaxDevices)
+    return DSA_E_INVALID;
 
   dsa_session* s = new dsa_session();
   s->cfg = *cfg;
@@ -505,6 +535,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   hipError_t e;
   if ((e = prepare_score_kernels()) != hipSuccess) return bail(DSA_E_HIP, "prepare");
   if ((e = prepare_topk_kernels()) != hipSuccess) return bail(DSA_E_HIP, "prepare");
+  if ((e = static_scratch_address(s->device, &s->static_scratch)) != hipSuccess) return bail(DSA_E_HIP, "static scratch");
   if (hipMalloc(&s->arena, s->arena_bytes) != hipSuccess) {
     s->arena = nullptr;
     (void)hipGetLastError();
@@ -772,9 +803,10 @@ dsa_status dsa_rollback_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t
 extern "C++" {
 namespace {
 
-// Validation, the step's launches, then the host-side round bookkeeping.
+// Shared by both decode entry points: validation, then the step's launches on
+// the scratch set `a` names, then the host-side round bookkeeping.
 dsa_status decode_common(dsa_session* s, int32_t layer, int32_t R, const void* index_q, const float* index_w,
-                         const void* q_latent, const void* q_rope, float* out, hipStream_t stream) {
+                         const void* q_latent, const void* q_rope, float* out, hipStream_t stream, bool on_static) {
   dsa_status st = entry(s);
   if (st != DSA_OK) return st;
   if (layer < 0 || layer >= s->cfg.n_layers) return fail(s, DSA_E_INVALID, "layer out of range");
@@ -786,7 +818,16 @@ dsa_status decode_common(dsa_session* s, int32_t layer, int32_t R, const void* i
   for (int q = 0; q < n_seqs; ++q)
     if (s->uh[unit_index(s, layer, q)].L < R) return fail(s, DSA_E_STATE, "a sequence holds fewer rows than rows_per_seq");
   const Geometry& g = s->g;
-  const StepArgs a = step_args(s, layer, R, false);
+  StepArgs a = step_args(s, layer, R, false);
+  if (on_static) {
+    const ScrOff lay = scratch_layout(g);
+    const size_t need = lay.bytes * (size_t)n_seqs;
+    if (need > kStaticScratchBytes)
+      return fail(s, DSA_E_UNSUPPORTED, "the step needs " + std::to_string(need) + " bytes of scratch; the static scratch holds " +
+                                            std::to_string(kStaticScratchBytes));
+    a.s0 = scratch_at(static_cast<uint8_t*>(s->static_scratch), lay);
+    a.s_stride = (int64_t)lay.bytes;
+  }
   DeviceGuard dg(s->device);
   const uint16_t* iq = static_cast<const uint16_t*>(index_q);
   const uint16_t* ql = static_cast<const uint16_t*>(q_latent);
@@ -795,20 +836,29 @@ dsa_status decode_common(dsa_session* s, int32_t layer, int32_t R, const void* i
   for (int l = 0; l < s->cfg.n_layers; ++l)
     if (s->pf_pending[l] && s->pf_stream[l] != stream)
       HIPCHK(hipStreamWaitEvent(stream, s->pf_done[l], 0), "hipStreamWaitEvent");
+  // the static array keeps the previous call's contents: zero what starts at zero
+  if (on_static) HIPCHK(launch_clear_step_scratch(g, a, stream), "scratch clear kernel");
   if ((st = timed_launch(s, KK_SCORE, "score kernel", [&] { return launch_score(g, a, iq, index_w, stream); })) != DSA_OK) return st;
   if ((st = timed_launch(s, KK_TOPK_PARTIAL, "top-k collect", [&] { return launch_topk_partial(g, a, stream); })) != DSA_OK)
     return st;
   if ((st = timed_launch(s, KK_TOPK_SELECT, "top-k resolve", [&] { return launch_topk_select(g, a, stream); })) != DSA_OK) return st;
-  HIPCHK(hipEventRecord(s->sel_ready, stream), "hipEventRecord");
-  s->sel_epoch += 1;
+  if (!on_static) {
+    HIPCHK(hipEventRecord(s->sel_ready, stream), "hipEventRecord");
+    s->sel_epoch += 1;
+  }
   if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream); })) != DSA_OK) return st;
   if ((st = timed_launch(s, KK_MERGE, "attention merge and assign", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK)
     return st;
   s->last_layer = layer;
   s->last_R = R;
-  s->topk_layer = layer;
-  s->topk_R = R;
-  for (int q = 0; q < n_seqs; ++q) s->topk_L[q] = s->uh[unit_index(s, layer, q)].L;
+  s->last_static = on_static;
+  if (on_static) {
+    s->topk_layer = -1;                  // the selection is not kept: no layer can reuse it
+  } else {
+    s->topk_layer = layer;
+    s->topk_R = R;
+    for (int q = 0; q < n_seqs; ++q) s->topk_L[q] = s->uh[unit_index(s, layer, q)].L;
+  }
   return finish_round(s, layer, stream);
 }
 
@@ -818,7 +868,13 @@ dsa_status decode_common(dsa_session* s, int32_t layer, int32_t R, const void* i
 dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq, const void* index_q,
                            const float* index_w, const void* q_latent, const void* q_rope, float* out,
                            hipStream_t stream) {
-  return decode_common(s, layer, rows_per_seq, index_q, index_w, q_latent, q_rope, out, stream);
+  return decode_common(s, layer, rows_per_seq, index_q, index_w, q_latent, q_rope, out, stream, false);
+}
+
+dsa_status dsa_decode_step_static(dsa_session* s, int32_t layer, int32_t rows_per_seq, const void* index_q,
+                                  const float* index_w, const void* q_latent, const void* q_rope, float* out,
+                                  hipStream_t stream) {
+  return decode_common(s, layer, rows_per_seq, index_q, index_w, q_latent, q_rope, out, stream, true);
 }
 
 dsa_status dsa_decode_step_reuse(dsa_session* s, int32_t layer, int32_t src_layer, int32_t rows_per_seq,
@@ -843,6 +899,7 @@ dsa_status dsa_decode_step_reuse(dsa_session* s, int32_t layer, int32_t src_laye
     return st;
   s->last_layer = layer;
   s->last_R = rows_per_seq;
+  s->last_static = false;
   return finish_round(s, layer, stream);
 }
 
@@ -941,6 +998,8 @@ dsa_status dsa_debug_get(dsa_session* s, int32_t layer, int32_t seq, int32_t ite
   if ((st = check_unit(s, layer, seq)) != DSA_OK) return st;
   const bool step_item = item <= DSA_DBG_COUNTERS;
   if (step_item && s->last_layer != layer) return fail(s, DSA_E_STATE, "no step of this layer is the most recent");
+  if (step_item && s->last_static)
+    return fail(s, DSA_E_STATE, "the most recent step ran on the static scratch, whose step items are not kept");
   size_t need = 0;
   if ((st = dsa_debug_size(s, layer, seq, item, &need)) != DSA_OK) return fail(s, st, "unknown item");
   if (!dst || bytes < need) return fail(s, DSA_E_INVALID, "destination too small");
