@@ -360,7 +360,10 @@ typedef enum {
   DSA_DBG_UNION_SRC = 5,   /* i32 [R*K]           slot / ring index / position */
   DSA_DBG_MAP = 6,         /* i32 [R][K]          union index per selected position, -1 padded */
   DSA_DBG_COMPACT = 7,     /* u8  [R*K][row_bytes] compact selection (first U rows valid) */
-  DSA_DBG_COUNTERS = 8,    /* i64 [8]  union, hit, ring, miss, miss_noslot, evict, host_bytes, resident */
+  DSA_DBG_COUNTERS = 8,    /* i64 [9]  union, hit, ring, miss, miss_noslot, evict, host_bytes (distinct missed
+                              rows x row_bytes), resident, host_reads (rows read from the host mirror: in a
+                              step every query row reads its own selected misses, so a miss several rows
+                              select counts once per row; in a prefetch round one read per filled slot) */
   DSA_DBG_SLOT_POS = 9,    /* i32 [S] */
   DSA_DBG_FILL_ROUND = 10, /* i32 [S] */
   DSA_DBG_PIN_ROUND = 11,  /* i32 [S] */
@@ -369,7 +372,7 @@ typedef enum {
   DSA_DBG_SLOT_BYTES = 14, /* u8  [S][row_bytes] */
   DSA_DBG_MIRROR = 15,     /* u8  [M][row_bytes] host mirror (resident: row store [L]) */
   DSA_DBG_KEYS = 16,       /* bf16 [L][index_dim] (dst 16-byte aligned; stored in another order, rebuilt by a kernel) */
-  DSA_DBG_TOTALS = 17,     /* i64 [8]  the counters above summed over every step of the unit */
+  DSA_DBG_TOTALS = 17,     /* i64 [9]  the counters above summed over every round of the unit */
   DSA_DBG_REF_BITS = 18    /* u32 [ceil(S/32)] reference bits, slot v = bit v%32 of word v/32 (CLOCK; 0 otherwise) */
 } dsa_debug_item;
 

@@ -29,7 +29,7 @@ KERNEL_KINDS = ("index_score", "topk_collect", "topk_resolve", "gather", "attent
 DBG = dict(scores=0, selection=1, sel_count=2, union=3, union_kind=4, union_src=5, map=6,
            compact=7, counters=8, slot_pos=9, fill_round=10, pin_round=11, pos_slot=12, hand=13,
            slot_bytes=14, mirror=15, keys=16, totals=17, ref_bits=18)
-COUNTER_NAMES = ("union", "hit", "ring", "miss", "miss_noslot", "evict", "host_bytes", "res")
+COUNTER_NAMES = ("union", "hit", "ring", "miss", "miss_noslot", "evict", "host_bytes", "res", "host_reads")
 
 # every symbol include/dsa.h declares
 EXPORTS = ("dsa_session_create", "dsa_session_destroy", "dsa_append_rows", "dsa_flush",

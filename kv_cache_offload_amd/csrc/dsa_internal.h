@@ -65,7 +65,7 @@ struct UnitT {
   P<uint32_t> ref;         // [ceil(S/32)] reference bits (CLOCK replacement)
   P<int32_t> hand;         // [1]
   P<int64_t> dyn;          // [4] L, M, round, reserved -- updated only by kernels, in stream order
-  P<int64_t> totals;       // [8] step counters summed over every decode step of the unit
+  P<int64_t> totals;       // [16] step counters summed over every round of the unit (first 9 used)
 };
 
 // Per-sequence step scratch, shared by the layers (layers run in stream order).
@@ -81,7 +81,8 @@ struct ScratchT {
   P<uint8_t> compact;       // [R_max*K][row_bytes]
   P<float> part_o;          // [R_max][nsplit_max][H][latent]
   P<float> part_ml;         // [R_max][nsplit_max][H][2]
-  P<int64_t> counters;      // [8] union, hit, ring, miss, miss_noslot, evict, host_bytes, resident
+  P<int64_t> counters;      // [16] union, hit, ring, miss, miss_noslot, evict, host_bytes, resident,
+                            //      host_reads (rows read from the host mirror, per reading query row)
   P<int64_t> info;          // [8] see kInfo* below
   P<uint32_t> selmask;      // [P_pad/32] positions selected by any row this step (cleared by the assign)
   P<uint32_t> hitmask;      // [P_pad/32] selected positions that hit a slot (written by the plan each step)

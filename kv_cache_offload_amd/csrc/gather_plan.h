@@ -304,6 +304,8 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
     }
     s.counters[tid] = cn;
     u.totals[tid] = total_prev + cn;
+  } else if (tid == 8) {
+    s.counters[8] = 0;                                 // host reads: the round's readers add them
   }
   if (tid == 0) {
     int64_t wb = -1;

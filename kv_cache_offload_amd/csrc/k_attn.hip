@@ -146,6 +146,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   const int n_sel = s.sel_n[r];
   i32x2 victim = (i32x2){-1, -1};
   bool assigned = false;                                 // this row's miss took the plan's victim
+  bool host = false;                                     // this row is read from the host mirror
   if (tid < kSplit) {
     const int64_t M = s.info[kInfoM];
     const uint32_t n_assigned = (uint32_t)s.info[kInfoAssigned];
@@ -180,6 +181,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
             assigned = true;
           }
           from = u.rows + (int64_t)pos * rb;
+          host = true;
         }
       }
     } else if (j < n_sel) {
@@ -188,6 +190,13 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     s_from[tid] = from;
     s_ux[tid] = from ? (int)ux : -1;
     if (j < ka.K) s.map[(int64_t)r * ka.K + j] = from ? (int)ux : -1;
+  }
+  if (wave == 0) {                                       // the split's host-mirror reads (one wave holds its rows)
+    const uint64_t hb = __ballot(host);
+    if (lane == 0 && hb) {
+      g_add(&s.counters[8], (int64_t)__popcll(hb));
+      g_add(&u.totals[8], (int64_t)__popcll(hb));
+    }
   }
   if (j_begin >= n_sel) return;                          // (uniform) map entries written above
   const int nrows = min(n_sel - j_begin, kSplit);

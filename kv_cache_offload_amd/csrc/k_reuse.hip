@@ -66,6 +66,7 @@ __global__ __launch_bounds__(256) void prefetch_fill_kernel(FillKArgs ka) {
   const ScratchG s = scratch_of(a, seq);
   const int64_t U = s.info[kInfoUnion];
   const int64_t rb = ka.row_bytes;
+  if (blockIdx.x == 0 && threadIdx.x == 0) g_add(&u.totals[8], s.info[kInfoAssigned]);   // one host read per fill
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < U * kCopyChunks16;
        t += (int64_t)gridDim.x * blockDim.x) {
     const int64_t ux = t / kCopyChunks16, c = t % kCopyChunks16;

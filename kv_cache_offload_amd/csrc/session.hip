@@ -260,7 +260,7 @@ ScrOff scratch_layout(const Geometry& g) {
   o.compact = take((size_t)RK * rb);
   o.po = take((size_t)g.r_max * g.nsplit_max * g.heads * g.latent * 4);
   o.pml = take((size_t)g.r_max * g.nsplit_max * g.heads * 2 * 4);
-  o.cnt = take(8 * 8);
+  o.cnt = take(16 * 8);
   o.info = take(8 * 8);
   o.selmask = take((size_t)P / 32 * 4);
   o.hitmask = take((size_t)P / 32 * 4);
@@ -502,7 +502,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
     uo[i].ref = off ? take((size_t)g.s_words * 4) : 0;
     uo[i].hand = take(4);
     uo[i].dyn = take(32);
-    uo[i].totals = take(64);
+    uo[i].totals = take(128);
   }
   const ScrOff lay = scratch_layout(g);
   std::vector<size_t> so(cfg->n_seqs);
@@ -511,7 +511,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   struct PfOff { size_t cnt, info, uni, kind, src, selmask, hitmask, base_u, base_m, pdesc, victim, done; };
   std::vector<PfOff> pf(off ? cfg->n_seqs : 0);
   for (auto& x : pf) {
-    x.cnt = take(8 * 8);
+    x.cnt = take(16 * 8);
     x.info = take(8 * 8);
     x.uni = take((size_t)RK * 4);
     x.kind = take((size_t)RK * 4);
@@ -976,14 +976,14 @@ dsa_status dsa_debug_size(const dsa_session* s, int32_t layer, int32_t seq, int3
     case DSA_DBG_UNION: case DSA_DBG_UNION_KIND: case DSA_DBG_UNION_SRC: b = (size_t)R * K * 4; break;
     case DSA_DBG_MAP: b = (size_t)R * K * 4; break;
     case DSA_DBG_COMPACT: b = (size_t)R * K * rb; break;
-    case DSA_DBG_COUNTERS: b = 64; break;
+    case DSA_DBG_COUNTERS: b = 72; break;
     case DSA_DBG_SLOT_POS: case DSA_DBG_FILL_ROUND: case DSA_DBG_PIN_ROUND: b = (size_t)S * 4; break;
     case DSA_DBG_POS_SLOT: b = g.mode == DSA_KV_OFFLOAD ? (size_t)h.L * 4 : 0; break;
     case DSA_DBG_HAND: b = 4; break;
     case DSA_DBG_SLOT_BYTES: b = (size_t)S * rb; break;
     case DSA_DBG_MIRROR: b = (size_t)(g.mode == DSA_KV_OFFLOAD ? h.M : h.L) * rb; break;
     case DSA_DBG_KEYS: b = (size_t)h.L * g.index_dim * 2; break;
-    case DSA_DBG_TOTALS: b = 64; break;
+    case DSA_DBG_TOTALS: b = 72; break;
     case DSA_DBG_REF_BITS: b = (size_t)g.s_words * 4; break;
     default: return DSA_E_INVALID;
   }

@@ -30,7 +30,7 @@ OK, E_INVALID, E_NOMEM, E_CAPACITY, E_STATE = 0, 1, 2, 3, 4
 MODE_OFFLOAD, MODE_RESIDENT = 0, 1
 REPL_RING, REPL_CLOCK = 0, 1
 SRC_HIT, SRC_RING, SRC_MISS, SRC_MISS_NOSLOT, SRC_RES = 0, 1, 2, 3, 4
-CNT_NAMES = ("union", "hit", "ring", "miss", "miss_noslot", "evict", "host_bytes", "res")
+CNT_NAMES = ("union", "hit", "ring", "miss", "miss_noslot", "evict", "host_bytes", "res", "host_reads")
 
 
 def build(force: bool = False) -> str:

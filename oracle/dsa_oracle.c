@@ -459,6 +459,18 @@ static int run_round(orc_unit* u, int32_t R, const uint16_t* q_lat, const uint16
       memcpy(u->compact + x * rb, from, (size_t)rb);
     }
     u->cnt[ORC_CNT_HOST_BYTES] = (u->cnt[ORC_CNT_MISS] + u->cnt[ORC_CNT_MISS_NOSLOT]) * rb;
+    /* Rows read from host memory: with attention, each query row reads every
+     * selected position of its own that missed; a prefetch round (no attention)
+     * reads each miss that took a slot once, to fill the slot. */
+    if (out) {
+      for (int32_t i = 0; i < R; i++)
+        for (int32_t j = 0; j < u->sel_n[i]; j++) {
+          const int32_t x = u->map[(int64_t)i * K + j];
+          if (x >= 0 && (u->kind[x] == ORC_SRC_MISS || u->kind[x] == ORC_SRC_MISS_NOSLOT)) u->cnt[ORC_CNT_HOST_READS]++;
+        }
+    } else {
+      u->cnt[ORC_CNT_HOST_READS] = u->cnt[ORC_CNT_MISS];
+    }
   }
 
   /* 9. Attention of each query row over its own selection. */

@@ -52,9 +52,15 @@ enum { ORC_REPL_RING = 0, ORC_REPL_CLOCK = 1 };
 /* Where a selected row's bytes come from in one round. */
 enum { ORC_SRC_HIT = 0, ORC_SRC_RING = 1, ORC_SRC_MISS = 2, ORC_SRC_MISS_NOSLOT = 3, ORC_SRC_RES = 4 };
 /* Per-step counters, in this order. */
+/* HOST_BYTES: bytes of the distinct missed positions (each once).  HOST_READS:
+ * rows actually read from the host mirror -- in a round with attention every
+ * query row reads each of its own selected misses, so a miss several rows
+ * select is read once per row (offload page, "GPU cache management errs too":
+ * repeated misses of one round read host memory); in a prefetch round, one read
+ * per miss that took a slot. */
 enum {
   ORC_CNT_UNION = 0, ORC_CNT_HIT, ORC_CNT_RING, ORC_CNT_MISS, ORC_CNT_MISS_NOSLOT,
-  ORC_CNT_EVICT, ORC_CNT_HOST_BYTES, ORC_CNT_RES, ORC_CNT__N
+  ORC_CNT_EVICT, ORC_CNT_HOST_BYTES, ORC_CNT_RES, ORC_CNT_HOST_READS, ORC_CNT__N
 };
 
 typedef struct {

@@ -163,7 +163,7 @@ def compare_unit(sess, o: OracleUnit, gl: int, seq: int, gout, oout, check_score
     assert np.array_equal(g["map"], o.map()), f"{what} map differs"
     assert np.array_equal(g["compact"], o.compact()), f"{what} compact bytes differ"
     oc = o.counters()
-    names = ("union", "hit", "ring", "miss", "miss_noslot", "evict", "host_bytes", "res")
+    names = ("union", "hit", "ring", "miss", "miss_noslot", "evict", "host_bytes", "res", "host_reads")
     assert [int(x) for x in g["counters"]] == [oc[k] for k in names], f"{what} counters differ"
     if S_:
         sp, fr, pr = o.slots()

@@ -47,8 +47,8 @@ def _reuse_run(w, mode, steps, layers=3, prefetch=(1,), replacement=REPL_RING, s
     orcs = oracle_units(w, mode, layers=range(layers), seqs=seqs, replacement=replacement)
     load_history(w, sess, orcs, layers=range(layers), seqs=seqs)
     side = torch.cuda.Stream()
-    totals = {(l, q): np.zeros(8, np.int64) for l in range(layers) for q in seqs}
-    names = ("union", "hit", "ring", "miss", "miss_noslot", "evict", "host_bytes", "res")
+    totals = {(l, q): np.zeros(9, np.int64) for l in range(layers) for q in seqs}
+    names = ("union", "hit", "ring", "miss", "miss_noslot", "evict", "host_bytes", "res", "host_reads")
     dev = sess.device
     for step in range(steps):
         for l in range(layers):
