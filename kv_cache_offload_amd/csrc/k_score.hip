@@ -33,8 +33,7 @@ typedef short bf16x8 __attribute__((__vector_size__(8 * sizeof(short))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 
 constexpr int kQStride = 136;           // bf16 per Q row in LDS (128 + 8 pad)
-constexpr int kWaves = 4;
-constexpr int kMaxQPieces = 256 * 16 / 256;   // 16-byte Q pieces per thread at R * H_I = 256
+constexpr int kMaxQRows = 256;          // R * H_I
 
 struct ScoreKArgs {
   StepArgs a;
@@ -60,13 +59,20 @@ __device__ inline void count_digit(uint32_t* lh, int r, float score) {
   atomicAdd(&lh[r * (kRadixBins / 2) + (d >> 1)], 1u << (16 * (d & 1)));
 }
 
-// Three workgroups per CU (the LDS allows three): the register budget this
-// implies (at most 168 VGPRs) lets 12 waves per CU keep their next key tile in
-// flight; with the compiler's unbounded choice (about 228) only 8 could, and the
-// kernel waited on HBM latency (2.7 TB/s on a million-row history, 3.5 TB/s with
-// the bound).  H_I = 4 keeps the default: it would spill under the bound.
-template <int HI>
-__global__ __launch_bounds__(256, HI >= 8 ? 3 : 1) void score_kernel(ScoreKArgs ka) {
+// NW waves share one staged Q.  Eight waves (launch_score picks them for a
+// large Q or a short history): a 50,023-row history needs 196 workgroups, one
+// tile per wave and every workgroup resident at once, even with 8 query rows,
+// whose 69 KiB of Q leave room for one workgroup per CU.  Four waves (long
+// histories, Q of at most 128 rows): three workgroups per CU (the LDS allows
+// three), and the register budget this implies (at most 168 VGPRs) lets 12 waves
+// per CU keep their next key tile in flight (with the compiler's unbounded
+// choice, about 228, only 8 could, and the kernel waited on HBM latency).
+// H_I = 4 keeps the default: it would spill under the bound.
+template <int HI, int NW>
+__global__ __launch_bounds__(NW * 64, NW == 4 && HI >= 8 ? 3 : 1) void score_kernel(ScoreKArgs ka) {
+  constexpr int kWaves = NW;
+  constexpr int kThreads = NW * 64;
+  constexpr int kMaxQPieces = kMaxQRows * 16 / kThreads;   // 16-byte Q pieces per thread
   extern __shared__ __align__(16) uint16_t sq[];   // [MT*32][kQStride], weights, digit histograms
   const StepArgs& a = ka.a;
   const int seq = blockIdx.y;
@@ -92,7 +98,7 @@ __global__ __launch_bounds__(256, HI >= 8 ? 3 : 1) void score_kernel(ScoreKArgs 
   bf16x8 qv[kMaxQPieces];
 #pragma unroll
   for (int e = 0; e < kMaxQPieces; ++e) {
-    const int c = threadIdx.x + e * 256;
+    const int c = threadIdx.x + e * kThreads;
     const int row = c >> 4, col = (c & 15) * 8;
     qv[e] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
     if (c < nq && row < M) qv[e] = *reinterpret_cast<const bf16x8*>(qg + (int64_t)row * 128 + col);
@@ -116,7 +122,7 @@ __global__ __launch_bounds__(256, HI >= 8 ? 3 : 1) void score_kernel(ScoreKArgs 
   for (int w = threadIdx.x; w < R * (kRadixBins / 2); w += blockDim.x) lh[w] = 0;
 #pragma unroll
   for (int e = 0; e < kMaxQPieces; ++e) {
-    const int c = threadIdx.x + e * 256;
+    const int c = threadIdx.x + e * kThreads;
     if (c < nq) *reinterpret_cast<bf16x8*>(sq + (c >> 4) * kQStride + (c & 15) * 8) = qv[e];
   }
   if (threadIdx.x < MT * 32) sw[threadIdx.x] = wv;
@@ -227,12 +233,16 @@ __global__ __launch_bounds__(256, HI >= 8 ? 3 : 1) void score_kernel(ScoreKArgs 
 }  // namespace
 
 hipError_t prepare_score_kernels() {
-  const int max_lds = 256 * kQStride * 2 + 256 * 4 + 8 * (kRadixBins / 2) * 4;
-  hipError_t e;
-  if ((e = hipFuncSetAttribute((const void*)score_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds))) return e;
-  if ((e = hipFuncSetAttribute((const void*)score_kernel<8>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds))) return e;
-  if ((e = hipFuncSetAttribute((const void*)score_kernel<16>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds))) return e;
-  return hipFuncSetAttribute((const void*)score_kernel<32>, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+  const int max_lds = kMaxQRows * kQStride * 2 + kMaxQRows * 4 + 8 * (kRadixBins / 2) * 4;
+  const void* kernels[] = {(const void*)score_kernel<4, 4>,  (const void*)score_kernel<8, 4>,
+                           (const void*)score_kernel<16, 4>, (const void*)score_kernel<32, 4>,
+                           (const void*)score_kernel<4, 8>,  (const void*)score_kernel<8, 8>,
+                           (const void*)score_kernel<16, 8>, (const void*)score_kernel<32, 8>};
+  for (const void* k : kernels) {
+    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_score(const Geometry& g, const StepArgs& a, const uint16_t* q, const float* w,
@@ -244,24 +254,34 @@ hipError_t launch_score(const Geometry& g, const StepArgs& a, const uint16_t* q,
   ka.p_pad = g.p_pad;
   ka.r_max = g.r_max;
   const int64_t subs = (a.l_max + 31) / 32;
+  const int M = a.R * g.index_heads;
+  // Eight waves for a large Q (more than 128 rows: one workgroup per CU) or a
+  // short history (about one tile per wave over the chip); four otherwise.
+  const bool wide = M > 128 || subs * a.n_seqs <= 8 * 256 * 2;
+  const int nw = wide ? 8 : 4;
   // Enough waves (over all sequences) to cover the chip several times; longer
   // per-wave runs amortise the Q staging and keep the next tile's keys in flight.
-  int spw = (int)((subs * a.n_seqs + 4 * 256 * 4 - 1) / (4 * 256 * 4));
+  int spw = (int)((subs * a.n_seqs + nw * 256 * 4 - 1) / (nw * 256 * 4));
   if (spw < 1) spw = 1;
   if (spw > 8) spw = 8;
   ka.subs_per_wave = spw;
-  const int64_t blocks = (subs + (int64_t)kWaves * spw - 1) / ((int64_t)kWaves * spw);
-  const int MT = (a.R * g.index_heads + 31) / 32;
+  const int64_t blocks = (subs + (int64_t)nw * spw - 1) / ((int64_t)nw * spw);
+  const int MT = (M + 31) / 32;
   const size_t lds = (size_t)MT * 32 * kQStride * sizeof(uint16_t) + (size_t)MT * 32 * sizeof(float) +
                      (size_t)a.R * (kRadixBins / 2) * sizeof(uint32_t);
-  dim3 grid((unsigned)blocks, (unsigned)a.n_seqs), block(256);
+  dim3 grid((unsigned)blocks, (unsigned)a.n_seqs), block(nw * 64);
+#define DSA_SCORE_CASE(HI)                                                                   \
+  case HI:                                                                                 \
+    return wide ? launch_k(score_kernel<HI, 8>, grid, block, lds, st, ka)                  \
+                : launch_k(score_kernel<HI, 4>, grid, block, lds, st, ka);
   switch (g.index_heads) {
-    case 4: return launch_k(score_kernel<4>, grid, block, lds, st, ka);
-    case 8: return launch_k(score_kernel<8>, grid, block, lds, st, ka);
-    case 16: return launch_k(score_kernel<16>, grid, block, lds, st, ka);
-    case 32: return launch_k(score_kernel<32>, grid, block, lds, st, ka);
+    DSA_SCORE_CASE(4)
+    DSA_SCORE_CASE(8)
+    DSA_SCORE_CASE(16)
+    DSA_SCORE_CASE(32)
     default: return hipErrorInvalidValue;
   }
+#undef DSA_SCORE_CASE
 }
 
 }  // namespace dsa
