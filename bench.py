@@ -55,6 +55,9 @@ def parse():
                         "selection; steps/s without and with prefetch on a second stream, and resident")
     p.add_argument("--quantize-rows", type=int, default=1 << 20,
                    help="rows of the quantise-on-append measurement (0 skips it)")
+    p.add_argument("--pairs", type=int, default=3,
+                   help="the timed steps of each mode are split into this many segments, offload and resident "
+                        "interleaved with the order alternating from pair to pair")
     return p.parse_args()
 
 
@@ -217,7 +220,7 @@ class Runner:
     def totals(self):
         """Step counters summed over every unit."""
         self.torch.cuda.synchronize()
-        t = np.zeros(8, np.int64)
+        t = np.zeros(9, np.int64)
         for l in range(self.w.layers):
             for q in range(self.w.seqs):
                 t += self.sess.debug("totals", l, q).cpu().numpy().view(np.int64)
@@ -262,9 +265,9 @@ def algorithmic_bytes(w, kind, n_steps, L0, cnt, long_hist):
         # union bookkeeping: descriptor + union arrays per entry, victim and slot-table entries per miss
         return assign
     if kind == "attention":
-        # every selected row read from its source (slot, ring, host mirror, HBM row store), the compact
-        # copy and the misses' slot fills written, the queries read
-        return Q * R * K * rb + U * rb + miss * rb + Q * R * H * (512 + 64) * 2
+        # every distinct selected row read once from its source (slot, ring, host mirror, HBM row store),
+        # its compact copy and the misses' slot fills written, the queries read
+        return U * rb + U * rb + miss * rb + Q * R * H * (512 + 64) * 2
     if kind == "attention_merge":
         # the merged output, and the assign pass that runs in the same launch
         return Q * R * H * 512 * 4 + assign
@@ -273,19 +276,9 @@ def algorithmic_bytes(w, kind, n_steps, L0, cnt, long_hist):
     return 0.0
 
 
-def run_mode(w, mode, inputs, args):
-    import kv_cache_offload_amd as K
-    name = "offload" if mode == K.KV_OFFLOAD else "resident"
-    r = Runner(w, mode, inputs, replacement=K.REPL_CLOCK if args.replacement == "clock" else K.REPL_RING)
-    log(f"{name}: history loaded (L={r.L()}), warmup {args.warmup}")
-    r.steps(args.warmup)
-    c_before = r.totals()
-    L_before = r.L()
-    dt = timed(r, args.steps)
-    c_timed = r.totals() - c_before
-    log(f"{name}: {args.steps} steps in {dt * 1e3:.1f} ms ({args.steps / dt:.1f} steps/s)")
-    # per-kernel durations: the same workload continues with the library's
-    # dispatch events on (their host-side cost would distort the timed region)
+def kernel_pass(r, w, args):
+    """Per-kernel durations: the same workload continues with the library's
+    dispatch events on (their host-side cost would distort the timed region)."""
     kc_before = r.totals()
     kL0 = r.L()
     r.sess.set_kernel_timing(True, reserve_steps=args.kernel_steps * w.layers)
@@ -294,15 +287,75 @@ def run_mode(w, mode, inputs, args):
     r.sess.set_kernel_timing(False)
     kc = r.totals() - kc_before
     long_hist = r.L() > 65536
-    res = dict(seconds=dt, steps_per_s=args.steps / dt, L_start=L_before, counters=c_timed.tolist(),
-               steps_per_s_with_kernel_events=args.kernel_steps / dt_ev, kernel_steps=args.kernel_steps,
-               kernels={k: dict(launches=c, avg_us=(m / c * 1e3) if c else 0.0,
-                                bytes_per_launch=algorithmic_bytes(w, k, args.kernel_steps, kL0, kc, long_hist))
-                        for k, (c, m) in kt.items() if c})
-    for k, v in res["kernels"].items():
+    kernels = {k: dict(launches=c, avg_us=(m / c * 1e3) if c else 0.0,
+                       bytes_per_launch=algorithmic_bytes(w, k, args.kernel_steps, kL0, kc, long_hist))
+               for k, (c, m) in kt.items() if c}
+    for v in kernels.values():
         v["GBps"] = v["bytes_per_launch"] / (v["avg_us"] * 1e-6) / 1e9 if v["avg_us"] > 0 else 0.0
-    r.sess.close()
+    return dict(steps_per_s_with_kernel_events=args.kernel_steps / dt_ev, kernel_steps=args.kernel_steps,
+                kernels=kernels, kernel_counters=kc.tolist())
+
+
+def run_pairs(w, inputs, args):
+    """The offloaded session (and, unless --no-resident, the resident one) over the
+    same inputs.  The timed steps of each mode are split into --pairs segments,
+    run offload/resident interleaved with the order alternating from pair to pair
+    (the offload page, section "Six interleaved pairs": the same binary, the order
+    alternated per restart), so a drift of the machine during the run falls on
+    both modes alike.  Returns one result per mode."""
+    import kv_cache_offload_amd as K
+    modes = [("offload", K.KV_OFFLOAD)] + ([] if args.no_resident else [("resident", K.KV_HBM_RESIDENT)])
+    repl = K.REPL_CLOCK if args.replacement == "clock" else K.REPL_RING
+    runners, res = {}, {}
+    for name, mode in modes:
+        runners[name] = Runner(w, mode, inputs, replacement=repl)
+        log(f"{name}: history loaded (L={runners[name].L()}), warmup {args.warmup}")
+        runners[name].steps(args.warmup)
+        res[name] = dict(seconds=0.0, steps=0, L_start=runners[name].L(), counters=np.zeros(9, np.int64),
+                         segments=[])
+    P = max(1, min(args.pairs, args.steps))
+    sizes = [args.steps // P + (1 if i < args.steps % P else 0) for i in range(P)]
+    names = [n for n, _ in modes]
+    for p, n_seg in enumerate(sizes):
+        for name in (names if p % 2 == 0 else names[::-1]):
+            r = runners[name]
+            c0 = r.totals()
+            dt = timed(r, n_seg)
+            res[name]["counters"] += r.totals() - c0
+            res[name]["seconds"] += dt
+            res[name]["steps"] += n_seg
+            res[name]["segments"].append(round(n_seg / dt, 2))
+    for name in names:
+        x = res[name]
+        x["steps_per_s"] = x["steps"] / x["seconds"]
+        x["counters"] = x["counters"].tolist()
+        log(f"{name}: {x['steps']} steps in {x['seconds'] * 1e3:.1f} ms ({x['steps_per_s']:.1f} steps/s; "
+            f"segments {x['segments']})")
+    for name in names:
+        res[name].update(kernel_pass(runners[name], w, args))
+        runners[name].sess.close()
     return res
+
+
+def environment():
+    """Read-only record of the host and software the run used."""
+    import torch
+
+    def read(path):
+        try:
+            return open(path).read().strip()
+        except OSError:
+            return None
+    cpu = None
+    try:
+        cpu = next((l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")), None)
+    except OSError:
+        pass
+    return {"cpu_model": cpu, "host_threads": len(os.sched_getaffinity(0)),
+            "kernel.numa_balancing": read("/proc/sys/kernel/numa_balancing"),
+            "vm.compaction_proactiveness": read("/proc/sys/vm/compaction_proactiveness"),
+            "rocm": read("/opt/rocm/.info/version"), "torch": torch.__version__, "hip": torch.version.hip,
+            "gpu": torch.cuda.get_device_name(0)}
 
 
 def replacement_probe(w, inputs, args):
@@ -488,30 +541,48 @@ def main():
         probe = replacement_probe(w, inputs, args)
         print(json.dumps({"workload": w.name, "replacement_probe": probe}), flush=True)
         return
-    off = run_mode(w, K.KV_OFFLOAD, inputs, args)
-    resd = None if args.no_resident else run_mode(w, K.KV_HBM_RESIDENT, inputs, args)
+    both = run_pairs(w, inputs, args)
+    off, resd = both["offload"], both.get("resident")
 
-    # dominant kernel of the offloaded step and its roofline
+    R, Q, NL = w.rows_per_step, w.seqs, w.layers
+    rb = w.row_bytes
     kern = off["kernels"]
+    kc = off["kernel_counters"]
+    # dominant kernel of the offloaded step and its roofline: the HBM view (algorithmic bytes), the host-link
+    # view (rows actually read from the host mirror, every reading query row counted) and the MFMA view
+    # (bf16 flops); the bound is the view the kernel is closest to
     total_ms = {k: v["avg_us"] * v["launches"] for k, v in kern.items()}
     dom = max(total_ms, key=total_ms.get)
     d = kern[dom]
-    roof = dict(kernel=dom, bound="hbm", achieved=d["GBps"], peak=HBM_PEAK_GBPS, unit="GB/s",
-                frac=d["GBps"] / HBM_PEAK_GBPS, traffic=pmc_traffic(w.name, dom), avg_us=d["avg_us"],
-                bytes_per_launch=d["bytes_per_launch"])
+    views = {"hbm": (d["GBps"], HBM_PEAK_GBPS, "GB/s", d["bytes_per_launch"])}
+    L_kern = off["L_start"] + R * (args.steps + args.kernel_steps / 2.0)
+    if dom == "attention":
+        host_b = kc[8] * rb / d["launches"]
+        views["host_link"] = (host_b / (d["avg_us"] * 1e-6) / 1e9, HOST_LINK_PEAK_GBPS, "GB/s", host_b)
+        flops = Q * R * w.top_k * w.heads * (576 + 512) * 2.0
+        views["mfma"] = (flops / (d["avg_us"] * 1e-6) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", flops)
+    elif dom == "index_score":
+        flops = Q * R * w.index_heads * L_kern * w.index_dim * 2.0
+        views["mfma"] = (flops / (d["avg_us"] * 1e-6) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", flops)
+    bound = max(views, key=lambda k: views[k][0] / views[k][1])
+    a_, p_, u_, per_launch = views[bound]
+    roof = dict(kernel=dom, bound=bound, achieved=a_, peak=p_, unit=u_, frac=a_ / p_,
+                traffic=pmc_traffic(w.name, dom), avg_us=d["avg_us"],
+                algorithmic_per_launch=per_launch,
+                views={k: {"achieved": v[0], "peak": v[1], "unit": v[2], "frac": v[0] / v[1], "per_launch": v[3]}
+                       for k, v in views.items()})
 
-    R, Q, NL = w.rows_per_step, w.seqs, w.layers
     c = off["counters"]
-    n = args.steps
+    n = off["steps"]
     per_step = lambda k: kern[k]["avg_us"] * kern[k]["launches"] / off["kernel_steps"] if k in kern else 0.0
-    rb = w.row_bytes
     L_mean = off["L_start"] + R * (n + 1) / 2.0
     # scoring + selection: every index key once per step (HBM)
     ss_us = per_step("index_score") + per_step("topk_collect") + per_step("topk_resolve")
     ss_bytes = NL * Q * L_mean * w.index_dim * 2
-    # gather + attention: selected rows from their sources (hits and ring rows from HBM, misses over the
-    # host link), compact rows and slot fills written to HBM
-    host_bytes = c[6] / n
+    # gather + attention: each distinct selected row from its source (hits and ring rows from HBM, misses over
+    # the host link), compact rows and slot fills written to HBM; host bytes as actually read
+    host_distinct = c[6] / n
+    host_read = c[8] * rb / n
     ga_us = per_step("gather") + per_step("attention")
     ga_hbm_bytes = ((c[1] + c[2] + c[7]) + c[0] + c[3]) * rb / n
     line = {
@@ -521,7 +592,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": 1e3 * off["seconds"] / args.steps,
+        "ms_per_step": 1e3 * off["seconds"] / off["steps"],
         "steps_per_s_with_kernel_events": off["steps_per_s_with_kernel_events"],
         "higher_is_better": True,
         "scaling": "weak",
@@ -537,23 +608,29 @@ def main():
         "score_select": {"us_per_step": ss_us, "hbm_bytes_per_step": ss_bytes,
                          "hbm_frac": ss_bytes / (ss_us * 1e-6) / 1e9 / HBM_PEAK_GBPS if ss_us else 0.0},
         "gather_attention": {"us_per_step": ga_us, "hbm_bytes_per_step": ga_hbm_bytes,
-                             "host_bytes_per_step": host_bytes,
+                             "host_bytes_read_per_step": host_read,
                              "hbm_frac": ga_hbm_bytes / (ga_us * 1e-6) / 1e9 / HBM_PEAK_GBPS if ga_us else 0.0,
-                             "host_link_GBps": host_bytes / (ga_us * 1e-6) / 1e9 if ga_us else 0.0,
-                             "host_link_frac": host_bytes / (ga_us * 1e-6) / 1e9 / HOST_LINK_PEAK_GBPS
+                             "host_link_GBps": host_read / (ga_us * 1e-6) / 1e9 if ga_us else 0.0,
+                             "host_link_frac": host_read / (ga_us * 1e-6) / 1e9 / HOST_LINK_PEAK_GBPS
                              if ga_us else 0.0},
-        "host_link": {"miss_bytes_per_step": host_bytes,
-                      "miss_rows_per_step": (c[3] + c[4]) / n,
+        "host_link": {"bytes_read_per_step": host_read,
+                      "rows_read_per_step": c[8] / n,
+                      "distinct_miss_bytes_per_step": host_distinct,
+                      "distinct_miss_rows_per_step": (c[3] + c[4]) / n,
                       "hit_rate": c[1] / max(1, c[0] - c[2]),
                       "peak_GBps": HOST_LINK_PEAK_GBPS},
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
         "kernels_GBps": {k: round(v["GBps"], 1) for k, v in kern.items()},
         "counters_timed": dict(zip(K.COUNTER_NAMES, c)),
+        "segments_steps_per_s": off["segments"],
+        "environment": environment(),
     }
     if resd is not None:
-        line["resident"] = {"value": resd["steps_per_s"], "ms_per_step": 1e3 * resd["seconds"] / args.steps,
+        line["resident"] = {"value": resd["steps_per_s"], "ms_per_step": 1e3 * resd["seconds"] / resd["steps"],
+                            "segments_steps_per_s": resd["segments"],
                             "kernels_us": {k: round(v["avg_us"], 2) for k, v in resd["kernels"].items()}}
         line["offload_slowdown"] = resd["steps_per_s"] / off["steps_per_s"] - 1.0
+        line["offload_slowdown_per_pair"] = [round(b / a - 1.0, 4) for a, b in zip(off["segments"], resd["segments"])]
     if args.quantize_rows > 0:
         log(f"quantise-on-append over {args.quantize_rows} rows")
         line["quantize"] = quantize_bench(args.quantize_rows)
