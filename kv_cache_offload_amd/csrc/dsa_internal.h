@@ -79,8 +79,8 @@ struct ScratchT {
   P<int32_t> src;           // [R_max*K]
   P<int32_t> map;           // [R_max][K]
   P<uint8_t> compact;       // [R_max*K][row_bytes]
-  P<float> part_o;          // [R_max][nsplit_max][H][latent]
-  P<float> part_ml;         // [R_max][nsplit_max][H][2]
+  P<uint16_t> part_o;       // fp16 [R_max][nsplit_max][H/16][32][16][16]: split partials (attention)
+  P<float> part_ml;         // [R_max][nsplit_max][H][4]: max, sum, scale of the split partial, 0
   P<int64_t> counters;      // [16] union, hit, ring, miss, miss_noslot, evict, host_bytes, resident,
                             //      host_reads (rows read from the host mirror, per reading query row)
   P<int64_t> info;          // [8] see kInfo* below

@@ -30,8 +30,11 @@
 //     through LDS; the B fragments (8 rows of one dim) come from the row-major
 //     latent with the LDS transpose read ds_read_b64_tr_b16 (4 rows x 1
 //     column per lane).
-// Each workgroup writes (max, sum, unnormalised O) and a merge kernel combines
-// the splits with the log-sum-exp rule.
+// Each workgroup writes its (max, sum) and its normalised O / sum in fp16 with
+// a power-of-two scale per head, and a merge kernel combines the splits with the
+// log-sum-exp rule.  The fp16 rounding is at most 2^-11 of the split's largest
+// |O / sum| for a head, a weighted mean of dequantised rows, so each output
+// element is off by at most 2^-11 of the largest |dequantised latent| it mixes.
 #include "gather_assign.h"
 
 namespace dsa {
@@ -64,6 +67,15 @@ struct AttnKArgs {
   int64_t max_positions;
   float scale_log2;          // softmax_scale * log2(e)
 };
+
+// Two fp32 -> packed fp16 (round to nearest even), as one 32-bit word.
+__device__ inline uint32_t pack_f16(float a, float b) {
+  const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+  uint16_t ua, ub;
+  __builtin_memcpy(&ua, &ha, 2);
+  __builtin_memcpy(&ub, &hb, 2);
+  return (uint32_t)ua | ((uint32_t)ub << 16);
+}
 
 // Two fp32 -> packed bf16 (round to nearest even), as one 32-bit word.
 __device__ inline uint32_t pack_bf16(float a, float b) {
@@ -412,15 +424,45 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
       for (int nt = 0; nt < 32; ++nt) dst[nt * 16 + l16] = o[nt][v] * inv;
     }
   } else {
-    // partials as [r][split][nt][l16][h]: the lane's four heads are contiguous
-    const auto dst = s.part_o + (((int64_t)r * ka.ns_stride + split) * 32 * 16 + l16) * H + h0 + 4 * q4;
+    // The split's partial, normalised (y = O / sum, a weighted mean of the
+    // split's dequantised rows) and stored as fp16 with a power-of-two scale per
+    // head that keeps |y| below 2^15: relative rounding 2^-11 per element, and
+    // half the bytes of fp32 for the merge to read.  Layout
+    // [r][split][wave][nt][l16][16 heads]: a wave's store covers 512 contiguous
+    // bytes per nt (whole lines); the lane's four heads are contiguous.
+    f32x4 amax = (f32x4){0.f, 0.f, 0.f, 0.f};        // per head, of the unnormalised O
 #pragma unroll
     for (int nt = 0; nt < 32; ++nt)
-      *reinterpret_cast<DSA_GLOBAL f32x4*>(dst + (int64_t)nt * 16 * H) = o[nt];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) amax[v] = fmaxf(amax[v], fabsf(o[nt][v]));
+    float scv[4], mul[4];                            // the scale, and 1 / sum times the scale
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float m = amax[v];
+#pragma unroll
+      for (int sh = 1; sh < 16; sh <<= 1) m = fmaxf(m, __shfl_xor(m, sh));
+      const float den = __shfl(ps, 4 * q4 + v);      // the sum of head h0 + 4 q4 + v
+      const float inv = den > 0.f ? 1.f / den : 0.f;
+      int ex = 0;
+      (void)frexpf(m * inv, &ex);                    // max |y| < 2^ex
+      scv[v] = ex > 15 ? ldexpf(1.f, 15 - ex) : 1.f;
+      mul[v] = inv * scv[v];
+    }
+    const auto dst = s.part_o + ((((int64_t)r * ka.ns_stride + split) * NW + wave) * 32 * 16 + l16) * 16 + 4 * q4;
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) {
+      u32x2 w;
+      w.x = pack_f16(o[nt][0] * mul[0], o[nt][1] * mul[1]);
+      w.y = pack_f16(o[nt][2] * mul[2], o[nt][3] * mul[3]);
+      *reinterpret_cast<DSA_GLOBAL u32x2*>(dst + (int64_t)nt * 16 * 16) = w;
+    }
+    // (max, sum, 1 / scale) of head h0 + l16: its scale sits in lane group l16 / 4, register l16 % 4
+    const float s0 = __shfl(scv[0], 16 * (l16 >> 2)), s1 = __shfl(scv[1], 16 * (l16 >> 2));
+    const float s2 = __shfl(scv[2], 16 * (l16 >> 2)), s3 = __shfl(scv[3], 16 * (l16 >> 2));
+    const float sc = (l16 & 3) == 0 ? s0 : (l16 & 3) == 1 ? s1 : (l16 & 3) == 2 ? s2 : s3;
     if (q4 == 0) {
       const int64_t base = ((int64_t)r * ka.ns_stride + split) * H + h0 + l16;
-      s.part_ml[base * 2 + 0] = mx;
-      s.part_ml[base * 2 + 1] = ps;
+      *reinterpret_cast<DSA_GLOBAL f32x4*>(s.part_ml + base * 4) = (f32x4){mx, ps, 1.f / sc, 0.f};
     }
   }
 }
@@ -436,12 +478,12 @@ struct MergeKArgs {
 // Workgroups [0, merge_blocks) of each sequence merge; the others run the
 // gather's assign pass (gather_assign.h), which nothing in the round waits for.
 // One merge workgroup per (16-dim tile nt, group of HW heads, query row), for
-// at most MAXS splits:
-// out[h][d] = sum_s w_s[h] O_s[h][d] with w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s'.
-// A split's [16][H] tile of dims nt has rows of H floats; the workgroup reads
-// the HW-head part of each row (whole 128-byte lines for HW = 32), EPT
-// consecutive floats per thread.  The sums leave through LDS as [h][16] (16
-// contiguous floats per head).
+// at most MAXS splits, each split s holding y_s = O_s / l_s times its scale c_s:
+// out[h][d] = sum_s w_s[h] y_s[h][d] with w_s = 2^(m_s - M) l_s / sum_s' 2^(m_s' - M) l_s'.
+// A split's tile of dims nt is 16 heads x 16 dims per attention wave (512
+// contiguous bytes of fp16); the workgroup reads the tiles of its HW heads
+// (whole lines), EPT consecutive values per thread.  The sums leave through LDS
+// as [h][16] (16 contiguous floats per head).
 template <int MAXS, int HW>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
   constexpr int EPT = 16 * HW / 256;          // tile elements per thread
@@ -450,6 +492,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
   static_assert(EPT >= 1 && 16 * HW == 256 * EPT, "tile of 16 x HW floats over 256 threads");
   __shared__ float wgt[MAXS * HW];            // [split][head]: the max, then the weight
   __shared__ float sl[MAXS * HW];             // [split][head]: the sum
+  __shared__ float isc[MAXS * HW];            // [split][head]: 1 / the partial's scale
   __shared__ float tile[HW * 17];
   const StepArgs& a = ka.ga.a;
   const int seq = blockIdx.y;
@@ -468,26 +511,29 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
   const int e0 = tid * EPT, l16 = e0 / HW, hl0 = e0 % HW;
   // this thread's elements of every split, loaded before the weights are known
   // (splits past `used` re-read the last one and get weight 0)
-  const auto src = s.part_o + (((int64_t)r * ka.ns_stride * 32 + nt) * 16 + l16) * H + HW * hg + hl0;
+  static_assert(EPT <= 2, "a thread's elements lie in one attention wave's tile");
+  const int hh = HW * hg + hl0;                          // the thread's first head
+  const auto src = s.part_o + (((int64_t)r * ka.ns_stride * (H / 16) + hh / 16) * 32 + nt) * 256 + l16 * 16 + hh % 16;
   const int64_t split_stride = (int64_t)32 * 16 * H;
   float x[MAXS][EPT];
 #pragma unroll
   for (int sp = 0; sp < MAXS; ++sp) {
     const auto at = src + (sp < used ? sp : used - 1) * split_stride;
     if constexpr (EPT == 2) {
-      const u32x2 v = *reinterpret_cast<const DSA_GLOBAL u32x2*>(at);
-      x[sp][0] = __uint_as_float(v.x);
-      x[sp][1] = __uint_as_float(v.y);
+      const uint32_t v = *reinterpret_cast<const DSA_GLOBAL uint32_t*>(at);
+      x[sp][0] = f16_bits_to_f32(v & 0xFFFFu);
+      x[sp][1] = f16_bits_to_f32(v >> 16);
     } else {
-#pragma unroll
-      for (int k = 0; k < EPT; ++k) x[sp][k] = at[k];
+      x[sp][0] = f16_bits_to_f32(*at);
     }
   }
-  for (int t = tid; t < used * HW; t += 256) {           // every split's (max, sum) at once
+  for (int t = tid; t < used * HW; t += 256) {           // every split's (max, sum, 1 / scale) at once
     const int sp = t / HW, h = t % HW;
     const int64_t base = ((int64_t)r * ka.ns_stride + sp) * H + HW * hg + h;
-    wgt[t] = s.part_ml[base * 2];
-    sl[t] = s.part_ml[base * 2 + 1];
+    const f32x4 ml = *reinterpret_cast<const DSA_GLOBAL f32x4*>(s.part_ml + base * 4);
+    wgt[t] = ml[0];
+    sl[t] = ml[1];
+    isc[t] = ml[2];
   }
   __syncthreads();
   {
@@ -519,7 +565,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       const int sp = c + TPH * e;
-      if (sp < used) wgt[sp * HW + wh] = wloc[e] * inv;
+      if (sp < used) wgt[sp * HW + wh] = wloc[e] * inv * sl[sp * HW + wh] * isc[sp * HW + wh];
     }
   }
   __syncthreads();

@@ -258,8 +258,8 @@ ScrOff scratch_layout(const Geometry& g) {
   o.src = take((size_t)RK * 4);
   o.map = take((size_t)RK * 4);
   o.compact = take((size_t)RK * rb);
-  o.po = take((size_t)g.r_max * g.nsplit_max * g.heads * g.latent * 4);
-  o.pml = take((size_t)g.r_max * g.nsplit_max * g.heads * 2 * 4);
+  o.po = take((size_t)g.r_max * g.nsplit_max * g.heads * g.latent * 2);
+  o.pml = take((size_t)g.r_max * g.nsplit_max * g.heads * 4 * 4);
   o.cnt = take(16 * 8);
   o.info = take(8 * 8);
   o.selmask = take((size_t)P / 32 * 4);
@@ -288,7 +288,7 @@ SeqScratch scratch_at(uint8_t* base, const ScrOff& o) {
   c.src = reinterpret_cast<int32_t*>(base + o.src);
   c.map = reinterpret_cast<int32_t*>(base + o.map);
   c.compact = base + o.compact;
-  c.part_o = reinterpret_cast<float*>(base + o.po);
+  c.part_o = reinterpret_cast<uint16_t*>(base + o.po);
   c.part_ml = reinterpret_cast<float*>(base + o.pml);
   c.counters = reinterpret_cast<int64_t*>(base + o.cnt);
   c.info = reinterpret_cast<int64_t*>(base + o.info);
