@@ -325,18 +325,21 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
 }
 
 // Called by every workgroup (one per query row) of a sequence at the end of its
-// selection; the last of the n_rows workgroups to arrive runs the plan.  Every
-// wave first releases its own marks (relaxed atomic ORs) at device scope: a
-// workgroup barrier alone does not wait for another wave's outstanding memory
-// operations, so without it a mark could still be in flight when thread 0
-// announces the arrival.  Thread 0's arrival is an acquire-release atomic at
-// device scope; the last workgroup's barrier after it hands the acquire to every
-// wave (they share the CU's caches), so all marks of all arrivals are visible to
-// the plan.  No workgroup waits for another.
+// selection; the last of the n_rows workgroups to arrive runs the plan.  What
+// the plan reads from the other workgroups is only their marks in the
+// selection bitmap, and every mark is a device-scope atomic OR: such an atomic
+// is performed where all XCDs see it once it has completed.  So before the
+// arrival every wave waits until its own marks have completed (a workgroup
+// barrier alone does not wait for another wave's outstanding memory
+// operations); thread 0's arrival is then an acquire-release atomic at device
+// scope, and the last workgroup's barrier after it hands the acquire to every
+// wave (they share the CU's caches).  Nothing else needs releasing -- the
+// selections themselves are read by later kernels -- so no wave writes its L2
+// back here.  No workgroup waits for another.
 __device__ inline void plan_if_last(const UnitG& u, const ScratchG& s, const PlanParams& pp, uint32_t n_rows,
                                     const PlanState& ps, uint32_t* lds) {
   __shared__ uint32_t s_last;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_s_waitcnt(0);                       // this wave's marks (and every other access) completed
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(s.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
