@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--workload", default="single_stream_50k")
     p.add_argument("--kernel-steps", type=int, default=1024, help="steps of the pass with per-kernel events")
     p.add_argument("--no-resident", action="store_true", help="skip the HBM-resident comparison run")
+    p.add_argument("--resident-only", action="store_true",
+                   help="run the HBM-resident session alone (counter runs of that mode); the line reports it")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--calib-copy", action="store_true", help="also run a plain 2 GiB device copy (PMC scaling)")
@@ -305,6 +307,8 @@ def run_pairs(w, inputs, args):
     both modes alike.  Returns one result per mode."""
     import kv_cache_offload_amd as K
     modes = [("offload", K.KV_OFFLOAD)] + ([] if args.no_resident else [("resident", K.KV_HBM_RESIDENT)])
+    if args.resident_only:
+        modes = [("resident", K.KV_HBM_RESIDENT)]
     repl = K.REPL_CLOCK if args.replacement == "clock" else K.REPL_RING
     runners, res = {}, {}
     for name, mode in modes:
@@ -542,7 +546,8 @@ def main():
         print(json.dumps({"workload": w.name, "replacement_probe": probe}), flush=True)
         return
     both = run_pairs(w, inputs, args)
-    off, resd = both["offload"], both.get("resident")
+    primary = "resident" if args.resident_only else "offload"
+    off, resd = both[primary], (None if args.resident_only else both.get("resident"))
 
     R, Q, NL = w.rows_per_step, w.seqs, w.layers
     rb = w.row_bytes
@@ -601,7 +606,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "layers": NL, "sequences": Q, "history": w.history, "query_rows": R,
                    "top_k": w.top_k, "hot_slots": w.hot_slots, "index_heads": w.index_heads, "heads": w.heads,
-                   "row_bytes": rb, "mode": "offload", "replacement": args.replacement,
+                   "row_bytes": rb, "mode": primary, "replacement": args.replacement,
                    "L_at_timed_start": off["L_start"]},
         "query_rows_per_s": off["steps_per_s"] * R * Q,
         "roofline": roof,

@@ -83,7 +83,7 @@ struct ScratchT {
   P<float> part_ml;         // [R_max][nsplit_max][H][4]: max, sum, scale of the split partial, 0
   P<int64_t> counters;      // [16] union, hit, ring, miss, miss_noslot, evict, host_bytes, resident,
                             //      host_reads (rows read from the host mirror, per reading query row)
-  P<int64_t> info;          // [8] see kInfo* below
+  P<int64_t> info;          // [16] see kInfo* below
   P<uint32_t> selmask;      // [P_pad/32] positions selected by any row this step (cleared by the assign)
   P<uint32_t> hitmask;      // [P_pad/32] selected positions that hit a slot (written by the plan each step)
   P<i32x4> pdesc;           // [P_pad] per selected position: union index, kind, source, slot to fill (this step)
@@ -104,8 +104,13 @@ using UnitG = UnitT<GlobalPtr>;
 using ScratchG = ScratchT<GlobalPtr>;
 static_assert(sizeof(UnitDev) == sizeof(UnitG) && sizeof(SeqScratch) == sizeof(ScratchG), "same layout");
 
-// SeqScratch::info fields, written by the gather scan for the rest of the step.
-enum { kInfoUnion = 0, kInfoWriteback = 1, kInfoAssigned = 2, kInfoRound = 3, kInfoM = 4, kInfoHand = 5 };
+// SeqScratch::info fields, written by the gather plan for the rest of the step:
+// the counts phase writes the round-start state and the union's counts, the
+// walk the writeback position and the number of misses that took a slot.
+enum {
+  kInfoUnion = 0, kInfoWriteback = 1, kInfoAssigned = 2, kInfoRound = 3, kInfoM = 4, kInfoHand = 5,
+  kInfoMiss = 6, kInfoRing = 7, kInfoHit = 8, kInfoWords = 16
+};
 
 struct Geometry {
   int index_heads, index_dim, heads, latent, rope, group, top_k, hot_slots;
@@ -221,10 +226,13 @@ hipError_t prepare_topk_kernels();
 // clear_hist: also zero the Top-K histograms for the next step (not in a
 // prefetch round, whose scratch set has none).
 hipError_t launch_gather(const Geometry& g, const StepArgs& a, hipStream_t st, bool clear_hist = true);
+// walk: an extra workgroup per sequence runs the walk of the gather plan (a
+// decode step, whose Top-K ran only the plan's counts phase).
 hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_lat,
-                       const uint16_t* q_rope, float* out, hipStream_t st);
+                       const uint16_t* q_rope, float* out, hipStream_t st, bool walk);
 // The split merge (skipped when one split covers the selection) and, in the
-// same launch, the gather's assign pass.
+// same launch, the gather's assign pass, which also copies each filled miss's
+// row from the compact rows into its slot.
 hipError_t launch_attn_merge(const Geometry& g, const StepArgs& a, float* out, hipStream_t st);
 
 // Unit maintenance (one unit per launch).

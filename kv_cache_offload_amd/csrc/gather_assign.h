@@ -7,11 +7,13 @@
 // "Decision 2": the recent ring goes back to the mirror in 64-row batches.
 // One wave per 64 positions, one lane per position: each selected lane writes
 // its union entry (position, kind, source) and descriptor and does its slot
-// work.  Further blocks clear the step's Top-K histograms and write a due ring
-// batch back.  It runs as its own kernel (prefetch rounds) or as extra
-// workgroups of the attention merge (decode steps), after attention: the
-// attention kernel derives its rows' sources from the plan's outputs, and no
-// reader of this round consults what this pass writes.
+// work; in a decode step the wave then copies its filled misses' rows from the
+// compact rows into their slots.  Further blocks clear the step's Top-K
+// histograms and write a due ring batch back.  It runs as its own kernel
+// (prefetch rounds, whose fill kernel copies the rows from the host mirror) or
+// as extra workgroups of the attention merge (decode steps), after attention:
+// the attention kernel derives its rows' sources from the plan's outputs, and
+// no reader of this round consults what this pass writes.
 #pragma once
 
 #include "gather_plan.h"
@@ -28,6 +30,7 @@ struct GatherKArgs {
   int clear_blocks;                     // then blocks clearing the Top-K histograms; the rest write back the ring
   int r_max;
   int clock;                            // CLOCK replacement: hits and fills set their slot's reference bit
+  int copy_fills;                       // copy each filled miss's row from the compact rows (attention wrote them)
   int64_t max_positions;
 };
 
@@ -89,15 +92,36 @@ __device__ inline void assign_block(const GatherKArgs& ka, int block, int seq) {
   const uint64_t selb = __ballot(mine);
   if (!selb) return;
   if (bitpos == 0 && sw) s.selmask[w] = 0;             // read by every lane above: clear for the next step
+  const uint32_t below = bit - 1u;
+  const uint32_t ux = bu + __popc(sw & below);         // this lane's union entry (if selected)
+  const uint32_t rw = off ? (sw & ring_bits(w, M)) : 0u;
+  const uint32_t k = bm + __popc(sw & ~hw & ~rw & below);   // this lane's miss index (if a miss)
+  const bool fills = off && mine && !((rw | hw) & bit) && k < n_assigned;
+  // Decode steps: the compact rows of the wave's first four misses that take a
+  // slot are requested now, beside the slot-table loads below; lane c holds
+  // 16-byte piece c of each.
+  const int64_t rb = ka.row_bytes;
+  uint64_t pre = ka.copy_fills ? __ballot(fills && ux < (uint32_t)ka.max_union) : 0ull;
+  int pl[4];
+  u32x4 pv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    pl[q] = -1;
+    if (pre) {                                         // (uniform)
+      pl[q] = __builtin_ctzll(pre);
+      pre &= pre - 1;
+      const uint32_t x = __shfl(ux, pl[q]);
+      if (lane < kCopyChunks16)
+        pv[q] = *reinterpret_cast<const DSA_GLOBAL u32x4*>(s.compact + (int64_t)x * rb + 16 * lane);
+    }
+  }
+  int32_t fill = -1;                                   // the slot this lane's miss fills
   if (mine) {
-    const uint32_t below = bit - 1u;
-    const uint32_t ux = bu + __popc(sw & below);
-    int32_t kind, src, fill = -1;
+    int32_t kind, src;
     if (!off) {
       kind = SRC_RES;
       src = (int32_t)p;
     } else {
-      const uint32_t rw = sw & ring_bits(w, M);
       if (rw & bit) {
         kind = SRC_RING;
         src = (int32_t)(p % ka.ring_cap);
@@ -111,7 +135,6 @@ __device__ inline void assign_block(const GatherKArgs& ka, int block, int seq) {
           raise_err(a.err, kErrHitSlot);
         }
       } else {
-        const uint32_t k = bm + __popc(sw & ~hw & ~rw & below);
         src = (int32_t)p;
         if (k < n_assigned) {
           kind = SRC_MISS;
@@ -143,12 +166,47 @@ __device__ inline void assign_block(const GatherKArgs& ka, int block, int seq) {
       s.pdesc[p] = (i32x4){(int32_t)ux, kind, src, fill};
     } else {
       raise_err(a.err, kErrSelection);
+      fill = -1;
     }
+  }
+  if (!ka.copy_fills) return;
+  // The filled misses' rows, from the compact rows attention wrote (the bytes it
+  // read from the host mirror) into their slots: the four requested above, then
+  // any others of the wave four at a time.
+  uint64_t fb = __ballot(fill >= 0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (pl[q] < 0) continue;                           // (uniform)
+    const int32_t f = __shfl(fill, pl[q]);
+    fb &= ~(1ull << pl[q]);
+    if (f >= 0 && lane < kCopyChunks16)
+      *reinterpret_cast<DSA_GLOBAL u32x4*>(u.slots + (int64_t)f * rb + 16 * lane) = pv[q];
+  }
+  while (fb) {                                         // (uniform)
+    int32_t f4[4];
+    u32x4 v4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f4[q] = -1;
+      if (fb) {
+        const int l = __builtin_ctzll(fb);
+        fb &= fb - 1;
+        f4[q] = __shfl(fill, l);
+        const uint32_t x = __shfl(ux, l);
+        if (lane < kCopyChunks16)
+          v4[q] = *reinterpret_cast<const DSA_GLOBAL u32x4*>(s.compact + (int64_t)x * rb + 16 * lane);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (f4[q] >= 0 && lane < kCopyChunks16)
+        *reinterpret_cast<DSA_GLOBAL u32x4*>(u.slots + (int64_t)f4[q] * rb + 16 * lane) = v4[q];
   }
 }
 
 // Arguments and the number of blocks per sequence of the assign pass.
-inline GatherKArgs gather_args(const Geometry& g, const StepArgs& a, bool clear_hist, int64_t* blocks_per_seq) {
+inline GatherKArgs gather_args(const Geometry& g, const StepArgs& a, bool clear_hist, bool copy_fills,
+                               int64_t* blocks_per_seq) {
   const int64_t words = (a.l_max + 31) / 32;
   const int64_t waves = (words + 1) / 2;
   const int64_t blocks = (waves + 3) / 4;
@@ -157,7 +215,7 @@ inline GatherKArgs gather_args(const Geometry& g, const StepArgs& a, bool clear_
       clear_hist ? ((int64_t)(kHistReps + 1) * a.R * (kRadixBins / 4) + kGatherThreads - 1) / kGatherThreads : 0;
   *blocks_per_seq = blocks + clear_blocks + (g.mode == 0 ? wb_blocks : 0);
   return GatherKArgs{a, g.hot_slots, g.ring_cap, g.ring_rows, g.mode, g.row_bytes, g.top_k, g.r_max * g.top_k,
-                     (int)blocks, (int)clear_blocks, g.r_max, g.clock ? 1 : 0, g.max_positions};
+                     (int)blocks, (int)clear_blocks, g.r_max, g.clock ? 1 : 0, copy_fills ? 1 : 0, g.max_positions};
 }
 
 }  // namespace dsa

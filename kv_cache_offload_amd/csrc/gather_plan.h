@@ -1,18 +1,22 @@
-// gather_plan.h -- the per-sequence plan of the hot gather, run by one
-// 1024-thread workgroup once every query row of the sequence has marked its
-// selection in the step's bitmaps.
+// gather_plan.h -- the per-sequence plan of the hot gather, once every query
+// row of the sequence has marked its selection in the step's bitmaps.
 //
 // Page "From 1M total to 15+ streams x 1M: the capacity breakthrough of
 // GLM-5.3 KV cache offload", section "GPU cache management errs too": slots in
 // use this round are pinned, a slot filled this round is a hit source only from
 // the next round, and replacement walks the slots as a ring, skipping the
-// pinned ones.  The plan classifies the round's union against the positions
-// cached at round start (a per-position bitmap: every cached slot was filled
-// in an earlier round), turns the bitmaps into per-32-position-word prefix
-// counts of union entries and of misses, lists the unpinned slots in ring
-// order from the hand (the victim of the k-th miss in ascending position order
-// is victim[k]), and publishes the step's counters, the new hand and the
-// round-end state (M after writeback, round + 1).
+// pinned ones.  The plan has two phases:
+//   * counts (one 1024-thread workgroup): classifies the round's union against
+//     the positions cached at round start (a per-position bitmap: every cached
+//     slot was filled in an earlier round) and turns the bitmaps into
+//     per-32-position-word prefix counts of union entries and of misses -- what
+//     attention needs to find each selected row's source and compact place;
+//   * walk (one workgroup of any size): lists the unpinned slots in ring order
+//     from the hand (the victim of the k-th miss in ascending position order is
+//     victim[k]) and publishes the step's counters, the new hand and the
+//     round-end state (M after writeback, round + 1).  Only the assign pass,
+//     which fills the slots, uses the victims: in a decode step the walk runs in
+//     one workgroup of the attention launch, beside attention.
 #pragma once
 
 #include "dev_util.h"
@@ -46,21 +50,26 @@ struct PlanState {
 constexpr int kPlanRegWords = 4;   // union words a thread keeps in registers (histories <= 131,072)
 constexpr int kPlanChunk = 8;      // 64-word rows of a wave per batch of loads (longer histories)
 constexpr int kWalkPer = 4;        // ring offsets a thread examines per pass of the victim walk
-constexpr int kWalkWords = kPlanThreads * kWalkPer / 32;   // 32-offset words per pass
+// 32-offset words per pass of a T-thread walk
+template <int T>
+constexpr int walk_words() { return T / 32 * kWalkPer; }
+constexpr int kWalkWords = walk_words<kPlanThreads>();
 
-// lds: at least kWalkWords + 32 words of LDS the caller no longer uses.
-__device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, const PlanParams& pp,
-                                         const PlanState& ps, uint32_t* lds) {
+// The union's size and its split by source, from the counts phase.
+struct PlanCounts {
+  uint32_t U, n_miss, n_ring, n_hit;
+};
+
+// Counts phase, by one kPlanThreads workgroup: the hit words, the per-word
+// prefix counts of union entries and of misses, and the totals.  Also zeroes
+// the step's host-read counter (the round's readers add to it).
+__device__ inline PlanCounts plan_counts_block(const UnitG& u, const ScratchG& s, const PlanParams& pp,
+                                               const PlanState& ps) {
   __shared__ uint32_t sh[4 * kPlanWaves];
-  __shared__ int s_last_v, s_assigned_last_v;
-  __shared__ int64_t s_end_o;                          // offset (lap * S + o) of the last victim
-  __shared__ uint32_t s_evict;
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t L = ps.L, M = ps.M;
   const int32_t round = ps.round;
   const bool off = pp.mode == 0;
-  const int hand = off ? ps.hand : 0;
-  const int S = pp.S;
   const int64_t nw = (L + 31) / 32;
   const auto sel = s.selmask;
   const int64_t per = (nw + kPlanThreads - 1) / kPlanThreads;
@@ -80,7 +89,6 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
       hwr[e] = (off && w < w1) ? u.hot[w] : 0u;
     }
   }
-  const int64_t total_prev = tid < 8 ? u.totals[tid] : 0;
 
   // Union, miss, ring and hit counts per word, scanned in word (= position) order.
   // (Register arrays are indexed only by unrolled constants.)
@@ -191,13 +199,49 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
     });
   }
 
+  if (tid == 0) {
+    s.info[kInfoUnion] = U;
+    s.info[kInfoMiss] = n_miss;
+    s.info[kInfoRing] = n_ring;
+    s.info[kInfoHit] = n_hit;
+    s.info[kInfoRound] = round;
+    s.info[kInfoM] = M;
+    s.info[kInfoHand] = off ? ps.hand : 0;
+  } else if (tid == 8) {
+    s.counters[8] = 0;                                 // host reads: the round's readers add them
+  }
+  return PlanCounts{U, n_miss, n_ring, n_hit};
+}
+
+// Walk phase, by one T-thread workgroup, after the counts phase (the selection
+// bitmap still holds the round's marks).  lds: at least walk_words<T>() + 32
+// words of LDS the caller no longer uses.
+template <int T>
+__device__ inline void plan_walk_block(const UnitG& u, const ScratchG& s, const PlanParams& pp,
+                                       const PlanState& ps, const PlanCounts& pc, uint32_t* lds) {
+  constexpr int NH = T / 32;                           // half-waves
+  constexpr int kWords = walk_words<T>();
+  constexpr int kEpl = (kWords + 63) / 64;             // pass words per lane in the pass scan
+  __shared__ int s_last_v, s_assigned_last_v;
+  __shared__ int64_t s_end_o;                          // offset (lap * S + o) of the last victim
+  __shared__ uint32_t s_evict;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t L = ps.L, M = ps.M;
+  const int32_t round = ps.round;
+  const bool off = pp.mode == 0;
+  const int hand = off ? ps.hand : 0;
+  const int S = pp.S;
+  const auto sel = s.selmask;
+  const uint32_t U = pc.U, n_miss = pc.n_miss, n_ring = pc.n_ring, n_hit = pc.n_hit;
+  const int64_t total_prev = tid < 8 ? u.totals[tid] : 0;
+
   // Victims: slots in ring order from the hand, never a pinned one -- a slot is
   // pinned this round iff the position it holds is selected (it is then a hit).
   // Ring policy: every unpinned slot is a candidate; one lap.  CLOCK (second
   // chance): on the first lap the unpinned slots whose reference bit was clear
   // at round start, on the second lap the unpinned slots whose bit was set (the
   // first lap cleared them and took every other unpinned slot).  Passes of
-  // kWalkWords * 32 ring offsets until every miss has a slot or the laps are
+  // walk_words<T>() * 32 ring offsets until every miss has a slot or the laps are
   // done; the k-th miss in ascending position order takes the k-th candidate.
   // victim[k] = (slot, the position it gives up).
   uint32_t n_assigned = 0;
@@ -208,17 +252,17 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
     s_evict = 0;
   }
   if (off && n_miss > 0) {
-    uint32_t* cnt_w = lds;                             // [kWalkWords] candidates per word, then their scan
+    uint32_t* cnt_w = lds;                             // [kWords] candidates per word, then their scan
     uint32_t cum = 0;                                  // candidates found in earlier passes
     const int half = tid >> 5, bit = tid & 31;
     const int laps = pp.clock ? 2 : 1;
     for (int lap = 0; lap < laps && cum < n_miss; ++lap) {
-      for (int64_t o0 = 0; o0 < S && cum < n_miss; o0 += (int64_t)kWalkWords * 32) {
+      for (int64_t o0 = 0; o0 < S && cum < n_miss; o0 += (int64_t)kWords * 32) {
         int32_t held[kWalkPer], slot[kWalkPer];
         uint32_t refw[kWalkPer];
 #pragma unroll
-        for (int e = 0; e < kWalkPer; ++e) {           // offset o0 + 32 (half + 32 e) + bit within the lap
-          const int64_t o = o0 + 32 * (half + 32 * e) + bit;
+        for (int e = 0; e < kWalkPer; ++e) {           // offset o0 + 32 (half + NH e) + bit within the lap
+          const int64_t o = o0 + 32 * (half + NH * e) + bit;
           slot[e] = o < S ? (int32_t)((hand + o) % S) : -1;
           held[e] = u.slot_pos[slot[e] >= 0 ? slot[e] : 0];
           refw[e] = pp.clock && slot[e] >= 0 ? u.ref[slot[e] >> 5] : 0u;
@@ -237,29 +281,39 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
           const bool referenced = slot[e] >= 0 && ((refw[e] >> (slot[e] & 31)) & 1u);
           const bool cand = slot[e] >= 0 && !pinned && (!pp.clock || referenced == (lap == 1));
           ub[e] = (uint32_t)(__ballot(cand) >> (tid & 32));   // this half-wave's word
-          if (bit == 0) cnt_w[half + 32 * e] = __popc(ub[e]);
+          if (bit == 0) cnt_w[half + NH * e] = __popc(ub[e]);
         }
         __syncthreads();
         if (tid < 64) {                                // exclusive scan of the pass's word counts, in offset order
-          const uint32_t a0 = cnt_w[2 * tid], a1 = cnt_w[2 * tid + 1];
-          const uint32_t inc = wave_incl_scan(a0 + a1, lane);
-          cnt_w[2 * tid] = inc - a0 - a1;
-          cnt_w[2 * tid + 1] = inc - a1;
-          if (tid == 63) cnt_w[kWalkWords] = inc;
+          uint32_t a[kEpl], sum = 0;
+#pragma unroll
+          for (int i = 0; i < kEpl; ++i) {
+            const int w = kEpl * tid + i;
+            a[i] = w < kWords ? cnt_w[w] : 0u;
+            sum += a[i];
+          }
+          uint32_t run = wave_incl_scan(sum, lane) - sum;
+#pragma unroll
+          for (int i = 0; i < kEpl; ++i) {
+            const int w = kEpl * tid + i;
+            if (w < kWords) cnt_w[w] = run;
+            run += a[i];
+          }
+          if (tid == 63) cnt_w[kWords] = run;
         }
         __syncthreads();
-        const uint32_t pass_total = cnt_w[kWalkWords];
+        const uint32_t pass_total = cnt_w[kWords];
 #pragma unroll
         for (int e = 0; e < kWalkPer; ++e) {
           if (!((ub[e] >> bit) & 1u)) continue;
-          const uint32_t k = cum + cnt_w[half + 32 * e] + __popc(ub[e] & ((1u << bit) - 1u));
+          const uint32_t k = cum + cnt_w[half + NH * e] + __popc(ub[e] & ((1u << bit) - 1u));
           if (k + 1 == cum + pass_total) s_last_v = slot[e];
           if (k < n_miss) {
             s.victim[k] = (i32x2){slot[e], held[e]};
             if (held[e] >= 0) atomicAdd(&s_evict, 1u);
             if (k + 1 == n_miss) {
               s_assigned_last_v = slot[e];
-              s_end_o = (int64_t)lap * S + o0 + 32 * (half + 32 * e) + bit;
+              s_end_o = (int64_t)lap * S + o0 + 32 * (half + NH * e) + bit;
             }
           }
         }
@@ -276,7 +330,7 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
   // bits of the hits (the only pinned slots) and of the filled victims.
   if (off && pp.clock && n_miss > 0) {
     const int64_t lim = min(s_end_o, (int64_t)S);
-    for (int w = tid; w < pp.s_words; w += kPlanThreads) {
+    for (int w = tid; w < pp.s_words; w += T) {
       uint32_t m = 0;
       for (int b = 0; b < 32; ++b) {
         const int64_t v = 32 * (int64_t)w + b;
@@ -304,18 +358,12 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
     }
     s.counters[tid] = cn;
     u.totals[tid] = total_prev + cn;
-  } else if (tid == 8) {
-    s.counters[8] = 0;                                 // host reads: the round's readers add them
   }
   if (tid == 0) {
     int64_t wb = -1;
     if (off && L - M >= pp.ring_rows) wb = M;
-    s.info[kInfoUnion] = U;
     s.info[kInfoWriteback] = wb;
     s.info[kInfoAssigned] = n_assigned;
-    s.info[kInfoRound] = round;
-    s.info[kInfoM] = M;
-    s.info[kInfoHand] = hand;
     if (off) {
       *u.hand = new_hand;
       if (wb >= 0) u.dyn[1] = M + pp.ring_rows;
@@ -325,31 +373,51 @@ __device__ inline void gather_plan_block(const UnitG& u, const ScratchG& s, cons
 }
 
 // Called by every workgroup (one per query row) of a sequence at the end of its
-// selection; the last of the n_rows workgroups to arrive runs the plan.  What
-// the plan reads from the other workgroups is only their marks in the
-// selection bitmap, and every mark is a device-scope atomic OR: such an atomic
-// is performed where all XCDs see it once it has completed.  So before the
-// arrival every wave waits until its own marks have completed (a workgroup
-// barrier alone does not wait for another wave's outstanding memory
-// operations); thread 0's arrival is then an acquire-release atomic at device
-// scope, and the last workgroup's barrier after it hands the acquire to every
-// wave (they share the CU's caches).  Nothing else needs releasing -- the
-// selections themselves are read by later kernels -- so no wave writes its L2
-// back here.  No workgroup waits for another.
+// selection; the last of the n_rows workgroups to arrive runs the counts phase
+// of the plan (kFull: then the walk too).  What the plan reads from the other
+// workgroups is only their marks in the selection bitmap, and every mark is a
+// device-scope atomic OR: such an atomic is performed where all XCDs see it
+// once it has completed.  So before the arrival every wave waits until its own
+// marks have completed (a workgroup barrier alone does not wait for another
+// wave's outstanding memory operations); thread 0's arrival is a relaxed
+// device-scope atomic, and the last workgroup then drops its cached copies
+// (an acquire fence at device scope, whose cache invalidation covers the whole
+// workgroup: its waves share the CU's and the XCD's caches) before reading the
+// bitmap.  Nothing needs releasing -- the selections themselves are read by
+// later kernels -- so no L2 is written back here.  No workgroup waits for
+// another.
+template <bool kFull>
 __device__ inline void plan_if_last(const UnitG& u, const ScratchG& s, const PlanParams& pp, uint32_t n_rows,
                                     const PlanState& ps, uint32_t* lds) {
   __shared__ uint32_t s_last;
   __builtin_amdgcn_s_waitcnt(0);                       // this wave's marks (and every other access) completed
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(s.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t prev = __hip_atomic_fetch_add(s.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = prev + 1 == n_rows;
     s_last = last ? 1u : 0u;
-    if (last) __hip_atomic_store(s.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (last) {
+      __hip_atomic_store(s.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
   }
   __syncthreads();
   if (!s_last) return;
-  gather_plan_block(u, s, pp, ps, lds);
+  const PlanCounts pc = plan_counts_block(u, s, pp, ps);
+  if constexpr (kFull) {
+    __syncthreads();
+    plan_walk_block<kPlanThreads>(u, s, pp, ps, pc, lds);
+  }
+}
+
+// The walk of a decode step, by one T-thread workgroup of the attention
+// launch: the round-start state and the counts from the step's info.
+template <int T>
+__device__ inline void plan_walk_from_info(const UnitG& u, const ScratchG& s, const PlanParams& pp, uint32_t* lds) {
+  const PlanState ps{u.dyn[0], s.info[kInfoM], (int32_t)s.info[kInfoRound], (int32_t)s.info[kInfoHand]};
+  const PlanCounts pc{(uint32_t)s.info[kInfoUnion], (uint32_t)s.info[kInfoMiss], (uint32_t)s.info[kInfoRing],
+                      (uint32_t)s.info[kInfoHit]};
+  plan_walk_block<T>(u, s, pp, ps, pc, lds);
 }
 
 }  // namespace dsa

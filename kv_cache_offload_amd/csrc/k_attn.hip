@@ -66,6 +66,8 @@ struct AttnKArgs {
   int off;                   // offload mode (hot slots, ring, host mirror)
   int64_t max_positions;
   float scale_log2;          // softmax_scale * log2(e)
+  int walk;                  // the extra workgroup of each sequence runs the plan's walk
+  PlanParams plan;
 };
 
 // Two fp32 -> packed fp16 (round to nearest even), as one 32-bit word.
@@ -129,12 +131,15 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   __shared__ __align__(16) float scl_s[2][8 * kBlk];
   __shared__ const DSA_GLOBAL uint8_t* s_from[kSplit];   // where each row is read from (null: masked)
   __shared__ int s_ux[kSplit];                            // its compact row, -1 if masked
-  __shared__ int s_fill[kSplit];                          // the slot a miss fills, -1 if none
 
   const StepArgs& a = ka.a;
   const int split = blockIdx.x, r = blockIdx.y, seq = blockIdx.z;
   const UnitG u = unit_of(a, seq);
   const ScratchG s = scratch_of(a, seq);
+  if (split == ka.nsplit) {                              // (uniform) past the splits: the walk of the sequence
+    if (ka.walk && r == 0) plan_walk_from_info<NT>(u, s, ka.plan, reinterpret_cast<uint32_t*>(lat_s[0]));
+    return;
+  }
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, q4 = lane >> 4;
   const int H = ka.H;
@@ -143,38 +148,32 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   const int j_begin = split * kSplit;
 
   // The split's rows: position (selection), then the row's place in the
-  // round, derived from the gather plan's outputs exactly as the assign pass
-  // derives it -- union index from the word's union count and the selected bits
-  // below, kind from the ring boundary M and the hit bits, and the source: a
-  // hit from its HBM slot (the position's slot), a ring row from the recent
-  // ring, a miss from the host mirror (repeated misses of the same round each
-  // read host memory; the k-th miss fills the plan's k-th victim slot), a
-  // resident row from the HBM row store.  The map entry of every selected index
-  // of the split is written here.
-  // Only the row's address is on the path to its data: a hit's slot is read
-  // with the words (for every selected position: a non-hit ignores it), and a
-  // miss's victim slot -- needed only when the row is written to it -- is
-  // requested here but used after the rows have been requested.
+  // round, derived from the counts phase of the gather plan exactly as the
+  // assign pass derives it -- union index from the word's union count and the
+  // selected bits below, kind from the ring boundary M and the hit bits, and
+  // the source: a hit from its HBM slot (the position's slot), a ring row from
+  // the recent ring, a miss from the host mirror (repeated misses of the same
+  // round each read host memory), a resident row from the HBM row store.  The
+  // map entry of every selected index of the split is written here.  A hit's
+  // slot is read with the words (for every selected position: a non-hit
+  // ignores it), so only the row's address is on the path to its data.
   const int n_sel = s.sel_n[r];
-  i32x2 victim = (i32x2){-1, -1};
-  bool assigned = false;                                 // this row's miss took the plan's victim
   bool host = false;                                     // this row is read from the host mirror
   if (tid < kSplit) {
     const int64_t M = s.info[kInfoM];
-    const uint32_t n_assigned = (uint32_t)s.info[kInfoAssigned];
     const int j = j_begin + tid;
     const int32_t pos = j < ka.K ? s.sel[(int64_t)r * ka.K + j] : -1;
     const bool ok = j < n_sel && pos >= 0 && pos < ka.max_positions;
     const int64_t w = ok ? pos >> 5 : 0;
     const uint32_t sw = s.selmask[w], hw = ka.off ? s.hitmask[w] : 0u;
-    const uint32_t bu = s.base_u[w], bm = s.base_m[w];
+    const uint32_t bu = s.base_u[w];
     const i32x2 ps = ka.off ? u.pos_slot[ok ? pos : 0] : (i32x2){-1, -1};
     const uint32_t bit = 1u << (pos & 31), below = bit - 1u;
     const uint32_t ux = bu + __popc(sw & below);
     const DSA_GLOBAL uint8_t* from = nullptr;
-    // A selected index whose position, bitmap bit, union index, hit slot or
-    // victim slot is not what the plan allows is skipped (its row masked) and
-    // raises the session's error flag: such a plan is inconsistent.
+    // A selected index whose position, bitmap bit, union index or hit slot is
+    // not what the plan allows is skipped (its row masked) and raises the
+    // session's error flag: such a plan is inconsistent.
     if (ok && (sw & bit) && ux < (uint32_t)ka.max_union) {
       if (!ka.off) {
         from = u.rows + (int64_t)pos * rb;
@@ -187,11 +186,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
           if (slot >= 0 && slot < ka.S) from = u.slots + (int64_t)slot * rb;
           else raise_err(a.err, kErrHitSlot);
         } else {
-          const uint32_t k = bm + __popc(sw & ~hw & ~rw & below);
-          if (k < n_assigned) {
-            victim = s.victim[k];                        // (slot, position it held)
-            assigned = true;
-          }
           from = u.rows + (int64_t)pos * rb;
           host = true;
         }
@@ -244,12 +238,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     }
   };
   request(0);
-  if (tid < kSplit) {
-    const bool fill_ok = victim.x >= 0 && victim.x < ka.S;
-    if (assigned && !fill_ok) raise_err(a.err, kErrVictim);
-    s_fill[tid] = (s_from[tid] && assigned && fill_ok) ? victim.x : -1;
-  }
-  __syncthreads();                                       // s_fill before block 0 is staged
 
   f32x4 o[32];
 #pragma unroll
@@ -263,10 +251,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     uint16_t* lat = lat_s[b & 1];
     uint16_t* rope = rope_s[b & 1];
     float* scl = scl_s[b & 1];
-    // This block's rows: the compact copy and a miss's slot fill (the gather's
-    // writes; nothing reads them again in this step, so they are streamed past
-    // the caches with non-temporal stores), and the LDS staging -- the int8
-    // latent widened to bf16, the scales as fp32, the RoPE as is.
+    // This block's rows: the compact copy (the gather's output; only the assign
+    // pass, which copies a miss's row into its slot, reads it again in this
+    // step, so it is streamed past the caches with non-temporal stores), and the
+    // LDS staging -- the int8 latent widened to bf16, the scales as fp32, the
+    // RoPE as is.
 #pragma unroll
     for (int e = 0; e < PPT; ++e) {
       const int q = tid + e * NT;
@@ -274,11 +263,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
       const int rl = q / kRowPieces, part = q % kRowPieces, row = b * kBlk + rl;
       const int ux = s_ux[row];
       const u32x4 v = ux >= 0 ? raw[b & 1][e] : (u32x4){0u, 0u, 0u, 0u};
-      if (ux >= 0) {
+      if (ux >= 0)
         __builtin_nontemporal_store(v, reinterpret_cast<DSA_GLOBAL u32x4*>(s.compact + (int64_t)ux * rb + 16 * part));
-        const int f = s_fill[row];
-        if (f >= 0) __builtin_nontemporal_store(v, reinterpret_cast<DSA_GLOBAL u32x4*>(u.slots + (int64_t)f * rb + 16 * part));
-      }
       if (part < 32) {
         uint32_t w[8];
         widen16(v, w);
@@ -472,11 +458,12 @@ struct MergeKArgs {
   float* out;
   int H, ns_stride;
   int split_rows;            // selected rows per attention split
-  int merge_blocks;          // merge workgroups per sequence; the rest of a row of the grid assign
+  int assign_blocks;         // assign workgroups per sequence (first: their chain of loads is the longer);
+                             // the rest of a row of the grid merge
 };
 
-// Workgroups [0, merge_blocks) of each sequence merge; the others run the
-// gather's assign pass (gather_assign.h), which nothing in the round waits for.
+// Workgroups [0, assign_blocks) of each sequence run the gather's assign pass
+// (gather_assign.h), which nothing in the round waits for; the others merge.
 // One merge workgroup per (16-dim tile nt, group of HW heads, query row), for
 // at most MAXS splits, each split s holding y_s = O_s / l_s times its scale c_s:
 // out[h][d] = sum_s w_s[h] y_s[h][d] with w_s = 2^(m_s - M) l_s / sum_s' 2^(m_s' - M) l_s'.
@@ -496,12 +483,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
   __shared__ float tile[HW * 17];
   const StepArgs& a = ka.ga.a;
   const int seq = blockIdx.y;
-  if ((int)blockIdx.x >= ka.merge_blocks) {             // (uniform) an assign workgroup
-    assign_block(ka.ga, (int)blockIdx.x - ka.merge_blocks, seq);
+  if ((int)blockIdx.x < ka.assign_blocks) {             // (uniform) an assign workgroup
+    assign_block(ka.ga, (int)blockIdx.x, seq);
     return;
   }
+  const int mb = (int)blockIdx.x - ka.assign_blocks;   // this merge workgroup
   const int n_hg = ka.H / HW;
-  const int r = blockIdx.x / (32 * n_hg), rem = blockIdx.x % (32 * n_hg);
+  const int r = mb / (32 * n_hg), rem = mb % (32 * n_hg);
   const int nt = rem / n_hg, hg = rem % n_hg;
   const ScratchG s = scratch_of(a, seq);
   const int H = ka.H;
@@ -591,13 +579,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
 inline int split_rows(const Geometry&) { return kSplit; }
 
 hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_lat, const uint16_t* q_rope,
-                       float* out, hipStream_t st) {
+                       float* out, hipStream_t st, bool walk) {
   const int rows = split_rows(g);
   const int nsplit = (g.top_k + rows - 1) / rows;
   AttnKArgs ka{a, q_lat, q_rope, out, g.top_k, g.heads, nsplit, g.nsplit_max, g.row_bytes,
                g.hot_slots, g.ring_cap, g.r_max * g.top_k, g.mode == 0 ? 1 : 0, g.max_positions,
-               g.softmax_scale * 1.4426950408889634f};
-  dim3 grid((unsigned)nsplit, (unsigned)a.R, (unsigned)a.n_seqs);
+               g.softmax_scale * 1.4426950408889634f, walk ? 1 : 0,
+               PlanParams{g.hot_slots, g.s_words, g.ring_rows, g.mode, g.clock ? 1 : 0}};
+  // one workgroup past the splits of each (row, sequence): row 0's runs the walk
+  dim3 grid((unsigned)nsplit + 1u, (unsigned)a.R, (unsigned)a.n_seqs);
   switch (g.heads) {
     case 16: return launch_k(attn_kernel<1, 2>, grid, dim3(64), 0, st, ka);
     case 32: return launch_k(attn_kernel<2, 2>, grid, dim3(128), 0, st, ka);
@@ -609,12 +599,12 @@ hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_l
 
 hipError_t launch_attn_merge(const Geometry& g, const StepArgs& a, float* out, hipStream_t st) {
   int64_t assign_blocks = 0;
-  const GatherKArgs ga = gather_args(g, a, true, &assign_blocks);
+  const GatherKArgs ga = gather_args(g, a, true, true, &assign_blocks);
   const int rows = split_rows(g);
   const int nsplit = (g.top_k + rows - 1) / rows;
   const int HW = g.heads == 16 ? 16 : 32;
   const int merge_blocks = nsplit == 1 ? 0 : 32 * (g.heads / HW) * a.R;   // one split: attention wrote out
-  MergeKArgs ka{ga, out, g.heads, g.nsplit_max, rows, merge_blocks};
+  MergeKArgs ka{ga, out, g.heads, g.nsplit_max, rows, (int)assign_blocks};
   const dim3 grid((unsigned)(merge_blocks + assign_blocks), (unsigned)a.n_seqs);
   static_assert(kGatherThreads == 256, "assign and merge workgroups share the launch");
   if (HW == 16) {

@@ -190,7 +190,7 @@ unsigned grid_for(int64_t work, int64_t cap = 4096) {
 
 hipError_t launch_gather(const Geometry& g, const StepArgs& a, hipStream_t st, bool clear_hist) {
   int64_t blocks = 0;
-  const GatherKArgs ka = gather_args(g, a, clear_hist, &blocks);
+  const GatherKArgs ka = gather_args(g, a, clear_hist, false, &blocks);
   return launch_k(gather_assign_kernel, dim3((unsigned)blocks, (unsigned)a.n_seqs), dim3(kGatherThreads), 0, st, ka);
 }
 

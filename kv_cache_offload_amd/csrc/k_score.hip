@@ -68,12 +68,16 @@ __device__ inline void count_digit(uint32_t* lh, int r, float score) {
 // per CU keep their next key tile in flight (with the compiler's unbounded
 // choice, about 228, only 8 could, and the kernel waited on HBM latency).
 // H_I = 4 keeps the default: it would spill under the bound.
-template <int HI, int NW>
+// G row tiles are multiplied at a time (Q is zero padded to a whole number of
+// groups): with G fixed at compile time the A fragments of the next k-step are
+// read from LDS while this k-step's G products run, instead of one read and one
+// wait per product.
+template <int HI, int NW, int G>
 __global__ __launch_bounds__(NW * 64, NW == 4 && HI >= 8 ? 3 : 1) void score_kernel(ScoreKArgs ka) {
   constexpr int kWaves = NW;
   constexpr int kThreads = NW * 64;
   constexpr int kMaxQPieces = kMaxQRows * 16 / kThreads;   // 16-byte Q pieces per thread
-  extern __shared__ __align__(16) uint16_t sq[];   // [MT*32][kQStride], weights, digit histograms
+  extern __shared__ __align__(16) uint16_t sq[];   // [MTP*32][kQStride], weights, digit histograms
   const StepArgs& a = ka.a;
   const int seq = blockIdx.y;
   const UnitG u = unit_of(a, seq);
@@ -82,8 +86,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 && HI >= 8 ? 3 : 1) void score_ker
   const int R = a.R;
   const int M = R * HI;
   const int MT = (M + 31) / 32;
-  float* sw = reinterpret_cast<float*>(sq + MT * 32 * kQStride);
-  uint32_t* lh = reinterpret_cast<uint32_t*>(sw + MT * 32);   // [R][1024] packed pairs of bins
+  const int MTP = (MT + G - 1) / G * G;                  // row tiles padded to whole groups
+  float* sw = reinterpret_cast<float*>(sq + MTP * 32 * kQStride);
+  uint32_t* lh = reinterpret_cast<uint32_t*>(sw + MTP * 32);   // [R][1024] packed pairs of bins
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -91,10 +96,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 && HI >= 8 ? 3 : 1) void score_ker
   const int hf = lane >> 5;
   const int64_t first_sub = ((int64_t)blockIdx.x * kWaves + wave) * ka.subs_per_wave;
 
-  // Q (zero padded to MT*32 rows) and the head weights, staged in LDS below;
+  // Q (zero padded to MTP*32 rows) and the head weights, staged in LDS below;
   // every load issued before the first is used (M <= 256: at most 16 per thread).
   const uint16_t* qg = ka.q + (int64_t)seq * M * 128;
-  const int nq = MT * 32 * 16;                           // 16-byte pieces of the padded Q
+  const int nq = MTP * 32 * 16;                          // 16-byte pieces of the padded Q
   bf16x8 qv[kMaxQPieces];
 #pragma unroll
   for (int e = 0; e < kMaxQPieces; ++e) {
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 && HI >= 8 ? 3 : 1) void score_ker
     const int c = threadIdx.x + e * kThreads;
     if (c < nq) *reinterpret_cast<bf16x8*>(sq + (c >> 4) * kQStride + (c & 15) * 8) = qv[e];
   }
-  if (threadIdx.x < MT * 32) sw[threadIdx.x] = wv;
+  if (threadIdx.x < MTP * 32) sw[threadIdx.x] = wv;
   __syncthreads();
 
   const auto scores = s.scores;
@@ -142,23 +147,32 @@ __global__ __launch_bounds__(NW * 64, NW == 4 && HI >= 8 ? 3 : 1) void score_ker
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) bn[ks] = kp[ks * 64];
     }
-    // Up to four row tiles at a time: independent accumulation chains, so the
-    // MFMA pipeline is never waiting on one accumulator.
-    for (int mt0 = 0; mt0 < MT; mt0 += 4) {
-      f32x16 acc4[4];
+    // G row tiles at a time: independent accumulation chains, so the MFMA
+    // pipeline is never waiting on one accumulator; the next k-step's A
+    // fragments are read while this k-step's products run.
+    for (int mt0 = 0; mt0 < MTP; mt0 += G) {
+      f32x16 acc4[G];
+      bf16x8 av[2][G];
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) acc4[i4] = (f32x16){0};
+      for (int i4 = 0; i4 < G; ++i4) {
+        acc4[i4] = (f32x16){0};
+        av[0][i4] = *reinterpret_cast<const bf16x8*>(sq + ((mt0 + i4) * 32 + n) * kQStride + 64 * hf);
+      }
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
+      for (int ks = 0; ks < 8; ++ks) {
+        if (ks + 1 < 8) {
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          if (mt0 + i4 >= MT) continue;
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(sq + ((mt0 + i4) * 32 + n) * kQStride + 64 * hf + 8 * ks);
-          acc4[i4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[ks], acc4[i4], 0, 0, 0);
+          for (int i4 = 0; i4 < G; ++i4)
+            av[(ks + 1) & 1][i4] =
+                *reinterpret_cast<const bf16x8*>(sq + ((mt0 + i4) * 32 + n) * kQStride + 64 * hf + 8 * (ks + 1));
         }
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        if (mt0 + i4 >= MT) continue;
+        for (int i4 = 0; i4 < G; ++i4)
+          acc4[i4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks & 1][i4], b[ks], acc4[i4], 0, 0, 0);
+      }
+#pragma unroll
+      for (int i4 = 0; i4 < G; ++i4) {
+        if (mt0 + i4 >= MT) continue;                  // (uniform) a padding tile
         const int mt = mt0 + i4;
         // acc[v] holds C[row = (v/4)*8 + hf*4 + v%4][col = n]
         float part[4];
@@ -232,18 +246,21 @@ __global__ __launch_bounds__(NW * 64, NW == 4 && HI >= 8 ? 3 : 1) void score_ker
 
 }  // namespace
 
+#define DSA_SCORE_KERNELS(HI, NW) \
+  (const void*)score_kernel<HI, NW, 1>, (const void*)score_kernel<HI, NW, 2>, (const void*)score_kernel<HI, NW, 4>
+
 hipError_t prepare_score_kernels() {
   const int max_lds = kMaxQRows * kQStride * 2 + kMaxQRows * 4 + 8 * (kRadixBins / 2) * 4;
-  const void* kernels[] = {(const void*)score_kernel<4, 4>,  (const void*)score_kernel<8, 4>,
-                           (const void*)score_kernel<16, 4>, (const void*)score_kernel<32, 4>,
-                           (const void*)score_kernel<4, 8>,  (const void*)score_kernel<8, 8>,
-                           (const void*)score_kernel<16, 8>, (const void*)score_kernel<32, 8>};
+  const void* kernels[] = {DSA_SCORE_KERNELS(4, 4),  DSA_SCORE_KERNELS(8, 4),  DSA_SCORE_KERNELS(16, 4),
+                           DSA_SCORE_KERNELS(32, 4), DSA_SCORE_KERNELS(4, 8),  DSA_SCORE_KERNELS(8, 8),
+                           DSA_SCORE_KERNELS(16, 8), DSA_SCORE_KERNELS(32, 8)};
   for (const void* k : kernels) {
     const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
+#undef DSA_SCORE_KERNELS
 
 hipError_t launch_score(const Geometry& g, const StepArgs& a, const uint16_t* q, const float* w,
                         hipStream_t st) {
@@ -267,13 +284,18 @@ hipError_t launch_score(const Geometry& g, const StepArgs& a, const uint16_t* q,
   ka.subs_per_wave = spw;
   const int64_t blocks = (subs + (int64_t)nw * spw - 1) / ((int64_t)nw * spw);
   const int MT = (M + 31) / 32;
-  const size_t lds = (size_t)MT * 32 * kQStride * sizeof(uint16_t) + (size_t)MT * 32 * sizeof(float) +
+  const int G = MT >= 4 ? 4 : MT >= 2 ? 2 : 1;         // row tiles per group (Q padded to whole groups)
+  const int MTP = (MT + G - 1) / G * G;
+  const size_t lds = (size_t)MTP * 32 * kQStride * sizeof(uint16_t) + (size_t)MTP * 32 * sizeof(float) +
                      (size_t)a.R * (kRadixBins / 2) * sizeof(uint32_t);
   dim3 grid((unsigned)blocks, (unsigned)a.n_seqs), block(nw * 64);
-#define DSA_SCORE_CASE(HI)                                                                   \
-  case HI:                                                                                 \
-    return wide ? launch_k(score_kernel<HI, 8>, grid, block, lds, st, ka)                  \
-                : launch_k(score_kernel<HI, 4>, grid, block, lds, st, ka);
+#define DSA_SCORE_G(HI, NW)                                                                  \
+  (G == 4 ? launch_k(score_kernel<HI, NW, 4>, grid, block, lds, st, ka)                    \
+          : G == 2 ? launch_k(score_kernel<HI, NW, 2>, grid, block, lds, st, ka)           \
+                   : launch_k(score_kernel<HI, NW, 1>, grid, block, lds, st, ka))
+#define DSA_SCORE_CASE(HI) \
+  case HI:                 \
+    return wide ? DSA_SCORE_G(HI, 8) : DSA_SCORE_G(HI, 4);
   switch (g.index_heads) {
     DSA_SCORE_CASE(4)
     DSA_SCORE_CASE(8)
@@ -282,6 +304,7 @@ hipError_t launch_score(const Geometry& g, const StepArgs& a, const uint16_t* q,
     default: return hipErrorInvalidValue;
   }
 #undef DSA_SCORE_CASE
+#undef DSA_SCORE_G
 }
 
 }  // namespace dsa

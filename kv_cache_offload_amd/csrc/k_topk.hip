@@ -24,10 +24,11 @@
 //     lowest-position keys equal to tau.  If the candidates do not fit in LDS
 //     (nearly all scores equal), the same passes read the candidate lists from
 //     global memory.
-// Each selected position is marked in the step's union bitmap and classified
-// against the hot cache, and the last row of each sequence to finish runs the
-// gather plan (gather_plan.h).  All per-position work is spread over the
-// chunks; only the candidates, a few thousand per row, reach the final step.
+// Each selected position is marked in the step's union bitmap, and the last
+// row of each sequence to finish runs the counts phase of the gather plan
+// (gather_plan.h; its walk runs in the attention launch).  All per-position
+// work is spread over the chunks; only the candidates, a few thousand per row,
+// reach the final step.
 //
 // Memory-level parallelism: gathers whose addresses are known are issued
 // together, unconditionally (indices clamped into the buffer), and pinned with
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_chunk_kernel(TopkKArgs ka) {
 }
 
 // One workgroup per (row, sequence): resolves the row from its candidate lists;
-// the last row of a sequence to finish then runs the gather plan.
+// the last row of a sequence to finish then runs the counts phase of the plan.
 __global__ __launch_bounds__(kSelThreads) void topk_final_kernel(TopkKArgs ka) {
   extern __shared__ __align__(16) uint32_t lds[];   // keys[kCandCap], positions[kCandCap]
   __shared__ SelectLds sm;
@@ -439,7 +440,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_final_kernel(TopkKArgs ka) {
     const uint32_t cnt = tid < n_chunks ? cnt_all : 0u;  // lists of this step's chunks only
     resolve_row(ka, s, r, n_vis, dig.x, dig.y, (uint32_t)dig.z, cnt, h1c, sm, lds);
   }
-  plan_if_last(u, s, ka.plan, (uint32_t)a.R, ps, lds);
+  plan_if_last<false>(u, s, ka.plan, (uint32_t)a.R, ps, lds);   // the walk runs in the attention launch
 }
 
 TopkKArgs topk_args(const Geometry& g, const StepArgs& a) {

@@ -261,7 +261,7 @@ ScrOff scratch_layout(const Geometry& g) {
   o.po = take((size_t)g.r_max * g.nsplit_max * g.heads * g.latent * 2);
   o.pml = take((size_t)g.r_max * g.nsplit_max * g.heads * 4 * 4);
   o.cnt = take(16 * 8);
-  o.info = take(8 * 8);
+  o.info = take(kInfoWords * 8);
   o.selmask = take((size_t)P / 32 * 4);
   o.hitmask = take((size_t)P / 32 * 4);
   o.base_u = take((size_t)P / 32 * 4);
@@ -512,7 +512,7 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   std::vector<PfOff> pf(off ? cfg->n_seqs : 0);
   for (auto& x : pf) {
     x.cnt = take(16 * 8);
-    x.info = take(8 * 8);
+    x.info = take(kInfoWords * 8);
     x.uni = take((size_t)RK * 4);
     x.kind = take((size_t)RK * 4);
     x.src = take((size_t)RK * 4);
@@ -846,7 +846,7 @@ dsa_status decode_common(dsa_session* s, int32_t layer, int32_t R, const void* i
     HIPCHK(hipEventRecord(s->sel_ready, stream), "hipEventRecord");
     s->sel_epoch += 1;
   }
-  if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream, true); })) != DSA_OK) return st;
   if ((st = timed_launch(s, KK_MERGE, "attention merge and assign", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK)
     return st;
   s->last_layer = layer;
@@ -894,7 +894,7 @@ dsa_status dsa_decode_step_reuse(dsa_session* s, int32_t layer, int32_t src_laye
   }
   if ((st = timed_launch(s, KK_TOPK_SELECT, "reuse mark", [&] { return launch_reuse_mark(g, a, s->scr[0], s->s_stride, stream); })) != DSA_OK)
     return st;
-  if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream, false); })) != DSA_OK) return st;
   if ((st = timed_launch(s, KK_MERGE, "attention merge and assign", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK)
     return st;
   s->last_layer = layer;
