@@ -374,7 +374,7 @@ __device__ inline void plan_walk_block(const UnitG& u, const ScratchG& s, const 
 
 // Called by every workgroup (one per query row) of a sequence at the end of its
 // selection; the last of the n_rows workgroups to arrive runs the counts phase
-// of the plan (kFull: then the walk too).  What the plan reads from the other
+// of the plan (full: then the walk too, with all kPlanThreads threads).  What the plan reads from the other
 // workgroups is only their marks in the selection bitmap, and every mark is a
 // device-scope atomic OR: such an atomic is performed where all XCDs see it
 // once it has completed.  So before the arrival every wave waits until its own
@@ -386,9 +386,8 @@ __device__ inline void plan_walk_block(const UnitG& u, const ScratchG& s, const 
 // bitmap.  Nothing needs releasing -- the selections themselves are read by
 // later kernels -- so no L2 is written back here.  No workgroup waits for
 // another.
-template <bool kFull>
 __device__ inline void plan_if_last(const UnitG& u, const ScratchG& s, const PlanParams& pp, uint32_t n_rows,
-                                    const PlanState& ps, uint32_t* lds) {
+                                    const PlanState& ps, uint32_t* lds, bool full) {
   __shared__ uint32_t s_last;
   __builtin_amdgcn_s_waitcnt(0);                       // this wave's marks (and every other access) completed
   __syncthreads();
@@ -404,7 +403,7 @@ __device__ inline void plan_if_last(const UnitG& u, const ScratchG& s, const Pla
   __syncthreads();
   if (!s_last) return;
   const PlanCounts pc = plan_counts_block(u, s, pp, ps);
-  if constexpr (kFull) {
+  if (full) {                                          // (uniform)
     __syncthreads();
     plan_walk_block<kPlanThreads>(u, s, pp, ps, pc, lds);
   }

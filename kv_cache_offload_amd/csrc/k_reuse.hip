@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kPlanThreads) void reuse_mark_kernel(MarkKArgs ka) 
     if (pos >= 0 && pos < ps.L) g_or(&s.selmask[pos >> 5], 1u << (pos & 31));
     else raise_err(a.err, kErrSelection);
   }
-  plan_if_last<true>(u, s, ka.plan, (uint32_t)a.R, ps, lds);
+  plan_if_last(u, s, ka.plan, (uint32_t)a.R, ps, lds, true);
 }
 
 struct FillKArgs {

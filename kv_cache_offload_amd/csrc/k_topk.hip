@@ -440,7 +440,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_final_kernel(TopkKArgs ka) {
     const uint32_t cnt = tid < n_chunks ? cnt_all : 0u;  // lists of this step's chunks only
     resolve_row(ka, s, r, n_vis, dig.x, dig.y, (uint32_t)dig.z, cnt, h1c, sm, lds);
   }
-  plan_if_last<false>(u, s, ka.plan, (uint32_t)a.R, ps, lds);   // the walk runs in the attention launch
+  // The ring walk runs in the attention launch, beside attention; CLOCK's walk,
+  // whose first lap can sweep the whole ring, keeps all 1,024 threads here.
+  plan_if_last(u, s, ka.plan, (uint32_t)a.R, ps, lds, ka.plan.clock != 0);
 }
 
 TopkKArgs topk_args(const Geometry& g, const StepArgs& a) {

@@ -846,7 +846,7 @@ dsa_status decode_common(dsa_session* s, int32_t layer, int32_t R, const void* i
     HIPCHK(hipEventRecord(s->sel_ready, stream), "hipEventRecord");
     s->sel_epoch += 1;
   }
-  if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream, true); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream, !g.clock); })) != DSA_OK) return st;
   if ((st = timed_launch(s, KK_MERGE, "attention merge and assign", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK)
     return st;
   s->last_layer = layer;
