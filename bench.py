@@ -103,6 +103,9 @@ def pmc_summary(workload, fetch_csv, write_csv):
     import re
 
     def per_kernel(path, counter):
+        # bytes per launch of a group: per kernel, the median dispatch times its dispatches per group
+        # launch (the fewest dispatches of any one of the group's kernels: the Top-K collect group runs
+        # its digits kernel twice per launch); the median keeps the history load's bulk appends out
         vals, calib = {}, []
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
@@ -112,11 +115,16 @@ def pmc_summary(workload, fetch_csv, write_csv):
                 calib.append(v)
                 continue
             for kind, names in KERNEL_NAMES.items():
-                if any(re.search(r"\b" + n + r"\b", name) for n in names):
-                    vals.setdefault(kind, []).append(v)
+                for n in names:
+                    if re.search(r"\b" + n + r"\b", name):
+                        vals.setdefault(kind, {}).setdefault(n, []).append(v)
         assert calib, f"no calibration copy in {path}"
         factor = (2 << 30) / (sum(calib) / len(calib))
-        return {k: factor * sum(v) / len(v) for k, v in vals.items()}, factor
+        out = {}
+        for k, by_name in vals.items():
+            launches = min(len(v) for v in by_name.values())
+            out[k] = factor * sum(sorted(v)[len(v) // 2] * len(v) / launches for v in by_name.values())
+        return out, factor
 
     f, ff = per_kernel(fetch_csv, "FETCH_SIZE")
     w, wf = per_kernel(write_csv, "WRITE_SIZE")

@@ -324,7 +324,10 @@ dsa_status dsa_decode_step_reuse(dsa_session* s, int32_t layer, int32_t src_laye
  * on another stream; the next dsa_decode_step waits for every prefetch still
  * pending on another stream, since it replaces the selection they read.
  * Between the prefetch and the layer's reuse step the caller enqueues no other
- * work of `layer`.  Resident mode: nothing to do (DSA_OK). */
+ * work of `layer`.  Resident mode: nothing to do (DSA_OK).
+ * On MI355X each of the two cross-stream waits costs more than the host-link
+ * time the prefetch saves a reusing layer, so the default is no prefetch:
+ * dsa_decode_step_reuse reads the misses itself. */
 dsa_status dsa_prefetch_reuse(dsa_session* s, int32_t layer, int32_t src_layer, int32_t rows_per_seq,
                               hipStream_t stream);
 
