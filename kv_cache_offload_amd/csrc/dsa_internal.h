@@ -109,8 +109,12 @@ static_assert(sizeof(UnitDev) == sizeof(UnitG) && sizeof(SeqScratch) == sizeof(S
 // walk the writeback position and the number of misses that took a slot.
 enum {
   kInfoUnion = 0, kInfoWriteback = 1, kInfoAssigned = 2, kInfoRound = 3, kInfoM = 4, kInfoHand = 5,
-  kInfoMiss = 6, kInfoRing = 7, kInfoHit = 8, kInfoWords = 16
+  kInfoMiss = 6, kInfoRing = 7, kInfoHit = 8, kInfoNewHand = 9, kInfoWords = 16
 };
+
+// Attention counts the union itself (and its extra workgroup runs the whole
+// gather plan) when the history's selection words fit this many.
+constexpr int64_t kAttnScanWords = 4608;
 
 struct Geometry {
   int index_heads, index_dim, heads, latent, rope, group, top_k, hot_slots;
@@ -121,6 +125,7 @@ struct Geometry {
   int n_chunks;           // top-k chunks per row at max_positions
   int nsplit_max;         // attention splits per row at K with the smallest split (64 rows)
   float softmax_scale;
+  int n_cu;               // compute units of the device
 };
 
 // Every unit's arena buffers, and every sequence's scratch, repeat one layout
@@ -128,6 +133,15 @@ struct Geometry {
 // descriptors of sequence 0 by value in its arguments and forms those of
 // sequence q by moving each pointer q strides on: no descriptor table in device
 // memory, so no dependent load stands between a kernel's start and its buffers.
+struct StepArgs;
+// Where a decode step's gather plan runs: 0 in the attention launch (attention
+// counts the union itself), 1 counts at the end of the Top-K and the walk in
+// the attention launch, 2 all of it at the end of the Top-K (CLOCK).  0 needs
+// a history whose selection words fit kAttnScanWords and an attention grid that
+// leaves a CU free for the plan's workgroup (attention holds one workgroup per
+// CU: a workgroup waiting for a CU would wait for the whole plan).
+int topk_plan_mode(const Geometry& g, const StepArgs& a);
+
 struct StepArgs {
   UnitDev u0;             // unit (layer, sequence 0)
   SeqScratch s0;          // scratch of sequence 0 (the main set or the prefetch set)
@@ -226,10 +240,11 @@ hipError_t prepare_topk_kernels();
 // clear_hist: also zero the Top-K histograms for the next step (not in a
 // prefetch round, whose scratch set has none).
 hipError_t launch_gather(const Geometry& g, const StepArgs& a, hipStream_t st, bool clear_hist = true);
-// walk: an extra workgroup per sequence runs the walk of the gather plan (a
-// decode step, whose Top-K ran only the plan's counts phase).
+// plan: what of the gather plan the launch runs (an extra workgroup per
+// sequence): 0 nothing (the plan ran before), 1 the walk (the counts ran
+// before), 2 the whole plan, each attention workgroup counting the union itself.
 hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_lat,
-                       const uint16_t* q_rope, float* out, hipStream_t st, bool walk);
+                       const uint16_t* q_rope, float* out, hipStream_t st, int plan);
 // The split merge (skipped when one split covers the selection) and, in the
 // same launch, the gather's assign pass, which also copies each filled miss's
 // row from the compact rows into its slot.

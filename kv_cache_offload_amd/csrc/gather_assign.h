@@ -42,6 +42,14 @@ __device__ inline void assign_block(const GatherKArgs& ka, int block, int seq) {
   const StepArgs& a = ka.a;
   const UnitG u = unit_of(a, seq);
   const ScratchG s = scratch_of(a, seq);
+  if (block == 0 && threadIdx.x == 0) {               // the round-end state the plan's walk computed
+    const int64_t wb = s.info[kInfoWriteback];
+    if (ka.mode == 0) {
+      *u.hand = (int32_t)s.info[kInfoNewHand];
+      if (wb >= 0) u.dyn[1] = wb + ka.ring_rows;
+    }
+    u.dyn[2] = s.info[kInfoRound] + 1;
+  }
   if ((int)block >= ka.word_blocks && (int)block < ka.word_blocks + ka.clear_blocks) {
     // the Top-K histograms of this step's rows, consumed: zero for the next step
     const int64_t t = (int64_t)(block - ka.word_blocks) * kGatherThreads + threadIdx.x;

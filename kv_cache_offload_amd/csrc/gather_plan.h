@@ -60,19 +60,21 @@ struct PlanCounts {
   uint32_t U, n_miss, n_ring, n_hit;
 };
 
-// Counts phase, by one kPlanThreads workgroup: the hit words, the per-word
-// prefix counts of union entries and of misses, and the totals.  Also zeroes
-// the step's host-read counter (the round's readers add to it).
+// Counts phase, by one T-thread workgroup: the hit words, the per-word prefix
+// counts of union entries and of misses, and the totals, published with the
+// round-start state in the step's info for the rest of the round.
+template <int T>
 __device__ inline PlanCounts plan_counts_block(const UnitG& u, const ScratchG& s, const PlanParams& pp,
                                                const PlanState& ps) {
-  __shared__ uint32_t sh[4 * kPlanWaves];
+  constexpr int kWaves = T / 64;
+  __shared__ uint32_t sh[4 * kWaves];
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t L = ps.L, M = ps.M;
   const int32_t round = ps.round;
   const bool off = pp.mode == 0;
   const int64_t nw = (L + 31) / 32;
   const auto sel = s.selmask;
-  const int64_t per = (nw + kPlanThreads - 1) / kPlanThreads;
+  const int64_t per = (nw + T - 1) / T;
   const int64_t w0 = min(nw, (int64_t)tid * per), w1 = min(nw, w0 + per);
   const bool words_in_regs = per <= kPlanRegWords;
 
@@ -107,7 +109,7 @@ __device__ inline PlanCounts plan_counts_block(const UnitG& u, const ScratchG& s
   // Longer histories: wave v owns the words [v seg, (v+1) seg), 64 consecutive
   // words per load instruction (coalesced), kPlanChunk rows of loads in flight.
   const int wave = tid >> 6;
-  const int64_t seg = ((nw + kPlanWaves * 64 - 1) / (kPlanWaves * 64)) * 64;
+  const int64_t seg = ((nw + kWaves * 64 - 1) / (kWaves * 64)) * 64;
   const int64_t sw0 = min(nw, (int64_t)wave * seg), sw1 = min(nw, sw0 + seg);
   auto wave_rows = [&](auto&& fn) {                    // fn(w, sel word, hit word, valid) per row, all lanes
     for (int64_t r0 = sw0; r0 < sw1; r0 += 64 * kPlanChunk) {
@@ -139,7 +141,7 @@ __device__ inline PlanCounts plan_counts_block(const UnitG& u, const ScratchG& s
   uint4 tot;
   uint4 base;
   if (words_in_regs) {
-    base = block_scan4<kPlanWaves>(c, &tot, sh);
+    base = block_scan4<kWaves>(c, &tot, sh);
   } else {
     // each wave's counts, then the waves' scan (a wave's words are contiguous)
 #pragma unroll
@@ -159,7 +161,7 @@ __device__ inline PlanCounts plan_counts_block(const UnitG& u, const ScratchG& s
     base = make_uint4(0u, 0u, 0u, 0u);
     tot = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int v = 0; v < kPlanWaves; ++v) {
+    for (int v = 0; v < kWaves; ++v) {
       const uint4 x = make_uint4(sh[4 * v], sh[4 * v + 1], sh[4 * v + 2], sh[4 * v + 3]);
       if (v < wave) { base.x += x.x; base.y += x.y; }
       tot.x += x.x; tot.y += x.y; tot.z += x.z; tot.w += x.w;
@@ -207,8 +209,6 @@ __device__ inline PlanCounts plan_counts_block(const UnitG& u, const ScratchG& s
     s.info[kInfoRound] = round;
     s.info[kInfoM] = M;
     s.info[kInfoHand] = off ? ps.hand : 0;
-  } else if (tid == 8) {
-    s.counters[8] = 0;                                 // host reads: the round's readers add them
   }
   return PlanCounts{U, n_miss, n_ring, n_hit};
 }
@@ -227,7 +227,6 @@ __device__ inline void plan_walk_block(const UnitG& u, const ScratchG& s, const 
   __shared__ uint32_t s_evict;
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t L = ps.L, M = ps.M;
-  const int32_t round = ps.round;
   const bool off = pp.mode == 0;
   const int hand = off ? ps.hand : 0;
   const int S = pp.S;
@@ -359,22 +358,24 @@ __device__ inline void plan_walk_block(const UnitG& u, const ScratchG& s, const 
     s.counters[tid] = cn;
     u.totals[tid] = total_prev + cn;
   }
+  // The round-end state (new hand, M after a due writeback, round + 1) goes to
+  // the unit with the assign pass: attention, which may run beside this walk,
+  // reads the round-start state.
   if (tid == 0) {
     int64_t wb = -1;
     if (off && L - M >= pp.ring_rows) wb = M;
     s.info[kInfoWriteback] = wb;
     s.info[kInfoAssigned] = n_assigned;
-    if (off) {
-      *u.hand = new_hand;
-      if (wb >= 0) u.dyn[1] = M + pp.ring_rows;
-    }
-    u.dyn[2] = round + 1;
+    s.info[kInfoNewHand] = off ? new_hand : 0;
   }
 }
 
 // Called by every workgroup (one per query row) of a sequence at the end of its
 // selection; the last of the n_rows workgroups to arrive runs the counts phase
-// of the plan (full: then the walk too, with all kPlanThreads threads).  What the plan reads from the other
+// of the plan (full: then the walk too, with all kPlanThreads threads).  Used
+// where attention needs the counts before it starts (histories too long for
+// attention to count the union itself) or the walk runs here (CLOCK, whose
+// first lap can sweep the whole ring; prefetch and reuse rounds).  What the plan reads from the other
 // workgroups is only their marks in the selection bitmap, and every mark is a
 // device-scope atomic OR: such an atomic is performed where all XCDs see it
 // once it has completed.  So before the arrival every wave waits until its own
@@ -402,7 +403,7 @@ __device__ inline void plan_if_last(const UnitG& u, const ScratchG& s, const Pla
   }
   __syncthreads();
   if (!s_last) return;
-  const PlanCounts pc = plan_counts_block(u, s, pp, ps);
+  const PlanCounts pc = plan_counts_block<kPlanThreads>(u, s, pp, ps);
   if (full) {                                          // (uniform)
     __syncthreads();
     plan_walk_block<kPlanThreads>(u, s, pp, ps, pc, lds);
@@ -416,6 +417,17 @@ __device__ inline void plan_walk_from_info(const UnitG& u, const ScratchG& s, co
   const PlanState ps{u.dyn[0], s.info[kInfoM], (int32_t)s.info[kInfoRound], (int32_t)s.info[kInfoHand]};
   const PlanCounts pc{(uint32_t)s.info[kInfoUnion], (uint32_t)s.info[kInfoMiss], (uint32_t)s.info[kInfoRing],
                       (uint32_t)s.info[kInfoHit]};
+  plan_walk_block<T>(u, s, pp, ps, pc, lds);
+}
+
+// The whole plan of a decode step, by one T-thread workgroup of the attention
+// launch, from the unit's round-start state (nothing updates it before the
+// assign pass).
+template <int T>
+__device__ inline void plan_counts_and_walk(const UnitG& u, const ScratchG& s, const PlanParams& pp, uint32_t* lds) {
+  const PlanState ps{u.dyn[0], u.dyn[1], (int32_t)u.dyn[2], pp.mode == 0 ? *u.hand : 0};
+  const PlanCounts pc = plan_counts_block<T>(u, s, pp, ps);
+  __syncthreads();
   plan_walk_block<T>(u, s, pp, ps, pc, lds);
 }
 

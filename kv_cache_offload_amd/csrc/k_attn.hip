@@ -66,8 +66,10 @@ struct AttnKArgs {
   int off;                   // offload mode (hot slots, ring, host mirror)
   int64_t max_positions;
   float scale_log2;          // softmax_scale * log2(e)
-  int walk;                  // the extra workgroup of each sequence runs the plan's walk
-  PlanParams plan;
+  int plan;                  // the extra workgroup of each sequence: 0 nothing (the plan ran before),
+                             // 1 the plan's walk (its counts ran before), 2 the whole plan, and every
+                             // workgroup counts the union words before its rows itself
+  PlanParams pp;
 };
 
 // Two fp32 -> packed fp16 (round to nearest even), as one 32-bit word.
@@ -131,13 +133,15 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   __shared__ __align__(16) float scl_s[2][8 * kBlk];
   __shared__ const DSA_GLOBAL uint8_t* s_from[kSplit];   // where each row is read from (null: masked)
   __shared__ int s_ux[kSplit];                            // its compact row, -1 if masked
+  __shared__ uint32_t s_scan[NW];
 
   const StepArgs& a = ka.a;
   const int split = blockIdx.x, r = blockIdx.y, seq = blockIdx.z;
   const UnitG u = unit_of(a, seq);
   const ScratchG s = scratch_of(a, seq);
-  if (split == ka.nsplit) {                              // (uniform) past the splits: the walk of the sequence
-    if (ka.walk && r == 0) plan_walk_from_info<NT>(u, s, ka.plan, reinterpret_cast<uint32_t*>(lat_s[0]));
+  if (split == ka.nsplit) {                              // (uniform) past the splits: the sequence's plan
+    if (r == 0 && ka.plan == 1) plan_walk_from_info<NT>(u, s, ka.pp, reinterpret_cast<uint32_t*>(lat_s[0]));
+    if (r == 0 && ka.plan == 2) plan_counts_and_walk<NT>(u, s, ka.pp, reinterpret_cast<uint32_t*>(lat_s[0]));
     return;
   }
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -158,15 +162,56 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   // slot is read with the words (for every selected position: a non-hit
   // ignores it), so only the row's address is on the path to its data.
   const int n_sel = s.sel_n[r];
+  // Whole plan here (ka.plan == 2): this workgroup counts the union entries
+  // before each selection word itself (the plan's workgroup runs beside it), from
+  // the round's bitmap -- every word's count read at once, then an exclusive
+  // scan in LDS (the second staging buffer, free until block 1).  A selected
+  // position is a hit iff it was cached at round start.
+  const bool own_counts = ka.plan == 2;
+  const uint32_t* pref = reinterpret_cast<const uint32_t*>(lat_s[1]);
+  const int64_t L = u.dyn[0];
+  if (own_counts) {
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(lat_s[1]);
+    const int64_t nw = (L + 31) / 32;                    // within kAttnScanWords (the host's choice)
+    constexpr int kLoads = (int)((kAttnScanWords / 4 + NT - 1) / NT);
+    static_assert(kAttnScanWords * 4 <= (int64_t)sizeof(lat_s[1]), "the word counts fit a staging buffer");
+    u32x4 wv[kLoads];
+#pragma unroll
+    for (int e = 0; e < kLoads; ++e) {
+      const int64_t q = tid + (int64_t)e * NT;          // 4-word piece
+      wv[e] = 4 * q < nw ? reinterpret_cast<const DSA_GLOBAL u32x4*>(s.selmask)[q] : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int e = 0; e < kLoads; ++e) {
+      const int64_t q = tid + (int64_t)e * NT;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * q + i < nw) cnt[4 * q + i] = __popc(wv[e][i]);
+    }
+    __syncthreads();
+    const int64_t per = (nw + NT - 1) / NT;
+    const int64_t c0 = min(nw, (int64_t)tid * per), c1 = min(nw, c0 + per);
+    uint32_t sum = 0;
+    for (int64_t w = c0; w < c1; ++w) sum += cnt[w];
+    uint32_t tot;
+    uint32_t run = block_scan<NW>(sum, &tot, s_scan);
+    for (int64_t w = c0; w < c1; ++w) {
+      const uint32_t x = cnt[w];
+      cnt[w] = run;
+      run += x;
+    }
+    __syncthreads();
+  }
   bool host = false;                                     // this row is read from the host mirror
   if (tid < kSplit) {
-    const int64_t M = s.info[kInfoM];
+    const int64_t M = own_counts ? u.dyn[1] : s.info[kInfoM];
     const int j = j_begin + tid;
     const int32_t pos = j < ka.K ? s.sel[(int64_t)r * ka.K + j] : -1;
-    const bool ok = j < n_sel && pos >= 0 && pos < ka.max_positions;
+    const bool ok = j < n_sel && pos >= 0 && pos < ka.max_positions && (!own_counts || pos < L);
     const int64_t w = ok ? pos >> 5 : 0;
-    const uint32_t sw = s.selmask[w], hw = ka.off ? s.hitmask[w] : 0u;
-    const uint32_t bu = s.base_u[w];
+    const uint32_t sw = s.selmask[w];
+    const uint32_t hw = !ka.off ? 0u : own_counts ? (u.hot[w] & sw) : s.hitmask[w];
+    const uint32_t bu = own_counts ? pref[w] : s.base_u[w];
     const i32x2 ps = ka.off ? u.pos_slot[ok ? pos : 0] : (i32x2){-1, -1};
     const uint32_t bit = 1u << (pos & 31), below = bit - 1u;
     const uint32_t ux = bu + __popc(sw & below);
@@ -579,14 +624,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
 inline int split_rows(const Geometry&) { return kSplit; }
 
 hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_lat, const uint16_t* q_rope,
-                       float* out, hipStream_t st, bool walk) {
+                       float* out, hipStream_t st, int plan) {
   const int rows = split_rows(g);
   const int nsplit = (g.top_k + rows - 1) / rows;
   AttnKArgs ka{a, q_lat, q_rope, out, g.top_k, g.heads, nsplit, g.nsplit_max, g.row_bytes,
                g.hot_slots, g.ring_cap, g.r_max * g.top_k, g.mode == 0 ? 1 : 0, g.max_positions,
-               g.softmax_scale * 1.4426950408889634f, walk ? 1 : 0,
+               g.softmax_scale * 1.4426950408889634f, plan,
                PlanParams{g.hot_slots, g.s_words, g.ring_rows, g.mode, g.clock ? 1 : 0}};
-  // one workgroup past the splits of each (row, sequence): row 0's runs the walk
+  // one workgroup past the splits of each (row, sequence): row 0's runs the plan's part
   dim3 grid((unsigned)nsplit + 1u, (unsigned)a.R, (unsigned)a.n_seqs);
   switch (g.heads) {
     case 16: return launch_k(attn_kernel<1, 2>, grid, dim3(64), 0, st, ka);

@@ -43,6 +43,7 @@ __global__ __launch_bounds__(kPlanThreads) void reuse_mark_kernel(MarkKArgs ka) 
   const PlanState ps{u.dyn[0], u.dyn[1], (int32_t)u.dyn[2], ka.mode == 0 ? *u.hand : 0};
   const int n = src.sel_n[r];
   const auto sel = src.sel + (int64_t)r * ka.K;
+  if (r == 0 && threadIdx.x == 0) s.counters[8] = 0;  // host reads: the round's readers add them
   for (int j = threadIdx.x; j < n; j += kPlanThreads) {
     const int32_t pos = sel[j];
     if (pos >= 0 && pos < ps.L) g_or(&s.selmask[pos >> 5], 1u << (pos & 31));

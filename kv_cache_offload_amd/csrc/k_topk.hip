@@ -69,6 +69,8 @@ struct TopkKArgs {
   int mode;
   int r_max;
   int long_mode;       // 0: candidates by the first digit; 1: by the first two (refine pass first)
+  int plan_mode;       // the gather plan here: 0 none (attention counts the union itself and its extra
+                       // workgroup runs the whole plan), 1 the counts phase, 2 counts and walk (CLOCK)
   PlanParams plan;
 };
 
@@ -433,6 +435,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_final_kernel(TopkKArgs ka) {
   load_bins<kSelWaves, kRadixBins, 1>(s.hist1 + (int64_t)r * kRadixBins, h1c);
   const int64_t n_vis = ps.L - a.R + r + 1;
   const int K = ka.K;
+  if (r == 0 && tid == 0) s.counters[8] = 0;          // host reads: the round's attention adds them
   if (n_vis <= K) {
     select_all_visible(s, r, K, n_vis, sm.sel);
   } else {
@@ -440,17 +443,25 @@ __global__ __launch_bounds__(kSelThreads) void topk_final_kernel(TopkKArgs ka) {
     const uint32_t cnt = tid < n_chunks ? cnt_all : 0u;  // lists of this step's chunks only
     resolve_row(ka, s, r, n_vis, dig.x, dig.y, (uint32_t)dig.z, cnt, h1c, sm, lds);
   }
-  // The ring walk runs in the attention launch, beside attention; CLOCK's walk,
-  // whose first lap can sweep the whole ring, keeps all 1,024 threads here.
-  plan_if_last(u, s, ka.plan, (uint32_t)a.R, ps, lds, ka.plan.clock != 0);
+  // The ring policy's plan runs in the attention launch, beside attention (the
+  // counts too, where attention can count the union itself); CLOCK's walk, whose
+  // first lap can sweep the whole ring, keeps all 1,024 threads here.
+  if (ka.plan_mode > 0) plan_if_last(u, s, ka.plan, (uint32_t)a.R, ps, lds, ka.plan_mode == 2);
 }
 
 TopkKArgs topk_args(const Geometry& g, const StepArgs& a) {
   return TopkKArgs{a, g.p_pad, g.n_chunks, g.top_k, g.mode, g.r_max, a.l_max > kShortMax ? 1 : 0,
+                   topk_plan_mode(g, a),
                    PlanParams{g.hot_slots, g.s_words, g.ring_rows, g.mode, g.clock ? 1 : 0}};
 }
 
 }  // namespace
+
+int topk_plan_mode(const Geometry& g, const StepArgs& a) {
+  if (g.clock) return 2;
+  const int64_t attn_wgs = (int64_t)a.n_seqs * (a.R * (int64_t)((g.top_k + 63) / 64) + 1);
+  return (a.l_max + 31) / 32 <= kAttnScanWords && attn_wgs <= g.n_cu ? 0 : 1;
+}
 
 hipError_t prepare_topk_kernels() {
   return hipFuncSetAttribute((const void*)topk_final_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -479,6 +479,9 @@ dsa_status dsa_session_create(const dsa_config* cfg, dsa_session** out) {
   g.s_words = (g.hot_slots + 31) / 32;
   g.nsplit_max = (cfg->top_k + 63) / 64;
   g.softmax_scale = cfg->softmax_scale;
+  g.n_cu = 0;
+  if (hipDeviceGetAttribute(&g.n_cu, hipDeviceAttributeMultiprocessorCount, s->device) != hipSuccess || g.n_cu < 1)
+    g.n_cu = 1;                                        // (then the plan never runs beside attention alone)
 
   const int n_units = cfg->n_layers * cfg->n_seqs;
   const int64_t P = g.p_pad, S = g.hot_slots, RK = (int64_t)g.r_max * g.top_k, rb = g.row_bytes;
@@ -846,7 +849,7 @@ dsa_status decode_common(dsa_session* s, int32_t layer, int32_t R, const void* i
     HIPCHK(hipEventRecord(s->sel_ready, stream), "hipEventRecord");
     s->sel_epoch += 1;
   }
-  if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream, !g.clock); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream, 2 - topk_plan_mode(g, a)); })) != DSA_OK) return st;
   if ((st = timed_launch(s, KK_MERGE, "attention merge and assign", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK)
     return st;
   s->last_layer = layer;
@@ -894,7 +897,7 @@ dsa_status dsa_decode_step_reuse(dsa_session* s, int32_t layer, int32_t src_laye
   }
   if ((st = timed_launch(s, KK_TOPK_SELECT, "reuse mark", [&] { return launch_reuse_mark(g, a, s->scr[0], s->s_stride, stream); })) != DSA_OK)
     return st;
-  if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream, false); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream, 0); })) != DSA_OK) return st;
   if ((st = timed_launch(s, KK_MERGE, "attention merge and assign", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK)
     return st;
   s->last_layer = layer;
