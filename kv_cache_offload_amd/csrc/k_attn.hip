@@ -163,18 +163,19 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   // ignores it), so only the row's address is on the path to its data.
   const int n_sel = s.sel_n[r];
   // Whole plan here (ka.plan == 2): this workgroup counts the union entries
-  // before each selection word itself (the plan's workgroup runs beside it), from
-  // the round's bitmap -- every word's count read at once, then an exclusive
-  // scan in LDS (the second staging buffer, free until block 1).  A selected
-  // position is a hit iff it was cached at round start.
+  // before each selection word itself (the plan's workgroup runs beside it),
+  // from the round's bitmap: every word requested at once with the selection,
+  // counted into LDS (the second staging buffer, free until block 1), and
+  // scanned once the rows are requested -- only the compact row and the map
+  // entry need the union index, not the row's source.  A selected position is
+  // a hit iff it was cached at round start.
   const bool own_counts = ka.plan == 2;
-  const uint32_t* pref = reinterpret_cast<const uint32_t*>(lat_s[1]);
   const int64_t L = u.dyn[0];
+  const int64_t nw = own_counts ? (L + 31) / 32 : 0;     // within kAttnScanWords (the host's choice)
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(lat_s[1]);
+  static_assert(kAttnScanWords * 4 <= (int64_t)sizeof(lat_s[1]), "the word counts fit a staging buffer");
   if (own_counts) {
-    uint32_t* cnt = reinterpret_cast<uint32_t*>(lat_s[1]);
-    const int64_t nw = (L + 31) / 32;                    // within kAttnScanWords (the host's choice)
     constexpr int kLoads = (int)((kAttnScanWords / 4 + NT - 1) / NT);
-    static_assert(kAttnScanWords * 4 <= (int64_t)sizeof(lat_s[1]), "the word counts fit a staging buffer");
     u32x4 wv[kLoads];
 #pragma unroll
     for (int e = 0; e < kLoads; ++e) {
@@ -188,21 +189,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
       for (int i = 0; i < 4; ++i)
         if (4 * q + i < nw) cnt[4 * q + i] = __popc(wv[e][i]);
     }
-    __syncthreads();
-    const int64_t per = (nw + NT - 1) / NT;
-    const int64_t c0 = min(nw, (int64_t)tid * per), c1 = min(nw, c0 + per);
-    uint32_t sum = 0;
-    for (int64_t w = c0; w < c1; ++w) sum += cnt[w];
-    uint32_t tot;
-    uint32_t run = block_scan<NW>(sum, &tot, s_scan);
-    for (int64_t w = c0; w < c1; ++w) {
-      const uint32_t x = cnt[w];
-      cnt[w] = run;
-      run += x;
-    }
-    __syncthreads();
   }
   bool host = false;                                     // this row is read from the host mirror
+  bool live = false;                                     // this row's source is known (own counts: ux pending)
+  uint32_t t_sw = 0, t_below = 0;                        // its selection word and the bits below it
+  int64_t t_w = 0;
   if (tid < kSplit) {
     const int64_t M = own_counts ? u.dyn[1] : s.info[kInfoM];
     const int j = j_begin + tid;
@@ -211,7 +202,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     const int64_t w = ok ? pos >> 5 : 0;
     const uint32_t sw = s.selmask[w];
     const uint32_t hw = !ka.off ? 0u : own_counts ? (u.hot[w] & sw) : s.hitmask[w];
-    const uint32_t bu = own_counts ? pref[w] : s.base_u[w];
+    const uint32_t bu = own_counts ? 0u : s.base_u[w];
     const i32x2 ps = ka.off ? u.pos_slot[ok ? pos : 0] : (i32x2){-1, -1};
     const uint32_t bit = 1u << (pos & 31), below = bit - 1u;
     const uint32_t ux = bu + __popc(sw & below);
@@ -219,7 +210,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     // A selected index whose position, bitmap bit, union index or hit slot is
     // not what the plan allows is skipped (its row masked) and raises the
     // session's error flag: such a plan is inconsistent.
-    if (ok && (sw & bit) && ux < (uint32_t)ka.max_union) {
+    if (ok && (sw & bit) && (own_counts || ux < (uint32_t)ka.max_union)) {
       if (!ka.off) {
         from = u.rows + (int64_t)pos * rb;
       } else {
@@ -239,8 +230,16 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
       raise_err(a.err, kErrSelection);
     }
     s_from[tid] = from;
-    s_ux[tid] = from ? (int)ux : -1;
-    if (j < ka.K) s.map[(int64_t)r * ka.K + j] = from ? (int)ux : -1;
+    live = from != nullptr;
+    t_sw = sw;
+    t_below = below;
+    t_w = w;
+    if (!own_counts) {
+      s_ux[tid] = from ? (int)ux : -1;
+      if (j < ka.K) s.map[(int64_t)r * ka.K + j] = from ? (int)ux : -1;
+    } else if (!from && j < ka.K) {
+      s.map[(int64_t)r * ka.K + j] = -1;
+    }
   }
   if (wave == 0) {                                       // the split's host-mirror reads (one wave holds its rows)
     const uint64_t hb = __ballot(host);
@@ -263,7 +262,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) qa[16 + ks] = *reinterpret_cast<const bf16x8*>(qr + 32 * ks);
   }
-  __syncthreads();
+  __syncthreads();                                       // s_from (and the word counts) for every thread
 
   // Every 16-byte piece of a block is requested at once.  Block b + 1 is
   // requested as soon as block b has arrived, before block b is computed: the
@@ -283,6 +282,32 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     }
   };
   request(0);
+  if (own_counts) {                                      // (uniform) the union indices, while the rows arrive
+    const int64_t per = (nw + NT - 1) / NT;
+    const int64_t c0 = min(nw, (int64_t)tid * per), c1 = min(nw, c0 + per);
+    uint32_t sum = 0;
+    for (int64_t w = c0; w < c1; ++w) sum += cnt[w];
+    uint32_t tot;
+    uint32_t run = block_scan<NW>(sum, &tot, s_scan);
+    for (int64_t w = c0; w < c1; ++w) {
+      const uint32_t x = cnt[w];
+      cnt[w] = run;
+      run += x;
+    }
+    __syncthreads();
+    if (tid < kSplit) {
+      const int j = j_begin + tid;
+      int ux = -1;
+      if (live) {
+        const uint32_t x = cnt[t_w] + __popc(t_sw & t_below);
+        if (x < (uint32_t)ka.max_union) ux = (int)x;
+        else raise_err(a.err, kErrSelection);           // (the row's data is then masked)
+      }
+      s_ux[tid] = ux;
+      if (live && j < ka.K) s.map[(int64_t)r * ka.K + j] = ux;
+    }
+    __syncthreads();                                     // s_ux before block 0 is staged
+  }
 
   f32x4 o[32];
 #pragma unroll
