@@ -46,6 +46,10 @@ struct ScoreKArgs {
 
 __device__ inline float canon0(float s) { return s == 0.0f ? 0.0f : s; }
 
+// max(0, x) for a finite x as one integer max on its bits: a negative float
+// (-0 included) is a negative int32, and positive floats order as their bits.
+__device__ inline float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 __device__ inline uint32_t first_digit(float f) {
   const uint32_t u = __float_as_uint(f);
   return ((u & 0x80000000u) ? ~u : (u | 0x80000000u)) >> 21;
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 && HI >= 8 ? 3 : 1) void score_ker
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             int m = mt * 32 + i * 8 + hf * 4 + j;
-            p += sw[m] * fmaxf(acc4[i4][i * 4 + j], 0.0f);
+            p += sw[m] * relu(acc4[i4][i * 4 + j]);
           }
           part[i] = p;
         }
@@ -233,14 +237,22 @@ __global__ __launch_bounds__(NW * 64, NW == 4 && HI >= 8 ? 3 : 1) void score_ker
     }
   }
   __syncthreads();
-  for (int w = threadIdx.x; w < R * (kRadixBins / 2); w += blockDim.x) {
-    const uint32_t v = lh[w];
-    if (!v) continue;
-    const int r = w / (kRadixBins / 2), d = 2 * (w % (kRadixBins / 2));
-    const int rep = blockIdx.x % kHistReps;
-    const auto gh = s.hist0 + ((int64_t)rep * ka.r_max + r) * kRadixBins + d;
-    if (v & 0xFFFFu) g_add(gh, v & 0xFFFFu);
-    if (v >> 16) g_add(gh + 1, v >> 16);
+  // Four packed words per thread per round, all read before any is added.
+  const int rep = blockIdx.x % kHistReps;
+  const int n_words = R * (kRadixBins / 2);
+  for (int w0 = threadIdx.x; w0 < n_words; w0 += 4 * kThreads) {
+    uint32_t v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = w0 + k * kThreads < n_words ? lh[w0 + k * kThreads] : 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (!v[k]) continue;
+      const int w = w0 + k * kThreads;
+      const int r = w / (kRadixBins / 2), d = 2 * (w % (kRadixBins / 2));
+      const auto gh = s.hist0 + ((int64_t)rep * ka.r_max + r) * kRadixBins + d;
+      if (v[k] & 0xFFFFu) g_add(gh, v[k] & 0xFFFFu);
+      if (v[k] >> 16) g_add(gh + 1, v[k] >> 16);
+    }
   }
 }
 
