@@ -12,7 +12,7 @@
 // bf16 RoPE.
 //
 // gfx950 mapping.  A workgroup owns one query row and a split of 64 of its
-// selected rows, all heads: wave w holds heads 16w..16w+15.  The rows are staged in 32-row blocks through two
+// selected rows (every nsplit-th), all heads: wave w holds heads 16w..16w+15.  The rows are staged in 32-row blocks through two
 // LDS buffers, once for all waves: the int8 latent widened to bf16 (exact,
 // |int8| < 2^8) in one row-major layout, the fp16 scales as fp32, the RoPE as
 // is.  Both products run on v_mfma_f32_16x16x32_bf16:
@@ -121,7 +121,10 @@ __device__ inline bf16x4 read_tr(const uint16_t* lat_s, int r0, int col0, int la
 }
 
 // One workgroup: one query row, all H = NW*16 heads, NBLK * 32 selected rows
-// (a split), staged in 32-row blocks through two LDS buffers.
+// (a split), staged in 32-row blocks through two LDS buffers.  Split s takes
+// the row's selected indices s, s + nsplit, s + 2 nsplit, ...: the host-mirror
+// reads of a row's misses (old positions, early in the ascending selection)
+// spread over all its workgroups instead of loading its first splits.
 template <int NW, int NBLK>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   constexpr int NT = NW * 64;
@@ -149,7 +152,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   const int H = ka.H;
   const int h0 = wave * 16;
   const int64_t rb = ka.row_bytes;
-  const int j_begin = split * kSplit;
 
   // The split's rows: position (selection), then the row's place in the
   // round, derived from the counts phase of the gather plan exactly as the
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   int64_t t_w = 0;
   if (tid < kSplit) {
     const int64_t M = own_counts ? u.dyn[1] : s.info[kInfoM];
-    const int j = j_begin + tid;
+    const int j = split + tid * ka.nsplit;
     const int32_t pos = j < ka.K ? s.sel[(int64_t)r * ka.K + j] : -1;
     const bool ok = j < n_sel && pos >= 0 && pos < ka.max_positions && (!own_counts || pos < L);
     const int64_t w = ok ? pos >> 5 : 0;
@@ -248,8 +250,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
       g_add(&u.totals[8], (int64_t)__popcll(hb));
     }
   }
-  if (j_begin >= n_sel) return;                          // (uniform) map entries written above
-  const int nrows = min(n_sel - j_begin, kSplit);
+  if (split >= n_sel) return;                            // (uniform) map entries written above
 
   // Query fragments (B operand of the logits): lane holds Q[h0 + l16][32 ks + 8 q4 .. +7].
   bf16x8 qa[18];
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     }
     __syncthreads();
     if (tid < kSplit) {
-      const int j = j_begin + tid;
+      const int j = split + tid * ka.nsplit;
       int ux = -1;
       if (live) {
         const uint32_t x = cnt[t_w] + __popc(t_sw & t_below);
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int j = b * kBlk + 16 * mt + 4 * q4 + v;
-          lg[mt][v] = (j < nrows && s_ux[j] >= 0) ? sacc[mt][v] * ka.scale_log2 : -INFINITY;
+          lg[mt][v] = s_ux[j] >= 0 ? sacc[mt][v] * ka.scale_log2 : -INFINITY;
         }
     }
 
@@ -563,7 +564,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
   const int nt = rem / n_hg, hg = rem % n_hg;
   const ScratchG s = scratch_of(a, seq);
   const int H = ka.H;
-  const int used = min(MAXS, (s.sel_n[r] + ka.split_rows - 1) / ka.split_rows);
+  const int used = min(MAXS, min((ka.ga.K + ka.split_rows - 1) / ka.split_rows, s.sel_n[r]));
   if (used < 1) return;                                  // (uniform) no selection: nothing to merge
   const int tid = threadIdx.x;
   const int e0 = tid * EPT, l16 = e0 / HW, hl0 = e0 % HW;
