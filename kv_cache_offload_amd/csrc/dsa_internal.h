@@ -95,7 +95,8 @@ struct ScratchT {
   P<i32x2> cand;            // [R_max][P_pad] top-k candidates (key, position), by chunk, in position order
   P<uint32_t> cand_n;       // [R_max][n_chunks] candidates per chunk
   P<int32_t> rowdig;        // [R_max][4] b0, b1, keys still needed: the row's threshold digits so far
-  P<uint32_t> done;         // [1] rows of the step that finished their selection (reset by the last)
+  P<uint32_t> done;         // [1 + R_max] rows of the step that finished their selection, then per row
+                            // the chunks that finished their lists (each reset by the last to arrive)
 };
 
 using UnitDev = UnitT<HostPtr>;

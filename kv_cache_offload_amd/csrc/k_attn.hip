@@ -12,8 +12,9 @@
 // bf16 RoPE.
 //
 // gfx950 mapping.  A workgroup owns one query row and a split of 64 of its
-// selected rows (every nsplit-th), all heads: wave w holds heads 16w..16w+15.  The rows are staged in 32-row blocks through two
-// LDS buffers, once for all waves: the int8 latent widened to bf16 (exact,
+// selected rows (every nsplit-th), all heads: wave w holds heads 16w..16w+15.
+// The rows are staged in 32-row blocks through two LDS buffers, once for all
+// waves: the int8 latent widened to bf16 (exact,
 // |int8| < 2^8) in one row-major layout, the fp16 scales as fp32, the RoPE as
 // is.  Both products run on v_mfma_f32_16x16x32_bf16:
 //   * logits, transposed: S^T[j][h] = sum_d C[j][d] Q[h][d], the A operand

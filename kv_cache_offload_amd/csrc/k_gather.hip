@@ -165,17 +165,17 @@ __global__ __launch_bounds__(256) void bad_slot_kernel(UnitDev ud, int64_t L, in
   }
 }
 
-// Zero the Top-K histograms, the selection bitmap and the arrival counter of
+// Zero the Top-K histograms, the selection bitmap and the arrival counters of
 // every sequence's scratch set (blockIdx.y = sequence), one word per thread.
 __global__ __launch_bounds__(256) void clear_step_kernel(StepArgs a, int r_max, int64_t sel_words) {
   const ScratchG s = scratch_of(a, (int)blockIdx.y);
   const int64_t n0 = (int64_t)kHistReps * r_max * kRadixBins, n1 = (int64_t)r_max * kRadixBins;
-  const int64_t n = n0 + n1 + sel_words + 1;
+  const int64_t n = n0 + n1 + sel_words + 1 + r_max;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
     if (t < n0) s.hist0[t] = 0u;
     else if (t < n0 + n1) s.hist1[t - n0] = 0u;
     else if (t < n0 + n1 + sel_words) s.selmask[t - n0 - n1] = 0u;
-    else s.done[0] = 0u;
+    else s.done[t - n0 - n1 - sel_words] = 0u;
   }
 }
 
@@ -229,7 +229,7 @@ hipError_t launch_rollback(const UnitDev& unit, int64_t L, int64_t M, hipStream_
 }
 
 hipError_t launch_clear_step_scratch(const Geometry& g, const StepArgs& a, hipStream_t st) {
-  const int64_t words = (int64_t)(kHistReps + 1) * g.r_max * kRadixBins + g.p_pad / 32 + 1;
+  const int64_t words = (int64_t)(kHistReps + 1) * g.r_max * kRadixBins + g.p_pad / 32 + 1 + g.r_max;
   return launch_k(clear_step_kernel, dim3(grid_for(words, 64), (unsigned)a.n_seqs), dim3(256), 0, st, a, g.r_max,
                   g.p_pad / 32);
 }

@@ -17,13 +17,14 @@
 //     than 65,536 positions that list would be long, so a refine pass first
 //     builds the second-digit histogram and the lists keep only keys whose
 //     first two digits are at or above (b0, b1): barely more than K;
-//   * final (one 1024-thread workgroup per row): loads the row's candidates
-//     into LDS, finds the remaining digits -- the threshold key tau and the
-//     number E of keys equal to tau that are taken -- and emits the selection
-//     in ascending position order: every key above tau plus the E
-//     lowest-position keys equal to tau.  If the candidates do not fit in LDS
-//     (nearly all scores equal), the same passes read the candidate lists from
-//     global memory.
+//   * final (one 1024-thread workgroup per row: for short histories the last
+//     of the row's chunk workgroups to finish, in the same launch; for long
+//     ones a launch of its own): loads the row's candidates into LDS, finds the
+//     remaining digits -- the threshold key tau and the number E of keys equal
+//     to tau that are taken -- and emits the selection in ascending position
+//     order: every key above tau plus the E lowest-position keys equal to tau.
+//     If the candidates do not fit in LDS (nearly all scores equal), the same
+//     passes read the candidate lists from global memory.
 // Each selected position is marked in the step's union bitmap, and the last
 // row of each sequence to finish runs the counts phase of the gather plan
 // (gather_plan.h; its walk runs in the attention launch).  All per-position
@@ -105,15 +106,13 @@ __device__ inline void mark_selection(const ScratchG& s, const int32_t* s_sel, i
 }
 
 // Fewer visible positions than K: every visible position is selected.
-__device__ inline void select_all_visible(const ScratchG& s, int r, int K, int64_t n_vis, int32_t* s_sel) {
+__device__ inline void select_all_visible(const ScratchG& s, int r, int K, int64_t n_vis) {
   const int tid = threadIdx.x;
   const auto sel = s.sel + (int64_t)r * K;
   for (int t = tid; t < K; t += kSelThreads) {
     sel[t] = t < n_vis ? t : -1;
-    s_sel[t] = t < n_vis ? t : -1;
+    if (t < n_vis) g_or(&s.selmask[t >> 5], 1u << (t & 31));
   }
-  __syncthreads();
-  mark_selection(s, s_sel, (int)n_vis);
   if (tid == 0) s.sel_n[r] = (int32_t)n_vis;
 }
 
@@ -212,6 +211,8 @@ struct SelectLds {
   uint32_t wcnt[2 * kSelWaves];
   int32_t sel[kMaxK];
   uint32_t last;
+  int b1;
+  uint32_t need;
 };
 
 // The row's final step: the remaining digits over the candidates -- the
@@ -225,44 +226,83 @@ __device__ void resolve_row(const TopkKArgs& ka, const ScratchG& s, int r, int64
   const int n_chunks = (int)((n_vis + kTopkChunk - 1) / kTopkChunk);
 
   // (the histograms are cleared for the next step by the gather's assign kernel)
-  if (!ka.long_mode) find_bin_regs<kSelWaves, kRadixBins, kRadixBins / kSelThreads>(h1c, need, sm.sh, &b1, &need);
+  // One scan for both: the second-digit histogram (short histories; its bins
+  // from the highest down, PER to a thread) and the chunk list sizes.
+  constexpr int kPer = kRadixBins / kSelThreads;
+  uint32_t hl = 0;
+  if (!ka.long_mode)
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) hl += h1c[e];
   {
-    uint32_t tot;
-    const uint32_t base = block_scan<kSelWaves>(cnt, &tot, sm.sh);
-    if (tid < n_chunks) sm.off[tid] = base;
-    if (tid == 0) sm.off[n_chunks] = tot;
+    uint4 tot;
+    const uint4 pre = block_scan4<kSelWaves>(make_uint4(hl, cnt, 0u, 0u), &tot, sm.sh);
+    if (tid < n_chunks) sm.off[tid] = pre.y;
+    if (tid == 0) sm.off[n_chunks] = tot.y;
+    if (!ka.long_mode && pre.x < need && pre.x + hl >= need) {   // the bin holding the need-th key
+      uint32_t acc = pre.x;
+      bool found = false;
+#pragma unroll
+      for (int e = kPer - 1; e >= 0; --e) {
+        if (!found && acc + h1c[e] >= need) {
+          sm.b1 = kRadixBins - (tid + 1) * kPer + e;
+          sm.need = need - acc;
+          found = true;
+        }
+        acc += h1c[e];
+      }
+    }
   }
+  for (int b = tid; b < 1024; b += kSelThreads) sm.hist[b] = 0;
+  for (int j = tid; j < K; j += kSelThreads) sm.sel[j] = -1;   // every entry is written below
   __syncthreads();
+  if (!ka.long_mode) {
+    b1 = sm.b1;
+    need = sm.need;
+  }
   const uint32_t C = sm.off[n_chunks];                 // >= K: every key of tau's first digits or above
+  const uint32_t p22 = ((uint32_t)b0 << 11) | (uint32_t)b1;
   uint32_t* lkey = lds;
   int32_t* lpos = reinterpret_cast<int32_t*>(lds + kCandCap);
   CandSrc src{nullptr, nullptr, s.cand + (int64_t)r * ka.p_pad, sm.off, n_chunks};
+  // The candidates into LDS, wave w copying the lists of chunks w, w + 16, ...
+  // (a chunk's list is contiguous at both ends), and the last digit counted of
+  // the keys whose first two digits are (b0, b1) as they pass.
   if (C <= (uint32_t)kCandCap) {
-    constexpr int kLoads = kCandCap / kSelThreads;
-    i32x2 kp[kLoads];
+    constexpr int kBatch = 8;
+    for (int c = wave; c < n_chunks; c += kSelWaves) {
+      const uint32_t base = sm.off[c], n = sm.off[c + 1] - base;
+      const DSA_GLOBAL i32x2* lst = src.gcand + (int64_t)c * kTopkChunk;
+      for (uint32_t i0 = 0; i0 < n; i0 += 64 * kBatch) {
+        i32x2 kp[kBatch];
 #pragma unroll
-    for (int e = 0; e < kLoads; ++e) {
-      const uint32_t i = e * kSelThreads + tid;
-      if (e * kSelThreads < (int)C) kp[e] = src.global(i < C ? i : C - 1);   // uniform branch
-    }
+        for (int q = 0; q < kBatch; ++q) {
+          const uint32_t i = i0 + q * 64 + lane;
+          kp[q] = lst[i < n ? i : n - 1];
+        }
 #pragma unroll
-    for (int e = 0; e < kLoads; ++e)
-      if (e * kSelThreads < (int)C) keep(kp[e]);
+        for (int q = 0; q < kBatch; ++q) keep(kp[q]);
 #pragma unroll
-    for (int e = 0; e < kLoads; ++e) {
-      const uint32_t i = e * kSelThreads + tid;
-      if (i < C) {
-        lkey[i] = (uint32_t)kp[e].x;
-        lpos[i] = kp[e].y;
+        for (int q = 0; q < kBatch; ++q) {
+          const uint32_t i = i0 + q * 64 + lane;
+          if (i < n) {
+            const uint32_t key = (uint32_t)kp[q].x;
+            lkey[base + i] = key;
+            lpos[base + i] = kp[q].y;
+            if ((key >> 10) == p22) atomicAdd(&sm.hist[key & 1023u], 1u);
+          }
+        }
       }
     }
     src.lkey = lkey;
     src.lpos = lpos;
+  } else {
+    for (uint32_t i = tid; i < C; i += kSelThreads) {
+      uint32_t key;
+      int32_t pos;
+      src.get(i, &key, &pos);
+      if ((key >> 10) == p22) atomicAdd(&sm.hist[key & 1023u], 1u);
+    }
   }
-  // last digit of the keys whose first two digits are (b0, b1)
-  const uint32_t p22 = ((uint32_t)b0 << 11) | (uint32_t)b1;
-  for (int b = tid; b < 1024; b += kSelThreads) sm.hist[b] = 0;
-  for (int j = tid; j < K; j += kSelThreads) sm.sel[j] = -1;   // every entry is written below
   __syncthreads();
 
   // Ordered emit layout: wave w owns candidates [w seg, (w+1) seg), 64
@@ -271,13 +311,6 @@ __device__ void resolve_row(const TopkKArgs& ka, const ScratchG& s, int r, int64
   const uint32_t w0 = min(C, wave * seg), w1 = min(C, w0 + seg);
   const bool fused = src.lkey != nullptr;              // seg <= 64 kEmitIters
 
-  for (uint32_t i = tid; i < C; i += kSelThreads) {
-    uint32_t key;
-    int32_t pos;
-    src.get(i, &key, &pos);
-    if ((key >> 10) == p22) atomicAdd(&sm.hist[key & 1023u], 1u);
-  }
-  __syncthreads();
   int b2;
   find_bin<kSelWaves, 1024, 1>(sm.hist, need, sm.sh, &b2, &need);
   const uint32_t tau = (p22 << 10) | (uint32_t)b2;
@@ -354,76 +387,13 @@ __device__ void resolve_row(const TopkKArgs& ka, const ScratchG& s, int r, int64
   if (tid == 0) s.sel_n[r] = K;
 }
 
-// Candidate lists.  One workgroup per (4096-position chunk, row, sequence)
-// keeps the chunk's candidates -- every key whose first digit is at or above
-// the bin b0 of the K-th key (whose first two digits are at or above (b0, b1)
-// for long histories, b1 from the refine pass) -- in position order, and, for
-// short histories, adds the second-digit histogram of its keys in bin b0.
-__global__ __launch_bounds__(kSelThreads) void topk_chunk_kernel(TopkKArgs ka) {
-  __shared__ uint32_t sh[kSelWaves];
-  __shared__ uint32_t hist[kRadixBins];
+// The row's final step, by one workgroup: resolves the row from its candidate
+// lists (or selects every visible position), then, if the gather plan runs
+// here, the last row of the sequence to finish runs its counts phase.
+__device__ void final_row(const TopkKArgs& ka, const UnitG& u, const ScratchG& s, int r, SelectLds& sm,
+                          uint32_t* lds) {
   const StepArgs& a = ka.a;
-  const int chunk = blockIdx.x, r = blockIdx.y, seq = blockIdx.z, tid = threadIdx.x;
-  const UnitG u = unit_of(a, seq);
-  const ScratchG s = scratch_of(a, seq);
-  const int64_t L = u.dyn[0];
-  const int64_t n_vis = L - a.R + r + 1;
-  const int64_t start = (int64_t)chunk * kTopkChunk;
-  if (n_vis <= ka.K || start >= n_vis) return;
-
-  const int64_t t0 = start + tid * kSelPer;
-  const f32x4v f = *reinterpret_cast<const DSA_GLOBAL f32x4v*>(s.scores + (int64_t)r * ka.p_pad + t0);
-  int b0, b1 = 0;
-  uint32_t need;
-  if (ka.long_mode) {                                  // both digits from the digits passes
-    const i32x4 d = *reinterpret_cast<const DSA_GLOBAL i32x4*>(s.rowdig + 4 * r);
-    b0 = d.x;
-    b1 = d.y;
-    need = (uint32_t)d.z;
-  } else {
-    find_bin<kSelWaves, kRadixBins, kHistReps>(s.hist0 + (int64_t)r * kRadixBins, (uint32_t)ka.K, sh, &b0, &need,
-                                               (int64_t)ka.r_max * kRadixBins);
-  }
-  uint32_t key[kSelPer];
-#pragma unroll
-  for (int e = 0; e < kSelPer; ++e) key[e] = t0 + e < n_vis ? order_key(f[e]) : 0u;   // 0: not visible
-  const int shift = ka.long_mode ? 10 : 21;
-  const uint32_t thr = ka.long_mode ? (((uint32_t)b0 << 11) | (uint32_t)b1) : (uint32_t)b0;
-  if (!ka.long_mode && chunk == 0 && tid == 0)         // the row's digits so far, for the final pass
-    *reinterpret_cast<DSA_GLOBAL i32x4*>(s.rowdig + 4 * r) = (i32x4){b0, b1, (int32_t)need, 0};
-
-  if (!ka.long_mode) {
-    for (int b = tid; b < kRadixBins; b += kSelThreads) hist[b] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < kSelPer; ++e)
-      if (t0 + e < n_vis && (key[e] >> 21) == (uint32_t)b0) atomicAdd(&hist[(key[e] >> 10) & 2047u], 1u);
-    __syncthreads();
-    const auto gh = s.hist1 + (int64_t)r * kRadixBins;
-    for (int b = tid; b < kRadixBins; b += kSelThreads)
-      if (hist[b]) g_add(&gh[b], hist[b]);
-  }
-  uint32_t mine = 0;
-#pragma unroll
-  for (int e = 0; e < kSelPer; ++e) mine += (t0 + e < n_vis && (key[e] >> shift) >= thr) ? 1u : 0u;
-  uint32_t tot;
-  uint32_t at = block_scan<kSelWaves>(mine, &tot, sh);
-  const auto out = s.cand + (int64_t)r * ka.p_pad + start;
-#pragma unroll
-  for (int e = 0; e < kSelPer; ++e)
-    if (t0 + e < n_vis && (key[e] >> shift) >= thr) out[at++] = (i32x2){(int)key[e], (int)(t0 + e)};
-  if (tid == 0) s.cand_n[(int64_t)r * ka.n_chunks + chunk] = tot;
-}
-
-// One workgroup per (row, sequence): resolves the row from its candidate lists;
-// the last row of a sequence to finish then runs the counts phase of the plan.
-__global__ __launch_bounds__(kSelThreads) void topk_final_kernel(TopkKArgs ka) {
-  extern __shared__ __align__(16) uint32_t lds[];   // keys[kCandCap], positions[kCandCap]
-  __shared__ SelectLds sm;
-  const StepArgs& a = ka.a;
-  const int r = blockIdx.x, seq = blockIdx.y, tid = threadIdx.x;
-  const UnitG u = unit_of(a, seq);
-  const ScratchG s = scratch_of(a, seq);
+  const int tid = threadIdx.x;
   // Everything this pass reads first, issued together: the round-start state
   // (the plan needs it too), the row's digits from the chunk pass, the chunk
   // list sizes (one chunk per thread at most) and this thread's bins of the
@@ -437,7 +407,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_final_kernel(TopkKArgs ka) {
   const int K = ka.K;
   if (r == 0 && tid == 0) s.counters[8] = 0;          // host reads: the round's attention adds them
   if (n_vis <= K) {
-    select_all_visible(s, r, K, n_vis, sm.sel);
+    select_all_visible(s, r, K, n_vis);
   } else {
     const int n_chunks = (int)((n_vis + kTopkChunk - 1) / kTopkChunk);
     const uint32_t cnt = tid < n_chunks ? cnt_all : 0u;  // lists of this step's chunks only
@@ -447,6 +417,118 @@ __global__ __launch_bounds__(kSelThreads) void topk_final_kernel(TopkKArgs ka) {
   // counts too, where attention can count the union itself); CLOCK's walk, whose
   // first lap can sweep the whole ring, keeps all 1,024 threads here.
   if (ka.plan_mode > 0) plan_if_last(u, s, ka.plan, (uint32_t)a.R, ps, lds, ka.plan_mode == 2);
+}
+
+// The chunk's candidate list (and, for short histories, its part of the
+// second-digit histogram).
+__device__ inline void chunk_lists(const TopkKArgs& ka, const ScratchG& s, int chunk, int r, int64_t n_vis,
+                                   SelectLds& sm) {
+  const int tid = threadIdx.x;
+  const int64_t start = (int64_t)chunk * kTopkChunk;
+
+  const int64_t t0 = start + tid * kSelPer;
+  const f32x4v f = *reinterpret_cast<const DSA_GLOBAL f32x4v*>(s.scores + (int64_t)r * ka.p_pad + t0);
+  int b0, b1 = 0;
+  uint32_t need;
+  if (ka.long_mode) {                                  // both digits from the digits passes
+    const i32x4 d = *reinterpret_cast<const DSA_GLOBAL i32x4*>(s.rowdig + 4 * r);
+    b0 = d.x;
+    b1 = d.y;
+    need = (uint32_t)d.z;
+  } else {
+    find_bin<kSelWaves, kRadixBins, kHistReps>(s.hist0 + (int64_t)r * kRadixBins, (uint32_t)ka.K, sm.sh, &b0,
+                                               &need, (int64_t)ka.r_max * kRadixBins);
+  }
+  uint32_t key[kSelPer];
+#pragma unroll
+  for (int e = 0; e < kSelPer; ++e) key[e] = t0 + e < n_vis ? order_key(f[e]) : 0u;   // 0: not visible
+  const int shift = ka.long_mode ? 10 : 21;
+  const uint32_t thr = ka.long_mode ? (((uint32_t)b0 << 11) | (uint32_t)b1) : (uint32_t)b0;
+  if (!ka.long_mode && chunk == 0 && tid == 0)         // the row's digits so far, for the final pass
+    *reinterpret_cast<DSA_GLOBAL i32x4*>(s.rowdig + 4 * r) = (i32x4){b0, b1, (int32_t)need, 0};
+
+  if (!ka.long_mode) {
+    for (int b = tid; b < kRadixBins; b += kSelThreads) sm.hist[b] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kSelPer; ++e)
+      if (t0 + e < n_vis && (key[e] >> 21) == (uint32_t)b0) atomicAdd(&sm.hist[(key[e] >> 10) & 2047u], 1u);
+    __syncthreads();
+    const auto gh = s.hist1 + (int64_t)r * kRadixBins;
+    for (int b = tid; b < kRadixBins; b += kSelThreads)
+      if (sm.hist[b]) g_add(&gh[b], sm.hist[b]);
+  }
+  uint32_t mine = 0;
+#pragma unroll
+  for (int e = 0; e < kSelPer; ++e) mine += (t0 + e < n_vis && (key[e] >> shift) >= thr) ? 1u : 0u;
+  uint32_t tot;
+  uint32_t at = block_scan<kSelWaves>(mine, &tot, sm.sh);
+  const auto out = s.cand + (int64_t)r * ka.p_pad + start;
+#pragma unroll
+  for (int e = 0; e < kSelPer; ++e)
+    if (t0 + e < n_vis && (key[e] >> shift) >= thr) out[at++] = (i32x2){(int)key[e], (int)(t0 + e)};
+  if (tid == 0) s.cand_n[(int64_t)r * ka.n_chunks + chunk] = tot;
+}
+
+// Candidate lists.  One workgroup per (4096-position chunk, row, sequence)
+// keeps the chunk's candidates -- every key whose first digit is at or above
+// the bin b0 of the K-th key (whose first two digits are at or above (b0, b1)
+// for long histories, b1 from the refine pass) -- in position order, and, for
+// short histories, adds the second-digit histogram of its keys in bin b0.
+// FUSED (short histories): the last of a row's chunk workgroups to finish then
+// resolves the row itself (final_row), so no launch separates the two passes.
+// Each workgroup publishes its lists before it arrives: every wave waits until
+// its own stores have completed, then thread 0's arrival is a device-scope
+// release (the XCD's L2 is written back, so a workgroup on another XCD reads
+// the lists from memory; the histogram adds are device-scope atomics).  The
+// last to arrive drops its cached copies (device-scope acquire) before it reads
+// the other chunks' lists.  No workgroup waits for another.
+template <bool FUSED>
+__global__ __launch_bounds__(kSelThreads) void topk_chunk_kernel(TopkKArgs ka) {
+  extern __shared__ __align__(16) uint32_t lds[];      // FUSED: keys[kCandCap], positions[kCandCap]
+  __shared__ SelectLds sm;
+  const StepArgs& a = ka.a;
+  const int chunk = blockIdx.x, r = blockIdx.y, seq = blockIdx.z, tid = threadIdx.x;
+  const UnitG u = unit_of(a, seq);
+  const ScratchG s = scratch_of(a, seq);
+  const int64_t L = u.dyn[0];
+  const int64_t n_vis = L - a.R + r + 1;
+  const int64_t start = (int64_t)chunk * kTopkChunk;
+  if (n_vis > ka.K) {
+    if (start >= n_vis) return;
+    chunk_lists(ka, s, chunk, r, n_vis, sm);
+    if (!FUSED) return;
+    __builtin_amdgcn_s_waitcnt(0);                     // this wave's stores and adds completed
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t n_ch = (uint32_t)((n_vis + kTopkChunk - 1) / kTopkChunk);
+      // release: the L2 written back, and the write-back waited for (explicitly:
+      // nothing else is outstanding, so no wait would otherwise be placed here)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __builtin_amdgcn_s_waitcnt(0);
+      const uint32_t prev = __hip_atomic_fetch_add(s.done + 1 + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = prev + 1 == n_ch;
+      sm.last = last ? 1u : 0u;
+      if (last) {
+        __hip_atomic_store(s.done + 1 + r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      }
+    }
+    __syncthreads();
+    if (!sm.last) return;
+  } else if (!FUSED || chunk != 0) {                   // every visible position is selected: chunk 0's work
+    return;
+  }
+  if constexpr (FUSED) final_row(ka, u, s, r, sm, lds);
+}
+
+// Long histories: one workgroup per (row, sequence) resolves the row from its
+// candidate lists after the chunk pass.
+__global__ __launch_bounds__(kSelThreads) void topk_final_kernel(TopkKArgs ka) {
+  extern __shared__ __align__(16) uint32_t lds[];   // keys[kCandCap], positions[kCandCap]
+  __shared__ SelectLds sm;
+  const int r = blockIdx.x, seq = blockIdx.y;
+  final_row(ka, unit_of(ka.a, seq), scratch_of(ka.a, seq), r, sm, lds);
 }
 
 TopkKArgs topk_args(const Geometry& g, const StepArgs& a) {
@@ -464,7 +546,10 @@ int topk_plan_mode(const Geometry& g, const StepArgs& a) {
 }
 
 hipError_t prepare_topk_kernels() {
-  return hipFuncSetAttribute((const void*)topk_final_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+  const hipError_t e = hipFuncSetAttribute((const void*)topk_final_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           2 * kCandCap * (int)sizeof(uint32_t));
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)topk_chunk_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                              2 * kCandCap * (int)sizeof(uint32_t));
 }
 
@@ -484,8 +569,11 @@ hipError_t launch_topk_partial(const Geometry& g, const StepArgs& a, hipStream_t
 hipError_t launch_topk_select(const Geometry& g, const StepArgs& a, hipStream_t st) {
   const TopkKArgs ka = topk_args(g, a);
   const int chunks = (int)((a.l_max + kTopkChunk - 1) / kTopkChunk);
-  const hipError_t e = launch_k(topk_chunk_kernel, dim3((unsigned)chunks, (unsigned)a.R, (unsigned)a.n_seqs),
-                                dim3(kSelThreads), 0, st, ka);
+  const dim3 grid((unsigned)chunks, (unsigned)a.R, (unsigned)a.n_seqs);
+  if (!ka.long_mode)
+    return launch_k(topk_chunk_kernel<true>, grid, dim3(kSelThreads), 2 * kCandCap * (uint32_t)sizeof(uint32_t), st,
+                    ka);
+  const hipError_t e = launch_k(topk_chunk_kernel<false>, grid, dim3(kSelThreads), 0, st, ka);
   if (e != hipSuccess) return e;
   return launch_k(topk_final_kernel, dim3((unsigned)a.R, (unsigned)a.n_seqs), dim3(kSelThreads),
                   2 * kCandCap * (uint32_t)sizeof(uint32_t), st, ka);

@@ -268,7 +268,7 @@ ScrOff scratch_layout(const Geometry& g) {
   o.base_m = take((size_t)P / 32 * 4);
   o.pdesc = take((size_t)P * 16);
   o.victim = take((size_t)g.s_words * 32 * 8);
-  o.done = take(4);
+  o.done = take((size_t)(1 + g.r_max) * 4);
   o.hist0 = take((size_t)kHistReps * g.r_max * kRadixBins * 4);
   o.hist1 = take((size_t)g.r_max * kRadixBins * 4);
   o.cand = take((size_t)g.r_max * P * 8);
