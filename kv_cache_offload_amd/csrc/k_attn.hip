@@ -138,6 +138,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   __shared__ const DSA_GLOBAL uint8_t* s_from[kSplit];   // where each row is read from (null: masked)
   __shared__ int s_ux[kSplit];                            // its compact row, -1 if masked
   __shared__ uint32_t s_scan[NW];
+  __shared__ uint32_t s_host;                             // any row of the split read from the host mirror
 
   const StepArgs& a = ka.a;
   const int split = blockIdx.x, r = blockIdx.y, seq = blockIdx.z;
@@ -246,6 +247,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   }
   if (wave == 0) {                                       // the split's host-mirror reads (one wave holds its rows)
     const uint64_t hb = __ballot(host);
+    if (lane == 0) s_host = hb ? 1u : 0u;
     if (lane == 0 && hb) {
       g_add(&s.counters[8], (int64_t)__popcll(hb));
       g_add(&u.totals[8], (int64_t)__popcll(hb));
@@ -266,10 +268,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   }
   __syncthreads();                                       // s_from (and the word counts) for every thread
 
-  // Every 16-byte piece of a block is requested at once.  Block b + 1 is
-  // requested as soon as block b has arrived, before block b is computed: the
-  // host link then serves every workgroup's first block before any second
-  // block, and each block is computed while the next one arrives.
+  // Every 16-byte piece of a block is requested at once.  A split with rows on
+  // the host requests block b + 1 as soon as block b has arrived, before block
+  // b is computed: the host link then serves every workgroup's first block
+  // before any second block, and each block is computed while the next one
+  // arrives.  A split whose rows are all in HBM requests its second block with
+  // the first (both register buffers are free): one memory round trip for both.
   // Piece q of a block: row q / 41, bytes 16 (q % 41) .. ; masked rows read the
   // unit's key store (always mapped) and are zeroed below.
   u32x4 raw[2][PPT];
@@ -283,7 +287,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
       raw[b & 1][e] = *reinterpret_cast<const DSA_GLOBAL u32x4*>(at);
     }
   };
+  const bool early = NBLK > 1 && !s_host;                // (uniform)
   request(0);
+  if (early) request(1);
   if (own_counts) {                                      // (uniform) the union indices, while the rows arrive
     const int64_t per = (nw + NT - 1) / NT;
     const int64_t c0 = min(nw, (int64_t)tid * per), c1 = min(nw, c0 + per);
@@ -353,7 +359,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
         *reinterpret_cast<u32x4*>(rope + rl * kRopeStride + 8 * (part - 33)) = v;
       }
     }
-    if (b + 1 < NBLK) request(b + 1);
+    if (b + 1 < NBLK && !(b == 0 && early)) request(b + 1);
     __syncthreads();
 
     // Logits S^T[j][h]: lane holds rows 16 mt + 4 q4 + v of head h0 + l16; each

@@ -106,6 +106,28 @@ def test_planted_ties_small_key_alphabet():
     _run_and_compare(w, MODE_OFFLOAD, steps=3, history_fn=hist, query_fn=q_small)
 
 
+def test_one_chunk_holds_every_candidate():
+    # positions 8192..12287 (the third 4096-position chunk) carry one key that
+    # outscores every other: the Top-K's candidates are that chunk's 4,096 equal
+    # keys, one chunk list far longer than the part the final step reads early,
+    # and the tie rule takes its lowest 2,048 positions
+    w = S.WORKLOADS["tiny"].scaled(history=20000, rows_per_step=2, steps=2, top_k=2048, hot_slots=4096)
+
+    def hist(w_, layer, seq):
+        keys, rows = S.history(w_, layer, seq)
+        keys = keys.copy()
+        keys[8192:12288] = S.bf16_bits(np.full((4096, keys.shape[1]), 8.0))
+        return keys, rows
+
+    def q_ones(w_, layer, seq, step):
+        iq, iw, ql, qr = S.step_queries(w_, layer, seq, step)
+        return S.bf16_bits(np.ones(iq.shape)), np.ones_like(iw), ql, qr
+    _note("one chunk of candidates")
+    orcs = _run_and_compare(w, MODE_OFFLOAD, steps=2, history_fn=hist, query_fn=q_ones)
+    sel, _ = orcs[(0, 0)].selection()
+    assert sel[0].tolist() == list(range(8192, 8192 + 2048))
+
+
 def test_peaked_attention():
     # queries x50 (integer-valued latent/rope queries in [-4, 4] * 50): softmax far from uniform,
     # so a wrong scale, RoPE term or row index moves outputs past the tolerance
