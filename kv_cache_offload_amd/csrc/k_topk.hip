@@ -264,14 +264,22 @@ __device__ void resolve_row(const TopkKArgs& ka, const ScratchG& s, int r, int64
   uint32_t* lkey = lds;
   int32_t* lpos = reinterpret_cast<int32_t*>(lds + kCandCap);
   CandSrc src{nullptr, nullptr, s.cand + (int64_t)r * ka.p_pad, sm.off, n_chunks};
-  // The candidates into LDS, wave w copying the lists of chunks w, w + 16, ...
-  // (a chunk's list is contiguous at both ends), and the last digit counted of
-  // the keys whose first two digits are (b0, b1) as they pass.
-  if (C <= (uint32_t)kCandCap) {
+  // The candidates into LDS, and the last digit counted of the keys whose first
+  // two digits are (b0, b1) as they pass.  At most one chunk per wave (short
+  // histories): wave w copies chunk w's list (contiguous at both ends).  More
+  // chunks (long histories, short lists): candidate i of the row is found by
+  // its chunk's offset, and every load of the row is issued at once.
+  auto put = [&](uint32_t at, i32x2 kp) {
+    const uint32_t key = (uint32_t)kp.x;
+    lkey[at] = key;
+    lpos[at] = kp.y;
+    if ((key >> 10) == p22) atomicAdd(&sm.hist[key & 1023u], 1u);
+  };
+  if (C <= (uint32_t)kCandCap && n_chunks <= kSelWaves) {
     constexpr int kBatch = 8;
-    for (int c = wave; c < n_chunks; c += kSelWaves) {
-      const uint32_t base = sm.off[c], n = sm.off[c + 1] - base;
-      const DSA_GLOBAL i32x2* lst = src.gcand + (int64_t)c * kTopkChunk;
+    if (wave < n_chunks) {
+      const uint32_t base = sm.off[wave], n = sm.off[wave + 1] - base;
+      const DSA_GLOBAL i32x2* lst = src.gcand + (int64_t)wave * kTopkChunk;
       for (uint32_t i0 = 0; i0 < n; i0 += 64 * kBatch) {
         i32x2 kp[kBatch];
 #pragma unroll
@@ -284,14 +292,27 @@ __device__ void resolve_row(const TopkKArgs& ka, const ScratchG& s, int r, int64
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
           const uint32_t i = i0 + q * 64 + lane;
-          if (i < n) {
-            const uint32_t key = (uint32_t)kp[q].x;
-            lkey[base + i] = key;
-            lpos[base + i] = kp[q].y;
-            if ((key >> 10) == p22) atomicAdd(&sm.hist[key & 1023u], 1u);
-          }
+          if (i < n) put(base + i, kp[q]);
         }
       }
+    }
+    src.lkey = lkey;
+    src.lpos = lpos;
+  } else if (C <= (uint32_t)kCandCap) {
+    constexpr int kLoads = kCandCap / kSelThreads;
+    i32x2 kp[kLoads];
+#pragma unroll
+    for (int e = 0; e < kLoads; ++e) {
+      const uint32_t i = e * kSelThreads + tid;
+      if (e * kSelThreads < (int)C) kp[e] = src.global(i < C ? i : C - 1);   // uniform branch
+    }
+#pragma unroll
+    for (int e = 0; e < kLoads; ++e)
+      if (e * kSelThreads < (int)C) keep(kp[e]);
+#pragma unroll
+    for (int e = 0; e < kLoads; ++e) {
+      const uint32_t i = e * kSelThreads + tid;
+      if (i < C) put(i, kp[e]);
     }
     src.lkey = lkey;
     src.lpos = lpos;
