@@ -57,6 +57,9 @@ def parse():
                         "selection; steps/s without and with prefetch on a second stream, and resident")
     p.add_argument("--quantize-rows", type=int, default=1 << 20,
                    help="rows of the quantise-on-append measurement (0 skips it)")
+    p.add_argument("--separate-append", action="store_true",
+                   help="append with dsa_append_rows and decode with dsa_decode_step (an append launch per "
+                        "sequence and layer step) instead of one dsa_append_decode_step call")
     p.add_argument("--pairs", type=int, default=3,
                    help="the timed steps of each mode are split into this many segments, offload and resident "
                         "interleaved with the order alternating from pair to pair")
@@ -182,13 +185,15 @@ class Runner:
     """One session (every layer and sequence of the workload) with every step's
     inputs already in HBM; calls the C ABI directly.  One step = for each layer
     in order: append R rows to each sequence, then one decode step of the layer
-    (all sequences together)."""
+    (all sequences together) -- one dsa_append_decode_step call, or, with
+    separate_append, dsa_append_rows per sequence and then dsa_decode_step."""
 
-    def __init__(self, w, mode, host_inputs, replacement=0):
+    def __init__(self, w, mode, host_inputs, replacement=0, separate_append=False):
         import torch
         import dsa_synth as S
         import kv_cache_offload_amd as K
         self.K, self.torch, self.w = K, torch, w
+        self.combined = not separate_append
         self.sess = make_session(w, mode, replacement=replacement)
         dev = self.sess.device
         for l in range(w.layers):
@@ -216,6 +221,13 @@ class Runner:
         kb, rb = w.index_dim * 2 * R, w.row_bytes * R          # bytes of one sequence's appended keys / rows
         for _ in range(n):
             for l, (pk, pr, piq, piw, pql, pqr) in enumerate(self.ptr[self.next]):
+                if self.combined:
+                    st = lib.dsa_append_decode_step(self.h, l, R, ctypes.c_void_p(pk), ctypes.c_void_p(pr),
+                                                    ctypes.c_void_p(piq), ctypes.c_void_p(piw), ctypes.c_void_p(pql),
+                                                    ctypes.c_void_p(pqr), out, self.stream)
+                    if st != K.OK:
+                        raise K.DsaError("dsa_append_decode_step", st, K.dsa_last_error(self.h))
+                    continue
                 for q in range(w.seqs):
                     st = lib.dsa_append_rows(self.h, l, q, R, ctypes.c_void_p(pk + q * kb), ctypes.c_void_p(pr + q * rb),
                                              self.stream)
@@ -249,7 +261,7 @@ def timed(runner, n):
     return time.perf_counter() - t0
 
 
-def algorithmic_bytes(w, kind, n_steps, L0, cnt, long_hist):
+def algorithmic_bytes(w, kind, n_steps, L0, cnt, long_hist, combined=False):
     """Bytes each kernel group must move per launch (one layer, every sequence),
     averaged over the timed steps.
 
@@ -264,8 +276,8 @@ def algorithmic_bytes(w, kind, n_steps, L0, cnt, long_hist):
     U = cnt[0] / launches
     hit, ring, miss, noslot = (cnt[i] / launches for i in (1, 2, 3, 4))
     wb = Q * w.ring_rows * rb * 2 * R / w.ring_rows      # 64-row writeback every 64/R steps, read + write
-    if kind == "index_score":
-        return Q * Lmean * w.index_dim * 2                 # every key once
+    if kind == "index_score":                           # every key once (+ the appended rows in one call)
+        return Q * Lmean * w.index_dim * 2 + (Q * R * (w.index_dim * 2 + rb) * 2 if combined else 0)
     if kind == "topk_collect":
         return Q * R * Lmean * 4 * (2 if long_hist else 1)
     if kind == "topk_resolve":
@@ -298,7 +310,8 @@ def kernel_pass(r, w, args):
     kc = r.totals() - kc_before
     long_hist = r.L() > 65536
     kernels = {k: dict(launches=c, avg_us=(m / c * 1e3) if c else 0.0,
-                       bytes_per_launch=algorithmic_bytes(w, k, args.kernel_steps, kL0, kc, long_hist))
+                       bytes_per_launch=algorithmic_bytes(w, k, args.kernel_steps, kL0, kc, long_hist,
+                                                          r.combined))
                for k, (c, m) in kt.items() if c}
     for v in kernels.values():
         v["GBps"] = v["bytes_per_launch"] / (v["avg_us"] * 1e-6) / 1e9 if v["avg_us"] > 0 else 0.0
@@ -320,7 +333,7 @@ def run_pairs(w, inputs, args):
     repl = K.REPL_CLOCK if args.replacement == "clock" else K.REPL_RING
     runners, res = {}, {}
     for name, mode in modes:
-        runners[name] = Runner(w, mode, inputs, replacement=repl)
+        runners[name] = Runner(w, mode, inputs, replacement=repl, separate_append=args.separate_append)
         log(f"{name}: history loaded (L={runners[name].L()}), warmup {args.warmup}")
         runners[name].steps(args.warmup)
         res[name] = dict(seconds=0.0, steps=0, L_start=runners[name].L(), counters=np.zeros(9, np.int64),
@@ -615,6 +628,7 @@ def main():
         "config": {"workload": w.name, "layers": NL, "sequences": Q, "history": w.history, "query_rows": R,
                    "top_k": w.top_k, "hot_slots": w.hot_slots, "index_heads": w.index_heads, "heads": w.heads,
                    "row_bytes": rb, "mode": primary, "replacement": args.replacement,
+                   "append": "separate dsa_append_rows" if args.separate_append else "in dsa_append_decode_step",
                    "L_at_timed_start": off["L_start"]},
         "query_rows_per_s": off["steps_per_s"] * R * Q,
         "roofline": roof,

@@ -266,6 +266,27 @@ dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq,
                            const void* index_q, const float* index_w, const void* q_latent,
                            const void* q_rope, float* out, hipStream_t stream);
 
+/* Append R = rows_per_seq rows to every sequence of `layer`, then one decode
+ * step of those sequences: the same result, state and errors as
+ * dsa_append_rows(layer, q, R, index_keys + q R index_dim, rows + q R
+ * row_bytes) for every sequence q followed by dsa_decode_step(layer, R, ...),
+ * in one call (offload page, section "Starting point": each decode step appends
+ * the step's new KV rows and then attends over the history; section "Decision
+ * 3": new rows enter the GPU's recent ring).  The score launch writes the new
+ * keys and rows itself (its scoring workgroups read the new keys straight from
+ * index_keys), so the step has no launch of its own for the append.
+ *   index_keys: device bf16 [n_seqs][R][index_dim], 16-byte aligned
+ *   rows:       device uint8 [n_seqs][R][row_bytes] packed Q8G64 rows, 16-byte aligned
+ *   index_q, index_w, q_latent, q_rope, out: as for dsa_decode_step.
+ * Both append buffers are read in stream order and may be reused once the
+ * stream has passed this call.  Errors (nothing enqueued): DSA_E_INVALID for a
+ * bad layer, R or buffer; DSA_E_CAPACITY if a sequence would pass
+ * max_positions. */
+dsa_status dsa_append_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq,
+                                  const void* index_keys, const void* rows,
+                                  const void* index_q, const float* index_w, const void* q_latent,
+                                  const void* q_rope, float* out, hipStream_t stream);
+
 /* dsa_decode_step for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments, checks, state changes and results as dsa_decode_step; the

@@ -37,7 +37,7 @@ EXPORTS = ("dsa_session_create", "dsa_session_destroy", "dsa_append_rows", "dsa_
            "dsa_decode_step", "dsa_decode_step_reuse", "dsa_prefetch_reuse", "dsa_unit_state",
            "dsa_mirror_rows",
            "dsa_last_error", "dsa_debug_size", "dsa_debug_get", "dsa_set_kernel_timing",
-           "dsa_kernel_times", "dsa_debug_inject", "dsa_decode_step_static")
+           "dsa_kernel_times", "dsa_debug_inject", "dsa_decode_step_static", "dsa_append_decode_step")
 INJECT_HIP_FAILURE, INJECT_BAD_SLOT = 0, 1
 
 
@@ -94,6 +94,7 @@ def _load_library() -> ctypes.CDLL:
         "dsa_kernel_times": ([P, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         "dsa_debug_inject": ([P, i32, i32, i32, P], ctypes.c_int),
         "dsa_decode_step_static": ([P, i32, i32, P, P, P, P, P, P], ctypes.c_int),
+        "dsa_append_decode_step": ([P, i32, i32, P, P, P, P, P, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -156,6 +157,12 @@ def dsa_rollback_rows(h, layer, seq, n, stream) -> int:
 def dsa_decode_step(h, layer, rows_per_seq, index_q, index_w, q_latent, q_rope, out, stream) -> int:
     return _lib.dsa_decode_step(_handle(h), layer, rows_per_seq, index_q, index_w, q_latent, q_rope,
                                 out, stream)
+
+
+def dsa_append_decode_step(h, layer, rows_per_seq, index_keys, rows, index_q, index_w, q_latent, q_rope, out,
+                           stream) -> int:
+    return _lib.dsa_append_decode_step(_handle(h), layer, rows_per_seq, index_keys, rows, index_q, index_w,
+                                       q_latent, q_rope, out, stream)
 
 
 def dsa_decode_step_static(h, layer, rows_per_seq, index_q, index_w, q_latent, q_rope, out, stream) -> int:
@@ -291,6 +298,14 @@ class Session:
         self._check("dsa_decode_step", dsa_decode_step(
             self.h, layer, R, self._ptr(index_q), self._ptr(index_w), self._ptr(q_latent),
             self._ptr(q_rope), self._ptr(out), self._stream()))
+
+    def append_decode_step(self, layer, index_keys, rows, index_q, index_w, q_latent, q_rope, out):
+        """index_keys [n_seqs][R][index_dim], rows [n_seqs][R][row_bytes]: appended to every sequence, then
+        one decode step."""
+        R = index_q.shape[1]
+        self._check("dsa_append_decode_step", dsa_append_decode_step(
+            self.h, layer, R, self._ptr(index_keys), self._ptr(rows), self._ptr(index_q), self._ptr(index_w),
+            self._ptr(q_latent), self._ptr(q_rope), self._ptr(out), self._stream()))
 
     def decode_step_static(self, layer, index_q, index_w, q_latent, q_rope, out):
         R = index_q.shape[1]

@@ -110,7 +110,7 @@ static_assert(sizeof(UnitDev) == sizeof(UnitG) && sizeof(SeqScratch) == sizeof(S
 // walk the writeback position and the number of misses that took a slot.
 enum {
   kInfoUnion = 0, kInfoWriteback = 1, kInfoAssigned = 2, kInfoRound = 3, kInfoM = 4, kInfoHand = 5,
-  kInfoMiss = 6, kInfoRing = 7, kInfoHit = 8, kInfoNewHand = 9, kInfoWords = 16
+  kInfoMiss = 6, kInfoRing = 7, kInfoHit = 8, kInfoNewHand = 9, kInfoL = 10, kInfoWords = 16
 };
 
 // Attention counts the union itself (and its extra workgroup runs the whole
@@ -151,8 +151,10 @@ struct StepArgs {
   int64_t s_stride;       // bytes between consecutive sequences' scratch
   int n_seqs;
   int R;
-  int64_t l_max;          // max L over the layer's sequences (grid sizing)
+  int64_t l_max;          // max L over the layer's sequences (grid sizing; the appended rows included)
   uint32_t* err;          // device address of the session's error flags (kDevErrWords words)
+  int add;                // rows the step's first launch appends to every sequence (an append-and-decode
+                          // step; 0 otherwise): until the round ends the unit's L lags by this many
 };
 
 // Device-side consistency checks.  A kernel that finds a position, slot or
@@ -214,6 +216,9 @@ __device__ inline G moved_desc(const D& d, int64_t delta, int alt, int64_t alt_d
 __device__ inline UnitG unit_of(const StepArgs& a, int seq) {
   return moved_desc<UnitG>(a.u0, seq * a.u_stride, (int)(offsetof(UnitDev, rows) / 8), seq * a.rows_stride);
 }
+// The history length a step's kernels work on: the unit's L plus the rows the
+// step's first launch appends (the assign pass publishes the sum at round end).
+__device__ inline int64_t step_L(const UnitG& u, const StepArgs& a) { return u.dyn[0] + a.add; }
 __device__ inline ScratchG scratch_of(const StepArgs& a, int seq) {
   return moved_desc<ScratchG>(a.s0, seq * a.s_stride, -1, 0);
 }
@@ -230,8 +235,10 @@ __device__ inline void g_add(DSA_GLOBAL int64_t* p, int64_t v) {
 }
 
 // ---- launchers (each returns the hipError_t of its launch) ----
+// app_keys/app_rows: the rows an append-and-decode step appends (a.add per
+// sequence; ignored when a.add is 0), written by extra workgroups of the launch.
 hipError_t launch_score(const Geometry& g, const StepArgs& a, const uint16_t* q, const float* w,
-                        hipStream_t st);
+                        const uint16_t* app_keys, const uint8_t* app_rows, hipStream_t st);
 // Top-K: a refine pass over chunks for long histories (partial), then candidate
 // lists per chunk and a per-row resolve (select); the resolve ends with the
 // gather plan, run by the last row of each sequence.

@@ -44,10 +44,14 @@ __device__ inline void assign_block(const GatherKArgs& ka, int block, int seq) {
   const ScratchG s = scratch_of(a, seq);
   if (block == 0 && threadIdx.x == 0) {               // the round-end state the plan's walk computed
     const int64_t wb = s.info[kInfoWriteback];
+    const int64_t Lr = s.info[kInfoL];                 // with the rows the step appended
     if (ka.mode == 0) {
       *u.hand = (int32_t)s.info[kInfoNewHand];
       if (wb >= 0) u.dyn[1] = wb + ka.ring_rows;
+    } else {
+      u.dyn[1] = Lr;
     }
+    u.dyn[0] = Lr;
     u.dyn[2] = s.info[kInfoRound] + 1;
   }
   if ((int)block >= ka.word_blocks && (int)block < ka.word_blocks + ka.clear_blocks) {
@@ -79,7 +83,7 @@ __device__ inline void assign_block(const GatherKArgs& ka, int block, int seq) {
   }
   const int lane = threadIdx.x & 63;
   const int64_t wave_id = ((int64_t)block * kGatherThreads + threadIdx.x) >> 6;
-  const int64_t L = u.dyn[0];
+  const int64_t L = s.info[kInfoL];                   // (block 0 publishes it as the unit's L)
   const int64_t nw = (L + 31) / 32;
   if (2 * wave_id >= nw) return;
   const int64_t w = 2 * wave_id + (lane >> 5);        // this lane's 32-position word

@@ -30,6 +30,7 @@ constexpr int kPlanWaves = kPlanThreads / 64;
 struct PlanParams {
   int S, s_words, ring_rows, mode;
   int clock;          // CLOCK replacement (second chance with reference bits)
+  int add;            // rows appended by the step's first launch, not yet in the unit's L
 };
 
 // Bits of word w (positions 32w..32w+31) that lie at or above M.
@@ -209,6 +210,7 @@ __device__ inline PlanCounts plan_counts_block(const UnitG& u, const ScratchG& s
     s.info[kInfoRound] = round;
     s.info[kInfoM] = M;
     s.info[kInfoHand] = off ? ps.hand : 0;
+    s.info[kInfoL] = ps.L;
   }
   return PlanCounts{U, n_miss, n_ring, n_hit};
 }
@@ -414,7 +416,7 @@ __device__ inline void plan_if_last(const UnitG& u, const ScratchG& s, const Pla
 // launch: the round-start state and the counts from the step's info.
 template <int T>
 __device__ inline void plan_walk_from_info(const UnitG& u, const ScratchG& s, const PlanParams& pp, uint32_t* lds) {
-  const PlanState ps{u.dyn[0], s.info[kInfoM], (int32_t)s.info[kInfoRound], (int32_t)s.info[kInfoHand]};
+  const PlanState ps{s.info[kInfoL], s.info[kInfoM], (int32_t)s.info[kInfoRound], (int32_t)s.info[kInfoHand]};
   const PlanCounts pc{(uint32_t)s.info[kInfoUnion], (uint32_t)s.info[kInfoMiss], (uint32_t)s.info[kInfoRing],
                       (uint32_t)s.info[kInfoHit]};
   plan_walk_block<T>(u, s, pp, ps, pc, lds);
@@ -425,7 +427,7 @@ __device__ inline void plan_walk_from_info(const UnitG& u, const ScratchG& s, co
 // assign pass).
 template <int T>
 __device__ inline void plan_counts_and_walk(const UnitG& u, const ScratchG& s, const PlanParams& pp, uint32_t* lds) {
-  const PlanState ps{u.dyn[0], u.dyn[1], (int32_t)u.dyn[2], pp.mode == 0 ? *u.hand : 0};
+  const PlanState ps{u.dyn[0] + pp.add, u.dyn[1], (int32_t)u.dyn[2], pp.mode == 0 ? *u.hand : 0};
   const PlanCounts pc = plan_counts_block<T>(u, s, pp, ps);
   __syncthreads();
   plan_walk_block<T>(u, s, pp, ps, pc, lds);

@@ -174,7 +174,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   // entry need the union index, not the row's source.  A selected position is
   // a hit iff it was cached at round start.
   const bool own_counts = ka.plan == 2;
-  const int64_t L = u.dyn[0];
+  const int64_t L = step_L(u, a);
   const int64_t nw = own_counts ? (L + 31) / 32 : 0;     // within kAttnScanWords (the host's choice)
   uint32_t* cnt = reinterpret_cast<uint32_t*>(lat_s[1]);
   static_assert(kAttnScanWords * 4 <= (int64_t)sizeof(lat_s[1]), "the word counts fit a staging buffer");
@@ -663,7 +663,7 @@ hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_l
   AttnKArgs ka{a, q_lat, q_rope, out, g.top_k, g.heads, nsplit, g.nsplit_max, g.row_bytes,
                g.hot_slots, g.ring_cap, g.r_max * g.top_k, g.mode == 0 ? 1 : 0, g.max_positions,
                g.softmax_scale * 1.4426950408889634f, plan,
-               PlanParams{g.hot_slots, g.s_words, g.ring_rows, g.mode, g.clock ? 1 : 0}};
+               PlanParams{g.hot_slots, g.s_words, g.ring_rows, g.mode, g.clock ? 1 : 0, a.add}};
   // one workgroup past the splits of each (row, sequence): row 0's runs the plan's part
   dim3 grid((unsigned)nsplit + 1u, (unsigned)a.R, (unsigned)a.n_seqs);
   switch (g.heads) {

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void prefetch_fill_kernel(FillKArgs ka) {
 
 hipError_t launch_reuse_mark(const Geometry& g, const StepArgs& a, const SeqScratch& sel0, int64_t sel_stride,
                              hipStream_t st) {
-  MarkKArgs ka{a, sel0, sel_stride, g.top_k, g.mode, PlanParams{g.hot_slots, g.s_words, g.ring_rows, g.mode, g.clock ? 1 : 0}};
+  MarkKArgs ka{a, sel0, sel_stride, g.top_k, g.mode, PlanParams{g.hot_slots, g.s_words, g.ring_rows, g.mode, g.clock ? 1 : 0, 0}};
   return launch_k(reuse_mark_kernel, dim3((unsigned)a.R, (unsigned)a.n_seqs), dim3(kPlanThreads), 0, st, ka);
 }
 

@@ -42,9 +42,59 @@ struct ScoreKArgs {
   int64_t p_pad;
   int subs_per_wave;                    // 32-position sub-tiles per wave
   int r_max;
+  // an append-and-decode step (a.add rows per sequence); null otherwise
+  const uint16_t* app_keys;             // [n_seqs][add][128] bf16
+  const uint8_t* app_rows;              // [n_seqs][add][row_bytes]
+  int score_blocks;                     // workgroups per sequence that score; the rest append
+  int row_bytes, ring_cap, mode;
 };
 
 __device__ inline float canon0(float s) { return s == 0.0f ? 0.0f : s; }
+
+// The B fragments of 32-position tile `tile` (load k gives lane (n, half) dims
+// 64 half + 8 k .. +7 of key tile * 32 + n): from the key store, which holds
+// them in operand order, except the positions [Lo, L) the step appends, whose
+// keys come from the caller's buffer (row-major, 16 pieces a key).
+__device__ inline void load_tile(const DSA_GLOBAL bf16x8* keys16, int64_t tile, int lane, const bf16x8* app16,
+                                 int64_t Lo, int64_t L, bf16x8* b) {
+  if (app16 && tile * 32 + 32 > Lo) {                  // (uniform) the tile holds appended positions
+    const int64_t t = tile * 32 + (lane & 31);
+    const bool fresh = t >= Lo && t < L;
+    const bf16x8* kp = fresh ? app16 + (t - Lo) * 16 + 8 * (lane >> 5) : (const bf16x8*)(keys16 + tile * 512 + lane);
+    const int st = fresh ? 1 : 64;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) b[ks] = kp[ks * st];
+  } else {
+    const DSA_GLOBAL bf16x8* kp = keys16 + tile * 512 + lane;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) b[ks] = kp[ks * 64];
+  }
+}
+
+// An append-and-decode step's appended rows, by the workgroups past the scoring
+// ones: each key to its operand-order place in the key store, each row to the
+// ring (offload; the spill that makes room ran before) or the HBM row store.
+__device__ inline void append_block(const ScoreKArgs& ka, const UnitG& u, int seq, int block, int n_blocks) {
+  const int64_t Lo = u.dyn[0], M = u.dyn[1];
+  const int64_t n = ka.a.add, rb = ka.row_bytes;
+  const int64_t key_pieces = n * 16, total = key_pieces + n * kCopyChunks16;
+  const uint16_t* keys = ka.app_keys + (int64_t)seq * n * 128;
+  const uint8_t* rows = ka.app_rows + (int64_t)seq * n * rb;
+  for (int64_t t = (int64_t)block * blockDim.x + threadIdx.x; t < total; t += (int64_t)n_blocks * blockDim.x) {
+    if (t < key_pieces) {
+      const int64_t i = t / 16;
+      const int c = (int)(t % 16);
+      reinterpret_cast<DSA_GLOBAL u32x4*>(u.keys)[key_piece(Lo + i, c)] =
+          reinterpret_cast<const u32x4*>(keys)[t];
+    } else {
+      const int64_t w = t - key_pieces, i = w / kCopyChunks16, c = w % kCopyChunks16;
+      const int64_t p = Lo + i;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(rows + i * rb + c * 16);
+      const auto dst = (ka.mode == 1 || p < M) ? u.rows + p * rb : u.ring + (p % ka.ring_cap) * rb;
+      *reinterpret_cast<DSA_GLOBAL u32x4*>(dst + c * 16) = v;
+    }
+  }
+}
 
 // max(0, x) for a finite x as one integer max on its bits: a negative float
 // (-0 included) is a negative int32, and positive floats order as their bits.
@@ -85,8 +135,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 && HI >= 8 ? 3 : 1) void score_ker
   const StepArgs& a = ka.a;
   const int seq = blockIdx.y;
   const UnitG u = unit_of(a, seq);
+  if ((int)blockIdx.x >= ka.score_blocks) {            // (uniform) an appending workgroup
+    append_block(ka, u, seq, (int)blockIdx.x - ka.score_blocks, (int)gridDim.x - ka.score_blocks);
+    return;
+  }
   const ScratchG s = scratch_of(a, seq);
-  const int64_t L = u.dyn[0];
+  const int64_t L = step_L(u, a);
+  const int64_t Lo = L - a.add;                          // the appended positions [Lo, L)
+  const bf16x8* app16 = ka.app_keys ? reinterpret_cast<const bf16x8*>(ka.app_keys) + (int64_t)seq * a.add * 16 : nullptr;
   const int R = a.R;
   const int M = R * HI;
   const int MT = (M + 31) / 32;
@@ -122,11 +178,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 && HI >= 8 ? 3 : 1) void score_ker
   const int64_t last_tile = ka.p_pad / 32 - 1;
   const DSA_GLOBAL bf16x8* keys16 = reinterpret_cast<const DSA_GLOBAL bf16x8*>(u.keys);
   bf16x8 b[8];
-  {
-    const DSA_GLOBAL bf16x8* kp = keys16 + min(first_sub, last_tile) * 512 + lane;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) b[ks] = kp[ks * 64];
-  }
+  load_tile(keys16, min(first_sub, last_tile), lane, app16, Lo, L, b);
 
   for (int w = threadIdx.x; w < R * (kRadixBins / 2); w += blockDim.x) lh[w] = 0;
 #pragma unroll
@@ -146,11 +198,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 && HI >= 8 ? 3 : 1) void score_ker
     // The next tile's keys are requested before this tile is computed (loads
     // complete in issue order, so this tile's wait does not include them).
     bf16x8 bn[8];
-    if (si + 1 < ka.subs_per_wave) {
-      const DSA_GLOBAL bf16x8* kp = keys16 + min(first_sub + si + 1, last_tile) * 512 + lane;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) bn[ks] = kp[ks * 64];
-    }
+    if (si + 1 < ka.subs_per_wave) load_tile(keys16, min(first_sub + si + 1, last_tile), lane, app16, Lo, L, bn);
     // G row tiles at a time: independent accumulation chains, so the MFMA
     // pipeline is never waiting on one accumulator; the next k-step's A
     // fragments are read while this k-step's products run.
@@ -275,13 +323,18 @@ hipError_t prepare_score_kernels() {
 #undef DSA_SCORE_KERNELS
 
 hipError_t launch_score(const Geometry& g, const StepArgs& a, const uint16_t* q, const float* w,
-                        hipStream_t st) {
+                        const uint16_t* app_keys, const uint8_t* app_rows, hipStream_t st) {
   ScoreKArgs ka;
   ka.a = a;
   ka.q = q;
   ka.w = w;
   ka.p_pad = g.p_pad;
   ka.r_max = g.r_max;
+  ka.app_keys = a.add > 0 ? app_keys : nullptr;
+  ka.app_rows = a.add > 0 ? app_rows : nullptr;
+  ka.row_bytes = g.row_bytes;
+  ka.ring_cap = g.ring_cap;
+  ka.mode = g.mode;
   const int64_t subs = (a.l_max + 31) / 32;
   const int M = a.R * g.index_heads;
   // Eight waves for a large Q (more than 128 rows: one workgroup per CU) or a
@@ -295,12 +348,15 @@ hipError_t launch_score(const Geometry& g, const StepArgs& a, const uint16_t* q,
   if (spw > 8) spw = 8;
   ka.subs_per_wave = spw;
   const int64_t blocks = (subs + (int64_t)nw * spw - 1) / ((int64_t)nw * spw);
+  ka.score_blocks = (int)blocks;
+  const int64_t app_work = ka.app_keys ? (int64_t)a.add * (16 + kCopyChunks16) : 0;
+  const int64_t app_blocks = (app_work + nw * 64 - 1) / (nw * 64);
   const int MT = (M + 31) / 32;
   const int G = MT >= 4 ? 4 : MT >= 2 ? 2 : 1;         // row tiles per group (Q padded to whole groups)
   const int MTP = (MT + G - 1) / G * G;
   const size_t lds = (size_t)MTP * 32 * kQStride * sizeof(uint16_t) + (size_t)MTP * 32 * sizeof(float) +
                      (size_t)a.R * (kRadixBins / 2) * sizeof(uint32_t);
-  dim3 grid((unsigned)blocks, (unsigned)a.n_seqs), block(nw * 64);
+  dim3 grid((unsigned)(blocks + app_blocks), (unsigned)a.n_seqs), block(nw * 64);
 #define DSA_SCORE_G(HI, NW)                                                                  \
   (G == 4 ? launch_k(score_kernel<HI, NW, 4>, grid, block, lds, st, ka)                    \
           : G == 2 ? launch_k(score_kernel<HI, NW, 2>, grid, block, lds, st, ka)           \

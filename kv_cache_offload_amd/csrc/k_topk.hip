@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_digits_kernel(TopkKArgs ka, 
   const int r = blockIdx.x, seq = blockIdx.y;
   const UnitG u = unit_of(a, seq);
   const ScratchG s = scratch_of(a, seq);
-  const int64_t n_vis = u.dyn[0] - a.R + r + 1;
+  const int64_t n_vis = step_L(u, a) - a.R + r + 1;
   if (n_vis <= ka.K) return;
   const auto dig = reinterpret_cast<DSA_GLOBAL i32x4*>(s.rowdig + 4 * r);
   int b;
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kPartThreads) void topk_refine_kernel(TopkKArgs ka)
   const int chunk = blockIdx.x, r = blockIdx.y, seq = blockIdx.z;
   const UnitG u = unit_of(a, seq);
   const ScratchG s = scratch_of(a, seq);
-  const int64_t L = u.dyn[0];
+  const int64_t L = step_L(u, a);
   const int64_t n_vis = L - a.R + r + 1;
   const int64_t start = (int64_t)chunk * kTopkChunk;
   if (n_vis <= ka.K || start >= n_vis) return;
@@ -419,7 +419,7 @@ __device__ void final_row(const TopkKArgs& ka, const UnitG& u, const ScratchG& s
   // (the plan needs it too), the row's digits from the chunk pass, the chunk
   // list sizes (one chunk per thread at most) and this thread's bins of the
   // second-digit histogram.
-  const PlanState ps{u.dyn[0], u.dyn[1], (int32_t)u.dyn[2], ka.mode == 0 ? *u.hand : 0};
+  const PlanState ps{step_L(u, a), u.dyn[1], (int32_t)u.dyn[2], ka.mode == 0 ? *u.hand : 0};
   const i32x4 dig = *reinterpret_cast<const DSA_GLOBAL i32x4*>(s.rowdig + 4 * r);
   const uint32_t cnt_all = tid < ka.n_chunks ? s.cand_n[(int64_t)r * ka.n_chunks + tid] : 0u;
   uint32_t h1c[kRadixBins / kSelThreads];
@@ -512,7 +512,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_chunk_kernel(TopkKArgs ka) {
   const int chunk = blockIdx.x, r = blockIdx.y, seq = blockIdx.z, tid = threadIdx.x;
   const UnitG u = unit_of(a, seq);
   const ScratchG s = scratch_of(a, seq);
-  const int64_t L = u.dyn[0];
+  const int64_t L = step_L(u, a);
   const int64_t n_vis = L - a.R + r + 1;
   const int64_t start = (int64_t)chunk * kTopkChunk;
   if (n_vis > ka.K) {
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_final_kernel(TopkKArgs ka) {
 TopkKArgs topk_args(const Geometry& g, const StepArgs& a) {
   return TopkKArgs{a, g.p_pad, g.n_chunks, g.top_k, g.mode, g.r_max, a.l_max > kShortMax ? 1 : 0,
                    topk_plan_mode(g, a),
-                   PlanParams{g.hot_slots, g.s_words, g.ring_rows, g.mode, g.clock ? 1 : 0}};
+                   PlanParams{g.hot_slots, g.s_words, g.ring_rows, g.mode, g.clock ? 1 : 0, a.add}};
 }
 
 }  // namespace

@@ -806,10 +806,14 @@ dsa_status dsa_rollback_rows(dsa_session* s, int32_t layer, int32_t seq, int64_t
 extern "C++" {
 namespace {
 
-// Shared by both decode entry points: validation, then the step's launches on
-// the scratch set `a` names, then the host-side round bookkeeping.
-dsa_status decode_common(dsa_session* s, int32_t layer, int32_t R, const void* index_q, const float* index_w,
-                         const void* q_latent, const void* q_rope, float* out, hipStream_t stream, bool on_static) {
+// Shared by the decode entry points: validation, then the step's launches on
+// the scratch set `a` names, then the host-side round bookkeeping.  With
+// app_keys (an append-and-decode step) every sequence of the layer first gains
+// R rows, which the score launch writes (its scoring workgroups read the new
+// keys from app_keys); the round's assign pass publishes the new L.
+dsa_status decode_common(dsa_session* s, int32_t layer, int32_t R, const void* app_keys, const void* app_rows,
+                         const void* index_q, const float* index_w, const void* q_latent, const void* q_rope,
+                         float* out, hipStream_t stream, bool on_static) {
   dsa_status st = entry(s);
   if (st != DSA_OK) return st;
   if (layer < 0 || layer >= s->cfg.n_layers) return fail(s, DSA_E_INVALID, "layer out of range");
@@ -817,11 +821,37 @@ dsa_status decode_common(dsa_session* s, int32_t layer, int32_t R, const void* i
   if (!index_q || !index_w || !q_latent || !q_rope || !out || !aligned(index_q, 16) || !aligned(q_latent, 16) ||
       !aligned(q_rope, 16) || !aligned(index_w, 4) || !aligned(out, 4))
     return fail(s, DSA_E_INVALID, "step buffers must be non-NULL; bf16 inputs 16-byte aligned");
+  const bool app = app_keys != nullptr;
+  if (app && (!app_rows || !aligned(app_keys, 16) || !aligned(app_rows, 16)))
+    return fail(s, DSA_E_INVALID, "keys and rows to append must be non-NULL and 16-byte aligned");
   const int n_seqs = s->cfg.n_seqs;
-  for (int q = 0; q < n_seqs; ++q)
-    if (s->uh[unit_index(s, layer, q)].L < R) return fail(s, DSA_E_STATE, "a sequence holds fewer rows than rows_per_seq");
+  for (int q = 0; q < n_seqs; ++q) {
+    const UnitHost& h = s->uh[unit_index(s, layer, q)];
+    if (app && h.L + R > s->cfg.max_positions) return fail(s, DSA_E_CAPACITY, "append past max_positions");
+    if (!app && h.L < R) return fail(s, DSA_E_STATE, "a sequence holds fewer rows than rows_per_seq");
+  }
   const Geometry& g = s->g;
+  if (app) {
+    DeviceGuard dg(s->device);
+    if ((st = wait_prefetch(s, layer, stream)) != DSA_OK) return st;
+    // room in the ring for the new rows: its oldest rows to the mirror first, as an append would
+    for (int q = 0; q < n_seqs && g.mode == DSA_KV_OFFLOAD; ++q) {
+      const size_t ui = unit_index(s, layer, q);
+      UnitHost& h = s->uh[ui];
+      int64_t newM = h.M;
+      while (h.L + R - newM > g.ring_cap) newM += g.ring_rows;
+      if (newM == h.M) continue;
+      const int64_t to = std::min(newM, h.L);
+      HIPCHK(launch_flush(g, s->units[ui], h.M, to, stream), "ring spill kernel");
+      h.M = newM;
+      if ((st = note_mirror(s, h, stream)) != DSA_OK) return st;
+    }
+  }
   StepArgs a = step_args(s, layer, R, false);
+  if (app) {
+    a.add = R;
+    a.l_max += R;
+  }
   if (on_static) {
     const ScrOff lay = scratch_layout(g);
     const size_t need = lay.bytes * (size_t)n_seqs;
@@ -841,7 +871,11 @@ dsa_status decode_common(dsa_session* s, int32_t layer, int32_t R, const void* i
       HIPCHK(hipStreamWaitEvent(stream, s->pf_done[l], 0), "hipStreamWaitEvent");
   // the static array keeps the previous call's contents: zero what starts at zero
   if (on_static) HIPCHK(launch_clear_step_scratch(g, a, stream), "scratch clear kernel");
-  if ((st = timed_launch(s, KK_SCORE, "score kernel", [&] { return launch_score(g, a, iq, index_w, stream); })) != DSA_OK) return st;
+  if ((st = timed_launch(s, KK_SCORE, "score kernel", [&] {
+         return launch_score(g, a, iq, index_w, static_cast<const uint16_t*>(app_keys),
+                             static_cast<const uint8_t*>(app_rows), stream);
+       })) != DSA_OK)
+    return st;
   if ((st = timed_launch(s, KK_TOPK_PARTIAL, "top-k collect", [&] { return launch_topk_partial(g, a, stream); })) != DSA_OK)
     return st;
   if ((st = timed_launch(s, KK_TOPK_SELECT, "top-k resolve", [&] { return launch_topk_select(g, a, stream); })) != DSA_OK) return st;
@@ -852,6 +886,12 @@ dsa_status decode_common(dsa_session* s, int32_t layer, int32_t R, const void* i
   if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream, 2 - topk_plan_mode(g, a)); })) != DSA_OK) return st;
   if ((st = timed_launch(s, KK_MERGE, "attention merge and assign", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK)
     return st;
+  if (app)
+    for (int q = 0; q < n_seqs; ++q) {
+      UnitHost& h = s->uh[unit_index(s, layer, q)];
+      h.L += R;
+      if (g.mode != DSA_KV_OFFLOAD) h.M = h.L;
+    }
   s->last_layer = layer;
   s->last_R = R;
   s->last_static = on_static;
@@ -871,13 +911,26 @@ dsa_status decode_common(dsa_session* s, int32_t layer, int32_t R, const void* i
 dsa_status dsa_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq, const void* index_q,
                            const float* index_w, const void* q_latent, const void* q_rope, float* out,
                            hipStream_t stream) {
-  return decode_common(s, layer, rows_per_seq, index_q, index_w, q_latent, q_rope, out, stream, false);
+  return decode_common(s, layer, rows_per_seq, nullptr, nullptr, index_q, index_w, q_latent, q_rope, out, stream,
+                       false);
+}
+
+dsa_status dsa_append_decode_step(dsa_session* s, int32_t layer, int32_t rows_per_seq, const void* index_keys,
+                                  const void* rows, const void* index_q, const float* index_w, const void* q_latent,
+                                  const void* q_rope, float* out, hipStream_t stream) {
+  if (!index_keys) {
+    const dsa_status st = entry(s);
+    return st != DSA_OK ? st : fail(s, DSA_E_INVALID, "keys to append must be non-NULL");
+  }
+  return decode_common(s, layer, rows_per_seq, index_keys, rows, index_q, index_w, q_latent, q_rope, out, stream,
+                       false);
 }
 
 dsa_status dsa_decode_step_static(dsa_session* s, int32_t layer, int32_t rows_per_seq, const void* index_q,
                                   const float* index_w, const void* q_latent, const void* q_rope, float* out,
                                   hipStream_t stream) {
-  return decode_common(s, layer, rows_per_seq, index_q, index_w, q_latent, q_rope, out, stream, true);
+  return decode_common(s, layer, rows_per_seq, nullptr, nullptr, index_q, index_w, q_latent, q_rope, out, stream,
+                       true);
 }
 
 dsa_status dsa_decode_step_reuse(dsa_session* s, int32_t layer, int32_t src_layer, int32_t rows_per_seq,

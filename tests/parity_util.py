@@ -79,8 +79,10 @@ def step_inputs(w, layer, step, seqs=None, rows_fn=None, query_fn=None):
     return new, (stack(0), stack(1), stack(2), stack(3))
 
 
-def run_step(w, layer, step, sess=None, orcs=None, gpu_layer=None, seqs=None, rows_fn=None, query_fn=None):
-    """Append the step's rows and run one decode step on both sides.
+def run_step(w, layer, step, sess=None, orcs=None, gpu_layer=None, seqs=None, rows_fn=None, query_fn=None,
+             combined=False):
+    """Append the step's rows and run one decode step on both sides (combined: on the GPU side through
+    dsa_append_decode_step, one call for every sequence; the oracle still appends, then decodes).
     Returns (gpu_out numpy [n_seqs][R][H][512] or None, {seq: oracle_out})."""
     seqs = list(range(w.seqs) if seqs is None else seqs)
     new, (iq, iw, ql, qr) = step_inputs(w, layer, step, seqs, rows_fn, query_fn)
@@ -88,12 +90,18 @@ def run_step(w, layer, step, sess=None, orcs=None, gpu_layer=None, seqs=None, ro
     gout = None
     if sess is not None:
         torch = _torch()
-        for i, q in enumerate(seqs):
-            sess.append_rows(gl, q, dev_tensor(new[i][0], sess.device), dev_tensor(new[i][1], sess.device))
         out = torch.full((len(seqs), w.rows_per_step, w.heads, w.latent_dim), float("nan"),
                          dtype=torch.float32, device=sess.device)
-        sess.decode_step(gl, dev_tensor(iq, sess.device), dev_tensor(iw, sess.device),
-                         dev_tensor(ql, sess.device), dev_tensor(qr, sess.device), out)
+        q_dev = [dev_tensor(x, sess.device) for x in (iq, iw, ql, qr)]
+        if combined:
+            assert seqs == list(range(w.seqs)), "the combined call appends to every sequence"
+            keys = dev_tensor(np.stack([x[0] for x in new]), sess.device)
+            rows = dev_tensor(np.stack([x[1] for x in new]), sess.device)
+            sess.append_decode_step(gl, keys, rows, *q_dev, out)
+        else:
+            for i, q in enumerate(seqs):
+                sess.append_rows(gl, q, dev_tensor(new[i][0], sess.device), dev_tensor(new[i][1], sess.device))
+            sess.decode_step(gl, *q_dev, out)
         gout = out
     oout = {}
     if orcs is not None:

@@ -91,6 +91,7 @@ def test_abi_version_mismatch_and_nulls():
     assert K._lib.dsa_decode_step_reuse(None, 1, 0, 1, None, None, None, None) == K.E_INVALID
     assert K._lib.dsa_prefetch_reuse(None, 1, 0, 1, None) == K.E_INVALID
     assert K._lib.dsa_decode_step_static(None, 0, 1, None, None, None, None, None, None) == K.E_INVALID
+    assert K._lib.dsa_append_decode_step(None, 0, 1, None, None, None, None, None, None, None, None) == K.E_INVALID
 
 
 def test_config_rejects_unknown_replacement_policy():

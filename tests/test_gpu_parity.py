@@ -25,15 +25,17 @@ def _note(*a):
 
 
 def _run_and_compare(w, mode, steps, layers=(0,), seqs=None, rows_fn=None, query_fn=None, history_fn=None,
-                     warm=None, check_scores=True, replacement=0):
+                     warm=None, check_scores=True, replacement=0, combined=False, before_steps=None):
     seqs = list(range(w.seqs) if seqs is None else seqs)
     sess = gpu_session(w, mode, n_layers=len(layers), replacement=replacement)
     orcs = oracle_units(w, mode, layers=layers, seqs=seqs, replacement=replacement)
     load_history(w, sess, orcs, layers=layers, seqs=seqs, warm=warm, history_fn=history_fn)
+    if before_steps is not None:
+        before_steps(sess, orcs)
     for step in range(steps):
         for gl, l in enumerate(layers):
             gout, oout = run_step(w, l, step, sess, orcs, gpu_layer=gl, seqs=seqs, rows_fn=rows_fn,
-                                  query_fn=query_fn)
+                                  query_fn=query_fn, combined=combined)
             gnp = gout.cpu().numpy()
             for i, q in enumerate(seqs):
                 compare_unit(sess, orcs[(l, q)], gl, q, gnp[i], oout[q], check_scores=check_scores,
@@ -164,6 +166,51 @@ def test_ring_rows_and_writeback_over_many_steps():
         return S.bf16_bits(np.full(keys.shape, 8.0)), rows     # new keys score high for positive queries
     _note("ring + writeback")
     _run_and_compare(w, MODE_OFFLOAD, steps=70, rows_fn=rows_recent, query_fn=q_recent)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_append_and_decode_in_one_call(mode):
+    # dsa_append_decode_step against the oracle's append then decode, every step of the tiny workload
+    w = S.WORKLOADS["tiny"]
+    _note("append + decode in one call", mode)
+    _run_and_compare(w, mode, steps=w.steps, combined=True)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_append_and_decode_in_one_call_batched(mode):
+    # five sequences: each gets its own rows from the one call
+    w = S.WORKLOADS["batched_16x131k"].scaled(history=9000, seqs=5, hot_slots=1024, steps=3)
+    _note("append + decode in one call, batched", mode)
+    _run_and_compare(w, mode, steps=3, combined=True)
+
+
+def test_append_and_decode_in_one_call_ring_and_writeback():
+    # the ring and its 64-row writeback over 70 one-row steps, appended by the score launch; the new
+    # keys score high, so the rows just appended are selected from the ring in the same step
+    w = S.WORKLOADS["tiny"].scaled(history=300, rows_per_step=1, top_k=64, hot_slots=128, steps=70)
+
+    def rows_recent(w_, layer, seq, step):
+        keys, rows = S.step_rows(w_, layer, seq, step)
+        return S.bf16_bits(np.full(keys.shape, 8.0)), rows
+    _note("append + decode in one call, ring + writeback")
+    _run_and_compare(w, MODE_OFFLOAD, steps=70, rows_fn=rows_recent, combined=True)
+
+
+def test_append_and_decode_in_one_call_spills_the_ring_first():
+    # 66 rows appended after the warm start leave the ring too full for a step's 4 rows: the call
+    # writes the oldest 64 back to the mirror before the score launch appends
+    w = S.WORKLOADS["tiny"].scaled(history=2000, rows_per_step=4, hot_slots=512, steps=20)   # room for 66 more
+
+    def extra_rows(sess, orcs):
+        g = np.random.default_rng(5)
+        keys = S.bf16_bits(g.integers(-8, 8, (66, w.index_dim)).astype(float))
+        rows = S.make_rows(g, 66, w)
+        sess.append_rows(0, 0, dev_tensor(keys, sess.device), dev_tensor(rows, sess.device))
+        orcs[(0, 0)].append(keys, rows)
+        st = sess.unit_state(0, 0)
+        assert st["L"] - st["M"] == 66, st
+    _note("append + decode in one call, ring spill")
+    _run_and_compare(w, MODE_OFFLOAD, steps=3, combined=True, before_steps=extra_rows)
 
 
 @pytest.mark.parametrize("mode", MODES)
