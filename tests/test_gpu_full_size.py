@@ -1,7 +1,8 @@
 """GPU parity at the full workload sizes, through the C ABI, against the CPU oracle.
 
 The first decode steps of each workload at its real shape: the same sessions,
-kernels and launch configurations `bench.py` times.  Every item the oracle keeps
+kernels and launch configurations `bench.py` times (its steps append and decode
+in one dsa_append_decode_step call; some cases here take the two-call form).  Every item the oracle keeps
 is compared (scores, selections, union, map, compact bytes, counters, slot
 table, outputs).  The 78-layer stress workload compares every layer against the oracle
 on its first step, in both modes, with the planted hit and miss counts checked
@@ -42,7 +43,7 @@ def _load(w, sess, orcs, layers, seqs, gpu_layers=None):
             sess.warm_hot(gl, q)
 
 
-def _full_size(name, mode, steps):
+def _full_size(name, mode, steps, combined=True):
     w = S.WORKLOADS[name]
     t0 = time.time()
     seqs = list(range(w.seqs))
@@ -51,7 +52,7 @@ def _full_size(name, mode, steps):
     _load(w, sess, orcs, (0,), seqs)
     _note(name, f"mode={mode} loaded in {time.time() - t0:.1f} s")
     for step in range(steps):
-        gout, oout = run_step(w, 0, step, sess, orcs, seqs=seqs)
+        gout, oout = run_step(w, 0, step, sess, orcs, seqs=seqs, combined=combined)
         gnp = gout.cpu().numpy()
         for i, q in enumerate(seqs):
             compare_unit(sess, orcs[(0, q)], 0, q, gnp[i], oout[q], what=f"{name} mode={mode} seq={q} step={step}")
@@ -66,7 +67,12 @@ def test_million_history_offload():
 
 
 def test_million_history_resident():
-    _full_size("million", MODE_RESIDENT, steps=1)
+    _full_size("million", MODE_RESIDENT, steps=1, combined=False)
+
+
+@pytest.mark.parametrize("mode", [MODE_OFFLOAD, MODE_RESIDENT], ids=["offload", "resident"])
+def test_single_stream_50k_append_and_decode_in_one_call(mode):
+    _full_size("single_stream_50k", mode, steps=3)
 
 
 def test_batched_16x131k_offload():
@@ -77,7 +83,8 @@ def _stress_every_layer(mode):
     # Every layer is loaded and stepped once with the oracle beside it (the oracle unit is
     # dropped after its comparison, except for three layers kept for a second step);
     # then every layer steps again, with the planted hit/miss counts checked on all of
-    # them (offload) and the kept layers compared in full.
+    # them (offload) and the kept layers compared in full.  The first step appends with
+    # dsa_append_rows, the second in the dsa_append_decode_step call.
     w = S.WORKLOADS["stress_78_layers"]
     t0 = time.time()
     kept = (0, 41, 77)
@@ -98,7 +105,7 @@ def _stress_every_layer(mode):
         if l % 13 == 12:
             _note(f"stress mode={mode}: layers 0..{l} match at step 0 ({time.time() - t0:.1f} s)")
     for l in range(w.layers):
-        gout, oout = run_step(w, l, 1, sess, orcs if l in kept else None)
+        gout, oout = run_step(w, l, 1, sess, orcs if l in kept else None, combined=True)
         if mode == MODE_OFFLOAD:
             cnt = sess.debug("counters", l, 0).cpu().numpy().view(np.int64)
             assert (int(cnt[1]), int(cnt[3])) == (2028, 80), f"layer {l} step 1: counters {cnt}"
@@ -194,5 +201,14 @@ def test_append_past_capacity_is_refused_without_change():
     assert e.value.status == K.E_CAPACITY
     assert sess.unit_state(0, 0)["L"] == 100
     sess.append_rows(0, 0, dev_tensor(k3[:2], sess.device), dev_tensor(r3[:2], sess.device))   # exactly full
+    assert sess.unit_state(0, 0)["L"] == 102
+    # the one-call step refuses rows past max_positions before it enqueues anything
+    import torch
+    iq, iw, ql, qr = (dev_tensor(x[None], sess.device) for x in S.step_queries(w, 0, 0, 0))
+    out = torch.zeros((1, 1, w.heads, w.latent_dim), dtype=torch.float32, device=sess.device)
+    with pytest.raises(K.DsaError) as e:
+        sess.append_decode_step(0, dev_tensor(k3[None, 2:3], sess.device), dev_tensor(r3[None, 2:3], sess.device),
+                                iq, iw, ql, qr, out)
+    assert e.value.status == K.E_CAPACITY
     assert sess.unit_state(0, 0)["L"] == 102
     sess.close()
