@@ -24,6 +24,13 @@
 // radix digit (top 11 bits of the order-preserving key) of every visible score
 // per query row, in packed 16-bit LDS counters, and adds them to the row's
 // global histogram -- the first pass of the exact Top-K.
+//
+// In an append-and-decode step the launch also appends the step's rows (the
+// new rows enter the history before it is scored: page as above, section
+// "Decision 3", the recent ring): workgroups past the scoring ones write the
+// new keys into the key store and the new rows into the ring or the row store,
+// and the scoring workgroups read the new positions' keys from the caller's
+// buffer instead of the key store.
 #include "dsa_internal.h"
 
 namespace dsa {
