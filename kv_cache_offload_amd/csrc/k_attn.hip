@@ -121,14 +121,23 @@ __device__ inline bf16x4 read_tr(const uint16_t* lat_s, int r0, int col0, int la
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS bf16x4*)(DSA_LDS void*)p);
 }
 
-// One workgroup: one query row, all H = NW*16 heads, NBLK * 32 selected rows
+// One workgroup: one query row, all H = HG*16 heads, NBLK * 32 selected rows
 // (a split), staged in 32-row blocks through two LDS buffers.  Split s takes
 // the row's selected indices s, s + nsplit, s + 2 nsplit, ...: the host-mirror
 // reads of a row's misses (old positions, early in the ascending selection)
 // spread over all its workgroups instead of loading its first splits.
-template <int NW, int NBLK>
-__global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
+// DS waves share each group of 16 heads: every one of them forms the group's
+// logits and softmax (the same instructions on the same operands, so the same
+// values), and wave (head group hg, part dh) accumulates output dims
+// [512 dh / DS, 512 (dh + 1) / DS).  With DS = 2 a wave holds half the output
+// accumulators, two waves fit a SIMD, and the staging has twice the threads.
+template <int HG, int DS, int NBLK>
+__global__ __launch_bounds__(HG * DS * 64) void attn_kernel(AttnKArgs ka) {
+  constexpr int NW = HG * DS;
   constexpr int NT = NW * 64;
+  constexpr int NTD = 32 / DS;                           // 16-dim output tiles of a wave
+  constexpr int GD = 8 / DS;                             // 64-dim scale groups of a wave's output dims
+  static_assert(DS == 1 || DS == 2, "one or two waves per head group");
   constexpr int kSplit = NBLK * kBlk;                    // this kernel's split
   static_assert(kSplit <= NT, "one thread per row of the split reads its source");
   constexpr int PPT = (kBlkPieces + NT - 1) / NT;        // row pieces per thread per block
@@ -139,6 +148,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   __shared__ int s_ux[kSplit];                            // its compact row, -1 if masked
   __shared__ uint32_t s_scan[NW];
   __shared__ uint32_t s_host;                             // any row of the split read from the host mirror
+  __shared__ float s_amax[NW][16];                        // per wave: its heads' largest |O| (DS > 1)
 
   const StepArgs& a = ka.a;
   const int split = blockIdx.x, r = blockIdx.y, seq = blockIdx.z;
@@ -152,7 +162,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, q4 = lane >> 4;
   const int H = ka.H;
-  const int h0 = wave * 16;
+  const int hg = DS == 1 ? wave : wave % HG;             // head group
+  const int dh = DS == 1 ? 0 : wave / HG;                // part of the output dims
+  const int h0 = hg * 16;
   const int64_t rb = ka.row_bytes;
 
   // The split's rows: position (selection), then the row's place in the
@@ -175,39 +187,40 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   // a hit iff it was cached at round start.
   const bool own_counts = ka.plan == 2;
   const int64_t L = step_L(u, a);
+  const int64_t M = own_counts ? u.dyn[1] : s.info[kInfoM];   // the ring boundary at round start
   const int64_t nw = own_counts ? (L + 31) / 32 : 0;     // within kAttnScanWords (the host's choice)
   uint32_t* cnt = reinterpret_cast<uint32_t*>(lat_s[1]);
   static_assert(kAttnScanWords * 4 <= (int64_t)sizeof(lat_s[1]), "the word counts fit a staging buffer");
-  if (own_counts) {
-    constexpr int kLoads = (int)((kAttnScanWords / 4 + NT - 1) / NT);
-    u32x4 wv[kLoads];
+  // The split's selected positions are requested first and the union words
+  // (own counts) behind them, all unconditionally (indices clamped into the
+  // buffers): the words' round trip then overlaps the positions', and the
+  // loads of the rows' sources wait for the positions only.
+  const int j = split + tid * ka.nsplit;
+  int32_t pos = -1;
+  if (tid < kSplit) pos = s.sel[(int64_t)r * ka.K + min(j, ka.K - 1)];
+  constexpr int kLoads = (int)((kAttnScanWords / 4 + NT - 1) / NT);
+  u32x4 wv[kLoads];
+  if (own_counts) {                                      // (uniform)
+    const int64_t last = (nw + 3) / 4 - 1;              // the last 4-word piece holding a word
 #pragma unroll
-    for (int e = 0; e < kLoads; ++e) {
-      const int64_t q = tid + (int64_t)e * NT;          // 4-word piece
-      wv[e] = 4 * q < nw ? reinterpret_cast<const DSA_GLOBAL u32x4*>(s.selmask)[q] : (u32x4){0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int e = 0; e < kLoads; ++e) {
-      const int64_t q = tid + (int64_t)e * NT;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * q + i < nw) cnt[4 * q + i] = __popc(wv[e][i]);
-    }
+    for (int e = 0; e < kLoads; ++e)
+      wv[e] = reinterpret_cast<const DSA_GLOBAL u32x4*>(s.selmask)[min(tid + (int64_t)e * NT, last)];
   }
   bool host = false;                                     // this row is read from the host mirror
   bool live = false;                                     // this row's source is known (own counts: ux pending)
+  int map_v = -2;                                        // its map entry, stored once the rows are requested
+                                                         // (-2: none, or own counts: after the scan)
   uint32_t t_sw = 0, t_below = 0;                        // its selection word and the bits below it
   int64_t t_w = 0;
   if (tid < kSplit) {
-    const int64_t M = own_counts ? u.dyn[1] : s.info[kInfoM];
-    const int j = split + tid * ka.nsplit;
-    const int32_t pos = j < ka.K ? s.sel[(int64_t)r * ka.K + j] : -1;
+    if (j >= ka.K) pos = -1;
     const bool ok = j < n_sel && pos >= 0 && pos < ka.max_positions && (!own_counts || pos < L);
     const int64_t w = ok ? pos >> 5 : 0;
     const uint32_t sw = s.selmask[w];
-    const uint32_t hw = !ka.off ? 0u : own_counts ? (u.hot[w] & sw) : s.hitmask[w];
+    const uint32_t hraw = !ka.off ? 0u : own_counts ? u.hot[w] : s.hitmask[w];
     const uint32_t bu = own_counts ? 0u : s.base_u[w];
     const i32x2 ps = ka.off ? u.pos_slot[ok ? pos : 0] : (i32x2){-1, -1};
+    const uint32_t hw = own_counts ? (hraw & sw) : hraw;   // (after every load is issued)
     const uint32_t bit = 1u << (pos & 31), below = bit - 1u;
     const uint32_t ux = bu + __popc(sw & below);
     const DSA_GLOBAL uint8_t* from = nullptr;
@@ -240,20 +253,38 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     t_w = w;
     if (!own_counts) {
       s_ux[tid] = from ? (int)ux : -1;
-      if (j < ka.K) s.map[(int64_t)r * ka.K + j] = from ? (int)ux : -1;
+      if (j < ka.K) map_v = from ? (int)ux : -1;
     } else if (!from && j < ka.K) {
-      s.map[(int64_t)r * ka.K + j] = -1;
+      map_v = -1;
     }
   }
+  if (own_counts) {                                      // (uniform) the union words counted into LDS
+#pragma unroll
+    for (int e = 0; e < kLoads; ++e) {
+      const int64_t q = tid + (int64_t)e * NT;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * q + i < nw) cnt[4 * q + i] = __popc(wv[e][i]);
+    }
+  }
+  uint64_t host_bits = 0;
   if (wave == 0) {                                       // the split's host-mirror reads (one wave holds its rows)
-    const uint64_t hb = __ballot(host);
-    if (lane == 0) s_host = hb ? 1u : 0u;
-    if (lane == 0 && hb) {
-      g_add(&s.counters[8], (int64_t)__popcll(hb));
-      g_add(&u.totals[8], (int64_t)__popcll(hb));
-    }
+    host_bits = __ballot(host);
+    if (lane == 0) s_host = host_bits ? 1u : 0u;
   }
-  if (split >= n_sel) return;                            // (uniform) map entries written above
+  // The map entries and the host-read counts are stored after the rows are
+  // requested: a store ahead of the row loads would be waited for first.
+  auto store_map_and_counts = [&]() {
+    if (map_v != -2) s.map[(int64_t)r * ka.K + j] = map_v;
+    if (lane == 0 && host_bits) {
+      g_add(&s.counters[8], (int64_t)__popcll(host_bits));
+      g_add(&u.totals[8], (int64_t)__popcll(host_bits));
+    }
+  };
+  if (split >= n_sel) {                                  // (uniform) nothing to attend: the map entries only
+    store_map_and_counts();
+    return;
+  }
 
   // Query fragments (B operand of the logits): lane holds Q[h0 + l16][32 ks + 8 q4 .. +7].
   bf16x8 qa[18];
@@ -290,6 +321,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   const bool early = NBLK > 1 && !s_host;                // (uniform)
   request(0);
   if (early) request(1);
+  store_map_and_counts();
   if (own_counts) {                                      // (uniform) the union indices, while the rows arrive
     const int64_t per = (nw + NT - 1) / NT;
     const int64_t c0 = min(nw, (int64_t)tid * per), c1 = min(nw, c0 + per);
@@ -317,9 +349,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     __syncthreads();                                     // s_ux before block 0 is staged
   }
 
-  f32x4 o[32];
+  f32x4 o[NTD];                                          // o[nt]: output dims 16 (NTD dh + nt) ..
 #pragma unroll
-  for (int i = 0; i < 32; ++i) o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NTD; ++i) o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;                  // of head h0 + l16
 
 #pragma unroll
@@ -436,7 +468,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
       for (int v = 0; v < 4; ++v) {
         const float av = __shfl(alpha, 4 * q4 + v);
 #pragma unroll
-        for (int nt = 0; nt < 32; ++nt) o[nt][v] *= av;
+        for (int nt = 0; nt < NTD; ++nt) o[nt][v] *= av;
       }
     }
 
@@ -444,7 +476,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     // head h0 + l16 holds rows {4 q4 .. 4 q4 + 3, 16 + 4 q4 .. 16 + 4 q4 + 3}, in
     // that order; the B fragments (LDS transpose reads) match it.
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
+    for (int gl = 0; gl < GD; ++gl) {
+      const int g = GD * dh + gl;                        // the 64-dim group (its scale)
       bf16x8 pa_hi, pa_lo;
       {
         const f32x4 sa = *reinterpret_cast<const f32x4*>(scl + g * kBlk + 4 * q4);
@@ -466,9 +499,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
       }
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) {
-        const int nt = 4 * g + t4;
-        const bf16x4 b0 = read_tr(lat, 4 * q4, 16 * nt, lane);
-        const bf16x4 b1 = read_tr(lat, 16 + 4 * q4, 16 * nt, lane);
+        const int nt = 4 * gl + t4, col = 16 * (4 * g + t4);
+        const bf16x4 b0 = read_tr(lat, 4 * q4, col, lane);
+        const bf16x4 b1 = read_tr(lat, 16 + 4 * q4, col, lane);
         const bf16x8 bv = (bf16x8){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, bv, o[nt], 0, 0, 0);
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, bv, o[nt], 0, 0, 0);
@@ -477,15 +510,15 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
   }
   const float mx = m_run, ps = l_run;
 
-  // o[nt][v] = O[h0 + 4 q4 + v][16 nt + l16]; (max, sum) of head h0 + l16 in every lane group
+  // o[nt][v] = O[h0 + 4 q4 + v][16 (NTD dh + nt) + l16]; (max, sum) of head h0 + l16 in every lane group
   if (ka.nsplit == 1) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const float den = __shfl(ps, 4 * q4 + v);
       const float inv = den > 0.f ? 1.f / den : 0.f;
-      float* dst = ka.out + (((int64_t)seq * a.R + r) * H + h0 + 4 * q4 + v) * 512;
+      float* dst = ka.out + (((int64_t)seq * a.R + r) * H + h0 + 4 * q4 + v) * 512 + 16 * NTD * dh;
 #pragma unroll
-      for (int nt = 0; nt < 32; ++nt) dst[nt * 16 + l16] = o[nt][v] * inv;
+      for (int nt = 0; nt < NTD; ++nt) dst[nt * 16 + l16] = o[nt][v] * inv;
     }
   } else {
     // The split's partial, normalised (y = O / sum, a weighted mean of the
@@ -494,17 +527,34 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     // half the bytes of fp32 for the merge to read.  Layout
     // [r][split][wave][nt][l16][16 heads]: a wave's store covers 512 contiguous
     // bytes per nt (whole lines); the lane's four heads are contiguous.
+    // The DS waves of a head group take the largest |O| over all 512 dims, so
+    // they agree on each head's scale.
     f32x4 amax = (f32x4){0.f, 0.f, 0.f, 0.f};        // per head, of the unnormalised O
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt)
+    for (int nt = 0; nt < NTD; ++nt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) amax[v] = fmaxf(amax[v], fabsf(o[nt][v]));
+    if constexpr (DS > 1) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int sh = 1; sh < 16; sh <<= 1) amax[v] = fmaxf(amax[v], __shfl_xor(amax[v], sh));
+      if (l16 == 0)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s_amax[wave][4 * q4 + v] = amax[v];
+      __syncthreads();
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int d = 0; d < DS; ++d) amax[v] = fmaxf(amax[v], s_amax[hg + HG * d][4 * q4 + v]);
+    }
     float scv[4], mul[4];                            // the scale, and 1 / sum times the scale
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       float m = amax[v];
+      if constexpr (DS == 1)
 #pragma unroll
-      for (int sh = 1; sh < 16; sh <<= 1) m = fmaxf(m, __shfl_xor(m, sh));
+        for (int sh = 1; sh < 16; sh <<= 1) m = fmaxf(m, __shfl_xor(m, sh));
       const float den = __shfl(ps, 4 * q4 + v);      // the sum of head h0 + 4 q4 + v
       const float inv = den > 0.f ? 1.f / den : 0.f;
       int ex = 0;
@@ -512,9 +562,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
       scv[v] = ex > 15 ? ldexpf(1.f, 15 - ex) : 1.f;
       mul[v] = inv * scv[v];
     }
-    const auto dst = s.part_o + ((((int64_t)r * ka.ns_stride + split) * NW + wave) * 32 * 16 + l16) * 16 + 4 * q4;
+    const auto dst = s.part_o + ((((int64_t)r * ka.ns_stride + split) * HG + hg) * 32 * 16 + l16) * 16 + 4 * q4 +
+                     (int64_t)NTD * dh * 16 * 16;
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt) {
+    for (int nt = 0; nt < NTD; ++nt) {
       u32x2 w;
       w.x = pack_f16(o[nt][0] * mul[0], o[nt][1] * mul[1]);
       w.y = pack_f16(o[nt][2] * mul[2], o[nt][3] * mul[3]);
@@ -524,7 +575,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnKArgs ka) {
     const float s0 = __shfl(scv[0], 16 * (l16 >> 2)), s1 = __shfl(scv[1], 16 * (l16 >> 2));
     const float s2 = __shfl(scv[2], 16 * (l16 >> 2)), s3 = __shfl(scv[3], 16 * (l16 >> 2));
     const float sc = (l16 & 3) == 0 ? s0 : (l16 & 3) == 1 ? s1 : (l16 & 3) == 2 ? s2 : s3;
-    if (q4 == 0) {
+    if (q4 == 0 && dh == 0) {
       const int64_t base = ((int64_t)r * ka.ns_stride + split) * H + h0 + l16;
       *reinterpret_cast<DSA_GLOBAL f32x4*>(s.part_ml + base * 4) = (f32x4){mx, ps, 1.f / sc, 0.f};
     }
@@ -666,11 +717,12 @@ hipError_t launch_attn(const Geometry& g, const StepArgs& a, const uint16_t* q_l
                PlanParams{g.hot_slots, g.s_words, g.ring_rows, g.mode, g.clock ? 1 : 0, a.add}};
   // one workgroup past the splits of each (row, sequence): row 0's runs the plan's part
   dim3 grid((unsigned)nsplit + 1u, (unsigned)a.R, (unsigned)a.n_seqs);
+  // Two waves per head group where that keeps a workgroup within 512 threads.
   switch (g.heads) {
-    case 16: return launch_k(attn_kernel<1, 2>, grid, dim3(64), 0, st, ka);
-    case 32: return launch_k(attn_kernel<2, 2>, grid, dim3(128), 0, st, ka);
-    case 64: return launch_k(attn_kernel<4, 2>, grid, dim3(256), 0, st, ka);
-    case 128: return launch_k(attn_kernel<8, 2>, grid, dim3(512), 0, st, ka);
+    case 16: return launch_k(attn_kernel<1, 2, 2>, grid, dim3(128), 0, st, ka);
+    case 32: return launch_k(attn_kernel<2, 2, 2>, grid, dim3(256), 0, st, ka);
+    case 64: return launch_k(attn_kernel<4, 2, 2>, grid, dim3(512), 0, st, ka);
+    case 128: return launch_k(attn_kernel<8, 1, 2>, grid, dim3(512), 0, st, ka);
     default: return hipErrorInvalidValue;
   }
 }
