@@ -86,6 +86,13 @@ struct dsa_session {
   std::vector<int64_t> topk_L;             // per sequence: L at that step
   hipEvent_t sel_ready = nullptr;          // recorded after that step's Top-K (its selection is final)
   int64_t sel_epoch = 0;                   // full decode steps so far
+  // An event recorded between two kernels costs the step a few µs (the next
+  // kernel starts later), so a step records sel_ready only once the session
+  // has prefetched; until then a prefetch orders itself after everything the
+  // step's stream had enqueued (sel_stream), the whole step included.
+  bool pf_used = false;
+  int64_t sel_recorded_epoch = -1;         // the epoch whose sel_ready is recorded
+  hipStream_t sel_stream = nullptr;        // the stream of the most recent full decode step
   hipStream_t sel_waited = nullptr;        // the stream that already waits for this epoch's selection
   int64_t sel_waited_epoch = -1;
   std::vector<hipEvent_t> pf_done;         // per layer: recorded after its prefetch round
@@ -880,8 +887,12 @@ dsa_status decode_common(dsa_session* s, int32_t layer, int32_t R, const void* a
     return st;
   if ((st = timed_launch(s, KK_TOPK_SELECT, "top-k resolve", [&] { return launch_topk_select(g, a, stream); })) != DSA_OK) return st;
   if (!on_static) {
-    HIPCHK(hipEventRecord(s->sel_ready, stream), "hipEventRecord");
     s->sel_epoch += 1;
+    s->sel_stream = stream;
+    if (s->pf_used) {
+      HIPCHK(hipEventRecord(s->sel_ready, stream), "hipEventRecord");
+      s->sel_recorded_epoch = s->sel_epoch;
+    }
   }
   if ((st = timed_launch(s, KK_ATTN, "attention", [&] { return launch_attn(g, a, ql, qr, out, stream, 2 - topk_plan_mode(g, a)); })) != DSA_OK) return st;
   if ((st = timed_launch(s, KK_MERGE, "attention merge and assign", [&] { return launch_attn_merge(g, a, out, stream); })) != DSA_OK)
@@ -967,6 +978,11 @@ dsa_status dsa_prefetch_reuse(dsa_session* s, int32_t layer, int32_t src_layer, 
   DeviceGuard dg(s->device);
   const StepArgs a = step_args(s, layer, rows_per_seq, true);
   const Geometry& g = s->g;
+  s->pf_used = true;
+  if (s->sel_recorded_epoch != s->sel_epoch) {         // the step did not record it: everything it enqueued
+    HIPCHK(hipEventRecord(s->sel_ready, s->sel_stream), "hipEventRecord");
+    s->sel_recorded_epoch = s->sel_epoch;
+  }
   if (s->sel_waited != stream || s->sel_waited_epoch != s->sel_epoch) {   // the selection is final
     HIPCHK(hipStreamWaitEvent(stream, s->sel_ready, 0), "hipStreamWaitEvent");
     s->sel_waited = stream;
