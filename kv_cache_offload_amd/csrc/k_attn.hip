@@ -633,31 +633,41 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
   if (used < 1) return;                                  // (uniform) no selection: nothing to merge
   const int tid = threadIdx.x;
   const int e0 = tid * EPT, l16 = e0 / HW, hl0 = e0 % HW;
-  // this thread's elements of every split, loaded before the weights are known
-  // (splits past `used` re-read the last one and get weight 0)
+  // Every split's (max, sum, 1 / scale) of the workgroup's heads is requested
+  // first, then this thread's elements of every split (splits past `used`
+  // re-read the last one and get weight 0): loads complete in issue order, so
+  // the weights are formed while the elements are still arriving.
   static_assert(EPT <= 2, "a thread's elements lie in one attention wave's tile");
+  constexpr int kMl = (MAXS * HW + 255) / 256;          // (max, sum, 1 / scale) loads per thread
+  // (every address first: the loads then issue back to back)
+  const DSA_GLOBAL f32x4* mlp[kMl];
+#pragma unroll
+  for (int e = 0; e < kMl; ++e) {
+    const int t = tid + 256 * e;
+    const int sp = min(t / HW, used - 1), h = t % HW;
+    mlp[e] = reinterpret_cast<const DSA_GLOBAL f32x4*>(s.part_ml) + ((int64_t)r * ka.ns_stride + sp) * H + HW * hg + h;
+  }
   const int hh = HW * hg + hl0;                          // the thread's first head
   const auto src = s.part_o + (((int64_t)r * ka.ns_stride * (H / 16) + hh / 16) * 32 + nt) * 256 + l16 * 16 + hh % 16;
   const int64_t split_stride = (int64_t)32 * 16 * H;
-  float x[MAXS][EPT];
+  f32x4 mlv[kMl];
+#pragma unroll
+  for (int e = 0; e < kMl; ++e) mlv[e] = *mlp[e];
+  uint32_t xr[MAXS];                                     // fp16 bits (two heads per word when EPT == 2)
 #pragma unroll
   for (int sp = 0; sp < MAXS; ++sp) {
     const auto at = src + (sp < used ? sp : used - 1) * split_stride;
-    if constexpr (EPT == 2) {
-      const uint32_t v = *reinterpret_cast<const DSA_GLOBAL uint32_t*>(at);
-      x[sp][0] = f16_bits_to_f32(v & 0xFFFFu);
-      x[sp][1] = f16_bits_to_f32(v >> 16);
-    } else {
-      x[sp][0] = f16_bits_to_f32(*at);
-    }
+    if constexpr (EPT == 2) xr[sp] = *reinterpret_cast<const DSA_GLOBAL uint32_t*>(at);
+    else xr[sp] = *at;
   }
-  for (int t = tid; t < used * HW; t += 256) {           // every split's (max, sum, 1 / scale) at once
-    const int sp = t / HW, h = t % HW;
-    const int64_t base = ((int64_t)r * ka.ns_stride + sp) * H + HW * hg + h;
-    const f32x4 ml = *reinterpret_cast<const DSA_GLOBAL f32x4*>(s.part_ml + base * 4);
-    wgt[t] = ml[0];
-    sl[t] = ml[1];
-    isc[t] = ml[2];
+#pragma unroll
+  for (int e = 0; e < kMl; ++e) {
+    const int t = tid + 256 * e;
+    if (t < used * HW) {
+      wgt[t] = mlv[e][0];
+      sl[t] = mlv[e][1];
+      isc[t] = mlv[e][2];
+    }
   }
   __syncthreads();
   {
@@ -697,7 +707,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeKArgs ka) {
   for (int k = 0; k < EPT; ++k) {
     float acc = 0.f;
 #pragma unroll
-    for (int sp = 0; sp < MAXS; ++sp) acc += (sp < used ? wgt[sp * HW + hl0 + k] : 0.f) * x[sp][k];
+    for (int sp = 0; sp < MAXS; ++sp)
+      acc += (sp < used ? wgt[sp * HW + hl0 + k] : 0.f) * f16_bits_to_f32(k == 0 ? (xr[sp] & 0xFFFFu) : (xr[sp] >> 16));
     tile[(hl0 + k) * 17 + l16] = acc;
   }
   __syncthreads();
