@@ -340,7 +340,11 @@ dsa_status dsa_decode_step_reuse(dsa_session* s, int32_t layer, int32_t src_laye
  * library orders it with events of its own: `stream` first waits for an event
  * recorded right after the source step's Top-K (once per selection and
  * stream), so the prefetch may be enqueued as soon as dsa_decode_step has
- * returned and overlaps that step's gather, attention and merge; the layer's
+ * returned and overlaps that step's gather, attention and merge.  A session
+ * records that event in its steps only once it has prefetched (an event
+ * between two launches delays the next one by a few µs): the session's first
+ * prefetch waits instead for everything the source step's stream had enqueued
+ * when the prefetch was called.  The layer's
  * dsa_decode_step_reuse waits for the prefetch's completion event when it runs
  * on another stream; the next dsa_decode_step waits for every prefetch still
  * pending on another stream, since it replaces the selection they read.
