@@ -147,9 +147,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 && HI >= 8 ? 3 : 1) void score_ker
     return;
   }
   const ScratchG s = scratch_of(a, seq);
-  const int64_t L = step_L(u, a);
-  const int64_t Lo = L - a.add;                          // the appended positions [Lo, L)
-  const bf16x8* app16 = ka.app_keys ? reinterpret_cast<const bf16x8*>(ka.app_keys) + (int64_t)seq * a.add * 16 : nullptr;
+  const int64_t L = step_L(u, a);                        // requested first; the key loads wait for it only
   const int R = a.R;
   const int M = R * HI;
   const int MT = (M + 31) / 32;
@@ -163,8 +161,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 && HI >= 8 ? 3 : 1) void score_ker
   const int hf = lane >> 5;
   const int64_t first_sub = ((int64_t)blockIdx.x * kWaves + wave) * ka.subs_per_wave;
 
-  // Q (zero padded to MTP*32 rows) and the head weights, staged in LDS below;
-  // every load issued before the first is used (M <= 256: at most 16 per thread).
+  // Q (zero padded to MTP*32 rows) and the head weights, staged in LDS below.
+  // They are requested right behind L, and without a branch per load: a padding piece reads row 0 and is zeroed where it is
+  // staged, so no load waits for another (M <= 256: at most 16 per thread).
   const uint16_t* qg = ka.q + (int64_t)seq * M * 128;
   const int nq = MTP * 32 * 16;                          // 16-byte pieces of the padded Q
   bf16x8 qv[kMaxQPieces];
@@ -172,10 +171,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 && HI >= 8 ? 3 : 1) void score_ker
   for (int e = 0; e < kMaxQPieces; ++e) {
     const int c = threadIdx.x + e * kThreads;
     const int row = c >> 4, col = (c & 15) * 8;
-    qv[e] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
-    if (c < nq && row < M) qv[e] = *reinterpret_cast<const bf16x8*>(qg + (int64_t)row * 128 + col);
+    const bool real = c < nq && row < M;
+    qv[e] = *reinterpret_cast<const bf16x8*>(qg + (real ? (int64_t)row * 128 + col : 0));
   }
-  const float wv = threadIdx.x < M ? ka.w[(int64_t)seq * M + threadIdx.x] : 0.0f;
+  const float wv_raw = ka.w[(int64_t)seq * M + min((int)threadIdx.x, M - 1)];
+  const int64_t Lo = L - a.add;                          // the appended positions [Lo, L)
+  const bf16x8* app16 = ka.app_keys ? reinterpret_cast<const bf16x8*>(ka.app_keys) + (int64_t)seq * a.add * 16 : nullptr;
   // The first key tile's loads, behind the Q loads: loads complete in issue
   // order, so staging Q does not wait for the keys (HBM).
   // Positions past L read (unused) rows of the key store, so the loads need not
@@ -191,9 +192,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 && HI >= 8 ? 3 : 1) void score_ker
 #pragma unroll
   for (int e = 0; e < kMaxQPieces; ++e) {
     const int c = threadIdx.x + e * kThreads;
-    if (c < nq) *reinterpret_cast<bf16x8*>(sq + (c >> 4) * kQStride + (c & 15) * 8) = qv[e];
+    const bf16x8 zero = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    if (c < nq) *reinterpret_cast<bf16x8*>(sq + (c >> 4) * kQStride + (c & 15) * 8) = (c >> 4) < M ? qv[e] : zero;
   }
-  if (threadIdx.x < MTP * 32) sw[threadIdx.x] = wv;
+  if (threadIdx.x < MTP * 32) sw[threadIdx.x] = (int)threadIdx.x < M ? wv_raw : 0.0f;
   __syncthreads();
 
   const auto scores = s.scores;
