@@ -21,6 +21,10 @@
 namespace dsa {
 
 constexpr int kGatherThreads = 256;
+// Filled misses' rows a wave copies per round trip.  The misses bunch where the
+// ring hand has just evicted, so a wave may fill 16 or more; eight in flight
+// keeps such a wave to two or three round trips.
+constexpr int kFillBatch = 8;
 
 struct GatherKArgs {
   StepArgs a;
@@ -109,15 +113,15 @@ __device__ inline void assign_block(const GatherKArgs& ka, int block, int seq) {
   const uint32_t rw = off ? (sw & ring_bits(w, M)) : 0u;
   const uint32_t k = bm + __popc(sw & ~hw & ~rw & below);   // this lane's miss index (if a miss)
   const bool fills = off && mine && !((rw | hw) & bit) && k < n_assigned;
-  // Decode steps: the compact rows of the wave's first four misses that take a
-  // slot are requested now, beside the slot-table loads below; lane c holds
-  // 16-byte piece c of each.
+  // Decode steps: the compact rows of the wave's first kFillBatch misses that
+  // take a slot are requested now, beside the slot-table loads below; lane c
+  // holds 16-byte piece c of each.
   const int64_t rb = ka.row_bytes;
   uint64_t pre = ka.copy_fills ? __ballot(fills && ux < (uint32_t)ka.max_union) : 0ull;
-  int pl[4];
-  u32x4 pv[4];
+  int pl[kFillBatch];
+  u32x4 pv[kFillBatch];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < kFillBatch; ++q) {
     pl[q] = -1;
     if (pre) {                                         // (uniform)
       pl[q] = __builtin_ctzll(pre);
@@ -183,11 +187,11 @@ __device__ inline void assign_block(const GatherKArgs& ka, int block, int seq) {
   }
   if (!ka.copy_fills) return;
   // The filled misses' rows, from the compact rows attention wrote (the bytes it
-  // read from the host mirror) into their slots: the four requested above, then
-  // any others of the wave four at a time.
+  // read from the host mirror) into their slots: the ones requested above, then
+  // any others of the wave kFillBatch at a time.
   uint64_t fb = __ballot(fill >= 0);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < kFillBatch; ++q) {
     if (pl[q] < 0) continue;                           // (uniform)
     const int32_t f = __shfl(fill, pl[q]);
     fb &= ~(1ull << pl[q]);
@@ -195,10 +199,10 @@ __device__ inline void assign_block(const GatherKArgs& ka, int block, int seq) {
       *reinterpret_cast<DSA_GLOBAL u32x4*>(u.slots + (int64_t)f * rb + 16 * lane) = pv[q];
   }
   while (fb) {                                         // (uniform)
-    int32_t f4[4];
-    u32x4 v4[4];
+    int32_t f4[kFillBatch];
+    u32x4 v4[kFillBatch];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kFillBatch; ++q) {
       f4[q] = -1;
       if (fb) {
         const int l = __builtin_ctzll(fb);
@@ -210,7 +214,7 @@ __device__ inline void assign_block(const GatherKArgs& ka, int block, int seq) {
       }
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < kFillBatch; ++q)
       if (f4[q] >= 0 && lane < kCopyChunks16)
         *reinterpret_cast<DSA_GLOBAL u32x4*>(u.slots + (int64_t)f4[q] * rb + 16 * lane) = v4[q];
   }

@@ -83,13 +83,24 @@ __device__ inline PlanCounts plan_counts_block(const UnitG& u, const ScratchG& s
   // words, and the running totals.  A selected position is a hit iff it was
   // cached when the round started (every cached slot was filled in an earlier
   // round); the hit words are published for the assign kernel.
+  // The loads are unconditional (a word past the thread's range reads word 0;
+  // resident sessions, which cache nothing, read the union words in place of the
+  // cached ones) and masked once all are issued: a load in a branch of its own
+  // is waited for inside it.
+  const auto hot = off ? u.hot : sel;
   uint32_t swr[kPlanRegWords], hwr[kPlanRegWords];
   if (words_in_regs) {
 #pragma unroll
     for (int e = 0; e < kPlanRegWords; ++e) {
-      const int64_t w = w0 + e;
-      swr[e] = w < w1 ? sel[w] : 0u;
-      hwr[e] = (off && w < w1) ? u.hot[w] : 0u;
+      const int64_t w = w0 + e < w1 ? w0 + e : 0;
+      swr[e] = sel[w];
+      hwr[e] = hot[w];
+    }
+#pragma unroll
+    for (int e = 0; e < kPlanRegWords; ++e) {
+      const bool in = w0 + e < w1;
+      swr[e] = in ? swr[e] : 0u;
+      hwr[e] = in && off ? hwr[e] : 0u;
     }
   }
 
@@ -117,14 +128,15 @@ __device__ inline PlanCounts plan_counts_block(const UnitG& u, const ScratchG& s
       uint32_t cs[kPlanChunk], ch[kPlanChunk];
 #pragma unroll
       for (int e = 0; e < kPlanChunk; ++e) {
-        const int64_t w = r0 + 64 * e + lane;
-        cs[e] = w < sw1 ? sel[w] : 0u;
-        ch[e] = (off && w < sw1) ? u.hot[w] : 0u;
+        const int64_t w = min(r0 + 64 * e + lane, sw1 - 1);
+        cs[e] = sel[w];
+        ch[e] = hot[w];
       }
 #pragma unroll
       for (int e = 0; e < kPlanChunk; ++e) {
         const int64_t w = r0 + 64 * e + lane;
-        if (r0 + 64 * e < sw1) fn(w, cs[e], cs[e] & ch[e], w < sw1);   // (uniform in the wave)
+        const uint32_t sw = w < sw1 ? cs[e] : 0u;
+        if (r0 + 64 * e < sw1) fn(w, sw, off ? sw & ch[e] : 0u, w < sw1);   // (uniform in the wave)
       }
     }
   };
