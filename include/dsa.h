@@ -344,7 +344,7 @@ dsa_status dsa_decode_step_reuse(dsa_session* s, int32_t layer, int32_t src_laye
  * records that event in its steps only once it has prefetched (an event
  * between two launches delays the next one by a few µs): the session's first
  * prefetch waits instead for everything the source step's stream had enqueued
- * when the prefetch was called.  The layer's
+ * when the prefetch was called (that stream must still exist then).  The layer's
  * dsa_decode_step_reuse waits for the prefetch's completion event when it runs
  * on another stream; the next dsa_decode_step waits for every prefetch still
  * pending on another stream, since it replaces the selection they read.
