@@ -206,7 +206,7 @@ __global__ __launch_bounds__(HG * DS * 64) void attn_kernel(AttnKArgs ka) {
   constexpr int kLoads = (int)((kAttnScanWords / 4 + NT - 1) / NT);
   u32x4 wv[kLoads];
   if (own_counts) {                                      // (uniform)
-    const int64_t last = (nw + 3) / 4 - 1;              // the last 4-word piece holding a word
+    const int64_t last = max((nw + 3) / 4 - 1, (int64_t)0);   // the last 4-word piece holding a word
 #pragma unroll
     for (int e = 0; e < kLoads; ++e)
       wv[e] = reinterpret_cast<const DSA_GLOBAL u32x4*>(s.selmask)[min(tid + (int64_t)e * NT, last)];

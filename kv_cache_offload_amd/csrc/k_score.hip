@@ -162,8 +162,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 && HI >= 8 ? 3 : 1) void score_ker
   const int64_t first_sub = ((int64_t)blockIdx.x * kWaves + wave) * ka.subs_per_wave;
 
   // Q (zero padded to MTP*32 rows) and the head weights, staged in LDS below.
-  // They are requested right behind L, and without a branch per load: a padding piece reads row 0 and is zeroed where it is
-  // staged, so no load waits for another (M <= 256: at most 16 per thread).
+  // They are requested right behind L, and without a branch per load: a
+  // padding piece reads row 0 and is zeroed where it is staged, so no load
+  // waits for another (M <= 256: at most 16 per thread).
   const uint16_t* qg = ka.q + (int64_t)seq * M * 128;
   const int nq = MTP * 32 * 16;                          // 16-byte pieces of the padded Q
   bf16x8 qv[kMaxQPieces];
