@@ -366,11 +366,17 @@ __global__ __launch_bounds__(HG * DS * 64) void attn_kernel(AttnKArgs ka) {
     uint16_t* lat = lat_s[b & 1];
     uint16_t* rope = rope_s[b & 1];
     float* scl = scl_s[b & 1];
-    // This block's rows: the compact copy (the gather's output; only the assign
-    // pass, which copies a miss's row into its slot, reads it again in this
-    // step, so it is streamed past the caches with non-temporal stores), and the
-    // LDS staging -- the int8 latent widened to bf16, the scales as fp32, the
-    // RoPE as is.
+    // This block's rows, staged in LDS: the int8 latent widened to bf16, the
+    // scales as fp32, the RoPE as is; and their compact copy (the gather's
+    // output; only the assign pass, which copies a miss's row into its slot,
+    // reads it again in this step, so it is streamed past the caches with
+    // non-temporal stores).  The copy is stored here, beside the staging, except
+    // for a block of a split with host-mirror rows whose next block is still to
+    // arrive: that block's copy is stored once it is computed, since a store
+    // whose data registers are reused is waited for there, and, behind a
+    // branch, together with every later load -- the next block's host rows --
+    // so a store issued here would hold the block's products until the next
+    // block had arrived.
 #pragma unroll
     for (int e = 0; e < PPT; ++e) {
       const int q = tid + e * NT;
@@ -378,7 +384,7 @@ __global__ __launch_bounds__(HG * DS * 64) void attn_kernel(AttnKArgs ka) {
       const int rl = q / kRowPieces, part = q % kRowPieces, row = b * kBlk + rl;
       const int ux = s_ux[row];
       const u32x4 v = ux >= 0 ? raw[b & 1][e] : (u32x4){0u, 0u, 0u, 0u};
-      if (ux >= 0)
+      if ((early || b + 1 == NBLK) && ux >= 0)
         __builtin_nontemporal_store(v, reinterpret_cast<DSA_GLOBAL u32x4*>(s.compact + (int64_t)ux * rb + 16 * part));
       if (part < 32) {
         uint32_t w[8];
@@ -511,6 +517,18 @@ __global__ __launch_bounds__(HG * DS * 64) void attn_kernel(AttnKArgs ka) {
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, bv, o[nt], 0, 0, 0);
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, bv, o[nt], 0, 0, 0);
       }
+    }
+
+    // A split with host-mirror rows, not its last block: the block's compact rows, now (above).
+#pragma unroll
+    for (int e = 0; e < PPT && !early && b + 1 < NBLK; ++e) {
+      const int q = tid + e * NT;
+      if (q >= kBlkPieces) continue;
+      const int rl = q / kRowPieces, part = q % kRowPieces;
+      const int ux = s_ux[b * kBlk + rl];
+      if (ux >= 0)
+        __builtin_nontemporal_store(raw[b & 1][e],
+                                    reinterpret_cast<DSA_GLOBAL u32x4*>(s.compact + (int64_t)ux * rb + 16 * part));
     }
   }
   const float mx = m_run, ps = l_run;
